@@ -1,0 +1,153 @@
+"""Seeded synthetic inputs shaped like RWKV-7 WKV7 tensors.
+
+This module only draws and rounds inputs; it contains none of the recurrence's
+arithmetic, so both the fp64 oracle (test infrastructure) and the HIP path can
+consume its arrays bit-for-bit.
+
+Recipe (the five workloads of the WKV7 hot path; RWKV-7 "Goose" pages, P2
+Abstract and P5 Architecture describe vector decay, a per-channel in-context
+learning rate and separate removal / replacement keys):
+
+* ``r, k, v ~ N(0, 1)``                      (receptance, replacement key, value)
+* ``w = exp(-0.6065 * sigmoid(u))``, ``u ~ N(0, 1)``   (decay in (0.5453, 1))
+* ``kappa = normalise(N(0, 1)^N)`` per (b, t, h) token-head (removal key)
+* ``alpha = sigmoid(N(0, 1))`` per element (in-context learning rate)
+* ``a = -kappa``, ``b = kappa * alpha``
+* ``s0 ~ 0.1 * N(0, 1)`` where the workload has a random initial state
+* ``dy ~ N(0, 1)``, ``dsT = 0`` for the backward workload
+
+Draw order from ``numpy.random.default_rng(seed)`` (PCG64): r, k, v, u, kappa,
+alpha_raw, then s0 (if any), then dy (if any).  Everything is drawn in fp64,
+rounded to fp32 (round-to-nearest-even) and, for bf16 workloads, rounded again
+fp32 -> bf16 (RNE).  The returned arrays are fp32 holding exactly those
+rounded values, so upcasting them to fp64 is exact.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Dict, Optional
+
+import numpy as np
+
+DECAY_SCALE = 0.6065
+
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round an fp32 array to the nearest bfloat16 value (ties to even).
+
+    Returns fp32 values that are exactly representable in bf16.  Inputs are
+    finite here; NaN handling is not needed for synthetic data.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    u = (u + 0x7FFF + lsb) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32)
+
+
+def _sigmoid(x: np.ndarray) -> np.ndarray:
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+@dataclass
+class Workload:
+    """A named shape + dtype + options, one of the WKV7 workloads."""
+
+    name: str
+    B: int
+    T: int
+    H: int
+    N: int = 64
+    dtype: str = "bf16"          # "fp32" or "bf16": dtype of r,w,k,v,a,b,y and gradients
+    random_s0: bool = False      # s0 ~ 0.1 N(0,1) instead of zeros
+    backward: bool = False       # also draw dy (dsT = 0)
+    chunk_len: int = 0           # 0 = sequential scan, else chunked form
+    decode_steps: int = 0        # >0: decode workload, T is the step count
+    notes: str = ""
+
+
+# The five workloads of the WKV7 hot path.  Index 0 is small enough for the
+# oracle to finish in well under a second.
+WORKLOADS: Dict[str, Workload] = {
+    "fwd_fp32_small": Workload("fwd_fp32_small", B=1, T=64, H=2, dtype="fp32"),
+    "fwd_0.19b": Workload("fwd_0.19b", B=4, T=1024, H=12, dtype="bf16"),
+    "chunked_fwd_1.5b": Workload("chunked_fwd_1.5b", B=8, T=4096, H=32, dtype="bf16",
+                                 random_s0=True, chunk_len=16),
+    "fwd_bwd_2.9b": Workload("fwd_bwd_2.9b", B=8, T=4096, H=40, dtype="bf16",
+                             backward=True, chunk_len=16),
+    "decode_2.9b": Workload("decode_2.9b", B=256, T=512, H=40, dtype="bf16",
+                            random_s0=True, decode_steps=512),
+}
+
+
+@dataclass
+class Inputs:
+    r: np.ndarray
+    w: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    a: np.ndarray
+    b: np.ndarray
+    s0: Optional[np.ndarray] = None
+    dy: Optional[np.ndarray] = None
+    dsT: Optional[np.ndarray] = None
+    dtype: str = "fp32"
+    meta: dict = field(default_factory=dict)
+
+    def tensors(self):
+        return (self.r, self.w, self.k, self.v, self.a, self.b)
+
+
+def generate(B: int, T: int, H: int, N: int = 64, *, dtype: str = "fp32", seed: int = 0,
+             random_s0: bool = False, backward: bool = False,
+             token_shape: Optional[tuple] = None) -> Inputs:
+    """Draw one workload's inputs.
+
+    ``token_shape`` overrides the token-tensor shape (default ``(B, T, H, N)``);
+    the decode workload uses ``(T, B, H, N)`` = one ``[B, H, N]`` slice per step.
+    """
+    if dtype not in ("fp32", "bf16"):
+        raise ValueError(f"dtype must be fp32 or bf16, got {dtype!r}")
+    shape = tuple(token_shape) if token_shape is not None else (B, T, H, N)
+    if shape[-1] != N:
+        raise ValueError("last dimension of token_shape must be N")
+    rng = np.random.default_rng(seed)
+
+    def rnd(x: np.ndarray) -> np.ndarray:
+        x32 = x.astype(np.float32)
+        return round_to_bf16(x32) if dtype == "bf16" else x32
+
+    r = rnd(rng.standard_normal(shape))
+    k = rnd(rng.standard_normal(shape))
+    v = rnd(rng.standard_normal(shape))
+    u = rng.standard_normal(shape)
+    w = rnd(np.exp(-DECAY_SCALE * _sigmoid(u)))
+    del u
+    kappa = rng.standard_normal(shape)
+    kappa /= np.linalg.norm(kappa, axis=-1, keepdims=True)
+    alpha = _sigmoid(rng.standard_normal(shape))
+    a = rnd(-kappa)
+    b = rnd(kappa * alpha)
+    del kappa, alpha
+    s0 = None
+    if random_s0:
+        s0 = (0.1 * rng.standard_normal((B, H, N, N))).astype(np.float32)
+    dy = dsT = None
+    if backward:
+        dy = rnd(rng.standard_normal(shape))
+        dsT = np.zeros((B, H, N, N), dtype=np.float32)
+    return Inputs(r=r, w=w, k=k, v=v, a=a, b=b, s0=s0, dy=dy, dsT=dsT, dtype=dtype,
+                  meta=dict(B=B, T=T, H=H, N=N, seed=seed, shape=shape))
+
+
+def generate_workload(wl: Workload, seed: int = 0, *, T: Optional[int] = None,
+                      B: Optional[int] = None) -> Inputs:
+    """Inputs for a named workload; ``T``/``B`` may shrink it (same recipe)."""
+    TT = wl.T if T is None else T
+    BB = wl.B if B is None else B
+    if wl.decode_steps:
+        return generate(BB, TT, wl.H, wl.N, dtype=wl.dtype, seed=seed, random_s0=True,
+                        token_shape=(TT, BB, wl.H, wl.N))
+    return generate(BB, TT, wl.H, wl.N, dtype=wl.dtype, seed=seed,
+                    random_s0=wl.random_s0, backward=wl.backward)
