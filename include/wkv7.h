@@ -1,0 +1,147 @@
+/*
+ * wkv7.h -- C ABI of the MI355X (gfx950) WKV7 library.
+ *
+ * The operation: the RWKV-7 "Goose" WKV state recurrence, a generalised delta
+ * rule with a diagonal-plus-rank-one transition, vector-valued data-dependent
+ * decay and separate removal and replacement keys ("Paper Review: RWKV-7
+ * Goose", sections Architecture and The approach; "RWKV-7 Goose with
+ * Expressive Dynamic State Evolution", Abstract).  Per batch row b and head h
+ * the state S is an N x N fp32 matrix, row i = value channel, column j = key
+ * channel, and every token t applies
+ *
+ *     S <- S (diag(w_t) + a_t b_t^T) + v_t k_t^T,      y_t = S r_t
+ *
+ * i.e. z = S a_t (old state), S[i][j] = S[i][j] w_t[j] + z[i] b_t[j] +
+ * v_t[i] k_t[j], then the receptance reads the updated state ("once the WKV
+ * state is updated", The approach).  In RWKV-7, a = -kappa (removal key),
+ * b = kappa * alpha (in-context learning rate), k = the replacement key; the
+ * library takes a and b as general vectors and never assumes that form.
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates, frees or synchronises, and keeps no pointer after the
+ *     call returns.  All work is enqueued asynchronously on `stream` (a
+ *     hipStream_t passed as void*; NULL = the default stream).
+ *   - Layouts are row-major, last index fastest:
+ *       token tensors r, w, k, v, a, b, y, dy, dr..db   [B][T][H][N]
+ *       states s0, sT, dsT, ds0, decode state           [B][H][N][N] (fp32)
+ *       checkpoints                                     [B][H][ceil(T/64)][N][N] (fp32)
+ *   - `dtype` selects the element type of the token tensors and gradients:
+ *     WKV7_F32 (IEEE float) or WKV7_BF16 (bfloat16, outputs rounded to
+ *     nearest even).  States and checkpoints are always fp32.
+ *   - w is the multiplicative decay itself (not its logarithm).  The
+ *     sequential scan and the decode step accept any finite w.  The chunked
+ *     form (chunk_len > 0) divides by running products of w inside a chunk
+ *     and requires 0 < w <= 1 with w^chunk_len above ~1e-30.
+ *   - Validation is synchronous and launches nothing on error:
+ *       WKV7_ERR_INVALID_ARG  negative sizes, NULL required pointers, pointers
+ *                             not 16-byte aligned, NULL desc;
+ *       WKV7_ERR_UNSUPPORTED  N != 64, unknown dtype, unsupported chunk_len;
+ *       WKV7_ERR_WORKSPACE    workspace smaller than wkv7_workspace_bytes();
+ *       WKV7_ERR_LAUNCH       the HIP runtime reported a launch error.
+ *     No exception crosses the ABI.  There is no global mutable state, so
+ *     concurrent calls on different streams are safe.
+ *   - Inputs must not alias outputs, except the decode state (in place).
+ *   - Empty problems (B, H or T equal to 0) are valid.  With T = 0 the forward
+ *     copies s0 (or zeros) to sT; y may then be NULL.
+ */
+#ifndef WKV7_H
+#define WKV7_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define WKV7_ABI_VERSION 1
+#define WKV7_HEAD_SIZE 64        /* the only supported N */
+#define WKV7_CKPT_INTERVAL 64    /* tokens between stored backward checkpoints */
+
+typedef enum {
+    WKV7_OK = 0,
+    WKV7_ERR_INVALID_ARG = 1,
+    WKV7_ERR_UNSUPPORTED = 2,
+    WKV7_ERR_WORKSPACE = 3,
+    WKV7_ERR_LAUNCH = 4
+} wkv7_status;
+
+typedef enum { WKV7_F32 = 0, WKV7_BF16 = 1 } wkv7_dtype;
+
+/* Problem descriptor.  chunk_len = 0 selects the sequential scan (one token
+   at a time, state rows in registers); 16 selects the chunked form, whose
+   intra-chunk products run on bf16 matrix cores with the carried state kept
+   in fp32 (the pages state that training remains parallelisable: Abstract;
+   Elamur summary, Summary). */
+typedef struct {
+    int32_t B, T, H, N;
+    int32_t dtype;      /* wkv7_dtype */
+    int32_t chunk_len;  /* 0 or 16 */
+} wkv7_desc;
+
+/* Returns WKV7_ABI_VERSION. */
+int wkv7_abi_version(void);
+
+/* Static, never-NULL description of a status code. */
+const char *wkv7_status_string(int status);
+
+/* Bytes of the checkpoint buffer for `desc`: the fp32 state entering every
+   block of WKV7_CKPT_INTERVAL tokens, [B][H][ceil(T/64)][N][N].  0 on an
+   invalid descriptor. */
+size_t wkv7_ckpt_bytes(const wkv7_desc *desc);
+
+/* Bytes of device scratch wkv7_backward needs when it is given no
+   checkpoints (it then recomputes them into the workspace).  When the caller
+   passes the checkpoints of a wkv7_forward call, 0 bytes suffice. */
+size_t wkv7_workspace_bytes(const wkv7_desc *desc);
+
+/*
+ * Forward over a whole sequence.
+ *   r, w, k, v, a, b  [B][T][H][N] inputs (dtype).
+ *   s0                [B][H][N][N] fp32 initial state, or NULL for zeros.
+ *   y                 [B][T][H][N] output y_t = S_t r_t (dtype).
+ *   sT                [B][H][N][N] fp32 final state, or NULL.
+ *   ckpt              NULL, or wkv7_ckpt_bytes(desc) bytes: receives the
+ *                     state entering tokens 0, 64, 128, ... for wkv7_backward.
+ */
+int wkv7_forward(const wkv7_desc *desc, const void *r, const void *w, const void *k,
+                 const void *v, const void *a, const void *b, const float *s0, void *y,
+                 float *sT, float *ckpt, void *stream);
+
+/*
+ * Gradients of the scalar  L = sum_t <dy_t, y_t> + <dsT, S_T>  with respect to
+ * r, w, k, v, a, b (written in dtype) and s0 (fp32).  This is the adjoint of
+ * the same recurrence: the adjoint state G = dL/dS runs backwards in time as
+ * G <- G (diag(w_t) + b_t a_t^T) + dy_{t-1} r_{t-1}^T.
+ *   s0          as given to the forward (NULL = zeros).
+ *   dy          [B][T][H][N] upstream gradient of y (dtype).
+ *   dsT         [B][H][N][N] fp32 upstream gradient of S_T, or NULL (= 0).
+ *   ckpt        checkpoints written by wkv7_forward with the same desc and
+ *               inputs, or NULL; then `workspace` must hold at least
+ *               wkv7_workspace_bytes(desc) bytes and a forward sweep refills
+ *               it first.
+ *   dr..db      [B][T][H][N] outputs (dtype).  ds0: [B][H][N][N] fp32 or NULL.
+ */
+int wkv7_backward(const wkv7_desc *desc, const void *r, const void *w, const void *k,
+                  const void *v, const void *a, const void *b, const float *s0,
+                  const void *dy, const float *dsT, const float *ckpt, void *dr, void *dw,
+                  void *dk, void *dv, void *da, void *db, float *ds0, void *workspace,
+                  size_t workspace_bytes, void *stream);
+
+/*
+ * One token on B*H resident states, in place: constant memory and constant
+ * time per token at inference (Abstract).
+ *   r, w, k, v, a, b  [B][H][N] this step's inputs (dtype).
+ *   state             [B][H][N][N] fp32, read and overwritten.
+ *   y                 [B][H][N] output (dtype).
+ */
+int wkv7_decode_step(int32_t B, int32_t H, int32_t N, int32_t dtype, const void *r,
+                     const void *w, const void *k, const void *v, const void *a,
+                     const void *b, float *state, void *y, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WKV7_H */

@@ -1,0 +1,197 @@
+"""WKV7 (RWKV-7 "Goose" generalised delta rule) on MI355X -- Python binding.
+
+A thin ctypes layer over the C ABI in ``include/wkv7.h`` (``libwkv7.so``):
+argument checks and marshalling only, every step of the computation runs in
+the HIP kernels.  Tensors are torch CUDA (HIP) tensors; work is enqueued on
+the current torch stream.  There is no CPU fallback: if the library is not
+built, every call raises.
+
+Per head the state S (N x N, row = value channel, column = key channel)
+evolves as ``S <- S (diag(w_t) + a_t b_t^T) + v_t k_t^T`` and ``y_t = S r_t``
+("Paper Review: RWKV-7 Goose", Architecture and The approach).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libwkv7.so")
+
+WKV7_OK = 0
+WKV7_ERR_INVALID_ARG = 1
+WKV7_ERR_UNSUPPORTED = 2
+WKV7_ERR_WORKSPACE = 3
+WKV7_ERR_LAUNCH = 4
+WKV7_F32 = 0
+WKV7_BF16 = 1
+HEAD_SIZE = 64
+CKPT_INTERVAL = 64
+
+EXPORTED = ("wkv7_abi_version", "wkv7_status_string", "wkv7_ckpt_bytes", "wkv7_workspace_bytes",
+            "wkv7_forward", "wkv7_backward", "wkv7_decode_step")
+
+
+class WKV7Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib().wkv7_status_string(status).decode() if _lib is not None else str(status)
+        super().__init__(f"{where}: status {status} ({msg})")
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("N", ctypes.c_int32), ("dtype", ctypes.c_int32), ("chunk_len", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libwkv7.so (after torch, so both share one HIP runtime)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m rwkv_wkv7_delta_amd.build` (no CPU fallback exists)")
+        try:
+            import torch  # noqa: F401  (load torch's HIP runtime first)
+        except ImportError:
+            pass
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, Z = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        D = ctypes.POINTER(Desc)
+        L.wkv7_abi_version.restype = ctypes.c_int
+        L.wkv7_status_string.argtypes = [ctypes.c_int]
+        L.wkv7_status_string.restype = ctypes.c_char_p
+        L.wkv7_ckpt_bytes.argtypes = [D]
+        L.wkv7_ckpt_bytes.restype = Z
+        L.wkv7_workspace_bytes.argtypes = [D]
+        L.wkv7_workspace_bytes.restype = Z
+        L.wkv7_forward.argtypes = [D] + [P] * 6 + [P, P, P, P, P]
+        L.wkv7_forward.restype = ctypes.c_int
+        L.wkv7_backward.argtypes = [D] + [P] * 6 + [P, P, P, P] + [P] * 6 + [P, P, Z, P]
+        L.wkv7_backward.restype = ctypes.c_int
+        L.wkv7_decode_step.argtypes = [I, I, I, I] + [P] * 6 + [P, P, P]
+        L.wkv7_decode_step.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return WKV7_F32
+    if t.dtype == torch.bfloat16:
+        return WKV7_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return _torch().cuda.current_stream().cuda_stream
+
+
+def _check_tokens(ts, shape, dtype):
+    for t in ts:
+        if t is None:
+            raise ValueError("token tensors are required")
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("token tensors must be contiguous device tensors")
+        if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+            raise ValueError(f"token tensor shape/dtype mismatch: {tuple(t.shape)} {t.dtype}")
+
+
+def _check_state(t, shape):
+    torch = _torch()
+    if t is None:
+        return
+    if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.float32:
+        raise ValueError("states must be contiguous float32 device tensors")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"state shape {tuple(t.shape)} != {tuple(shape)}")
+
+
+def make_desc(B: int, T: int, H: int, N: int, dtype: int, chunk_len: int) -> Desc:
+    return Desc(B, T, H, N, dtype, chunk_len)
+
+
+def ckpt_bytes(desc: Desc) -> int:
+    return int(lib().wkv7_ckpt_bytes(ctypes.byref(desc)))
+
+
+def workspace_bytes(desc: Desc) -> int:
+    return int(lib().wkv7_workspace_bytes(ctypes.byref(desc)))
+
+
+def forward(r, w, k, v, a, b, s0=None, *, chunk_len: int = 0, want_state: bool = True,
+            want_ckpt: bool = False, out=None):
+    """Run the recurrence over [B, T, H, N] inputs.
+
+    Returns ``(y, sT, ckpt)``; ``sT`` / ``ckpt`` are None unless requested.
+    ``chunk_len`` 0 = sequential scan, 16 = chunked bf16-MFMA form.
+    """
+    torch = _torch()
+    B, T, H, N = r.shape
+    _check_tokens((r, w, k, v, a, b), r.shape, r.dtype)
+    _check_state(s0, (B, H, N, N))
+    desc = make_desc(B, T, H, N, _dtype_code(r), chunk_len)
+    y = out if out is not None else torch.empty_like(r)
+    sT = torch.empty((B, H, N, N), device=r.device, dtype=torch.float32) if want_state else None
+    ck = None
+    if want_ckpt:
+        nbytes = ckpt_bytes(desc)
+        ck = torch.empty(max(nbytes // 4, 1), device=r.device, dtype=torch.float32)
+    st = lib().wkv7_forward(ctypes.byref(desc), _ptr(r), _ptr(w), _ptr(k), _ptr(v), _ptr(a),
+                            _ptr(b), _ptr(s0), _ptr(y), _ptr(sT), _ptr(ck), _stream())
+    if st != WKV7_OK:
+        raise WKV7Error(st, "wkv7_forward")
+    return y, sT, ck
+
+
+def backward(r, w, k, v, a, b, dy, s0=None, dsT=None, ckpt=None, *, chunk_len: int = 16,
+             want_ds0: bool = True):
+    """Gradients of ``<dy, y> + <dsT, S_T>``: returns (dr, dw, dk, dv, da, db, ds0)."""
+    torch = _torch()
+    B, T, H, N = r.shape
+    _check_tokens((r, w, k, v, a, b, dy), r.shape, r.dtype)
+    _check_state(s0, (B, H, N, N))
+    _check_state(dsT, (B, H, N, N))
+    desc = make_desc(B, T, H, N, _dtype_code(r), chunk_len)
+    grads = [torch.empty_like(r) for _ in range(6)]
+    ds0 = torch.empty((B, H, N, N), device=r.device, dtype=torch.float32) if want_ds0 else None
+    ws = None
+    wsb = 0
+    if ckpt is None:
+        wsb = workspace_bytes(desc)
+        ws = torch.empty(max(wsb // 4, 1), device=r.device, dtype=torch.float32)
+    st = lib().wkv7_backward(ctypes.byref(desc), _ptr(r), _ptr(w), _ptr(k), _ptr(v), _ptr(a),
+                             _ptr(b), _ptr(s0), _ptr(dy), _ptr(dsT), _ptr(ckpt),
+                             *[_ptr(x) for x in grads], _ptr(ds0), _ptr(ws), wsb, _stream())
+    if st != WKV7_OK:
+        raise WKV7Error(st, "wkv7_backward")
+    return tuple(grads) + (ds0,)
+
+
+def decode_step(r, w, k, v, a, b, state, out=None):
+    """One token on resident states [B, H, N, N] (updated in place); returns y [B, H, N]."""
+    torch = _torch()
+    B, H, N = r.shape
+    _check_tokens((r, w, k, v, a, b), r.shape, r.dtype)
+    _check_state(state, (B, H, N, N))
+    y = out if out is not None else torch.empty_like(r)
+    st = lib().wkv7_decode_step(B, H, N, _dtype_code(r), _ptr(r), _ptr(w), _ptr(k), _ptr(v),
+                                _ptr(a), _ptr(b), _ptr(state), _ptr(y), _stream())
+    if st != WKV7_OK:
+        raise WKV7Error(st, "wkv7_decode_step")
+    return y

@@ -1,0 +1,80 @@
+// wkv7_device.h -- device helpers shared by the WKV7 kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wkv7 {
+
+constexpr int kN = 64;           // head size: state is kN x kN
+constexpr int kCkptInterval = 64;
+
+typedef uint16_t bf16_t;         // raw IEEE bfloat16 bits
+
+// ---------------------------------------------------------------------------
+// Element access for the two token dtypes.  bf16 -> fp32 is exact (a shift);
+// fp32 -> bf16 rounds to nearest even via the gfx950 conversion instruction.
+// ---------------------------------------------------------------------------
+template <typename T> struct Elem;
+
+template <> struct Elem<float> {
+    static __device__ __forceinline__ float4 load4(const float* p) {
+        return *reinterpret_cast<const float4*>(p);
+    }
+    static __device__ __forceinline__ float load1(const float* p) { return *p; }
+    static __device__ __forceinline__ void store1(float* p, float x) { *p = x; }
+    static __device__ __forceinline__ void store4(float* p, float4 x) {
+        *reinterpret_cast<float4*>(p) = x;
+    }
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+__device__ __forceinline__ bf16_t f2bf(float x) {
+    __bf16 h = static_cast<__bf16>(x);
+    return __builtin_bit_cast(bf16_t, h);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+
+template <> struct Elem<bf16_t> {
+    static __device__ __forceinline__ float4 load4(const bf16_t* p) {
+        const uint2 u = *reinterpret_cast<const uint2*>(p);
+        return make_float4(bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y));
+    }
+    static __device__ __forceinline__ float load1(const bf16_t* p) {
+        return __uint_as_float((uint32_t)(*p) << 16);
+    }
+    static __device__ __forceinline__ void store1(bf16_t* p, float x) { *p = f2bf(x); }
+    static __device__ __forceinline__ void store4(bf16_t* p, float4 x) {
+        uint2 u;
+        u.x = pack_bf16x2(x.x, x.y);
+        u.y = pack_bf16x2(x.z, x.w);
+        *reinterpret_cast<uint2*>(p) = u;
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Sum over the 16 lanes of a DPP row; every lane of the row gets the total.
+// quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float row16_sum(float x) {
+    x += __builtin_amdgcn_update_dpp(0.0f, x, 0xB1, 0xF, 0xF, false);
+    x += __builtin_amdgcn_update_dpp(0.0f, x, 0x4E, 0xF, 0xF, false);
+    x += __builtin_amdgcn_update_dpp(0.0f, x, 0x141, 0xF, 0xF, false);
+    x += __builtin_amdgcn_update_dpp(0.0f, x, 0x140, 0xF, 0xF, false);
+    return x;
+}
+
+__device__ __forceinline__ float dot4(float4 s, float4 q) {
+    return fmaf(s.w, q.w, fmaf(s.z, q.z, fmaf(s.y, q.y, s.x * q.x)));
+}
+
+// Token tensor offset for [B][T][H][N].
+__device__ __forceinline__ size_t tok_off(int b, int t, int h, int T, int H) {
+    return (((size_t)b * T + t) * H + h) * kN;
+}
+
+}  // namespace wkv7

@@ -1,0 +1,45 @@
+// wkv7_internal.h -- launcher interface between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace wkv7 {
+
+struct FwdArgs {
+    int B, T, H;
+    bool bf16;
+    const void *r, *w, *k, *v, *a, *b;
+    const float* s0;  // may be null
+    void* y;          // may be null only when T == 0
+    float* sT;        // may be null
+    float* ckpt;      // may be null
+};
+
+struct BwdArgs {
+    int B, T, H;
+    bool bf16;
+    const void *r, *w, *k, *v, *a, *b;
+    const float* s0;   // may be null
+    const void* dy;
+    const float* dsT;  // may be null
+    const float* ckpt; // checkpoints (never null here)
+    void *dr, *dw, *dk, *dv, *da, *db;
+    float* ds0;        // may be null
+};
+
+struct DecodeArgs {
+    int B, H;
+    bool bf16;
+    const void *r, *w, *k, *v, *a, *b;
+    float* state;
+    void* y;
+};
+
+hipError_t launch_seq_fwd(const FwdArgs& p, hipStream_t stream);
+hipError_t launch_chunk_fwd(const FwdArgs& p, int chunk_len, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs& p, int chunk_len, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& p, hipStream_t stream);
+hipError_t launch_state_copy(int BH, const float* s0, float* sT, hipStream_t stream);
+
+}  // namespace wkv7

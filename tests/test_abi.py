@@ -1,0 +1,110 @@
+"""C ABI checks that need no GPU: symbols, version, sizes, validation errors.
+
+No call here reaches a kernel launch: every case fails validation or is an
+empty problem, which returns before touching the device.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import rwkv_wkv7_delta_amd as wk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(wk.LIB_PATH):
+        pytest.skip("libwkv7.so not built")
+    return wk.lib()
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "wkv7.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(wkv7_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared()
+    assert set(names) == set(wk.EXPORTED), names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings(L):
+    assert L.wkv7_abi_version() == 1
+    for s in range(5):
+        assert len(L.wkv7_status_string(s)) > 0
+    assert L.wkv7_status_string(99) == b"unknown status"
+
+
+def test_ckpt_and_workspace_sizes(L):
+    d = wk.make_desc(8, 4096, 40, 64, wk.WKV7_BF16, 16)
+    assert wk.ckpt_bytes(d) == 8 * 40 * 64 * 64 * 64 * 4
+    assert wk.workspace_bytes(d) == wk.ckpt_bytes(d)
+    d = wk.make_desc(1, 65, 2, 64, wk.WKV7_F32, 0)
+    assert wk.ckpt_bytes(d) == 1 * 2 * 2 * 64 * 64 * 4
+    assert wk.ckpt_bytes(wk.make_desc(1, 64, 1, 32, wk.WKV7_F32, 0)) == 0   # invalid N
+
+
+FAKE = 1 << 20   # aligned, never dereferenced (validation fails first or nothing runs)
+
+
+def _fwd(L, d, ptrs=None, y=FAKE):
+    p = ptrs if ptrs is not None else [FAKE] * 6
+    return L.wkv7_forward(ctypes.byref(d), *p, None, y, None, None, None)
+
+
+def test_forward_validation(L):
+    assert L.wkv7_forward(None, *[FAKE] * 6, None, FAKE, None, None, None) == wk.WKV7_ERR_INVALID_ARG
+    assert _fwd(L, wk.make_desc(1, 8, 1, 32, wk.WKV7_BF16, 0)) == wk.WKV7_ERR_UNSUPPORTED
+    assert _fwd(L, wk.make_desc(-1, 8, 1, 64, wk.WKV7_BF16, 0)) == wk.WKV7_ERR_INVALID_ARG
+    assert _fwd(L, wk.make_desc(1, 8, 1, 64, 7, 0)) == wk.WKV7_ERR_UNSUPPORTED
+    assert _fwd(L, wk.make_desc(1, 8, 1, 64, wk.WKV7_BF16, 8)) == wk.WKV7_ERR_UNSUPPORTED
+    assert _fwd(L, wk.make_desc(1, 8, 1, 64, wk.WKV7_F32, 16)) == wk.WKV7_ERR_UNSUPPORTED
+    d = wk.make_desc(1, 8, 1, 64, wk.WKV7_BF16, 0)
+    assert _fwd(L, d, ptrs=[FAKE] * 5 + [None]) == wk.WKV7_ERR_INVALID_ARG
+    assert _fwd(L, d, ptrs=[FAKE] * 5 + [FAKE + 8]) == wk.WKV7_ERR_INVALID_ARG
+    assert _fwd(L, d, y=None) == wk.WKV7_ERR_INVALID_ARG
+    # Empty problems return OK without launching anything.
+    assert _fwd(L, wk.make_desc(0, 8, 4, 64, wk.WKV7_BF16, 0)) == wk.WKV7_OK
+    assert _fwd(L, wk.make_desc(2, 8, 0, 64, wk.WKV7_BF16, 16)) == wk.WKV7_OK
+
+
+def test_backward_validation(L):
+    d = wk.make_desc(1, 8, 1, 64, wk.WKV7_BF16, 16)
+    args = [FAKE] * 6 + [None, FAKE, None]
+    grads = [FAKE] * 6
+    assert L.wkv7_backward(ctypes.byref(d), *args, None, *grads, None, None, 0, None) == \
+        wk.WKV7_ERR_WORKSPACE
+    assert L.wkv7_backward(ctypes.byref(d), *args, None, *grads, None, FAKE, 100, None) == \
+        wk.WKV7_ERR_WORKSPACE
+    assert L.wkv7_backward(ctypes.byref(d), *args, None, *[FAKE] * 5, None, None, FAKE,
+                           1 << 30, None) == wk.WKV7_ERR_INVALID_ARG
+    d32 = wk.make_desc(1, 8, 1, 64, wk.WKV7_F32, 0)
+    assert L.wkv7_backward(ctypes.byref(d32), *args, FAKE, *grads, None, None, 0, None) == \
+        wk.WKV7_ERR_UNSUPPORTED
+    d0 = wk.make_desc(0, 8, 1, 64, wk.WKV7_BF16, 16)
+    assert L.wkv7_backward(ctypes.byref(d0), *args, FAKE, *grads, None, None, 0, None) == wk.WKV7_OK
+
+
+def test_decode_validation(L):
+    f = L.wkv7_decode_step
+    assert f(1, 1, 32, wk.WKV7_BF16, *[FAKE] * 8, None) == wk.WKV7_ERR_UNSUPPORTED
+    assert f(-1, 1, 64, wk.WKV7_BF16, *[FAKE] * 8, None) == wk.WKV7_ERR_INVALID_ARG
+    assert f(1, 1, 64, 5, *[FAKE] * 8, None) == wk.WKV7_ERR_UNSUPPORTED
+    assert f(1, 1, 64, wk.WKV7_BF16, *[FAKE] * 6, None, FAKE, None) == wk.WKV7_ERR_INVALID_ARG
+    assert f(1, 1, 64, wk.WKV7_BF16, *[FAKE] * 6, FAKE + 4, FAKE, None) == wk.WKV7_ERR_INVALID_ARG
+    assert f(0, 3, 64, wk.WKV7_BF16, *[FAKE] * 8, None) == wk.WKV7_OK
+
+
+def test_binding_has_no_cpu_fallback():
+    """The binding routes every call through libwkv7.so and never imports the oracle."""
+    import inspect
+    src = inspect.getsource(wk)
+    assert "oracle" not in src.replace("no CPU fallback", "")
