@@ -35,6 +35,8 @@ __device__ __forceinline__ bf16_t f2bf(float x) {
     __bf16 h = static_cast<__bf16>(x);
     return __builtin_bit_cast(bf16_t, h);
 }
+// Raw bits of a bf16 value (assigning __bf16 to an integer would convert the value).
+__device__ __forceinline__ bf16_t bits(__bf16 h) { return __builtin_bit_cast(bf16_t, h); }
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
 }
