@@ -41,27 +41,32 @@ namespace {
 constexpr int kL = 16;
 constexpr int kThreads = 256;
 constexpr int kChunksPerBlock = kCkptInterval / kL;   // 4
+// LDS row strides (bf16 elements): 144-byte and 40-byte rows keep the MFMA
+// operand reads (16 lanes on 16 different rows) off a single bank set.
+constexpr int kRow = kN + 8;
+constexpr int kRowT = kL + 4;
 
 enum { RAW_R = 0, RAW_W = 1, RAW_K = 2, RAW_A = 3, RAW_B = 4, RAW_V = 5, RAW_DY = 6 };
 enum { GS_DR = 0, GS_DW = 1, GS_DK = 2, GS_DV = 3, GS_DA = 4, GS_DB = 5 };
 
 struct __align__(16) BwdSmem {
-    bf16_t raw[7][kL][kN];                   // r, w, k, a, b, v, dy (bf16 bits)
+    bf16_t raw[7][kL][kRow];                   // r, w, k, a, b, v, dy (bf16 bits)
     float G[kL + 1][kN];                     // running decay products, G[0] = 1
     float gtot[4][kN];
-    bf16_t At[kL][kN], Rt[kL][kN], Bh[kL][kN], Kh[kL][kN], Bb[kL][kN], Kb[kL][kN];
-    bf16_t AtT[kN][kL], RtT[kN][kL], BhT[kN][kL], KhT[kN][kL], BbT[kN][kL], KbT[kN][kL];
+    bf16_t At[kL][kRow], Rt[kL][kRow], Bh[kL][kRow], Kh[kL][kRow], Bb[kL][kRow], Kb[kL][kRow];
+    bf16_t AtT[kN][kRowT], RtT[kN][kRowT], BhT[kN][kRowT], KhT[kN][kRowT], BbT[kN][kRowT],
+        KbT[kN][kRowT];
     float Amat[4][kL][kL];                   // Aab, Aak, Arb, Ark
     float Tm[kL][kL];                        // (I - Aab)^-1
-    bf16_t Wm[kL][kN];                       // Tm At
-    bf16_t Sblk[kChunksPerBlock][kN][kN];    // entry states of the block's chunks, [j][i]
-    bf16_t Zblk[kChunksPerBlock][kL][kN];    // removal read-outs Z of the block's chunks, [t][i]
-    bf16_t dXs[kL][kN];                      // [t][i]
-    bf16_t dSs[kN][kN];                      // adjoint of the chunk's exit state, [j][i]
+    bf16_t Wm[kL][kRow];                       // Tm At
+    bf16_t Sblk[kChunksPerBlock][kN][kRow];    // entry states of the block's chunks, [j][i]
+    bf16_t Zblk[kChunksPerBlock][kL][kRow];    // removal read-outs Z of the block's chunks, [t][i]
+    bf16_t dXs[kL][kRow];                      // [t][i]
+    bf16_t dSs[kN][kRow];                      // adjoint of the chunk's exit state, [j][i]
     float dAm[4][kL][kL];                    // dAab, dAak, dArb, dArk
     float colsum[4][kN];                     // per-wave partial sum_i dS[i][j] S0[i][j]
     float red[4][3][4][16];                  // per-wave scratch for token sums
-    bf16_t gst[6][kL][kN];                   // gradient staging for coalesced stores
+    bf16_t gst[6][kL][kRow];                   // gradient staging for coalesced stores
 };
 
 __device__ __forceinline__ float bf2f(bf16_t x) { return __uint_as_float((uint32_t)x << 16); }
@@ -84,7 +89,7 @@ __device__ __forceinline__ void wave_sync() {
 
 struct Ctx {
     int T, H, bb, hh, tid, wv, lane, l16, g, irow;
-    const bf16_t* src[7];
+    const bf16_t *r, *w, *k, *a, *b, *v, *dy;
 };
 
 // Raw loads of one chunk (nvec = 6 without dy, 7 with): 128 x 16 B per vector.
@@ -98,7 +103,10 @@ __device__ __forceinline__ void load_raw(const Ctx& c, int t0, int nvec, Prefetc
         const int item = c.tid + p * kThreads;
         const int q = item >> 7, t = (item >> 3) & 15, c8 = item & 7;
         if (q >= nvec) continue;
-        const bf16_t* sp = (q & 1) ? c.src[(2 * p + 1) < 7 ? 2 * p + 1 : 6] : c.src[2 * p];
+        // vector q = 2p + (tid >= 128): r/w, k/a, b/v, dy
+        const bool hi = c.tid >= 128;
+        const bf16_t* sp = p == 0 ? (hi ? c.w : c.r) : p == 1 ? (hi ? c.a : c.k)
+                         : p == 2 ? (hi ? c.v : c.b) : c.dy;
         if (t0 + t < c.T) {
             pf.v[p] = *reinterpret_cast<const uint4*>(sp + tok_off(c.bb, t0 + t, c.hh, c.T, c.H) + c8 * 8);
         } else {
@@ -167,35 +175,29 @@ __device__ void prep_chunk(const Ctx& c, BwdSmem& sm, bool need_w) {
     }
     __syncthreads();
     {
-        // L x L products: wave 0 Aab, 1 Aak, 2 Arb, 3 Ark.
+        // L x L products: wave 0 Aab (+ transpose, then Tm = (I - Aab)^-1),
+        // 1 Aak, 2 Arb, 3 Ark.
         const bf16_t* lrow = (c.wv < 2) ? &sm.At[c.l16][0] : &sm.Rt[c.l16][0];
         const bf16_t* rrow = (c.wv & 1) ? &sm.Kh[c.l16][0] : &sm.Bh[c.l16][0];
-        f32x4 acc = zero4();
+        f32x4 acc = zero4(), accT = zero4();
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) acc = mfma32(ld8(lrow + 32 * k2 + 8 * c.g), ld8(rrow + 32 * k2 + 8 * c.g), acc);
+        for (int k2 = 0; k2 < 2; ++k2) {
+            const bf16x8 av = ld8(lrow + 32 * k2 + 8 * c.g), bv = ld8(rrow + 32 * k2 + 8 * c.g);
+            acc = mfma32(av, bv, acc);
+            if (c.wv == 0) accT = mfma32(bv, av, accT);
+        }
         const bool strict = c.wv < 2;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int t = 4 * c.g + q, s = c.l16;
-            sm.Amat[c.wv][t][s] = (strict ? (s < t) : (s <= t)) ? acc[q] : 0.f;
+            acc[q] = (strict ? (s < t) : (s <= t)) ? acc[q] : 0.f;
+            accT[q] = (t < s) ? accT[q] : 0.f;
+            sm.Amat[c.wv][t][s] = acc[q];
         }
-    }
-    __syncthreads();
-    if (c.wv == 0) {
-        // Tm = (I - Aab)^-1 by forward substitution, one column per lane.
-        float col[kL];
+        if (c.wv == 0) {
+            const f32x4 TT = unit_lower_inverse_T(acc, accT, c.g, c.l16);
 #pragma unroll
-        for (int t = 0; t < kL; ++t) col[t] = (t == c.l16) ? 1.f : 0.f;
-#pragma unroll
-        for (int t = 1; t < kL; ++t) {
-            float acc = col[t];
-#pragma unroll
-            for (int s = 0; s < t; ++s) acc = fmaf(sm.Amat[0][t][s], col[s], acc);
-            col[t] = acc;
-        }
-        if (c.g == 0) {
-#pragma unroll
-            for (int t = 0; t < kL; ++t) sm.Tm[t][c.l16] = col[t];
+            for (int q = 0; q < 4; ++q) sm.Tm[c.l16][4 * c.g + q] = TT[q];
         }
     }
     __syncthreads();
@@ -231,8 +233,7 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_kernel(
     c.l16 = c.lane & 15;
     c.g = c.lane >> 4;
     c.irow = 16 * c.wv + c.l16;
-    c.src[0] = r; c.src[1] = w; c.src[2] = k; c.src[3] = a; c.src[4] = b; c.src[5] = v; c.src[6] = dy;
-    bf16_t* gout[6] = {dr, dw, dk, dv, da, db};
+    c.r = r; c.w = w; c.k = k; c.a = a; c.b = b; c.v = v; c.dy = dy;
     const int l16 = c.l16, g = c.g, wv = c.wv, irow = c.irow;
     const int nck = (T + kCkptInterval - 1) / kCkptInterval;
 
@@ -371,7 +372,7 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_kernel(
                 for (int q = 0; q < 4; ++q) {
                     const int j = 16 * jt + 4 * g + q;
                     sm.dSs[j][irow] = bits(dSb[jt][q]);
-                    const float p = row16_sum(dSt[jt][q] * bf2f(Ss[j * kN + irow]));
+                    const float p = row16_sum(dSt[jt][q] * bf2f(Ss[j * kRow + irow]));
                     if (l16 == 0) sm.colsum[wv][j] = p;
                 }
             }
@@ -389,7 +390,7 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_kernel(
             // ---- L x L adjoints: wave 0 dAab, 1 dAak, 2 dArb, 3 dArk ---------------
             {
                 const bf16_t* lrow = (wv < 2) ? &sm.dXs[l16][0] : &sm.raw[RAW_DY][l16][0];
-                const bf16_t* rrow = (wv & 1) ? &sm.raw[RAW_V][l16][0] : Zs + l16 * kN;
+                const bf16_t* rrow = (wv & 1) ? &sm.raw[RAW_V][l16][0] : Zs + l16 * kRow;
                 f32x4 acc = zero4();
 #pragma unroll
                 for (int k2 = 0; k2 < 2; ++k2)
@@ -408,11 +409,11 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_kernel(
             f32x4 dAt = zero4(), dRt = zero4(), dBh, dKh, dBb = zero4(), dKb = zero4();
 #pragma unroll
             for (int k2 = 0; k2 < 2; ++k2) {
-                const bf16x8 s0v = ld8(Ss + jcol * kN + 32 * k2 + 8 * g);
+                const bf16x8 s0v = ld8(Ss + jcol * kRow + 32 * k2 + 8 * g);
                 const bf16x8 dsv = ld8(&sm.dSs[jcol][32 * k2 + 8 * g]);
                 dAt = mfma32(ld8(&sm.dXs[l16][32 * k2 + 8 * g]), s0v, dAt);
                 dRt = mfma32(ld8(&sm.raw[RAW_DY][l16][32 * k2 + 8 * g]), s0v, dRt);
-                dBb = mfma32(ld8(Zs + l16 * kN + 32 * k2 + 8 * g), dsv, dBb);
+                dBb = mfma32(ld8(Zs + l16 * kRow + 32 * k2 + 8 * g), dsv, dBb);
                 dKb = mfma32(ld8(&sm.raw[RAW_V][l16][32 * k2 + 8 * g]), dsv, dKb);
             }
             {
@@ -501,7 +502,8 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_kernel(
             for (int p = 0; p < 3; ++p) {
                 const int item = c.tid + p * kThreads;
                 const int q = item >> 7, t = (item >> 3) & 15, c8 = item & 7;
-                bf16_t* gp = (q & 1) ? gout[2 * p + 1] : gout[2 * p];   // q in {2p, 2p+1}
+                const bool hi = c.tid >= 128;   // q = 2p + hi: dr/dw, dk/dv, da/db
+                bf16_t* gp = p == 0 ? (hi ? dw : dr) : p == 1 ? (hi ? dv : dk) : (hi ? db : da);
                 if (t0 + t < T)
                     *reinterpret_cast<uint4*>(gp + tok_off(c.bb, t0 + t, c.hh, T, H) + c8 * 8) =
                         *reinterpret_cast<const uint4*>(&sm.gst[q][t][c8 * 8]);

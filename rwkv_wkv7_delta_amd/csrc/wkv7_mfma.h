@@ -33,27 +33,39 @@ __device__ __forceinline__ f32x4 zero4() {
     return z;
 }
 
-__device__ __forceinline__ bf16x4 cvt4(f32x4 x) {
-    bf16x4 r;
-    r[0] = (__bf16)x[0];
-    r[1] = (__bf16)x[1];
-    r[2] = (__bf16)x[2];
-    r[3] = (__bf16)x[3];
-    return r;
-}
+// fp32 -> bf16, round to nearest even, two values per v_cvt_pk_bf16_f32.
+__device__ __forceinline__ bf16x4 cvt4(f32x4 x) { return __builtin_convertvector(x, bf16x4); }
 __device__ __forceinline__ bf16x4 cvt4(float a, float b, float c, float d) {
-    bf16x4 r;
-    r[0] = (__bf16)a;
-    r[1] = (__bf16)b;
-    r[2] = (__bf16)c;
-    r[3] = (__bf16)d;
-    return r;
+    const f32x4 x = {a, b, c, d};
+    return __builtin_convertvector(x, bf16x4);
 }
 __device__ __forceinline__ bf16x8 cat8(bf16x4 lo, bf16x4 hi) {
     bf16x8 r;
     r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
     r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
     return r;
+}
+
+// (I - A)^-1 for a strictly lower triangular 16x16 A (so A^16 = 0) as the
+// doubling product (I + A)(I + A^2)(I + A^4)(I + A^8), all on bf16 MFMA with
+// fp32 accumulation.  Inputs are the accumulator tiles of A and A^T; C-layout
+// registers fed as an A operand stand for the transpose of their matrix, so
+// the chain needs no data movement.  Returns T^T in C layout, i.e. lane
+// (g, l16) register q holds T[l16][4g+q] -- exactly T's A-operand layout.
+__device__ __forceinline__ f32x4 unit_lower_inverse_T(f32x4 A, f32x4 AT, int g, int l16) {
+    const f32x4 z = zero4();
+    const f32x4 A2 = mfma16(cvt4(AT), cvt4(A), z);     // A A
+    const f32x4 A2T = mfma16(cvt4(A), cvt4(AT), z);    // A^T A^T
+    const f32x4 A4 = mfma16(cvt4(A2T), cvt4(A2), z);
+    const f32x4 A4T = mfma16(cvt4(A2), cvt4(A2T), z);
+    const f32x4 A8 = mfma16(cvt4(A4T), cvt4(A4), z);
+    f32x4 P = AT;                                      // (I + A)^T
+#pragma unroll
+    for (int q = 0; q < 4; ++q) P[q] += (4 * g + q == l16) ? 1.f : 0.f;
+    P = mfma16(cvt4(A2), cvt4(P), P);                  // P^T += (A^2)^T P^T
+    P = mfma16(cvt4(A4), cvt4(P), P);
+    P = mfma16(cvt4(A8), cvt4(P), P);
+    return P;
 }
 
 }  // namespace wkv7
