@@ -17,30 +17,27 @@
 //   Y   = Q S0^T + Y0                (row t of Y is y_t)
 //   S_L^T = diag(G_L) S0^T + H + Bb^T Z
 //
-// Mapping to gfx950: one workgroup of 4 waves per (b, h).  Wave w owns value
-// rows 16w..16w+15 of the state, held as S^T in four 16x16 fp32 accumulator
-// tiles (key blocks); because an accumulator tile feeds the next product
-// directly as its B operand (wkv7_mfma.h), every state-dependent product is a
-// left multiplication that reads the state straight from registers.
-//
-// The per-chunk work is software-pipelined with ONE barrier per chunk.  In
-// the barrier interval of iteration `it` every wave does, independently:
-//   E(it)    decay products and scaled vectors of chunk it for its 16 key
-//            columns (the running product over tokens is a prefix across
-//            the wave's four lane groups, exchanged through wave-private LDS);
-//   MW(it-1) the 16x16 products of chunk it-1, the triangular inverse, its
-//            key block of W and Q, and U, Y0, H for its value rows -- each
-//            wave recomputes the small L x L tiles itself instead of
-//            exchanging them;
-//   ST(it-2) the state chain of chunk it-2;
-//   the coalesced y store of chunk it-3, the LDS stash of chunk it+1 and
-//   the global loads of chunk it+4 (a three-deep register ring, so no load's
-//   latency is ever waited on within the interval that issued it).
-// Within the interval every LDS operand read is issued before any LDS write,
-// since the compiler cannot prove the rotating slots disjoint.
-// The four streams are independent within the interval, so their latencies
-// overlap instead of adding up.  Chunks beyond T are all-padding (w = 1,
-// everything else 0), for which every stage is the identity on the state.
+// Mapping to gfx950: one workgroup of 8 waves per (b, h), split by role.
+//   Producer waves p = 0..3 build each chunk's state-independent factors:
+//     E   decay products and scaled vectors for key columns 16p..16p+15 (the
+//         running product over tokens is a prefix across the wave's four
+//         lane groups, exchanged through wave-private LDS);
+//     MW  the 16x16 products, the triangular inverse (every producer
+//         computes the small tiles itself instead of exchanging them) and
+//         key block p of W and Q.
+//   Consumer waves p = 0..3 own value rows 16p..16p+15 of the state, held as
+//   S^T in four 16x16 fp32 accumulator tiles (key blocks); an accumulator
+//   tile feeds the next product directly as its B operand (wkv7_mfma.h), so
+//   every state-dependent product (U, Y0, Z, Y, the state update) is a left
+//   multiplication that reads the state straight from registers.
+// The work is software-pipelined with ONE barrier per chunk: in interval
+// `it` the producers run E(it) and MW(it-1) while the consumers run the
+// state chain of chunk it-2 and store y of chunk it-3; chunk factors pass
+// through three rotating LDS slots.  Each role needs few enough registers for
+// two waves per SIMD, so a consumer's MFMA chain interleaves with a
+// producer's VALU work.  Raw token loads run three intervals ahead in a
+// register ring.  Chunks beyond T are all-padding (w = 1, everything else 0),
+// for which every stage is the identity on the state.
 
 #include "wkv7_device.h"
 #include "wkv7_internal.h"
@@ -51,7 +48,7 @@ namespace wkv7 {
 namespace {
 
 constexpr int kL = 16;
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 // LDS row strides (bf16 elements).  A 64-wide row would be exactly one sweep
 // of the 32 four-byte banks, so the operand reads below (16 lanes on 16
 // different rows, same columns) would all hit the same banks; 144-byte and
@@ -60,20 +57,23 @@ constexpr int kRow = kN + 8;    // rows of 64 elements
 constexpr int kRowT = kL + 4;   // rows of 16 elements
 
 enum { RAW_R = 0, RAW_W = 1, RAW_K = 2, RAW_A = 3, RAW_B = 4, RAW_V = 5 };
+enum { TILE_T = 0, TILE_AK = 1, TILE_RB = 2, TILE_RK = 3 };
 
-// State-independent factors of one chunk, shared by the four waves.
+// Everything one chunk passes from the producers to the consumers.
 struct Slot {
-    bf16_t At[kL][kRow], Rt[kL][kRow], Bh[kL][kRow], Kh[kL][kRow];  // row-major [t][j]
-    bf16_t BbT[kN][kRowT], KbT[kN][kRowT];                          // [j][t]
-    float gL[kN];
+    bf16_t At[kL][kRow], Rt[kL][kRow], Bh[kL][kRow], Kh[kL][kRow];  // E -> MW, row-major [t][j]
+    bf16_t BbT[kN][kRowT], KbT[kN][kRowT];                          // E -> ST, [j][t]
+    bf16_t Vt[kN][kRowT];                                           // E -> ST, v as [i][t]
+    float gL[kN];                                                   // E -> ST
+    bf16_t Wm[kL][kRow], Qm[kL][kRow];                              // MW -> ST
+    uint2 tiles[4][64];   // MW -> ST: A-operand register images of Tm, Aak, Arb, Ark
 };
 
 struct __align__(16) FwdSmem {
     bf16_t raw[2][6][kL][kRow];   // r, w, k, a, b, v of two chunks (bf16 bits)
     Slot sl[3];
-    bf16_t Wm[2][kL][kRow], Qm[2][kL][kRow];
     bf16_t Ys[2][kL][kRow];
-    float red[4][4][16];          // wave-private prefix scratch
+    float red[4][4][16];          // producer-private prefix scratch
 };
 
 __device__ __forceinline__ float bf2f(bf16_t x) { return __uint_as_float((uint32_t)x << 16); }
@@ -90,19 +90,18 @@ __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Outputs of E kept in registers for the same wave's MW one interval later.
+// Outputs of E kept in a producer's registers for its MW one interval later.
 struct ERegs {
-    bf16x4 At;   // At[4g+q][16w+l16]: B operand of W = Tm At
-    f32x4 Rt;    // Rt[4g+q][16w+l16]: accumulator init of Q
-    bf16x4 V;    // v[4g+q][16w+l16]: B operand of the V products
-};
-// Outputs of MW kept for the same wave's ST one interval later.
-struct MWRegs {
-    f32x4 U, Y0;
-    bf16x4 V;    // v of the chunk again, for H = Kb^T V inside ST
+    bf16x4 At;   // At[4g+q][16p+l16]: B operand of W = Tm At
+    f32x4 Rt;    // Rt[4g+q][16p+l16]: accumulator init of Q
 };
 
-__global__ __launch_bounds__(kThreads, 2) void chunk_fwd_kernel(
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));   // plain SSA vector
+struct Raw {
+    u32x4 x[3];
+};
+
+__global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
     int T, int H, const bf16_t* __restrict__ r, const bf16_t* __restrict__ w,
     const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const bf16_t* __restrict__ a,
     const bf16_t* __restrict__ b, const float* __restrict__ s0, bf16_t* __restrict__ y,
@@ -111,23 +110,25 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_fwd_kernel(
     const int bh = blockIdx.x;
     const int bb = bh / H, hh = bh % H;
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wv = tid >> 6;
+    const bool producer = tid < 256;
+    const int rtid = tid & 255;               // index within the role
+    const int lane = tid & 63, wp = rtid >> 6;
     const int l16 = lane & 15, g = lane >> 4;
-    const int col = 16 * wv + l16;            // key column (E) / value row (MW, ST) of this lane
+    const int col = 16 * wp + l16;            // key column (producer) / value row (consumer)
     const int nck = (T + kCkptInterval - 1) / kCkptInterval;
     const int nch = (T + kL - 1) / kL;
 
-    // ---- state: S^T tiles, lane holds S[col][16 jt + 4 g + q] ------------------
+    // ---- consumer state: S^T tiles, lane holds S[col][16 jt + 4 g + q] ----------
     f32x4 S[4];
-    {
-        const float* base = s0 ? s0 + ((size_t)bh * kN + col) * kN : nullptr;
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
-            if (base) {
+    for (int jt = 0; jt < 4; ++jt) S[jt] = zero4();
+    if (!producer) {
+        if (s0) {
+            const float* base = s0 + ((size_t)bh * kN + col) * kN;
+#pragma unroll
+            for (int jt = 0; jt < 4; ++jt) {
                 const float4 x = *reinterpret_cast<const float4*>(base + 16 * jt + 4 * g);
                 S[jt][0] = x.x; S[jt][1] = x.y; S[jt][2] = x.z; S[jt][3] = x.w;
-            } else {
-                S[jt] = zero4();
             }
         }
         if (ckpt && T > 0) {
@@ -139,40 +140,33 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_fwd_kernel(
         }
     }
 
-    // ---- raw token loads: 6 vectors x 16 tokens x 64 = 768 x 16 bytes.  Thread
-    // tid loads vector 2p + (tid >= 128), token (tid >> 3) & 15, columns
-    // 8 (tid & 7) .. +7, for p = 0, 1, 2.  Loads are branch-free (tokens past
-    // T re-read token T-1; E replaces them by padding) and are issued three
-    // intervals before E uses them, into a three-deep register ring; the
-    // stash into LDS happens one interval before use, so it waits only on
-    // loads that were issued two intervals earlier.
-    const bool hi = tid >= 128;
+    // ---- producer raw loads: 6 vectors x 16 tokens x 64 = 768 x 16 bytes.  Thread
+    // rtid loads vector 2p + (rtid >= 128), token (rtid >> 3) & 15, columns
+    // 8 (rtid & 7) .. +7, for p = 0, 1, 2.  Loads are branch-free (tokens past
+    // T re-read token T-1 and become padding when stashed) and are issued
+    // three intervals before use into a three-deep register ring; the stash
+    // into LDS happens one interval before use.
+    const bool hi = rtid >= 128;
     const bf16_t* const sp_p[3] = {hi ? w : r, hi ? a : k, hi ? v : b};
-    const int ld_t = (tid >> 3) & 15, ld_c8 = tid & 7;
-    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));   // plain SSA vector
-    struct Raw {
-        u32x4 x[3];
-    };
+    const int ld_t = (rtid >> 3) & 15, ld_c8 = rtid & 7;
     auto load_raw = [&](int c, Raw& o) __attribute__((always_inline)) {
         const int t = min(c * kL + ld_t, T - 1);
         const size_t off = tok_off(bb, t, hh, T, H) + ld_c8 * 8;
 #pragma unroll
         for (int p = 0; p < 3; ++p) o.x[p] = *reinterpret_cast<const u32x4*>(sp_p[p] + off);
     };
-    // Padding tokens (past T) become w = 1 and zeros here, once, so that E's
-    // reads need no conditions.
     auto stash_raw = [&](int c, const Raw& o) __attribute__((always_inline)) {
         const bool ok = c * kL + ld_t < T;
 #pragma unroll
         for (int p = 0; p < 3; ++p) {
-            const unsigned pad = (p == 0 && hi) ? 0x3F803F80u : 0u;
+            const unsigned pad = (p == 0 && hi) ? 0x3F803F80u : 0u;   // padding: w = 1
             const u32x4 padv = {pad, pad, pad, pad};
             *reinterpret_cast<u32x4*>(&sm.raw[c & 1][2 * p + (hi ? 1 : 0)][ld_t][ld_c8 * 8]) =
                 ok ? o.x[p] : padv;
         }
     };
 
-    // ---- E: decay products and scaled vectors of chunk c, key columns `col` ----
+    // ---- E (producer): decay products and scaled vectors, key columns `col` -----
     auto stage_E = [&](int c) __attribute__((always_inline)) -> ERegs {
         Slot& s = sm.sl[c % 3];
         const bf16_t(*Rr)[kL][kRow] = sm.raw[c & 1];
@@ -188,10 +182,10 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_fwd_kernel(
             run *= R[RAW_W][q];
             gp[q] = run;
         }
-        sm.red[wv][g][l16] = run;
+        sm.red[wp][g][l16] = run;
         wave_sync();
-        const float g0 = sm.red[wv][0][l16], g1 = sm.red[wv][1][l16];
-        const float g2 = sm.red[wv][2][l16], g3 = sm.red[wv][3][l16];
+        const float g0 = sm.red[wp][0][l16], g1 = sm.red[wp][1][l16];
+        const float g2 = sm.red[wp][2][l16], g3 = sm.red[wp][3][l16];
         const float before = g == 0 ? 1.f : g == 1 ? g0 : g == 2 ? g0 * g1 : (g0 * g1) * g2;
         const float GL = ((g0 * g1) * g2) * g3;
         ERegs e;
@@ -216,13 +210,14 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_fwd_kernel(
         }
         *reinterpret_cast<bf16x4*>(&s.BbT[col][4 * g]) = cvt4(bb4[0], bb4[1], bb4[2], bb4[3]);
         *reinterpret_cast<bf16x4*>(&s.KbT[col][4 * g]) = cvt4(kb4[0], kb4[1], kb4[2], kb4[3]);
+        *reinterpret_cast<bf16x4*>(&s.Vt[col][4 * g]) =
+            cvt4(R[RAW_V][0], R[RAW_V][1], R[RAW_V][2], R[RAW_V][3]);
         if (g == 0) s.gL[col] = GL;
         e.At = cvt4(at[0], at[1], at[2], at[3]);
-        e.V = cvt4(R[RAW_V][0], R[RAW_V][1], R[RAW_V][2], R[RAW_V][3]);
         return e;
     };
 
-    // ---- MW: L x L tiles, inverse, W / Q key block, U / Y0 / H value block -----
+    // ---- MW (producer): L x L tiles, inverse, key block of W and Q --------------
     struct MWIn {
         bf16x8 av[2], rv[2], bv[2], kv[2];
     };
@@ -238,7 +233,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_fwd_kernel(
         }
         return in;
     };
-    auto stage_MW = [&](int c, const MWIn& in, const ERegs& e) __attribute__((always_inline)) -> MWRegs {
+    auto stage_MW = [&](int c, const MWIn& in, const ERegs& e) __attribute__((always_inline)) {
+        Slot& s = sm.sl[c % 3];
         f32x4 ab = zero4(), abT = zero4(), akT = zero4(), rbT = zero4(), rkT = zero4();
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
@@ -258,41 +254,43 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_fwd_kernel(
             rbT[q] = (m <= n) ? rbT[q] : 0.f;
             rkT[q] = (m <= n) ? rkT[q] : 0.f;
         }
-        // Tile registers of X^T fed as an A operand stand for X: Tm, Aak, Arb, Ark.
+        // Tile registers of X^T fed as an A operand stand for X: Tm, Arb.
         const bf16x4 Tm = cvt4(unit_lower_inverse_T(ab, abT, g, l16));
-        const bf16x4 Aak = cvt4(akT), Arb = cvt4(rbT), Ark = cvt4(rkT);
+        const bf16x4 Arb = cvt4(rbT);
         const f32x4 Wt = mfma16(Tm, e.At, zero4());              // W[t][col]
         const f32x4 Qt = mfma16(Arb, cvt4(Wt), e.Rt);             // Q[t][col]
-        bf16_t* Wd = &sm.Wm[c & 1][0][0];
-        bf16_t* Qd = &sm.Qm[c & 1][0][0];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            Wd[(4 * g + q) * kRow + col] = f2bf(Wt[q]);
-            Qd[(4 * g + q) * kRow + col] = f2bf(Qt[q]);
+            s.Wm[4 * g + q][col] = f2bf(Wt[q]);
+            s.Qm[4 * g + q][col] = f2bf(Qt[q]);
         }
-        MWRegs m;
-        const f32x4 AkV = mfma16(Aak, e.V, zero4());
-        m.U = mfma16(Tm, cvt4(AkV), zero4());
-        m.Y0 = mfma16(Ark, e.V, mfma16(Arb, cvt4(m.U), zero4()));
-        m.V = e.V;
-        return m;
+        if (wp == 0) {
+            s.tiles[TILE_T][lane] = __builtin_bit_cast(uint2, Tm);
+            s.tiles[TILE_AK][lane] = __builtin_bit_cast(uint2, cvt4(akT));
+            s.tiles[TILE_RB][lane] = __builtin_bit_cast(uint2, Arb);
+            s.tiles[TILE_RK][lane] = __builtin_bit_cast(uint2, cvt4(rkT));
+        }
     };
 
-    // ---- ST: the state chain of chunk c -----------------------------------------
+    // ---- ST (consumer): value-row block `col` of the state chain of chunk c -----
     struct STIn {
+        bf16x4 Tm, Aak, Arb, Ark, V;
         bf16x8 wa[2], qa[2];
         bf16x4 bbt[4], kbt[4];
         float4 gl[4];
     };
     auto read_ST = [&](int c) __attribute__((always_inline)) -> STIn {
         const Slot& s = sm.sl[c % 3];
-        const bf16_t* Wm = &sm.Wm[c & 1][0][0];
-        const bf16_t* Qm = &sm.Qm[c & 1][0][0];
         STIn in;
+        in.Tm = __builtin_bit_cast(bf16x4, s.tiles[TILE_T][lane]);
+        in.Aak = __builtin_bit_cast(bf16x4, s.tiles[TILE_AK][lane]);
+        in.Arb = __builtin_bit_cast(bf16x4, s.tiles[TILE_RB][lane]);
+        in.Ark = __builtin_bit_cast(bf16x4, s.tiles[TILE_RK][lane]);
+        in.V = ld4(&s.Vt[col][4 * g]);
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
-            in.wa[k2] = ld4x2(Wm + l16 * kRow + 32 * k2 + 4 * g);
-            in.qa[k2] = ld4x2(Qm + l16 * kRow + 32 * k2 + 4 * g);
+            in.wa[k2] = ld4x2(&s.Wm[l16][32 * k2 + 4 * g]);
+            in.qa[k2] = ld4x2(&s.Qm[l16][32 * k2 + 4 * g]);
         }
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
@@ -302,11 +300,15 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_fwd_kernel(
         }
         return in;
     };
-    auto stage_ST = [&](int c, const STIn& in, const MWRegs& m) __attribute__((always_inline)) {
+    auto stage_ST = [&](int c, const STIn& in) __attribute__((always_inline)) {
+        // U = Tm Aak V,  Y0 = Arb U + Ark V   (value block `col`)
+        const f32x4 AkV = mfma16(in.Aak, in.V, zero4());
+        const f32x4 U = mfma16(in.Tm, cvt4(AkV), zero4());
+        const f32x4 Y0 = mfma16(in.Ark, in.V, mfma16(in.Arb, cvt4(U), zero4()));
         bf16x4 Sb[4];
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) Sb[jt] = cvt4(S[jt]);
-        f32x4 Z = m.U, Yt = m.Y0;
+        f32x4 Z = U, Yt = Y0;
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
             const bf16x8 bs = cat8(Sb[2 * k2], Sb[2 * k2 + 1]);
@@ -321,12 +323,12 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_fwd_kernel(
             acc[1] = in.gl[jt].y * S[jt][1];
             acc[2] = in.gl[jt].z * S[jt][2];
             acc[3] = in.gl[jt].w * S[jt][3];
-            acc = mfma16(in.kbt[jt], m.V, acc);          // + H = Kb^T V
-            S[jt] = mfma16(in.bbt[jt], Zb, acc);
+            acc = mfma16(in.kbt[jt], in.V, acc);          // + H = Kb^T V
+            S[jt] = mfma16(in.bbt[jt], Zb, acc);           // + Bb^T Z
         }
-        bf16_t* Yd = &sm.Ys[c & 1][0][0];
+        const bf16x4 Yb = cvt4(Yt);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) Yd[(4 * g + q) * kRow + col] = f2bf(Yt[q]);
+        for (int q = 0; q < 4; ++q) sm.Ys[c & 1][4 * g + q][col] = bits(Yb[q]);
         const int done = (c + 1) * kL;
         if (ckpt && (done % kCkptInterval) == 0 && done < T) {
             float* dst = ckpt + (((size_t)bh * nck + done / kCkptInterval) * kN + col) * kN;
@@ -337,8 +339,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_fwd_kernel(
         }
     };
 
-    // y of chunk c: 16 tokens x 16 lanes x 8 B from the staged read-outs.
-    const int yt = tid >> 4, yc4 = tid & 15;
+    // y of chunk c (consumers): 16 tokens x 16 lanes x 8 B from the staged read-outs.
+    const int yt = rtid >> 4, yc4 = rtid & 15;
     auto read_y = [&](int c) __attribute__((always_inline)) -> uint2 {
         return *reinterpret_cast<const uint2*>(&sm.Ys[c & 1][yt][yc4 * 4]);
     };
@@ -349,59 +351,59 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_fwd_kernel(
     };
 
     if (T > 0) {
-        // Register ring: the raw loads of chunk c live in ring slot c % 3 until
-        // stashed.  Three named variables, not an array, so that the ring is
-        // never promoted to LDS or scratch.
+        // Producer register ring: the raw loads of chunk c live in ring slot
+        // c % 3 until stashed (three named variables, never an array, so that
+        // the ring is neither promoted to LDS nor to scratch).
         Raw rb0, rb1, rb2;
-        load_raw(0, rb0);
-        load_raw(1, rb1);
-        load_raw(2, rb2);
-        stash_raw(0, rb0);
-        load_raw(3, rb0);
+        ERegs e_prev;
+        e_prev.At = cvt4(zero4());
+        e_prev.Rt = zero4();
+        if (producer) {
+            load_raw(0, rb0);
+            load_raw(1, rb1);
+            load_raw(2, rb2);
+            stash_raw(0, rb0);
+            load_raw(3, rb0);
+        }
         __syncthreads();
-        // Prologue: E of chunks 0, 1 and MW of chunk 0.
-        stash_raw(1, rb1);
-        load_raw(4, rb1);
-        ERegs e_prev = stage_E(0);
-        __syncthreads();
-        stash_raw(2, rb2);
-        load_raw(5, rb2);
-        MWRegs m_prev = stage_MW(0, read_MW(0), e_prev);
-        e_prev = stage_E(1);
-        __syncthreads();
-        // One pipeline interval: E(it), MW(it-1), ST(it-2), y of chunk it-3;
-        // chunk it+1 moves from the ring into LDS and chunk it+4 is loaded
-        // into the freed ring slot.  (A macro rather than a lambda: the ring
-        // variables must stay plain SSA values so they live in registers.)
-#define WKV7_FWD_INTERVAL(IT, RING)                                   \
-    {                                                                 \
-        const int it_ = (IT);                                         \
-        const MWIn mi = read_MW(it_ - 1);                             \
-        const STIn si = read_ST(it_ - 2);                             \
-        const uint2 yv = read_y(it_ - 3);                             \
-        const ERegs e_cur = stage_E(it_);                             \
-        stash_raw(it_ + 1, RING);                                     \
-        load_raw(it_ + 4, RING);                                      \
-        const MWRegs m_cur = stage_MW(it_ - 1, mi, e_prev);           \
-        stage_ST(it_ - 2, si, m_prev);                                \
-        if (it_ >= 3) store_y(it_ - 3, yv);                           \
-        __syncthreads();                                              \
-        e_prev = e_cur;                                               \
-        m_prev = m_cur;                                               \
+        // Interval it: producers E(it) and MW(it-1), stash chunk it+1 and load
+        // chunk it+4 into the ring slot it frees; consumers ST(it-2) and the y
+        // store of chunk it-3.  (A macro, not a lambda, so that the ring stays
+        // plain SSA values.)
+#define WKV7_FWD_INTERVAL(IT, RING)                                         \
+    {                                                                       \
+        const int it_ = (IT);                                               \
+        if (producer) {                                                     \
+            MWIn mi;                                                        \
+            if (it_ >= 1) mi = read_MW(it_ - 1);                            \
+            const ERegs e_cur = stage_E(it_);                               \
+            stash_raw(it_ + 1, RING);                                       \
+            load_raw(it_ + 4, RING);                                        \
+            if (it_ >= 1) stage_MW(it_ - 1, mi, e_prev);                    \
+            e_prev = e_cur;                                                 \
+        } else {                                                            \
+            if (it_ >= 2) {                                                 \
+                const STIn si = read_ST(it_ - 2);                           \
+                uint2 yv = make_uint2(0u, 0u);                              \
+                if (it_ >= 3) yv = read_y(it_ - 3);                         \
+                stage_ST(it_ - 2, si);                                      \
+                if (it_ >= 3) store_y(it_ - 3, yv);                         \
+            }                                                               \
+        }                                                                   \
+        __syncthreads();                                                    \
     }
-        // Chunk it+1 sits in ring slot (it+1) % 3: it = 2, 3, 4 -> slots 0, 1, 2
-        // (unrolled so the slot is a compile-time constant).
-        for (int it = 2; it <= nch + 2; it += 3) {
-            WKV7_FWD_INTERVAL(it, rb0);
+        // Ring slot of interval it is (it + 1) % 3: it = 0, 1, 2 -> rb1, rb2, rb0.
+        for (int it = 0; it <= nch + 2; it += 3) {
+            WKV7_FWD_INTERVAL(it, rb1);
             if (it + 1 > nch + 2) break;
-            WKV7_FWD_INTERVAL(it + 1, rb1);
+            WKV7_FWD_INTERVAL(it + 1, rb2);
             if (it + 2 > nch + 2) break;
-            WKV7_FWD_INTERVAL(it + 2, rb2);
+            WKV7_FWD_INTERVAL(it + 2, rb0);
         }
 #undef WKV7_FWD_INTERVAL
     }
 
-    if (sT) {
+    if (sT && !producer) {
         float* dst = sT + ((size_t)bh * kN + col) * kN;
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt)
