@@ -3,8 +3,9 @@
 
 One step is one pass of the whole training hot path over one batch of the
 2.9B-model-shaped workload (B=8, T=4096, H=40, N=64, bf16 inputs, fp32 state):
-the chunked forward writing checkpoints, then the chunked backward producing
-dr, dw, dk, dv, da, db and ds0.  Inputs are seeded synthetic data resident in
+the chunked forward writing its tape (removal read-outs and chunk entry
+states), then the two-pass chunked backward producing dr, dw, dk, dv, da, db
+and ds0.  Inputs are seeded synthetic data resident in
 HBM before the timed region.  Prints ONE JSON line.
 
 Also measured (reported under "secondary", not the headline): the chunked
@@ -89,7 +90,9 @@ def main():
 
     desc = wk.make_desc(B, T, H, N, wk.WKV7_BF16, 16)
     y = torch.empty_like(ins[0])
-    ck = torch.empty(wk.ckpt_bytes(desc) // 4, device=dev, dtype=torch.float32)
+    tape = torch.empty(wk.tape_bytes(desc) // 2, device=dev, dtype=torch.bfloat16)
+    wsb = wk.workspace_bytes(desc, True)
+    work = torch.empty(wsb // 2, device=dev, dtype=torch.bfloat16)
     grads = [torch.empty_like(ins[0]) for _ in range(6)]
     ds0 = torch.empty((B, H, N, N), device=dev, dtype=torch.float32)
     L = wk.lib()
@@ -98,15 +101,15 @@ def main():
     stream = torch.cuda.current_stream()
 
     def fwd():
-        st = L.wkv7_forward(ctypes.byref(desc), *ptr, None, y.data_ptr(), None, ck.data_ptr(),
+        st = L.wkv7_forward(ctypes.byref(desc), *ptr, None, y.data_ptr(), None, tape.data_ptr(),
                             stream.cuda_stream)
         if st != 0:
             raise RuntimeError(f"wkv7_forward status {st}")
 
     def bwd():
-        st = L.wkv7_backward(ctypes.byref(desc), *ptr, None, dy.data_ptr(), None, ck.data_ptr(),
-                             *[g.data_ptr() for g in grads], ds0.data_ptr(), None, 0,
-                             stream.cuda_stream)
+        st = L.wkv7_backward(ctypes.byref(desc), *ptr, None, dy.data_ptr(), None,
+                             tape.data_ptr(), *[g.data_ptr() for g in grads], ds0.data_ptr(),
+                             work.data_ptr(), wsb, stream.cuda_stream)
         if st != 0:
             raise RuntimeError(f"wkv7_backward status {st}")
 
@@ -164,7 +167,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "fwd_bwd_2.9b: B=8 T=4096 H=40 N=64 bf16 inputs, fp32 state, "
-                               "dy~N(0,1), dsT=0, chunked L=16, checkpoints every 64 tokens",
+                               "dy~N(0,1), dsT=0, chunked L=16, bf16 tape",
                    "global_batch": B, "seq_len": T, "heads": H, "head_size": N,
                    "parallelism": "none (1 GPU)"},
         "roofline": roofline,

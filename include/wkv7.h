@@ -25,10 +25,10 @@
  *   - Layouts are row-major, last index fastest:
  *       token tensors r, w, k, v, a, b, y, dy, dr..db   [B][T][H][N]
  *       states s0, sT, dsT, ds0, decode state           [B][H][N][N] (fp32)
- *       checkpoints                                     [B][H][ceil(T/64)][N][N] (fp32)
+ *       tape (forward -> backward), see wkv7_tape_bytes
  *   - `dtype` selects the element type of the token tensors and gradients:
  *     WKV7_F32 (IEEE float) or WKV7_BF16 (bfloat16, outputs rounded to
- *     nearest even).  States and checkpoints are always fp32.
+ *     nearest even).  States are always fp32; the tape is always bf16.
  *   - w is the multiplicative decay itself (not its logarithm).  The
  *     sequential scan and the decode step accept any finite w.  The chunked
  *     form (chunk_len > 0) divides by running products of w inside a chunk
@@ -57,7 +57,7 @@ extern "C" {
 
 #define WKV7_ABI_VERSION 1
 #define WKV7_HEAD_SIZE 64        /* the only supported N */
-#define WKV7_CKPT_INTERVAL 64    /* tokens between stored backward checkpoints */
+#define WKV7_TAPE_CHUNK 16       /* tokens per chunk of the forward tape */
 
 typedef enum {
     WKV7_OK = 0,
@@ -86,15 +86,20 @@ int wkv7_abi_version(void);
 /* Static, never-NULL description of a status code. */
 const char *wkv7_status_string(int status);
 
-/* Bytes of the checkpoint buffer for `desc`: the fp32 state entering every
-   block of WKV7_CKPT_INTERVAL tokens, [B][H][ceil(T/64)][N][N].  0 on an
-   invalid descriptor. */
-size_t wkv7_ckpt_bytes(const wkv7_desc *desc);
+/* Bytes of the tape that wkv7_forward can write for wkv7_backward:
+     Z   [B][T][H][N]              bf16: z_t = S_{t-1} a_t, the removal read-outs;
+     S   [B][H][ceil(T/16)][N][N]  bf16: the state entering every 16-token chunk,
+                                   stored key-major (element [j][i] = S[i][j]).
+   0 on an invalid descriptor. */
+size_t wkv7_tape_bytes(const wkv7_desc *desc);
 
-/* Bytes of device scratch wkv7_backward needs when it is given no
-   checkpoints (it then recomputes them into the workspace).  When the caller
-   passes the checkpoints of a wkv7_forward call, 0 bytes suffice. */
-size_t wkv7_workspace_bytes(const wkv7_desc *desc);
+/* Bytes of device scratch wkv7_backward needs: with_tape != 0 when the caller
+   passes a tape written by wkv7_forward (the backward then keeps the adjoint of
+   every chunk's exit state and one per-token intermediate adjoint there, as much again
+   as the tape), with_tape = 0 when it passes none (then a forward re-run also
+   writes its tape into the workspace: twice the tape).  0 on an invalid
+   descriptor. */
+size_t wkv7_workspace_bytes(const wkv7_desc *desc, int with_tape);
 
 /*
  * Forward over a whole sequence.
@@ -102,12 +107,13 @@ size_t wkv7_workspace_bytes(const wkv7_desc *desc);
  *   s0                [B][H][N][N] fp32 initial state, or NULL for zeros.
  *   y                 [B][T][H][N] output y_t = S_t r_t (dtype).
  *   sT                [B][H][N][N] fp32 final state, or NULL.
- *   ckpt              NULL, or wkv7_ckpt_bytes(desc) bytes: receives the
- *                     state entering tokens 0, 64, 128, ... for wkv7_backward.
+ *   tape              NULL, or wkv7_tape_bytes(desc) bytes: receives the
+ *                     removal read-outs and chunk entry states for
+ *                     wkv7_backward (layout at wkv7_tape_bytes).
  */
 int wkv7_forward(const wkv7_desc *desc, const void *r, const void *w, const void *k,
                  const void *v, const void *a, const void *b, const float *s0, void *y,
-                 float *sT, float *ckpt, void *stream);
+                 float *sT, void *tape, void *stream);
 
 /*
  * Gradients of the scalar  L = sum_t <dy_t, y_t> + <dsT, S_T>  with respect to
@@ -117,15 +123,19 @@ int wkv7_forward(const wkv7_desc *desc, const void *r, const void *w, const void
  *   s0          as given to the forward (NULL = zeros).
  *   dy          [B][T][H][N] upstream gradient of y (dtype).
  *   dsT         [B][H][N][N] fp32 upstream gradient of S_T, or NULL (= 0).
- *   ckpt        checkpoints written by wkv7_forward with the same desc and
- *               inputs, or NULL; then `workspace` must hold at least
- *               wkv7_workspace_bytes(desc) bytes and a forward sweep refills
- *               it first.
+ *   tape        the tape written by wkv7_forward with the same inputs, or
+ *               NULL; then the backward first re-runs the forward (sequential
+ *               scan if desc->chunk_len = 0, chunked otherwise) to write it.
  *   dr..db      [B][T][H][N] outputs (dtype).  ds0: [B][H][N][N] fp32 or NULL.
+ *   workspace   at least wkv7_workspace_bytes(desc, tape != NULL) bytes of
+ *               device scratch (contents on entry are ignored); else
+ *               WKV7_ERR_WORKSPACE.  Required whenever B*T*H > 0.
+ * The gradients are computed chunk by chunk (16 tokens) on bf16 matrix cores
+ * whatever desc->chunk_len is; only dtype = WKV7_BF16 is supported.
  */
 int wkv7_backward(const wkv7_desc *desc, const void *r, const void *w, const void *k,
                   const void *v, const void *a, const void *b, const float *s0,
-                  const void *dy, const float *dsT, const float *ckpt, void *dr, void *dw,
+                  const void *dy, const float *dsT, const void *tape, void *dr, void *dw,
                   void *dk, void *dv, void *da, void *db, float *ds0, void *workspace,
                   size_t workspace_bytes, void *stream);
 

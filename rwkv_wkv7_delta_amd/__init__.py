@@ -28,9 +28,9 @@ WKV7_ERR_LAUNCH = 4
 WKV7_F32 = 0
 WKV7_BF16 = 1
 HEAD_SIZE = 64
-CKPT_INTERVAL = 64
+TAPE_CHUNK = 16
 
-EXPORTED = ("wkv7_abi_version", "wkv7_status_string", "wkv7_ckpt_bytes", "wkv7_workspace_bytes",
+EXPORTED = ("wkv7_abi_version", "wkv7_status_string", "wkv7_tape_bytes", "wkv7_workspace_bytes",
             "wkv7_forward", "wkv7_backward", "wkv7_decode_step")
 
 
@@ -66,9 +66,9 @@ def lib():
         L.wkv7_abi_version.restype = ctypes.c_int
         L.wkv7_status_string.argtypes = [ctypes.c_int]
         L.wkv7_status_string.restype = ctypes.c_char_p
-        L.wkv7_ckpt_bytes.argtypes = [D]
-        L.wkv7_ckpt_bytes.restype = Z
-        L.wkv7_workspace_bytes.argtypes = [D]
+        L.wkv7_tape_bytes.argtypes = [D]
+        L.wkv7_tape_bytes.restype = Z
+        L.wkv7_workspace_bytes.argtypes = [D, ctypes.c_int]
         L.wkv7_workspace_bytes.restype = Z
         L.wkv7_forward.argtypes = [D] + [P] * 6 + [P, P, P, P, P]
         L.wkv7_forward.restype = ctypes.c_int
@@ -126,19 +126,30 @@ def make_desc(B: int, T: int, H: int, N: int, dtype: int, chunk_len: int) -> Des
     return Desc(B, T, H, N, dtype, chunk_len)
 
 
-def ckpt_bytes(desc: Desc) -> int:
-    return int(lib().wkv7_ckpt_bytes(ctypes.byref(desc)))
+def tape_bytes(desc: Desc) -> int:
+    return int(lib().wkv7_tape_bytes(ctypes.byref(desc)))
 
 
-def workspace_bytes(desc: Desc) -> int:
-    return int(lib().wkv7_workspace_bytes(ctypes.byref(desc)))
+def workspace_bytes(desc: Desc, with_tape: bool = True) -> int:
+    return int(lib().wkv7_workspace_bytes(ctypes.byref(desc), 1 if with_tape else 0))
+
+
+def split_tape(tape, B: int, T: int, H: int, N: int = HEAD_SIZE):
+    """Views of a forward tape: Z [B, T, H, N] (removal read-outs z_t = S_{t-1} a_t)
+    and the chunk entry states [B, H, ceil(T/16), N (key j), N (value i)], both bf16."""
+    nch = (T + TAPE_CHUNK - 1) // TAPE_CHUNK
+    ntok = B * T * H * N
+    z = tape[:ntok].view(B, T, H, N)
+    st = tape[ntok:ntok + B * H * nch * N * N].view(B, H, nch, N, N)
+    return z, st
 
 
 def forward(r, w, k, v, a, b, s0=None, *, chunk_len: int = 0, want_state: bool = True,
-            want_ckpt: bool = False, out=None):
+            want_tape: bool = False, out=None):
     """Run the recurrence over [B, T, H, N] inputs.
 
-    Returns ``(y, sT, ckpt)``; ``sT`` / ``ckpt`` are None unless requested.
+    Returns ``(y, sT, tape)``; ``sT`` / ``tape`` are None unless requested (the
+    tape is a flat bf16 tensor for ``backward``; ``split_tape`` gives its parts).
     ``chunk_len`` 0 = sequential scan, 16 = chunked bf16-MFMA form.
     """
     torch = _torch()
@@ -149,9 +160,9 @@ def forward(r, w, k, v, a, b, s0=None, *, chunk_len: int = 0, want_state: bool =
     y = out if out is not None else torch.empty_like(r)
     sT = torch.empty((B, H, N, N), device=r.device, dtype=torch.float32) if want_state else None
     ck = None
-    if want_ckpt:
-        nbytes = ckpt_bytes(desc)
-        ck = torch.empty(max(nbytes // 4, 1), device=r.device, dtype=torch.float32)
+    if want_tape:
+        nbytes = tape_bytes(desc)
+        ck = torch.empty(max(nbytes // 2, 8), device=r.device, dtype=torch.bfloat16)
     st = lib().wkv7_forward(ctypes.byref(desc), _ptr(r), _ptr(w), _ptr(k), _ptr(v), _ptr(a),
                             _ptr(b), _ptr(s0), _ptr(y), _ptr(sT), _ptr(ck), _stream())
     if st != WKV7_OK:
@@ -159,9 +170,13 @@ def forward(r, w, k, v, a, b, s0=None, *, chunk_len: int = 0, want_state: bool =
     return y, sT, ck
 
 
-def backward(r, w, k, v, a, b, dy, s0=None, dsT=None, ckpt=None, *, chunk_len: int = 16,
-             want_ds0: bool = True):
-    """Gradients of ``<dy, y> + <dsT, S_T>``: returns (dr, dw, dk, dv, da, db, ds0)."""
+def backward(r, w, k, v, a, b, dy, s0=None, dsT=None, tape=None, *, chunk_len: int = 16,
+             want_ds0: bool = True, workspace=None):
+    """Gradients of ``<dy, y> + <dsT, S_T>``: returns (dr, dw, dk, dv, da, db, ds0).
+
+    ``tape`` is the one ``forward(..., want_tape=True)`` returned for the same
+    inputs, or None (the forward is then re-run inside the call).
+    """
     torch = _torch()
     B, T, H, N = r.shape
     _check_tokens((r, w, k, v, a, b, dy), r.shape, r.dtype)
@@ -170,13 +185,14 @@ def backward(r, w, k, v, a, b, dy, s0=None, dsT=None, ckpt=None, *, chunk_len: i
     desc = make_desc(B, T, H, N, _dtype_code(r), chunk_len)
     grads = [torch.empty_like(r) for _ in range(6)]
     ds0 = torch.empty((B, H, N, N), device=r.device, dtype=torch.float32) if want_ds0 else None
-    ws = None
-    wsb = 0
-    if ckpt is None:
-        wsb = workspace_bytes(desc)
-        ws = torch.empty(max(wsb // 4, 1), device=r.device, dtype=torch.float32)
+    wsb = workspace_bytes(desc, tape is not None)
+    ws = workspace
+    if ws is None:
+        ws = torch.empty(max(wsb // 4, 4), device=r.device, dtype=torch.float32)
+    else:
+        wsb = ws.numel() * ws.element_size()
     st = lib().wkv7_backward(ctypes.byref(desc), _ptr(r), _ptr(w), _ptr(k), _ptr(v), _ptr(a),
-                             _ptr(b), _ptr(s0), _ptr(dy), _ptr(dsT), _ptr(ckpt),
+                             _ptr(b), _ptr(s0), _ptr(dy), _ptr(dsT), _ptr(tape),
                              *[_ptr(x) for x in grads], _ptr(ds0), _ptr(ws), wsb, _stream())
     if st != WKV7_OK:
         raise WKV7Error(st, "wkv7_backward")

@@ -29,22 +29,27 @@ int check_desc(const wkv7_desc* d) {
     return WKV7_OK;
 }
 
-size_t ckpt_bytes_unchecked(const wkv7_desc* d) {
-    const size_t nck = ((size_t)d->T + WKV7_CKPT_INTERVAL - 1) / WKV7_CKPT_INTERVAL;
-    return (size_t)d->B * d->H * nck * d->N * d->N * sizeof(float);
+// Tape: bf16 removal read-outs [B][T][H][N], then the bf16 state entering every
+// 16-token chunk [B][H][ceil(T/16)][N][N].  The backward's own scratch (dX and the
+// adjoint entering every chunk) has the same shape.
+size_t tape_bytes_unchecked(const wkv7_desc* d) {
+    const size_t nch = ((size_t)d->T + WKV7_TAPE_CHUNK - 1) / WKV7_TAPE_CHUNK;
+    const size_t tok = (size_t)d->B * d->T * d->H * d->N;
+    const size_t st = (size_t)d->B * d->H * nch * d->N * d->N;
+    return (tok + st) * 2;
 }
 
 int from_hip(hipError_t e) { return e == hipSuccess ? WKV7_OK : WKV7_ERR_LAUNCH; }
 
 int run_forward(const wkv7_desc* d, const void* r, const void* w, const void* k, const void* v,
                 const void* a, const void* b, const float* s0, void* y, float* sT,
-                float* ckpt, hipStream_t stream) {
+                void* tape, hipStream_t stream) {
     if ((int64_t)d->B * d->H == 0) return WKV7_OK;
     if (d->T == 0) {
         if (sT) return from_hip(wkv7::launch_state_copy(d->B * d->H, s0, sT, stream));
         return WKV7_OK;
     }
-    wkv7::FwdArgs p{d->B, d->T, d->H, d->dtype == WKV7_BF16, r, w, k, v, a, b, s0, y, sT, ckpt};
+    wkv7::FwdArgs p{d->B, d->T, d->H, d->dtype == WKV7_BF16, r, w, k, v, a, b, s0, y, sT, tape};
     if (d->chunk_len == 0) return from_hip(wkv7::launch_seq_fwd(p, stream));
     return from_hip(wkv7::launch_chunk_fwd(p, d->chunk_len, stream));
 }
@@ -66,46 +71,48 @@ const char* wkv7_status_string(int status) {
     }
 }
 
-size_t wkv7_ckpt_bytes(const wkv7_desc* desc) {
+size_t wkv7_tape_bytes(const wkv7_desc* desc) {
     if (check_desc(desc) != WKV7_OK) return 0;
-    return ckpt_bytes_unchecked(desc);
+    return tape_bytes_unchecked(desc);
 }
 
-size_t wkv7_workspace_bytes(const wkv7_desc* desc) {
+size_t wkv7_workspace_bytes(const wkv7_desc* desc, int with_tape) {
     if (check_desc(desc) != WKV7_OK) return 0;
-    return ckpt_bytes_unchecked(desc);
+    return tape_bytes_unchecked(desc) * (with_tape ? 1 : 2);
 }
 
 int wkv7_forward(const wkv7_desc* desc, const void* r, const void* w, const void* k,
                  const void* v, const void* a, const void* b, const float* s0, void* y,
-                 float* sT, float* ckpt, void* stream) {
+                 float* sT, void* tape, void* stream) {
     const int st = check_desc(desc);
     if (st != WKV7_OK) return st;
     const bool has_tokens = (int64_t)desc->B * desc->T * desc->H > 0;
     if (has_tokens && !(req(r) && req(w) && req(k) && req(v) && req(a) && req(b) && req(y)))
         return WKV7_ERR_INVALID_ARG;
-    if (!(opt(s0) && opt(sT) && opt(ckpt))) return WKV7_ERR_INVALID_ARG;
-    return run_forward(desc, r, w, k, v, a, b, s0, y, sT, ckpt, static_cast<hipStream_t>(stream));
+    if (!(opt(s0) && opt(sT) && opt(tape))) return WKV7_ERR_INVALID_ARG;
+    return run_forward(desc, r, w, k, v, a, b, s0, y, sT, tape, static_cast<hipStream_t>(stream));
 }
 
 int wkv7_backward(const wkv7_desc* desc, const void* r, const void* w, const void* k,
                   const void* v, const void* a, const void* b, const float* s0, const void* dy,
-                  const float* dsT, const float* ckpt, void* dr, void* dw, void* dk, void* dv,
+                  const float* dsT, const void* tape, void* dr, void* dw, void* dk, void* dv,
                   void* da, void* db, float* ds0, void* workspace, size_t workspace_bytes,
                   void* stream) {
     int st = check_desc(desc);
     if (st != WKV7_OK) return st;
-    // The backward runs the chunked adjoint on bf16 matrix cores.
+    // The backward runs the chunked adjoint on bf16 matrix cores, one workgroup
+    // per chunk and head in its second pass.
     if (desc->dtype != WKV7_BF16) return WKV7_ERR_UNSUPPORTED;
+    if ((int64_t)desc->B * desc->H * ((desc->T + WKV7_TAPE_CHUNK - 1) / WKV7_TAPE_CHUNK) > INT32_MAX)
+        return WKV7_ERR_UNSUPPORTED;
     const bool has_tokens = (int64_t)desc->B * desc->T * desc->H > 0;
     if (has_tokens && !(req(r) && req(w) && req(k) && req(v) && req(a) && req(b) && req(dy) &&
                         req(dr) && req(dw) && req(dk) && req(dv) && req(da) && req(db)))
         return WKV7_ERR_INVALID_ARG;
-    if (!(opt(s0) && opt(dsT) && opt(ckpt) && opt(ds0) && opt(workspace)))
+    if (!(opt(s0) && opt(dsT) && opt(tape) && opt(ds0) && opt(workspace)))
         return WKV7_ERR_INVALID_ARG;
-    const size_t need = ckpt_bytes_unchecked(desc);
-    if (has_tokens && !ckpt && (workspace == nullptr || workspace_bytes < need))
-        return WKV7_ERR_WORKSPACE;
+    const size_t need = tape_bytes_unchecked(desc) * (tape ? 1 : 2);
+    if (has_tokens && (workspace == nullptr || workspace_bytes < need)) return WKV7_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if ((int64_t)desc->B * desc->H == 0) return WKV7_OK;
     if (desc->T == 0) {
@@ -113,14 +120,16 @@ int wkv7_backward(const wkv7_desc* desc, const void* r, const void* w, const voi
         if (ds0) return from_hip(wkv7::launch_state_copy(desc->B * desc->H, dsT, ds0, s));
         return WKV7_OK;
     }
-    if (!ckpt) {
-        float* ws = static_cast<float*>(workspace);
-        st = run_forward(desc, r, w, k, v, a, b, s0, nullptr, nullptr, ws, s);
+    char* ws = static_cast<char*>(workspace);
+    if (!tape) {
+        // Re-run the forward (without y) into the second half of the workspace.
+        void* own = ws + tape_bytes_unchecked(desc);
+        st = run_forward(desc, r, w, k, v, a, b, s0, nullptr, nullptr, own, s);
         if (st != WKV7_OK) return st;
-        ckpt = ws;
+        tape = own;
     }
-    wkv7::BwdArgs p{desc->B, desc->T, desc->H, true, r, w, k, v, a, b, s0, dy, dsT, ckpt,
-                    dr, dw, dk, dv, da, db, ds0};
+    wkv7::BwdArgs p{desc->B, desc->T, desc->H, true, r, w, k, v, a, b, s0, dy, dsT, tape,
+                    dr, dw, dk, dv, da, db, ds0, ws};
     return from_hip(wkv7::launch_bwd(p, 16, s));
 }
 

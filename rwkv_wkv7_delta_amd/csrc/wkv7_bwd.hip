@@ -1,34 +1,33 @@
-// wkv7_bwd.hip -- chunked WKV7 backward (adjoint) on bf16 MFMA, gfx950.
+// wkv7_bwd.hip -- chunked WKV7 backward on bf16 MFMA, gfx950.
 //
 // Gradient of L = sum_t <dy_t, y_t> + <dsT, S_T> through the chunk form of
-// the recurrence (the forward's rearrangement, see wkv7_chunk_fwd.hip),
-// visiting chunks of L = 16 tokens last to first and carrying the fp32
-// adjoint dS of each chunk's exit state.  Per chunk, with entry state S0,
-// Z the removal read-outs and dY the read-out adjoint:
+// the recurrence (wkv7_chunk_fwd.hip).  Per chunk of L = 16 tokens with entry
+// state S0, removal read-outs Z, read-out adjoint dY and the adjoint dS of
+// the chunk's exit state:
 //
 //   dZ  = Arb^T dY + Bb dS^T            dX = Tm^T dZ
 //   dV  = Aak^T dX + Ark^T dY + Kb dS^T
+//   dS0 = dS diag(G_L) + dY^T Rt + dX^T At       (adjoint carried to the previous chunk)
 //   dAab = tril_-1(dX Z^T)  dAak = tril_-1(dX V^T)
 //   dArb = tril_0(dY Z^T)   dArk = tril_0(dY V^T)
 //   dAt = dX S0 + dAab Bh + dAak Kh     dRt = dY S0 + dArb Bh + dArk Kh
 //   dBh = dAab^T At + dArb^T Rt         dKh = dAak^T At + dArk^T Rt
 //   dBb = Z dS                          dKb = V dS
-//   dS0 = dS diag(G_L) + dY^T Rt + dX^T At     (carried to the previous chunk)
-// followed by the chain rule through the decay products: for each token,
-// da = dAt G_{t-1}, dr = dRt G_t, db = dBh / G_t + dBb G_L / G_t,
-// dk = dKh / G_t + dKb G_L / G_t, and d log G_t collects every factor that
-// G_t enters; d log w_u = sum_{t >= u} d log G_t, dw = d log w / w.
+// followed by the chain rule through the decay products: per token
+// da = dAt G_{t-1}, dr = dRt G_t, db = (dBh + dBb G_L) / G_t,
+// dk = (dKh + dKb G_L) / G_t, and d log w_u collects every factor that the
+// running products G_t (t >= u) enter.
 //
-// Entry states come from the forward's checkpoints (one every 64 tokens):
-// for each 64-token block the kernel first re-runs the forward state chain
-// over the block's chunks, keeping every chunk's entry state and removal
-// read-outs Z in LDS (bf16), then walks the block's chunks backwards.
-//
-// Mapping: one workgroup of 4 waves per (b, h).  Wave w owns value rows
-// 16w..16w+15 for the state-shaped work (dS^T is held in four 16x16 fp32
-// accumulator tiles, exactly like the forward's state) and key columns
-// 16w..16w+15 for the per-key gradients; contractions over value rows read
-// the chunk's shared bf16 copies of S0, dS, Z and dX from LDS.
+// Only the adjoint dS is sequential.  The backward therefore runs in two
+// passes:
+//   pass 1 (one workgroup per head, chunks last to first): the adjoint chain,
+//     with the forward's producer/consumer structure -- producers rebuild the
+//     chunk's decay products, scaled vectors, 16x16 tiles and inverse;
+//     consumers own 16 value rows each of dS^T in accumulator tiles and emit
+//     dv, dX and the chunk's incoming dS;
+//   pass 2 (one independent wave per chunk and key block, no barriers): every
+//     per-key gradient, from pass 1's dX and dS and the forward's tape (entry
+//     states S0 and read-outs Z).
 
 #include "wkv7_device.h"
 #include "wkv7_internal.h"
@@ -39,35 +38,8 @@ namespace wkv7 {
 namespace {
 
 constexpr int kL = 16;
-constexpr int kThreads = 256;
-constexpr int kChunksPerBlock = kCkptInterval / kL;   // 4
-// LDS row strides (bf16 elements): 144-byte and 40-byte rows keep the MFMA
-// operand reads (16 lanes on 16 different rows) off a single bank set.
-constexpr int kRow = kN + 8;
+constexpr int kRow = kN + 8;    // padded LDS rows (see wkv7_chunk_fwd.hip)
 constexpr int kRowT = kL + 4;
-
-enum { RAW_R = 0, RAW_W = 1, RAW_K = 2, RAW_A = 3, RAW_B = 4, RAW_V = 5, RAW_DY = 6 };
-enum { GS_DR = 0, GS_DW = 1, GS_DK = 2, GS_DV = 3, GS_DA = 4, GS_DB = 5 };
-
-struct __align__(16) BwdSmem {
-    bf16_t raw[7][kL][kRow];                   // r, w, k, a, b, v, dy (bf16 bits)
-    float G[kL + 1][kN];                     // running decay products, G[0] = 1
-    float gtot[4][kN];
-    bf16_t At[kL][kRow], Rt[kL][kRow], Bh[kL][kRow], Kh[kL][kRow], Bb[kL][kRow], Kb[kL][kRow];
-    bf16_t AtT[kN][kRowT], RtT[kN][kRowT], BhT[kN][kRowT], KhT[kN][kRowT], BbT[kN][kRowT],
-        KbT[kN][kRowT];
-    float Amat[4][kL][kL];                   // Aab, Aak, Arb, Ark
-    float Tm[kL][kL];                        // (I - Aab)^-1
-    bf16_t Wm[kL][kRow];                       // Tm At
-    bf16_t Sblk[kChunksPerBlock][kN][kRow];    // entry states of the block's chunks, [j][i]
-    bf16_t Zblk[kChunksPerBlock][kL][kRow];    // removal read-outs Z of the block's chunks, [t][i]
-    bf16_t dXs[kL][kRow];                      // [t][i]
-    bf16_t dSs[kN][kRow];                      // adjoint of the chunk's exit state, [j][i]
-    float dAm[4][kL][kL];                    // dAab, dAak, dArb, dArk
-    float colsum[4][kN];                     // per-wave partial sum_i dS[i][j] S0[i][j]
-    float red[4][3][4][16];                  // per-wave scratch for token sums
-    bf16_t gst[6][kL][kRow];                   // gradient staging for coalesced stores
-};
 
 __device__ __forceinline__ float bf2f(bf16_t x) { return __uint_as_float((uint32_t)x << 16); }
 __device__ __forceinline__ bf16x4 ld4(const bf16_t* p) {
@@ -76,446 +48,561 @@ __device__ __forceinline__ bf16x4 ld4(const bf16_t* p) {
 __device__ __forceinline__ bf16x8 ld8(const bf16_t* p) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
 }
-// 32-deep operand built from two 4-wide pieces at p and p + 16 (see wkv7_mfma.h).
 __device__ __forceinline__ bf16x8 ld4x2(const bf16_t* p) { return cat8(ld4(p), ld4(p + 16)); }
-__device__ __forceinline__ bf16x4 f4(const float* p0, int stride) {
-    return cvt4(p0[0], p0[stride], p0[2 * stride], p0[3 * stride]);
-}
 __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-struct Ctx {
-    int T, H, bb, hh, tid, wv, lane, l16, g, irow;
-    const bf16_t *r, *w, *k, *a, *b, *v, *dy;
-};
-
-// Raw loads of one chunk (nvec = 6 without dy, 7 with): 128 x 16 B per vector.
-struct Prefetch {
-    uint4 v[4];
-};
-
-__device__ __forceinline__ void load_raw(const Ctx& c, int t0, int nvec, Prefetch& pf) {
+// (I - A)^-1 in accumulator layout (lane (g, l16) register q holds
+// T[4g+q][l16]) for strictly lower triangular A, as the doubling product
+// with left factors: P <- P + A^(2k) P, each A^(2k) fed through the registers
+// of its transpose.
+__device__ __forceinline__ f32x4 unit_lower_inverse_C(f32x4 A, f32x4 AT, int g, int l16) {
+    const f32x4 z = zero4();
+    const f32x4 A2 = mfma16(cvt4(AT), cvt4(A), z);
+    const f32x4 A2T = mfma16(cvt4(A), cvt4(AT), z);
+    const f32x4 A4 = mfma16(cvt4(A2T), cvt4(A2), z);
+    const f32x4 A4T = mfma16(cvt4(A2), cvt4(A2T), z);
+    const f32x4 A8T = mfma16(cvt4(A4), cvt4(A4T), z);
+    f32x4 P = A;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const int item = c.tid + p * kThreads;
-        const int q = item >> 7, t = (item >> 3) & 15, c8 = item & 7;
-        if (q >= nvec) continue;
-        // vector q = 2p + (tid >= 128): r/w, k/a, b/v, dy
-        const bool hi = c.tid >= 128;
-        const bf16_t* sp = p == 0 ? (hi ? c.w : c.r) : p == 1 ? (hi ? c.a : c.k)
-                         : p == 2 ? (hi ? c.v : c.b) : c.dy;
-        if (t0 + t < c.T) {
-            pf.v[p] = *reinterpret_cast<const uint4*>(sp + tok_off(c.bb, t0 + t, c.hh, c.T, c.H) + c8 * 8);
-        } else {
-            const uint32_t pad = (q == RAW_W) ? 0x3F803F80u : 0u;   // padding token: w = 1
-            pf.v[p] = make_uint4(pad, pad, pad, pad);
+    for (int q = 0; q < 4; ++q) P[q] += (4 * g + q == l16) ? 1.f : 0.f;
+    P = mfma16(cvt4(A2T), cvt4(P), P);   // P += A^2 P
+    P = mfma16(cvt4(A4T), cvt4(P), P);
+    P = mfma16(cvt4(A8T), cvt4(P), P);
+    return P;
+}
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+struct Raw {
+    u32x4 x[3];
+};
+
+// =============================================================================
+// Pass 1: the adjoint chain.
+// =============================================================================
+
+constexpr int kP1Threads = 512;
+enum { P1_R = 0, P1_W = 1, P1_K = 2, P1_A = 3, P1_B = 4, P1_DY = 5 };
+enum { TILE_T = 0, TILE_RB = 1, TILE_AK = 2, TILE_RK = 3 };
+
+struct P1Slot {
+    bf16_t At[kL][kRow], Rt[kL][kRow], Bh[kL][kRow], Kh[kL][kRow];  // E -> MW, [t][j]
+    bf16_t Bb[kL][kRow], Kb[kL][kRow];                              // E -> chain, [t][j]
+    bf16_t AtT[kN][kRowT], RtT[kN][kRowT];                          // E -> chain, [j][t]
+    bf16_t dYt[kN][kRowT];                                          // E -> chain, dy as [i][t]
+    float gL[kN];
+    uint2 tiles[4][64];   // MW -> chain: A-operand register images of Tm^T, Arb^T, Aak^T, Ark^T
+};
+
+struct __align__(16) P1Smem {
+    bf16_t raw[2][6][kL][kRow];   // r, w, k, a, b, dy of two chunks
+    P1Slot sl[3];
+    bf16_t dXs[2][kL][kRow];      // [t][i]
+    bf16_t dVs[2][kL][kRow];      // [t][i]
+    bf16_t dSs[2][kN][kRow];      // the chunk's incoming adjoint as [j][i]
+    float red[4][4][16];
+};
+
+__global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
+    int T, int H, const bf16_t* __restrict__ r, const bf16_t* __restrict__ w,
+    const bf16_t* __restrict__ k, const bf16_t* __restrict__ a, const bf16_t* __restrict__ b,
+    const bf16_t* __restrict__ dy, const float* __restrict__ dsT, bf16_t* __restrict__ dv,
+    float* __restrict__ ds0, bf16_t* __restrict__ work) {
+    __shared__ P1Smem sm;
+    const int bh = blockIdx.x;
+    const int bb = bh / H, hh = bh % H;
+    const int B = gridDim.x / H;
+    const int tid = threadIdx.x;
+    const bool producer = tid < 256;
+    const int rtid = tid & 255;
+    const int lane = tid & 63, wp = rtid >> 6;
+    const int l16 = lane & 15, g = lane >> 4;
+    const int col = 16 * wp + l16;
+    const int nch = (T + kL - 1) / kL;
+    bf16_t* const wdX = work;                                   // [B][T][H][N]
+    bf16_t* const wdS = work + (size_t)B * T * H * kN;          // [B][H][nch][N][N]
+    // Interval it handles chunks from the last one down; negative chunk
+    // indices are all-padding, for which every stage is the identity.
+    auto chunk_of = [&](int it) __attribute__((always_inline)) { return nch - 1 - it; };
+    auto slot_of = [&](int c) __attribute__((always_inline)) { return (c + 3) % 3; };
+
+    // ---- consumer adjoint: dS^T tiles, lane holds dS[col][16 jt + 4 g + q] -------
+    f32x4 dSt[4];
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) dSt[jt] = zero4();
+    if (!producer && dsT) {
+        const float* base = dsT + ((size_t)bh * kN + col) * kN;
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+            const float4 x = *reinterpret_cast<const float4*>(base + 16 * jt + 4 * g);
+            dSt[jt][0] = x.x; dSt[jt][1] = x.y; dSt[jt][2] = x.z; dSt[jt][3] = x.w;
         }
     }
-}
 
-__device__ __forceinline__ void stash_raw(const Ctx& c, BwdSmem& sm, int nvec, const Prefetch& pf) {
+    // ---- producer raw loads (as in the forward; vector 5 is dy) -------------------
+    const bool hi = rtid >= 128;
+    const bf16_t* const sp_p[3] = {hi ? w : r, hi ? a : k, hi ? dy : b};
+    const int ld_t = (rtid >> 3) & 15, ld_c8 = rtid & 7;
+    auto load_raw = [&](int c, Raw& o) __attribute__((always_inline)) {
+        const int t = max(0, min(c * kL + ld_t, T - 1));
+        const size_t off = tok_off(bb, t, hh, T, H) + ld_c8 * 8;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const int item = c.tid + p * kThreads;
-        const int q = item >> 7, t = (item >> 3) & 15, c8 = item & 7;
-        if (q < nvec) *reinterpret_cast<uint4*>(&sm.raw[q][t][c8 * 8]) = pf.v[p];
+        for (int p = 0; p < 3; ++p) o.x[p] = *reinterpret_cast<const u32x4*>(sp_p[p] + off);
+    };
+    auto stash_raw = [&](int c, const Raw& o) __attribute__((always_inline)) {
+        const int t = c * kL + ld_t;
+        const bool ok = c >= 0 && t < T;
+#pragma unroll
+        for (int p = 0; p < 3; ++p) {
+            const unsigned pad = (p == 0 && hi) ? 0x3F803F80u : 0u;   // padding: w = 1
+            const u32x4 padv = {pad, pad, pad, pad};
+            *reinterpret_cast<u32x4*>(&sm.raw[c & 1][2 * p + (hi ? 1 : 0)][ld_t][ld_c8 * 8]) =
+                ok ? o.x[p] : padv;
+        }
+    };
+
+    // ---- E (producer): decay products, scaled vectors, dy^T -----------------------
+    auto stage_E = [&](int c) __attribute__((always_inline)) {
+        P1Slot& s = sm.sl[slot_of(c)];
+        const bf16_t(*Rr)[kL][kRow] = sm.raw[c & 1];
+        float R[6][4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int vi = 0; vi < 6; ++vi) R[vi][q] = bf2f(Rr[vi][4 * g + q][col]);
+        float gp[4];
+        float run = 1.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            run *= R[P1_W][q];
+            gp[q] = run;
+        }
+        sm.red[wp][g][l16] = run;
+        wave_sync();
+        const float g0 = sm.red[wp][0][l16], g1 = sm.red[wp][1][l16];
+        const float g2 = sm.red[wp][2][l16], g3 = sm.red[wp][3][l16];
+        const float before = g == 0 ? 1.f : g == 1 ? g0 : g == 2 ? g0 * g1 : (g0 * g1) * g2;
+        const float GL = ((g0 * g1) * g2) * g3;
+        float at[4], rt[4], bb4[4], kb4[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int t = 4 * g + q;
+            const float Gt = before * gp[q];
+            const float Gp = q == 0 ? before : before * gp[q - 1];
+            const float inv = __builtin_amdgcn_rcpf(Gt);
+            at[q] = R[P1_A][q] * Gp;
+            rt[q] = R[P1_R][q] * Gt;
+            const float bh_ = R[P1_B][q] * inv;
+            const float kh_ = R[P1_K][q] * inv;
+            bb4[q] = bh_ * GL;
+            kb4[q] = kh_ * GL;
+            s.At[t][col] = f2bf(at[q]);
+            s.Rt[t][col] = f2bf(rt[q]);
+            s.Bh[t][col] = f2bf(bh_);
+            s.Kh[t][col] = f2bf(kh_);
+            s.Bb[t][col] = f2bf(bb4[q]);
+            s.Kb[t][col] = f2bf(kb4[q]);
+        }
+        *reinterpret_cast<bf16x4*>(&s.AtT[col][4 * g]) = cvt4(at[0], at[1], at[2], at[3]);
+        *reinterpret_cast<bf16x4*>(&s.RtT[col][4 * g]) = cvt4(rt[0], rt[1], rt[2], rt[3]);
+        *reinterpret_cast<bf16x4*>(&s.dYt[col][4 * g]) =
+            cvt4(R[P1_DY][0], R[P1_DY][1], R[P1_DY][2], R[P1_DY][3]);
+        if (g == 0) s.gL[col] = GL;
+    };
+
+    // ---- MW (producer): 16x16 tiles and the inverse, as A-operand images ----------
+    struct MWIn {
+        bf16x8 av[2], rv[2], bv[2], kv[2];
+    };
+    auto read_MW = [&](int c) __attribute__((always_inline)) -> MWIn {
+        const P1Slot& s = sm.sl[slot_of(c)];
+        MWIn in;
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+            in.av[k2] = ld8(&s.At[l16][32 * k2 + 8 * g]);
+            in.rv[k2] = ld8(&s.Rt[l16][32 * k2 + 8 * g]);
+            in.bv[k2] = ld8(&s.Bh[l16][32 * k2 + 8 * g]);
+            in.kv[k2] = ld8(&s.Kh[l16][32 * k2 + 8 * g]);
+        }
+        return in;
+    };
+    auto stage_MW = [&](int c, const MWIn& in) __attribute__((always_inline)) {
+        P1Slot& s = sm.sl[slot_of(c)];
+        f32x4 ab = zero4(), abT = zero4(), rb = zero4(), ak = zero4(), rk = zero4();
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+            ab = mfma32(in.av[k2], in.bv[k2], ab);    // [t][s] = At_t . Bh_s
+            abT = mfma32(in.bv[k2], in.av[k2], abT);  // [s][t]
+            rb = mfma32(in.rv[k2], in.bv[k2], rb);    // [t][s] = Rt_t . Bh_s
+            ak = mfma32(in.av[k2], in.kv[k2], ak);    // [t][s] = At_t . Kh_s
+            rk = mfma32(in.rv[k2], in.kv[k2], rk);    // [t][s] = Rt_t . Kh_s
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int m = 4 * g + q, n = l16;
+            ab[q] = (n < m) ? ab[q] : 0.f;
+            abT[q] = (m < n) ? abT[q] : 0.f;
+            rb[q] = (n <= m) ? rb[q] : 0.f;
+            ak[q] = (n < m) ? ak[q] : 0.f;
+            rk[q] = (n <= m) ? rk[q] : 0.f;
+        }
+        // Accumulator registers of X fed as an A operand stand for X^T.
+        const f32x4 Tc = unit_lower_inverse_C(ab, abT, g, l16);
+        if (wp == 0) {
+            s.tiles[TILE_T][lane] = __builtin_bit_cast(uint2, cvt4(Tc));
+            s.tiles[TILE_RB][lane] = __builtin_bit_cast(uint2, cvt4(rb));
+            s.tiles[TILE_AK][lane] = __builtin_bit_cast(uint2, cvt4(ak));
+            s.tiles[TILE_RK][lane] = __builtin_bit_cast(uint2, cvt4(rk));
+        }
+    };
+
+    // ---- chain (consumer): value rows `col` of the adjoint ------------------------
+    struct CIn {
+        bf16x4 TmT, ArbT, AakT, ArkT, dY;
+        bf16x8 bb[2], kb[2];
+        bf16x4 rtT[4], atT[4];
+        float4 gl[4];
+    };
+    auto read_C = [&](int c) __attribute__((always_inline)) -> CIn {
+        const P1Slot& s = sm.sl[slot_of(c)];
+        CIn in;
+        in.TmT = __builtin_bit_cast(bf16x4, s.tiles[TILE_T][lane]);
+        in.ArbT = __builtin_bit_cast(bf16x4, s.tiles[TILE_RB][lane]);
+        in.AakT = __builtin_bit_cast(bf16x4, s.tiles[TILE_AK][lane]);
+        in.ArkT = __builtin_bit_cast(bf16x4, s.tiles[TILE_RK][lane]);
+        in.dY = ld4(&s.dYt[col][4 * g]);
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+            in.bb[k2] = ld4x2(&s.Bb[l16][32 * k2 + 4 * g]);
+            in.kb[k2] = ld4x2(&s.Kb[l16][32 * k2 + 4 * g]);
+        }
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+            in.rtT[jt] = ld4(&s.RtT[16 * jt + l16][4 * g]);
+            in.atT[jt] = ld4(&s.AtT[16 * jt + l16][4 * g]);
+            in.gl[jt] = *reinterpret_cast<const float4*>(&s.gL[16 * jt + 4 * g]);
+        }
+        return in;
+    };
+    auto stage_C = [&](int c, const CIn& in) __attribute__((always_inline)) {
+        bf16x4 dSb[4];
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) dSb[jt] = cvt4(dSt[jt]);
+        // Partial sums of the two MFMA shapes meet on the vector ALU (add4).
+        f32x4 dZ = zero4(), dVk = zero4();
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+            const bf16x8 ds8 = cat8(dSb[2 * k2], dSb[2 * k2 + 1]);
+            dZ = mfma32(in.bb[k2], ds8, dZ);
+            dVk = mfma32(in.kb[k2], ds8, dVk);
+        }
+        dZ = add4(dZ, mfma16(in.ArbT, in.dY, zero4()));
+        const bf16x4 dXb = cvt4(mfma16(in.TmT, cvt4(dZ), zero4()));
+        f32x4 dV = mfma16(in.AakT, dXb, zero4());
+        dV = mfma16(in.ArkT, in.dY, dV);
+        const bf16x4 dVb = cvt4(add4(dV, dVk));
+        const int sb = c & 1;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            sm.dXs[sb][4 * g + q][col] = bits(dXb[q]);
+            sm.dVs[sb][4 * g + q][col] = bits(dVb[q]);
+        }
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) sm.dSs[sb][16 * jt + 4 * g + q][col] = bits(dSb[jt][q]);
+        // dS0^T = G_L dS^T + Rt^T dY + At^T dX
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+            f32x4 acc;
+            acc[0] = in.gl[jt].x * dSt[jt][0];
+            acc[1] = in.gl[jt].y * dSt[jt][1];
+            acc[2] = in.gl[jt].z * dSt[jt][2];
+            acc[3] = in.gl[jt].w * dSt[jt][3];
+            acc = mfma16(in.rtT[jt], in.dY, acc);
+            dSt[jt] = mfma16(in.atT[jt], dXb, acc);
+        }
+    };
+
+    // ---- outputs of chunk c (consumers): dv and dX rows, incoming dS ---------------
+    const int yt = rtid >> 4, yc4 = rtid & 15;
+    auto store_out = [&](int c) __attribute__((always_inline)) {
+        if (c < 0) return;
+        const int sb = c & 1;
+        const int tt = c * kL + yt;
+        if (tt < T) {
+            const size_t o = tok_off(bb, tt, hh, T, H) + yc4 * 4;
+            *reinterpret_cast<uint2*>(dv + o) = *reinterpret_cast<const uint2*>(&sm.dVs[sb][yt][yc4 * 4]);
+            *reinterpret_cast<uint2*>(wdX + o) = *reinterpret_cast<const uint2*>(&sm.dXs[sb][yt][yc4 * 4]);
+        }
+        const int j = rtid >> 2, part = rtid & 3;
+        const uint4* src = reinterpret_cast<const uint4*>(&sm.dSs[sb][j][16 * part]);
+        uint4* dst = reinterpret_cast<uint4*>(wdS + (((size_t)bh * nch + c) * kN + j) * kN + 16 * part);
+        dst[0] = src[0];
+        dst[1] = src[1];
+    };
+
+    {
+        Raw rb0, rb1, rb2;
+        if (producer) {
+            load_raw(chunk_of(0), rb0);
+            load_raw(chunk_of(1), rb1);
+            load_raw(chunk_of(2), rb2);
+            stash_raw(chunk_of(0), rb0);
+            load_raw(chunk_of(3), rb0);
+        }
+        __syncthreads();
+        // Interval it: producers E(chunk_of(it)) and MW(chunk_of(it-1)), stash
+        // chunk_of(it+1) and load chunk_of(it+4); consumers run the chain on
+        // chunk_of(it-2) and store the outputs of chunk_of(it-3).  (A macro, not
+        // a lambda, so that the register ring stays plain SSA values.)
+#define WKV7_BWD_INTERVAL(IT, RING)                                            \
+    {                                                                          \
+        const int it_ = (IT);                                                  \
+        if (producer) {                                                        \
+            MWIn mi;                                                           \
+            if (it_ >= 1) mi = read_MW(chunk_of(it_ - 1));                     \
+            stage_E(chunk_of(it_));                                            \
+            stash_raw(chunk_of(it_ + 1), RING);                                \
+            load_raw(chunk_of(it_ + 4), RING);                                 \
+            if (it_ >= 1) stage_MW(chunk_of(it_ - 1), mi);                     \
+        } else {                                                               \
+            if (it_ >= 2) {                                                    \
+                const CIn ci = read_C(chunk_of(it_ - 2));                      \
+                stage_C(chunk_of(it_ - 2), ci);                                \
+            }                                                                  \
+            if (it_ >= 3) store_out(chunk_of(it_ - 3));                        \
+        }                                                                      \
+        __syncthreads();                                                       \
+    }
+        for (int it = 0; it <= nch + 2; it += 3) {
+            WKV7_BWD_INTERVAL(it, rb1);
+            if (it + 1 > nch + 2) break;
+            WKV7_BWD_INTERVAL(it + 1, rb2);
+            if (it + 2 > nch + 2) break;
+            WKV7_BWD_INTERVAL(it + 2, rb0);
+        }
+#undef WKV7_BWD_INTERVAL
+    }
+
+    if (ds0 && !producer) {
+        float* dst = ds0 + ((size_t)bh * kN + col) * kN;
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt)
+            *reinterpret_cast<float4*>(dst + 16 * jt + 4 * g) =
+                make_float4(dSt[jt][0], dSt[jt][1], dSt[jt][2], dSt[jt][3]);
     }
 }
 
-// State-independent factors of the chunk whose raw inputs are in sm.raw.
-// Ends with a barrier; Wm only when need_w.
-__device__ void prep_chunk(const Ctx& c, BwdSmem& sm, bool need_w) {
-    const int ej = c.tid & 63, eg = c.tid >> 6;
+// =============================================================================
+// Pass 2: per-key gradients, one independent wave per (chunk, key block).
+// =============================================================================
+
+constexpr int kP2Threads = 256;   // the four key blocks of one chunk
+
+__global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
+    int T, int H, int nch, const bf16_t* __restrict__ r, const bf16_t* __restrict__ w,
+    const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const bf16_t* __restrict__ a,
+    const bf16_t* __restrict__ b, const bf16_t* __restrict__ dy, const bf16_t* __restrict__ tape,
+    const bf16_t* __restrict__ work, bf16_t* __restrict__ dr, bf16_t* __restrict__ dw,
+    bf16_t* __restrict__ dk, bf16_t* __restrict__ da, bf16_t* __restrict__ db) {
+    __shared__ float red[4][5][4][16];   // wave-private cross-lane-group exchange
+    const int c = blockIdx.x % nch;
+    const int bh = blockIdx.x / nch;
+    const int bb = bh / H, hh = bh % H;
+    const int B = gridDim.x / nch / H;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wp = tid >> 6;
+    const int l16 = lane & 15, g = lane >> 4;
+    const int col = 16 * wp + l16;     // key column j of this lane
+    const int t0 = c * kL;
+    const bf16_t* const tapeZ = tape;
+    const bf16_t* const tapeS = tape + (size_t)B * T * H * kN;
+    const bf16_t* const wdX = work;
+    const bf16_t* const wdS = work + (size_t)B * T * H * kN;
+    float* const rd = &red[wp][0][0][0];
+    auto RD = [&](int kind, int gg) __attribute__((always_inline)) -> float& {
+        return rd[(kind * 4 + gg) * 16 + l16];
+    };
+
+    // ---- loads: this lane's key column over tokens 4g..4g+3, the chunk's rows
+    // (row l16, 8 values at 32 k2 + 8 g), and column `col` of S0 and dS --------
+    float R[5][4];
+    bool okq[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int t = t0 + 4 * g + q;
+        okq[q] = t < T;
+        const size_t o = tok_off(bb, min(t, T - 1), hh, T, H) + col;
+        R[0][q] = bf2f(r[o]);
+        R[1][q] = bf2f(w[o]);
+        R[2][q] = bf2f(k[o]);
+        R[3][q] = bf2f(a[o]);
+        R[4][q] = bf2f(b[o]);
+    }
+    const int trow = t0 + l16;
+    const bool okrow = trow < T;
+    const size_t orow = tok_off(bb, min(trow, T - 1), hh, T, H);
+    bf16x8 dXr[2], Zr[2], dYr[2], Vr[2], S0c[2], dSc[2];
+    const bf16x8 zero8 = __builtin_bit_cast(bf16x8, make_uint4(0u, 0u, 0u, 0u));
+    const size_t ocol = (((size_t)bh * nch + c) * kN + col) * kN;
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+        const int i0 = 32 * k2 + 8 * g;
+        const bf16x8 x0 = ld8(wdX + orow + i0), x1 = ld8(tapeZ + orow + i0);
+        const bf16x8 x2 = ld8(dy + orow + i0), x3 = ld8(v + orow + i0);
+        dXr[k2] = okrow ? x0 : zero8;
+        Zr[k2] = okrow ? x1 : zero8;
+        dYr[k2] = okrow ? x2 : zero8;
+        Vr[k2] = okrow ? x3 : zero8;
+        S0c[k2] = ld8(tapeS + ocol + i0);
+        dSc[k2] = ld8(wdS + ocol + i0);
+    }
+
+    // ---- decay products and scaled vectors of column `col` -----------------------
     float gp[4];
     {
         float run = 1.f;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            run *= bf2f(sm.raw[RAW_W][4 * eg + u][ej]);
-            gp[u] = run;
-        }
-        sm.gtot[eg][ej] = run;
-    }
-    __syncthreads();
-    {
-        const float g0 = sm.gtot[0][ej], g1 = sm.gtot[1][ej], g2 = sm.gtot[2][ej], g3 = sm.gtot[3][ej];
-        const float before = eg == 0 ? 1.f : eg == 1 ? g0 : eg == 2 ? g0 * g1 : (g0 * g1) * g2;
-        const float GL = ((g0 * g1) * g2) * g3;
-        float at4[4], rt4[4], bh4[4], kh4[4], bb4[4], kb4[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int t = 4 * eg + u;
-            const float Gt = before * gp[u];
-            const float Gprev = u == 0 ? before : before * gp[u - 1];
-            const float inv = __builtin_amdgcn_rcpf(Gt);
-            at4[u] = bf2f(sm.raw[RAW_A][t][ej]) * Gprev;
-            rt4[u] = bf2f(sm.raw[RAW_R][t][ej]) * Gt;
-            bh4[u] = bf2f(sm.raw[RAW_B][t][ej]) * inv;
-            kh4[u] = bf2f(sm.raw[RAW_K][t][ej]) * inv;
-            bb4[u] = bh4[u] * GL;
-            kb4[u] = kh4[u] * GL;
-            sm.G[t + 1][ej] = Gt;
-            sm.At[t][ej] = f2bf(at4[u]);
-            sm.Rt[t][ej] = f2bf(rt4[u]);
-            sm.Bh[t][ej] = f2bf(bh4[u]);
-            sm.Kh[t][ej] = f2bf(kh4[u]);
-            sm.Bb[t][ej] = f2bf(bb4[u]);
-            sm.Kb[t][ej] = f2bf(kb4[u]);
-        }
-        if (eg == 0) sm.G[0][ej] = 1.f;
-        *reinterpret_cast<bf16x4*>(&sm.AtT[ej][4 * eg]) = cvt4(at4[0], at4[1], at4[2], at4[3]);
-        *reinterpret_cast<bf16x4*>(&sm.RtT[ej][4 * eg]) = cvt4(rt4[0], rt4[1], rt4[2], rt4[3]);
-        *reinterpret_cast<bf16x4*>(&sm.BhT[ej][4 * eg]) = cvt4(bh4[0], bh4[1], bh4[2], bh4[3]);
-        *reinterpret_cast<bf16x4*>(&sm.KhT[ej][4 * eg]) = cvt4(kh4[0], kh4[1], kh4[2], kh4[3]);
-        *reinterpret_cast<bf16x4*>(&sm.BbT[ej][4 * eg]) = cvt4(bb4[0], bb4[1], bb4[2], bb4[3]);
-        *reinterpret_cast<bf16x4*>(&sm.KbT[ej][4 * eg]) = cvt4(kb4[0], kb4[1], kb4[2], kb4[3]);
-    }
-    __syncthreads();
-    {
-        // L x L products: wave 0 Aab (+ transpose, then Tm = (I - Aab)^-1),
-        // 1 Aak, 2 Arb, 3 Ark.
-        const bf16_t* lrow = (c.wv < 2) ? &sm.At[c.l16][0] : &sm.Rt[c.l16][0];
-        const bf16_t* rrow = (c.wv & 1) ? &sm.Kh[c.l16][0] : &sm.Bh[c.l16][0];
-        f32x4 acc = zero4(), accT = zero4();
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-            const bf16x8 av = ld8(lrow + 32 * k2 + 8 * c.g), bv = ld8(rrow + 32 * k2 + 8 * c.g);
-            acc = mfma32(av, bv, acc);
-            if (c.wv == 0) accT = mfma32(bv, av, accT);
-        }
-        const bool strict = c.wv < 2;
-#pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int t = 4 * c.g + q, s = c.l16;
-            acc[q] = (strict ? (s < t) : (s <= t)) ? acc[q] : 0.f;
-            accT[q] = (t < s) ? accT[q] : 0.f;
-            sm.Amat[c.wv][t][s] = acc[q];
+            run *= okq[q] ? R[1][q] : 1.f;
+            gp[q] = run;
         }
-        if (c.wv == 0) {
-            const f32x4 TT = unit_lower_inverse_T(acc, accT, c.g, c.l16);
+        RD(0, g) = run;
+    }
+    wave_sync();
+    const float g0 = RD(0, 0), g1 = RD(0, 1), g2 = RD(0, 2), g3 = RD(0, 3);
+    const float before = g == 0 ? 1.f : g == 1 ? g0 : g == 2 ? g0 * g1 : (g0 * g1) * g2;
+    const float GL = ((g0 * g1) * g2) * g3;
+    float Gt[4], Gp[4], inv[4];
+    float at[4], rt[4], bh_[4], kh_[4], bbar[4], kbar[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) sm.Tm[c.l16][4 * c.g + q] = TT[q];
+    for (int q = 0; q < 4; ++q) {
+        Gt[q] = before * gp[q];
+        Gp[q] = q == 0 ? before : before * gp[q - 1];
+        inv[q] = __builtin_amdgcn_rcpf(Gt[q]);
+        const float m = okq[q] ? 1.f : 0.f;   // padding tokens carry zeros
+        at[q] = m * R[3][q] * Gp[q];
+        rt[q] = m * R[0][q] * Gt[q];
+        bh_[q] = m * R[4][q] * inv[q];
+        kh_[q] = m * R[2][q] * inv[q];
+        bbar[q] = bh_[q] * GL;
+        kbar[q] = kh_[q] * GL;
+    }
+    // bf16 images: the forward's MFMA operand values, and the B operands (key
+    // s = 4g+q, column col) of the products below.
+    const bf16x4 atI = cvt4(at[0], at[1], at[2], at[3]);
+    const bf16x4 rtI = cvt4(rt[0], rt[1], rt[2], rt[3]);
+    const bf16x4 bhI = cvt4(bh_[0], bh_[1], bh_[2], bh_[3]);
+    const bf16x4 khI = cvt4(kh_[0], kh_[1], kh_[2], kh_[3]);
+    const bf16x4 bbI = cvt4(bbar[0], bbar[1], bbar[2], bbar[3]);
+    const bf16x4 kbI = cvt4(kbar[0], kbar[1], kbar[2], kbar[3]);
+
+    // ---- L x L adjoints in both orientations ([t][s] and [s][t]) and the
+    // contractions over the value rows ----------------------------------------------
+    f32x4 dAab = zero4(), dAabT = zero4(), dAak = zero4(), dAakT = zero4();
+    f32x4 dArb = zero4(), dArbT = zero4(), dArk = zero4(), dArkT = zero4();
+    f32x4 dAt = zero4(), dRt = zero4(), dBb = zero4(), dKb = zero4();
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+        dAab = mfma32(dXr[k2], Zr[k2], dAab);
+        dAabT = mfma32(Zr[k2], dXr[k2], dAabT);
+        dAak = mfma32(dXr[k2], Vr[k2], dAak);
+        dAakT = mfma32(Vr[k2], dXr[k2], dAakT);
+        dArb = mfma32(dYr[k2], Zr[k2], dArb);
+        dArbT = mfma32(Zr[k2], dYr[k2], dArbT);
+        dArk = mfma32(dYr[k2], Vr[k2], dArk);
+        dArkT = mfma32(Vr[k2], dYr[k2], dArkT);
+        dAt = mfma32(dXr[k2], S0c[k2], dAt);     // dX S0
+        dRt = mfma32(dYr[k2], S0c[k2], dRt);     // dY S0
+        dBb = mfma32(Zr[k2], dSc[k2], dBb);      // Z dS
+        dKb = mfma32(Vr[k2], dSc[k2], dKb);      // V dS
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int m = 4 * g + q, n = l16;
+        dAab[q] = (n < m) ? dAab[q] : 0.f;
+        dAak[q] = (n < m) ? dAak[q] : 0.f;
+        dArb[q] = (n <= m) ? dArb[q] : 0.f;
+        dArk[q] = (n <= m) ? dArk[q] : 0.f;
+        dAabT[q] = (m < n) ? dAabT[q] : 0.f;
+        dAakT[q] = (m < n) ? dAakT[q] : 0.f;
+        dArbT[q] = (m <= n) ? dArbT[q] : 0.f;
+        dArkT[q] = (m <= n) ? dArkT[q] : 0.f;
+    }
+    // Accumulator registers of X fed as an A operand stand for X^T.  The
+    // 16-deep partial sums join the 32-deep ones on the vector ALU (add4).
+    dAt = add4(dAt, mfma16(cvt4(dAakT), khI, mfma16(cvt4(dAabT), bhI, zero4())));
+    dRt = add4(dRt, mfma16(cvt4(dArkT), khI, mfma16(cvt4(dArbT), bhI, zero4())));
+    f32x4 dBh = mfma16(cvt4(dAab), atI, zero4());
+    dBh = mfma16(cvt4(dArb), rtI, dBh);
+    f32x4 dKh = mfma16(cvt4(dAak), atI, zero4());
+    dKh = mfma16(cvt4(dArk), rtI, dKh);
+
+    // ---- sum_i dS[i][col] S0[i][col] over this lane's 16 value rows ---------------
+    float cs = 0.f;
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) cs = fmaf((float)dSc[k2][q], (float)S0c[k2][q], cs);
+
+    // ---- chain rule through the decay products (tokens t = 4g+q) ------------------
+    // d log w_u = sum_{t>=u} (dRt Rt - dBh Bh - dKh Kh)_t + sum_{t>=u+1} (dAt At)_t
+    //           + sum_{t<u} (dBb Bb + dKb Kb)_t + G_L sum_i dS[i][j] S0[i][j];
+    // the products use the bf16 operand values so that pair terms that cancel
+    // exactly in the chunk algebra cancel to fp32 rounding.
+    float base[4], e[4], bk[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        e[q] = dAt[q] * (float)atI[q];
+        bk[q] = dBb[q] * (float)bbI[q] + dKb[q] * (float)kbI[q];
+        base[q] = dRt[q] * (float)rtI[q] - dBh[q] * (float)bhI[q] - dKh[q] * (float)khI[q];
+    }
+    RD(1, g) = base[0] + base[1] + base[2] + base[3];
+    RD(2, g) = e[0] + e[1] + e[2] + e[3];
+    RD(3, g) = bk[0] + bk[1] + bk[2] + bk[3];
+    RD(4, g) = cs;
+    wave_sync();
+    float base_after = 0.f, e_after = 0.f, bk_before = 0.f, cs_all = 0.f;
+#pragma unroll
+    for (int g2 = 0; g2 < 4; ++g2) {
+        const float bs = RD(1, g2), es = RD(2, g2), ks = RD(3, g2);
+        cs_all += RD(4, g2);
+        if (g2 > g) {
+            base_after += bs;
+            e_after += es;
         }
+        if (g2 < g) bk_before += ks;
     }
-    __syncthreads();
-    if (need_w) {
-        const int j = 16 * c.wv + c.l16;
-        const bf16x4 Trow = f4(&sm.Tm[c.l16][4 * c.g], 1);
-        const bf16x4 Acol = cvt4(bf2f(sm.At[4 * c.g][j]), bf2f(sm.At[4 * c.g + 1][j]),
-                                 bf2f(sm.At[4 * c.g + 2][j]), bf2f(sm.At[4 * c.g + 3][j]));
-        const f32x4 Wt = mfma16(Trow, Acol, zero4());
+    const float csL = cs_all * GL;
+    float pbk[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) sm.Wm[4 * c.g + q][j] = f2bf(Wt[q]);
-        __syncthreads();
+    for (int q = 0; q < 4; ++q) {
+        pbk[q] = bk_before;
+        bk_before += bk[q];
     }
-}
-
-__global__ __launch_bounds__(kThreads) void chunk_bwd_kernel(
-    int T, int H, const bf16_t* __restrict__ r, const bf16_t* __restrict__ w,
-    const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const bf16_t* __restrict__ a,
-    const bf16_t* __restrict__ b, const bf16_t* __restrict__ dy, const float* __restrict__ dsT,
-    const float* __restrict__ ckpt, bf16_t* __restrict__ dr, bf16_t* __restrict__ dw,
-    bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, bf16_t* __restrict__ da,
-    bf16_t* __restrict__ db, float* __restrict__ ds0) {
-    __shared__ BwdSmem sm;
-    Ctx c;
-    c.T = T;
-    c.H = H;
-    const int bh = blockIdx.x;
-    c.bb = bh / H;
-    c.hh = bh % H;
-    c.tid = threadIdx.x;
-    c.lane = c.tid & 63;
-    c.wv = c.tid >> 6;
-    c.l16 = c.lane & 15;
-    c.g = c.lane >> 4;
-    c.irow = 16 * c.wv + c.l16;
-    c.r = r; c.w = w; c.k = k; c.a = a; c.b = b; c.v = v; c.dy = dy;
-    const int l16 = c.l16, g = c.g, wv = c.wv, irow = c.irow;
-    const int nck = (T + kCkptInterval - 1) / kCkptInterval;
-
-    // Adjoint of the current exit state, held as dS^T tiles like the forward's S^T.
-    f32x4 dSt[4];
-#pragma unroll
-    for (int jt = 0; jt < 4; ++jt) {
-        if (dsT) {
-            const float4 x = *reinterpret_cast<const float4*>(dsT + ((size_t)bh * kN + irow) * kN + 16 * jt + 4 * g);
-            dSt[jt][0] = x.x; dSt[jt][1] = x.y; dSt[jt][2] = x.z; dSt[jt][3] = x.w;
-        } else {
-            dSt[jt] = zero4();
-        }
-    }
-
-    // Visiting order: for each block (last first) its chunks forwards (state
-    // re-run), then backwards (adjoint).  step -> (chunk start, needs dy).
-    auto step_chunk = [&](int blk, int nc, int s, int& t0, bool& back) {
-        back = s >= nc;
-        const int ci = back ? (2 * nc - 1 - s) : s;
-        t0 = blk * kCkptInterval + ci * kL;
-    };
-
-    Prefetch pf;
+    float dlw[4];
     {
-        const int blk = nck - 1;
-        const int nc = (T - blk * kCkptInterval + kL - 1) / kL;
-        int t0; bool back;
-        step_chunk(blk, nc, 0, t0, back);
-        load_raw(c, t0, back ? 7 : 6, pf);
-    }
-
-    for (int blk = nck - 1; blk >= 0; --blk) {
-        const int tb0 = blk * kCkptInterval;
-        const int nc = min(kChunksPerBlock, (T - tb0 + kL - 1) / kL);
-
-        // Entry state of the block.
-        f32x4 S[4];
-        {
-            const float* src = ckpt + (((size_t)bh * nck + blk) * kN + irow) * kN;
+        float sb = base_after, se = e_after;
 #pragma unroll
-            for (int jt = 0; jt < 4; ++jt) {
-                const float4 x = *reinterpret_cast<const float4*>(src + 16 * jt + 4 * g);
-                S[jt][0] = x.x; S[jt][1] = x.y; S[jt][2] = x.z; S[jt][3] = x.w;
-            }
-        }
-
-        for (int s = 0; s < 2 * nc; ++s) {
-            int t0; bool back;
-            step_chunk(blk, nc, s, t0, back);
-            const int ci = (t0 - tb0) / kL;
-            const int nvec = back ? 7 : 6;
-            __syncthreads();                 // previous users of sm.raw are done
-            stash_raw(c, sm, nvec, pf);
-            {
-                // Prefetch the next step's raw inputs.
-                int nblk = blk, ns = s + 1, nnc = nc;
-                if (ns >= 2 * nc) {
-                    nblk = blk - 1;
-                    ns = 0;
-                    nnc = nblk >= 0 ? min(kChunksPerBlock, (T - nblk * kCkptInterval + kL - 1) / kL) : 0;
-                }
-                if (nblk >= 0) {
-                    int nt0; bool nback;
-                    step_chunk(nblk, nnc, ns, nt0, nback);
-                    load_raw(c, nt0, nback ? 7 : 6, pf);
-                }
-            }
-            __syncthreads();
-            prep_chunk(c, sm, !back);
-
-            if (!back) {
-                // ---- forward re-run: Z = W S0^T + Tm Aak V, next entry state ----
-                const bf16x4 Vb = cvt4(bf2f(sm.raw[RAW_V][4 * g][irow]), bf2f(sm.raw[RAW_V][4 * g + 1][irow]),
-                                       bf2f(sm.raw[RAW_V][4 * g + 2][irow]), bf2f(sm.raw[RAW_V][4 * g + 3][irow]));
-                const f32x4 AkV = mfma16(f4(&sm.Amat[1][l16][4 * g], 1), Vb, zero4());
-                f32x4 Z = mfma16(f4(&sm.Tm[l16][4 * g], 1), cvt4(AkV), zero4());
-                bf16x4 Sb[4];
-#pragma unroll
-                for (int jt = 0; jt < 4; ++jt) Sb[jt] = cvt4(S[jt]);
-#pragma unroll
-                for (int k2 = 0; k2 < 2; ++k2)
-                    Z = mfma32(ld4x2(&sm.Wm[l16][32 * k2 + 4 * g]), cat8(Sb[2 * k2], Sb[2 * k2 + 1]), Z);
-#pragma unroll
-                for (int jt = 0; jt < 4; ++jt)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) sm.Sblk[ci][16 * jt + 4 * g + q][irow] = bits(Sb[jt][q]);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) sm.Zblk[ci][4 * g + q][irow] = f2bf(Z[q]);
-                if (ci + 1 < nc) {
-                    const bf16x4 Zb = cvt4(Z);
-#pragma unroll
-                    for (int jt = 0; jt < 4; ++jt) {
-                        f32x4 acc = mfma16(ld4(&sm.KbT[16 * jt + l16][4 * g]), Vb, zero4());
-#pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            acc[q] = fmaf(sm.G[kL][16 * jt + 4 * g + q], S[jt][q], acc[q]);
-                        S[jt] = mfma16(ld4(&sm.BbT[16 * jt + l16][4 * g]), Zb, acc);
-                    }
-                }
-                continue;
-            }
-
-            // ---- backward step for chunk ci of this block ------------------------
-            const bf16_t* Ss = &sm.Sblk[ci][0][0];
-            const bf16_t* Zs = &sm.Zblk[ci][0][0];
-            const bf16x4 dYb = cvt4(bf2f(sm.raw[RAW_DY][4 * g][irow]), bf2f(sm.raw[RAW_DY][4 * g + 1][irow]),
-                                    bf2f(sm.raw[RAW_DY][4 * g + 2][irow]), bf2f(sm.raw[RAW_DY][4 * g + 3][irow]));
-            const bf16x4 Vb = cvt4(bf2f(sm.raw[RAW_V][4 * g][irow]), bf2f(sm.raw[RAW_V][4 * g + 1][irow]),
-                                   bf2f(sm.raw[RAW_V][4 * g + 2][irow]), bf2f(sm.raw[RAW_V][4 * g + 3][irow]));
-            bf16x4 dSb[4];
-#pragma unroll
-            for (int jt = 0; jt < 4; ++jt) dSb[jt] = cvt4(dSt[jt]);
-            // dZ = Arb^T dY + Bb dS^T ;  dX = Tm^T dZ
-            f32x4 dZ = mfma16(f4(&sm.Amat[2][4 * g][l16], kL), dYb, zero4());
-#pragma unroll
-            for (int k2 = 0; k2 < 2; ++k2)
-                dZ = mfma32(ld4x2(&sm.Bb[l16][32 * k2 + 4 * g]), cat8(dSb[2 * k2], dSb[2 * k2 + 1]), dZ);
-            const f32x4 dX = mfma16(f4(&sm.Tm[4 * g][l16], kL), cvt4(dZ), zero4());
-            const bf16x4 dXb = cvt4(dX);
-            // dV = Aak^T dX + Ark^T dY + Kb dS^T
-            f32x4 dV = mfma16(f4(&sm.Amat[1][4 * g][l16], kL), dXb, zero4());
-            dV = mfma16(f4(&sm.Amat[3][4 * g][l16], kL), dYb, dV);
-#pragma unroll
-            for (int k2 = 0; k2 < 2; ++k2)
-                dV = mfma32(ld4x2(&sm.Kb[l16][32 * k2 + 4 * g]), cat8(dSb[2 * k2], dSb[2 * k2 + 1]), dV);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                sm.dXs[4 * g + q][irow] = bits(dXb[q]);
-                sm.gst[GS_DV][4 * g + q][irow] = f2bf(dV[q]);
-            }
-            // Share the incoming dS (bf16) and the partial sum_i dS * S0.
-#pragma unroll
-            for (int jt = 0; jt < 4; ++jt) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int j = 16 * jt + 4 * g + q;
-                    sm.dSs[j][irow] = bits(dSb[jt][q]);
-                    const float p = row16_sum(dSt[jt][q] * bf2f(Ss[j * kRow + irow]));
-                    if (l16 == 0) sm.colsum[wv][j] = p;
-                }
-            }
-            // dS0 = dS diag(G_L) + dY^T Rt + dX^T At   (as transposed tiles)
-#pragma unroll
-            for (int jt = 0; jt < 4; ++jt) {
-                f32x4 acc;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) acc[q] = sm.G[kL][16 * jt + 4 * g + q] * dSt[jt][q];
-                acc = mfma16(ld4(&sm.RtT[16 * jt + l16][4 * g]), dYb, acc);
-                dSt[jt] = mfma16(ld4(&sm.AtT[16 * jt + l16][4 * g]), dXb, acc);
-            }
-            __syncthreads();
-
-            // ---- L x L adjoints: wave 0 dAab, 1 dAak, 2 dArb, 3 dArk ---------------
-            {
-                const bf16_t* lrow = (wv < 2) ? &sm.dXs[l16][0] : &sm.raw[RAW_DY][l16][0];
-                const bf16_t* rrow = (wv & 1) ? &sm.raw[RAW_V][l16][0] : Zs + l16 * kRow;
-                f32x4 acc = zero4();
-#pragma unroll
-                for (int k2 = 0; k2 < 2; ++k2)
-                    acc = mfma32(ld8(lrow + 32 * k2 + 8 * g), ld8(rrow + 32 * k2 + 8 * g), acc);
-                const bool strict = wv < 2;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int t = 4 * g + q, s2 = l16;
-                    sm.dAm[wv][t][s2] = (strict ? (s2 < t) : (s2 <= t)) ? acc[q] : 0.f;
-                }
-            }
-            __syncthreads();
-
-            // ---- per-key adjoints for key columns j = 16 wv + l16 -----------------
-            const int jcol = 16 * wv + l16;
-            f32x4 dAt = zero4(), dRt = zero4(), dBh, dKh, dBb = zero4(), dKb = zero4();
-#pragma unroll
-            for (int k2 = 0; k2 < 2; ++k2) {
-                const bf16x8 s0v = ld8(Ss + jcol * kRow + 32 * k2 + 8 * g);
-                const bf16x8 dsv = ld8(&sm.dSs[jcol][32 * k2 + 8 * g]);
-                dAt = mfma32(ld8(&sm.dXs[l16][32 * k2 + 8 * g]), s0v, dAt);
-                dRt = mfma32(ld8(&sm.raw[RAW_DY][l16][32 * k2 + 8 * g]), s0v, dRt);
-                dBb = mfma32(ld8(Zs + l16 * kRow + 32 * k2 + 8 * g), dsv, dBb);
-                dKb = mfma32(ld8(&sm.raw[RAW_V][l16][32 * k2 + 8 * g]), dsv, dKb);
-            }
-            {
-                const bf16x4 bhT = ld4(&sm.BhT[jcol][4 * g]);
-                const bf16x4 khT = ld4(&sm.KhT[jcol][4 * g]);
-                const bf16x4 atT = ld4(&sm.AtT[jcol][4 * g]);
-                const bf16x4 rtT = ld4(&sm.RtT[jcol][4 * g]);
-                dAt = mfma16(f4(&sm.dAm[0][l16][4 * g], 1), bhT, dAt);
-                dAt = mfma16(f4(&sm.dAm[1][l16][4 * g], 1), khT, dAt);
-                dRt = mfma16(f4(&sm.dAm[2][l16][4 * g], 1), bhT, dRt);
-                dRt = mfma16(f4(&sm.dAm[3][l16][4 * g], 1), khT, dRt);
-                dBh = mfma16(f4(&sm.dAm[0][4 * g][l16], kL), atT, zero4());
-                dBh = mfma16(f4(&sm.dAm[2][4 * g][l16], kL), rtT, dBh);
-                dKh = mfma16(f4(&sm.dAm[1][4 * g][l16], kL), atT, zero4());
-                dKh = mfma16(f4(&sm.dAm[3][4 * g][l16], kL), rtT, dKh);
-            }
-
-            // ---- chain rule through the decay products, tokens t = 4g+q ----------
-            // d log w_u = sum_{t>=u} (dRt Rt - dBh Bh - dKh Kh)_t + sum_{t>=u+1} (dAt At)_t
-            //           + sum_{t<u} (dBb Bb + dKb Kb)_t + G_L sum_i dS[i][j] S0[i][j].
-            // The products use the same bf16 values as the MFMA operands, so the
-            // pair terms that cancel exactly (both ends of an L x L factor on
-            // the same side of u) cancel to fp32 rounding.
-            {
-                const float GL = sm.G[kL][jcol];
-                float base[4], e[4], bk[4];
-                float dav[4], drv[4], dbv[4], dkv[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int t = 4 * g + q;
-                    const float Gt = sm.G[t + 1][jcol], Gp = sm.G[t][jcol];
-                    const float inv = __builtin_amdgcn_rcpf(Gt);
-                    dav[q] = dAt[q] * Gp;
-                    drv[q] = dRt[q] * Gt;
-                    dbv[q] = (dBh[q] + dBb[q] * GL) * inv;
-                    dkv[q] = (dKh[q] + dKb[q] * GL) * inv;
-                    e[q] = dAt[q] * bf2f(sm.At[t][jcol]);
-                    bk[q] = dBb[q] * bf2f(sm.Bb[t][jcol]) + dKb[q] * bf2f(sm.Kb[t][jcol]);
-                    base[q] = dRt[q] * bf2f(sm.Rt[t][jcol]) - dBh[q] * bf2f(sm.Bh[t][jcol]) -
-                              dKh[q] * bf2f(sm.Kh[t][jcol]);
-                }
-                // Token sums across the four lane groups (tokens 4g..4g+3) of this wave.
-                float* red = &sm.red[wv][0][0][0];
-                red[(0 * 4 + g) * 16 + l16] = base[0] + base[1] + base[2] + base[3];
-                red[(1 * 4 + g) * 16 + l16] = e[0] + e[1] + e[2] + e[3];
-                red[(2 * 4 + g) * 16 + l16] = bk[0] + bk[1] + bk[2] + bk[3];
-                wave_sync();
-                float base_after = 0.f, e_after = 0.f, bk_before = 0.f;
-#pragma unroll
-                for (int g2 = 0; g2 < 4; ++g2) {
-                    const float bs = red[(0 * 4 + g2) * 16 + l16];
-                    const float es = red[(1 * 4 + g2) * 16 + l16];
-                    const float ks = red[(2 * 4 + g2) * 16 + l16];
-                    if (g2 > g) {
-                        base_after += bs;
-                        e_after += es;
-                    }
-                    if (g2 < g) bk_before += ks;
-                }
-                const float cs = (sm.colsum[0][jcol] + sm.colsum[1][jcol] + sm.colsum[2][jcol] +
-                                  sm.colsum[3][jcol]) * GL;
-                float pbk[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    pbk[q] = bk_before;
-                    bk_before += bk[q];
-                }
-                float sb = base_after, se = e_after;
-#pragma unroll
-                for (int q = 3; q >= 0; --q) {
-                    const int t = 4 * g + q;
-                    sb += base[q];
-                    const float dlw = (sb + se) + (pbk[q] + cs);
-                    se += e[q];
-                    const float wt = bf2f(sm.raw[RAW_W][t][jcol]);
-                    sm.gst[GS_DW][t][jcol] = f2bf(dlw / wt);
-                    sm.gst[GS_DA][t][jcol] = f2bf(dav[q]);
-                    sm.gst[GS_DR][t][jcol] = f2bf(drv[q]);
-                    sm.gst[GS_DB][t][jcol] = f2bf(dbv[q]);
-                    sm.gst[GS_DK][t][jcol] = f2bf(dkv[q]);
-                }
-            }
-            __syncthreads();
-            // ---- coalesced gradient stores: 6 x 16 tokens x 128 B -----------------
-#pragma unroll
-            for (int p = 0; p < 3; ++p) {
-                const int item = c.tid + p * kThreads;
-                const int q = item >> 7, t = (item >> 3) & 15, c8 = item & 7;
-                const bool hi = c.tid >= 128;   // q = 2p + hi: dr/dw, dk/dv, da/db
-                bf16_t* gp = p == 0 ? (hi ? dw : dr) : p == 1 ? (hi ? dv : dk) : (hi ? db : da);
-                if (t0 + t < T)
-                    *reinterpret_cast<uint4*>(gp + tok_off(c.bb, t0 + t, c.hh, T, H) + c8 * 8) =
-                        *reinterpret_cast<const uint4*>(&sm.gst[q][t][c8 * 8]);
-            }
+        for (int q = 3; q >= 0; --q) {
+            sb += base[q];
+            dlw[q] = (sb + se) + (pbk[q] + csL);
+            se += e[q];
         }
     }
-
-    if (ds0) {
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt)
-            *reinterpret_cast<float4*>(ds0 + ((size_t)bh * kN + irow) * kN + 16 * jt + 4 * g) =
-                make_float4(dSt[jt][0], dSt[jt][1], dSt[jt][2], dSt[jt][3]);
+    for (int q = 0; q < 4; ++q) {
+        if (!okq[q]) continue;
+        const size_t o = tok_off(bb, t0 + 4 * g + q, hh, T, H) + col;
+        da[o] = f2bf(dAt[q] * Gp[q]);
+        dr[o] = f2bf(dRt[q] * Gt[q]);
+        db[o] = f2bf((dBh[q] + dBb[q] * GL) * inv[q]);
+        dk[o] = f2bf((dKh[q] + dKb[q] * GL) * inv[q]);
+        dw[o] = f2bf(dlw[q] / R[1][q]);
     }
 }
 
@@ -523,13 +610,23 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_kernel(
 
 hipError_t launch_bwd(const BwdArgs& p, int chunk_len, hipStream_t stream) {
     if (chunk_len != kL || !p.bf16) return hipErrorInvalidValue;
-    chunk_bwd_kernel<<<dim3(p.B * p.H), dim3(kThreads), 0, stream>>>(
-        p.T, p.H, static_cast<const bf16_t*>(p.r), static_cast<const bf16_t*>(p.w),
-        static_cast<const bf16_t*>(p.k), static_cast<const bf16_t*>(p.v),
-        static_cast<const bf16_t*>(p.a), static_cast<const bf16_t*>(p.b),
-        static_cast<const bf16_t*>(p.dy), p.dsT, p.ckpt, static_cast<bf16_t*>(p.dr),
-        static_cast<bf16_t*>(p.dw), static_cast<bf16_t*>(p.dk), static_cast<bf16_t*>(p.dv),
-        static_cast<bf16_t*>(p.da), static_cast<bf16_t*>(p.db), p.ds0);
+    const bf16_t* r = static_cast<const bf16_t*>(p.r);
+    const bf16_t* w = static_cast<const bf16_t*>(p.w);
+    const bf16_t* k = static_cast<const bf16_t*>(p.k);
+    const bf16_t* v = static_cast<const bf16_t*>(p.v);
+    const bf16_t* a = static_cast<const bf16_t*>(p.a);
+    const bf16_t* b = static_cast<const bf16_t*>(p.b);
+    const bf16_t* dy = static_cast<const bf16_t*>(p.dy);
+    bf16_t* work = static_cast<bf16_t*>(p.work);
+    bwd_chain_kernel<<<dim3(p.B * p.H), dim3(kP1Threads), 0, stream>>>(
+        p.T, p.H, r, w, k, a, b, dy, p.dsT, static_cast<bf16_t*>(p.dv), p.ds0, work);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int nch = (p.T + kL - 1) / kL;
+    bwd_keys_kernel<<<dim3(p.B * p.H * nch), dim3(kP2Threads), 0, stream>>>(
+        p.T, p.H, nch, r, w, k, v, a, b, dy, static_cast<const bf16_t*>(p.tape), work,
+        static_cast<bf16_t*>(p.dr), static_cast<bf16_t*>(p.dw), static_cast<bf16_t*>(p.dk),
+        static_cast<bf16_t*>(p.da), static_cast<bf16_t*>(p.db));
     return hipGetLastError();
 }
 

@@ -73,6 +73,8 @@ struct __align__(16) FwdSmem {
     bf16_t raw[2][6][kL][kRow];   // r, w, k, a, b, v of two chunks (bf16 bits)
     Slot sl[3];
     bf16_t Ys[2][kL][kRow];
+    bf16_t Zs[2][kL][kRow];       // removal read-outs, staged for the tape
+    bf16_t S0s[2][kN][kRow];      // chunk entry states as [j][i], staged for the tape
     float red[4][4][16];          // producer-private prefix scratch
 };
 
@@ -105,7 +107,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
     int T, int H, const bf16_t* __restrict__ r, const bf16_t* __restrict__ w,
     const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const bf16_t* __restrict__ a,
     const bf16_t* __restrict__ b, const float* __restrict__ s0, bf16_t* __restrict__ y,
-    float* __restrict__ sT, float* __restrict__ ckpt) {
+    float* __restrict__ sT, bf16_t* __restrict__ tape) {
     __shared__ FwdSmem sm;
     const int bh = blockIdx.x;
     const int bb = bh / H, hh = bh % H;
@@ -115,8 +117,11 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
     const int lane = tid & 63, wp = rtid >> 6;
     const int l16 = lane & 15, g = lane >> 4;
     const int col = 16 * wp + l16;            // key column (producer) / value row (consumer)
-    const int nck = (T + kCkptInterval - 1) / kCkptInterval;
     const int nch = (T + kL - 1) / kL;
+    // Tape for the backward: removal read-outs Z as [B][T][H][N] bf16, then every
+    // chunk's entry state as [B][H][nch][N (key j)][N (value i)] bf16.
+    bf16_t* const tapeZ = tape;
+    bf16_t* const tapeS = tape ? tape + (size_t)gridDim.x / H * T * H * kN : nullptr;
 
     // ---- consumer state: S^T tiles, lane holds S[col][16 jt + 4 g + q] ----------
     f32x4 S[4];
@@ -130,13 +135,6 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
                 const float4 x = *reinterpret_cast<const float4*>(base + 16 * jt + 4 * g);
                 S[jt][0] = x.x; S[jt][1] = x.y; S[jt][2] = x.z; S[jt][3] = x.w;
             }
-        }
-        if (ckpt && T > 0) {
-            float* dst = ckpt + ((size_t)bh * nck * kN + col) * kN;
-#pragma unroll
-            for (int jt = 0; jt < 4; ++jt)
-                *reinterpret_cast<float4*>(dst + 16 * jt + 4 * g) =
-                    make_float4(S[jt][0], S[jt][1], S[jt][2], S[jt][3]);
         }
     }
 
@@ -308,13 +306,15 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
         bf16x4 Sb[4];
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) Sb[jt] = cvt4(S[jt]);
-        f32x4 Z = U, Yt = Y0;
+        f32x4 Z = zero4(), Yt = zero4();
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
             const bf16x8 bs = cat8(Sb[2 * k2], Sb[2 * k2 + 1]);
             Z = mfma32(in.wa[k2], bs, Z);
             Yt = mfma32(in.qa[k2], bs, Yt);
         }
+        Z = add4(Z, U);      // the 16-deep and 32-deep partial sums meet on the vector ALU
+        Yt = add4(Yt, Y0);
         const bf16x4 Zb = cvt4(Z);
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
@@ -329,13 +329,13 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
         const bf16x4 Yb = cvt4(Yt);
 #pragma unroll
         for (int q = 0; q < 4; ++q) sm.Ys[c & 1][4 * g + q][col] = bits(Yb[q]);
-        const int done = (c + 1) * kL;
-        if (ckpt && (done % kCkptInterval) == 0 && done < T) {
-            float* dst = ckpt + (((size_t)bh * nck + done / kCkptInterval) * kN + col) * kN;
+        if (tape) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) sm.Zs[c & 1][4 * g + q][col] = bits(Zb[q]);
 #pragma unroll
             for (int jt = 0; jt < 4; ++jt)
-                *reinterpret_cast<float4*>(dst + 16 * jt + 4 * g) =
-                    make_float4(S[jt][0], S[jt][1], S[jt][2], S[jt][3]);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) sm.S0s[c & 1][16 * jt + 4 * g + q][col] = bits(Sb[jt][q]);
         }
     };
 
@@ -348,6 +348,21 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
         const int tt = c * kL + yt;
         if (y && tt < T)
             *reinterpret_cast<uint2*>(y + tok_off(bb, tt, hh, T, H) + yc4 * 4) = val;
+    };
+    // Tape of chunk c: Z rows like y; the entry state as 64 rows x 128 B, each
+    // consumer thread copying 32 bytes of row rtid / 4.
+    auto store_tape = [&](int c) __attribute__((always_inline)) {
+        const int tt = c * kL + yt;
+        if (tt < T)
+            *reinterpret_cast<uint2*>(tapeZ + tok_off(bb, tt, hh, T, H) + yc4 * 4) =
+                *reinterpret_cast<const uint2*>(&sm.Zs[c & 1][yt][yc4 * 4]);
+        if (c < nch) {
+            const int j = rtid >> 2, part = rtid & 3;
+            const uint4* src = reinterpret_cast<const uint4*>(&sm.S0s[c & 1][j][16 * part]);
+            uint4* dst = reinterpret_cast<uint4*>(tapeS + (((size_t)bh * nch + c) * kN + j) * kN + 16 * part);
+            dst[0] = src[0];
+            dst[1] = src[1];
+        }
     };
 
     if (T > 0) {
@@ -388,6 +403,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
                 if (it_ >= 3) yv = read_y(it_ - 3);                         \
                 stage_ST(it_ - 2, si);                                      \
                 if (it_ >= 3) store_y(it_ - 3, yv);                         \
+                if (tape && it_ >= 3) store_tape(it_ - 3);                  \
             }                                                               \
         }                                                                   \
         __syncthreads();                                                    \
@@ -420,7 +436,7 @@ hipError_t launch_chunk_fwd(const FwdArgs& p, int chunk_len, hipStream_t stream)
         p.T, p.H, static_cast<const bf16_t*>(p.r), static_cast<const bf16_t*>(p.w),
         static_cast<const bf16_t*>(p.k), static_cast<const bf16_t*>(p.v),
         static_cast<const bf16_t*>(p.a), static_cast<const bf16_t*>(p.b), p.s0,
-        static_cast<bf16_t*>(p.y), p.sT, p.ckpt);
+        static_cast<bf16_t*>(p.y), p.sT, static_cast<bf16_t*>(p.tape));
     return hipGetLastError();
 }
 

@@ -7,7 +7,6 @@
 namespace wkv7 {
 
 constexpr int kN = 64;           // head size: state is kN x kN
-constexpr int kCkptInterval = 64;
 
 typedef uint16_t bf16_t;         // raw IEEE bfloat16 bits
 

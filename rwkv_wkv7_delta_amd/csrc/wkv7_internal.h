@@ -13,7 +13,7 @@ struct FwdArgs {
     const float* s0;  // may be null
     void* y;          // may be null only when T == 0
     float* sT;        // may be null
-    float* ckpt;      // may be null
+    void* tape;       // may be null: bf16 Z [B][T][H][N] then entry states [B][H][nch][N][N]
 };
 
 struct BwdArgs {
@@ -23,9 +23,10 @@ struct BwdArgs {
     const float* s0;   // may be null
     const void* dy;
     const float* dsT;  // may be null
-    const float* ckpt; // checkpoints (never null here)
+    const void* tape;  // written by the forward (never null here)
     void *dr, *dw, *dk, *dv, *da, *db;
     float* ds0;        // may be null
+    void* work;        // dX [B][T][H][N] bf16, then incoming dS [B][H][nch][N][N] bf16
 };
 
 struct DecodeArgs {

@@ -24,13 +24,14 @@ namespace wkv7 {
 namespace {
 
 constexpr int kTB = 16;  // tokens per LDS stage
+static_assert(kTB == 16, "the tape stores the state entering every 16-token chunk");
 
 template <typename Tin, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void seq_fwd_kernel(
     int T, int H, const Tin* __restrict__ r, const Tin* __restrict__ w,
     const Tin* __restrict__ k, const Tin* __restrict__ v, const Tin* __restrict__ a,
     const Tin* __restrict__ b, const float* __restrict__ s0, Tin* __restrict__ y,
-    float* __restrict__ sT, float* __restrict__ ckpt) {
+    float* __restrict__ sT, bf16_t* __restrict__ tape) {
     constexpr int R = 4 * WAVES;     // state rows per workgroup
     constexpr int NRB = kN / R;      // workgroups per head
     constexpr int NT = 64 * WAVES;   // threads
@@ -40,6 +41,7 @@ __global__ __launch_bounds__(64 * WAVES) void seq_fwd_kernel(
     __shared__ float4 sm[5][kTB][16];   // r, w, k, a, b as fp32
     __shared__ float sv[kTB][R];        // this workgroup's v slice
     __shared__ float sy[kTB][R];        // read-outs before the coalesced store
+    __shared__ float sz[kTB][R];        // removal read-outs z = S a, for the tape
 
     const int rb = blockIdx.x % NRB;
     const int bh = blockIdx.x / NRB;
@@ -53,9 +55,11 @@ __global__ __launch_bounds__(64 * WAVES) void seq_fwd_kernel(
 
     const size_t soff = ((size_t)bh * kN + row) * kN + cq * 4;
     float4 S = s0 ? *reinterpret_cast<const float4*>(s0 + soff) : make_float4(0.f, 0.f, 0.f, 0.f);
-    const int nck = (T + kCkptInterval - 1) / kCkptInterval;
-    if (ckpt && T > 0)
-        *reinterpret_cast<float4*>(ckpt + ((size_t)bh * nck * kN + row) * kN + cq * 4) = S;
+    // Tape for the backward: z as [B][T][H][N] bf16, then the state entering every
+    // 16-token chunk as [B][H][nch][N (key)][N (value)] bf16.
+    const int nch = (T + 15) / 16;
+    bf16_t* const tapeZ = tape;
+    bf16_t* const tapeS = tape ? tape + (size_t)(gridDim.x / NRB) / H * T * H * kN : nullptr;
 
     float4 pre[5][PER];
     float4 prev = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -97,26 +101,34 @@ __global__ __launch_bounds__(64 * WAVES) void seq_fwd_kernel(
     for (int t0 = 0; t0 < T; t0 += kTB) {
         const int nt = min(kTB, T - t0);
         if (t0 + kTB < T) load_regs(t0 + kTB);
+        if (tape) {   // entry state of chunk t0 / 16 (kTB == 16)
+            bf16_t* dst = tapeS + ((size_t)bh * nch + t0 / kTB) * kN * kN + row;
+            dst[(cq * 4 + 0) * kN] = f2bf(S.x);
+            dst[(cq * 4 + 1) * kN] = f2bf(S.y);
+            dst[(cq * 4 + 2) * kN] = f2bf(S.z);
+            dst[(cq * 4 + 3) * kN] = f2bf(S.w);
+        }
         for (int t = 0; t < nt; ++t) {
             const float4 A = sm[3][t][cq], Bv = sm[4][t][cq], W = sm[1][t][cq];
             const float4 K = sm[2][t][cq], Rr = sm[0][t][cq];
             const float vi = sv[t][rloc];
             const float z = row16_sum(dot4(S, A));
+            if (cq == 0) sz[t][rloc] = z;
             S.x = fmaf(vi, K.x, fmaf(z, Bv.x, S.x * W.x));
             S.y = fmaf(vi, K.y, fmaf(z, Bv.y, S.y * W.y));
             S.z = fmaf(vi, K.z, fmaf(z, Bv.z, S.z * W.z));
             S.w = fmaf(vi, K.w, fmaf(z, Bv.w, S.w * W.w));
             const float yy = row16_sum(dot4(S, Rr));
             if (cq == 0) sy[t][rloc] = yy;
-            const int done = t0 + t + 1;
-            if (ckpt && (done % kCkptInterval) == 0 && done < T)
-                *reinterpret_cast<float4*>(
-                    ckpt + (((size_t)bh * nck + done / kCkptInterval) * kN + row) * kN + cq * 4) = S;
         }
         __syncthreads();
         for (int idx = tid; y && idx < nt * R; idx += NT) {
             const int t = idx / R, i = idx % R;
             Elem<Tin>::store1(y + tok_off(bb, t0 + t, hh, T, H) + rb * R + i, sy[t][i]);
+        }
+        for (int idx = tid; tape && idx < nt * R; idx += NT) {
+            const int t = idx / R, i = idx % R;
+            tapeZ[tok_off(bb, t0 + t, hh, T, H) + rb * R + i] = f2bf(sz[t][i]);
         }
         if (t0 + kTB < T) store_lds();
         __syncthreads();
@@ -187,10 +199,10 @@ hipError_t launch_seq_fwd_t(const FwdArgs& p, hipStream_t stream) {
     // Few heads: split each head's rows over 4 workgroups to occupy more CUs.
     if (BH < 512) {
         seq_fwd_kernel<Tin, 4><<<dim3(BH * 4), dim3(256), 0, stream>>>(
-            p.T, p.H, r, w, k, v, a, b, p.s0, y, p.sT, p.ckpt);
+            p.T, p.H, r, w, k, v, a, b, p.s0, y, p.sT, static_cast<bf16_t*>(p.tape));
     } else {
         seq_fwd_kernel<Tin, 16><<<dim3(BH), dim3(1024), 0, stream>>>(
-            p.T, p.H, r, w, k, v, a, b, p.s0, y, p.sT, p.ckpt);
+            p.T, p.H, r, w, k, v, a, b, p.s0, y, p.sT, static_cast<bf16_t*>(p.tape));
     }
     return hipGetLastError();
 }

@@ -43,13 +43,17 @@ def test_version_and_status_strings(L):
     assert L.wkv7_status_string(99) == b"unknown status"
 
 
-def test_ckpt_and_workspace_sizes(L):
+def test_tape_and_workspace_sizes(L):
     d = wk.make_desc(8, 4096, 40, 64, wk.WKV7_BF16, 16)
-    assert wk.ckpt_bytes(d) == 8 * 40 * 64 * 64 * 64 * 4
-    assert wk.workspace_bytes(d) == wk.ckpt_bytes(d)
-    d = wk.make_desc(1, 65, 2, 64, wk.WKV7_F32, 0)
-    assert wk.ckpt_bytes(d) == 1 * 2 * 2 * 64 * 64 * 4
-    assert wk.ckpt_bytes(wk.make_desc(1, 64, 1, 32, wk.WKV7_F32, 0)) == 0   # invalid N
+    tape = 8 * 4096 * 40 * 64 * 2 + 8 * 40 * 256 * 64 * 64 * 2
+    assert wk.tape_bytes(d) == tape
+    assert wk.workspace_bytes(d, True) == tape
+    assert wk.workspace_bytes(d, False) == 2 * tape
+    d = wk.make_desc(1, 65, 2, 64, wk.WKV7_F32, 0)   # 5 chunks, the last ragged
+    assert wk.tape_bytes(d) == 65 * 2 * 64 * 2 + 2 * 5 * 64 * 64 * 2
+    assert wk.tape_bytes(wk.make_desc(3, 0, 2, 64, wk.WKV7_BF16, 16)) == 0
+    assert wk.tape_bytes(wk.make_desc(1, 64, 1, 32, wk.WKV7_F32, 0)) == 0   # invalid N
+    assert wk.workspace_bytes(wk.make_desc(1, 64, 1, 32, wk.WKV7_F32, 0), True) == 0
 
 
 FAKE = 1 << 20   # aligned, never dereferenced (validation fails first or nothing runs)
@@ -86,6 +90,14 @@ def test_backward_validation(L):
         wk.WKV7_ERR_WORKSPACE
     assert L.wkv7_backward(ctypes.byref(d), *args, None, *[FAKE] * 5, None, None, FAKE,
                            1 << 30, None) == wk.WKV7_ERR_INVALID_ARG
+    # With a tape the workspace still has to hold the backward's own scratch.
+    need = wk.workspace_bytes(d, True)
+    assert L.wkv7_backward(ctypes.byref(d), *args, FAKE, *grads, None, FAKE, need - 16, None) == \
+        wk.WKV7_ERR_WORKSPACE
+    # B*H*ceil(T/16) workgroups must fit a 32-bit grid.
+    big = wk.make_desc(1 << 14, 256, 1 << 14, 64, wk.WKV7_BF16, 16)
+    assert L.wkv7_backward(ctypes.byref(big), *args, FAKE, *grads, None, FAKE, 1 << 40, None) == \
+        wk.WKV7_ERR_UNSUPPORTED
     d32 = wk.make_desc(1, 8, 1, 64, wk.WKV7_F32, 0)
     assert L.wkv7_backward(ctypes.byref(d32), *args, FAKE, *grads, None, None, 0, None) == \
         wk.WKV7_ERR_UNSUPPORTED

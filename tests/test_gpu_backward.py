@@ -28,16 +28,16 @@ def wk():
     return wk
 
 
-def _gpu_grads(wk, inp, dsT=None, use_ckpt=True, fwd_chunk=16):
+def _gpu_grads(wk, inp, dsT=None, use_tape=True, fwd_chunk=16):
     import torch
     dev = [to_dev(x, inp.dtype) for x in inp.tensors()]
     s0 = to_dev(inp.s0, "fp32") if inp.s0 is not None else None
     dy = to_dev(inp.dy, inp.dtype)
     dsT_d = to_dev(dsT, "fp32") if dsT is not None else None
-    ck = None
-    if use_ckpt:
-        _, _, ck = wk.forward(*dev, s0, chunk_len=fwd_chunk, want_state=False, want_ckpt=True)
-    g = wk.backward(*dev, dy, s0, dsT_d, ck, chunk_len=16)
+    tape = None
+    if use_tape:
+        _, _, tape = wk.forward(*dev, s0, chunk_len=fwd_chunk, want_state=False, want_tape=True)
+    g = wk.backward(*dev, dy, s0, dsT_d, tape, chunk_len=fwd_chunk)
     torch.cuda.synchronize()
     return [to_np(x) for x in g]
 
@@ -57,14 +57,15 @@ def test_bwd_ragged(wk, T):
 
 
 @pytest.mark.parametrize("fwd_chunk", [0, 16])
-def test_bwd_workspace_path_matches_ckpt_path(wk, fwd_chunk):
-    """Without checkpoints the library re-runs the forward into the workspace."""
+def test_bwd_without_tape_matches_tape_path(wk, fwd_chunk):
+    """Without a tape the library re-runs the forward (sequential or chunked) into
+    the workspace first."""
     inp = synth.generate(1, 150, 3, 64, dtype="bf16", seed=31, random_s0=True, backward=True)
-    a = _gpu_grads(wk, inp, use_ckpt=True, fwd_chunk=fwd_chunk)
-    b = _gpu_grads(wk, inp, use_ckpt=False)
+    a = _gpu_grads(wk, inp, use_tape=True, fwd_chunk=fwd_chunk)
+    b = _gpu_grads(wk, inp, use_tape=False, fwd_chunk=fwd_chunk)
     ref = oracle.backward(*inp.tensors(), inp.s0, inp.dy)
-    _check(a, ref, "ckpt")
-    _check(b, ref, "workspace")
+    _check(a, ref, "tape")
+    _check(b, ref, "re-run")
 
 
 def test_bwd_zero_initial_state_no_dsT(wk):

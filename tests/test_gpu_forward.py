@@ -25,13 +25,16 @@ def wk():
     return wk
 
 
-def _run_fwd(wk, inp, chunk_len, want_ckpt=False):
+def _run_fwd(wk, inp, chunk_len, want_tape=False):
     import torch
     dev = [to_dev(x, inp.dtype) for x in inp.tensors()]
     s0 = to_dev(inp.s0, "fp32") if inp.s0 is not None else None
-    y, sT, ck = wk.forward(*dev, s0, chunk_len=chunk_len, want_ckpt=want_ckpt)
+    y, sT, tape = wk.forward(*dev, s0, chunk_len=chunk_len, want_tape=want_tape)
     torch.cuda.synchronize()
-    return to_np(y), to_np(sT), (to_np(ck) if ck is not None else None)
+    if tape is not None:
+        B, T, H, N = inp.r.shape
+        tape = tuple(to_np(x) for x in wk.split_tape(tape, B, T, H, N))
+    return to_np(y), to_np(sT), tape
 
 
 def _check_fwd(wk, inp, chunk_len, what):
@@ -114,17 +117,25 @@ def test_chunk_fwd_1_5b_full_sampled(wk):
 # Checkpoints and edge cases
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("chunk_len", [0, 16])
-def test_checkpoints_are_block_entry_states(wk, chunk_len):
-    T = 200
-    inp = synth.generate(1, T, 2, 64, dtype="bf16", seed=9, random_s0=True)
-    _, _, ck = _run_fwd(wk, inp, chunk_len, want_ckpt=True)
-    nck = (T + 63) // 64
-    ck = ck[: 1 * 2 * nck * 64 * 64].reshape(1, 2, nck, 64, 64)
-    np.testing.assert_array_equal(ck[:, :, 0], inp.s0)
-    for c in range(1, nck):
-        _, sr = oracle.forward(*(x[:, : 64 * c] for x in inp.tensors()), inp.s0)
-        assert_close(ck[:, :, c], sr, "bf16", f"ckpt {c}")
+@pytest.mark.parametrize("dtype,chunk_len", [("bf16", 0), ("bf16", 16), ("fp32", 0)])
+def test_tape_holds_entry_states_and_removal_readouts(wk, dtype, chunk_len):
+    """The forward's tape: z_t = S_{t-1} a_t for every token and the state
+    entering every 16-token chunk (stored key-major), against the oracle's
+    prefix states."""
+    B, T, H = 1, 75, 2
+    inp = synth.generate(B, T, H, 64, dtype=dtype, seed=9, random_s0=True)
+    _, _, (z, st) = _run_fwd(wk, inp, chunk_len, want_tape=True)
+    xs = inp.tensors()
+    prefix = [inp.s0.astype(np.float64)]
+    for t in range(1, T):
+        prefix.append(oracle.forward(*(x[:, :t] for x in xs), inp.s0)[1])
+    zr = np.stack([np.einsum("bhij,bhj->bhi", prefix[t], xs[4][:, t].astype(np.float64))
+                   for t in range(T)], axis=1)
+    assert_close(z, zr, "bf16", "tape z")
+    nch = (T + 15) // 16
+    assert st.shape == (B, H, nch, 64, 64)
+    for c in range(nch):
+        assert_close(st[:, :, c], np.swapaxes(prefix[16 * c], -1, -2), "bf16", f"tape state {c}")
 
 
 def test_empty_sequence_copies_state(wk):
