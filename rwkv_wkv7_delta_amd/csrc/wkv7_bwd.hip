@@ -116,9 +116,13 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
     const int bb = bh / H, hh = bh % H;
     const int B = gridDim.x / H;
     const int tid = threadIdx.x;
-    const bool producer = tid < 256;
+    // Roles split by wave (the tests are uniform within a wave).  They are left
+    // as per-lane conditions: branching on an SGPR copy of the wave index
+    // measured several per cent slower.
+    const int wave = tid >> 6;
+    const bool producer = wave < 4;
     const int rtid = tid & 255;
-    const int lane = tid & 63, wp = rtid >> 6;
+    const int lane = tid & 63, wp = (tid >> 6) & 3;
     const int l16 = lane & 15, g = lane >> 4;
     const int col = 16 * wp + l16;
     const int nch = (T + kL - 1) / kL;
@@ -184,7 +188,7 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
         wave_sync();
         const float g0 = sm.red[wp][0][l16], g1 = sm.red[wp][1][l16];
         const float g2 = sm.red[wp][2][l16], g3 = sm.red[wp][3][l16];
-        const float before = g == 0 ? 1.f : g == 1 ? g0 : g == 2 ? g0 * g1 : (g0 * g1) * g2;
+        const float before = ((g >= 1 ? g0 : 1.f) * (g >= 2 ? g1 : 1.f)) * (g >= 3 ? g2 : 1.f);
         const float GL = ((g0 * g1) * g2) * g3;
         float at[4], rt[4], bb4[4], kb4[4];
 #pragma unroll
@@ -251,7 +255,7 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
         }
         // Accumulator registers of X fed as an A operand stand for X^T.
         const f32x4 Tc = unit_lower_inverse_C(ab, abT, g, l16);
-        if (wp == 0) {
+        if (wave == 0) {
             s.tiles[TILE_T][lane] = __builtin_bit_cast(uint2, cvt4(Tc));
             s.tiles[TILE_RB][lane] = __builtin_bit_cast(uint2, cvt4(rb));
             s.tiles[TILE_AK][lane] = __builtin_bit_cast(uint2, cvt4(ak));
@@ -475,7 +479,7 @@ __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
     }
     wave_sync();
     const float g0 = RD(0, 0), g1 = RD(0, 1), g2 = RD(0, 2), g3 = RD(0, 3);
-    const float before = g == 0 ? 1.f : g == 1 ? g0 : g == 2 ? g0 * g1 : (g0 * g1) * g2;
+    const float before = ((g >= 1 ? g0 : 1.f) * (g >= 2 ? g1 : 1.f)) * (g >= 3 ? g2 : 1.f);
     const float GL = ((g0 * g1) * g2) * g3;
     float Gt[4], Gp[4], inv[4];
     float at[4], rt[4], bh_[4], kh_[4], bbar[4], kbar[4];

@@ -19,9 +19,10 @@
 //
 // Mapping to gfx950: one workgroup of 8 waves per (b, h), split by role.
 //   Producer waves p = 0..3 build each chunk's state-independent factors:
-//     E   decay products and scaled vectors for key columns 16p..16p+15 (the
-//         running product over tokens is a prefix across the wave's four
-//         lane groups, exchanged through wave-private LDS);
+//     E   decay products and scaled vectors for key columns 16p..16p+15, in
+//         row layout (a lane per token, four columns each: 8-byte LDS
+//         accesses, the running product over tokens a DPP scan), with the
+//         operand images the consumers need turned through the matrix core;
 //     MW  the 16x16 products, the triangular inverse (every producer
 //         computes the small tiles itself instead of exchanging them) and
 //         key block p of W and Q.
@@ -32,7 +33,7 @@
 //   multiplication that reads the state straight from registers.
 // The work is software-pipelined with ONE barrier per chunk: in interval
 // `it` the producers run E(it) and MW(it-1) while the consumers run the
-// state chain of chunk it-2 and store y of chunk it-3; chunk factors pass
+// state chain of chunk it-2, storing its y (and tape) directly; chunk factors pass
 // through three rotating LDS slots.  Each role needs few enough registers for
 // two waves per SIMD, so a consumer's MFMA chain interleaves with a
 // producer's VALU work.  Raw token loads run three intervals ahead in a
@@ -49,33 +50,32 @@ namespace {
 
 constexpr int kL = 16;
 constexpr int kThreads = 512;
-// LDS row strides (bf16 elements).  A 64-wide row would be exactly one sweep
-// of the 32 four-byte banks, so the operand reads below (16 lanes on 16
-// different rows, same columns) would all hit the same banks; 144-byte and
-// 40-byte rows spread them.
+// LDS row stride (bf16 elements).  A 64-wide row would be exactly one sweep
+// of the four-byte banks, so the row reads below (16 lanes on 16 different
+// rows, same columns) would all hit the same banks; 144-byte rows spread them.
 constexpr int kRow = kN + 8;    // rows of 64 elements
-constexpr int kRowT = kL + 4;   // rows of 16 elements
 
 enum { RAW_R = 0, RAW_W = 1, RAW_K = 2, RAW_A = 3, RAW_B = 4, RAW_V = 5 };
 enum { TILE_T = 0, TILE_AK = 1, TILE_RB = 2, TILE_RK = 3 };
 
-// Everything one chunk passes from the producers to the consumers.
+// Everything one chunk passes from the producers to the consumers.  "Images"
+// are register contents stored lane by lane (8 bytes per lane, read back by
+// the same lane index), so they cost one conflict-free LDS access each way.
 struct Slot {
     bf16_t At[kL][kRow], Rt[kL][kRow], Bh[kL][kRow], Kh[kL][kRow];  // E -> MW, row-major [t][j]
-    bf16_t BbT[kN][kRowT], KbT[kN][kRowT];                          // E -> ST, [j][t]
-    bf16_t Vt[kN][kRowT];                                           // E -> ST, v as [i][t]
+    uint2 bbimg[4][64], kbimg[4][64];   // E -> ST: accumulator layout of Bb, Kb per key block
+    uint2 vimg[4][64];                  // E -> ST: accumulator layout of v per value block
     float gL[kN];                                                   // E -> ST
-    bf16_t Wm[kL][kRow], Qm[kL][kRow];                              // MW -> ST
+    bf16_t Wm[kL][kRow], Qm[kL][kRow];                              // MW -> ST, row-major [t][j]
     uint2 tiles[4][64];   // MW -> ST: A-operand register images of Tm, Aak, Arb, Ark
 };
 
 struct __align__(16) FwdSmem {
     bf16_t raw[2][6][kL][kRow];   // r, w, k, a, b, v of two chunks (bf16 bits)
     Slot sl[3];
-    bf16_t Ys[2][kL][kRow];
+    bf16_t Ys[2][kL][kRow];       // read-outs, staged in row layout
     bf16_t Zs[2][kL][kRow];       // removal read-outs, staged for the tape
     bf16_t S0s[2][kN][kRow];      // chunk entry states as [j][i], staged for the tape
-    float red[4][4][16];          // producer-private prefix scratch
 };
 
 __device__ __forceinline__ float bf2f(bf16_t x) { return __uint_as_float((uint32_t)x << 16); }
@@ -86,16 +86,12 @@ __device__ __forceinline__ bf16x8 ld8(const bf16_t* p) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
 }
 __device__ __forceinline__ bf16x8 ld4x2(const bf16_t* p) { return cat8(ld4(p), ld4(p + 16)); }
-__device__ __forceinline__ void wave_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
-// Outputs of E kept in a producer's registers for its MW one interval later.
+// Outputs of E kept in a producer's registers for its MW one interval later,
+// in row layout: lane (g, l16) holds token l16, key columns 16p + 4g .. +3.
 struct ERegs {
-    bf16x4 At;   // At[4g+q][16p+l16]: B operand of W = Tm At
-    f32x4 Rt;    // Rt[4g+q][16p+l16]: accumulator init of Q
+    bf16x4 At;
+    f32x4 Rt;
 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));   // plain SSA vector
@@ -112,9 +108,13 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
     const int bh = blockIdx.x;
     const int bb = bh / H, hh = bh % H;
     const int tid = threadIdx.x;
-    const bool producer = tid < 256;
+    // Roles split by wave (the tests are uniform within a wave).  They are left
+    // as per-lane conditions: branching on an SGPR copy of the wave index
+    // measured several per cent slower.
+    const int wave = tid >> 6;
+    const bool producer = wave < 4;
     const int rtid = tid & 255;               // index within the role
-    const int lane = tid & 63, wp = rtid >> 6;
+    const int lane = tid & 63, wp = (tid >> 6) & 3;
     const int l16 = lane & 15, g = lane >> 4;
     const int col = 16 * wp + l16;            // key column (producer) / value row (consumer)
     const int nch = (T + kL - 1) / kL;
@@ -164,54 +164,52 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
         }
     };
 
-    // ---- E (producer): decay products and scaled vectors, key columns `col` -----
+    // ---- E (producer): decay products and scaled vectors --------------------------
+    // Row layout: lane (g, l16) takes token t = l16 and key columns j0 .. j0+3,
+    // j0 = 16p + 4g, so every LDS access is 8 bytes wide and the running product
+    // over tokens is a scan along the lanes of a DPP row.
+    const int j0 = 16 * wp + 4 * g;
+    const bf16x4 ident = identity_b(g, l16);
     auto stage_E = [&](int c) __attribute__((always_inline)) -> ERegs {
         Slot& s = sm.sl[c % 3];
         const bf16_t(*Rr)[kL][kRow] = sm.raw[c & 1];
-        float R[6][4];
+        uint2 raw6[6];
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int vi = 0; vi < 6; ++vi) raw6[vi] = *reinterpret_cast<const uint2*>(&Rr[vi][l16][j0]);
+        float X[6][4];
 #pragma unroll
-            for (int vi = 0; vi < 6; ++vi) R[vi][q] = bf2f(Rr[vi][4 * g + q][col]);
-        float gp[4];
-        float run = 1.f;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            run *= R[RAW_W][q];
-            gp[q] = run;
+        for (int vi = 0; vi < 6; ++vi) {
+            X[vi][0] = __uint_as_float(raw6[vi].x << 16);
+            X[vi][1] = __uint_as_float(raw6[vi].x & 0xFFFF0000u);
+            X[vi][2] = __uint_as_float(raw6[vi].y << 16);
+            X[vi][3] = __uint_as_float(raw6[vi].y & 0xFFFF0000u);
         }
-        sm.red[wp][g][l16] = run;
-        wave_sync();
-        const float g0 = sm.red[wp][0][l16], g1 = sm.red[wp][1][l16];
-        const float g2 = sm.red[wp][2][l16], g3 = sm.red[wp][3][l16];
-        const float before = g == 0 ? 1.f : g == 1 ? g0 : g == 2 ? g0 * g1 : (g0 * g1) * g2;
-        const float GL = ((g0 * g1) * g2) * g3;
         ERegs e;
-        float at[4], bb4[4], kb4[4];
+        f32x4 at, bh4, kh4, bb4, kb4, gt;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int t = 4 * g + q;
-            const float Gt = before * gp[q];
-            const float Gp = q == 0 ? before : before * gp[q - 1];
+        for (int cc = 0; cc < 4; ++cc) {
+            const float Gt = row16_cumprod(X[RAW_W][cc]);
+            const float Gp = row16_prev(Gt, 1.f);
+            const float GL = row16_last(Gt);
             const float inv = __builtin_amdgcn_rcpf(Gt);
-            at[q] = R[RAW_A][q] * Gp;
-            const float rt = R[RAW_R][q] * Gt;
-            const float bh_ = R[RAW_B][q] * inv;
-            const float kh_ = R[RAW_K][q] * inv;
-            bb4[q] = bh_ * GL;
-            kb4[q] = kh_ * GL;
-            e.Rt[q] = rt;
-            s.At[t][col] = f2bf(at[q]);
-            s.Rt[t][col] = f2bf(rt);
-            s.Bh[t][col] = f2bf(bh_);
-            s.Kh[t][col] = f2bf(kh_);
+            gt[cc] = Gt;
+            at[cc] = X[RAW_A][cc] * Gp;
+            e.Rt[cc] = X[RAW_R][cc] * Gt;
+            bh4[cc] = X[RAW_B][cc] * inv;
+            kh4[cc] = X[RAW_K][cc] * inv;
+            bb4[cc] = bh4[cc] * GL;
+            kb4[cc] = kh4[cc] * GL;
         }
-        *reinterpret_cast<bf16x4*>(&s.BbT[col][4 * g]) = cvt4(bb4[0], bb4[1], bb4[2], bb4[3]);
-        *reinterpret_cast<bf16x4*>(&s.KbT[col][4 * g]) = cvt4(kb4[0], kb4[1], kb4[2], kb4[3]);
-        *reinterpret_cast<bf16x4*>(&s.Vt[col][4 * g]) =
-            cvt4(R[RAW_V][0], R[RAW_V][1], R[RAW_V][2], R[RAW_V][3]);
-        if (g == 0) s.gL[col] = GL;
-        e.At = cvt4(at[0], at[1], at[2], at[3]);
+        e.At = cvt4(at);
+        *reinterpret_cast<bf16x4*>(&s.At[l16][j0]) = e.At;
+        *reinterpret_cast<bf16x4*>(&s.Rt[l16][j0]) = cvt4(e.Rt);
+        *reinterpret_cast<bf16x4*>(&s.Bh[l16][j0]) = cvt4(bh4);
+        *reinterpret_cast<bf16x4*>(&s.Kh[l16][j0]) = cvt4(kh4);
+        s.bbimg[wp][lane] = __builtin_bit_cast(uint2, swap_layout(cvt4(bb4), ident));
+        s.kbimg[wp][lane] = __builtin_bit_cast(uint2, swap_layout(cvt4(kb4), ident));
+        s.vimg[wp][lane] = __builtin_bit_cast(
+            uint2, swap_layout(__builtin_bit_cast(bf16x4, raw6[RAW_V]), ident));
+        if (l16 == kL - 1) *reinterpret_cast<float4*>(&s.gL[j0]) = make_float4(gt[0], gt[1], gt[2], gt[3]);
         return e;
     };
 
@@ -252,17 +250,18 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
             rbT[q] = (m <= n) ? rbT[q] : 0.f;
             rkT[q] = (m <= n) ? rkT[q] : 0.f;
         }
-        // Tile registers of X^T fed as an A operand stand for X: Tm, Arb.
+        // Tile registers of X^T fed as an A operand stand for X: Tm, Arb.  As a B
+        // operand the registers of rbT stand for Arb^T.
         const bf16x4 Tm = cvt4(unit_lower_inverse_T(ab, abT, g, l16));
         const bf16x4 Arb = cvt4(rbT);
-        const f32x4 Wt = mfma16(Tm, e.At, zero4());              // W[t][col]
-        const f32x4 Qt = mfma16(Arb, cvt4(Wt), e.Rt);             // Q[t][col]
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            s.Wm[4 * g + q][col] = f2bf(Wt[q]);
-            s.Qm[4 * g + q][col] = f2bf(Qt[q]);
-        }
-        if (wp == 0) {
+        // Key block p of W = Tm At in accumulator layout, then W^T (Arb^T) =
+        // (Arb W)^T, whose accumulator layout is the row layout of Arb W; Q = Rt +
+        // Arb W is formed in row layout with Rt still in fp32.
+        const bf16x4 Wc = cvt4(mfma16(Tm, swap_layout(e.At, ident), zero4()));
+        const f32x4 ArbW = mfma16(Wc, Arb, zero4());
+        *reinterpret_cast<bf16x4*>(&s.Wm[l16][j0]) = swap_layout(Wc, ident);
+        *reinterpret_cast<bf16x4*>(&s.Qm[l16][j0]) = cvt4(add4(e.Rt, ArbW));
+        if (wave == 0) {
             s.tiles[TILE_T][lane] = __builtin_bit_cast(uint2, Tm);
             s.tiles[TILE_AK][lane] = __builtin_bit_cast(uint2, cvt4(akT));
             s.tiles[TILE_RB][lane] = __builtin_bit_cast(uint2, Arb);
@@ -284,7 +283,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
         in.Aak = __builtin_bit_cast(bf16x4, s.tiles[TILE_AK][lane]);
         in.Arb = __builtin_bit_cast(bf16x4, s.tiles[TILE_RB][lane]);
         in.Ark = __builtin_bit_cast(bf16x4, s.tiles[TILE_RK][lane]);
-        in.V = ld4(&s.Vt[col][4 * g]);
+        in.V = __builtin_bit_cast(bf16x4, s.vimg[wp][lane]);
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
             in.wa[k2] = ld4x2(&s.Wm[l16][32 * k2 + 4 * g]);
@@ -292,8 +291,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
         }
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
-            in.bbt[jt] = ld4(&s.BbT[16 * jt + l16][4 * g]);
-            in.kbt[jt] = ld4(&s.KbT[16 * jt + l16][4 * g]);
+            in.bbt[jt] = __builtin_bit_cast(bf16x4, s.bbimg[jt][lane]);
+            in.kbt[jt] = __builtin_bit_cast(bf16x4, s.kbimg[jt][lane]);
             in.gl[jt] = *reinterpret_cast<const float4*>(&s.gL[16 * jt + 4 * g]);
         }
         return in;
@@ -326,42 +325,37 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
             acc = mfma16(in.kbt[jt], in.V, acc);          // + H = Kb^T V
             S[jt] = mfma16(in.bbt[jt], Zb, acc);           // + Bb^T Z
         }
-        const bf16x4 Yb = cvt4(Yt);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) sm.Ys[c & 1][4 * g + q][col] = bits(Yb[q]);
+        // Outputs are staged in LDS in row layout (swap_layout: lane (g, l16)
+        // holds 8 bytes of row l16) and leave next interval as whole 128-byte
+        // rows (store_out), which HBM takes far better than 32-byte pieces.
+        const int i0 = 16 * wp + 4 * g;
+        *reinterpret_cast<bf16x4*>(&sm.Ys[c & 1][l16][i0]) = swap_layout(cvt4(Yt), ident);
         if (tape) {
+            *reinterpret_cast<bf16x4*>(&sm.Zs[c & 1][l16][i0]) = swap_layout(Zb, ident);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) sm.Zs[c & 1][4 * g + q][col] = bits(Zb[q]);
-#pragma unroll
-            for (int jt = 0; jt < 4; ++jt)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) sm.S0s[c & 1][16 * jt + 4 * g + q][col] = bits(Sb[jt][q]);
+            for (int jt = 0; jt < 4; ++jt)   // entry state as [j][i]: row layout of S^T tile jt
+                *reinterpret_cast<bf16x4*>(&sm.S0s[c & 1][16 * jt + l16][i0]) = swap_layout(Sb[jt], ident);
         }
     };
-
-    // y of chunk c (consumers): 16 tokens x 16 lanes x 8 B from the staged read-outs.
-    const int yt = rtid >> 4, yc4 = rtid & 15;
-    auto read_y = [&](int c) __attribute__((always_inline)) -> uint2 {
-        return *reinterpret_cast<const uint2*>(&sm.Ys[c & 1][yt][yc4 * 4]);
-    };
-    auto store_y = [&](int c, uint2 val) __attribute__((always_inline)) {
-        const int tt = c * kL + yt;
-        if (y && tt < T)
-            *reinterpret_cast<uint2*>(y + tok_off(bb, tt, hh, T, H) + yc4 * 4) = val;
-    };
-    // Tape of chunk c: Z rows like y; the entry state as 64 rows x 128 B, each
-    // consumer thread copying 32 bytes of row rtid / 4.
-    auto store_tape = [&](int c) __attribute__((always_inline)) {
-        const int tt = c * kL + yt;
-        if (tt < T)
-            *reinterpret_cast<uint2*>(tapeZ + tok_off(bb, tt, hh, T, H) + yc4 * 4) =
-                *reinterpret_cast<const uint2*>(&sm.Zs[c & 1][yt][yc4 * 4]);
-        if (c < nch) {
-            const int j = rtid >> 2, part = rtid & 3;
-            const uint4* src = reinterpret_cast<const uint4*>(&sm.S0s[c & 1][j][16 * part]);
-            uint4* dst = reinterpret_cast<uint4*>(tapeS + (((size_t)bh * nch + c) * kN + j) * kN + 16 * part);
-            dst[0] = src[0];
-            dst[1] = src[1];
+    // Staged outputs of chunk c to global memory; 8 consecutive threads write
+    // one 128-byte row with 16-byte stores.
+    auto store_out = [&](int c) __attribute__((always_inline)) {
+        const int row = (rtid >> 3) & 15, piece = rtid & 7;
+        const int tt = c * kL + row;
+        if (tt < T) {
+            bf16_t* base = rtid < 128 ? y : tapeZ;
+            const bf16_t(*src)[kRow] = rtid < 128 ? sm.Ys[c & 1] : sm.Zs[c & 1];
+            if (base)
+                *reinterpret_cast<uint4*>(base + tok_off(bb, tt, hh, T, H) + 8 * piece) =
+                    *reinterpret_cast<const uint4*>(&src[row][8 * piece]);
+        }
+        if (tape) {
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2) {
+                const int j = 32 * k2 + (rtid >> 3);
+                *reinterpret_cast<uint4*>(tapeS + (((size_t)bh * nch + c) * kN + j) * kN + 8 * piece) =
+                    *reinterpret_cast<const uint4*>(&sm.S0s[c & 1][j][8 * piece]);
+            }
         }
     };
 
@@ -382,8 +376,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
         }
         __syncthreads();
         // Interval it: producers E(it) and MW(it-1), stash chunk it+1 and load
-        // chunk it+4 into the ring slot it frees; consumers ST(it-2) and the y
-        // store of chunk it-3.  (A macro, not a lambda, so that the ring stays
+        // chunk it+4 into the ring slot it frees; consumers ST(it-2) with its
+        // stores.  (A macro, not a lambda, so that the ring stays
         // plain SSA values.)
 #define WKV7_FWD_INTERVAL(IT, RING)                                         \
     {                                                                       \
@@ -399,11 +393,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
         } else {                                                            \
             if (it_ >= 2) {                                                 \
                 const STIn si = read_ST(it_ - 2);                           \
-                uint2 yv = make_uint2(0u, 0u);                              \
-                if (it_ >= 3) yv = read_y(it_ - 3);                         \
                 stage_ST(it_ - 2, si);                                      \
-                if (it_ >= 3) store_y(it_ - 3, yv);                         \
-                if (tape && it_ >= 3) store_tape(it_ - 3);                  \
+                if (it_ >= 3) store_out(it_ - 3);                           \
             }                                                               \
         }                                                                   \
         __syncthreads();                                                    \

@@ -69,6 +69,24 @@ __device__ __forceinline__ float row16_sum(float x) {
     return x;
 }
 
+// Inclusive running product over the 16 lanes of each DPP row, in lane order
+// (row_shr 1, 2, 4, 8; lanes shifted in from outside the row contribute 1).
+__device__ __forceinline__ float row16_cumprod(float x) {
+    x *= __builtin_amdgcn_update_dpp(1.0f, x, 0x111, 0xF, 0xF, false);
+    x *= __builtin_amdgcn_update_dpp(1.0f, x, 0x112, 0xF, 0xF, false);
+    x *= __builtin_amdgcn_update_dpp(1.0f, x, 0x114, 0xF, 0xF, false);
+    x *= __builtin_amdgcn_update_dpp(1.0f, x, 0x118, 0xF, 0xF, false);
+    return x;
+}
+// The value of the previous lane of the row (row_shr 1); the row's first lane gets `first`.
+__device__ __forceinline__ float row16_prev(float x, float first) {
+    return __builtin_amdgcn_update_dpp(first, x, 0x111, 0xF, 0xF, false);
+}
+// Lane 15 of each row broadcast to the whole row (row_newbcast 15).
+__device__ __forceinline__ float row16_last(float x) {
+    return __builtin_amdgcn_update_dpp(0.0f, x, 0x15F, 0xF, 0xF, false);
+}
+
 __device__ __forceinline__ float dot4(float4 s, float4 q) {
     return fmaf(s.w, q.w, fmaf(s.z, q.z, fmaf(s.y, q.y, s.x * q.x)));
 }

@@ -36,22 +36,55 @@ __device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
 // (add4); the compiler does protect a vector ALU read of an MFMA result.
 __device__ __forceinline__ f32x4 add4(f32x4 a, f32x4 b) { return a + b; }
 
+// An MFMA runs across the whole wave: with part of the EXEC mask off it does
+// not compute the product of the full operands.  The compiler may sink an MFMA
+// whose result only feeds a store under a divergent branch into that branch,
+// so such results are pinned first (an empty asm that the branch cannot move).
+__device__ __forceinline__ bf16x4 pin(bf16x4 x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
 __device__ __forceinline__ f32x4 zero4() {
     f32x4 z = {0.f, 0.f, 0.f, 0.f};
     return z;
 }
 
-// fp32 -> bf16, round to nearest even, two values per v_cvt_pk_bf16_f32.
-__device__ __forceinline__ bf16x4 cvt4(f32x4 x) { return __builtin_convertvector(x, bf16x4); }
-__device__ __forceinline__ bf16x4 cvt4(float a, float b, float c, float d) {
-    const f32x4 x = {a, b, c, d};
-    return __builtin_convertvector(x, bf16x4);
+// fp32 -> bf16, round to nearest even, two values per v_cvt_pk_bf16_f32.  The
+// pairs travel as 32-bit words: converting a 4-vector directly makes the
+// compiler convert one element at a time and repack with v_perm.
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ unsigned cvt2(float a, float b) {
+    const f32x2 x = {a, b};
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(x, bf16x2));
 }
+__device__ __forceinline__ bf16x4 cvt4(float a, float b, float c, float d) {
+    const u32x2_t r = {cvt2(a, b), cvt2(c, d)};
+    return __builtin_bit_cast(bf16x4, r);
+}
+__device__ __forceinline__ bf16x4 cvt4(f32x4 x) { return cvt4(x[0], x[1], x[2], x[3]); }
 __device__ __forceinline__ bf16x8 cat8(bf16x4 lo, bf16x4 hi) {
     bf16x8 r;
     r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
     r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
     return r;
+}
+
+// The 16x16 identity as a B operand: lane (g, l16) register q is [4g+q == l16].
+__device__ __forceinline__ bf16x4 identity_b(int g, int l16) {
+    return cvt4(4 * g + 0 == l16 ? 1.f : 0.f, 4 * g + 1 == l16 ? 1.f : 0.f,
+                4 * g + 2 == l16 ? 1.f : 0.f, 4 * g + 3 == l16 ? 1.f : 0.f);
+}
+// Layout exchange of a 16x16 bf16 tile through the matrix core (exact: one
+// non-zero product per output).  The row layout of X (lane (g, l16) holds
+// X[l16][4g..4g+3], i.e. X as an A operand) and the accumulator layout of X
+// (lane (g, l16) holds X[4g..4g+3][l16]) map to each other: X A-operand times
+// I gives X's accumulator tile, and accumulator registers fed as an A operand
+// stand for X^T, so X^T times I gives the row layout of X.
+__device__ __forceinline__ bf16x4 swap_layout(bf16x4 x, bf16x4 ident) {
+    return cvt4(mfma16(x, ident, zero4()));
 }
 
 // (I - A)^-1 for a strictly lower triangular 16x16 A (so A^16 = 0) as the

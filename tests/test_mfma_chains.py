@@ -1,11 +1,15 @@
-"""Static check of the compiled kernels: no MFMA accumulator chain mixes shapes.
+"""Static checks of the compiled kernels' MFMA use (hipcc, no GPU needed).
 
-On gfx950 a v_mfma_f32_16x16x16_bf16 whose accumulator input (SrcC) was
-written by a v_mfma_f32_16x16x32_bf16 (or the reverse) needs 5 wait states
-that the compiler does not insert; the kernels keep every chain within one
-shape and join partial sums on the vector ALU.  This test compiles each HIP
-source to gfx950 assembly and walks every kernel linearly, tracking which
-registers were last written by which MFMA shape.  It needs hipcc but no GPU.
+1. No MFMA accumulator chain mixes shapes.  On gfx950 a
+   v_mfma_f32_16x16x16_bf16 whose accumulator input (SrcC) was written by a
+   v_mfma_f32_16x16x32_bf16 (or the reverse) needs 5 wait states that the
+   compiler does not insert; the kernels keep every chain within one shape and
+   join partial sums on the vector ALU.
+2. No MFMA runs under a divergent branch (between an s_and_saveexec and the
+   s_or_b64 exec that closes it): with part of EXEC off the product is wrong.
+
+Each HIP source is compiled to gfx950 assembly and every kernel is walked
+linearly.
 """
 
 import os
@@ -65,6 +69,55 @@ def mixed_shape_chains(asm: str):
     return bad
 
 
+def mfma_under_partial_exec(asm: str, allowed_depth=None):
+    """(line number, text) of every MFMA issued while more divergent regions
+    (s_and_saveexec / s_xor_saveexec ... s_or_b64 exec) are open than the
+    function may have around it.  allowed_depth maps a kernel-name fragment to
+    the number of enclosing regions that are known to be wave-uniform (a role
+    split by wave, which the compiler cannot prove uniform)."""
+    allowed_depth = allowed_depth or {}
+    bad = []
+    depth = 0
+    allow = 0
+    for n, line in enumerate(asm.splitlines(), 1):
+        t = line.strip()
+        if t.endswith("@function"):
+            depth = 0
+            allow = next((d for k, d in allowed_depth.items() if k in t), 0)
+        elif t.startswith("s_endpgm"):
+            depth = 0
+        elif t.startswith("s_and_saveexec") or t.startswith("s_xor_saveexec"):
+            depth += 1
+        elif re.match(r"s_or_b64\s+exec,\s*exec", t):
+            depth = max(0, depth - 1)
+        elif t.startswith("v_mfma") and depth > allow:
+            bad.append((n, t))
+    return bad
+
+
+# Kernels whose producer/consumer role split (by wave) encloses the MFMA code.
+ROLE_SPLIT = {"chunk_fwd_kernel": 1, "bwd_chain_kernel": 1}
+
+
+def test_scanner_flags_mfma_under_saveexec():
+    asm = "\n".join([
+        "k:",
+        "v_mfma_f32_16x16x16_bf16 v[4:7], v[0:1], v[2:3], 0",
+        "s_and_saveexec_b64 s[0:1], vcc",
+        "v_mfma_f32_16x16x16_bf16 v[4:7], v[0:1], v[2:3], 0",
+        "s_or_b64 exec, exec, s[0:1]",
+        "v_mfma_f32_16x16x16_bf16 v[4:7], v[0:1], v[2:3], 0",
+        "s_endpgm",
+    ])
+    assert [n for n, _ in mfma_under_partial_exec(asm)] == [4]
+    role = "\n".join(["k_role: ; @function", "s_and_saveexec_b64 s[0:1], vcc",
+                      "v_mfma_f32_16x16x16_bf16 v[4:7], v[0:1], v[2:3], 0",
+                      "s_and_saveexec_b64 s[2:3], s[4:5]",
+                      "v_mfma_f32_16x16x16_bf16 v[4:7], v[0:1], v[2:3], 0",
+                      "s_or_b64 exec, exec, s[2:3]", "s_or_b64 exec, exec, s[0:1]", "s_endpgm"])
+    assert [n for n, _ in mfma_under_partial_exec(role, {"k_role": 1})] == [5]
+
+
 def test_scanner_flags_a_mixed_chain():
     asm = "\n".join([
         "k:",
@@ -82,10 +135,13 @@ def test_scanner_flags_a_mixed_chain():
 @pytest.mark.skipif(shutil.which(hip_build.HIPCC) is None and not os.path.exists(hip_build.HIPCC),
                     reason="hipcc not available")
 @pytest.mark.parametrize("src", SOURCES)
-def test_no_mixed_shape_accumulator_chain(src, tmp_path):
+def test_compiled_mfma_use(src, tmp_path):
     out = tmp_path / (src + ".s")
     cmd = [hip_build.HIPCC, *hip_build.COMMON, "--offload-device-only", "-S", "-x", "hip",
            os.path.join(hip_build.CSRC, src), "-o", str(out)]
     subprocess.run(cmd, check=True, capture_output=True)
-    bad = mixed_shape_chains(out.read_text())
+    asm = out.read_text()
+    bad = mixed_shape_chains(asm)
     assert not bad, f"{src}: MFMA accumulator chains across shapes at {bad[:5]}"
+    bad = mfma_under_partial_exec(asm, ROLE_SPLIT)
+    assert not bad, f"{src}: MFMA under a divergent branch at {bad[:5]}"
