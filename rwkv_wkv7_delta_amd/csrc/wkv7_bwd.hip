@@ -39,7 +39,6 @@ namespace {
 
 constexpr int kL = 16;
 constexpr int kRow = kN + 8;    // padded LDS rows (see wkv7_chunk_fwd.hip)
-constexpr int kRowT = kL + 4;
 
 __device__ __forceinline__ float bf2f(bf16_t x) { return __uint_as_float((uint32_t)x << 16); }
 __device__ __forceinline__ bf16x4 ld4(const bf16_t* p) {
@@ -88,11 +87,13 @@ constexpr int kP1Threads = 512;
 enum { P1_R = 0, P1_W = 1, P1_K = 2, P1_A = 3, P1_B = 4, P1_DY = 5 };
 enum { TILE_T = 0, TILE_RB = 1, TILE_AK = 2, TILE_RK = 3 };
 
+// Images are register contents stored lane by lane (8 bytes per lane, read
+// back by the same lane index): one conflict-free LDS access each way.
 struct P1Slot {
     bf16_t At[kL][kRow], Rt[kL][kRow], Bh[kL][kRow], Kh[kL][kRow];  // E -> MW, [t][j]
     bf16_t Bb[kL][kRow], Kb[kL][kRow];                              // E -> chain, [t][j]
-    bf16_t AtT[kN][kRowT], RtT[kN][kRowT];                          // E -> chain, [j][t]
-    bf16_t dYt[kN][kRowT];                                          // E -> chain, dy as [i][t]
+    uint2 atimg[4][64], rtimg[4][64];   // E -> chain: accumulator layout of At, Rt per key block
+    uint2 dyimg[4][64];                 // E -> chain: accumulator layout of dy per value block
     float gL[kN];
     uint2 tiles[4][64];   // MW -> chain: A-operand register images of Tm^T, Arb^T, Aak^T, Ark^T
 };
@@ -103,7 +104,6 @@ struct __align__(16) P1Smem {
     bf16_t dXs[2][kL][kRow];      // [t][i]
     bf16_t dVs[2][kL][kRow];      // [t][i]
     bf16_t dSs[2][kN][kRow];      // the chunk's incoming adjoint as [j][i]
-    float red[4][4][16];
 };
 
 __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
@@ -168,99 +168,102 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
         }
     };
 
-    // ---- E (producer): decay products, scaled vectors, dy^T -----------------------
-    auto stage_E = [&](int c) __attribute__((always_inline)) {
-        P1Slot& s = sm.sl[slot_of(c)];
+    // ---- E (producer): decay products, scaled vectors, dy images ------------------
+    // Row layout: lane (g, l16) takes token t = l16 and key columns j0 .. j0+3,
+    // j0 = 16p + 4g (8-byte LDS accesses; the running product over tokens is a
+    // scan along the lanes of a DPP row).
+    const int j0 = 16 * wp + 4 * g;
+    const bf16x4 ident = identity_b(g, l16);
+    struct ERaw {
+        uint2 v[6];
+    };
+    auto read_E = [&](int c) __attribute__((always_inline)) -> ERaw {
         const bf16_t(*Rr)[kL][kRow] = sm.raw[c & 1];
-        float R[6][4];
+        ERaw e;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int vi = 0; vi < 6; ++vi) e.v[vi] = *reinterpret_cast<const uint2*>(&Rr[vi][l16][j0]);
+        return e;
+    };
+    auto stage_E = [&](int c, const ERaw& er) __attribute__((always_inline)) {
+        P1Slot& s = sm.sl[slot_of(c)];
+        const uint2* raw6 = er.v;
+        float X[6][4];
 #pragma unroll
-            for (int vi = 0; vi < 6; ++vi) R[vi][q] = bf2f(Rr[vi][4 * g + q][col]);
-        float gp[4];
-        float run = 1.f;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            run *= R[P1_W][q];
-            gp[q] = run;
+        for (int vi = 0; vi < 6; ++vi) {
+            X[vi][0] = __uint_as_float(raw6[vi].x << 16);
+            X[vi][1] = __uint_as_float(raw6[vi].x & 0xFFFF0000u);
+            X[vi][2] = __uint_as_float(raw6[vi].y << 16);
+            X[vi][3] = __uint_as_float(raw6[vi].y & 0xFFFF0000u);
         }
-        sm.red[wp][g][l16] = run;
-        wave_sync();
-        const float g0 = sm.red[wp][0][l16], g1 = sm.red[wp][1][l16];
-        const float g2 = sm.red[wp][2][l16], g3 = sm.red[wp][3][l16];
-        const float before = ((g >= 1 ? g0 : 1.f) * (g >= 2 ? g1 : 1.f)) * (g >= 3 ? g2 : 1.f);
-        const float GL = ((g0 * g1) * g2) * g3;
-        float at[4], rt[4], bb4[4], kb4[4];
+        f32x4 at, rt, bh4, kh4, bb4, kb4, gt;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int t = 4 * g + q;
-            const float Gt = before * gp[q];
-            const float Gp = q == 0 ? before : before * gp[q - 1];
+        for (int cc = 0; cc < 4; ++cc) {
+            const float Gt = row16_cumprod(X[P1_W][cc]);
+            const float Gp = row16_prev(Gt, 1.f);
+            const float GL = row16_last(Gt);
             const float inv = __builtin_amdgcn_rcpf(Gt);
-            at[q] = R[P1_A][q] * Gp;
-            rt[q] = R[P1_R][q] * Gt;
-            const float bh_ = R[P1_B][q] * inv;
-            const float kh_ = R[P1_K][q] * inv;
-            bb4[q] = bh_ * GL;
-            kb4[q] = kh_ * GL;
-            s.At[t][col] = f2bf(at[q]);
-            s.Rt[t][col] = f2bf(rt[q]);
-            s.Bh[t][col] = f2bf(bh_);
-            s.Kh[t][col] = f2bf(kh_);
-            s.Bb[t][col] = f2bf(bb4[q]);
-            s.Kb[t][col] = f2bf(kb4[q]);
+            gt[cc] = Gt;
+            at[cc] = X[P1_A][cc] * Gp;
+            rt[cc] = X[P1_R][cc] * Gt;
+            bh4[cc] = X[P1_B][cc] * inv;
+            kh4[cc] = X[P1_K][cc] * inv;
+            bb4[cc] = bh4[cc] * GL;
+            kb4[cc] = kh4[cc] * GL;
         }
-        *reinterpret_cast<bf16x4*>(&s.AtT[col][4 * g]) = cvt4(at[0], at[1], at[2], at[3]);
-        *reinterpret_cast<bf16x4*>(&s.RtT[col][4 * g]) = cvt4(rt[0], rt[1], rt[2], rt[3]);
-        *reinterpret_cast<bf16x4*>(&s.dYt[col][4 * g]) =
-            cvt4(R[P1_DY][0], R[P1_DY][1], R[P1_DY][2], R[P1_DY][3]);
-        if (g == 0) s.gL[col] = GL;
+        const bf16x4 atb = cvt4(at), rtb = cvt4(rt);
+        *reinterpret_cast<bf16x4*>(&s.At[l16][j0]) = atb;
+        *reinterpret_cast<bf16x4*>(&s.Rt[l16][j0]) = rtb;
+        *reinterpret_cast<bf16x4*>(&s.Bh[l16][j0]) = cvt4(bh4);
+        *reinterpret_cast<bf16x4*>(&s.Kh[l16][j0]) = cvt4(kh4);
+        *reinterpret_cast<bf16x4*>(&s.Bb[l16][j0]) = cvt4(bb4);
+        *reinterpret_cast<bf16x4*>(&s.Kb[l16][j0]) = cvt4(kb4);
+        s.atimg[wp][lane] = __builtin_bit_cast(uint2, swap_layout(atb, ident));
+        s.rtimg[wp][lane] = __builtin_bit_cast(uint2, swap_layout(rtb, ident));
+        s.dyimg[wp][lane] = __builtin_bit_cast(
+            uint2, swap_layout(__builtin_bit_cast(bf16x4, raw6[P1_DY]), ident));
+        if (l16 == kL - 1) *reinterpret_cast<float4*>(&s.gL[j0]) = make_float4(gt[0], gt[1], gt[2], gt[3]);
     };
 
-    // ---- MW (producer): 16x16 tiles and the inverse, as A-operand images ----------
+    // ---- MW (producer): one 16x16 tile per wave, as an A-operand image ------------
+    // Wave p forms tile p from the rows of X = (At or Rt) and Y = (Bh or Kh):
+    // Aab and then the inverse Tm (p = 0), Arb (1), Aak (2), Ark (3).
     struct MWIn {
-        bf16x8 av[2], rv[2], bv[2], kv[2];
+        bf16x8 xv[2], yv[2];
     };
     auto read_MW = [&](int c) __attribute__((always_inline)) -> MWIn {
         const P1Slot& s = sm.sl[slot_of(c)];
+        const bf16_t(*Xr)[kRow] = (wp & 1) ? s.Rt : s.At;
+        const bf16_t(*Yr)[kRow] = (wp & 2) ? s.Kh : s.Bh;
         MWIn in;
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
-            in.av[k2] = ld8(&s.At[l16][32 * k2 + 8 * g]);
-            in.rv[k2] = ld8(&s.Rt[l16][32 * k2 + 8 * g]);
-            in.bv[k2] = ld8(&s.Bh[l16][32 * k2 + 8 * g]);
-            in.kv[k2] = ld8(&s.Kh[l16][32 * k2 + 8 * g]);
+            in.xv[k2] = ld8(&Xr[l16][32 * k2 + 8 * g]);
+            in.yv[k2] = ld8(&Yr[l16][32 * k2 + 8 * g]);
         }
         return in;
     };
     auto stage_MW = [&](int c, const MWIn& in) __attribute__((always_inline)) {
         P1Slot& s = sm.sl[slot_of(c)];
-        f32x4 ab = zero4(), abT = zero4(), rb = zero4(), ak = zero4(), rk = zero4();
+        f32x4 P = zero4();
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-            ab = mfma32(in.av[k2], in.bv[k2], ab);    // [t][s] = At_t . Bh_s
-            abT = mfma32(in.bv[k2], in.av[k2], abT);  // [s][t]
-            rb = mfma32(in.rv[k2], in.bv[k2], rb);    // [t][s] = Rt_t . Bh_s
-            ak = mfma32(in.av[k2], in.kv[k2], ak);    // [t][s] = At_t . Kh_s
-            rk = mfma32(in.rv[k2], in.kv[k2], rk);    // [t][s] = Rt_t . Kh_s
-        }
+        for (int k2 = 0; k2 < 2; ++k2) P = mfma32(in.xv[k2], in.yv[k2], P);   // [t][s] = X_t . Y_s
+        const bool diag = (wp & 1) != 0;   // Arb, Ark keep the diagonal
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int m = 4 * g + q, n = l16;
-            ab[q] = (n < m) ? ab[q] : 0.f;
-            abT[q] = (m < n) ? abT[q] : 0.f;
-            rb[q] = (n <= m) ? rb[q] : 0.f;
-            ak[q] = (n < m) ? ak[q] : 0.f;
-            rk[q] = (n <= m) ? rk[q] : 0.f;
+            P[q] = (n < m || (diag && n == m)) ? P[q] : 0.f;
+        }
+        f32x4 img = P;
+        if (__builtin_amdgcn_readfirstlane(wp) == 0) {
+            f32x4 PT = zero4();
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2) PT = mfma32(in.yv[k2], in.xv[k2], PT);   // [s][t]
+#pragma unroll
+            for (int q = 0; q < 4; ++q) PT[q] = (4 * g + q < l16) ? PT[q] : 0.f;
+            img = unit_lower_inverse_C(P, PT, g, l16);
         }
         // Accumulator registers of X fed as an A operand stand for X^T.
-        const f32x4 Tc = unit_lower_inverse_C(ab, abT, g, l16);
-        if (wave == 0) {
-            s.tiles[TILE_T][lane] = __builtin_bit_cast(uint2, cvt4(Tc));
-            s.tiles[TILE_RB][lane] = __builtin_bit_cast(uint2, cvt4(rb));
-            s.tiles[TILE_AK][lane] = __builtin_bit_cast(uint2, cvt4(ak));
-            s.tiles[TILE_RK][lane] = __builtin_bit_cast(uint2, cvt4(rk));
-        }
+        s.tiles[wp][lane] = __builtin_bit_cast(uint2, cvt4(img));
     };
 
     // ---- chain (consumer): value rows `col` of the adjoint ------------------------
@@ -277,7 +280,7 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
         in.ArbT = __builtin_bit_cast(bf16x4, s.tiles[TILE_RB][lane]);
         in.AakT = __builtin_bit_cast(bf16x4, s.tiles[TILE_AK][lane]);
         in.ArkT = __builtin_bit_cast(bf16x4, s.tiles[TILE_RK][lane]);
-        in.dY = ld4(&s.dYt[col][4 * g]);
+        in.dY = __builtin_bit_cast(bf16x4, s.dyimg[wp][lane]);
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
             in.bb[k2] = ld4x2(&s.Bb[l16][32 * k2 + 4 * g]);
@@ -285,8 +288,8 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
         }
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
-            in.rtT[jt] = ld4(&s.RtT[16 * jt + l16][4 * g]);
-            in.atT[jt] = ld4(&s.AtT[16 * jt + l16][4 * g]);
+            in.rtT[jt] = __builtin_bit_cast(bf16x4, s.rtimg[jt][lane]);
+            in.atT[jt] = __builtin_bit_cast(bf16x4, s.atimg[jt][lane]);
             in.gl[jt] = *reinterpret_cast<const float4*>(&s.gL[16 * jt + 4 * g]);
         }
         return in;
@@ -308,16 +311,14 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
         f32x4 dV = mfma16(in.AakT, dXb, zero4());
         dV = mfma16(in.ArkT, in.dY, dV);
         const bf16x4 dVb = cvt4(add4(dV, dVk));
+        // Staged in row layout (swap_layout), 8 bytes per lane.
         const int sb = c & 1;
+        const int i0 = 16 * wp + 4 * g;
+        *reinterpret_cast<bf16x4*>(&sm.dXs[sb][l16][i0]) = swap_layout(dXb, ident);
+        *reinterpret_cast<bf16x4*>(&sm.dVs[sb][l16][i0]) = swap_layout(dVb, ident);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            sm.dXs[sb][4 * g + q][col] = bits(dXb[q]);
-            sm.dVs[sb][4 * g + q][col] = bits(dVb[q]);
-        }
-#pragma unroll
-        for (int jt = 0; jt < 4; ++jt)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) sm.dSs[sb][16 * jt + 4 * g + q][col] = bits(dSb[jt][q]);
+        for (int jt = 0; jt < 4; ++jt)   // as [j][i]: row layout of the dS^T tile of key block jt
+            *reinterpret_cast<bf16x4*>(&sm.dSs[sb][16 * jt + l16][i0]) = swap_layout(dSb[jt], ident);
         // dS0^T = G_L dS^T + Rt^T dY + At^T dX
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
@@ -331,22 +332,25 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
         }
     };
 
-    // ---- outputs of chunk c (consumers): dv and dX rows, incoming dS ---------------
-    const int yt = rtid >> 4, yc4 = rtid & 15;
+    // ---- outputs of chunk c (consumers): dv and dX rows, the chunk's exit adjoint --
+    // 8 consecutive threads write one 128-byte row with 16-byte stores.
     auto store_out = [&](int c) __attribute__((always_inline)) {
         if (c < 0) return;
         const int sb = c & 1;
-        const int tt = c * kL + yt;
+        const int row = (rtid >> 3) & 15, piece = rtid & 7;
+        const int tt = c * kL + row;
         if (tt < T) {
-            const size_t o = tok_off(bb, tt, hh, T, H) + yc4 * 4;
-            *reinterpret_cast<uint2*>(dv + o) = *reinterpret_cast<const uint2*>(&sm.dVs[sb][yt][yc4 * 4]);
-            *reinterpret_cast<uint2*>(wdX + o) = *reinterpret_cast<const uint2*>(&sm.dXs[sb][yt][yc4 * 4]);
+            bf16_t* base = rtid < 128 ? dv : wdX;
+            const bf16_t(*src)[kRow] = rtid < 128 ? sm.dVs[sb] : sm.dXs[sb];
+            *reinterpret_cast<uint4*>(base + tok_off(bb, tt, hh, T, H) + 8 * piece) =
+                *reinterpret_cast<const uint4*>(&src[row][8 * piece]);
         }
-        const int j = rtid >> 2, part = rtid & 3;
-        const uint4* src = reinterpret_cast<const uint4*>(&sm.dSs[sb][j][16 * part]);
-        uint4* dst = reinterpret_cast<uint4*>(wdS + (((size_t)bh * nch + c) * kN + j) * kN + 16 * part);
-        dst[0] = src[0];
-        dst[1] = src[1];
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+            const int j = 32 * k2 + (rtid >> 3);
+            *reinterpret_cast<uint4*>(wdS + (((size_t)bh * nch + c) * kN + j) * kN + 8 * piece) =
+                *reinterpret_cast<const uint4*>(&sm.dSs[sb][j][8 * piece]);
+        }
     };
 
     {
@@ -367,9 +371,10 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
     {                                                                          \
         const int it_ = (IT);                                                  \
         if (producer) {                                                        \
+            const ERaw er = read_E(chunk_of(it_));                             \
             MWIn mi;                                                           \
             if (it_ >= 1) mi = read_MW(chunk_of(it_ - 1));                     \
-            stage_E(chunk_of(it_));                                            \
+            stage_E(chunk_of(it_), er);                                        \
             stash_raw(chunk_of(it_ + 1), RING);                                \
             load_raw(chunk_of(it_ + 4), RING);                                 \
             if (it_ >= 1) stage_MW(chunk_of(it_ - 1), mi);                     \

@@ -11,11 +11,10 @@
 //   Aab = tril_-1(At Bh^T), Aak = tril_-1(At Kh^T),
 //   Arb = tril_0(Rt Bh^T),  Ark = tril_0(Rt Kh^T)        (L x L)
 //   Tm  = (I - Aab)^-1                                   (unit lower triangular)
-//   W   = Tm At,   Q = Rt + Arb W                        (depend on r,w,k,a,b only)
-//   U   = Tm Aak V,  Y0 = Arb U + Ark V,  H = Kb^T V     (add v, not the state)
-//   Z   = W S0^T + U                 (row t of Z is z_t = S_{t-1} a_t)
-//   Y   = Q S0^T + Y0                (row t of Y is y_t)
-//   S_L^T = diag(G_L) S0^T + H + Bb^T Z
+//   X   = At S0^T + Aak V
+//   Z   = Tm X                       (row t of Z is z_t = S_{t-1} a_t)
+//   Y   = Rt S0^T + Arb Z + Ark V    (row t of Y is y_t)
+//   S_L^T = diag(G_L) S0^T + Kb^T V + Bb^T Z
 //
 // Mapping to gfx950: one workgroup of 8 waves per (b, h), split by role.
 //   Producer waves p = 0..3 build each chunk's state-independent factors:
@@ -23,13 +22,12 @@
 //         row layout (a lane per token, four columns each: 8-byte LDS
 //         accesses, the running product over tokens a DPP scan), with the
 //         operand images the consumers need turned through the matrix core;
-//     MW  the 16x16 products, the triangular inverse (every producer
-//         computes the small tiles itself instead of exchanging them) and
-//         key block p of W and Q.
+//     MW  one 16x16 tile each: wave 0 Aab and the triangular inverse Tm,
+//         waves 1..3 Aak, Arb, Ark.
 //   Consumer waves p = 0..3 own value rows 16p..16p+15 of the state, held as
 //   S^T in four 16x16 fp32 accumulator tiles (key blocks); an accumulator
 //   tile feeds the next product directly as its B operand (wkv7_mfma.h), so
-//   every state-dependent product (U, Y0, Z, Y, the state update) is a left
+//   every state-dependent product (X, Z, Y, the state update) is a left
 //   multiplication that reads the state straight from registers.
 // The work is software-pipelined with ONE barrier per chunk: in interval
 // `it` the producers run E(it) and MW(it-1) while the consumers run the
@@ -62,12 +60,11 @@ enum { TILE_T = 0, TILE_AK = 1, TILE_RB = 2, TILE_RK = 3 };
 // are register contents stored lane by lane (8 bytes per lane, read back by
 // the same lane index), so they cost one conflict-free LDS access each way.
 struct Slot {
-    bf16_t At[kL][kRow], Rt[kL][kRow], Bh[kL][kRow], Kh[kL][kRow];  // E -> MW, row-major [t][j]
+    bf16_t At[kL][kRow], Rt[kL][kRow], Bh[kL][kRow], Kh[kL][kRow];  // E -> MW, ST: row-major [t][j]
     uint2 bbimg[4][64], kbimg[4][64];   // E -> ST: accumulator layout of Bb, Kb per key block
     uint2 vimg[4][64];                  // E -> ST: accumulator layout of v per value block
     float gL[kN];                                                   // E -> ST
-    bf16_t Wm[kL][kRow], Qm[kL][kRow];                              // MW -> ST, row-major [t][j]
-    uint2 tiles[4][64];   // MW -> ST: A-operand register images of Tm, Aak, Arb, Ark
+    uint2 tiles[4][64];   // MW -> ST: A-operand images of Tm, Aak, Arb, Ark (tile p from wave p)
 };
 
 struct __align__(16) FwdSmem {
@@ -86,13 +83,6 @@ __device__ __forceinline__ bf16x8 ld8(const bf16_t* p) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
 }
 __device__ __forceinline__ bf16x8 ld4x2(const bf16_t* p) { return cat8(ld4(p), ld4(p + 16)); }
-
-// Outputs of E kept in a producer's registers for its MW one interval later,
-// in row layout: lane (g, l16) holds token l16, key columns 16p + 4g .. +3.
-struct ERegs {
-    bf16x4 At;
-    f32x4 Rt;
-};
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));   // plain SSA vector
 struct Raw {
@@ -170,12 +160,19 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
     // over tokens is a scan along the lanes of a DPP row.
     const int j0 = 16 * wp + 4 * g;
     const bf16x4 ident = identity_b(g, l16);
-    auto stage_E = [&](int c) __attribute__((always_inline)) -> ERegs {
-        Slot& s = sm.sl[c % 3];
+    struct ERaw {
+        uint2 v[6];
+    };
+    auto read_E = [&](int c) __attribute__((always_inline)) -> ERaw {
         const bf16_t(*Rr)[kL][kRow] = sm.raw[c & 1];
-        uint2 raw6[6];
+        ERaw e;
 #pragma unroll
-        for (int vi = 0; vi < 6; ++vi) raw6[vi] = *reinterpret_cast<const uint2*>(&Rr[vi][l16][j0]);
+        for (int vi = 0; vi < 6; ++vi) e.v[vi] = *reinterpret_cast<const uint2*>(&Rr[vi][l16][j0]);
+        return e;
+    };
+    auto stage_E = [&](int c, const ERaw& er) __attribute__((always_inline)) {
+        Slot& s = sm.sl[c % 3];
+        const uint2* raw6 = er.v;
         float X[6][4];
 #pragma unroll
         for (int vi = 0; vi < 6; ++vi) {
@@ -184,8 +181,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
             X[vi][2] = __uint_as_float(raw6[vi].y << 16);
             X[vi][3] = __uint_as_float(raw6[vi].y & 0xFFFF0000u);
         }
-        ERegs e;
-        f32x4 at, bh4, kh4, bb4, kb4, gt;
+        f32x4 at, rt, bh4, kh4, bb4, kb4, gt;
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
             const float Gt = row16_cumprod(X[RAW_W][cc]);
@@ -194,15 +190,14 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
             const float inv = __builtin_amdgcn_rcpf(Gt);
             gt[cc] = Gt;
             at[cc] = X[RAW_A][cc] * Gp;
-            e.Rt[cc] = X[RAW_R][cc] * Gt;
+            rt[cc] = X[RAW_R][cc] * Gt;
             bh4[cc] = X[RAW_B][cc] * inv;
             kh4[cc] = X[RAW_K][cc] * inv;
             bb4[cc] = bh4[cc] * GL;
             kb4[cc] = kh4[cc] * GL;
         }
-        e.At = cvt4(at);
-        *reinterpret_cast<bf16x4*>(&s.At[l16][j0]) = e.At;
-        *reinterpret_cast<bf16x4*>(&s.Rt[l16][j0]) = cvt4(e.Rt);
+        *reinterpret_cast<bf16x4*>(&s.At[l16][j0]) = cvt4(at);
+        *reinterpret_cast<bf16x4*>(&s.Rt[l16][j0]) = cvt4(rt);
         *reinterpret_cast<bf16x4*>(&s.Bh[l16][j0]) = cvt4(bh4);
         *reinterpret_cast<bf16x4*>(&s.Kh[l16][j0]) = cvt4(kh4);
         s.bbimg[wp][lane] = __builtin_bit_cast(uint2, swap_layout(cvt4(bb4), ident));
@@ -210,69 +205,55 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
         s.vimg[wp][lane] = __builtin_bit_cast(
             uint2, swap_layout(__builtin_bit_cast(bf16x4, raw6[RAW_V]), ident));
         if (l16 == kL - 1) *reinterpret_cast<float4*>(&s.gL[j0]) = make_float4(gt[0], gt[1], gt[2], gt[3]);
-        return e;
     };
 
-    // ---- MW (producer): L x L tiles, inverse, key block of W and Q --------------
+    // ---- MW (producer): one 16x16 tile per wave, as an A-operand image ------------
+    // Wave p forms tile p from the rows of X = (At or Rt) and Y = (Bh or Kh):
+    // Tm (p = 0, from Aab), Aak (1), Arb (2), Ark (3).  Accumulator registers of
+    // M^T fed as an A operand stand for M, so each wave forms the transposed
+    // product [s][t] = X_t . Y_s.
     struct MWIn {
-        bf16x8 av[2], rv[2], bv[2], kv[2];
+        bf16x8 xv[2], yv[2];
     };
     auto read_MW = [&](int c) __attribute__((always_inline)) -> MWIn {
         const Slot& s = sm.sl[c % 3];
+        const bf16_t(*Xr)[kRow] = (wp & 2) ? s.Rt : s.At;
+        const bf16_t(*Yr)[kRow] = (wp & 1) ? s.Kh : s.Bh;
         MWIn in;
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
-            in.av[k2] = ld8(&s.At[l16][32 * k2 + 8 * g]);
-            in.rv[k2] = ld8(&s.Rt[l16][32 * k2 + 8 * g]);
-            in.bv[k2] = ld8(&s.Bh[l16][32 * k2 + 8 * g]);
-            in.kv[k2] = ld8(&s.Kh[l16][32 * k2 + 8 * g]);
+            in.xv[k2] = ld8(&Xr[l16][32 * k2 + 8 * g]);
+            in.yv[k2] = ld8(&Yr[l16][32 * k2 + 8 * g]);
         }
         return in;
     };
-    auto stage_MW = [&](int c, const MWIn& in, const ERegs& e) __attribute__((always_inline)) {
+    auto stage_MW = [&](int c, const MWIn& in) __attribute__((always_inline)) {
         Slot& s = sm.sl[c % 3];
-        f32x4 ab = zero4(), abT = zero4(), akT = zero4(), rbT = zero4(), rkT = zero4();
+        f32x4 PT = zero4();
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-            ab = mfma32(in.av[k2], in.bv[k2], ab);     // [t][s] = At_t . Bh_s
-            abT = mfma32(in.bv[k2], in.av[k2], abT);   // [s][t]
-            akT = mfma32(in.kv[k2], in.av[k2], akT);   // [s][t] = At_t . Kh_s
-            rbT = mfma32(in.bv[k2], in.rv[k2], rbT);   // [s][t] = Rt_t . Bh_s
-            rkT = mfma32(in.kv[k2], in.rv[k2], rkT);   // [s][t] = Rt_t . Kh_s
-        }
-        // Masks in accumulator coordinates (row m = 4g+q, column n = l16).
+        for (int k2 = 0; k2 < 2; ++k2) PT = mfma32(in.yv[k2], in.xv[k2], PT);   // [s][t]
+        const bool diag = (wp & 2) != 0;   // Arb, Ark keep the diagonal
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int m = 4 * g + q, n = l16;
-            ab[q] = (n < m) ? ab[q] : 0.f;
-            abT[q] = (m < n) ? abT[q] : 0.f;
-            akT[q] = (m < n) ? akT[q] : 0.f;
-            rbT[q] = (m <= n) ? rbT[q] : 0.f;
-            rkT[q] = (m <= n) ? rkT[q] : 0.f;
+            const int m = 4 * g + q, n = l16;   // m = s, n = t
+            PT[q] = (m < n || (diag && m == n)) ? PT[q] : 0.f;
         }
-        // Tile registers of X^T fed as an A operand stand for X: Tm, Arb.  As a B
-        // operand the registers of rbT stand for Arb^T.
-        const bf16x4 Tm = cvt4(unit_lower_inverse_T(ab, abT, g, l16));
-        const bf16x4 Arb = cvt4(rbT);
-        // Key block p of W = Tm At in accumulator layout, then W^T (Arb^T) =
-        // (Arb W)^T, whose accumulator layout is the row layout of Arb W; Q = Rt +
-        // Arb W is formed in row layout with Rt still in fp32.
-        const bf16x4 Wc = cvt4(mfma16(Tm, swap_layout(e.At, ident), zero4()));
-        const f32x4 ArbW = mfma16(Wc, Arb, zero4());
-        *reinterpret_cast<bf16x4*>(&s.Wm[l16][j0]) = swap_layout(Wc, ident);
-        *reinterpret_cast<bf16x4*>(&s.Qm[l16][j0]) = cvt4(add4(e.Rt, ArbW));
-        if (wave == 0) {
-            s.tiles[TILE_T][lane] = __builtin_bit_cast(uint2, Tm);
-            s.tiles[TILE_AK][lane] = __builtin_bit_cast(uint2, cvt4(akT));
-            s.tiles[TILE_RB][lane] = __builtin_bit_cast(uint2, Arb);
-            s.tiles[TILE_RK][lane] = __builtin_bit_cast(uint2, cvt4(rkT));
+        f32x4 img = PT;
+        if (__builtin_amdgcn_readfirstlane(wp) == 0) {
+            f32x4 P = zero4();
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2) P = mfma32(in.xv[k2], in.yv[k2], P);   // [t][s]
+#pragma unroll
+            for (int q = 0; q < 4; ++q) P[q] = (l16 < 4 * g + q) ? P[q] : 0.f;
+            img = unit_lower_inverse_T(P, PT, g, l16);
         }
+        s.tiles[wp][lane] = __builtin_bit_cast(uint2, cvt4(img));
     };
 
     // ---- ST (consumer): value-row block `col` of the state chain of chunk c -----
     struct STIn {
         bf16x4 Tm, Aak, Arb, Ark, V;
-        bf16x8 wa[2], qa[2];
+        bf16x8 at[2], rt[2];
         bf16x4 bbt[4], kbt[4];
         float4 gl[4];
     };
@@ -286,8 +267,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
         in.V = __builtin_bit_cast(bf16x4, s.vimg[wp][lane]);
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
-            in.wa[k2] = ld4x2(&s.Wm[l16][32 * k2 + 4 * g]);
-            in.qa[k2] = ld4x2(&s.Qm[l16][32 * k2 + 4 * g]);
+            in.at[k2] = ld4x2(&s.At[l16][32 * k2 + 4 * g]);
+            in.rt[k2] = ld4x2(&s.Rt[l16][32 * k2 + 4 * g]);
         }
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
@@ -298,23 +279,22 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
         return in;
     };
     auto stage_ST = [&](int c, const STIn& in) __attribute__((always_inline)) {
-        // U = Tm Aak V,  Y0 = Arb U + Ark V   (value block `col`)
-        const f32x4 AkV = mfma16(in.Aak, in.V, zero4());
-        const f32x4 U = mfma16(in.Tm, cvt4(AkV), zero4());
-        const f32x4 Y0 = mfma16(in.Ark, in.V, mfma16(in.Arb, cvt4(U), zero4()));
+        // Value block `col`: X = At S0^T + Aak V, Z = Tm X, Y = Rt S0^T + Arb Z + Ark V.
+        // The 32-deep products (over keys) and the 16-deep ones (over tokens)
+        // accumulate separately and meet on the vector ALU (add4).
         bf16x4 Sb[4];
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) Sb[jt] = cvt4(S[jt]);
-        f32x4 Z = zero4(), Yt = zero4();
+        f32x4 Xs = zero4(), Ys = zero4();
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
             const bf16x8 bs = cat8(Sb[2 * k2], Sb[2 * k2 + 1]);
-            Z = mfma32(in.wa[k2], bs, Z);
-            Yt = mfma32(in.qa[k2], bs, Yt);
+            Xs = mfma32(in.at[k2], bs, Xs);
+            Ys = mfma32(in.rt[k2], bs, Ys);
         }
-        Z = add4(Z, U);      // the 16-deep and 32-deep partial sums meet on the vector ALU
-        Yt = add4(Yt, Y0);
-        const bf16x4 Zb = cvt4(Z);
+        const f32x4 AkV = mfma16(in.Aak, in.V, zero4());
+        const bf16x4 Zb = cvt4(mfma16(in.Tm, cvt4(add4(Xs, AkV)), zero4()));
+        const f32x4 Yt = add4(Ys, mfma16(in.Ark, in.V, mfma16(in.Arb, Zb, zero4())));
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
             f32x4 acc;
@@ -364,9 +344,6 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
         // c % 3 until stashed (three named variables, never an array, so that
         // the ring is neither promoted to LDS nor to scratch).
         Raw rb0, rb1, rb2;
-        ERegs e_prev;
-        e_prev.At = cvt4(zero4());
-        e_prev.Rt = zero4();
         if (producer) {
             load_raw(0, rb0);
             load_raw(1, rb1);
@@ -383,13 +360,13 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
     {                                                                       \
         const int it_ = (IT);                                               \
         if (producer) {                                                     \
+            const ERaw er = read_E(it_);                                    \
             MWIn mi;                                                        \
             if (it_ >= 1) mi = read_MW(it_ - 1);                            \
-            const ERegs e_cur = stage_E(it_);                               \
+            stage_E(it_, er);                                               \
             stash_raw(it_ + 1, RING);                                       \
             load_raw(it_ + 4, RING);                                        \
-            if (it_ >= 1) stage_MW(it_ - 1, mi, e_prev);                    \
-            e_prev = e_cur;                                                 \
+            if (it_ >= 1) stage_MW(it_ - 1, mi);                            \
         } else {                                                            \
             if (it_ >= 2) {                                                 \
                 const STIn si = read_ST(it_ - 2);                           \
