@@ -412,13 +412,22 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
 
 constexpr int kP2Threads = 256;   // the four key blocks of one chunk
 
+// Rows of the chunk staged in LDS: the six token inputs the gradients need,
+// then dX and Z; and the chunk's entry state and exit adjoint as [j][i].
+enum { P2_R = 0, P2_W = 1, P2_K = 2, P2_A = 3, P2_B = 4, P2_DY = 5, P2_V = 6, P2_DX = 7, P2_Z = 8 };
+struct __align__(16) P2Smem {
+    bf16_t rows[9][kL][kRow];
+    bf16_t st[2][kN][kRow];      // S0, dS
+    float red[4][5][4][16];      // wave-private cross-lane-group exchange
+};
+
 __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
     int T, int H, int nch, const bf16_t* __restrict__ r, const bf16_t* __restrict__ w,
     const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const bf16_t* __restrict__ a,
     const bf16_t* __restrict__ b, const bf16_t* __restrict__ dy, const bf16_t* __restrict__ tape,
     const bf16_t* __restrict__ work, bf16_t* __restrict__ dr, bf16_t* __restrict__ dw,
     bf16_t* __restrict__ dk, bf16_t* __restrict__ da, bf16_t* __restrict__ db) {
-    __shared__ float red[4][5][4][16];   // wave-private cross-lane-group exchange
+    __shared__ P2Smem sm;
     const int c = blockIdx.x % nch;
     const int bh = blockIdx.x / nch;
     const int bb = bh / H, hh = bh % H;
@@ -432,43 +441,64 @@ __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
     const bf16_t* const tapeS = tape + (size_t)B * T * H * kN;
     const bf16_t* const wdX = work;
     const bf16_t* const wdS = work + (size_t)B * T * H * kN;
-    float* const rd = &red[wp][0][0][0];
+    float* const rd = &sm.red[wp][0][0][0];
     auto RD = [&](int kind, int gg) __attribute__((always_inline)) -> float& {
         return rd[(kind * 4 + gg) * 16 + l16];
     };
 
-    // ---- loads: this lane's key column over tokens 4g..4g+3, the chunk's rows
-    // (row l16, 8 values at 32 k2 + 8 g), and column `col` of S0 and dS --------
-    float R[5][4];
-    bool okq[4];
+    // ---- stage the chunk through LDS with whole-row loads: 8 threads per
+    // 128-byte row, 16 bytes each.  Tokens past T become padding (w = 1,
+    // everything else 0). --------------------------------------------------------
+    {
+        const int row = (tid >> 3) & 15, piece = tid & 7;
+        const int t = t0 + row;
+        const bool ok = t < T;
+        const size_t off = tok_off(bb, min(t, T - 1), hh, T, H) + 8 * piece;
+        auto stage_row = [&](int set, const bf16_t* src, unsigned pad) __attribute__((always_inline)) {
+            const uint4 x = *reinterpret_cast<const uint4*>(src + off);
+            *reinterpret_cast<uint4*>(&sm.rows[set][row][8 * piece]) = ok ? x : make_uint4(pad, pad, pad, pad);
+        };
+        if (tid < 128) {
+            stage_row(P2_R, r, 0u);
+            stage_row(P2_K, k, 0u);
+            stage_row(P2_B, b, 0u);
+            stage_row(P2_V, v, 0u);
+            stage_row(P2_Z, tapeZ, 0u);
+        } else {
+            stage_row(P2_W, w, 0x3F803F80u);
+            stage_row(P2_A, a, 0u);
+            stage_row(P2_DY, dy, 0u);
+            stage_row(P2_DX, wdX, 0u);
+        }
+        const size_t sbase = ((size_t)bh * nch + c) * kN * kN;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int t = t0 + 4 * g + q;
-        okq[q] = t < T;
-        const size_t o = tok_off(bb, min(t, T - 1), hh, T, H) + col;
-        R[0][q] = bf2f(r[o]);
-        R[1][q] = bf2f(w[o]);
-        R[2][q] = bf2f(k[o]);
-        R[3][q] = bf2f(a[o]);
-        R[4][q] = bf2f(b[o]);
+        for (int h2 = 0; h2 < 2; ++h2) {
+            const int j = (tid >> 3) + 32 * h2;
+            *reinterpret_cast<uint4*>(&sm.st[0][j][8 * piece]) =
+                *reinterpret_cast<const uint4*>(tapeS + sbase + j * kN + 8 * piece);
+            *reinterpret_cast<uint4*>(&sm.st[1][j][8 * piece]) =
+                *reinterpret_cast<const uint4*>(wdS + sbase + j * kN + 8 * piece);
+        }
     }
-    const int trow = t0 + l16;
-    const bool okrow = trow < T;
-    const size_t orow = tok_off(bb, min(trow, T - 1), hh, T, H);
+    __syncthreads();
+
+    // ---- this lane's key column over tokens 4g..4g+3, the chunk's rows (row l16,
+    // 8 values at 32 k2 + 8 g), and column `col` of S0 and dS ----------------------
+    float R[5][4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int vi = 0; vi < 5; ++vi) R[vi][q] = bf2f(sm.rows[vi][4 * g + q][col]);
     bf16x8 dXr[2], Zr[2], dYr[2], Vr[2], S0c[2], dSc[2];
-    const bf16x8 zero8 = __builtin_bit_cast(bf16x8, make_uint4(0u, 0u, 0u, 0u));
-    const size_t ocol = (((size_t)bh * nch + c) * kN + col) * kN;
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
         const int i0 = 32 * k2 + 8 * g;
-        const bf16x8 x0 = ld8(wdX + orow + i0), x1 = ld8(tapeZ + orow + i0);
-        const bf16x8 x2 = ld8(dy + orow + i0), x3 = ld8(v + orow + i0);
-        dXr[k2] = okrow ? x0 : zero8;
-        Zr[k2] = okrow ? x1 : zero8;
-        dYr[k2] = okrow ? x2 : zero8;
-        Vr[k2] = okrow ? x3 : zero8;
-        S0c[k2] = ld8(tapeS + ocol + i0);
-        dSc[k2] = ld8(wdS + ocol + i0);
+        dXr[k2] = ld8(&sm.rows[P2_DX][l16][i0]);
+        Zr[k2] = ld8(&sm.rows[P2_Z][l16][i0]);
+        dYr[k2] = ld8(&sm.rows[P2_DY][l16][i0]);
+        Vr[k2] = ld8(&sm.rows[P2_V][l16][i0]);
+        S0c[k2] = ld8(&sm.st[0][col][i0]);
+        dSc[k2] = ld8(&sm.st[1][col][i0]);
     }
 
     // ---- decay products and scaled vectors of column `col` -----------------------
@@ -477,7 +507,7 @@ __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
         float run = 1.f;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            run *= okq[q] ? R[1][q] : 1.f;
+            run *= R[P2_W][q];
             gp[q] = run;
         }
         RD(0, g) = run;
@@ -493,11 +523,10 @@ __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
         Gt[q] = before * gp[q];
         Gp[q] = q == 0 ? before : before * gp[q - 1];
         inv[q] = __builtin_amdgcn_rcpf(Gt[q]);
-        const float m = okq[q] ? 1.f : 0.f;   // padding tokens carry zeros
-        at[q] = m * R[3][q] * Gp[q];
-        rt[q] = m * R[0][q] * Gt[q];
-        bh_[q] = m * R[4][q] * inv[q];
-        kh_[q] = m * R[2][q] * inv[q];
+        at[q] = R[P2_A][q] * Gp[q];
+        rt[q] = R[P2_R][q] * Gt[q];
+        bh_[q] = R[P2_B][q] * inv[q];
+        kh_[q] = R[P2_K][q] * inv[q];
         bbar[q] = bh_[q] * GL;
         kbar[q] = kh_[q] * GL;
     }
@@ -603,15 +632,44 @@ __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
             se += e[q];
         }
     }
+
+    // ---- outputs: accumulator tiles [t][col] -> row layout (swap_layout) -> LDS
+    // rows -> whole-row stores ------------------------------------------------------
+    f32x4 o_da, o_dr, o_db, o_dk, o_dw;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        if (!okq[q]) continue;
-        const size_t o = tok_off(bb, t0 + 4 * g + q, hh, T, H) + col;
-        da[o] = f2bf(dAt[q] * Gp[q]);
-        dr[o] = f2bf(dRt[q] * Gt[q]);
-        db[o] = f2bf((dBh[q] + dBb[q] * GL) * inv[q]);
-        dk[o] = f2bf((dKh[q] + dKb[q] * GL) * inv[q]);
-        dw[o] = f2bf(dlw[q] / R[1][q]);
+        o_da[q] = dAt[q] * Gp[q];
+        o_dr[q] = dRt[q] * Gt[q];
+        o_db[q] = (dBh[q] + dBb[q] * GL) * inv[q];
+        o_dk[q] = (dKh[q] + dKb[q] * GL) * inv[q];
+        o_dw[q] = dlw[q] / R[P2_W][q];
+    }
+    const bf16x4 ident = identity_b(g, l16);
+    __syncthreads();   // every wave is done reading the staged rows
+    const int j0 = 16 * wp + 4 * g;
+    *reinterpret_cast<bf16x4*>(&sm.rows[0][l16][j0]) = swap_layout(cvt4(o_dr), ident);
+    *reinterpret_cast<bf16x4*>(&sm.rows[1][l16][j0]) = swap_layout(cvt4(o_dw), ident);
+    *reinterpret_cast<bf16x4*>(&sm.rows[2][l16][j0]) = swap_layout(cvt4(o_dk), ident);
+    *reinterpret_cast<bf16x4*>(&sm.rows[3][l16][j0]) = swap_layout(cvt4(o_da), ident);
+    *reinterpret_cast<bf16x4*>(&sm.rows[4][l16][j0]) = swap_layout(cvt4(o_db), ident);
+    __syncthreads();
+    {
+        const int row = (tid >> 3) & 15, piece = tid & 7;
+        const int t = t0 + row;
+        if (t < T) {
+            const size_t off = tok_off(bb, t, hh, T, H) + 8 * piece;
+            auto put = [&](int set, bf16_t* dst) __attribute__((always_inline)) {
+                *reinterpret_cast<uint4*>(dst + off) = *reinterpret_cast<const uint4*>(&sm.rows[set][row][8 * piece]);
+            };
+            if (tid < 128) {
+                put(0, dr);
+                put(2, dk);
+                put(4, db);
+            } else {
+                put(1, dw);
+                put(3, da);
+            }
+        }
     }
 }
 
