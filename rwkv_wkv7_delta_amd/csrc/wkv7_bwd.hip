@@ -131,7 +131,8 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
     // Interval it handles chunks from the last one down; negative chunk
     // indices are all-padding, for which every stage is the identity.
     auto chunk_of = [&](int it) __attribute__((always_inline)) { return nch - 1 - it; };
-    auto slot_of = [&](int c) __attribute__((always_inline)) { return (c + 3) % 3; };
+    // (chunk indices reach -6 in the padding intervals)
+    auto slot_of = [&](int c) __attribute__((always_inline)) { return (c + 9) % 3; };
 
     // ---- consumer adjoint: dS^T tiles, lane holds dS[col][16 jt + 4 g + q] -------
     f32x4 dSt[4];
@@ -144,6 +145,10 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
             const float4 x = *reinterpret_cast<const float4*>(base + 16 * jt + 4 * g);
             dSt[jt][0] = x.x; dSt[jt][1] = x.y; dSt[jt][2] = x.z; dSt[jt][3] = x.w;
         }
+        // Settle the loads here: left pending into the loop, the compiler
+        // guards every later use of dS with a wait on the whole memory counter,
+        // which then also waits for the previous chunk's stores.
+        __builtin_amdgcn_s_waitcnt(0);
     }
 
     // ---- producer raw loads (as in the forward; vector 5 is dy) -------------------
@@ -354,47 +359,57 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
     };
 
     {
-        Raw rb0, rb1, rb2;
+        // Intervals 0 .. nch+2 carry real work; the count is rounded up to a
+        // multiple of three for the unrolled producer loop.  The extra intervals
+        // see only all-padding chunks (negative indices: identity, nothing stored).
+        const int n_it = (nch + 5) / 3 * 3;
+        // Each role runs its own loop over the same number of intervals (one
+        // barrier each), so the compiler sees only loads on the producer side
+        // and only stores on the consumer side; with both kinds in one loop it
+        // must treat the memory counter as unordered and drain it completely.
         if (producer) {
+            Raw rb0, rb1, rb2;
             load_raw(chunk_of(0), rb0);
             load_raw(chunk_of(1), rb1);
             load_raw(chunk_of(2), rb2);
             stash_raw(chunk_of(0), rb0);
             load_raw(chunk_of(3), rb0);
-        }
-        __syncthreads();
-        // Interval it: producers E(chunk_of(it)) and MW(chunk_of(it-1)), stash
-        // chunk_of(it+1) and load chunk_of(it+4); consumers run the chain on
-        // chunk_of(it-2) and store the outputs of chunk_of(it-3).  (A macro, not
-        // a lambda, so that the register ring stays plain SSA values.)
-#define WKV7_BWD_INTERVAL(IT, RING)                                            \
+            __syncthreads();
+            // Interval it: E(chunk_of(it)) and MW(chunk_of(it-1)), stash
+            // chunk_of(it+1) and load chunk_of(it+4).  (A macro, not a lambda, so
+            // that the register ring stays plain SSA values.)  No early exit
+            // inside the unrolled body: one makes the compiler drain the whole
+            // counter before every stash.
+#define WKV7_BWD_PRODUCE(IT, RING)                                             \
     {                                                                          \
         const int it_ = (IT);                                                  \
-        if (producer) {                                                        \
-            const ERaw er = read_E(chunk_of(it_));                             \
-            MWIn mi;                                                           \
-            if (it_ >= 1) mi = read_MW(chunk_of(it_ - 1));                     \
-            stage_E(chunk_of(it_), er);                                        \
-            stash_raw(chunk_of(it_ + 1), RING);                                \
-            load_raw(chunk_of(it_ + 4), RING);                                 \
-            if (it_ >= 1) stage_MW(chunk_of(it_ - 1), mi);                     \
-        } else {                                                               \
-            if (it_ >= 2) {                                                    \
-                const CIn ci = read_C(chunk_of(it_ - 2));                      \
-                stage_C(chunk_of(it_ - 2), ci);                                \
-            }                                                                  \
-            if (it_ >= 3) store_out(chunk_of(it_ - 3));                        \
-        }                                                                      \
+        const ERaw er = read_E(chunk_of(it_));                                 \
+        MWIn mi;                                                               \
+        if (it_ >= 1) mi = read_MW(chunk_of(it_ - 1));                         \
+        stage_E(chunk_of(it_), er);                                            \
+        stash_raw(chunk_of(it_ + 1), RING);                                    \
+        load_raw(chunk_of(it_ + 4), RING);                                     \
+        if (it_ >= 1) stage_MW(chunk_of(it_ - 1), mi);                         \
         __syncthreads();                                                       \
     }
-        for (int it = 0; it <= nch + 2; it += 3) {
-            WKV7_BWD_INTERVAL(it, rb1);
-            if (it + 1 > nch + 2) break;
-            WKV7_BWD_INTERVAL(it + 1, rb2);
-            if (it + 2 > nch + 2) break;
-            WKV7_BWD_INTERVAL(it + 2, rb0);
+            for (int it = 0; it < n_it; it += 3) {
+                WKV7_BWD_PRODUCE(it, rb1);
+                WKV7_BWD_PRODUCE(it + 1, rb2);
+                WKV7_BWD_PRODUCE(it + 2, rb0);
+            }
+#undef WKV7_BWD_PRODUCE
+        } else {
+            __syncthreads();
+            // Interval it: the chain on chunk_of(it-2), the stores of chunk_of(it-3).
+            for (int it = 0; it < n_it; ++it) {
+                if (it >= 2) {
+                    const CIn ci = read_C(chunk_of(it - 2));
+                    stage_C(chunk_of(it - 2), ci);
+                }
+                if (it >= 3) store_out(chunk_of(it - 3));
+                __syncthreads();
+            }
         }
-#undef WKV7_BWD_INTERVAL
     }
 
     if (ds0 && !producer) {

@@ -125,6 +125,10 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
                 const float4 x = *reinterpret_cast<const float4*>(base + 16 * jt + 4 * g);
                 S[jt][0] = x.x; S[jt][1] = x.y; S[jt][2] = x.z; S[jt][3] = x.w;
             }
+            // Settle the loads here: left pending into the loop, the compiler
+            // guards every later use of S with a wait on the whole memory
+            // counter, which then also waits for the previous chunk's stores.
+            __builtin_amdgcn_s_waitcnt(0);
         }
     }
 
@@ -329,7 +333,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
                 *reinterpret_cast<uint4*>(base + tok_off(bb, tt, hh, T, H) + 8 * piece) =
                     *reinterpret_cast<const uint4*>(&src[row][8 * piece]);
         }
-        if (tape) {
+        if (tape && c < nch) {
 #pragma unroll
             for (int k2 = 0; k2 < 2; ++k2) {
                 const int j = 32 * k2 + (rtid >> 3);
@@ -340,51 +344,63 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
     };
 
     if (T > 0) {
-        // Producer register ring: the raw loads of chunk c live in ring slot
-        // c % 3 until stashed (three named variables, never an array, so that
-        // the ring is neither promoted to LDS nor to scratch).
-        Raw rb0, rb1, rb2;
+        // Intervals 0 .. nch+2 carry real work; the count is rounded up to a
+        // multiple of three for the unrolled producer loop.  The extra intervals
+        // see only all-padding chunks (identity on the state, nothing stored).
+        const int n_it = (nch + 5) / 3 * 3;
+        // Each role runs its own loop over the same number of intervals (one
+        // barrier each), so the compiler sees only loads on the producer side
+        // and only stores on the consumer side.  With both kinds in one loop it
+        // must treat the memory counter as unordered and wait for it to drain
+        // completely, which serialises the producers' read-ahead and makes the
+        // consumers wait for their own previous stores.
         if (producer) {
+            // Register ring: the raw loads of chunk c live in ring slot c % 3
+            // until stashed (three named variables, never an array, so that the
+            // ring is neither promoted to LDS nor to scratch).
+            Raw rb0, rb1, rb2;
             load_raw(0, rb0);
             load_raw(1, rb1);
             load_raw(2, rb2);
             stash_raw(0, rb0);
             load_raw(3, rb0);
-        }
-        __syncthreads();
-        // Interval it: producers E(it) and MW(it-1), stash chunk it+1 and load
-        // chunk it+4 into the ring slot it frees; consumers ST(it-2) with its
-        // stores.  (A macro, not a lambda, so that the ring stays
-        // plain SSA values.)
-#define WKV7_FWD_INTERVAL(IT, RING)                                         \
+            __syncthreads();
+            // Interval it: E(it) and MW(it-1), stash chunk it+1 and load chunk
+            // it+4 into the ring slot it frees.  (A macro, not a lambda, so that
+            // the ring stays plain SSA values.)
+#define WKV7_FWD_PRODUCE(IT, RING)                                          \
     {                                                                       \
         const int it_ = (IT);                                               \
-        if (producer) {                                                     \
-            const ERaw er = read_E(it_);                                    \
-            MWIn mi;                                                        \
-            if (it_ >= 1) mi = read_MW(it_ - 1);                            \
-            stage_E(it_, er);                                               \
-            stash_raw(it_ + 1, RING);                                       \
-            load_raw(it_ + 4, RING);                                        \
-            if (it_ >= 1) stage_MW(it_ - 1, mi);                            \
-        } else {                                                            \
-            if (it_ >= 2) {                                                 \
-                const STIn si = read_ST(it_ - 2);                           \
-                stage_ST(it_ - 2, si);                                      \
-                if (it_ >= 3) store_out(it_ - 3);                           \
-            }                                                               \
-        }                                                                   \
+        const ERaw er = read_E(it_);                                        \
+        MWIn mi;                                                            \
+        if (it_ >= 1) mi = read_MW(it_ - 1);                                \
+        stage_E(it_, er);                                                   \
+        stash_raw(it_ + 1, RING);                                           \
+        load_raw(it_ + 4, RING);                                            \
+        if (it_ >= 1) stage_MW(it_ - 1, mi);                                \
         __syncthreads();                                                    \
     }
-        // Ring slot of interval it is (it + 1) % 3: it = 0, 1, 2 -> rb1, rb2, rb0.
-        for (int it = 0; it <= nch + 2; it += 3) {
-            WKV7_FWD_INTERVAL(it, rb1);
-            if (it + 1 > nch + 2) break;
-            WKV7_FWD_INTERVAL(it + 1, rb2);
-            if (it + 2 > nch + 2) break;
-            WKV7_FWD_INTERVAL(it + 2, rb0);
+            // Ring slot of interval it is (it + 1) % 3: it = 0, 1, 2 -> rb1, rb2, rb0.
+            // No early exit inside the unrolled body: an exit there again makes
+            // the compiler drain the whole counter before every stash.
+            for (int it = 0; it < n_it; it += 3) {
+                WKV7_FWD_PRODUCE(it, rb1);
+                WKV7_FWD_PRODUCE(it + 1, rb2);
+                WKV7_FWD_PRODUCE(it + 2, rb0);
+            }
+#undef WKV7_FWD_PRODUCE
+        } else {
+            __syncthreads();
+            // Interval it: the state chain of chunk it-2 and the stores of chunk it-3.
+            for (int it = 0; it < n_it; ++it) {
+                if (it >= 2) {
+                    const STIn si = read_ST(it - 2);
+                    stage_ST(it - 2, si);
+                    if (it >= 3) store_out(it - 3);
+                }
+                __syncthreads();
+            }
         }
-#undef WKV7_FWD_INTERVAL
     }
 
     if (sT && !producer) {
