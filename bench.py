@@ -28,10 +28,20 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-# Algorithmic bytes per token-head (bf16 token tensors, 128 B per vector):
-FWD_BYTES_PER_TH = 7 * 128          # r, w, k, v, a, b in + y out
-BWD_BYTES_PER_TH = (7 + 6) * 128    # r, w, k, v, a, b, dy in + 6 gradients out
+# Algorithmic bytes per token-head of each kernel (bf16 token tensors, 128 B per
+# vector): the token tensors of the method that the kernel reads and writes;
+# the forward tape and the backward workspace are implementation traffic.
+FWD_BYTES_PER_TH = 7 * 128          # forward: r, w, k, v, a, b in, y out
+ADJ_BYTES_PER_TH = 7 * 128          # adjoint pass: r, w, k, a, b, dy in, dv out
+GRAD_BYTES_PER_TH = 12 * 128        # gradient pass: r, w, k, v, a, b, dy in, dr, dw, dk, da, db out
 STATE_BYTES = 64 * 64 * 4           # one fp32 state
+KERNELS = {   # kernel symbol -> (entry point that launches it alone, source, bytes per token-head)
+    "chunk_fwd_kernel": ("wkv7_forward", "wkv7_chunk_fwd.hip", FWD_BYTES_PER_TH),
+    "bwd_chain_kernel": ("wkv7_backward_adjoint", "wkv7_bwd.hip", ADJ_BYTES_PER_TH),
+    "bwd_keys_kernel": ("wkv7_backward_gradients", "wkv7_bwd.hip", GRAD_BYTES_PER_TH),
+}
+PROFILE_JSON = os.path.join(ROOT, "profiles", "hbm_traffic_fwd_bwd_2.9b.json")
+COPY_BYTES = 1 << 30                # calibration copy: 1 GiB read + 1 GiB written
 
 
 def parse():
@@ -42,6 +52,10 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true")
     p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run one plain 1 GiB device copy (for scaling HBM counters)")
+    p.add_argument("--summarize-profile", nargs=4, metavar=("KTRACE_DIR", "FETCH_DIR", "WRITE_DIR", "CMD"),
+                   help="turn rocprofv3 outputs of this script into profiles/ summaries and exit")
     return p.parse_args()
 
 
@@ -53,22 +67,108 @@ def src_digest(*names):
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel_file, digest, per_launch_units):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when the kernel source changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", "hbm_traffic_fwd_bwd_2.9b.json")
-    if not os.path.exists(path):
+def load_traffic(kernel, digest):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, or None when absent or when the kernel's source changed since."""
+    if not os.path.exists(PROFILE_JSON):
         return None
-    with open(path) as f:
+    with open(PROFILE_JSON) as f:
         rec = json.load(f)
-    k = rec.get("kernels", {}).get(kernel_file)
+    k = rec.get("kernels", {}).get(kernel)
     if not k or k.get("source_digest") != digest:
         return None
     return float(k["hbm_bytes_per_launch"])
 
 
+def _csv_rows(d, suffix):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *{suffix} under {d}")
+    with open(files[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def _short(name):
+    for k in KERNELS:
+        if f"::{k}(" in name:
+            return k
+    return None
+
+
+def summarize_profile(ktrace_dir, fetch_dir, write_dir, cmd):
+    """Write profiles/ summaries from this script's rocprofv3 runs: the kernel-trace
+    statistics and FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled by what
+    the same counter reads for the 1 GiB calibration copy."""
+    stats = {}
+    for r in _csv_rows(ktrace_dir, "kernel_stats.csv"):
+        k = _short(r["Name"])
+        if k:
+            stats[k] = {"calls": int(r["Calls"]), "avg_ns": float(r["AverageNs"]),
+                        "min_ns": float(r["MinNs"]), "max_ns": float(r["MaxNs"])}
+    counters = {}
+    for d, cname in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
+        per, copy = {}, []
+        for r in _csv_rows(d, "counter_collection.csv"):
+            if r["Counter_Name"] != cname:
+                continue
+            k = _short(r["Kernel_Name"])
+            if k:
+                per.setdefault(k, []).append(float(r["Counter_Value"]))
+            elif "neg_kernel" in r["Kernel_Name"]:
+                copy.append(float(r["Counter_Value"]))
+        if len(copy) != 1:
+            raise SystemExit(f"{cname}: expected one calibration copy, found {len(copy)}")
+        counters[cname] = {"per_kernel_kib": {k: float(np.mean(v)) for k, v in per.items()},
+                           "copy_kib": copy[0],
+                           "bytes_per_unit": COPY_BYTES / copy[0]}
+    os.makedirs(os.path.dirname(PROFILE_JSON), exist_ok=True)
+    rec = {"workload": "fwd_bwd_2.9b: B=8 T=4096 H=40 N=64 bf16, chunked L=16, bf16 tape",
+           "command": cmd,
+           "calibration": {c: {"copy_bytes": COPY_BYTES, "copy_counter_kib": v["copy_kib"],
+                               "bytes_per_counter_unit": round(v["bytes_per_unit"], 4)}
+                           for c, v in counters.items()},
+           "kernels": {}}
+    th = 8 * 4096 * 40
+    lines = ["# rocprofv3 summary: WKV7 fwd+bwd, B=8 T=4096 H=40 N=64 bf16 (2.9B-model shape)", "",
+             "Command (run from the repository root; kernel trace, then one counter pass each):", "",
+             "```", cmd, "```", "",
+             "HBM bytes = counter (KiB per dispatch) x bytes-per-unit of the 1 GiB calibration copy "
+             f"(FETCH {counters['FETCH_SIZE']['bytes_per_unit']:.1f}, "
+             f"WRITE {counters['WRITE_SIZE']['bytes_per_unit']:.1f} bytes per KiB counted).", "",
+             "| kernel | calls | avg us | min us | max us | HBM read MB | HBM write MB | "
+             "algorithmic MB | counted / algorithmic |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    for k, (entry, src, per_th) in KERNELS.items():
+        st = stats.get(k)
+        fk = counters["FETCH_SIZE"]["per_kernel_kib"].get(k)
+        wk_ = counters["WRITE_SIZE"]["per_kernel_kib"].get(k)
+        if st is None or fk is None or wk_ is None:
+            continue
+        rd = fk * counters["FETCH_SIZE"]["bytes_per_unit"]
+        wr = wk_ * counters["WRITE_SIZE"]["bytes_per_unit"]
+        alg = th * per_th
+        rec["kernels"][k] = {"entry_point": entry, "source": src, "source_digest": src_digest(src),
+                             **st, "fetch_kib": fk, "write_kib": wk_,
+                             "hbm_read_bytes": round(rd), "hbm_write_bytes": round(wr),
+                             "hbm_bytes_per_launch": round(rd + wr),
+                             "algorithmic_bytes_per_launch": alg}
+        lines.append(f"| {k} | {st['calls']} | {st['avg_ns'] / 1e3:.1f} | {st['min_ns'] / 1e3:.1f} | "
+                     f"{st['max_ns'] / 1e3:.1f} | {rd / 1e6:.0f} | {wr / 1e6:.0f} | {alg / 1e6:.0f} | "
+                     f"{(rd + wr) / alg:.2f} |")
+    with open(PROFILE_JSON, "w") as f:
+        json.dump(rec, f, indent=1)
+    with open(os.path.join(ROOT, "profiles", "kernels_fwd_bwd_2.9b.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     args = parse()
+    if args.summarize_profile:
+        summarize_profile(*args.summarize_profile)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; --gpus must be 1",
                           "gpus_requested": args.gpus}))
@@ -100,58 +200,81 @@ def main():
     ptr = [x.data_ptr() for x in ins]
     stream = torch.cuda.current_stream()
 
+    def call(name, *args):
+        st = getattr(L, name)(*args)
+        if st != 0:
+            raise RuntimeError(f"{name} status {st}")
+
     def fwd():
-        st = L.wkv7_forward(ctypes.byref(desc), *ptr, None, y.data_ptr(), None, tape.data_ptr(),
-                            stream.cuda_stream)
-        if st != 0:
-            raise RuntimeError(f"wkv7_forward status {st}")
+        call("wkv7_forward", ctypes.byref(desc), *ptr, None, y.data_ptr(), None, tape.data_ptr(),
+             stream.cuda_stream)
 
-    def bwd():
-        st = L.wkv7_backward(ctypes.byref(desc), *ptr, None, dy.data_ptr(), None,
-                             tape.data_ptr(), *[g.data_ptr() for g in grads], ds0.data_ptr(),
-                             work.data_ptr(), wsb, stream.cuda_stream)
-        if st != 0:
-            raise RuntimeError(f"wkv7_backward status {st}")
+    bargs = lambda: (ctypes.byref(desc), *ptr, None, dy.data_ptr(), None, tape.data_ptr(),
+                     *[g.data_ptr() for g in grads], ds0.data_ptr(), work.data_ptr(), wsb,
+                     stream.cuda_stream)
 
+    # wkv7_backward = wkv7_backward_adjoint + wkv7_backward_gradients; the step
+    # calls the two stages so that each kernel can be timed on its own.
+    def bwd_adjoint():
+        call("wkv7_backward_adjoint", *bargs())
+
+    def bwd_gradients():
+        call("wkv7_backward_gradients", *bargs())
+
+    stages = [("chunk_fwd_kernel", fwd), ("bwd_chain_kernel", bwd_adjoint),
+              ("bwd_keys_kernel", bwd_gradients)]
     for _ in range(args.warmup):
-        fwd()
-        bwd()
+        for _, fn in stages:
+            fn()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    if args.copy_calibration:
+        # A plain copy of known size on the same stream, so that HBM counters
+        # of a profiled run can be scaled (bytes per counted unit).
+        # torch.neg is a plain streaming elementwise kernel (a same-dtype copy_
+        # may go to a DMA engine instead of a kernel).
+        csrc = torch.empty(COPY_BYTES // 4, device=dev, dtype=torch.float32).fill_(1.0)
+        cdst = torch.empty_like(csrc)
+        torch.cuda.synchronize()
+        torch.neg(csrc, out=cdst)
+        torch.cuda.synchronize()
+        del csrc, cdst
+    # HIP events on the stream the kernels are launched on, around every launch.
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+          for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
         ev[s][0].record(stream)
-        fwd()
-        ev[s][1].record(stream)
-        bwd()
-        ev[s][2].record(stream)
+        for i, (_, fn) in enumerate(stages):
+            fn()
+            ev[s][i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    kernel_ms = {name: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in ev]))
+                 for i, (name, _) in enumerate(stages)}
     ms_per_step = wall * 1e3 / args.steps
     tokens = B * T
     value = tokens / (ms_per_step / 1e3)
 
-    # Roofline of the dominant kernel (the backward), algorithmic bytes per launch.
+    # Roofline of the dominant kernel: algorithmic bytes per launch (per token-head
+    # figure x B*T*H token-heads) over its average launch duration.
     th = B * T * H
-    bwd_bytes = th * BWD_BYTES_PER_TH
-    fwd_bytes = th * FWD_BYTES_PER_TH
-    dominant = "chunk_bwd_kernel" if bwd_ms >= fwd_ms else "chunk_fwd_kernel"
-    if dominant == "chunk_bwd_kernel":
-        dom_bytes, dom_ms, dom_file = bwd_bytes, bwd_ms, "wkv7_bwd.hip"
-    else:
-        dom_bytes, dom_ms, dom_file = fwd_bytes, fwd_ms, "wkv7_chunk_fwd.hip"
-    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    traffic = load_traffic(dom_file, src_digest(dom_file), th)
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+    per_kernel = {}
+    for name, ms in kernel_ms.items():
+        entry, src, per_th = KERNELS[name]
+        nbytes = th * per_th
+        per_kernel[name] = {"entry_point": entry, "ms": round(ms, 4),
+                            "algorithmic_bytes": nbytes,
+                            "achieved_GBs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                            "hbm_bytes_counted": load_traffic(name, src_digest(src))}
+    dominant = max(kernel_ms, key=kernel_ms.get)
+    dk = per_kernel[dominant]
+    achieved = dk["achieved_GBs"]
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": traffic, "kernel": dominant,
-                "kernel_ms": round(dom_ms, 4),
-                "fwd_kernel_ms": round(fwd_ms, 4), "bwd_kernel_ms": round(bwd_ms, 4),
-                "fwd_achieved_GBs": round(fwd_bytes / (fwd_ms * 1e-3) / 1e9, 1),
-                "algorithmic_bytes_per_launch": dom_bytes}
+                "traffic": dk["hbm_bytes_counted"], "kernel": dominant,
+                "kernel_ms": dk["ms"], "algorithmic_bytes_per_launch": dk["algorithmic_bytes"],
+                "kernels": per_kernel}
 
     out = {
         "metric": "WKV7 fwd+bwd tokens/s (H=40,N=64,T=4096) and achieved HBM GB/s / MFMA % peak",

@@ -140,6 +140,38 @@ int wkv7_backward(const wkv7_desc *desc, const void *r, const void *w, const voi
                   size_t workspace_bytes, void *stream);
 
 /*
+ * The two stages of wkv7_backward as separate calls, for callers that schedule
+ * or time them apart; both take exactly wkv7_backward's arguments, and calling
+ * wkv7_backward_adjoint then wkv7_backward_gradients on one stream with the
+ * same arguments computes what wkv7_backward computes.  `tape` is required
+ * (WKV7_ERR_INVALID_ARG when NULL and B*T*H > 0): the workspace carries the
+ * first stage's results to the second, so both calls must receive the same
+ * workspace, untouched in between.
+ *   wkv7_backward_adjoint    the sequential part: the adjoint state carried
+ *                            backwards through the chunks (the transposed
+ *                            transition of "Paper Review: RWKV-7 Goose", The
+ *                            approach), one chunk at a time.  Writes dv and
+ *                            ds0 (if not NULL) and fills the workspace with the
+ *                            adjoint entering every chunk and the per-token
+ *                            intermediate adjoint.  dr, dw, dk, da, db are not
+ *                            touched.
+ *   wkv7_backward_gradients  the parallel part: every chunk independently,
+ *                            from the tape and the workspace.  Writes dr, dw,
+ *                            dk, da, db; dv, ds0 and the workspace are not
+ *                            touched.
+ */
+int wkv7_backward_adjoint(const wkv7_desc *desc, const void *r, const void *w, const void *k,
+                          const void *v, const void *a, const void *b, const float *s0,
+                          const void *dy, const float *dsT, const void *tape, void *dr,
+                          void *dw, void *dk, void *dv, void *da, void *db, float *ds0,
+                          void *workspace, size_t workspace_bytes, void *stream);
+int wkv7_backward_gradients(const wkv7_desc *desc, const void *r, const void *w, const void *k,
+                            const void *v, const void *a, const void *b, const float *s0,
+                            const void *dy, const float *dsT, const void *tape, void *dr,
+                            void *dw, void *dk, void *dv, void *da, void *db, float *ds0,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * One token on B*H resident states, in place: constant memory and constant
  * time per token at inference (Abstract).
  *   r, w, k, v, a, b  [B][H][N] this step's inputs (dtype).

@@ -31,7 +31,8 @@ HEAD_SIZE = 64
 TAPE_CHUNK = 16
 
 EXPORTED = ("wkv7_abi_version", "wkv7_status_string", "wkv7_tape_bytes", "wkv7_workspace_bytes",
-            "wkv7_forward", "wkv7_backward", "wkv7_decode_step")
+            "wkv7_forward", "wkv7_backward", "wkv7_backward_adjoint", "wkv7_backward_gradients",
+            "wkv7_decode_step")
 
 
 class WKV7Error(RuntimeError):
@@ -72,8 +73,10 @@ def lib():
         L.wkv7_workspace_bytes.restype = Z
         L.wkv7_forward.argtypes = [D] + [P] * 6 + [P, P, P, P, P]
         L.wkv7_forward.restype = ctypes.c_int
-        L.wkv7_backward.argtypes = [D] + [P] * 6 + [P, P, P, P] + [P] * 6 + [P, P, Z, P]
-        L.wkv7_backward.restype = ctypes.c_int
+        for name in ("wkv7_backward", "wkv7_backward_adjoint", "wkv7_backward_gradients"):
+            fn = getattr(L, name)
+            fn.argtypes = [D] + [P] * 6 + [P, P, P, P] + [P] * 6 + [P, P, Z, P]
+            fn.restype = ctypes.c_int
         L.wkv7_decode_step.argtypes = [I, I, I, I] + [P] * 6 + [P, P, P]
         L.wkv7_decode_step.restype = ctypes.c_int
         _lib = L
@@ -170,12 +173,18 @@ def forward(r, w, k, v, a, b, s0=None, *, chunk_len: int = 0, want_state: bool =
     return y, sT, ck
 
 
+_STAGES = {"all": "wkv7_backward", "adjoint": "wkv7_backward_adjoint",
+           "gradients": "wkv7_backward_gradients"}
+
+
 def backward(r, w, k, v, a, b, dy, s0=None, dsT=None, tape=None, *, chunk_len: int = 16,
-             want_ds0: bool = True, workspace=None):
+             want_ds0: bool = True, workspace=None, stage: str = "all", grads=None, ds0=None):
     """Gradients of ``<dy, y> + <dsT, S_T>``: returns (dr, dw, dk, dv, da, db, ds0).
 
     ``tape`` is the one ``forward(..., want_tape=True)`` returned for the same
-    inputs, or None (the forward is then re-run inside the call).
+    inputs, or None (the forward is then re-run inside the call).  ``stage``
+    selects the whole backward ("all") or one of its two stages ("adjoint",
+    then "gradients" with the same ``workspace``, ``grads`` and ``ds0``).
     """
     torch = _torch()
     B, T, H, N = r.shape
@@ -183,19 +192,24 @@ def backward(r, w, k, v, a, b, dy, s0=None, dsT=None, tape=None, *, chunk_len: i
     _check_state(s0, (B, H, N, N))
     _check_state(dsT, (B, H, N, N))
     desc = make_desc(B, T, H, N, _dtype_code(r), chunk_len)
-    grads = [torch.empty_like(r) for _ in range(6)]
-    ds0 = torch.empty((B, H, N, N), device=r.device, dtype=torch.float32) if want_ds0 else None
+    if grads is None:
+        grads = [torch.empty_like(r) for _ in range(6)]
+    _check_tokens(grads, r.shape, r.dtype)
+    if ds0 is None and want_ds0:
+        ds0 = torch.empty((B, H, N, N), device=r.device, dtype=torch.float32)
+    _check_state(ds0, (B, H, N, N))
     wsb = workspace_bytes(desc, tape is not None)
     ws = workspace
     if ws is None:
         ws = torch.empty(max(wsb // 4, 4), device=r.device, dtype=torch.float32)
     else:
         wsb = ws.numel() * ws.element_size()
-    st = lib().wkv7_backward(ctypes.byref(desc), _ptr(r), _ptr(w), _ptr(k), _ptr(v), _ptr(a),
-                             _ptr(b), _ptr(s0), _ptr(dy), _ptr(dsT), _ptr(tape),
-                             *[_ptr(x) for x in grads], _ptr(ds0), _ptr(ws), wsb, _stream())
+    name = _STAGES[stage]
+    st = getattr(lib(), name)(ctypes.byref(desc), _ptr(r), _ptr(w), _ptr(k), _ptr(v), _ptr(a),
+                              _ptr(b), _ptr(s0), _ptr(dy), _ptr(dsT), _ptr(tape),
+                              *[_ptr(x) for x in grads], _ptr(ds0), _ptr(ws), wsb, _stream())
     if st != WKV7_OK:
-        raise WKV7Error(st, "wkv7_backward")
+        raise WKV7Error(st, name)
     return tuple(grads) + (ds0,)
 
 

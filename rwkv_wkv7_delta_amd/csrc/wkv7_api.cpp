@@ -93,11 +93,16 @@ int wkv7_forward(const wkv7_desc* desc, const void* r, const void* w, const void
     return run_forward(desc, r, w, k, v, a, b, s0, y, sT, tape, static_cast<hipStream_t>(stream));
 }
 
-int wkv7_backward(const wkv7_desc* desc, const void* r, const void* w, const void* k,
-                  const void* v, const void* a, const void* b, const float* s0, const void* dy,
-                  const float* dsT, const void* tape, void* dr, void* dw, void* dk, void* dv,
-                  void* da, void* db, float* ds0, void* workspace, size_t workspace_bytes,
-                  void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by wkv7_backward and its two stage entry points.
+int run_backward(const wkv7_desc* desc, const void* r, const void* w, const void* k,
+                 const void* v, const void* a, const void* b, const float* s0, const void* dy,
+                 const float* dsT, const void* tape, void* dr, void* dw, void* dk, void* dv,
+                 void* da, void* db, float* ds0, void* workspace, size_t workspace_bytes,
+                 void* stream, int stages) {
     int st = check_desc(desc);
     if (st != WKV7_OK) return st;
     // The backward runs the chunked adjoint on bf16 matrix cores, one workgroup
@@ -111,13 +116,18 @@ int wkv7_backward(const wkv7_desc* desc, const void* r, const void* w, const voi
         return WKV7_ERR_INVALID_ARG;
     if (!(opt(s0) && opt(dsT) && opt(tape) && opt(ds0) && opt(workspace)))
         return WKV7_ERR_INVALID_ARG;
+    // A single stage needs the forward's tape: the workspace carries the
+    // chain's results to the second stage, and a re-run would overwrite it.
+    if (stages != (wkv7::BWD_CHAIN | wkv7::BWD_KEYS) && has_tokens && !tape)
+        return WKV7_ERR_INVALID_ARG;
     const size_t need = tape_bytes_unchecked(desc) * (tape ? 1 : 2);
     if (has_tokens && (workspace == nullptr || workspace_bytes < need)) return WKV7_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if ((int64_t)desc->B * desc->H == 0) return WKV7_OK;
     if (desc->T == 0) {
         // L = <dsT, S_T> with S_T = s0: ds0 = dsT.
-        if (ds0) return from_hip(wkv7::launch_state_copy(desc->B * desc->H, dsT, ds0, s));
+        if (ds0 && (stages & wkv7::BWD_CHAIN))
+            return from_hip(wkv7::launch_state_copy(desc->B * desc->H, dsT, ds0, s));
         return WKV7_OK;
     }
     char* ws = static_cast<char*>(workspace);
@@ -130,7 +140,38 @@ int wkv7_backward(const wkv7_desc* desc, const void* r, const void* w, const voi
     }
     wkv7::BwdArgs p{desc->B, desc->T, desc->H, true, r, w, k, v, a, b, s0, dy, dsT, tape,
                     dr, dw, dk, dv, da, db, ds0, ws};
-    return from_hip(wkv7::launch_bwd(p, 16, s));
+    return from_hip(wkv7::launch_bwd(p, 16, stages, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int wkv7_backward(const wkv7_desc* desc, const void* r, const void* w, const void* k,
+                  const void* v, const void* a, const void* b, const float* s0, const void* dy,
+                  const float* dsT, const void* tape, void* dr, void* dw, void* dk, void* dv,
+                  void* da, void* db, float* ds0, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+    return run_backward(desc, r, w, k, v, a, b, s0, dy, dsT, tape, dr, dw, dk, dv, da, db, ds0,
+                        workspace, workspace_bytes, stream, wkv7::BWD_CHAIN | wkv7::BWD_KEYS);
+}
+
+int wkv7_backward_adjoint(const wkv7_desc* desc, const void* r, const void* w, const void* k,
+                          const void* v, const void* a, const void* b, const float* s0,
+                          const void* dy, const float* dsT, const void* tape, void* dr, void* dw,
+                          void* dk, void* dv, void* da, void* db, float* ds0, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+    return run_backward(desc, r, w, k, v, a, b, s0, dy, dsT, tape, dr, dw, dk, dv, da, db, ds0,
+                        workspace, workspace_bytes, stream, wkv7::BWD_CHAIN);
+}
+
+int wkv7_backward_gradients(const wkv7_desc* desc, const void* r, const void* w, const void* k,
+                            const void* v, const void* a, const void* b, const float* s0,
+                            const void* dy, const float* dsT, const void* tape, void* dr,
+                            void* dw, void* dk, void* dv, void* da, void* db, float* ds0,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+    return run_backward(desc, r, w, k, v, a, b, s0, dy, dsT, tape, dr, dw, dk, dv, da, db, ds0,
+                        workspace, workspace_bytes, stream, wkv7::BWD_KEYS);
 }
 
 int wkv7_decode_step(int32_t B, int32_t H, int32_t N, int32_t dtype, const void* r,

@@ -690,7 +690,7 @@ __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
 
 }  // namespace
 
-hipError_t launch_bwd(const BwdArgs& p, int chunk_len, hipStream_t stream) {
+hipError_t launch_bwd(const BwdArgs& p, int chunk_len, int stages, hipStream_t stream) {
     if (chunk_len != kL || !p.bf16) return hipErrorInvalidValue;
     const bf16_t* r = static_cast<const bf16_t*>(p.r);
     const bf16_t* w = static_cast<const bf16_t*>(p.w);
@@ -700,10 +700,13 @@ hipError_t launch_bwd(const BwdArgs& p, int chunk_len, hipStream_t stream) {
     const bf16_t* b = static_cast<const bf16_t*>(p.b);
     const bf16_t* dy = static_cast<const bf16_t*>(p.dy);
     bf16_t* work = static_cast<bf16_t*>(p.work);
-    bwd_chain_kernel<<<dim3(p.B * p.H), dim3(kP1Threads), 0, stream>>>(
-        p.T, p.H, r, w, k, a, b, dy, p.dsT, static_cast<bf16_t*>(p.dv), p.ds0, work);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (stages & BWD_CHAIN) {
+        bwd_chain_kernel<<<dim3(p.B * p.H), dim3(kP1Threads), 0, stream>>>(
+            p.T, p.H, r, w, k, a, b, dy, p.dsT, static_cast<bf16_t*>(p.dv), p.ds0, work);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (!(stages & BWD_KEYS)) return hipSuccess;
     const int nch = (p.T + kL - 1) / kL;
     bwd_keys_kernel<<<dim3(p.B * p.H * nch), dim3(kP2Threads), 0, stream>>>(
         p.T, p.H, nch, r, w, k, v, a, b, dy, static_cast<const bf16_t*>(p.tape), work,

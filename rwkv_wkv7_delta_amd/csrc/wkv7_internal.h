@@ -39,7 +39,10 @@ struct DecodeArgs {
 
 hipError_t launch_seq_fwd(const FwdArgs& p, hipStream_t stream);
 hipError_t launch_chunk_fwd(const FwdArgs& p, int chunk_len, hipStream_t stream);
-hipError_t launch_bwd(const BwdArgs& p, int chunk_len, hipStream_t stream);
+// stages: bit 0 = the adjoint chain (dv, ds0, workspace), bit 1 = the per-key
+// gradients (dr, dw, dk, da, db; reads the workspace the chain wrote).
+enum { BWD_CHAIN = 1, BWD_KEYS = 2 };
+hipError_t launch_bwd(const BwdArgs& p, int chunk_len, int stages, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& p, hipStream_t stream);
 hipError_t launch_state_copy(int BH, const float* s0, float* sT, hipStream_t stream);
 

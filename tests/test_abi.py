@@ -105,6 +105,27 @@ def test_backward_validation(L):
     assert L.wkv7_backward(ctypes.byref(d0), *args, FAKE, *grads, None, None, 0, None) == wk.WKV7_OK
 
 
+def test_backward_stage_validation(L):
+    """The two stage entry points validate like wkv7_backward and need a tape."""
+    d = wk.make_desc(1, 8, 1, 64, wk.WKV7_BF16, 16)
+    args = [FAKE] * 6 + [None, FAKE, None]
+    grads = [FAKE] * 6
+    need = wk.workspace_bytes(d, True)
+    for name in ("wkv7_backward_adjoint", "wkv7_backward_gradients"):
+        f = getattr(L, name)
+        assert f(ctypes.byref(d), *args, None, *grads, None, FAKE, 1 << 30, None) == \
+            wk.WKV7_ERR_INVALID_ARG, name
+        assert f(ctypes.byref(d), *args, FAKE, *grads, None, FAKE, need - 16, None) == \
+            wk.WKV7_ERR_WORKSPACE, name
+        assert f(ctypes.byref(d), *args, FAKE, *[FAKE] * 5, None, None, FAKE, need, None) == \
+            wk.WKV7_ERR_INVALID_ARG, name
+        d32 = wk.make_desc(1, 8, 1, 64, wk.WKV7_F32, 0)
+        assert f(ctypes.byref(d32), *args, FAKE, *grads, None, FAKE, need, None) == \
+            wk.WKV7_ERR_UNSUPPORTED, name
+        d0 = wk.make_desc(0, 8, 1, 64, wk.WKV7_BF16, 16)
+        assert f(ctypes.byref(d0), *args, None, *grads, None, None, 0, None) == wk.WKV7_OK, name
+
+
 def test_decode_validation(L):
     f = L.wkv7_decode_step
     assert f(1, 1, 32, wk.WKV7_BF16, *[FAKE] * 8, None) == wk.WKV7_ERR_UNSUPPORTED

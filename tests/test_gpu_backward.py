@@ -56,6 +56,33 @@ def test_bwd_ragged(wk, T):
     _check(got, ref, f"T={T}")
 
 
+def test_bwd_stages_compose_to_backward(wk):
+    """wkv7_backward_adjoint then wkv7_backward_gradients == wkv7_backward, bit for bit
+    (same kernels, same inputs), and each stage writes only its own outputs."""
+    import torch
+    inp = synth.generate(2, 150, 3, 64, dtype="bf16", seed=77, random_s0=True, backward=True)
+    dev = [to_dev(x, "bf16") for x in inp.tensors()]
+    s0 = to_dev(inp.s0, "fp32")
+    dy = to_dev(inp.dy, "bf16")
+    _, _, tape = wk.forward(*dev, s0, chunk_len=16, want_state=False, want_tape=True)
+    whole = wk.backward(*dev, dy, s0, None, tape)
+    sentinel = torch.tensor(1234.0, dtype=torch.bfloat16)
+    grads = [torch.full_like(dev[0], 1234.0) for _ in range(6)]
+    ds0 = torch.full_like(s0, 1234.0)
+    desc = wk.make_desc(2, 150, 3, 64, wk.WKV7_BF16, 16)
+    ws = torch.empty(wk.workspace_bytes(desc, True) // 4, device=s0.device)
+    wk.backward(*dev, dy, s0, None, tape, workspace=ws, stage="adjoint", grads=grads, ds0=ds0)
+    torch.cuda.synchronize()
+    for i in (0, 1, 2, 4, 5):   # dr, dw, dk, da, db untouched by the first stage
+        assert bool((grads[i].cpu() == sentinel).all()), NAMES[i]
+    assert torch.equal(grads[3], whole[3]) and torch.equal(ds0, whole[6])
+    wk.backward(*dev, dy, s0, None, tape, workspace=ws, stage="gradients", grads=grads, ds0=ds0)
+    torch.cuda.synchronize()
+    for i in range(6):
+        assert torch.equal(grads[i], whole[i]), NAMES[i]
+    assert torch.equal(ds0, whole[6])
+
+
 @pytest.mark.parametrize("fwd_chunk", [0, 16])
 def test_bwd_without_tape_matches_tape_path(wk, fwd_chunk):
     """Without a tape the library re-runs the forward (sequential or chunked) into
