@@ -47,7 +47,7 @@ namespace wkv7 {
 namespace {
 
 constexpr int kL = 16;
-constexpr int kThreads = 512;
+constexpr int kThreads = 576;   // 4 producer, 4 consumer waves, 1 inverse wave
 // LDS row stride (bf16 elements).  A 64-wide row would be exactly one sweep
 // of the four-byte banks, so the row reads below (16 lanes on 16 different
 // rows, same columns) would all hit the same banks; 144-byte rows spread them.
@@ -103,6 +103,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
     // measured several per cent slower.
     const int wave = tid >> 6;
     const bool producer = wave < 4;
+    const bool consumer = wave >= 4 && wave < 8;
+    const bool inverter = wave == 8;
     const int rtid = tid & 255;               // index within the role
     const int lane = tid & 63, wp = (tid >> 6) & 3;
     const int l16 = lane & 15, g = lane >> 4;
@@ -117,7 +119,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
     f32x4 S[4];
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt) S[jt] = zero4();
-    if (!producer) {
+    if (consumer) {
         if (s0) {
             const float* base = s0 + ((size_t)bh * kN + col) * kN;
 #pragma unroll
@@ -242,16 +244,31 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
             const int m = 4 * g + q, n = l16;   // m = s, n = t
             PT[q] = (m < n || (diag && m == n)) ? PT[q] : 0.f;
         }
-        f32x4 img = PT;
-        if (__builtin_amdgcn_readfirstlane(wp) == 0) {
-            f32x4 P = zero4();
+        s.tiles[wp][lane] = __builtin_bit_cast(uint2, cvt4(PT));
+    };
+    // ---- INV (inverse wave): Aab and Tm = (I - Aab)^-1 for tile 0 ----------------
+    // Wave 8 forms Aab from At and Bh (as MW does with wp = 0) and inverts it,
+    // so the long dependent MFMA chain of the inverse leaves the producers.
+    auto stage_INV = [&](int c) __attribute__((always_inline)) {
+        Slot& s = sm.sl[c % 3];
+        bf16x8 xv[2], yv[2];
 #pragma unroll
-            for (int k2 = 0; k2 < 2; ++k2) P = mfma32(in.xv[k2], in.yv[k2], P);   // [t][s]
-#pragma unroll
-            for (int q = 0; q < 4; ++q) P[q] = (l16 < 4 * g + q) ? P[q] : 0.f;
-            img = unit_lower_inverse_T(P, PT, g, l16);
+        for (int k2 = 0; k2 < 2; ++k2) {
+            xv[k2] = ld8(&s.At[l16][32 * k2 + 8 * g]);
+            yv[k2] = ld8(&s.Bh[l16][32 * k2 + 8 * g]);
         }
-        s.tiles[wp][lane] = __builtin_bit_cast(uint2, cvt4(img));
+        f32x4 P = zero4(), PT = zero4();
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+            PT = mfma32(yv[k2], xv[k2], PT);   // [s][t]
+            P = mfma32(xv[k2], yv[k2], P);     // [t][s]
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            PT[q] = (4 * g + q < l16) ? PT[q] : 0.f;
+            P[q] = (l16 < 4 * g + q) ? P[q] : 0.f;
+        }
+        s.tiles[TILE_T][lane] = __builtin_bit_cast(uint2, cvt4(unit_lower_inverse_T(P, PT, g, l16)));
     };
 
     // ---- ST (consumer): value-row block `col` of the state chain of chunk c -----
@@ -373,11 +390,11 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
         const int it_ = (IT);                                               \
         const ERaw er = read_E(it_);                                        \
         MWIn mi;                                                            \
-        if (it_ >= 1) mi = read_MW(it_ - 1);                                \
+        if (it_ >= 1 && wp != 0) mi = read_MW(it_ - 1);                     \
         stage_E(it_, er);                                                   \
         stash_raw(it_ + 1, RING);                                           \
         load_raw(it_ + 4, RING);                                            \
-        if (it_ >= 1) stage_MW(it_ - 1, mi);                                \
+        if (it_ >= 1 && wp != 0) stage_MW(it_ - 1, mi);                     \
         __syncthreads();                                                    \
     }
             // Ring slot of interval it is (it + 1) % 3: it = 0, 1, 2 -> rb1, rb2, rb0.
@@ -389,6 +406,14 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
                 WKV7_FWD_PRODUCE(it + 2, rb0);
             }
 #undef WKV7_FWD_PRODUCE
+        } else if (inverter) {
+            __syncthreads();
+            // Interval it: the inverse of chunk it-1 (after E(it-1), read by the
+            // consumers' chain in interval it+1).
+            for (int it = 0; it < n_it; ++it) {
+                if (it >= 1) stage_INV(it - 1);
+                __syncthreads();
+            }
         } else {
             __syncthreads();
             // Interval it: the state chain of chunk it-2 and the stores of chunk it-3.
@@ -403,7 +428,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
         }
     }
 
-    if (sT && !producer) {
+    if (sT && consumer) {
         float* dst = sT + ((size_t)bh * kN + col) * kN;
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt)
