@@ -22,9 +22,9 @@
 // passes:
 //   pass 1 (one workgroup per head, chunks last to first): the adjoint chain,
 //     with the forward's producer/consumer structure -- producers rebuild the
-//     chunk's decay products, scaled vectors, 16x16 tiles and inverse;
-//     consumers own 16 value rows each of dS^T in accumulator tiles and emit
-//     dv, dX and the chunk's incoming dS;
+//     chunk's decay products, scaled vectors and 16x16 tiles, a ninth wave the
+//     triangular inverse; consumers own 16 value rows each of dS^T in
+//     accumulator tiles and emit dv, dX and the chunk's incoming dS;
 //   pass 2 (one independent wave per chunk and key block, no barriers): every
 //     per-key gradient, from pass 1's dX and dS and the forward's tape (entry
 //     states S0 and read-outs Z).
@@ -83,7 +83,7 @@ struct Raw {
 // Pass 1: the adjoint chain.
 // =============================================================================
 
-constexpr int kP1Threads = 512;
+constexpr int kP1Threads = 576;   // 4 producer, 4 consumer waves, 1 inverse wave
 enum { P1_R = 0, P1_W = 1, P1_K = 2, P1_A = 3, P1_B = 4, P1_DY = 5 };
 enum { TILE_T = 0, TILE_RB = 1, TILE_AK = 2, TILE_RK = 3 };
 
@@ -121,6 +121,8 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
     // measured several per cent slower.
     const int wave = tid >> 6;
     const bool producer = wave < 4;
+    const bool consumer = wave >= 4 && wave < 8;
+    const bool inverter = wave == 8;
     const int rtid = tid & 255;
     const int lane = tid & 63, wp = (tid >> 6) & 3;
     const int l16 = lane & 15, g = lane >> 4;
@@ -138,7 +140,7 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
     f32x4 dSt[4];
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt) dSt[jt] = zero4();
-    if (!producer && dsT) {
+    if (consumer && dsT) {
         const float* base = dsT + ((size_t)bh * kN + col) * kN;
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
@@ -230,8 +232,9 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
     };
 
     // ---- MW (producer): one 16x16 tile per wave, as an A-operand image ------------
-    // Wave p forms tile p from the rows of X = (At or Rt) and Y = (Bh or Kh):
-    // Aab and then the inverse Tm (p = 0), Arb (1), Aak (2), Ark (3).
+    // Wave p = 1..3 forms tile p from the rows of X = (At or Rt) and Y = (Bh or
+    // Kh): Arb (1), Aak (2), Ark (3); tile 0 (Aab, then its inverse Tm) comes
+    // from the inverse wave.
     struct MWIn {
         bf16x8 xv[2], yv[2];
     };
@@ -258,17 +261,32 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
             const int m = 4 * g + q, n = l16;
             P[q] = (n < m || (diag && n == m)) ? P[q] : 0.f;
         }
-        f32x4 img = P;
-        if (__builtin_amdgcn_readfirstlane(wp) == 0) {
-            f32x4 PT = zero4();
-#pragma unroll
-            for (int k2 = 0; k2 < 2; ++k2) PT = mfma32(in.yv[k2], in.xv[k2], PT);   // [s][t]
-#pragma unroll
-            for (int q = 0; q < 4; ++q) PT[q] = (4 * g + q < l16) ? PT[q] : 0.f;
-            img = unit_lower_inverse_C(P, PT, g, l16);
-        }
         // Accumulator registers of X fed as an A operand stand for X^T.
-        s.tiles[wp][lane] = __builtin_bit_cast(uint2, cvt4(img));
+        s.tiles[wp][lane] = __builtin_bit_cast(uint2, cvt4(P));
+    };
+    // ---- INV (inverse wave): Aab and Tm = (I - Aab)^-1 for tile 0 ----------------
+    // Wave 8 forms Aab from At and Bh (as MW would with wp = 0) and inverts it,
+    // keeping the long dependent MFMA chain of the inverse off the producers.
+    auto stage_INV = [&](int c) __attribute__((always_inline)) {
+        P1Slot& s = sm.sl[slot_of(c)];
+        bf16x8 xv[2], yv[2];
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+            xv[k2] = ld8(&s.At[l16][32 * k2 + 8 * g]);
+            yv[k2] = ld8(&s.Bh[l16][32 * k2 + 8 * g]);
+        }
+        f32x4 P = zero4(), PT = zero4();
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+            P = mfma32(xv[k2], yv[k2], P);     // [t][s]
+            PT = mfma32(yv[k2], xv[k2], PT);   // [s][t]
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            P[q] = (l16 < 4 * g + q) ? P[q] : 0.f;
+            PT[q] = (4 * g + q < l16) ? PT[q] : 0.f;
+        }
+        s.tiles[TILE_T][lane] = __builtin_bit_cast(uint2, cvt4(unit_lower_inverse_C(P, PT, g, l16)));
     };
 
     // ---- chain (consumer): value rows `col` of the adjoint ------------------------
@@ -385,11 +403,11 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
         const int it_ = (IT);                                                  \
         const ERaw er = read_E(chunk_of(it_));                                 \
         MWIn mi;                                                               \
-        if (it_ >= 1) mi = read_MW(chunk_of(it_ - 1));                         \
+        if (it_ >= 1 && wp != 0) mi = read_MW(chunk_of(it_ - 1));              \
         stage_E(chunk_of(it_), er);                                            \
         stash_raw(chunk_of(it_ + 1), RING);                                    \
         load_raw(chunk_of(it_ + 4), RING);                                     \
-        if (it_ >= 1) stage_MW(chunk_of(it_ - 1), mi);                         \
+        if (it_ >= 1 && wp != 0) stage_MW(chunk_of(it_ - 1), mi);              \
         __syncthreads();                                                       \
     }
             for (int it = 0; it < n_it; it += 3) {
@@ -398,6 +416,14 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
                 WKV7_BWD_PRODUCE(it + 2, rb0);
             }
 #undef WKV7_BWD_PRODUCE
+        } else if (inverter) {
+            __syncthreads();
+            // Interval it: the inverse of chunk_of(it-1), read by the chain in
+            // interval it+1.
+            for (int it = 0; it < n_it; ++it) {
+                if (it >= 1) stage_INV(chunk_of(it - 1));
+                __syncthreads();
+            }
         } else {
             __syncthreads();
             // Interval it: the chain on chunk_of(it-2), the stores of chunk_of(it-3).
@@ -412,7 +438,7 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
         }
     }
 
-    if (ds0 && !producer) {
+    if (ds0 && consumer) {
         float* dst = ds0 + ((size_t)bh * kN + col) * kN;
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt)

@@ -16,14 +16,15 @@
 //   Y   = Rt S0^T + Arb Z + Ark V    (row t of Y is y_t)
 //   S_L^T = diag(G_L) S0^T + Kb^T V + Bb^T Z
 //
-// Mapping to gfx950: one workgroup of 8 waves per (b, h), split by role.
+// Mapping to gfx950: one workgroup of 9 waves per (b, h), split by role.
 //   Producer waves p = 0..3 build each chunk's state-independent factors:
 //     E   decay products and scaled vectors for key columns 16p..16p+15, in
 //         row layout (a lane per token, four columns each: 8-byte LDS
 //         accesses, the running product over tokens a DPP scan), with the
 //         operand images the consumers need turned through the matrix core;
-//     MW  one 16x16 tile each: wave 0 Aab and the triangular inverse Tm,
-//         waves 1..3 Aak, Arb, Ark.
+//     MW  one 16x16 tile each on waves 1..3: Aak, Arb, Ark.
+//   A ninth wave forms Aab and its triangular inverse Tm (a long chain of
+//   dependent matrix-core products, kept off the producers' path).
 //   Consumer waves p = 0..3 own value rows 16p..16p+15 of the state, held as
 //   S^T in four 16x16 fp32 accumulator tiles (key blocks); an accumulator
 //   tile feeds the next product directly as its B operand (wkv7_mfma.h), so
