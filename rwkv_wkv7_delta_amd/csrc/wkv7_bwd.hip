@@ -417,6 +417,7 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
             }
 #undef WKV7_BWD_PRODUCE
         } else if (inverter) {
+            __builtin_amdgcn_s_setprio(2);
             __syncthreads();
             // Interval it: the inverse of chunk_of(it-1), read by the chain in
             // interval it+1.
@@ -425,6 +426,9 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
                 __syncthreads();
             }
         } else {
+            // The chain is the critical path: its waves issue first (then the
+            // inverse wave, then the producers) when several are ready.
+            __builtin_amdgcn_s_setprio(3);
             __syncthreads();
             // Interval it: the chain on chunk_of(it-2), the stores of chunk_of(it-3).
             for (int it = 0; it < n_it; ++it) {

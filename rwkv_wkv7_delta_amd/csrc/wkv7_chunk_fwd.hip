@@ -408,6 +408,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
             }
 #undef WKV7_FWD_PRODUCE
         } else if (inverter) {
+            __builtin_amdgcn_s_setprio(2);
             __syncthreads();
             // Interval it: the inverse of chunk it-1 (after E(it-1), read by the
             // consumers' chain in interval it+1).
@@ -416,6 +417,11 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
                 __syncthreads();
             }
         } else {
+            // The state chain is the critical path: its waves issue first (then
+            // the inverse wave, then the producers) when several are ready, so
+            // their LDS reads after each barrier are not queued behind the
+            // producers' traffic.
+            __builtin_amdgcn_s_setprio(3);
             __syncthreads();
             // Interval it: the state chain of chunk it-2 and the stores of chunk it-3.
             for (int it = 0; it < n_it; ++it) {
