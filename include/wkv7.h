@@ -57,7 +57,8 @@ extern "C" {
 
 #define WKV7_ABI_VERSION 1
 #define WKV7_HEAD_SIZE 64        /* the only supported N */
-#define WKV7_TAPE_CHUNK 16       /* tokens per chunk of the forward tape */
+#define WKV7_TAPE_CHUNK 16       /* tokens per chunk of the backward */
+#define WKV7_TAPE_BLOCK 32       /* tokens per state saved in the forward tape */
 
 typedef enum {
     WKV7_OK = 0,
@@ -88,15 +89,16 @@ const char *wkv7_status_string(int status);
 
 /* Bytes of the tape that wkv7_forward can write for wkv7_backward:
      Z   [B][T][H][N]              bf16: z_t = S_{t-1} a_t, the removal read-outs;
-     S   [B][H][ceil(T/16)][N][N]  bf16: the state entering every 16-token chunk,
-                                   stored key-major (element [j][i] = S[i][j]).
+     S   [B][H][ceil(T/32)][N][N]  bf16: the state entering every 32-token block
+                                   (tokens 32m ..), stored key-major (element
+                                   [j][i] = S[i][j]).
    0 on an invalid descriptor. */
 size_t wkv7_tape_bytes(const wkv7_desc *desc);
 
 /* Bytes of device scratch wkv7_backward needs: with_tape != 0 when the caller
-   passes a tape written by wkv7_forward (the backward then keeps the adjoint of
-   every chunk's exit state and one per-token intermediate adjoint there, as much again
-   as the tape), with_tape = 0 when it passes none (then a forward re-run also
+   passes a tape written by wkv7_forward (the backward then keeps one per-token
+   intermediate adjoint and the adjoint of the state leaving every 32-token block
+   there, as much again as the tape), with_tape = 0 when it passes none (then a forward re-run also
    writes its tape into the workspace: twice the tape).  0 on an invalid
    descriptor. */
 size_t wkv7_workspace_bytes(const wkv7_desc *desc, int with_tape);

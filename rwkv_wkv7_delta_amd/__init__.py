@@ -29,6 +29,7 @@ WKV7_F32 = 0
 WKV7_BF16 = 1
 HEAD_SIZE = 64
 TAPE_CHUNK = 16
+TAPE_BLOCK = 32
 
 EXPORTED = ("wkv7_abi_version", "wkv7_status_string", "wkv7_tape_bytes", "wkv7_workspace_bytes",
             "wkv7_forward", "wkv7_backward", "wkv7_backward_adjoint", "wkv7_backward_gradients",
@@ -139,11 +140,12 @@ def workspace_bytes(desc: Desc, with_tape: bool = True) -> int:
 
 def split_tape(tape, B: int, T: int, H: int, N: int = HEAD_SIZE):
     """Views of a forward tape: Z [B, T, H, N] (removal read-outs z_t = S_{t-1} a_t)
-    and the chunk entry states [B, H, ceil(T/16), N (key j), N (value i)], both bf16."""
-    nch = (T + TAPE_CHUNK - 1) // TAPE_CHUNK
+    and the states entering every 32-token block [B, H, ceil(T/32), N (key j),
+    N (value i)], both bf16."""
+    nblk = (T + TAPE_BLOCK - 1) // TAPE_BLOCK
     ntok = B * T * H * N
     z = tape[:ntok].view(B, T, H, N)
-    st = tape[ntok:ntok + B * H * nch * N * N].view(B, H, nch, N, N)
+    st = tape[ntok:ntok + B * H * nblk * N * N].view(B, H, nblk, N, N)
     return z, st
 
 

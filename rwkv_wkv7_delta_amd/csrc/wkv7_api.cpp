@@ -30,12 +30,12 @@ int check_desc(const wkv7_desc* d) {
 }
 
 // Tape: bf16 removal read-outs [B][T][H][N], then the bf16 state entering every
-// 16-token chunk [B][H][ceil(T/16)][N][N].  The backward's own scratch (dX and the
-// adjoint entering every chunk) has the same shape.
+// 32-token block [B][H][ceil(T/32)][N][N].  The backward's own scratch (dX, and
+// the adjoint leaving every block) has the same shape.
 size_t tape_bytes_unchecked(const wkv7_desc* d) {
-    const size_t nch = ((size_t)d->T + WKV7_TAPE_CHUNK - 1) / WKV7_TAPE_CHUNK;
+    const size_t nblk = ((size_t)d->T + WKV7_TAPE_BLOCK - 1) / WKV7_TAPE_BLOCK;
     const size_t tok = (size_t)d->B * d->T * d->H * d->N;
-    const size_t st = (size_t)d->B * d->H * nch * d->N * d->N;
+    const size_t st = (size_t)d->B * d->H * nblk * d->N * d->N;
     return (tok + st) * 2;
 }
 

@@ -103,7 +103,7 @@ struct __align__(16) P1Smem {
     P1Slot sl[3];
     bf16_t dXs[2][kL][kRow];      // [t][i]
     bf16_t dVs[2][kL][kRow];      // [t][i]
-    bf16_t dSs[2][kN][kRow];      // the chunk's incoming adjoint as [j][i]
+    bf16_t dSs[2][kN][kRow];      // the adjoint leaving the chunk as [j][i] (kept per 32 tokens)
 };
 
 __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
@@ -129,7 +129,10 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
     const int col = 16 * wp + l16;
     const int nch = (T + kL - 1) / kL;
     bf16_t* const wdX = work;                                   // [B][T][H][N]
-    bf16_t* const wdS = work + (size_t)B * T * H * kN;          // [B][H][nch][N][N]
+    bf16_t* const wdS = work + (size_t)B * T * H * kN;          // [B][H][nblk][N][N]
+    const int nblk = (nch + 1) / 2;
+    // The adjoint leaving a 32-token block: after chunk c when c is odd or the last.
+    auto keeps_dS = [&](int c) __attribute__((always_inline)) { return c >= 0 && ((c & 1) || c == nch - 1); };
     // Interval it handles chunks from the last one down; negative chunk
     // indices are all-padding, for which every stage is the identity.
     auto chunk_of = [&](int it) __attribute__((always_inline)) { return nch - 1 - it; };
@@ -339,9 +342,11 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
         const int i0 = 16 * wp + 4 * g;
         *reinterpret_cast<bf16x4*>(&sm.dXs[sb][l16][i0]) = swap_layout(dXb, ident);
         *reinterpret_cast<bf16x4*>(&sm.dVs[sb][l16][i0]) = swap_layout(dVb, ident);
+        if (keeps_dS(c)) {
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt)   // as [j][i]: row layout of the dS^T tile of key block jt
-            *reinterpret_cast<bf16x4*>(&sm.dSs[sb][16 * jt + l16][i0]) = swap_layout(dSb[jt], ident);
+            for (int jt = 0; jt < 4; ++jt)   // as [j][i]: row layout of the dS^T tile of key block jt
+                *reinterpret_cast<bf16x4*>(&sm.dSs[sb][16 * jt + l16][i0]) = swap_layout(dSb[jt], ident);
+        }
         // dS0^T = G_L dS^T + Rt^T dY + At^T dX
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
@@ -368,11 +373,13 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
             *reinterpret_cast<uint4*>(base + tok_off(bb, tt, hh, T, H) + 8 * piece) =
                 *reinterpret_cast<const uint4*>(&src[row][8 * piece]);
         }
+        if (keeps_dS(c)) {
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-            const int j = 32 * k2 + (rtid >> 3);
-            *reinterpret_cast<uint4*>(wdS + (((size_t)bh * nch + c) * kN + j) * kN + 8 * piece) =
-                *reinterpret_cast<const uint4*>(&sm.dSs[sb][j][8 * piece]);
+            for (int k2 = 0; k2 < 2; ++k2) {
+                const int j = 32 * k2 + (rtid >> 3);
+                *reinterpret_cast<uint4*>(wdS + (((size_t)bh * nblk + (c >> 1)) * kN + j) * kN + 8 * piece) =
+                    *reinterpret_cast<const uint4*>(&sm.dSs[sb][j][8 * piece]);
+            }
         }
     };
 
@@ -452,267 +459,324 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
 }
 
 // =============================================================================
-// Pass 2: per-key gradients, one independent wave per (chunk, key block).
+// Pass 2: per-key gradients, one workgroup per pair of chunks (32 tokens).
 // =============================================================================
+//
+// The tape holds the state entering every 32-token block and the workspace the
+// adjoint leaving it, which halves their traffic.  A workgroup takes the two
+// chunks c0 = 2m, c1 = 2m + 1 of block m and first steps across the middle:
+//   S0(c1)^T   = diag(G_L(c0)) S0(c0)^T + Kb(c0)^T V(c0) + Bb(c0)^T Z(c0)
+//   dS(c0)^T   = diag(G_L(c1)) dS(c1)^T + Rt(c1)^T dY(c1) + At(c1)^T dX(c1)
+// (the forward's state update and the chain's adjoint update of one chunk,
+// contracted over the chunk's tokens), then computes every per-key gradient
+// of c0 and of c1.  Wave p owns key columns 16p .. 16p+15 throughout, and
+// reads and writes only its own rows of the [j][i] states.
 
-constexpr int kP2Threads = 256;   // the four key blocks of one chunk
+constexpr int kP2Threads = 256;   // the four key blocks
 
-// Rows of the chunk staged in LDS: the six token inputs the gradients need,
-// then dX and Z; and the chunk's entry state and exit adjoint as [j][i].
+// Rows of a chunk staged in LDS: the six token inputs the gradients need,
+// then dX and Z; and the entry state and exit adjoint of both chunks as [j][i].
 enum { P2_R = 0, P2_W = 1, P2_K = 2, P2_A = 3, P2_B = 4, P2_DY = 5, P2_V = 6, P2_DX = 7, P2_Z = 8 };
 struct __align__(16) P2Smem {
-    bf16_t rows[9][kL][kRow];
-    bf16_t st[2][kN][kRow];      // S0, dS
-    float red[4][5][4][16];      // wave-private cross-lane-group exchange
+    bf16_t rows[2][9][kL][kRow];
+    bf16_t st[2][2][kN][kRow];   // [S0 | dS][chunk of the pair][j][i]
 };
 
+// Lane (g, l16) of wave p: key column col = 16p + l16, tokens 4g .. 4g+3.
+struct KeyFactors {
+    float R[5][4];                 // r, w, k, a, b
+    float Gt[4], Gp[4], inv[4], GL;
+    bf16x4 atI, rtI, bhI, khI, bbI, kbI;   // bf16 operand values of the forward
+};
+
+// The value that lane (gg, l16) of this wave holds, for every gg.
+__device__ __forceinline__ float from_group(float x, int gg, int l16) {
+    return __shfl(x, l16 + 16 * gg, 64);
+}
+
 __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
-    int T, int H, int nch, const bf16_t* __restrict__ r, const bf16_t* __restrict__ w,
+    int T, int H, int nch, int nblk, const bf16_t* __restrict__ r, const bf16_t* __restrict__ w,
     const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const bf16_t* __restrict__ a,
     const bf16_t* __restrict__ b, const bf16_t* __restrict__ dy, const bf16_t* __restrict__ tape,
     const bf16_t* __restrict__ work, bf16_t* __restrict__ dr, bf16_t* __restrict__ dw,
     bf16_t* __restrict__ dk, bf16_t* __restrict__ da, bf16_t* __restrict__ db) {
     __shared__ P2Smem sm;
-    const int c = blockIdx.x % nch;
-    const int bh = blockIdx.x / nch;
+    const int m = blockIdx.x % nblk;
+    const int bh = blockIdx.x / nblk;
     const int bb = bh / H, hh = bh % H;
-    const int B = gridDim.x / nch / H;
+    const int B = gridDim.x / nblk / H;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wp = tid >> 6;
     const int l16 = lane & 15, g = lane >> 4;
     const int col = 16 * wp + l16;     // key column j of this lane
-    const int t0 = c * kL;
+    const int c0 = 2 * m;
+    const int nh = c0 + 1 < nch ? 2 : 1;   // chunks in this block
     const bf16_t* const tapeZ = tape;
     const bf16_t* const tapeS = tape + (size_t)B * T * H * kN;
     const bf16_t* const wdX = work;
     const bf16_t* const wdS = work + (size_t)B * T * H * kN;
-    float* const rd = &sm.red[wp][0][0][0];
-    auto RD = [&](int kind, int gg) __attribute__((always_inline)) -> float& {
-        return rd[(kind * 4 + gg) * 16 + l16];
-    };
 
-    // ---- stage the chunk through LDS with whole-row loads: 8 threads per
+    // ---- stage both chunks through LDS with whole-row loads: 8 threads per
     // 128-byte row, 16 bytes each.  Tokens past T become padding (w = 1,
-    // everything else 0). --------------------------------------------------------
+    // everything else 0).  The block's entry state goes to st[0][0], its exit
+    // adjoint to st[1][nh - 1]. ------------------------------------------------------
     {
         const int row = (tid >> 3) & 15, piece = tid & 7;
-        const int t = t0 + row;
-        const bool ok = t < T;
-        const size_t off = tok_off(bb, min(t, T - 1), hh, T, H) + 8 * piece;
-        auto stage_row = [&](int set, const bf16_t* src, unsigned pad) __attribute__((always_inline)) {
-            const uint4 x = *reinterpret_cast<const uint4*>(src + off);
-            *reinterpret_cast<uint4*>(&sm.rows[set][row][8 * piece]) = ok ? x : make_uint4(pad, pad, pad, pad);
-        };
-        if (tid < 128) {
-            stage_row(P2_R, r, 0u);
-            stage_row(P2_K, k, 0u);
-            stage_row(P2_B, b, 0u);
-            stage_row(P2_V, v, 0u);
-            stage_row(P2_Z, tapeZ, 0u);
-        } else {
-            stage_row(P2_W, w, 0x3F803F80u);
-            stage_row(P2_A, a, 0u);
-            stage_row(P2_DY, dy, 0u);
-            stage_row(P2_DX, wdX, 0u);
+        // Both chunks are staged even when the block has one (the second is then
+        // all padding and never used): a fixed count keeps the code branch-free.
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int t = (c0 + h) * kL + row;
+            const bool ok = t < T;
+            const size_t off = tok_off(bb, min(t, T - 1), hh, T, H) + 8 * piece;
+            auto stage_row = [&](int set, const bf16_t* src, unsigned pad) __attribute__((always_inline)) {
+                const uint4 x = *reinterpret_cast<const uint4*>(src + off);
+                *reinterpret_cast<uint4*>(&sm.rows[h][set][row][8 * piece]) =
+                    ok ? x : make_uint4(pad, pad, pad, pad);
+            };
+            if (tid < 128) {
+                stage_row(P2_R, r, 0u);
+                stage_row(P2_K, k, 0u);
+                stage_row(P2_B, b, 0u);
+                stage_row(P2_V, v, 0u);
+                stage_row(P2_Z, tapeZ, 0u);
+            } else {
+                stage_row(P2_W, w, 0x3F803F80u);
+                stage_row(P2_A, a, 0u);
+                stage_row(P2_DY, dy, 0u);
+                stage_row(P2_DX, wdX, 0u);
+            }
         }
-        const size_t sbase = ((size_t)bh * nch + c) * kN * kN;
+        const size_t sbase = ((size_t)bh * nblk + m) * kN * kN;
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
             const int j = (tid >> 3) + 32 * h2;
-            *reinterpret_cast<uint4*>(&sm.st[0][j][8 * piece]) =
+            *reinterpret_cast<uint4*>(&sm.st[0][0][j][8 * piece]) =
                 *reinterpret_cast<const uint4*>(tapeS + sbase + j * kN + 8 * piece);
-            *reinterpret_cast<uint4*>(&sm.st[1][j][8 * piece]) =
+            *reinterpret_cast<uint4*>(&sm.st[1][nh - 1][j][8 * piece]) =
                 *reinterpret_cast<const uint4*>(wdS + sbase + j * kN + 8 * piece);
         }
     }
     __syncthreads();
 
-    // ---- this lane's key column over tokens 4g..4g+3, the chunk's rows (row l16,
-    // 8 values at 32 k2 + 8 g), and column `col` of S0 and dS ----------------------
-    float R[5][4];
+    // ---- decay products and scaled vectors of column `col` in chunk h ----------
+    auto factors = [&](int h) __attribute__((always_inline)) -> KeyFactors {
+        KeyFactors f;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int vi = 0; vi < 5; ++vi) R[vi][q] = bf2f(sm.rows[vi][4 * g + q][col]);
-    bf16x8 dXr[2], Zr[2], dYr[2], Vr[2], S0c[2], dSc[2];
-#pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
-        const int i0 = 32 * k2 + 8 * g;
-        dXr[k2] = ld8(&sm.rows[P2_DX][l16][i0]);
-        Zr[k2] = ld8(&sm.rows[P2_Z][l16][i0]);
-        dYr[k2] = ld8(&sm.rows[P2_DY][l16][i0]);
-        Vr[k2] = ld8(&sm.rows[P2_V][l16][i0]);
-        S0c[k2] = ld8(&sm.st[0][col][i0]);
-        dSc[k2] = ld8(&sm.st[1][col][i0]);
-    }
-
-    // ---- decay products and scaled vectors of column `col` -----------------------
-    float gp[4];
-    {
+            for (int vi = 0; vi < 5; ++vi) f.R[vi][q] = bf2f(sm.rows[h][vi][4 * g + q][col]);
+        float gp[4];
         float run = 1.f;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            run *= R[P2_W][q];
+            run *= f.R[P2_W][q];
             gp[q] = run;
         }
-        RD(0, g) = run;
-    }
-    wave_sync();
-    const float g0 = RD(0, 0), g1 = RD(0, 1), g2 = RD(0, 2), g3 = RD(0, 3);
-    const float before = ((g >= 1 ? g0 : 1.f) * (g >= 2 ? g1 : 1.f)) * (g >= 3 ? g2 : 1.f);
-    const float GL = ((g0 * g1) * g2) * g3;
-    float Gt[4], Gp[4], inv[4];
-    float at[4], rt[4], bh_[4], kh_[4], bbar[4], kbar[4];
+        const float g0 = from_group(run, 0, l16), g1 = from_group(run, 1, l16);
+        const float g2 = from_group(run, 2, l16), g3 = from_group(run, 3, l16);
+        const float before = ((g >= 1 ? g0 : 1.f) * (g >= 2 ? g1 : 1.f)) * (g >= 3 ? g2 : 1.f);
+        f.GL = ((g0 * g1) * g2) * g3;
+        float at[4], rt[4], bh_[4], kh_[4], bbar[4], kbar[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        Gt[q] = before * gp[q];
-        Gp[q] = q == 0 ? before : before * gp[q - 1];
-        inv[q] = __builtin_amdgcn_rcpf(Gt[q]);
-        at[q] = R[P2_A][q] * Gp[q];
-        rt[q] = R[P2_R][q] * Gt[q];
-        bh_[q] = R[P2_B][q] * inv[q];
-        kh_[q] = R[P2_K][q] * inv[q];
-        bbar[q] = bh_[q] * GL;
-        kbar[q] = kh_[q] * GL;
-    }
-    // bf16 images: the forward's MFMA operand values, and the B operands (key
-    // s = 4g+q, column col) of the products below.
-    const bf16x4 atI = cvt4(at[0], at[1], at[2], at[3]);
-    const bf16x4 rtI = cvt4(rt[0], rt[1], rt[2], rt[3]);
-    const bf16x4 bhI = cvt4(bh_[0], bh_[1], bh_[2], bh_[3]);
-    const bf16x4 khI = cvt4(kh_[0], kh_[1], kh_[2], kh_[3]);
-    const bf16x4 bbI = cvt4(bbar[0], bbar[1], bbar[2], bbar[3]);
-    const bf16x4 kbI = cvt4(kbar[0], kbar[1], kbar[2], kbar[3]);
-
-    // ---- L x L adjoints in both orientations ([t][s] and [s][t]) and the
-    // contractions over the value rows ----------------------------------------------
-    f32x4 dAab = zero4(), dAabT = zero4(), dAak = zero4(), dAakT = zero4();
-    f32x4 dArb = zero4(), dArbT = zero4(), dArk = zero4(), dArkT = zero4();
-    f32x4 dAt = zero4(), dRt = zero4(), dBb = zero4(), dKb = zero4();
-#pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
-        dAab = mfma32(dXr[k2], Zr[k2], dAab);
-        dAabT = mfma32(Zr[k2], dXr[k2], dAabT);
-        dAak = mfma32(dXr[k2], Vr[k2], dAak);
-        dAakT = mfma32(Vr[k2], dXr[k2], dAakT);
-        dArb = mfma32(dYr[k2], Zr[k2], dArb);
-        dArbT = mfma32(Zr[k2], dYr[k2], dArbT);
-        dArk = mfma32(dYr[k2], Vr[k2], dArk);
-        dArkT = mfma32(Vr[k2], dYr[k2], dArkT);
-        dAt = mfma32(dXr[k2], S0c[k2], dAt);     // dX S0
-        dRt = mfma32(dYr[k2], S0c[k2], dRt);     // dY S0
-        dBb = mfma32(Zr[k2], dSc[k2], dBb);      // Z dS
-        dKb = mfma32(Vr[k2], dSc[k2], dKb);      // V dS
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int m = 4 * g + q, n = l16;
-        dAab[q] = (n < m) ? dAab[q] : 0.f;
-        dAak[q] = (n < m) ? dAak[q] : 0.f;
-        dArb[q] = (n <= m) ? dArb[q] : 0.f;
-        dArk[q] = (n <= m) ? dArk[q] : 0.f;
-        dAabT[q] = (m < n) ? dAabT[q] : 0.f;
-        dAakT[q] = (m < n) ? dAakT[q] : 0.f;
-        dArbT[q] = (m <= n) ? dArbT[q] : 0.f;
-        dArkT[q] = (m <= n) ? dArkT[q] : 0.f;
-    }
-    // Accumulator registers of X fed as an A operand stand for X^T.  The
-    // 16-deep partial sums join the 32-deep ones on the vector ALU (add4).
-    dAt = add4(dAt, mfma16(cvt4(dAakT), khI, mfma16(cvt4(dAabT), bhI, zero4())));
-    dRt = add4(dRt, mfma16(cvt4(dArkT), khI, mfma16(cvt4(dArbT), bhI, zero4())));
-    f32x4 dBh = mfma16(cvt4(dAab), atI, zero4());
-    dBh = mfma16(cvt4(dArb), rtI, dBh);
-    f32x4 dKh = mfma16(cvt4(dAak), atI, zero4());
-    dKh = mfma16(cvt4(dArk), rtI, dKh);
-
-    // ---- sum_i dS[i][col] S0[i][col] over this lane's 16 value rows ---------------
-    float cs = 0.f;
-#pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-        for (int q = 0; q < 8; ++q) cs = fmaf((float)dSc[k2][q], (float)S0c[k2][q], cs);
-
-    // ---- chain rule through the decay products (tokens t = 4g+q) ------------------
-    // d log w_u = sum_{t>=u} (dRt Rt - dBh Bh - dKh Kh)_t + sum_{t>=u+1} (dAt At)_t
-    //           + sum_{t<u} (dBb Bb + dKb Kb)_t + G_L sum_i dS[i][j] S0[i][j];
-    // the products use the bf16 operand values so that pair terms that cancel
-    // exactly in the chunk algebra cancel to fp32 rounding.
-    float base[4], e[4], bk[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        e[q] = dAt[q] * (float)atI[q];
-        bk[q] = dBb[q] * (float)bbI[q] + dKb[q] * (float)kbI[q];
-        base[q] = dRt[q] * (float)rtI[q] - dBh[q] * (float)bhI[q] - dKh[q] * (float)khI[q];
-    }
-    RD(1, g) = base[0] + base[1] + base[2] + base[3];
-    RD(2, g) = e[0] + e[1] + e[2] + e[3];
-    RD(3, g) = bk[0] + bk[1] + bk[2] + bk[3];
-    RD(4, g) = cs;
-    wave_sync();
-    float base_after = 0.f, e_after = 0.f, bk_before = 0.f, cs_all = 0.f;
-#pragma unroll
-    for (int g2 = 0; g2 < 4; ++g2) {
-        const float bs = RD(1, g2), es = RD(2, g2), ks = RD(3, g2);
-        cs_all += RD(4, g2);
-        if (g2 > g) {
-            base_after += bs;
-            e_after += es;
+        for (int q = 0; q < 4; ++q) {
+            f.Gt[q] = before * gp[q];
+            f.Gp[q] = q == 0 ? before : before * gp[q - 1];
+            f.inv[q] = __builtin_amdgcn_rcpf(f.Gt[q]);
+            at[q] = f.R[P2_A][q] * f.Gp[q];
+            rt[q] = f.R[P2_R][q] * f.Gt[q];
+            bh_[q] = f.R[P2_B][q] * f.inv[q];
+            kh_[q] = f.R[P2_K][q] * f.inv[q];
+            bbar[q] = bh_[q] * f.GL;
+            kbar[q] = kh_[q] * f.GL;
         }
-        if (g2 < g) bk_before += ks;
-    }
-    const float csL = cs_all * GL;
-    float pbk[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        pbk[q] = bk_before;
-        bk_before += bk[q];
-    }
-    float dlw[4];
-    {
-        float sb = base_after, se = e_after;
-#pragma unroll
-        for (int q = 3; q >= 0; --q) {
-            sb += base[q];
-            dlw[q] = (sb + se) + (pbk[q] + csL);
-            se += e[q];
-        }
-    }
-
-    // ---- outputs: accumulator tiles [t][col] -> row layout (swap_layout) -> LDS
-    // rows -> whole-row stores ------------------------------------------------------
-    f32x4 o_da, o_dr, o_db, o_dk, o_dw;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        o_da[q] = dAt[q] * Gp[q];
-        o_dr[q] = dRt[q] * Gt[q];
-        o_db[q] = (dBh[q] + dBb[q] * GL) * inv[q];
-        o_dk[q] = (dKh[q] + dKb[q] * GL) * inv[q];
-        o_dw[q] = dlw[q] / R[P2_W][q];
-    }
+        // bf16 images: the forward's MFMA operand values, and the B operands (key
+        // s = 4g+q, column col) of the products below.
+        f.atI = cvt4(at[0], at[1], at[2], at[3]);
+        f.rtI = cvt4(rt[0], rt[1], rt[2], rt[3]);
+        f.bhI = cvt4(bh_[0], bh_[1], bh_[2], bh_[3]);
+        f.khI = cvt4(kh_[0], kh_[1], kh_[2], kh_[3]);
+        f.bbI = cvt4(bbar[0], bbar[1], bbar[2], bbar[3]);
+        f.kbI = cvt4(kbar[0], kbar[1], kbar[2], kbar[3]);
+        return f;
+    };
     const bf16x4 ident = identity_b(g, l16);
-    __syncthreads();   // every wave is done reading the staged rows
-    const int j0 = 16 * wp + 4 * g;
-    *reinterpret_cast<bf16x4*>(&sm.rows[0][l16][j0]) = swap_layout(cvt4(o_dr), ident);
-    *reinterpret_cast<bf16x4*>(&sm.rows[1][l16][j0]) = swap_layout(cvt4(o_dw), ident);
-    *reinterpret_cast<bf16x4*>(&sm.rows[2][l16][j0]) = swap_layout(cvt4(o_dk), ident);
-    *reinterpret_cast<bf16x4*>(&sm.rows[3][l16][j0]) = swap_layout(cvt4(o_da), ident);
-    *reinterpret_cast<bf16x4*>(&sm.rows[4][l16][j0]) = swap_layout(cvt4(o_db), ident);
-    __syncthreads();
-    {
-        const int row = (tid >> 3) & 15, piece = tid & 7;
-        const int t = t0 + row;
-        if (t < T) {
-            const size_t off = tok_off(bb, t, hh, T, H) + 8 * piece;
-            auto put = [&](int set, bf16_t* dst) __attribute__((always_inline)) {
-                *reinterpret_cast<uint4*>(dst + off) = *reinterpret_cast<const uint4*>(&sm.rows[set][row][8 * piece]);
-            };
-            if (tid < 128) {
-                put(0, dr);
-                put(2, dk);
-                put(4, db);
-            } else {
-                put(1, dw);
-                put(3, da);
+
+    // ---- across the middle of the block: S0(c1) and dS(c0), rows `col` ---------
+    if (nh == 2) {
+        const KeyFactors f0 = factors(0), f1 = factors(1);
+#pragma unroll
+        for (int vb = 0; vb < 4; ++vb) {
+            const int i0 = 16 * vb + 4 * g;
+            // [t][i] tiles of value block vb in accumulator layout (lane holds
+            // [4g+q][l16]); fed as A operands they stand for their transposes.
+            const bf16x4 Vt = swap_layout(ld4(&sm.rows[0][P2_V][l16][16 * vb + 4 * g]), ident);
+            const bf16x4 Zt = swap_layout(ld4(&sm.rows[0][P2_Z][l16][16 * vb + 4 * g]), ident);
+            const bf16x4 dYt = swap_layout(ld4(&sm.rows[1][P2_DY][l16][16 * vb + 4 * g]), ident);
+            const bf16x4 dXt = swap_layout(ld4(&sm.rows[1][P2_DX][l16][16 * vb + 4 * g]), ident);
+            const bf16x4 s0 = ld4(&sm.st[0][0][col][i0]);
+            const bf16x4 ds1 = ld4(&sm.st[1][1][col][i0]);
+            f32x4 sacc, dacc;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                sacc[q] = f0.GL * (float)s0[q];
+                dacc[q] = f1.GL * (float)ds1[q];
+            }
+            sacc = mfma16(Vt, f0.kbI, sacc);    // + V^T Kb  ([i][j])
+            sacc = mfma16(Zt, f0.bbI, sacc);    // + Z^T Bb
+            dacc = mfma16(dYt, f1.rtI, dacc);   // + dY^T Rt
+            dacc = mfma16(dXt, f1.atI, dacc);   // + dX^T At
+            *reinterpret_cast<bf16x4*>(&sm.st[0][1][col][i0]) = cvt4(sacc);
+            *reinterpret_cast<bf16x4*>(&sm.st[1][0][col][i0]) = cvt4(dacc);
+        }
+    }
+
+    for (int h = 0; h < nh; ++h) {
+        const int t0 = (c0 + h) * kL;
+        const KeyFactors f = factors(h);
+        // ---- the chunk's rows (row l16, 8 values at 32 k2 + 8 g) and column
+        // `col` of S0 and dS ----------------------------------------------------------
+        bf16x8 dXr[2], Zr[2], dYr[2], Vr[2], S0c[2], dSc[2];
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+            const int i0 = 32 * k2 + 8 * g;
+            dXr[k2] = ld8(&sm.rows[h][P2_DX][l16][i0]);
+            Zr[k2] = ld8(&sm.rows[h][P2_Z][l16][i0]);
+            dYr[k2] = ld8(&sm.rows[h][P2_DY][l16][i0]);
+            Vr[k2] = ld8(&sm.rows[h][P2_V][l16][i0]);
+            S0c[k2] = ld8(&sm.st[0][h][col][i0]);
+            dSc[k2] = ld8(&sm.st[1][h][col][i0]);
+        }
+
+        // ---- L x L adjoints in both orientations ([t][s] and [s][t]) and the
+        // contractions over the value rows ------------------------------------------
+        f32x4 dAab = zero4(), dAabT = zero4(), dAak = zero4(), dAakT = zero4();
+        f32x4 dArb = zero4(), dArbT = zero4(), dArk = zero4(), dArkT = zero4();
+        f32x4 dAt = zero4(), dRt = zero4(), dBb = zero4(), dKb = zero4();
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+            dAab = mfma32(dXr[k2], Zr[k2], dAab);
+            dAabT = mfma32(Zr[k2], dXr[k2], dAabT);
+            dAak = mfma32(dXr[k2], Vr[k2], dAak);
+            dAakT = mfma32(Vr[k2], dXr[k2], dAakT);
+            dArb = mfma32(dYr[k2], Zr[k2], dArb);
+            dArbT = mfma32(Zr[k2], dYr[k2], dArbT);
+            dArk = mfma32(dYr[k2], Vr[k2], dArk);
+            dArkT = mfma32(Vr[k2], dYr[k2], dArkT);
+            dAt = mfma32(dXr[k2], S0c[k2], dAt);     // dX S0
+            dRt = mfma32(dYr[k2], S0c[k2], dRt);     // dY S0
+            dBb = mfma32(Zr[k2], dSc[k2], dBb);      // Z dS
+            dKb = mfma32(Vr[k2], dSc[k2], dKb);      // V dS
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int mm = 4 * g + q, n = l16;
+            dAab[q] = (n < mm) ? dAab[q] : 0.f;
+            dAak[q] = (n < mm) ? dAak[q] : 0.f;
+            dArb[q] = (n <= mm) ? dArb[q] : 0.f;
+            dArk[q] = (n <= mm) ? dArk[q] : 0.f;
+            dAabT[q] = (mm < n) ? dAabT[q] : 0.f;
+            dAakT[q] = (mm < n) ? dAakT[q] : 0.f;
+            dArbT[q] = (mm <= n) ? dArbT[q] : 0.f;
+            dArkT[q] = (mm <= n) ? dArkT[q] : 0.f;
+        }
+        // Accumulator registers of X fed as an A operand stand for X^T.  The
+        // 16-deep partial sums join the 32-deep ones on the vector ALU (add4).
+        dAt = add4(dAt, mfma16(cvt4(dAakT), f.khI, mfma16(cvt4(dAabT), f.bhI, zero4())));
+        dRt = add4(dRt, mfma16(cvt4(dArkT), f.khI, mfma16(cvt4(dArbT), f.bhI, zero4())));
+        f32x4 dBh = mfma16(cvt4(dAab), f.atI, zero4());
+        dBh = mfma16(cvt4(dArb), f.rtI, dBh);
+        f32x4 dKh = mfma16(cvt4(dAak), f.atI, zero4());
+        dKh = mfma16(cvt4(dArk), f.rtI, dKh);
+
+        // ---- sum_i dS[i][col] S0[i][col] over this lane's 16 value rows -----------
+        float cs = 0.f;
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+            for (int q = 0; q < 8; ++q) cs = fmaf((float)dSc[k2][q], (float)S0c[k2][q], cs);
+
+        // ---- chain rule through the decay products (tokens t = 4g+q) --------------
+        // d log w_u = sum_{t>=u} (dRt Rt - dBh Bh - dKh Kh)_t + sum_{t>=u+1} (dAt At)_t
+        //           + sum_{t<u} (dBb Bb + dKb Kb)_t + G_L sum_i dS[i][j] S0[i][j];
+        // the products use the bf16 operand values so that pair terms that cancel
+        // exactly in the chunk algebra cancel to fp32 rounding.
+        float base[4], e[4], bk[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            e[q] = dAt[q] * (float)f.atI[q];
+            bk[q] = dBb[q] * (float)f.bbI[q] + dKb[q] * (float)f.kbI[q];
+            base[q] = dRt[q] * (float)f.rtI[q] - dBh[q] * (float)f.bhI[q] - dKh[q] * (float)f.khI[q];
+        }
+        const float sum_base = base[0] + base[1] + base[2] + base[3];
+        const float sum_e = e[0] + e[1] + e[2] + e[3];
+        const float sum_bk = bk[0] + bk[1] + bk[2] + bk[3];
+        float base_after = 0.f, e_after = 0.f, bk_before = 0.f, cs_all = 0.f;
+#pragma unroll
+        for (int g2 = 0; g2 < 4; ++g2) {
+            const float bs = from_group(sum_base, g2, l16), es = from_group(sum_e, g2, l16);
+            const float ks = from_group(sum_bk, g2, l16);
+            cs_all += from_group(cs, g2, l16);
+            if (g2 > g) {
+                base_after += bs;
+                e_after += es;
+            }
+            if (g2 < g) bk_before += ks;
+        }
+        const float csL = cs_all * f.GL;
+        float pbk[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            pbk[q] = bk_before;
+            bk_before += bk[q];
+        }
+        float dlw[4];
+        {
+            float sb = base_after, se = e_after;
+#pragma unroll
+            for (int q = 3; q >= 0; --q) {
+                sb += base[q];
+                dlw[q] = (sb + se) + (pbk[q] + csL);
+                se += e[q];
+            }
+        }
+
+        // ---- outputs: accumulator tiles [t][col] -> row layout (swap_layout) -> LDS
+        // rows (over this chunk's r, w, k, a, b) -> whole-row stores -------------------
+        f32x4 o_da, o_dr, o_db, o_dk, o_dw;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            o_da[q] = dAt[q] * f.Gp[q];
+            o_dr[q] = dRt[q] * f.Gt[q];
+            o_db[q] = (dBh[q] + dBb[q] * f.GL) * f.inv[q];
+            o_dk[q] = (dKh[q] + dKb[q] * f.GL) * f.inv[q];
+            o_dw[q] = dlw[q] / f.R[P2_W][q];
+        }
+        __syncthreads();   // every wave is done reading this chunk's staged rows
+        const int j0 = 16 * wp + 4 * g;
+        *reinterpret_cast<bf16x4*>(&sm.rows[h][0][l16][j0]) = swap_layout(cvt4(o_dr), ident);
+        *reinterpret_cast<bf16x4*>(&sm.rows[h][1][l16][j0]) = swap_layout(cvt4(o_dw), ident);
+        *reinterpret_cast<bf16x4*>(&sm.rows[h][2][l16][j0]) = swap_layout(cvt4(o_dk), ident);
+        *reinterpret_cast<bf16x4*>(&sm.rows[h][3][l16][j0]) = swap_layout(cvt4(o_da), ident);
+        *reinterpret_cast<bf16x4*>(&sm.rows[h][4][l16][j0]) = swap_layout(cvt4(o_db), ident);
+        __syncthreads();
+        {
+            const int row = (tid >> 3) & 15, piece = tid & 7;
+            const int t = t0 + row;
+            if (t < T) {
+                const size_t off = tok_off(bb, t, hh, T, H) + 8 * piece;
+                auto put = [&](int set, bf16_t* dst) __attribute__((always_inline)) {
+                    *reinterpret_cast<uint4*>(dst + off) =
+                        *reinterpret_cast<const uint4*>(&sm.rows[h][set][row][8 * piece]);
+                };
+                if (tid < 128) {
+                    put(0, dr);
+                    put(2, dk);
+                    put(4, db);
+                } else {
+                    put(1, dw);
+                    put(3, da);
+                }
             }
         }
     }
@@ -738,8 +802,9 @@ hipError_t launch_bwd(const BwdArgs& p, int chunk_len, int stages, hipStream_t s
     }
     if (!(stages & BWD_KEYS)) return hipSuccess;
     const int nch = (p.T + kL - 1) / kL;
-    bwd_keys_kernel<<<dim3(p.B * p.H * nch), dim3(kP2Threads), 0, stream>>>(
-        p.T, p.H, nch, r, w, k, v, a, b, dy, static_cast<const bf16_t*>(p.tape), work,
+    const int nblk = (nch + 1) / 2;
+    bwd_keys_kernel<<<dim3(p.B * p.H * nblk), dim3(kP2Threads), 0, stream>>>(
+        p.T, p.H, nch, nblk, r, w, k, v, a, b, dy, static_cast<const bf16_t*>(p.tape), work,
         static_cast<bf16_t*>(p.dr), static_cast<bf16_t*>(p.dw), static_cast<bf16_t*>(p.dk),
         static_cast<bf16_t*>(p.da), static_cast<bf16_t*>(p.db));
     return hipGetLastError();

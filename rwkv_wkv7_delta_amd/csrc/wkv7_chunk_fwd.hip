@@ -111,8 +111,10 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
     const int l16 = lane & 15, g = lane >> 4;
     const int col = 16 * wp + l16;            // key column (producer) / value row (consumer)
     const int nch = (T + kL - 1) / kL;
-    // Tape for the backward: removal read-outs Z as [B][T][H][N] bf16, then every
-    // chunk's entry state as [B][H][nch][N (key j)][N (value i)] bf16.
+    // Tape for the backward: removal read-outs Z as [B][T][H][N] bf16, then the
+    // state entering every 32-token block (even chunks) as
+    // [B][H][nblk][N (key j)][N (value i)] bf16.
+    const int nblk = (nch + 1) / 2;
     bf16_t* const tapeZ = tape;
     bf16_t* const tapeS = tape ? tape + (size_t)gridDim.x / H * T * H * kN : nullptr;
 
@@ -334,9 +336,12 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
         *reinterpret_cast<bf16x4*>(&sm.Ys[c & 1][l16][i0]) = swap_layout(cvt4(Yt), ident);
         if (tape) {
             *reinterpret_cast<bf16x4*>(&sm.Zs[c & 1][l16][i0]) = swap_layout(Zb, ident);
+            if ((c & 1) == 0) {   // entry state of a 32-token block as [j][i]: row layout of S^T tile jt
 #pragma unroll
-            for (int jt = 0; jt < 4; ++jt)   // entry state as [j][i]: row layout of S^T tile jt
-                *reinterpret_cast<bf16x4*>(&sm.S0s[c & 1][16 * jt + l16][i0]) = swap_layout(Sb[jt], ident);
+                for (int jt = 0; jt < 4; ++jt)
+                    *reinterpret_cast<bf16x4*>(&sm.S0s[(c >> 1) & 1][16 * jt + l16][i0]) =
+                        swap_layout(Sb[jt], ident);
+            }
         }
     };
     // Staged outputs of chunk c to global memory; 8 consecutive threads write
@@ -351,12 +356,12 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
                 *reinterpret_cast<uint4*>(base + tok_off(bb, tt, hh, T, H) + 8 * piece) =
                     *reinterpret_cast<const uint4*>(&src[row][8 * piece]);
         }
-        if (tape && c < nch) {
+        if (tape && c < nch && (c & 1) == 0) {
 #pragma unroll
             for (int k2 = 0; k2 < 2; ++k2) {
                 const int j = 32 * k2 + (rtid >> 3);
-                *reinterpret_cast<uint4*>(tapeS + (((size_t)bh * nch + c) * kN + j) * kN + 8 * piece) =
-                    *reinterpret_cast<const uint4*>(&sm.S0s[c & 1][j][8 * piece]);
+                *reinterpret_cast<uint4*>(tapeS + (((size_t)bh * nblk + (c >> 1)) * kN + j) * kN + 8 * piece) =
+                    *reinterpret_cast<const uint4*>(&sm.S0s[(c >> 1) & 1][j][8 * piece]);
             }
         }
     };

@@ -24,7 +24,7 @@ namespace wkv7 {
 namespace {
 
 constexpr int kTB = 16;  // tokens per LDS stage
-static_assert(kTB == 16, "the tape stores the state entering every 16-token chunk");
+static_assert(kTB == 16, "the tape's removal read-outs and states follow 16-token chunks");
 
 template <typename Tin, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void seq_fwd_kernel(
@@ -56,8 +56,8 @@ __global__ __launch_bounds__(64 * WAVES) void seq_fwd_kernel(
     const size_t soff = ((size_t)bh * kN + row) * kN + cq * 4;
     float4 S = s0 ? *reinterpret_cast<const float4*>(s0 + soff) : make_float4(0.f, 0.f, 0.f, 0.f);
     // Tape for the backward: z as [B][T][H][N] bf16, then the state entering every
-    // 16-token chunk as [B][H][nch][N (key)][N (value)] bf16.
-    const int nch = (T + 15) / 16;
+    // 32-token block as [B][H][nblk][N (key)][N (value)] bf16.
+    const int nblk = (T + 31) / 32;
     bf16_t* const tapeZ = tape;
     bf16_t* const tapeS = tape ? tape + (size_t)(gridDim.x / NRB) / H * T * H * kN : nullptr;
 
@@ -101,8 +101,8 @@ __global__ __launch_bounds__(64 * WAVES) void seq_fwd_kernel(
     for (int t0 = 0; t0 < T; t0 += kTB) {
         const int nt = min(kTB, T - t0);
         if (t0 + kTB < T) load_regs(t0 + kTB);
-        if (tape) {   // entry state of chunk t0 / 16 (kTB == 16)
-            bf16_t* dst = tapeS + ((size_t)bh * nch + t0 / kTB) * kN * kN + row;
+        if (tape && t0 % 32 == 0) {   // entry state of block t0 / 32
+            bf16_t* dst = tapeS + ((size_t)bh * nblk + t0 / 32) * kN * kN + row;
             dst[(cq * 4 + 0) * kN] = f2bf(S.x);
             dst[(cq * 4 + 1) * kN] = f2bf(S.y);
             dst[(cq * 4 + 2) * kN] = f2bf(S.z);

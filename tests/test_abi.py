@@ -45,12 +45,12 @@ def test_version_and_status_strings(L):
 
 def test_tape_and_workspace_sizes(L):
     d = wk.make_desc(8, 4096, 40, 64, wk.WKV7_BF16, 16)
-    tape = 8 * 4096 * 40 * 64 * 2 + 8 * 40 * 256 * 64 * 64 * 2
+    tape = 8 * 4096 * 40 * 64 * 2 + 8 * 40 * 128 * 64 * 64 * 2   # states every 32 tokens
     assert wk.tape_bytes(d) == tape
     assert wk.workspace_bytes(d, True) == tape
     assert wk.workspace_bytes(d, False) == 2 * tape
-    d = wk.make_desc(1, 65, 2, 64, wk.WKV7_F32, 0)   # 5 chunks, the last ragged
-    assert wk.tape_bytes(d) == 65 * 2 * 64 * 2 + 2 * 5 * 64 * 64 * 2
+    d = wk.make_desc(1, 65, 2, 64, wk.WKV7_F32, 0)   # 3 blocks of 32 tokens, the last ragged
+    assert wk.tape_bytes(d) == 65 * 2 * 64 * 2 + 2 * 3 * 64 * 64 * 2
     assert wk.tape_bytes(wk.make_desc(3, 0, 2, 64, wk.WKV7_BF16, 16)) == 0
     assert wk.tape_bytes(wk.make_desc(1, 64, 1, 32, wk.WKV7_F32, 0)) == 0   # invalid N
     assert wk.workspace_bytes(wk.make_desc(1, 64, 1, 32, wk.WKV7_F32, 0), True) == 0

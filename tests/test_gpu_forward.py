@@ -120,7 +120,7 @@ def test_chunk_fwd_1_5b_full_sampled(wk):
 @pytest.mark.parametrize("dtype,chunk_len", [("bf16", 0), ("bf16", 16), ("fp32", 0)])
 def test_tape_holds_entry_states_and_removal_readouts(wk, dtype, chunk_len):
     """The forward's tape: z_t = S_{t-1} a_t for every token and the state
-    entering every 16-token chunk (stored key-major), against the oracle's
+    entering every 32-token block (stored key-major), against the oracle's
     prefix states."""
     B, T, H = 1, 75, 2
     inp = synth.generate(B, T, H, 64, dtype=dtype, seed=9, random_s0=True)
@@ -132,10 +132,10 @@ def test_tape_holds_entry_states_and_removal_readouts(wk, dtype, chunk_len):
     zr = np.stack([np.einsum("bhij,bhj->bhi", prefix[t], xs[4][:, t].astype(np.float64))
                    for t in range(T)], axis=1)
     assert_close(z, zr, "bf16", "tape z")
-    nch = (T + 15) // 16
-    assert st.shape == (B, H, nch, 64, 64)
-    for c in range(nch):
-        assert_close(st[:, :, c], np.swapaxes(prefix[16 * c], -1, -2), "bf16", f"tape state {c}")
+    nblk = (T + 31) // 32
+    assert st.shape == (B, H, nblk, 64, 64)
+    for m in range(nblk):
+        assert_close(st[:, :, m], np.swapaxes(prefix[32 * m], -1, -2), "bf16", f"tape state {m}")
 
 
 def test_empty_sequence_copies_state(wk):

@@ -95,8 +95,10 @@ def mfma_under_partial_exec(asm: str, allowed_depth=None):
     return bad
 
 
-# Kernels whose producer/consumer role split (by wave) encloses the MFMA code.
-ROLE_SPLIT = {"chunk_fwd_kernel": 1, "bwd_chain_kernel": 1}
+# Kernels whose role split by wave (producers / inverse wave / consumers: an
+# if, else-if, else on the wave index, two nested exec regions) encloses the
+# MFMA code.
+ROLE_SPLIT = {"chunk_fwd_kernel": 2, "bwd_chain_kernel": 2}
 
 
 def test_scanner_flags_mfma_under_saveexec():
