@@ -473,6 +473,7 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
 // reads and writes only its own rows of the [j][i] states.
 
 constexpr int kP2Threads = 256;   // the four key blocks
+constexpr int kP2Grid = 512;      // two resident workgroups per compute unit, looping over blocks
 
 // Rows of a chunk staged in LDS: the six token inputs the gradients need,
 // then dX and Z; and the entry state and exit adjoint of both chunks as [j][i].
@@ -495,69 +496,92 @@ __device__ __forceinline__ float from_group(float x, int gg, int l16) {
 }
 
 __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
-    int T, int H, int nch, int nblk, const bf16_t* __restrict__ r, const bf16_t* __restrict__ w,
-    const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const bf16_t* __restrict__ a,
-    const bf16_t* __restrict__ b, const bf16_t* __restrict__ dy, const bf16_t* __restrict__ tape,
-    const bf16_t* __restrict__ work, bf16_t* __restrict__ dr, bf16_t* __restrict__ dw,
-    bf16_t* __restrict__ dk, bf16_t* __restrict__ da, bf16_t* __restrict__ db) {
+    int T, int H, int nch, int nblk, int nblocks, const bf16_t* __restrict__ r,
+    const bf16_t* __restrict__ w, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const bf16_t* __restrict__ a, const bf16_t* __restrict__ b, const bf16_t* __restrict__ dy,
+    const bf16_t* __restrict__ tape, const bf16_t* __restrict__ work, bf16_t* __restrict__ dr,
+    bf16_t* __restrict__ dw, bf16_t* __restrict__ dk, bf16_t* __restrict__ da,
+    bf16_t* __restrict__ db) {
     __shared__ P2Smem sm;
-    const int m = blockIdx.x % nblk;
-    const int bh = blockIdx.x / nblk;
-    const int bb = bh / H, hh = bh % H;
-    const int B = gridDim.x / nblk / H;
+    const int B = nblocks / nblk / H;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wp = tid >> 6;
     const int l16 = lane & 15, g = lane >> 4;
     const int col = 16 * wp + l16;     // key column j of this lane
-    const int c0 = 2 * m;
-    const int nh = c0 + 1 < nch ? 2 : 1;   // chunks in this block
     const bf16_t* const tapeZ = tape;
     const bf16_t* const tapeS = tape + (size_t)B * T * H * kN;
     const bf16_t* const wdX = work;
     const bf16_t* const wdS = work + (size_t)B * T * H * kN;
 
-    // ---- stage both chunks through LDS with whole-row loads: 8 threads per
-    // 128-byte row, 16 bytes each.  Tokens past T become padding (w = 1,
-    // everything else 0).  The block's entry state goes to st[0][0], its exit
-    // adjoint to st[1][nh - 1]. ------------------------------------------------------
-    {
-        const int row = (tid >> 3) & 15, piece = tid & 7;
-        // Both chunks are staged even when the block has one (the second is then
-        // all padding and never used): a fixed count keeps the code branch-free.
+    // ---- loads of one block: both chunks' rows as whole 128-byte rows (8 threads
+    // per row, 16 bytes each; threads 0..127: r, k, b, v, Z, 128..255: w, a, dy,
+    // dX), the block's entry state and exit adjoint (two 16-byte pieces each).
+    // Both chunks are loaded even when the block has one (the second is then all
+    // padding and never used).  They are issued one block ahead into registers
+    // and stashed in LDS when the block comes up, tokens past T as padding
+    // (w = 1, everything else 0). ------------------------------------------------
+    const int ld_row = (tid >> 3) & 15, ld_piece = tid & 7;
+    const bool lo = tid < 128;
+    const bf16_t* const src4[4] = {lo ? r : w, lo ? k : a, lo ? b : dy, lo ? v : wdX};
+    struct P2Raw {
+        uint4 x[2][5], s[4];
+    };
+    auto load_block = [&](int bi, P2Raw& o) __attribute__((always_inline)) {
+        const int m = bi % nblk, bh = bi / nblk;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const int t = (c0 + h) * kL + row;
-            const bool ok = t < T;
-            const size_t off = tok_off(bb, min(t, T - 1), hh, T, H) + 8 * piece;
-            auto stage_row = [&](int set, const bf16_t* src, unsigned pad) __attribute__((always_inline)) {
-                const uint4 x = *reinterpret_cast<const uint4*>(src + off);
-                *reinterpret_cast<uint4*>(&sm.rows[h][set][row][8 * piece]) =
-                    ok ? x : make_uint4(pad, pad, pad, pad);
-            };
-            if (tid < 128) {
-                stage_row(P2_R, r, 0u);
-                stage_row(P2_K, k, 0u);
-                stage_row(P2_B, b, 0u);
-                stage_row(P2_V, v, 0u);
-                stage_row(P2_Z, tapeZ, 0u);
-            } else {
-                stage_row(P2_W, w, 0x3F803F80u);
-                stage_row(P2_A, a, 0u);
-                stage_row(P2_DY, dy, 0u);
-                stage_row(P2_DX, wdX, 0u);
-            }
+            const int t = min((2 * m + h) * kL + ld_row, T - 1);
+            const size_t off = tok_off(bh / H, t, bh % H, T, H) + 8 * ld_piece;
+#pragma unroll
+            for (int vi = 0; vi < 4; ++vi) o.x[h][vi] = *reinterpret_cast<const uint4*>(src4[vi] + off);
+            if (lo) o.x[h][4] = *reinterpret_cast<const uint4*>(tapeZ + off);
         }
-        const size_t sbase = ((size_t)bh * nblk + m) * kN * kN;
+        const size_t sbase = (size_t)bi * kN * kN;
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
             const int j = (tid >> 3) + 32 * h2;
-            *reinterpret_cast<uint4*>(&sm.st[0][0][j][8 * piece]) =
-                *reinterpret_cast<const uint4*>(tapeS + sbase + j * kN + 8 * piece);
-            *reinterpret_cast<uint4*>(&sm.st[1][nh - 1][j][8 * piece]) =
-                *reinterpret_cast<const uint4*>(wdS + sbase + j * kN + 8 * piece);
+            o.s[h2] = *reinterpret_cast<const uint4*>(tapeS + sbase + j * kN + 8 * ld_piece);
+            o.s[2 + h2] = *reinterpret_cast<const uint4*>(wdS + sbase + j * kN + 8 * ld_piece);
         }
-    }
+    };
+    auto stash_block = [&](int bi, int nh, const P2Raw& o) __attribute__((always_inline)) {
+        const int m = bi % nblk;
+        const int set_lo[5] = {P2_R, P2_K, P2_B, P2_V, P2_Z};
+        const int set_hi[4] = {P2_W, P2_A, P2_DY, P2_DX};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const bool ok = (2 * m + h) * kL + ld_row < T;
+#pragma unroll
+            for (int vi = 0; vi < 4; ++vi) {
+                const unsigned pad = (!lo && vi == 0) ? 0x3F803F80u : 0u;
+                *reinterpret_cast<uint4*>(&sm.rows[h][lo ? set_lo[vi] : set_hi[vi]][ld_row][8 * ld_piece]) =
+                    ok ? o.x[h][vi] : make_uint4(pad, pad, pad, pad);
+            }
+            if (lo)
+                *reinterpret_cast<uint4*>(&sm.rows[h][P2_Z][ld_row][8 * ld_piece]) =
+                    ok ? o.x[h][4] : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+            const int j = (tid >> 3) + 32 * h2;
+            *reinterpret_cast<uint4*>(&sm.st[0][0][j][8 * ld_piece]) = o.s[h2];
+            *reinterpret_cast<uint4*>(&sm.st[1][nh - 1][j][8 * ld_piece]) = o.s[2 + h2];
+        }
+    };
+
+    // Blocks blockIdx.x, blockIdx.x + gridDim.x, ...: the loads of the next one
+    // are in flight while the current one is computed.
+    P2Raw nxt;
+    if ((int)blockIdx.x < nblocks) load_block(blockIdx.x, nxt);
+    for (int bi = blockIdx.x; bi < nblocks; bi += gridDim.x) {
+    const int m = bi % nblk;
+    const int bh = bi / nblk;
+    const int bb = bh / H, hh = bh % H;
+    const int c0 = 2 * m;
+    const int nh = c0 + 1 < nch ? 2 : 1;   // chunks in this block
+    stash_block(bi, nh, nxt);
     __syncthreads();
+    if (bi + (int)gridDim.x < nblocks) load_block(bi + gridDim.x, nxt);
 
     // ---- decay products and scaled vectors of column `col` in chunk h ----------
     auto factors = [&](int h) __attribute__((always_inline)) -> KeyFactors {
@@ -780,6 +804,8 @@ __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
             }
         }
     }
+    __syncthreads();   // the output rows are read before the next stash overwrites them
+    }
 }
 
 }  // namespace
@@ -803,8 +829,10 @@ hipError_t launch_bwd(const BwdArgs& p, int chunk_len, int stages, hipStream_t s
     if (!(stages & BWD_KEYS)) return hipSuccess;
     const int nch = (p.T + kL - 1) / kL;
     const int nblk = (nch + 1) / 2;
-    bwd_keys_kernel<<<dim3(p.B * p.H * nblk), dim3(kP2Threads), 0, stream>>>(
-        p.T, p.H, nch, nblk, r, w, k, v, a, b, dy, static_cast<const bf16_t*>(p.tape), work,
+    const int nblocks = p.B * p.H * nblk;
+    const int grid = nblocks < kP2Grid ? nblocks : kP2Grid;
+    bwd_keys_kernel<<<dim3(grid), dim3(kP2Threads), 0, stream>>>(
+        p.T, p.H, nch, nblk, nblocks, r, w, k, v, a, b, dy, static_cast<const bf16_t*>(p.tape), work,
         static_cast<bf16_t*>(p.dr), static_cast<bf16_t*>(p.dw), static_cast<bf16_t*>(p.dk),
         static_cast<bf16_t*>(p.da), static_cast<bf16_t*>(p.db));
     return hipGetLastError();
