@@ -167,6 +167,12 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
         for (int p = 0; p < 3; ++p) o.x[p] = *reinterpret_cast<const u32x4*>(sp_p[p] + off);
     };
     auto stash_raw = [&](int c, const Raw& o) __attribute__((always_inline)) {
+        if (c >= 0 && (c + 1) * kL <= T) {   // a whole chunk (the common case: no selects)
+#pragma unroll
+            for (int p = 0; p < 3; ++p)
+                *reinterpret_cast<u32x4*>(&sm.raw[c & 1][2 * p + (hi ? 1 : 0)][ld_t][ld_c8 * 8]) = o.x[p];
+            return;
+        }
         const int t = c * kL + ld_t;
         const bool ok = c >= 0 && t < T;
 #pragma unroll
@@ -206,9 +212,11 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
             X[vi][3] = __uint_as_float(raw6[vi].y & 0xFFFF0000u);
         }
         f32x4 at, rt, bh4, kh4, bb4, kb4, gt;
+        float G4[4] = {X[P1_W][0], X[P1_W][1], X[P1_W][2], X[P1_W][3]};
+        row16_cumprod4(G4[0], G4[1], G4[2], G4[3]);
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
-            const float Gt = row16_cumprod(X[P1_W][cc]);
+            const float Gt = G4[cc];
             const float Gp = row16_prev(Gt, 1.f);
             const float GL = row16_last(Gt);
             const float inv = __builtin_amdgcn_rcpf(Gt);

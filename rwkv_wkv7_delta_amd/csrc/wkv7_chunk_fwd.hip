@@ -153,6 +153,12 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
         for (int p = 0; p < 3; ++p) o.x[p] = *reinterpret_cast<const u32x4*>(sp_p[p] + off);
     };
     auto stash_raw = [&](int c, const Raw& o) __attribute__((always_inline)) {
+        if ((c + 1) * kL <= T) {   // a whole chunk (the common case: no selects)
+#pragma unroll
+            for (int p = 0; p < 3; ++p)
+                *reinterpret_cast<u32x4*>(&sm.raw[c & 1][2 * p + (hi ? 1 : 0)][ld_t][ld_c8 * 8]) = o.x[p];
+            return;
+        }
         const bool ok = c * kL + ld_t < T;
 #pragma unroll
         for (int p = 0; p < 3; ++p) {
@@ -191,9 +197,11 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
             X[vi][3] = __uint_as_float(raw6[vi].y & 0xFFFF0000u);
         }
         f32x4 at, rt, bh4, kh4, bb4, kb4, gt;
+        float G4[4] = {X[RAW_W][0], X[RAW_W][1], X[RAW_W][2], X[RAW_W][3]};
+        row16_cumprod4(G4[0], G4[1], G4[2], G4[3]);
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
-            const float Gt = row16_cumprod(X[RAW_W][cc]);
+            const float Gt = G4[cc];
             const float Gp = row16_prev(Gt, 1.f);
             const float GL = row16_last(Gt);
             const float inv = __builtin_amdgcn_rcpf(Gt);

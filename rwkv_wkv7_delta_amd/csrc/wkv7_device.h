@@ -78,6 +78,33 @@ __device__ __forceinline__ float row16_cumprod(float x) {
     x *= __builtin_amdgcn_update_dpp(1.0f, x, 0x118, 0xF, 0xF, false);
     return x;
 }
+// The same running product for four independent values at once, one DPP
+// multiply per step: with the bound control off, a lane whose source lies
+// outside its row is left unwritten, i.e. keeps x (x times 1).  The leading
+// s_nop gives the two wait states a DPP read needs after the VALU write of its
+// operand; inside, each operand was written three instructions earlier.
+__device__ __forceinline__ void row16_cumprod4(float& x0, float& x1, float& x2, float& x3) {
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_mul_f32_dpp %0, %0, %0 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %1, %1, %1 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %2, %2, %2 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %3, %3, %3 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %0, %0, %0 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %1, %1, %1 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %2, %2, %2 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %3, %3, %3 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %0, %0, %0 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %1, %1, %1 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %2, %2, %2 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %3, %3, %3 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %0, %0, %0 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %1, %1, %1 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %2, %2, %2 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %3, %3, %3 row_shr:8 row_mask:0xf bank_mask:0xf"
+        : "+v"(x0), "+v"(x1), "+v"(x2), "+v"(x3));
+}
+
 // The value of the previous lane of the row (row_shr 1); the row's first lane gets `first`.
 __device__ __forceinline__ float row16_prev(float x, float first) {
     return __builtin_amdgcn_update_dpp(first, x, 0x111, 0xF, 0xF, false);
