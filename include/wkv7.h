@@ -98,7 +98,7 @@ size_t wkv7_tape_bytes(const wkv7_desc *desc);
 /* Bytes of device scratch wkv7_backward needs: with_tape != 0 when the caller
    passes a tape written by wkv7_forward (the backward then keeps one per-token
    intermediate adjoint and the adjoint of the state leaving every 32-token block
-   there, as much again as the tape), with_tape = 0 when it passes none (then a forward re-run also
+   there, as much again as the tape, plus 256 bytes of work queues), with_tape = 0 when it passes none (then a forward re-run also
    writes its tape into the workspace: twice the tape).  0 on an invalid
    descriptor. */
 size_t wkv7_workspace_bytes(const wkv7_desc *desc, int with_tape);
@@ -172,6 +172,25 @@ int wkv7_backward_gradients(const wkv7_desc *desc, const void *r, const void *w,
                             const void *dy, const float *dsT, const void *tape, void *dr,
                             void *dw, void *dk, void *dv, void *da, void *db, float *ds0,
                             void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * wkv7_backward on two streams, for callers that have a second one: same
+ * arguments and results, plus `aux_stream` (a hipStream_t as void*, or NULL =
+ * plain wkv7_backward on `stream`).  When B*H exceeds the device's compute
+ * units and B > 1, the batch rows split into a first group that fills the
+ * device with one workgroup per head and the rest; the first group's per-key
+ * pass runs on aux_stream beside the second group's adjoint chain (the chain
+ * is one workgroup per head, so it alone would leave most of the device idle
+ * in its last round).  All work has finished, as seen from `stream`, when the
+ * work enqueued on `stream` has: `stream` waits for aux_stream's part.  The
+ * library creates and destroys two events per call; it never synchronises.
+ */
+int wkv7_backward_overlapped(const wkv7_desc *desc, const void *r, const void *w, const void *k,
+                             const void *v, const void *a, const void *b, const float *s0,
+                             const void *dy, const float *dsT, const void *tape, void *dr,
+                             void *dw, void *dk, void *dv, void *da, void *db, float *ds0,
+                             void *workspace, size_t workspace_bytes, void *stream,
+                             void *aux_stream);
 
 /*
  * One token on B*H resident states, in place: constant memory and constant

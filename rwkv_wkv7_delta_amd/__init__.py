@@ -33,7 +33,7 @@ TAPE_BLOCK = 32
 
 EXPORTED = ("wkv7_abi_version", "wkv7_status_string", "wkv7_tape_bytes", "wkv7_workspace_bytes",
             "wkv7_forward", "wkv7_backward", "wkv7_backward_adjoint", "wkv7_backward_gradients",
-            "wkv7_decode_step")
+            "wkv7_backward_overlapped", "wkv7_decode_step")
 
 
 class WKV7Error(RuntimeError):
@@ -78,6 +78,8 @@ def lib():
             fn = getattr(L, name)
             fn.argtypes = [D] + [P] * 6 + [P, P, P, P] + [P] * 6 + [P, P, Z, P]
             fn.restype = ctypes.c_int
+        L.wkv7_backward_overlapped.argtypes = [D] + [P] * 6 + [P, P, P, P] + [P] * 6 + [P, P, Z, P, P]
+        L.wkv7_backward_overlapped.restype = ctypes.c_int
         L.wkv7_decode_step.argtypes = [I, I, I, I] + [P] * 6 + [P, P, P]
         L.wkv7_decode_step.restype = ctypes.c_int
         _lib = L
@@ -176,17 +178,20 @@ def forward(r, w, k, v, a, b, s0=None, *, chunk_len: int = 0, want_state: bool =
 
 
 _STAGES = {"all": "wkv7_backward", "adjoint": "wkv7_backward_adjoint",
-           "gradients": "wkv7_backward_gradients"}
+           "gradients": "wkv7_backward_gradients", "overlapped": "wkv7_backward_overlapped"}
 
 
 def backward(r, w, k, v, a, b, dy, s0=None, dsT=None, tape=None, *, chunk_len: int = 16,
-             want_ds0: bool = True, workspace=None, stage: str = "all", grads=None, ds0=None):
+             want_ds0: bool = True, workspace=None, stage: str = "all", grads=None, ds0=None,
+             aux_stream=None):
     """Gradients of ``<dy, y> + <dsT, S_T>``: returns (dr, dw, dk, dv, da, db, ds0).
 
     ``tape`` is the one ``forward(..., want_tape=True)`` returned for the same
     inputs, or None (the forward is then re-run inside the call).  ``stage``
     selects the whole backward ("all") or one of its two stages ("adjoint",
     then "gradients" with the same ``workspace``, ``grads`` and ``ds0``).
+    ``aux_stream`` (a torch stream) runs the whole backward on two streams
+    (wkv7_backward_overlapped).
     """
     torch = _torch()
     B, T, H, N = r.shape
@@ -206,10 +211,14 @@ def backward(r, w, k, v, a, b, dy, s0=None, dsT=None, tape=None, *, chunk_len: i
         ws = torch.empty(max(wsb // 4, 4), device=r.device, dtype=torch.float32)
     else:
         wsb = ws.numel() * ws.element_size()
-    name = _STAGES[stage]
+    name = _STAGES["overlapped" if aux_stream is not None else stage]
+    if aux_stream is not None and stage != "all":
+        raise ValueError("aux_stream applies to the whole backward only")
+    extra = (aux_stream.cuda_stream,) if aux_stream is not None else ()
     st = getattr(lib(), name)(ctypes.byref(desc), _ptr(r), _ptr(w), _ptr(k), _ptr(v), _ptr(a),
                               _ptr(b), _ptr(s0), _ptr(dy), _ptr(dsT), _ptr(tape),
-                              *[_ptr(x) for x in grads], _ptr(ds0), _ptr(ws), wsb, _stream())
+                              *[_ptr(x) for x in grads], _ptr(ds0), _ptr(ws), wsb, _stream(),
+                              *extra)
     if st != WKV7_OK:
         raise WKV7Error(st, name)
     return tuple(grads) + (ds0,)

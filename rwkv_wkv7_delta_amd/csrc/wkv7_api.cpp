@@ -39,6 +39,12 @@ size_t tape_bytes_unchecked(const wkv7_desc* d) {
     return (tok + st) * 2;
 }
 
+// Workspace of the backward: its own scratch (dX per token, then the adjoint
+// leaving every 32-token block: as large as the tape), the per-key pass's
+// block queues (two groups of two ints, in 256 bytes), then -- when no tape is
+// passed -- the tape of a forward re-run.
+constexpr size_t kQueueBytes = 256;
+
 int from_hip(hipError_t e) { return e == hipSuccess ? WKV7_OK : WKV7_ERR_LAUNCH; }
 
 int run_forward(const wkv7_desc* d, const void* r, const void* w, const void* k, const void* v,
@@ -78,7 +84,7 @@ size_t wkv7_tape_bytes(const wkv7_desc* desc) {
 
 size_t wkv7_workspace_bytes(const wkv7_desc* desc, int with_tape) {
     if (check_desc(desc) != WKV7_OK) return 0;
-    return tape_bytes_unchecked(desc) * (with_tape ? 1 : 2);
+    return tape_bytes_unchecked(desc) * (with_tape ? 1 : 2) + kQueueBytes;
 }
 
 int wkv7_forward(const wkv7_desc* desc, const void* r, const void* w, const void* k,
@@ -97,16 +103,43 @@ int wkv7_forward(const wkv7_desc* desc, const void* r, const void* w, const void
 
 namespace {
 
-// Shared by wkv7_backward and its two stage entry points.
+// The backward's arguments restricted to batch rows [b0, b0 + nb).
+wkv7::BwdArgs slice(const wkv7_desc* d, int b0, int nb, const void* r, const void* w,
+                    const void* k, const void* v, const void* a, const void* b, const float* s0,
+                    const void* dy, const float* dsT, const void* tape, void* dr, void* dw,
+                    void* dk, void* dv, void* da, void* db, float* ds0, void* workspace,
+                    int group) {
+    const size_t tok = (size_t)d->T * d->H * d->N;                 // elements per batch row
+    const size_t nblk = ((size_t)d->T + WKV7_TAPE_BLOCK - 1) / WKV7_TAPE_BLOCK;
+    const size_t st = (size_t)d->H * nblk * d->N * d->N;         // elements per batch row
+    const size_t sst = (size_t)d->H * d->N * d->N;               // fp32 state elements per row
+    const size_t ztot = (size_t)d->B * tok;
+    auto tk = [&](const void* p) -> const void* {
+        return p ? static_cast<const uint16_t*>(p) + (size_t)b0 * tok : nullptr;
+    };
+    auto tkm = [&](void* p) -> void* { return static_cast<uint16_t*>(p) + (size_t)b0 * tok; };
+    auto sf = [&](const float* p) -> const float* { return p ? p + (size_t)b0 * sst : nullptr; };
+    const uint16_t* tp = static_cast<const uint16_t*>(tape);
+    uint16_t* wsp = static_cast<uint16_t*>(workspace);
+    int* queue = reinterpret_cast<int*>(static_cast<char*>(workspace) + tape_bytes_unchecked(d)) + 2 * group;
+    return wkv7::BwdArgs{nb, d->T, d->H, true, tk(r), tk(w), tk(k), tk(v), tk(a), tk(b), sf(s0),
+                         tk(dy), sf(dsT), tp + (size_t)b0 * tok, tp + ztot + (size_t)b0 * st,
+                         tkm(dr), tkm(dw), tkm(dk), tkm(dv), tkm(da), tkm(db),
+                         ds0 ? ds0 + (size_t)b0 * sst : nullptr, wsp + (size_t)b0 * tok,
+                         wsp + ztot + (size_t)b0 * st, queue};
+}
+
+// Shared by every backward entry point.  stages: the passes to run; aux: a
+// second stream (or null) that lets the per-key pass of the first batch rows
+// overlap the adjoint chain of the remaining ones.
 int run_backward(const wkv7_desc* desc, const void* r, const void* w, const void* k,
                  const void* v, const void* a, const void* b, const float* s0, const void* dy,
                  const float* dsT, const void* tape, void* dr, void* dw, void* dk, void* dv,
                  void* da, void* db, float* ds0, void* workspace, size_t workspace_bytes,
-                 void* stream, int stages) {
+                 void* stream, int stages, void* aux) {
     int st = check_desc(desc);
     if (st != WKV7_OK) return st;
-    // The backward runs the chunked adjoint on bf16 matrix cores, one workgroup
-    // per chunk and head in its second pass.
+    // The backward runs the chunked adjoint on bf16 matrix cores.
     if (desc->dtype != WKV7_BF16) return WKV7_ERR_UNSUPPORTED;
     if ((int64_t)desc->B * desc->H * ((desc->T + WKV7_TAPE_CHUNK - 1) / WKV7_TAPE_CHUNK) > INT32_MAX)
         return WKV7_ERR_UNSUPPORTED;
@@ -120,7 +153,7 @@ int run_backward(const wkv7_desc* desc, const void* r, const void* w, const void
     // chain's results to the second stage, and a re-run would overwrite it.
     if (stages != (wkv7::BWD_CHAIN | wkv7::BWD_KEYS) && has_tokens && !tape)
         return WKV7_ERR_INVALID_ARG;
-    const size_t need = tape_bytes_unchecked(desc) * (tape ? 1 : 2);
+    const size_t need = tape_bytes_unchecked(desc) * (tape ? 1 : 2) + kQueueBytes;
     if (has_tokens && (workspace == nullptr || workspace_bytes < need)) return WKV7_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if ((int64_t)desc->B * desc->H == 0) return WKV7_OK;
@@ -132,15 +165,48 @@ int run_backward(const wkv7_desc* desc, const void* r, const void* w, const void
     }
     char* ws = static_cast<char*>(workspace);
     if (!tape) {
-        // Re-run the forward (without y) into the second half of the workspace.
-        void* own = ws + tape_bytes_unchecked(desc);
+        // Re-run the forward (without y) into the last part of the workspace.
+        void* own = ws + tape_bytes_unchecked(desc) + kQueueBytes;
         st = run_forward(desc, r, w, k, v, a, b, s0, nullptr, nullptr, own, s);
         if (st != WKV7_OK) return st;
         tape = own;
     }
-    wkv7::BwdArgs p{desc->B, desc->T, desc->H, true, r, w, k, v, a, b, s0, dy, dsT, tape,
-                    dr, dw, dk, dv, da, db, ds0, ws};
-    return from_hip(wkv7::launch_bwd(p, 16, stages, s));
+    // Two groups of batch rows when a second stream is given and the heads
+    // exceed one per compute unit: the first group's chain fills the device
+    // in one round, and its per-key pass runs beside the second group's chain.
+    int b1 = desc->B;
+    if (aux && desc->B > 1) {
+        int dev = 0, ncu = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            (int64_t)desc->B * desc->H > ncu) {
+            b1 = ncu / desc->H;
+            if (b1 < 1) b1 = 1;
+            if (b1 > desc->B - 1) b1 = desc->B - 1;
+        }
+    }
+    const wkv7::BwdArgs g1 = slice(desc, 0, b1, r, w, k, v, a, b, s0, dy, dsT, tape, dr, dw, dk, dv,
+                                   da, db, ds0, ws, 0);
+    if (b1 == desc->B) return from_hip(wkv7::launch_bwd(g1, 16, stages, s));
+    const wkv7::BwdArgs g2 = slice(desc, b1, desc->B - b1, r, w, k, v, a, b, s0, dy, dsT, tape,
+                                   dr, dw, dk, dv, da, db, ds0, ws, 1);
+    hipStream_t s2 = static_cast<hipStream_t>(aux);
+    hipEvent_t chained = nullptr, keyed = nullptr;
+    if (hipEventCreateWithFlags(&chained, hipEventDisableTiming) != hipSuccess) return WKV7_ERR_LAUNCH;
+    if (hipEventCreateWithFlags(&keyed, hipEventDisableTiming) != hipSuccess) {
+        hipEventDestroy(chained);
+        return WKV7_ERR_LAUNCH;
+    }
+    hipError_t e = wkv7::launch_bwd(g1, 16, wkv7::BWD_CHAIN, s);
+    if (e == hipSuccess) e = hipEventRecord(chained, s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s2, chained, 0);
+    if (e == hipSuccess) e = wkv7::launch_bwd(g1, 16, wkv7::BWD_KEYS, s2);
+    if (e == hipSuccess) e = hipEventRecord(keyed, s2);
+    if (e == hipSuccess) e = wkv7::launch_bwd(g2, 16, wkv7::BWD_CHAIN | wkv7::BWD_KEYS, s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s, keyed, 0);
+    hipEventDestroy(chained);
+    hipEventDestroy(keyed);
+    return from_hip(e);
 }
 
 }  // namespace
@@ -153,7 +219,18 @@ int wkv7_backward(const wkv7_desc* desc, const void* r, const void* w, const voi
                   void* da, void* db, float* ds0, void* workspace, size_t workspace_bytes,
                   void* stream) {
     return run_backward(desc, r, w, k, v, a, b, s0, dy, dsT, tape, dr, dw, dk, dv, da, db, ds0,
-                        workspace, workspace_bytes, stream, wkv7::BWD_CHAIN | wkv7::BWD_KEYS);
+                        workspace, workspace_bytes, stream, wkv7::BWD_CHAIN | wkv7::BWD_KEYS,
+                        nullptr);
+}
+
+int wkv7_backward_overlapped(const wkv7_desc* desc, const void* r, const void* w, const void* k,
+                             const void* v, const void* a, const void* b, const float* s0,
+                             const void* dy, const float* dsT, const void* tape, void* dr, void* dw,
+                             void* dk, void* dv, void* da, void* db, float* ds0, void* workspace,
+                             size_t workspace_bytes, void* stream, void* aux_stream) {
+    return run_backward(desc, r, w, k, v, a, b, s0, dy, dsT, tape, dr, dw, dk, dv, da, db, ds0,
+                        workspace, workspace_bytes, stream, wkv7::BWD_CHAIN | wkv7::BWD_KEYS,
+                        aux_stream);
 }
 
 int wkv7_backward_adjoint(const wkv7_desc* desc, const void* r, const void* w, const void* k,
@@ -162,7 +239,7 @@ int wkv7_backward_adjoint(const wkv7_desc* desc, const void* r, const void* w, c
                           void* dk, void* dv, void* da, void* db, float* ds0, void* workspace,
                           size_t workspace_bytes, void* stream) {
     return run_backward(desc, r, w, k, v, a, b, s0, dy, dsT, tape, dr, dw, dk, dv, da, db, ds0,
-                        workspace, workspace_bytes, stream, wkv7::BWD_CHAIN);
+                        workspace, workspace_bytes, stream, wkv7::BWD_CHAIN, nullptr);
 }
 
 int wkv7_backward_gradients(const wkv7_desc* desc, const void* r, const void* w, const void* k,
@@ -171,7 +248,7 @@ int wkv7_backward_gradients(const wkv7_desc* desc, const void* r, const void* w,
                             void* dw, void* dk, void* dv, void* da, void* db, float* ds0,
                             void* workspace, size_t workspace_bytes, void* stream) {
     return run_backward(desc, r, w, k, v, a, b, s0, dy, dsT, tape, dr, dw, dk, dv, da, db, ds0,
-                        workspace, workspace_bytes, stream, wkv7::BWD_KEYS);
+                        workspace, workspace_bytes, stream, wkv7::BWD_KEYS, nullptr);
 }
 
 int wkv7_decode_step(int32_t B, int32_t H, int32_t N, int32_t dtype, const void* r,

@@ -110,11 +110,11 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
     int T, int H, const bf16_t* __restrict__ r, const bf16_t* __restrict__ w,
     const bf16_t* __restrict__ k, const bf16_t* __restrict__ a, const bf16_t* __restrict__ b,
     const bf16_t* __restrict__ dy, const float* __restrict__ dsT, bf16_t* __restrict__ dv,
-    float* __restrict__ ds0, bf16_t* __restrict__ work) {
+    float* __restrict__ ds0, bf16_t* __restrict__ wdX, bf16_t* __restrict__ wdS,
+    int* __restrict__ counter) {
     __shared__ P1Smem sm;
     const int bh = blockIdx.x;
     const int bb = bh / H, hh = bh % H;
-    const int B = gridDim.x / H;
     const int tid = threadIdx.x;
     // Roles split by wave (the tests are uniform within a wave).  They are left
     // as per-lane conditions: branching on an SGPR copy of the wave index
@@ -128,8 +128,7 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
     const int l16 = lane & 15, g = lane >> 4;
     const int col = 16 * wp + l16;
     const int nch = (T + kL - 1) / kL;
-    bf16_t* const wdX = work;                                   // [B][T][H][N]
-    bf16_t* const wdS = work + (size_t)B * T * H * kN;          // [B][H][nblk][N][N]
+    // wdX: [B][T][H][N]; wdS: [B][H][nblk][N][N]
     const int nblk = (nch + 1) / 2;
     // The adjoint leaving a 32-token block: after chunk c when c is odd or the last.
     auto keeps_dS = [&](int c) __attribute__((always_inline)) { return c >= 0 && ((c & 1) || c == nch - 1); };
@@ -138,6 +137,12 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
     auto chunk_of = [&](int it) __attribute__((always_inline)) { return nch - 1 - it; };
     // (chunk indices reach -6 in the padding intervals)
     auto slot_of = [&](int c) __attribute__((always_inline)) { return (c + 9) % 3; };
+
+    // The per-key pass that follows takes its blocks from a queue: start it empty.
+    if (blockIdx.x == 0 && tid == 0) {
+        counter[0] = 0;
+        counter[1] = 0;
+    }
 
     // ---- consumer adjoint: dS^T tiles, lane holds dS[col][16 jt + 4 g + q] -------
     f32x4 dSt[4];
@@ -507,19 +512,16 @@ __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
     int T, int H, int nch, int nblk, int nblocks, const bf16_t* __restrict__ r,
     const bf16_t* __restrict__ w, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ a, const bf16_t* __restrict__ b, const bf16_t* __restrict__ dy,
-    const bf16_t* __restrict__ tape, const bf16_t* __restrict__ work, bf16_t* __restrict__ dr,
+    const bf16_t* __restrict__ tapeZ, const bf16_t* __restrict__ tapeS,
+    const bf16_t* __restrict__ wdX, const bf16_t* __restrict__ wdS, bf16_t* __restrict__ dr,
     bf16_t* __restrict__ dw, bf16_t* __restrict__ dk, bf16_t* __restrict__ da,
-    bf16_t* __restrict__ db) {
+    bf16_t* __restrict__ db, int* __restrict__ counter) {
     __shared__ P2Smem sm;
-    const int B = nblocks / nblk / H;
+    __shared__ int next_block;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wp = tid >> 6;
     const int l16 = lane & 15, g = lane >> 4;
     const int col = 16 * wp + l16;     // key column j of this lane
-    const bf16_t* const tapeZ = tape;
-    const bf16_t* const tapeS = tape + (size_t)B * T * H * kN;
-    const bf16_t* const wdX = work;
-    const bf16_t* const wdS = work + (size_t)B * T * H * kN;
 
     // ---- loads of one block: both chunks' rows as whole 128-byte rows (8 threads
     // per row, 16 bytes each; threads 0..127: r, k, b, v, Z, 128..255: w, a, dy,
@@ -577,19 +579,25 @@ __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
         }
     };
 
-    // Blocks blockIdx.x, blockIdx.x + gridDim.x, ...: the loads of the next one
-    // are in flight while the current one is computed.
+    // Blocks come from a queue (counter[0]), so workgroups that start late (the
+    // compute units may still be busy with other work) simply take fewer; the
+    // loads of the next block are in flight while the current one is computed.
+    if (tid == 0) next_block = atomicAdd(&counter[0], 1);
+    __syncthreads();
+    int bi = next_block;
     P2Raw nxt;
-    if ((int)blockIdx.x < nblocks) load_block(blockIdx.x, nxt);
-    for (int bi = blockIdx.x; bi < nblocks; bi += gridDim.x) {
+    if (bi < nblocks) load_block(bi, nxt);
+    while (bi < nblocks) {
     const int m = bi % nblk;
     const int bh = bi / nblk;
     const int bb = bh / H, hh = bh % H;
     const int c0 = 2 * m;
     const int nh = c0 + 1 < nch ? 2 : 1;   // chunks in this block
     stash_block(bi, nh, nxt);
+    if (tid == 0) next_block = atomicAdd(&counter[0], 1);
     __syncthreads();
-    if (bi + (int)gridDim.x < nblocks) load_block(bi + gridDim.x, nxt);
+    const int bn = next_block;
+    if (bn < nblocks) load_block(bn, nxt);
 
     // ---- decay products and scaled vectors of column `col` in chunk h ----------
     auto factors = [&](int h) __attribute__((always_inline)) -> KeyFactors {
@@ -813,6 +821,12 @@ __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
         }
     }
     __syncthreads();   // the output rows are read before the next stash overwrites them
+    bi = bn;
+    }
+    // The last workgroup out empties the queue for the next launch.
+    if (tid == 0 && atomicAdd(&counter[1], 1) == (int)gridDim.x - 1) {
+        counter[0] = 0;
+        counter[1] = 0;
     }
 }
 
@@ -827,10 +841,10 @@ hipError_t launch_bwd(const BwdArgs& p, int chunk_len, int stages, hipStream_t s
     const bf16_t* a = static_cast<const bf16_t*>(p.a);
     const bf16_t* b = static_cast<const bf16_t*>(p.b);
     const bf16_t* dy = static_cast<const bf16_t*>(p.dy);
-    bf16_t* work = static_cast<bf16_t*>(p.work);
     if (stages & BWD_CHAIN) {
         bwd_chain_kernel<<<dim3(p.B * p.H), dim3(kP1Threads), 0, stream>>>(
-            p.T, p.H, r, w, k, a, b, dy, p.dsT, static_cast<bf16_t*>(p.dv), p.ds0, work);
+            p.T, p.H, r, w, k, a, b, dy, p.dsT, static_cast<bf16_t*>(p.dv), p.ds0,
+            static_cast<bf16_t*>(p.workX), static_cast<bf16_t*>(p.workS), p.counter);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -840,9 +854,10 @@ hipError_t launch_bwd(const BwdArgs& p, int chunk_len, int stages, hipStream_t s
     const int nblocks = p.B * p.H * nblk;
     const int grid = nblocks < kP2Grid ? nblocks : kP2Grid;
     bwd_keys_kernel<<<dim3(grid), dim3(kP2Threads), 0, stream>>>(
-        p.T, p.H, nch, nblk, nblocks, r, w, k, v, a, b, dy, static_cast<const bf16_t*>(p.tape), work,
-        static_cast<bf16_t*>(p.dr), static_cast<bf16_t*>(p.dw), static_cast<bf16_t*>(p.dk),
-        static_cast<bf16_t*>(p.da), static_cast<bf16_t*>(p.db));
+        p.T, p.H, nch, nblk, nblocks, r, w, k, v, a, b, dy, static_cast<const bf16_t*>(p.tapeZ),
+        static_cast<const bf16_t*>(p.tapeS), static_cast<const bf16_t*>(p.workX),
+        static_cast<const bf16_t*>(p.workS), static_cast<bf16_t*>(p.dr), static_cast<bf16_t*>(p.dw),
+        static_cast<bf16_t*>(p.dk), static_cast<bf16_t*>(p.da), static_cast<bf16_t*>(p.db), p.counter);
     return hipGetLastError();
 }
 

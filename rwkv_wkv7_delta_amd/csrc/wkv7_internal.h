@@ -17,16 +17,19 @@ struct FwdArgs {
 };
 
 struct BwdArgs {
-    int B, T, H;
+    int B, T, H;        // B: the batch rows of this call (a slice of the caller's)
     bool bf16;
     const void *r, *w, *k, *v, *a, *b;
     const float* s0;   // may be null
     const void* dy;
     const float* dsT;  // may be null
-    const void* tape;  // written by the forward (never null here)
+    const void* tapeZ; // removal read-outs [B][T][H][N] bf16, written by the forward
+    const void* tapeS; // block entry states [B][H][nblk][N][N] bf16, written by the forward
     void *dr, *dw, *dk, *dv, *da, *db;
     float* ds0;        // may be null
-    void* work;        // dX [B][T][H][N] bf16, then incoming dS [B][H][nch][N][N] bf16
+    void* workX;       // dX [B][T][H][N] bf16
+    void* workS;       // adjoint leaving every 32-token block [B][H][nblk][N][N] bf16
+    int* counter;      // two ints: the per-key pass's block queue (reset by both passes)
 };
 
 struct DecodeArgs {

@@ -47,8 +47,8 @@ def test_tape_and_workspace_sizes(L):
     d = wk.make_desc(8, 4096, 40, 64, wk.WKV7_BF16, 16)
     tape = 8 * 4096 * 40 * 64 * 2 + 8 * 40 * 128 * 64 * 64 * 2   # states every 32 tokens
     assert wk.tape_bytes(d) == tape
-    assert wk.workspace_bytes(d, True) == tape
-    assert wk.workspace_bytes(d, False) == 2 * tape
+    assert wk.workspace_bytes(d, True) == tape + 256      # + the per-key pass's work queues
+    assert wk.workspace_bytes(d, False) == 2 * tape + 256
     d = wk.make_desc(1, 65, 2, 64, wk.WKV7_F32, 0)   # 3 blocks of 32 tokens, the last ragged
     assert wk.tape_bytes(d) == 65 * 2 * 64 * 2 + 2 * 3 * 64 * 64 * 2
     assert wk.tape_bytes(wk.make_desc(3, 0, 2, 64, wk.WKV7_BF16, 16)) == 0
@@ -124,6 +124,22 @@ def test_backward_stage_validation(L):
             wk.WKV7_ERR_UNSUPPORTED, name
         d0 = wk.make_desc(0, 8, 1, 64, wk.WKV7_BF16, 16)
         assert f(ctypes.byref(d0), *args, None, *grads, None, None, 0, None) == wk.WKV7_OK, name
+
+
+def test_backward_overlapped_validation(L):
+    """wkv7_backward_overlapped validates exactly like wkv7_backward (aux stream or not)."""
+    d = wk.make_desc(1, 8, 1, 64, wk.WKV7_BF16, 16)
+    args = [FAKE] * 6 + [None, FAKE, None]
+    grads = [FAKE] * 6
+    f = L.wkv7_backward_overlapped
+    for aux in (None, FAKE):
+        assert f(ctypes.byref(d), *args, None, *grads, None, None, 0, None, aux) == wk.WKV7_ERR_WORKSPACE
+        assert f(ctypes.byref(d), *args, None, *[FAKE] * 5, None, None, FAKE, 1 << 30, None, aux) == \
+            wk.WKV7_ERR_INVALID_ARG
+        d32 = wk.make_desc(1, 8, 1, 64, wk.WKV7_F32, 0)
+        assert f(ctypes.byref(d32), *args, FAKE, *grads, None, None, 0, None, aux) == wk.WKV7_ERR_UNSUPPORTED
+        d0 = wk.make_desc(0, 8, 1, 64, wk.WKV7_BF16, 16)
+        assert f(ctypes.byref(d0), *args, FAKE, *grads, None, None, 0, None, aux) == wk.WKV7_OK
 
 
 def test_decode_validation(L):

@@ -83,6 +83,42 @@ def test_bwd_stages_compose_to_backward(wk):
     assert torch.equal(ds0, whole[6])
 
 
+@pytest.mark.parametrize("use_tape", [True, False])
+def test_bwd_overlapped_matches_single_stream(wk, use_tape):
+    """wkv7_backward_overlapped (two batch-row groups, the first group's per-key
+    pass on a second stream) == wkv7_backward, bit for bit, at 320 heads (more
+    than one per compute unit); the per-key pass's block queue resets itself, so
+    a second gradients stage on the same workspace repeats the result."""
+    import torch
+    B, T, H = 8, 96, 40
+    inp = synth.generate(B, T, H, 64, dtype="bf16", seed=31, random_s0=True, backward=True)
+    dev = [to_dev(x, "bf16") for x in inp.tensors()]
+    s0 = to_dev(inp.s0, "fp32")
+    dy = to_dev(inp.dy, "bf16")
+    dsT = to_dev((0.1 * np.random.default_rng(5).standard_normal(inp.s0.shape)).astype(np.float32), "fp32")
+    tape = None
+    if use_tape:
+        _, _, tape = wk.forward(*dev, s0, chunk_len=16, want_state=False, want_tape=True)
+    ref = wk.backward(*dev, dy, s0, dsT, tape)
+    aux = torch.cuda.Stream()
+    got = wk.backward(*dev, dy, s0, dsT, tape, aux_stream=aux)
+    torch.cuda.synchronize()
+    for i, name in enumerate(NAMES):
+        assert torch.equal(got[i], ref[i]), name
+    if use_tape:
+        desc = wk.make_desc(B, T, H, 64, wk.WKV7_BF16, 16)
+        ws = torch.empty(wk.workspace_bytes(desc, True) // 4, device=s0.device)
+        grads = [torch.empty_like(dev[0]) for _ in range(6)]
+        wk.backward(*dev, dy, s0, dsT, tape, workspace=ws, stage="adjoint", grads=grads)
+        for rep in range(2):
+            for i in (0, 1, 2, 4, 5):
+                grads[i].fill_(7.0)
+            wk.backward(*dev, dy, s0, dsT, tape, workspace=ws, stage="gradients", grads=grads)
+            torch.cuda.synchronize()
+            for i in range(6):
+                assert torch.equal(grads[i], ref[i]), (rep, NAMES[i])
+
+
 @pytest.mark.parametrize("fwd_chunk", [0, 16])
 def test_bwd_without_tape_matches_tape_path(wk, fwd_chunk):
     """Without a tape the library re-runs the forward (sequential or chunked) into
