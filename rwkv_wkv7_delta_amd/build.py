@@ -26,6 +26,10 @@ COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Matrix-core results stay in ordinary VGPRs (the kernels read every
+    # accumulator tile back on the vector ALU; accumulation registers would need
+    # a copy instruction per element).
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wno-unused-command-line-argument",
 ]
 
