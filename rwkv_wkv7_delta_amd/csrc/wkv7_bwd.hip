@@ -496,6 +496,8 @@ struct __align__(16) P2Smem {
     bf16_t st[2][2][kN][kRow];   // [S0 | dS][chunk of the pair][j][i]
 };
 
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_v;
+
 // Lane (g, l16) of wave p: key column col = 16p + l16, tokens 4g .. 4g+3.
 struct KeyFactors {
     float R[5][4];                 // r, w, k, a, b
@@ -732,9 +734,12 @@ __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
         // ---- sum_i dS[i][col] S0[i][col] over this lane's 16 value rows -----------
         float cs = 0.f;
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2)
+        for (int k2 = 0; k2 < 2; ++k2) {
+            const bf16x2_v* ds2 = reinterpret_cast<const bf16x2_v*>(&dSc[k2]);
+            const bf16x2_v* s02 = reinterpret_cast<const bf16x2_v*>(&S0c[k2]);
 #pragma unroll
-            for (int q = 0; q < 8; ++q) cs = fmaf((float)dSc[k2][q], (float)S0c[k2][q], cs);
+            for (int q = 0; q < 4; ++q) cs = __builtin_amdgcn_fdot2_f32_bf16(ds2[q], s02[q], cs, false);
+        }
 
         // ---- chain rule through the decay products (tokens t = 4g+q) --------------
         // d log w_u = sum_{t>=u} (dRt Rt - dBh Bh - dKh Kh)_t + sum_{t>=u+1} (dAt At)_t
