@@ -383,15 +383,15 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
         if (tt < T) {
             bf16_t* base = rtid < 128 ? dv : wdX;
             const bf16_t(*src)[kRow] = rtid < 128 ? sm.dVs[sb] : sm.dXs[sb];
-            *reinterpret_cast<uint4*>(base + tok_off(bb, tt, hh, T, H) + 8 * piece) =
-                *reinterpret_cast<const uint4*>(&src[row][8 * piece]);
+            store_stream(base + tok_off(bb, tt, hh, T, H) + 8 * piece,
+                         *reinterpret_cast<const uint4*>(&src[row][8 * piece]));
         }
         if (keeps_dS(c)) {
 #pragma unroll
             for (int k2 = 0; k2 < 2; ++k2) {
                 const int j = 32 * k2 + (rtid >> 3);
-                *reinterpret_cast<uint4*>(wdS + (((size_t)bh * nblk + (c >> 1)) * kN + j) * kN + 8 * piece) =
-                    *reinterpret_cast<const uint4*>(&sm.dSs[sb][j][8 * piece]);
+                store_stream(wdS + (((size_t)bh * nblk + (c >> 1)) * kN + j) * kN + 8 * piece,
+                             *reinterpret_cast<const uint4*>(&sm.dSs[sb][j][8 * piece]));
             }
         }
     };
@@ -811,8 +811,7 @@ __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
             if (t < T) {
                 const size_t off = tok_off(bb, t, hh, T, H) + 8 * piece;
                 auto put = [&](int set, bf16_t* dst) __attribute__((always_inline)) {
-                    *reinterpret_cast<uint4*>(dst + off) =
-                        *reinterpret_cast<const uint4*>(&sm.rows[h][set][row][8 * piece]);
+                    store_stream(dst + off, *reinterpret_cast<const uint4*>(&sm.rows[h][set][row][8 * piece]));
                 };
                 if (tid < 128) {
                     put(0, dr);

@@ -361,15 +361,15 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
             bf16_t* base = rtid < 128 ? y : tapeZ;
             const bf16_t(*src)[kRow] = rtid < 128 ? sm.Ys[c & 1] : sm.Zs[c & 1];
             if (base)
-                *reinterpret_cast<uint4*>(base + tok_off(bb, tt, hh, T, H) + 8 * piece) =
-                    *reinterpret_cast<const uint4*>(&src[row][8 * piece]);
+                store_stream(base + tok_off(bb, tt, hh, T, H) + 8 * piece,
+                             *reinterpret_cast<const uint4*>(&src[row][8 * piece]));
         }
         if (tape && c < nch && (c & 1) == 0) {
 #pragma unroll
             for (int k2 = 0; k2 < 2; ++k2) {
                 const int j = 32 * k2 + (rtid >> 3);
-                *reinterpret_cast<uint4*>(tapeS + (((size_t)bh * nblk + (c >> 1)) * kN + j) * kN + 8 * piece) =
-                    *reinterpret_cast<const uint4*>(&sm.S0s[(c >> 1) & 1][j][8 * piece]);
+                store_stream(tapeS + (((size_t)bh * nblk + (c >> 1)) * kN + j) * kN + 8 * piece,
+                             *reinterpret_cast<const uint4*>(&sm.S0s[(c >> 1) & 1][j][8 * piece]));
             }
         }
     };

@@ -118,6 +118,13 @@ __device__ __forceinline__ float dot4(float4 s, float4 q) {
     return fmaf(s.w, q.w, fmaf(s.z, q.z, fmaf(s.y, q.y, s.x * q.x)));
 }
 
+// 16-byte store of an output nothing in this kernel reads again (streamed past
+// the caches: the non-temporal hint).
+__device__ __forceinline__ void store_stream(void* dst, uint4 x) {
+    typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store(__builtin_bit_cast(u4, x), reinterpret_cast<u4*>(dst));
+}
+
 // Token tensor offset for [B][T][H][N].
 __device__ __forceinline__ size_t tok_off(int b, int t, int h, int T, int H) {
     return (((size_t)b * T + t) * H + h) * kN;
