@@ -119,6 +119,23 @@ def test_bwd_overlapped_matches_single_stream(wk, use_tape):
                 assert torch.equal(grads[i], ref[i]), (rep, NAMES[i])
 
 
+def test_bwd_overlapped_without_split_is_plain_backward(wk):
+    """Few heads (B*H below the compute units) or one batch row: the two-stream
+    entry point runs the plain backward on the first stream."""
+    import torch
+    for (B, H) in [(2, 3), (1, 40)]:
+        inp = synth.generate(B, 70, H, 64, dtype="bf16", seed=40 + B, random_s0=True, backward=True)
+        dev = [to_dev(x, "bf16") for x in inp.tensors()]
+        s0 = to_dev(inp.s0, "fp32")
+        dy = to_dev(inp.dy, "bf16")
+        _, _, tape = wk.forward(*dev, s0, chunk_len=16, want_state=False, want_tape=True)
+        ref = wk.backward(*dev, dy, s0, None, tape)
+        got = wk.backward(*dev, dy, s0, None, tape, aux_stream=torch.cuda.Stream())
+        torch.cuda.synchronize()
+        for i, name in enumerate(NAMES):
+            assert torch.equal(got[i], ref[i]), (B, H, name)
+
+
 @pytest.mark.parametrize("fwd_chunk", [0, 16])
 def test_bwd_without_tape_matches_tape_path(wk, fwd_chunk):
     """Without a tape the library re-runs the forward (sequential or chunked) into

@@ -86,6 +86,14 @@ def test_chunk_fwd_ragged(wk, T):
     _check_fwd(wk, inp, 16, f"chunk T={T}")
 
 
+def test_chunk_fwd_0_19b_full(wk):
+    """B=4, T=1024, H=12 (0.19B-model shape), bf16, zero state, through the
+    chunked form: every head against the oracle."""
+    wl = synth.WORKLOADS["fwd_0.19b"]
+    inp = synth.generate_workload(wl, seed=0)
+    _check_fwd(wk, inp, 16, "chunked fwd_0.19b")
+
+
 def test_chunk_fwd_zero_state(wk):
     inp = synth.generate(1, 96, 2, 64, dtype="bf16", seed=7)
     _check_fwd(wk, inp, 16, "chunk zero s0")
