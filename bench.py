@@ -394,6 +394,17 @@ def secondary(torch, wk, dev):
                                "alg_GBs": round(nbytes / ms / 1e6, 1),
                                "frac_hbm": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
     del ins, s0, y
+    # The 0.19B-model shape: few heads (48), so the T-long serial chain sets the
+    # time (latency, not bandwidth); both forms of the forward.
+    B, T, H = 4, 1024, 12
+    ins = _dev_inputs(torch, (B, T, H, N), dev, 3)
+    y = torch.empty_like(ins[0])
+    for name, cl in (("chunked_fwd_0.19b", 16), ("sequential_fwd_0.19b", 0)):
+        ms = _time(torch, lambda: wk.forward(*ins, None, chunk_len=cl, out=y, want_state=False), 5)
+        res[name] = {"workload": f"B=4 T=1024 H=12 bf16, zero s0, chunk_len={cl}",
+                     "ms": round(ms, 4), "tokens_per_s": round(B * T / ms * 1e3, 1),
+                     "us_per_16_tokens": round(ms * 1e3 / (T / 16), 3)}
+    del ins, y
     Bd, Hd, steps = 256, 40, 512
     st = 0.1 * torch.randn(Bd, Hd, N, N, device=dev)
     seq = _dev_inputs(torch, (steps, Bd, Hd, N), dev, 2)
@@ -411,6 +422,24 @@ def secondary(torch, wk, dev):
                           "tokens_per_s": round(Bd / per_step * 1e3, 1),
                           "alg_GBs": round(nbytes / per_step / 1e6, 1),
                           "note": "the 168 MB state fits the 256 MB Infinity Cache"}
+    del st, seq, yd
+    # B=512: the 335 MB of state no longer fits the 256 MB cache (HBM-bound).
+    Bd2 = 512
+    st = 0.1 * torch.randn(Bd2, Hd, N, N, device=dev)
+    one = _dev_inputs(torch, (8, Bd2, Hd, N), dev, 4)
+    yd = torch.empty(Bd2, Hd, N, device=dev, dtype=torch.bfloat16)
+
+    def run_8():
+        for t in range(8):
+            wk.decode_step(*(x[t] for x in one), st, out=yd)
+
+    per_step = _time(torch, run_8, 5) / 8
+    nbytes = Bd2 * Hd * (2 * STATE_BYTES + FWD_BYTES_PER_TH)
+    res["decode_b512"] = {"workload": "B=512 H=40, in-place steps, fp32 state, bf16 inputs",
+                          "us_per_step": round(per_step * 1e3, 2),
+                          "tokens_per_s": round(Bd2 / per_step * 1e3, 1),
+                          "alg_GBs": round(nbytes / per_step / 1e6, 1),
+                          "frac_hbm": round(nbytes / per_step / 1e6 / HBM_PEAK_GBS, 4)}
     return res
 
 
