@@ -234,6 +234,16 @@ def main():
         call("wkv7_forward", ctypes.byref(desc), *ptr, None, y.data_ptr(), None, tape.data_ptr(),
              stream.cuda_stream)
 
+    # The step's forward: wkv7_forward_split with the library's own plan (with
+    # more heads than compute units, the heads of the last, partial round run
+    # split in time).
+    sws_bytes = wk.split_workspace_bytes(desc, 0)
+    sws = torch.empty(max(sws_bytes // 4, 4), device=dev, dtype=torch.float32)
+
+    def fwd_split():
+        call("wkv7_forward_split", ctypes.byref(desc), *ptr, None, y.data_ptr(), None,
+             tape.data_ptr(), 0, sws.data_ptr(), sws_bytes, stream.cuda_stream)
+
     bargs = lambda: (ctypes.byref(desc), *ptr, None, dy.data_ptr(), None, tape.data_ptr(),
                      *[g.data_ptr() for g in grads], ds0.data_ptr(), work.data_ptr(), wsb,
                      stream.cuda_stream)
@@ -257,7 +267,7 @@ def main():
     stages = [("chunk_fwd_kernel", fwd), ("bwd_chain_kernel", bwd_adjoint),
               ("bwd_keys_kernel", bwd_gradients)]
     for _ in range(args.warmup):
-        fwd()
+        fwd_split()
         bwd_overlapped()
     torch.cuda.synchronize()
     if args.copy_calibration:
@@ -276,13 +286,20 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        fwd()
+        fwd_split()
         bwd_overlapped()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
     tokens = B * T
     value = tokens / (ms_per_step / 1e3)
+
+    # The step's two halves on their own (HIP events on the launch stream),
+    # before the per-kernel loop so that its launches stay the last ones.
+    halves = {}
+    for name, fn in (("forward_split_ms", fwd_split), ("forward_unsplit_ms", fwd),
+                     ("backward_overlapped_ms", bwd_overlapped)):
+        halves[name] = round(_time(torch, fn, args.steps), 4)
 
     # Timed region 2 (per kernel): K steps of the same kernels one at a time, a
     # HIP event on the launch stream around every launch.  These are the last K
@@ -325,7 +342,8 @@ def main():
                 "timed_separately": "kernel times from K further steps with the backward's two "
                                     "stages launched one at a time (one kernel per call, HIP "
                                     "events around each); their sum per step: "
-                                    f"{staged_ms:.4f} ms"}
+                                    f"{staged_ms:.4f} ms",
+                "step_parts": halves}
 
     out = {
         "metric": "WKV7 fwd+bwd tokens/s (H=40,N=64,T=4096) and achieved HBM GB/s / MFMA % peak",
@@ -341,8 +359,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "fwd_bwd_2.9b: B=8 T=4096 H=40 N=64 bf16 inputs, fp32 state, "
-                               "dy~N(0,1), dsT=0, chunked L=16, bf16 tape; step = wkv7_forward + "
-                               "wkv7_backward_overlapped (two streams)",
+                               "dy~N(0,1), dsT=0, chunked L=16, bf16 tape; step = wkv7_forward_split "
+                               "(automatic plan) + wkv7_backward_overlapped (two streams)",
                    "global_batch": B, "seq_len": T, "heads": H, "head_size": N,
                    "parallelism": "none (1 GPU)"},
         "roofline": roofline,
@@ -399,12 +417,43 @@ def secondary(torch, wk, dev):
     B, T, H = 4, 1024, 12
     ins = _dev_inputs(torch, (B, T, H, N), dev, 3)
     y = torch.empty_like(ins[0])
-    for name, cl in (("chunked_fwd_0.19b", 16), ("sequential_fwd_0.19b", 0)):
-        ms = _time(torch, lambda: wk.forward(*ins, None, chunk_len=cl, out=y, want_state=False), 5)
-        res[name] = {"workload": f"B=4 T=1024 H=12 bf16, zero s0, chunk_len={cl}",
+    # Calls through the C ABI with prepared arguments: at tens of microseconds
+    # per call the binding's own checks would otherwise be part of the time.
+    import ctypes
+    L = wk.lib()
+    ptr = [x.data_ptr() for x in ins]
+    stream = torch.cuda.current_stream().cuda_stream
+    sdesc = wk.make_desc(B, T, H, N, wk.WKV7_BF16, 16)
+    sws_bytes = wk.split_workspace_bytes(sdesc, 0)
+    sws = torch.empty(max(sws_bytes // 4, 4), device=dev)
+    qdesc = wk.make_desc(B, T, H, N, wk.WKV7_BF16, 0)
+
+    def split_call():
+        if L.wkv7_forward_split(ctypes.byref(sdesc), *ptr, None, y.data_ptr(), None, None, 0,
+                                sws.data_ptr(), sws_bytes, stream) != 0:
+            raise RuntimeError("wkv7_forward_split failed")
+
+    def plain_call(d):
+        def fn():
+            if L.wkv7_forward(ctypes.byref(d), *ptr, None, y.data_ptr(), None, None, stream) != 0:
+                raise RuntimeError("wkv7_forward failed")
+        return fn
+
+    forms = (("chunked_split_fwd_0.19b", 16, split_call),
+             ("chunked_fwd_0.19b", 16, plain_call(sdesc)),
+             ("sequential_fwd_0.19b", 0, plain_call(qdesc)))
+    reps = {name: [] for name, _, _ in forms}
+    for _ in range(3):   # interleaved repetitions; the median is reported
+        for name, _, fn in forms:
+            reps[name].append(_time(torch, fn, 20))
+    for name, cl, fn in forms:
+        ms = float(np.median(reps[name]))
+        form = ("wkv7_forward_split, automatic plan (every head in time segments)"
+                if fn is split_call else f"chunk_len={cl}")
+        res[name] = {"workload": f"B=4 T=1024 H=12 bf16, zero s0, {form}",
                      "ms": round(ms, 4), "tokens_per_s": round(B * T / ms * 1e3, 1),
                      "us_per_16_tokens": round(ms * 1e3 / (T / 16), 3)}
-    del ins, y
+    del ins, y, sws
     Bd, Hd, steps = 256, 40, 512
     st = 0.1 * torch.randn(Bd, Hd, N, N, device=dev)
     seq = _dev_inputs(torch, (steps, Bd, Hd, N), dev, 2)

@@ -32,7 +32,7 @@ TAPE_CHUNK = 16
 TAPE_BLOCK = 32
 
 EXPORTED = ("wkv7_abi_version", "wkv7_status_string", "wkv7_tape_bytes", "wkv7_workspace_bytes",
-            "wkv7_forward", "wkv7_backward", "wkv7_backward_adjoint", "wkv7_backward_gradients",
+            "wkv7_forward", "wkv7_forward_split_workspace_bytes", "wkv7_forward_split", "wkv7_backward", "wkv7_backward_adjoint", "wkv7_backward_gradients",
             "wkv7_backward_overlapped", "wkv7_decode_step")
 
 
@@ -74,6 +74,10 @@ def lib():
         L.wkv7_workspace_bytes.restype = Z
         L.wkv7_forward.argtypes = [D] + [P] * 6 + [P, P, P, P, P]
         L.wkv7_forward.restype = ctypes.c_int
+        L.wkv7_forward_split_workspace_bytes.argtypes = [D, I]
+        L.wkv7_forward_split_workspace_bytes.restype = Z
+        L.wkv7_forward_split.argtypes = [D] + [P] * 6 + [P, P, P, P, I, P, Z, P]
+        L.wkv7_forward_split.restype = ctypes.c_int
         for name in ("wkv7_backward", "wkv7_backward_adjoint", "wkv7_backward_gradients"):
             fn = getattr(L, name)
             fn.argtypes = [D] + [P] * 6 + [P, P, P, P] + [P] * 6 + [P, P, Z, P]
@@ -140,6 +144,10 @@ def workspace_bytes(desc: Desc, with_tape: bool = True) -> int:
     return int(lib().wkv7_workspace_bytes(ctypes.byref(desc), 1 if with_tape else 0))
 
 
+def split_workspace_bytes(desc: Desc, segments: int = 0) -> int:
+    return int(lib().wkv7_forward_split_workspace_bytes(ctypes.byref(desc), segments))
+
+
 def split_tape(tape, B: int, T: int, H: int, N: int = HEAD_SIZE):
     """Views of a forward tape: Z [B, T, H, N] (removal read-outs z_t = S_{t-1} a_t)
     and the states entering every 32-token block [B, H, ceil(T/32), N (key j),
@@ -152,12 +160,15 @@ def split_tape(tape, B: int, T: int, H: int, N: int = HEAD_SIZE):
 
 
 def forward(r, w, k, v, a, b, s0=None, *, chunk_len: int = 0, want_state: bool = True,
-            want_tape: bool = False, out=None):
+            want_tape: bool = False, out=None, segments: Optional[int] = None, workspace=None):
     """Run the recurrence over [B, T, H, N] inputs.
 
     Returns ``(y, sT, tape)``; ``sT`` / ``tape`` are None unless requested (the
     tape is a flat bf16 tensor for ``backward``; ``split_tape`` gives its parts).
     ``chunk_len`` 0 = sequential scan, 16 = chunked bf16-MFMA form.
+    ``segments`` (not None) selects wkv7_forward_split: 0 = the library's
+    choice, 1 = no split, n >= 2 = every head in up to n time segments;
+    ``workspace`` is then its device scratch (allocated here when None).
     """
     torch = _torch()
     B, T, H, N = r.shape
@@ -170,10 +181,23 @@ def forward(r, w, k, v, a, b, s0=None, *, chunk_len: int = 0, want_state: bool =
     if want_tape:
         nbytes = tape_bytes(desc)
         ck = torch.empty(max(nbytes // 2, 8), device=r.device, dtype=torch.bfloat16)
-    st = lib().wkv7_forward(ctypes.byref(desc), _ptr(r), _ptr(w), _ptr(k), _ptr(v), _ptr(a),
-                            _ptr(b), _ptr(s0), _ptr(y), _ptr(sT), _ptr(ck), _stream())
+    if segments is None:
+        st = lib().wkv7_forward(ctypes.byref(desc), _ptr(r), _ptr(w), _ptr(k), _ptr(v), _ptr(a),
+                                _ptr(b), _ptr(s0), _ptr(y), _ptr(sT), _ptr(ck), _stream())
+        if st != WKV7_OK:
+            raise WKV7Error(st, "wkv7_forward")
+        return y, sT, ck
+    wsb = split_workspace_bytes(desc, segments)
+    ws = workspace
+    if ws is None and wsb > 0:
+        ws = torch.empty(wsb // 4, device=r.device, dtype=torch.float32)
+    if ws is not None:
+        wsb = ws.numel() * ws.element_size()
+    st = lib().wkv7_forward_split(ctypes.byref(desc), _ptr(r), _ptr(w), _ptr(k), _ptr(v), _ptr(a),
+                                  _ptr(b), _ptr(s0), _ptr(y), _ptr(sT), _ptr(ck), segments,
+                                  _ptr(ws), wsb, _stream())
     if st != WKV7_OK:
-        raise WKV7Error(st, "wkv7_forward")
+        raise WKV7Error(st, "wkv7_forward_split")
     return y, sT, ck
 
 

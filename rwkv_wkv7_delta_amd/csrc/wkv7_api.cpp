@@ -47,6 +47,63 @@ constexpr size_t kQueueBytes = 256;
 
 int from_hip(hipError_t e) { return e == hipSuccess ? WKV7_OK : WKV7_ERR_LAUNCH; }
 
+// Compute units of the current device (0 if the runtime cannot say).
+int device_cus() {
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    return ncu;
+}
+
+// ---- segment plan of wkv7_forward_split --------------------------------------
+// Splitting a head in nseg segments takes 2 nseg - 3 workgroups in the first
+// pass (segment 0 and the two map runs of each of segments 1 .. nseg-2) and
+// nseg - 1 in the second, each over about T / nseg tokens: the serial chain of
+// a head shrinks from T to about 2 T / nseg.
+constexpr int kMaxSegments = 16;
+constexpr int kMinSegmentTokens = 128;
+
+struct SplitPlan {
+    int split_from, nseg, seg_len;
+};
+
+SplitPlan plan_split(const wkv7_desc* d, int segments, int ncu) {
+    const int nbh = d->B * d->H;
+    const SplitPlan none{nbh, 1, d->T};
+    if (nbh == 0 || d->T == 0 || d->chunk_len != 16 || segments == 1) return none;
+    int from = 0, nseg = segments;
+    if (segments == 0) {
+        // Automatic: split every head when the heads fill at most a third of
+        // the device; else, with more heads than compute units, split the
+        // heads of the last, partial round when they are few enough.
+        if (ncu <= 0) return none;
+        int part = nbh;
+        if (nbh > ncu) {
+            part = nbh % ncu;
+            from = nbh - part;
+        }
+        if (part == 0 || 3 * part > ncu) return none;
+        nseg = (ncu / part + 3) / 2;
+        if (nseg > d->T / kMinSegmentTokens) nseg = d->T / kMinSegmentTokens;
+    }
+    if (nseg > kMaxSegments) nseg = kMaxSegments;
+    // Segments start at multiples of 32 tokens (the tape's state blocks); the
+    // last one must keep at least one token.
+    while (nseg >= 2) {
+        const int per = (d->T + nseg - 1) / nseg;
+        const int len = (per + 31) / 32 * 32;
+        if ((int64_t)(nseg - 1) * len < d->T) return SplitPlan{from, nseg, len};
+        --nseg;
+    }
+    return none;
+}
+
+size_t split_bytes(const wkv7_desc* d, const SplitPlan& p) {
+    const size_t nsplit = (size_t)d->B * d->H - p.split_from;
+    return nsplit == 0 ? 0 : nsplit * 3 * p.nseg * (size_t)d->N * d->N * sizeof(float);
+}
+
 int run_forward(const wkv7_desc* d, const void* r, const void* w, const void* k, const void* v,
                 const void* a, const void* b, const float* s0, void* y, float* sT,
                 void* tape, hipStream_t stream) {
@@ -97,6 +154,34 @@ int wkv7_forward(const wkv7_desc* desc, const void* r, const void* w, const void
         return WKV7_ERR_INVALID_ARG;
     if (!(opt(s0) && opt(sT) && opt(tape))) return WKV7_ERR_INVALID_ARG;
     return run_forward(desc, r, w, k, v, a, b, s0, y, sT, tape, static_cast<hipStream_t>(stream));
+}
+
+size_t wkv7_forward_split_workspace_bytes(const wkv7_desc* desc, int32_t segments) {
+    if (check_desc(desc) != WKV7_OK || segments < 0) return 0;
+    return split_bytes(desc, plan_split(desc, segments, segments == 0 ? device_cus() : 0));
+}
+
+int wkv7_forward_split(const wkv7_desc* desc, const void* r, const void* w, const void* k,
+                       const void* v, const void* a, const void* b, const float* s0, void* y,
+                       float* sT, void* tape, int32_t segments, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    const int st = check_desc(desc);
+    if (st != WKV7_OK) return st;
+    if (segments < 0) return WKV7_ERR_INVALID_ARG;
+    if (segments > 1 && desc->chunk_len != 16) return WKV7_ERR_UNSUPPORTED;
+    const bool has_tokens = (int64_t)desc->B * desc->T * desc->H > 0;
+    if (has_tokens && !(req(r) && req(w) && req(k) && req(v) && req(a) && req(b) && req(y)))
+        return WKV7_ERR_INVALID_ARG;
+    if (!(opt(s0) && opt(sT) && opt(tape) && opt(workspace))) return WKV7_ERR_INVALID_ARG;
+    const SplitPlan plan = plan_split(desc, segments, segments == 0 ? device_cus() : 0);
+    const size_t need = split_bytes(desc, plan);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return WKV7_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (need == 0) return run_forward(desc, r, w, k, v, a, b, s0, y, sT, tape, s);
+    const wkv7::FwdArgs p{desc->B, desc->T, desc->H, true, r, w, k, v, a, b, s0, y, sT, tape};
+    return from_hip(wkv7::launch_chunk_fwd_split(
+        p, 16, wkv7::FwdSplit{plan.split_from, plan.nseg, plan.seg_len, static_cast<float*>(workspace)},
+        s));
 }
 
 }  // extern "C"
@@ -176,10 +261,8 @@ int run_backward(const wkv7_desc* desc, const void* r, const void* w, const void
     // in one round, and its per-key pass runs beside the second group's chain.
     int b1 = desc->B;
     if (aux && desc->B > 1) {
-        int dev = 0, ncu = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-            (int64_t)desc->B * desc->H > ncu) {
+        const int ncu = device_cus();
+        if (ncu > 0 && (int64_t)desc->B * desc->H > ncu) {
             b1 = ncu / desc->H;
             if (b1 < 1) b1 = 1;
             if (b1 > desc->B - 1) b1 = desc->B - 1;

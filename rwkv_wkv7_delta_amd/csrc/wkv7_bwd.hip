@@ -94,7 +94,7 @@ struct P1Slot {
     bf16_t Bb[kL][kRow], Kb[kL][kRow];                              // E -> chain, [t][j]
     uint2 atimg[4][64], rtimg[4][64];   // E -> chain: accumulator layout of At, Rt per key block
     uint2 dyimg[4][64];                 // E -> chain: accumulator layout of dy per value block
-    float gL[kN];
+    float gL[kN];         // G_L of key 16 jt + 4 g + q at word 16 g + 4 jt + q
     uint2 tiles[4][64];   // MW -> chain: A-operand register images of Tm^T, Arb^T, Aak^T, Ark^T
 };
 
@@ -244,7 +244,7 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
         s.rtimg[wp][lane] = __builtin_bit_cast(uint2, swap_layout(rtb, ident));
         s.dyimg[wp][lane] = __builtin_bit_cast(
             uint2, swap_layout(__builtin_bit_cast(bf16x4, raw6[P1_DY]), ident));
-        if (l16 == kL - 1) *reinterpret_cast<float4*>(&s.gL[j0]) = make_float4(gt[0], gt[1], gt[2], gt[3]);
+        if (l16 == kL - 1) *reinterpret_cast<float4*>(&s.gL[16 * g + 4 * wp]) = make_float4(gt[0], gt[1], gt[2], gt[3]);
     };
 
     // ---- MW (producer): one 16x16 tile per wave, as an A-operand image ------------
@@ -310,7 +310,7 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
         bf16x4 TmT, ArbT, AakT, ArkT, dY;
         bf16x8 bb[2], kb[2];
         bf16x4 rtT[4], atT[4];
-        float4 gl[4];
+        float gl;   // G_L of key 16 jt + 4 g + q sits in lane 4 jt + q of row g
     };
     auto read_C = [&](int c) __attribute__((always_inline)) -> CIn {
         const P1Slot& s = sm.sl[slot_of(c)];
@@ -329,8 +329,8 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
         for (int jt = 0; jt < 4; ++jt) {
             in.rtT[jt] = __builtin_bit_cast(bf16x4, s.rtimg[jt][lane]);
             in.atT[jt] = __builtin_bit_cast(bf16x4, s.atimg[jt][lane]);
-            in.gl[jt] = *reinterpret_cast<const float4*>(&s.gL[16 * jt + 4 * g]);
         }
+        in.gl = s.gL[lane];
         return in;
     };
     auto stage_C = [&](int c, const CIn& in) __attribute__((always_inline)) {
@@ -361,14 +361,11 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
                 *reinterpret_cast<bf16x4*>(&sm.dSs[sb][16 * jt + l16][i0]) = swap_layout(dSb[jt], ident);
         }
         // dS0^T = G_L dS^T + Rt^T dY + At^T dX
+        const f32x4 dec[4] = {mul_row_lanes4<0>(in.gl, dSt[0]), mul_row_lanes4<1>(in.gl, dSt[1]),
+                              mul_row_lanes4<2>(in.gl, dSt[2]), mul_row_lanes4<3>(in.gl, dSt[3])};
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
-            f32x4 acc;
-            acc[0] = in.gl[jt].x * dSt[jt][0];
-            acc[1] = in.gl[jt].y * dSt[jt][1];
-            acc[2] = in.gl[jt].z * dSt[jt][2];
-            acc[3] = in.gl[jt].w * dSt[jt][3];
-            acc = mfma16(in.rtT[jt], in.dY, acc);
+            const f32x4 acc = mfma16(in.rtT[jt], in.dY, dec[jt]);
             dSt[jt] = mfma16(in.atT[jt], dXb, acc);
         }
     };

@@ -64,7 +64,7 @@ struct Slot {
     bf16_t At[kL][kRow], Rt[kL][kRow], Bh[kL][kRow], Kh[kL][kRow];  // E -> MW, ST: row-major [t][j]
     uint2 bbimg[4][64], kbimg[4][64];   // E -> ST: accumulator layout of Bb, Kb per key block
     uint2 vimg[4][64];                  // E -> ST: accumulator layout of v per value block
-    float gL[kN];                                                   // E -> ST
+    float gL[kN];   // E -> ST: G_L of key 16 jt + 4 g + q at word 16 g + 4 jt + q
     uint2 tiles[4][64];   // MW -> ST: A-operand images of Tm, Aak, Arb, Ark (tile p from wave p)
 };
 
@@ -90,14 +90,78 @@ struct Raw {
     u32x4 x[3];
 };
 
+// Work of one workgroup: a head over tokens [t_begin, t_end), started from the
+// state rows at `init` (else the identity when `ident`, else zero), with v
+// taken as zero when `vzero`; outputs (y, tape) only when `outs`; the final
+// state to `fin` when not null.
+struct Work {
+    int bh, t_begin, t_end;
+    const float* init;
+    float* fin;
+    bool ident, vzero, outs;
+};
+
+// blockIdx -> Work under a segment plan (FwdSplit): heads below split_from run
+// whole in pass 0; every later head runs in nseg segments of seg_len tokens.
+// Pass 0 also runs each split head's segment 0 (with outputs; its final state
+// is the entry state of segment 1) and, for segments 1 .. nseg-2, the two runs
+// whose final states give the segment's affine map S_out = S_in P + Hm: Hm from
+// zero with the real v, P from the identity with v = 0 (the recurrence is
+// affine in the state: S <- S M_t + v_t k_t^T).  Pass 1 re-runs segments
+// 1 .. nseg-1 from their entry states (composed in between), with outputs.
+// Per split head the workspace holds 3 nseg states: entry states (slot s),
+// Hm (nseg + s) and P (2 nseg + s).
+__device__ __forceinline__ Work work_of(int blk, int pass, int T, const float* s0, float* sT,
+                                        int split_from, int nseg, int seg_len, float* states) {
+    constexpr size_t NN = (size_t)kN * kN;
+    Work wk{0, 0, T, nullptr, nullptr, false, false, true};
+    if (pass == 0 && blk < split_from) {
+        wk.bh = blk;
+        wk.init = s0 ? s0 + (size_t)blk * NN : nullptr;
+        wk.fin = sT ? sT + (size_t)blk * NN : nullptr;
+        return wk;
+    }
+    const int j = pass == 0 ? blk - split_from : blk;
+    const int per = pass == 0 ? 2 * nseg - 3 : nseg - 1;
+    const int hs = j / per, rr = j % per;
+    wk.bh = split_from + hs;
+    float* const hst = states + (size_t)hs * 3 * nseg * NN;
+    if (pass == 0 && rr == 0) {
+        wk.t_end = seg_len;
+        wk.init = s0 ? s0 + (size_t)wk.bh * NN : nullptr;
+        wk.fin = hst + NN;
+    } else if (pass == 0) {
+        const int sg = 1 + (rr - 1) / 2;
+        const bool pm = ((rr - 1) & 1) != 0;
+        wk.t_begin = sg * seg_len;
+        wk.t_end = wk.t_begin + seg_len;
+        wk.ident = pm;
+        wk.vzero = pm;
+        wk.outs = false;
+        wk.fin = hst + (size_t)((pm ? 2 : 1) * nseg + sg) * NN;
+    } else {
+        const int sg = 1 + rr;
+        wk.t_begin = sg * seg_len;
+        wk.t_end = sg == nseg - 1 ? T : wk.t_begin + seg_len;
+        wk.init = hst + (size_t)sg * NN;
+        wk.fin = (sg == nseg - 1 && sT) ? sT + (size_t)wk.bh * NN : nullptr;
+    }
+    return wk;
+}
+
 __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
-    int T, int H, const bf16_t* __restrict__ r, const bf16_t* __restrict__ w,
+    int B, int T, int H, const bf16_t* __restrict__ r, const bf16_t* __restrict__ w,
     const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const bf16_t* __restrict__ a,
-    const bf16_t* __restrict__ b, const float* __restrict__ s0, bf16_t* __restrict__ y,
-    float* __restrict__ sT, bf16_t* __restrict__ tape) {
+    const bf16_t* __restrict__ b, const float* __restrict__ s0, bf16_t* __restrict__ y_all,
+    float* __restrict__ sT, bf16_t* __restrict__ tape_all, int pass, int split_from, int nseg,
+    int seg_len, float* __restrict__ states) {
     __shared__ FwdSmem sm;
-    const int bh = blockIdx.x;
+    const Work wk = work_of(blockIdx.x, pass, T, s0, sT, split_from, nseg, seg_len, states);
+    const int bh = wk.bh;
     const int bb = bh / H, hh = bh % H;
+    const int t_end = wk.t_end;
+    bf16_t* const y = wk.outs ? y_all : nullptr;
+    bf16_t* const tape = wk.outs ? tape_all : nullptr;
     const int tid = threadIdx.x;
     // Roles split by wave (the tests are uniform within a wave).  They are left
     // as per-lane conditions: branching on an SGPR copy of the wave index
@@ -110,21 +174,22 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
     const int lane = tid & 63, wp = (tid >> 6) & 3;
     const int l16 = lane & 15, g = lane >> 4;
     const int col = 16 * wp + l16;            // key column (producer) / value row (consumer)
-    const int nch = (T + kL - 1) / kL;
+    // Chunks [c_begin, c_end) of the sequence (t_begin is a multiple of 32).
+    const int c_begin = wk.t_begin / kL, c_end = (t_end + kL - 1) / kL;
     // Tape for the backward: removal read-outs Z as [B][T][H][N] bf16, then the
     // state entering every 32-token block (even chunks) as
     // [B][H][nblk][N (key j)][N (value i)] bf16.
-    const int nblk = (nch + 1) / 2;
+    const int nblk = ((T + kL - 1) / kL + 1) / 2;
     bf16_t* const tapeZ = tape;
-    bf16_t* const tapeS = tape ? tape + (size_t)gridDim.x / H * T * H * kN : nullptr;
+    bf16_t* const tapeS = tape ? tape + (size_t)B * T * H * kN : nullptr;
 
     // ---- consumer state: S^T tiles, lane holds S[col][16 jt + 4 g + q] ----------
     f32x4 S[4];
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt) S[jt] = zero4();
     if (consumer) {
-        if (s0) {
-            const float* base = s0 + ((size_t)bh * kN + col) * kN;
+        if (wk.init) {
+            const float* base = wk.init + (size_t)col * kN;
 #pragma unroll
             for (int jt = 0; jt < 4; ++jt) {
                 const float4 x = *reinterpret_cast<const float4*>(base + 16 * jt + 4 * g);
@@ -134,32 +199,37 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
             // guards every later use of S with a wait on the whole memory
             // counter, which then also waits for the previous chunk's stores.
             __builtin_amdgcn_s_waitcnt(0);
+        } else if (wk.ident) {
+#pragma unroll
+            for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) S[jt][q] = col == 16 * jt + 4 * g + q ? 1.f : 0.f;
         }
     }
 
     // ---- producer raw loads: 6 vectors x 16 tokens x 64 = 768 x 16 bytes.  Thread
     // rtid loads vector 2p + (rtid >= 128), token (rtid >> 3) & 15, columns
-    // 8 (rtid & 7) .. +7, for p = 0, 1, 2.  Loads are branch-free (tokens past
-    // T re-read token T-1 and become padding when stashed) and are issued
-    // three intervals before use into a three-deep register ring; the stash
-    // into LDS happens one interval before use.
+    // 8 (rtid & 7) .. +7, for p = 0, 1, 2.  Loads are branch-free (tokens from
+    // t_end on re-read token t_end-1 and become padding when stashed) and are
+    // issued three intervals before use into a three-deep register ring; the
+    // stash into LDS happens one interval before use.
     const bool hi = rtid >= 128;
     const bf16_t* const sp_p[3] = {hi ? w : r, hi ? a : k, hi ? v : b};
     const int ld_t = (rtid >> 3) & 15, ld_c8 = rtid & 7;
     auto load_raw = [&](int c, Raw& o) __attribute__((always_inline)) {
-        const int t = min(c * kL + ld_t, T - 1);
+        const int t = min(c * kL + ld_t, t_end - 1);
         const size_t off = tok_off(bb, t, hh, T, H) + ld_c8 * 8;
 #pragma unroll
         for (int p = 0; p < 3; ++p) o.x[p] = *reinterpret_cast<const u32x4*>(sp_p[p] + off);
     };
     auto stash_raw = [&](int c, const Raw& o) __attribute__((always_inline)) {
-        if ((c + 1) * kL <= T) {   // a whole chunk (the common case: no selects)
+        if ((c + 1) * kL <= t_end) {   // a whole chunk (the common case: no selects)
 #pragma unroll
             for (int p = 0; p < 3; ++p)
                 *reinterpret_cast<u32x4*>(&sm.raw[c & 1][2 * p + (hi ? 1 : 0)][ld_t][ld_c8 * 8]) = o.x[p];
             return;
         }
-        const bool ok = c * kL + ld_t < T;
+        const bool ok = c * kL + ld_t < t_end;
 #pragma unroll
         for (int p = 0; p < 3; ++p) {
             const unsigned pad = (p == 0 && hi) ? 0x3F803F80u : 0u;   // padding: w = 1
@@ -219,9 +289,9 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
         *reinterpret_cast<bf16x4*>(&s.Kh[l16][j0]) = cvt4(kh4);
         s.bbimg[wp][lane] = __builtin_bit_cast(uint2, swap_layout(cvt4(bb4), ident));
         s.kbimg[wp][lane] = __builtin_bit_cast(uint2, swap_layout(cvt4(kb4), ident));
-        s.vimg[wp][lane] = __builtin_bit_cast(
-            uint2, swap_layout(__builtin_bit_cast(bf16x4, raw6[RAW_V]), ident));
-        if (l16 == kL - 1) *reinterpret_cast<float4*>(&s.gL[j0]) = make_float4(gt[0], gt[1], gt[2], gt[3]);
+        const uint2 vraw = wk.vzero ? make_uint2(0u, 0u) : raw6[RAW_V];
+        s.vimg[wp][lane] = __builtin_bit_cast(uint2, swap_layout(__builtin_bit_cast(bf16x4, vraw), ident));
+        if (l16 == kL - 1) *reinterpret_cast<float4*>(&s.gL[16 * g + 4 * wp]) = make_float4(gt[0], gt[1], gt[2], gt[3]);
     };
 
     // ---- MW (producer): one 16x16 tile per wave, as an A-operand image ------------
@@ -287,7 +357,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
         bf16x4 Tm, Aak, Arb, Ark, V;
         bf16x8 at[2], rt[2];
         bf16x4 bbt[4], kbt[4];
-        float4 gl[4];
+        float gl;   // G_L of key 16 jt + 4 g + q sits in lane 4 jt + q of row g
     };
     auto read_ST = [&](int c) __attribute__((always_inline)) -> STIn {
         const Slot& s = sm.sl[c % 3];
@@ -306,8 +376,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
         for (int jt = 0; jt < 4; ++jt) {
             in.bbt[jt] = __builtin_bit_cast(bf16x4, s.bbimg[jt][lane]);
             in.kbt[jt] = __builtin_bit_cast(bf16x4, s.kbimg[jt][lane]);
-            in.gl[jt] = *reinterpret_cast<const float4*>(&s.gL[16 * jt + 4 * g]);
         }
+        in.gl = s.gL[lane];
         return in;
     };
     auto stage_ST = [&](int c, const STIn& in) __attribute__((always_inline)) {
@@ -327,15 +397,12 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
         const f32x4 AkV = mfma16(in.Aak, in.V, zero4());
         const bf16x4 Zb = cvt4(mfma16(in.Tm, cvt4(add4(Xs, AkV)), zero4()));
         const f32x4 Yt = add4(Ys, mfma16(in.Ark, in.V, mfma16(in.Arb, Zb, zero4())));
+        const f32x4 dec[4] = {mul_row_lanes4<0>(in.gl, S[0]), mul_row_lanes4<1>(in.gl, S[1]),
+                              mul_row_lanes4<2>(in.gl, S[2]), mul_row_lanes4<3>(in.gl, S[3])};
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
-            f32x4 acc;
-            acc[0] = in.gl[jt].x * S[jt][0];
-            acc[1] = in.gl[jt].y * S[jt][1];
-            acc[2] = in.gl[jt].z * S[jt][2];
-            acc[3] = in.gl[jt].w * S[jt][3];
-            acc = mfma16(in.kbt[jt], in.V, acc);          // + H = Kb^T V
-            S[jt] = mfma16(in.bbt[jt], Zb, acc);           // + Bb^T Z
+            const f32x4 acc = mfma16(in.kbt[jt], in.V, dec[jt]);   // G_L S^T + Kb^T V
+            S[jt] = mfma16(in.bbt[jt], Zb, acc);                    // + Bb^T Z
         }
         // Outputs are staged in LDS in row layout (swap_layout: lane (g, l16)
         // holds 8 bytes of row l16) and leave next interval as whole 128-byte
@@ -357,14 +424,14 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
     auto store_out = [&](int c) __attribute__((always_inline)) {
         const int row = (rtid >> 3) & 15, piece = rtid & 7;
         const int tt = c * kL + row;
-        if (tt < T) {
+        if (tt < t_end) {
             bf16_t* base = rtid < 128 ? y : tapeZ;
             const bf16_t(*src)[kRow] = rtid < 128 ? sm.Ys[c & 1] : sm.Zs[c & 1];
             if (base)
                 store_stream(base + tok_off(bb, tt, hh, T, H) + 8 * piece,
                              *reinterpret_cast<const uint4*>(&src[row][8 * piece]));
         }
-        if (tape && c < nch && (c & 1) == 0) {
+        if (tape && c < c_end && (c & 1) == 0) {
 #pragma unroll
             for (int k2 = 0; k2 < 2; ++k2) {
                 const int j = 32 * k2 + (rtid >> 3);
@@ -374,10 +441,13 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
         }
     };
 
-    if (T > 0) {
-        // Intervals 0 .. nch+2 carry real work; the count is rounded up to a
-        // multiple of three for the unrolled producer loop.  The extra intervals
-        // see only all-padding chunks (identity on the state, nothing stored).
+    if (t_end > wk.t_begin) {
+        // Intervals 0 .. nch+2 carry real work (chunk c_begin + i in interval
+        // i); the count is rounded up to a multiple of three for the unrolled
+        // producer loop.  The extra intervals see only all-padding chunks
+        // (identity on the state, nothing stored).
+        const int nch = c_end - c_begin;
+        const int cb = c_begin;
         const int n_it = (nch + 5) / 3 * 3;
         // Each role runs its own loop over the same number of intervals (one
         // barrier each), so the compiler sees only loads on the producer side
@@ -390,11 +460,11 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
             // until stashed (three named variables, never an array, so that the
             // ring is neither promoted to LDS nor to scratch).
             Raw rb0, rb1, rb2;
-            load_raw(0, rb0);
-            load_raw(1, rb1);
-            load_raw(2, rb2);
-            stash_raw(0, rb0);
-            load_raw(3, rb0);
+            load_raw(cb, rb0);
+            load_raw(cb + 1, rb1);
+            load_raw(cb + 2, rb2);
+            stash_raw(cb, rb0);
+            load_raw(cb + 3, rb0);
             __syncthreads();
             // Interval it: E(it) and MW(it-1), stash chunk it+1 and load chunk
             // it+4 into the ring slot it frees.  (A macro, not a lambda, so that
@@ -402,13 +472,14 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
 #define WKV7_FWD_PRODUCE(IT, RING)                                          \
     {                                                                       \
         const int it_ = (IT);                                               \
-        const ERaw er = read_E(it_);                                        \
+        const int c_ = cb + it_;                                            \
+        const ERaw er = read_E(c_);                                         \
         MWIn mi;                                                            \
-        if (it_ >= 1 && wp != 0) mi = read_MW(it_ - 1);                     \
-        stage_E(it_, er);                                                   \
-        stash_raw(it_ + 1, RING);                                           \
-        load_raw(it_ + 4, RING);                                            \
-        if (it_ >= 1 && wp != 0) stage_MW(it_ - 1, mi);                     \
+        if (it_ >= 1 && wp != 0) mi = read_MW(c_ - 1);                      \
+        stage_E(c_, er);                                                    \
+        stash_raw(c_ + 1, RING);                                            \
+        load_raw(c_ + 4, RING);                                             \
+        if (it_ >= 1 && wp != 0) stage_MW(c_ - 1, mi);                      \
         __syncthreads();                                                    \
     }
             // Ring slot of interval it is (it + 1) % 3: it = 0, 1, 2 -> rb1, rb2, rb0.
@@ -426,7 +497,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
             // Interval it: the inverse of chunk it-1 (after E(it-1), read by the
             // consumers' chain in interval it+1).
             for (int it = 0; it < n_it; ++it) {
-                if (it >= 1) stage_INV(it - 1);
+                if (it >= 1) stage_INV(cb + it - 1);
                 __syncthreads();
             }
         } else {
@@ -439,17 +510,17 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
             // Interval it: the state chain of chunk it-2 and the stores of chunk it-3.
             for (int it = 0; it < n_it; ++it) {
                 if (it >= 2) {
-                    const STIn si = read_ST(it - 2);
-                    stage_ST(it - 2, si);
-                    if (it >= 3) store_out(it - 3);
+                    const STIn si = read_ST(cb + it - 2);
+                    stage_ST(cb + it - 2, si);
+                    if (it >= 3) store_out(cb + it - 3);
                 }
                 __syncthreads();
             }
         }
     }
 
-    if (sT && consumer) {
-        float* dst = sT + ((size_t)bh * kN + col) * kN;
+    if (wk.fin && consumer) {
+        float* dst = wk.fin + (size_t)col * kN;
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt)
             *reinterpret_cast<float4*>(dst + 16 * jt + 4 * g) =
@@ -457,16 +528,82 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
     }
 }
 
+// Entry states of the split segments: S_in(s+1) = S_in(s) P(s) + Hm(s) for
+// s = 1 .. nseg-2, in fp32 (S_in(1) is segment 0's final state).  Rows are
+// independent, so workgroup (head, q) takes rows 16 q .. 16 q + 15 of one split
+// head through every step; thread t owns row 16 q + t / 16 and columns
+// 4 (t % 16) .. +3.  The next step's P and Hm are loaded during the current one.
+constexpr int kCombineRows = 16;
+__global__ __launch_bounds__(256) void seg_combine_kernel(int nseg, float* __restrict__ states) {
+    constexpr size_t NN = (size_t)kN * kN;
+    __shared__ float4 Pm[2][kN][kN / 4];
+    __shared__ float Sr[kCombineRows][kN + 4];
+    float* const hst = states + (size_t)(blockIdx.x / (kN / kCombineRows)) * 3 * nseg * NN;
+    const int t = threadIdx.x;
+    const int i = (blockIdx.x % (kN / kCombineRows)) * kCombineRows + t / 16, li = t / 16;
+    const int c4 = t % 16;
+    float4 pn[4], hn;
+    auto fetch = [&](int sg) __attribute__((always_inline)) {
+        const float4* P = reinterpret_cast<const float4*>(hst + (size_t)(2 * nseg + sg) * NN);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) pn[u] = P[t + 256 * u];   // rows 4u + t / 16 .. of P
+        hn = reinterpret_cast<const float4*>(hst + (size_t)(nseg + sg) * NN + i * kN)[c4];
+    };
+    *reinterpret_cast<float4*>(&Sr[li][4 * c4]) = reinterpret_cast<const float4*>(hst + NN + i * kN)[c4];
+    fetch(1);
+    for (int sg = 1; sg + 1 < nseg; ++sg) {
+        const int buf = sg & 1;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) Pm[buf][(t + 256 * u) / 16][(t + 256 * u) % 16] = pn[u];
+        float4 acc = hn;
+        if (sg + 2 < nseg) fetch(sg + 1);
+        __syncthreads();
+#pragma unroll 8
+        for (int kk = 0; kk < kN; ++kk) {
+            const float sik = Sr[li][kk];
+            const float4 p = Pm[buf][kk][c4];
+            acc.x = fmaf(sik, p.x, acc.x);
+            acc.y = fmaf(sik, p.y, acc.y);
+            acc.z = fmaf(sik, p.z, acc.z);
+            acc.w = fmaf(sik, p.w, acc.w);
+        }
+        __syncthreads();   // every row of Sr is read before it is replaced
+        reinterpret_cast<float4*>(hst + (size_t)(sg + 1) * NN + i * kN)[c4] = acc;
+        *reinterpret_cast<float4*>(&Sr[li][4 * c4]) = acc;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_chunk_fwd(const FwdArgs& p, int chunk_len, hipStream_t stream) {
+    return launch_chunk_fwd_split(p, chunk_len, FwdSplit{p.B * p.H, 1, p.T, nullptr}, stream);
+}
+
+hipError_t launch_chunk_fwd_split(const FwdArgs& p, int chunk_len, const FwdSplit& sp,
+                                  hipStream_t stream) {
     if (chunk_len != kL || !p.bf16) return hipErrorInvalidValue;
-    chunk_fwd_kernel<<<dim3(p.B * p.H), dim3(kThreads), 0, stream>>>(
-        p.T, p.H, static_cast<const bf16_t*>(p.r), static_cast<const bf16_t*>(p.w),
-        static_cast<const bf16_t*>(p.k), static_cast<const bf16_t*>(p.v),
-        static_cast<const bf16_t*>(p.a), static_cast<const bf16_t*>(p.b), p.s0,
-        static_cast<bf16_t*>(p.y), p.sT, static_cast<bf16_t*>(p.tape));
-    return hipGetLastError();
+    const int nbh = p.B * p.H;
+    const int nsplit = nbh - sp.split_from;
+    if (nsplit < 0 || (nsplit > 0 && (sp.nseg < 2 || sp.seg_len % 32 != 0 || sp.seg_len <= 0 ||
+                                       (long long)(sp.nseg - 1) * sp.seg_len >= p.T || !sp.states)))
+        return hipErrorInvalidValue;
+    auto run = [&](int pass, int grid) {
+        chunk_fwd_kernel<<<dim3(grid), dim3(kThreads), 0, stream>>>(
+            p.B, p.T, p.H, static_cast<const bf16_t*>(p.r), static_cast<const bf16_t*>(p.w),
+            static_cast<const bf16_t*>(p.k), static_cast<const bf16_t*>(p.v),
+            static_cast<const bf16_t*>(p.a), static_cast<const bf16_t*>(p.b), p.s0,
+            static_cast<bf16_t*>(p.y), p.sT, static_cast<bf16_t*>(p.tape), pass, sp.split_from,
+            sp.nseg, sp.seg_len, sp.states);
+        return hipGetLastError();
+    };
+    hipError_t e = run(0, sp.split_from + (nsplit > 0 ? nsplit * (2 * sp.nseg - 3) : 0));
+    if (e != hipSuccess || nsplit == 0) return e;
+    if (sp.nseg > 2) {
+        seg_combine_kernel<<<dim3(nsplit * (kN / kCombineRows)), dim3(256), 0, stream>>>(sp.nseg, sp.states);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return run(1, nsplit * (sp.nseg - 1));
 }
 
 }  // namespace wkv7

@@ -114,6 +114,11 @@ __device__ __forceinline__ float row16_last(float x) {
     return __builtin_amdgcn_update_dpp(0.0f, x, 0x15F, 0xF, 0xF, false);
 }
 
+// Lane n of each row broadcast to the whole row (row_newbcast n).
+template <int n>
+__device__ __forceinline__ float row16_bcast(float x) {
+    return __builtin_amdgcn_update_dpp(0.0f, x, 0x150 + n, 0xF, 0xF, false);
+}
 __device__ __forceinline__ float dot4(float4 s, float4 q) {
     return fmaf(s.w, q.w, fmaf(s.z, q.z, fmaf(s.y, q.y, s.x * q.x)));
 }

@@ -42,6 +42,19 @@ struct DecodeArgs {
 
 hipError_t launch_seq_fwd(const FwdArgs& p, hipStream_t stream);
 hipError_t launch_chunk_fwd(const FwdArgs& p, int chunk_len, hipStream_t stream);
+
+// Segment plan of the chunked forward, split in time.  Heads [0, split_from)
+// run whole; heads [split_from, B*H) run as nseg >= 2 segments of seg_len
+// tokens (a multiple of 32; the last segment takes the rest, at least one
+// token).  `states` holds 3 * nseg fp32 N x N states per split head.
+struct FwdSplit {
+    int split_from;
+    int nseg;
+    int seg_len;
+    float* states;
+};
+hipError_t launch_chunk_fwd_split(const FwdArgs& p, int chunk_len, const FwdSplit& split,
+                                  hipStream_t stream);
 // stages: bit 0 = the adjoint chain (dv, ds0, workspace), bit 1 = the per-key
 // gradients (dr, dw, dk, da, db; reads the workspace the chain wrote).
 enum { BWD_CHAIN = 1, BWD_KEYS = 2 };

@@ -15,6 +15,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include "wkv7_device.h"
+
 namespace wkv7 {
 
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
@@ -26,6 +28,20 @@ __device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c) {
 }
 __device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// x[q] times what lane 4 JT + q of this lane's row holds in `f`: one DPP
+// multiply each, so that 16 per-column factors spread over a row's lanes
+// (one 4-byte LDS read per lane) reach an accumulator tile without a broadcast
+// read of all 16 into every lane.
+template <int JT>
+__device__ __forceinline__ f32x4 mul_row_lanes4(float f, f32x4 x) {
+    f32x4 o;
+    o[0] = row16_bcast<4 * JT + 0>(f) * x[0];
+    o[1] = row16_bcast<4 * JT + 1>(f) * x[1];
+    o[2] = row16_bcast<4 * JT + 2>(f) * x[2];
+    o[3] = row16_bcast<4 * JT + 3>(f) * x[3];
+    return o;
 }
 
 // Accumulator chains never mix shapes.  On gfx950 a 16x16x16 MFMA whose

@@ -80,6 +80,37 @@ def test_forward_validation(L):
     assert _fwd(L, wk.make_desc(2, 8, 0, 64, wk.WKV7_BF16, 16)) == wk.WKV7_OK
 
 
+def test_split_workspace_sizes(L):
+    """Explicit segment counts need no device: 3 states (entry, and the two map
+    runs) of 64 x 64 fp32 per segment of every split head."""
+    st = 64 * 64 * 4
+    d = wk.make_desc(4, 1024, 12, 64, wk.WKV7_BF16, 16)
+    assert wk.split_workspace_bytes(d, 4) == 48 * 3 * 4 * st
+    assert wk.split_workspace_bytes(d, 1) == 0
+    assert wk.split_workspace_bytes(d, 40) == 48 * 3 * 16 * st      # at most 16 segments
+    assert wk.split_workspace_bytes(d, -1) == 0
+    # T = 64: four segments would start at 0, 32, 64, 96; two fit.
+    assert wk.split_workspace_bytes(wk.make_desc(1, 64, 2, 64, wk.WKV7_BF16, 16), 4) == 2 * 3 * 2 * st
+    assert wk.split_workspace_bytes(wk.make_desc(1, 32, 2, 64, wk.WKV7_BF16, 16), 4) == 0
+    assert wk.split_workspace_bytes(wk.make_desc(1, 1024, 2, 64, wk.WKV7_BF16, 0), 4) == 0
+
+
+def test_split_forward_validation(L):
+    d = wk.make_desc(1, 256, 1, 64, wk.WKV7_BF16, 16)
+    f = L.wkv7_forward_split
+    args = [FAKE] * 6 + [None, FAKE, None, None]
+    assert f(ctypes.byref(d), *args, -1, None, 0, None) == wk.WKV7_ERR_INVALID_ARG
+    assert f(ctypes.byref(d), *args, 4, None, 0, None) == wk.WKV7_ERR_WORKSPACE
+    need = wk.split_workspace_bytes(d, 4)
+    assert f(ctypes.byref(d), *args, 4, FAKE, need - 16, None) == wk.WKV7_ERR_WORKSPACE
+    assert f(ctypes.byref(d), *args, 4, FAKE + 8, need, None) == wk.WKV7_ERR_INVALID_ARG
+    d0 = wk.make_desc(1, 256, 1, 64, wk.WKV7_BF16, 0)
+    assert f(ctypes.byref(d0), *args, 4, FAKE, need, None) == wk.WKV7_ERR_UNSUPPORTED
+    assert f(None, *args, 4, FAKE, need, None) == wk.WKV7_ERR_INVALID_ARG
+    de = wk.make_desc(0, 256, 1, 64, wk.WKV7_BF16, 16)
+    assert f(ctypes.byref(de), *args, 4, None, 0, None) == wk.WKV7_OK
+
+
 def test_backward_validation(L):
     d = wk.make_desc(1, 8, 1, 64, wk.WKV7_BF16, 16)
     args = [FAKE] * 6 + [None, FAKE, None]

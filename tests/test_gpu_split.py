@@ -1,0 +1,158 @@
+"""GPU parity of the forward split in time (wkv7_forward_split).
+
+Each head's sequence runs as segments: segment 0 and the affine maps of the
+middle segments first, their entry states composed in fp32, then the remaining
+segments again with their outputs.  Every result (y, the final state, the tape
+and gradients computed from that tape) is compared with the fp64 oracle on the
+same seeded inputs, to the bf16 tolerance (max relative error <= 2e-2, cosine
+>= 0.9999).
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from rwkv_wkv7_delta_amd import synth
+from tests._util import assert_close, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def wk():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import rwkv_wkv7_delta_amd as wk
+    wk.lib()
+    return wk
+
+
+def _run(wk, inp, segments, want_tape=False):
+    import torch
+    dev = [to_dev(x, inp.dtype) for x in inp.tensors()]
+    s0 = to_dev(inp.s0, "fp32") if inp.s0 is not None else None
+    y, sT, tape = wk.forward(*dev, s0, chunk_len=16, want_tape=want_tape, segments=segments)
+    torch.cuda.synchronize()
+    return to_np(y), to_np(sT), tape
+
+
+def _plan_bytes(wk, inp, segments):
+    B, T, H, N = inp.r.shape
+    return wk.split_workspace_bytes(wk.make_desc(B, T, H, N, wk.WKV7_BF16, 16), segments)
+
+
+@pytest.mark.parametrize("segments", [2, 3, 4, 7])
+@pytest.mark.parametrize("T", [100, 257, 512])
+def test_split_fwd_matches_oracle(wk, segments, T):
+    inp = synth.generate(2, T, 3, 64, dtype="bf16", seed=300 + T + segments, random_s0=True)
+    assert _plan_bytes(wk, inp, segments) > 0
+    y, sT, _ = _run(wk, inp, segments)
+    yr, sr = oracle.forward(*inp.tensors(), inp.s0)
+    assert_close(y, yr, "bf16", f"split{segments} T={T} y")
+    assert_close(sT, sr, "bf16", f"split{segments} T={T} sT")
+
+
+def test_split_fwd_zero_state_and_short_last_segment(wk):
+    """T = 193: three segments of 96, 96 and 1 token; zero initial state."""
+    inp = synth.generate(1, 193, 2, 64, dtype="bf16", seed=31)
+    y, sT, _ = _run(wk, inp, 3)
+    yr, sr = oracle.forward(*inp.tensors(), inp.s0)
+    assert_close(y, yr, "bf16", "split short last y")
+    assert_close(sT, sr, "bf16", "split short last sT")
+
+
+def test_split_fwd_too_short_to_split(wk):
+    """T = 32 cannot take a second segment: the call runs unsplit."""
+    inp = synth.generate(1, 32, 2, 64, dtype="bf16", seed=32, random_s0=True)
+    assert _plan_bytes(wk, inp, 4) == 0
+    y, sT, _ = _run(wk, inp, 4)
+    yr, sr = oracle.forward(*inp.tensors(), inp.s0)
+    assert_close(y, yr, "bf16", "unsplit y")
+    assert_close(sT, sr, "bf16", "unsplit sT")
+
+
+def test_split_fwd_tape(wk):
+    """The tape of a split run: removal read-outs z_t = S_{t-1} a_t and the
+    state entering every 32-token block, against the oracle's prefix states
+    (segments [0, 32), [32, 64), [64, 75))."""
+    B, T, H = 1, 75, 2
+    inp = synth.generate(B, T, H, 64, dtype="bf16", seed=33, random_s0=True)
+    _, _, tape = _run(wk, inp, 3, want_tape=True)
+    z, st = (to_np(x) for x in wk.split_tape(tape, B, T, H, 64))
+    xs = inp.tensors()
+    prefix = [inp.s0.astype(np.float64)]
+    for t in range(1, T):
+        prefix.append(oracle.forward(*(x[:, :t] for x in xs), inp.s0)[1])
+    zr = np.stack([np.einsum("bhij,bhj->bhi", prefix[t], xs[4][:, t].astype(np.float64))
+                   for t in range(T)], axis=1)
+    assert_close(z, zr, "bf16", "split tape z")
+    for m in range((T + 31) // 32):
+        assert_close(st[:, :, m], np.swapaxes(prefix[32 * m], -1, -2), "bf16", f"split tape state {m}")
+
+
+def test_backward_from_split_tape(wk):
+    """Gradients computed from a split forward's tape match the oracle's."""
+    import torch
+    inp = synth.generate(2, 200, 2, 64, dtype="bf16", seed=34, random_s0=True, backward=True)
+    dev = [to_dev(x, "bf16") for x in inp.tensors()]
+    s0 = to_dev(inp.s0, "fp32")
+    _, _, tape = wk.forward(*dev, s0, chunk_len=16, want_state=False, want_tape=True, segments=4)
+    g = wk.backward(*dev, to_dev(inp.dy, "bf16"), s0, None, tape)
+    torch.cuda.synchronize()
+    ref = oracle.backward(*inp.tensors(), inp.s0, inp.dy, None)
+    for name, x, rr in zip(("dr", "dw", "dk", "dv", "da", "db", "ds0"), g, ref):
+        assert_close(to_np(x), rr, "bf16", f"split-tape {name}")
+
+
+def test_split_fwd_0_19b_automatic(wk):
+    """B=4, T=1024, H=12 (0.19B-model shape), zero state, the library's own
+    segment count: every head against the oracle."""
+    wl = synth.WORKLOADS["fwd_0.19b"]
+    inp = synth.generate_workload(wl, seed=0)
+    assert _plan_bytes(wk, inp, 0) > 0   # 48 heads fill well under a third of the device
+    y, sT, _ = _run(wk, inp, 0)
+    yr, sr = oracle.forward(*inp.tensors(), inp.s0)
+    assert_close(y, yr, "bf16", "auto split 0.19b y")
+    assert_close(sT, sr, "bf16", "auto split 0.19b sT")
+
+
+def test_split_fwd_partial_last_round(wk):
+    """More heads than compute units: the automatic plan splits only the heads
+    of the last, partial round.  Sampled heads on both sides of the boundary."""
+    import torch
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    H = ncu + ncu // 8
+    T = 640
+    inp = synth.generate(1, T, H, 64, dtype="bf16", seed=35, random_s0=True)
+    assert _plan_bytes(wk, inp, 0) > 0
+    y, sT, _ = _run(wk, inp, 0)
+    pairs = [(0, 0), (0, ncu - 1), (0, ncu), (0, H - 1), (0, ncu + 3)]
+    sel = [oracle.select_heads(x, pairs) for x in inp.tensors()]
+    yr, sr = oracle.forward(*sel, oracle.select_heads(inp.s0, pairs, state=True))
+    assert_close(oracle.select_heads(y, pairs), yr, "bf16", "tail split y")
+    assert_close(oracle.select_heads(sT, pairs, state=True), sr, "bf16", "tail split sT")
+
+
+def test_split_fwd_2_9b_shape_sampled(wk):
+    """B=8, T=4096, H=40 (2.9B-model shape) with the automatic plan (the heads
+    past the first full round are split) and the tape: sampled heads against
+    the oracle, the tape against the unsplit forward's."""
+    import torch
+    B, T, H = 8, 4096, 40
+    inp = synth.generate(B, T, H, 64, dtype="bf16", seed=36)
+    dev = [to_dev(x, "bf16") for x in inp.tensors()]
+    y, sT, tape = wk.forward(*dev, None, chunk_len=16, want_tape=True, segments=0)
+    y1, sT1, tape1 = wk.forward(*dev, None, chunk_len=16, want_tape=True)
+    torch.cuda.synchronize()
+    pairs = [(0, 0), (6, 15), (6, 16), (7, 39), (7, 2)]
+    sel = [oracle.select_heads(x, pairs) for x in inp.tensors()]
+    yr, sr = oracle.forward(*sel, None)
+    yn, sn = to_np(y), to_np(sT)
+    assert_close(oracle.select_heads(yn, pairs), yr, "bf16", "2.9b split y")
+    assert_close(oracle.select_heads(sn, pairs, state=True), sr, "bf16", "2.9b split sT")
+    assert_close(yn, to_np(y1), "bf16", "2.9b split vs unsplit y")
+    z, st = wk.split_tape(tape, B, T, H, 64)
+    z1, st1 = wk.split_tape(tape1, B, T, H, 64)
+    assert_close(to_np(z[6:]), to_np(z1[6:]), "bf16", "2.9b split tape z")
+    assert_close(to_np(st[6:]), to_np(st1[6:]), "bf16", "2.9b split tape states")
