@@ -71,26 +71,39 @@ def mixed_shape_chains(asm: str):
 
 def mfma_under_partial_exec(asm: str, allowed_depth=None):
     """(line number, text) of every MFMA issued while more divergent regions
-    (s_and_saveexec / s_xor_saveexec ... s_or_b64 exec) are open than the
-    function may have around it.  allowed_depth maps a kernel-name fragment to
-    the number of enclosing regions that are known to be wave-uniform (a role
-    split by wave, which the compiler cannot prove uniform)."""
+    are open than the function may have around it.  A region opens with an
+    s_and_saveexec / s_xor_saveexec / s_andn2_saveexec that saves EXEC to a new
+    register pair (an s_andn2_saveexec into a pair already saved is the else
+    half of an if/else: same region) and closes with the s_or_b64 exec that
+    restores that pair -- which also closes every region opened inside it (the
+    compiler often restores an outer mask without restoring the inner ones).
+    allowed_depth maps a kernel-name fragment to the number of enclosing
+    regions that are known to be wave-uniform (a role split by wave, which the
+    compiler cannot prove uniform)."""
     allowed_depth = allowed_depth or {}
     bad = []
-    depth = 0
+    stack = []
     allow = 0
+    save = re.compile(r"s_(?:and|xor|andn2)_saveexec_b64\s+(s\[\d+:\d+\])")
+    restore = re.compile(r"s_or_b64\s+exec,\s*exec,\s*(s\[\d+:\d+\])")
     for n, line in enumerate(asm.splitlines(), 1):
         t = line.strip()
         if t.endswith("@function"):
-            depth = 0
+            stack = []
             allow = next((d for k, d in allowed_depth.items() if k in t), 0)
         elif t.startswith("s_endpgm"):
-            depth = 0
-        elif t.startswith("s_and_saveexec") or t.startswith("s_xor_saveexec"):
-            depth += 1
-        elif re.match(r"s_or_b64\s+exec,\s*exec", t):
-            depth = max(0, depth - 1)
-        elif t.startswith("v_mfma") and depth > allow:
+            stack = []
+        elif save.match(t):
+            reg = save.match(t).group(1)
+            if reg not in stack:
+                stack.append(reg)
+        elif restore.match(t):
+            reg = restore.match(t).group(1)
+            if reg in stack:
+                del stack[stack.index(reg):]
+            elif stack:
+                stack.pop()
+        elif t.startswith("v_mfma") and len(stack) > allow:
             bad.append((n, t))
     return bad
 
@@ -118,6 +131,17 @@ def test_scanner_flags_mfma_under_saveexec():
                       "v_mfma_f32_16x16x16_bf16 v[4:7], v[0:1], v[2:3], 0",
                       "s_or_b64 exec, exec, s[2:3]", "s_or_b64 exec, exec, s[0:1]", "s_endpgm"])
     assert [n for n, _ in mfma_under_partial_exec(role, {"k_role": 1})] == [5]
+    # An if/else nested in an if whose one restore of the outer mask closes both.
+    nested = "\n".join(["k2: ; @function",
+                         "s_and_saveexec_b64 s[30:31], vcc",
+                         "s_and_saveexec_b64 s[62:63], s[10:11]",
+                         "s_xor_b64 s[62:63], exec, s[62:63]",
+                         "v_mfma_f32_16x16x16_bf16 v[4:7], v[0:1], v[2:3], 0",
+                         "s_andn2_saveexec_b64 s[62:63], s[62:63]",
+                         "s_or_b64 exec, exec, s[30:31]",
+                         "v_mfma_f32_16x16x16_bf16 v[4:7], v[0:1], v[2:3], 0",
+                         "s_endpgm"])
+    assert [n for n, _ in mfma_under_partial_exec(nested)] == [5]
 
 
 def test_scanner_flags_a_mixed_chain():
