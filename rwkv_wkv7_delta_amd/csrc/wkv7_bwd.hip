@@ -488,9 +488,14 @@ constexpr int kP2Grid = 512;      // two resident workgroups per compute unit, l
 // Rows of a chunk staged in LDS: the six token inputs the gradients need,
 // then dX and Z; and the entry state and exit adjoint of both chunks as [j][i].
 enum { P2_R = 0, P2_W = 1, P2_K = 2, P2_A = 3, P2_B = 4, P2_DY = 5, P2_V = 6, P2_DX = 7, P2_Z = 8 };
+// The chunk's four L x L adjoints dAab, dAak, dArb, dArk (tile p from wave p),
+// bf16 in row layout; 20-element rows keep both the row reads and the
+// transposed reads of a tile nearly free of bank conflicts.
+constexpr int kTileRow = 20;
 struct __align__(16) P2Smem {
     bf16_t rows[2][9][kL][kRow];
     bf16_t st[2][2][kN][kRow];   // [S0 | dS][chunk of the pair][j][i]
+    bf16_t adj[4][kL][kTileRow];
 };
 
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_v;
@@ -518,7 +523,8 @@ __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
     __shared__ P2Smem sm;
     __shared__ int next_block;
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wp = tid >> 6;
+    // The wave index as a scalar (so that per-wave choices are uniform).
+    const int lane = tid & 63, wp = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, g = lane >> 4;
     const int col = 16 * wp + l16;     // key column j of this lane
 
@@ -649,10 +655,10 @@ __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
             const int i0 = 16 * vb + 4 * g;
             // [t][i] tiles of value block vb in accumulator layout (lane holds
             // [4g+q][l16]); fed as A operands they stand for their transposes.
-            const bf16x4 Vt = swap_layout(ld4(&sm.rows[0][P2_V][l16][16 * vb + 4 * g]), ident);
-            const bf16x4 Zt = swap_layout(ld4(&sm.rows[0][P2_Z][l16][16 * vb + 4 * g]), ident);
-            const bf16x4 dYt = swap_layout(ld4(&sm.rows[1][P2_DY][l16][16 * vb + 4 * g]), ident);
-            const bf16x4 dXt = swap_layout(ld4(&sm.rows[1][P2_DX][l16][16 * vb + 4 * g]), ident);
+            const bf16x4 Vt = ld4_tr(tr_addr(&sm.rows[0][P2_V][0][16 * vb], kRow, g, l16));
+            const bf16x4 Zt = ld4_tr(tr_addr(&sm.rows[0][P2_Z][0][16 * vb], kRow, g, l16));
+            const bf16x4 dYt = ld4_tr(tr_addr(&sm.rows[1][P2_DY][0][16 * vb], kRow, g, l16));
+            const bf16x4 dXt = ld4_tr(tr_addr(&sm.rows[1][P2_DX][0][16 * vb], kRow, g, l16));
             const bf16x4 s0 = ld4(&sm.st[0][0][col][i0]);
             const bf16x4 ds1 = ld4(&sm.st[1][1][col][i0]);
             f32x4 sacc, dacc;
@@ -687,46 +693,51 @@ __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
             dSc[k2] = ld8(&sm.st[1][h][col][i0]);
         }
 
-        // ---- L x L adjoints in both orientations ([t][s] and [s][t]) and the
-        // contractions over the value rows ------------------------------------------
-        f32x4 dAab = zero4(), dAabT = zero4(), dAak = zero4(), dAakT = zero4();
-        f32x4 dArb = zero4(), dArbT = zero4(), dArk = zero4(), dArkT = zero4();
+        // ---- the L x L adjoints, one per wave: wave p forms tile p of
+        // dAab = tril_-1(dX Z^T), dAak = tril_-1(dX V^T), dArb = tril_0(dY Z^T),
+        // dArk = tril_0(dY V^T) ([t][s], contracted over the value rows) and
+        // leaves it in row layout for the others -------------------------------------
+        {
+            const bool dyrow = (wp & 2) != 0, vcol = (wp & 1) != 0;
+            f32x4 At_s = zero4();
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2)
+                At_s = mfma32(dyrow ? dYr[k2] : dXr[k2], vcol ? Vr[k2] : Zr[k2], At_s);
+            // bf16 bits of the four values, taken from the packed words with
+            // integer shifts (a bit_cast of a single element of a bf16 vector
+            // compiled to the low half of the first word for every element).
+            const unsigned w01 = cvt2(At_s[0], At_s[1]), w23 = cvt2(At_s[2], At_s[3]);
+            const unsigned bits[4] = {w01 & 0xFFFFu, w01 >> 16, w23 & 0xFFFFu, w23 >> 16};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int t = 4 * g + q, s_ = l16;   // accumulator layout: [t][s] = [4g+q][l16]
+                const bool keep = dyrow ? s_ <= t : s_ < t;
+                sm.adj[wp][t][s_] = (bf16_t)(keep ? bits[q] : 0u);
+            }
+        }
+        // ---- the contractions over value rows that involve this wave's columns ------
         f32x4 dAt = zero4(), dRt = zero4(), dBb = zero4(), dKb = zero4();
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
-            dAab = mfma32(dXr[k2], Zr[k2], dAab);
-            dAabT = mfma32(Zr[k2], dXr[k2], dAabT);
-            dAak = mfma32(dXr[k2], Vr[k2], dAak);
-            dAakT = mfma32(Vr[k2], dXr[k2], dAakT);
-            dArb = mfma32(dYr[k2], Zr[k2], dArb);
-            dArbT = mfma32(Zr[k2], dYr[k2], dArbT);
-            dArk = mfma32(dYr[k2], Vr[k2], dArk);
-            dArkT = mfma32(Vr[k2], dYr[k2], dArkT);
             dAt = mfma32(dXr[k2], S0c[k2], dAt);     // dX S0
             dRt = mfma32(dYr[k2], S0c[k2], dRt);     // dY S0
             dBb = mfma32(Zr[k2], dSc[k2], dBb);      // Z dS
             dKb = mfma32(Vr[k2], dSc[k2], dKb);      // V dS
         }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int mm = 4 * g + q, n = l16;
-            dAab[q] = (n < mm) ? dAab[q] : 0.f;
-            dAak[q] = (n < mm) ? dAak[q] : 0.f;
-            dArb[q] = (n <= mm) ? dArb[q] : 0.f;
-            dArk[q] = (n <= mm) ? dArk[q] : 0.f;
-            dAabT[q] = (mm < n) ? dAabT[q] : 0.f;
-            dAakT[q] = (mm < n) ? dAakT[q] : 0.f;
-            dArbT[q] = (mm <= n) ? dArbT[q] : 0.f;
-            dArkT[q] = (mm <= n) ? dArkT[q] : 0.f;
-        }
-        // Accumulator registers of X fed as an A operand stand for X^T.  The
-        // 16-deep partial sums join the 32-deep ones on the vector ALU (add4).
-        dAt = add4(dAt, mfma16(cvt4(dAakT), f.khI, mfma16(cvt4(dAabT), f.bhI, zero4())));
-        dRt = add4(dRt, mfma16(cvt4(dArkT), f.khI, mfma16(cvt4(dArbT), f.bhI, zero4())));
-        f32x4 dBh = mfma16(cvt4(dAab), f.atI, zero4());
-        dBh = mfma16(cvt4(dArb), f.rtI, dBh);
-        f32x4 dKh = mfma16(cvt4(dAak), f.atI, zero4());
-        dKh = mfma16(cvt4(dArk), f.rtI, dKh);
+        __syncthreads();   // the four adjoint tiles are in LDS
+        // A tile read by rows is its A operand; read transposed, that of its
+        // transpose.  The 16-deep partial sums join the 32-deep ones on the
+        // vector ALU (add4).
+        const bf16x4 Aab = ld4(&sm.adj[0][l16][4 * g]), AabT = ld4_tr(tr_addr(&sm.adj[0][0][0], kTileRow, g, l16));
+        const bf16x4 Aak = ld4(&sm.adj[1][l16][4 * g]), AakT = ld4_tr(tr_addr(&sm.adj[1][0][0], kTileRow, g, l16));
+        const bf16x4 Arb = ld4(&sm.adj[2][l16][4 * g]), ArbT = ld4_tr(tr_addr(&sm.adj[2][0][0], kTileRow, g, l16));
+        const bf16x4 Ark = ld4(&sm.adj[3][l16][4 * g]), ArkT = ld4_tr(tr_addr(&sm.adj[3][0][0], kTileRow, g, l16));
+        dAt = add4(dAt, mfma16(Aak, f.khI, mfma16(Aab, f.bhI, zero4())));    // + dAab Bh + dAak Kh
+        dRt = add4(dRt, mfma16(Ark, f.khI, mfma16(Arb, f.bhI, zero4())));    // + dArb Bh + dArk Kh
+        f32x4 dBh = mfma16(AabT, f.atI, zero4());                             // dAab^T At
+        dBh = mfma16(ArbT, f.rtI, dBh);                                       // + dArb^T Rt
+        f32x4 dKh = mfma16(AakT, f.atI, zero4());                             // dAak^T At
+        dKh = mfma16(ArkT, f.rtI, dKh);                                       // + dArk^T Rt
 
         // ---- sum_i dS[i][col] S0[i][col] over this lane's 16 value rows -----------
         float cs = 0.f;
@@ -792,7 +803,7 @@ __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
             o_dr[q] = dRt[q] * f.Gt[q];
             o_db[q] = (dBh[q] + dBb[q] * f.GL) * f.inv[q];
             o_dk[q] = (dKh[q] + dKb[q] * f.GL) * f.inv[q];
-            o_dw[q] = dlw[q] / f.R[P2_W][q];
+            o_dw[q] = dlw[q] * __builtin_amdgcn_rcpf(f.R[P2_W][q]);
         }
         __syncthreads();   // every wave is done reading this chunk's staged rows
         const int j0 = 16 * wp + 4 * g;

@@ -103,6 +103,23 @@ __device__ __forceinline__ bf16x4 swap_layout(bf16x4 x, bf16x4 ident) {
     return cvt4(mfma16(x, ident, zero4()));
 }
 
+// Transposed LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane i receives element i % 4 of the 8-byte pieces that lanes i / 4 + 4 q
+// (q = 0 .. 3) point at.  So for a row-major bf16 array X whose 16 x 16 tile
+// starts at X[r0][c0], lane (g, j) passing &X[r0 + 4g + j/4][c0 + 4 (j%4)]
+// receives X[r0 + 4g + q][c0 + j], q = 0 .. 3: the accumulator layout of the
+// tile, i.e. the tile's transpose as an A operand (what swap_layout gives for
+// the row-layout read, without the matrix core).
+__device__ __forceinline__ const bf16_t* tr_addr(const bf16_t* tile, int row_stride, int g, int l16) {
+    return tile + (4 * g + (l16 >> 2)) * row_stride + 4 * (l16 & 3);
+}
+__device__ __forceinline__ bf16x4 ld4_tr(const bf16_t* p) {
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4s*)(p));
+    return __builtin_bit_cast(bf16x4, r);
+}
+
 // (I - A)^-1 for a strictly lower triangular 16x16 A (so A^16 = 0) as the
 // doubling product (I + A)(I + A^2)(I + A^4)(I + A^8), all on bf16 MFMA with
 // fp32 accumulation.  Inputs are the accumulator tiles of A and A^T; C-layout
