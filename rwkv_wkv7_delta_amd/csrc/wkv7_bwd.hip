@@ -607,10 +607,15 @@ __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
     // ---- decay products and scaled vectors of column `col` in chunk h ----------
     auto factors = [&](int h) __attribute__((always_inline)) -> KeyFactors {
         KeyFactors f;
+        // Tokens 4g .. 4g+3 of column col, one transposed read per vector.
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int vi = 0; vi < 5; ++vi) f.R[vi][q] = bf2f(sm.rows[h][vi][4 * g + q][col]);
+        for (int vi = 0; vi < 5; ++vi) {
+            const uint2 u = __builtin_bit_cast(uint2, ld4_tr(tr_addr(&sm.rows[h][vi][0][16 * wp], kRow, g, l16)));
+            f.R[vi][0] = __uint_as_float(u.x << 16);
+            f.R[vi][1] = __uint_as_float(u.x & 0xFFFF0000u);
+            f.R[vi][2] = __uint_as_float(u.y << 16);
+            f.R[vi][3] = __uint_as_float(u.y & 0xFFFF0000u);
+        }
         float gp[4];
         float run = 1.f;
 #pragma unroll
