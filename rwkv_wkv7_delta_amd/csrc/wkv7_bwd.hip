@@ -87,13 +87,12 @@ constexpr int kP1Threads = 576;   // 4 producer, 4 consumer waves, 1 inverse wav
 enum { P1_R = 0, P1_W = 1, P1_K = 2, P1_A = 3, P1_B = 4, P1_DY = 5 };
 enum { TILE_T = 0, TILE_RB = 1, TILE_AK = 2, TILE_RK = 3 };
 
-// Images are register contents stored lane by lane (8 bytes per lane, read
-// back by the same lane index): one conflict-free LDS access each way.
+// Rows [t][j] (the chain reads At, Rt and dy transposed, which gives the
+// matrix-core operand layouts directly) and images: register contents stored
+// lane by lane (8 bytes per lane, read back by the same lane index).
 struct P1Slot {
-    bf16_t At[kL][kRow], Rt[kL][kRow], Bh[kL][kRow], Kh[kL][kRow];  // E -> MW, [t][j]
-    bf16_t Bb[kL][kRow], Kb[kL][kRow];                              // E -> chain, [t][j]
-    uint2 atimg[4][64], rtimg[4][64];   // E -> chain: accumulator layout of At, Rt per key block
-    uint2 dyimg[4][64];                 // E -> chain: accumulator layout of dy per value block
+    bf16_t At[kL][kRow], Rt[kL][kRow], Bh[kL][kRow], Kh[kL][kRow];  // E -> MW, chain
+    bf16_t Bb[kL][kRow], Kb[kL][kRow], dY[kL][kRow];                // E -> chain
     float gL[kN];         // G_L of key 16 jt + 4 g + q at word 16 g + 4 jt + q
     uint2 tiles[4][64];   // MW -> chain: A-operand register images of Tm^T, Arb^T, Aak^T, Ark^T
 };
@@ -240,10 +239,7 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
         *reinterpret_cast<bf16x4*>(&s.Kh[l16][j0]) = cvt4(kh4);
         *reinterpret_cast<bf16x4*>(&s.Bb[l16][j0]) = cvt4(bb4);
         *reinterpret_cast<bf16x4*>(&s.Kb[l16][j0]) = cvt4(kb4);
-        s.atimg[wp][lane] = __builtin_bit_cast(uint2, swap_layout(atb, ident));
-        s.rtimg[wp][lane] = __builtin_bit_cast(uint2, swap_layout(rtb, ident));
-        s.dyimg[wp][lane] = __builtin_bit_cast(
-            uint2, swap_layout(__builtin_bit_cast(bf16x4, raw6[P1_DY]), ident));
+        *reinterpret_cast<uint2*>(&s.dY[l16][j0]) = raw6[P1_DY];
         if (l16 == kL - 1) *reinterpret_cast<float4*>(&s.gL[16 * g + 4 * wp]) = make_float4(gt[0], gt[1], gt[2], gt[3]);
     };
 
@@ -319,7 +315,7 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
         in.ArbT = __builtin_bit_cast(bf16x4, s.tiles[TILE_RB][lane]);
         in.AakT = __builtin_bit_cast(bf16x4, s.tiles[TILE_AK][lane]);
         in.ArkT = __builtin_bit_cast(bf16x4, s.tiles[TILE_RK][lane]);
-        in.dY = __builtin_bit_cast(bf16x4, s.dyimg[wp][lane]);
+        in.dY = ld4_tr(tr_addr(&s.dY[0][16 * wp], kRow, g, l16));   // [t][i] as a B operand
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
             in.bb[k2] = ld4x2(&s.Bb[l16][32 * k2 + 4 * g]);
@@ -327,8 +323,8 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
         }
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
-            in.rtT[jt] = __builtin_bit_cast(bf16x4, s.rtimg[jt][lane]);
-            in.atT[jt] = __builtin_bit_cast(bf16x4, s.atimg[jt][lane]);
+            in.rtT[jt] = ld4_tr(tr_addr(&s.Rt[0][16 * jt], kRow, g, l16));   // Rt^T as an A operand
+            in.atT[jt] = ld4_tr(tr_addr(&s.At[0][16 * jt], kRow, g, l16));
         }
         in.gl = s.gL[lane];
         return in;

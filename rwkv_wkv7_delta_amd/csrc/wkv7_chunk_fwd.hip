@@ -20,8 +20,9 @@
 //   Producer waves p = 0..3 build each chunk's state-independent factors:
 //     E   decay products and scaled vectors for key columns 16p..16p+15, in
 //         row layout (a lane per token, four columns each: 8-byte LDS
-//         accesses, the running product over tokens a DPP scan), with the
-//         operand images the consumers need turned through the matrix core;
+//         accesses, the running product over tokens a DPP scan); the
+//         consumers read Bb, Kb and v transposed (ds_read_b64_tr_b16), which
+//         is the layout their matrix-core products take;
 //     MW  one 16x16 tile each on waves 1..3: Aak, Arb, Ark.
 //   A ninth wave forms Aab and its triangular inverse Tm (a long chain of
 //   dependent matrix-core products, kept off the producers' path).
@@ -57,13 +58,13 @@ constexpr int kRow = kN + 8;    // rows of 64 elements
 enum { RAW_R = 0, RAW_W = 1, RAW_K = 2, RAW_A = 3, RAW_B = 4, RAW_V = 5 };
 enum { TILE_T = 0, TILE_AK = 1, TILE_RB = 2, TILE_RK = 3 };
 
-// Everything one chunk passes from the producers to the consumers.  "Images"
-// are register contents stored lane by lane (8 bytes per lane, read back by
-// the same lane index), so they cost one conflict-free LDS access each way.
+// Everything one chunk passes from the producers to the consumers: rows
+// [t][j] (the consumers read Bb, Kb and V transposed, which gives them the
+// matrix-core operand layouts directly) and "images", register contents
+// stored lane by lane (8 bytes per lane, read back by the same lane index).
 struct Slot {
-    bf16_t At[kL][kRow], Rt[kL][kRow], Bh[kL][kRow], Kh[kL][kRow];  // E -> MW, ST: row-major [t][j]
-    uint2 bbimg[4][64], kbimg[4][64];   // E -> ST: accumulator layout of Bb, Kb per key block
-    uint2 vimg[4][64];                  // E -> ST: accumulator layout of v per value block
+    bf16_t At[kL][kRow], Rt[kL][kRow], Bh[kL][kRow], Kh[kL][kRow];  // E -> MW, ST
+    bf16_t Bb[kL][kRow], Kb[kL][kRow], V[kL][kRow];                  // E -> ST
     float gL[kN];   // E -> ST: G_L of key 16 jt + 4 g + q at word 16 g + 4 jt + q
     uint2 tiles[4][64];   // MW -> ST: A-operand images of Tm, Aak, Arb, Ark (tile p from wave p)
 };
@@ -287,10 +288,9 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
         *reinterpret_cast<bf16x4*>(&s.Rt[l16][j0]) = cvt4(rt);
         *reinterpret_cast<bf16x4*>(&s.Bh[l16][j0]) = cvt4(bh4);
         *reinterpret_cast<bf16x4*>(&s.Kh[l16][j0]) = cvt4(kh4);
-        s.bbimg[wp][lane] = __builtin_bit_cast(uint2, swap_layout(cvt4(bb4), ident));
-        s.kbimg[wp][lane] = __builtin_bit_cast(uint2, swap_layout(cvt4(kb4), ident));
-        const uint2 vraw = wk.vzero ? make_uint2(0u, 0u) : raw6[RAW_V];
-        s.vimg[wp][lane] = __builtin_bit_cast(uint2, swap_layout(__builtin_bit_cast(bf16x4, vraw), ident));
+        *reinterpret_cast<bf16x4*>(&s.Bb[l16][j0]) = cvt4(bb4);
+        *reinterpret_cast<bf16x4*>(&s.Kb[l16][j0]) = cvt4(kb4);
+        *reinterpret_cast<uint2*>(&s.V[l16][j0]) = wk.vzero ? make_uint2(0u, 0u) : raw6[RAW_V];
         if (l16 == kL - 1) *reinterpret_cast<float4*>(&s.gL[16 * g + 4 * wp]) = make_float4(gt[0], gt[1], gt[2], gt[3]);
     };
 
@@ -366,7 +366,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
         in.Aak = __builtin_bit_cast(bf16x4, s.tiles[TILE_AK][lane]);
         in.Arb = __builtin_bit_cast(bf16x4, s.tiles[TILE_RB][lane]);
         in.Ark = __builtin_bit_cast(bf16x4, s.tiles[TILE_RK][lane]);
-        in.V = __builtin_bit_cast(bf16x4, s.vimg[wp][lane]);
+        in.V = ld4_tr(tr_addr(&s.V[0][16 * wp], kRow, g, l16));   // [t][i] as a B operand
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
             in.at[k2] = ld4x2(&s.At[l16][32 * k2 + 4 * g]);
@@ -374,8 +374,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
         }
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
-            in.bbt[jt] = __builtin_bit_cast(bf16x4, s.bbimg[jt][lane]);
-            in.kbt[jt] = __builtin_bit_cast(bf16x4, s.kbimg[jt][lane]);
+            in.bbt[jt] = ld4_tr(tr_addr(&s.Bb[0][16 * jt], kRow, g, l16));   // Bb^T as an A operand
+            in.kbt[jt] = ld4_tr(tr_addr(&s.Kb[0][16 * jt], kRow, g, l16));
         }
         in.gl = s.gL[lane];
         return in;
