@@ -503,9 +503,19 @@ struct KeyFactors {
     bf16x4 atI, rtI, bhI, khI, bbI, kbI;   // bf16 operand values of the forward
 };
 
-// The value that lane (gg, l16) of this wave holds, for every gg.
-__device__ __forceinline__ float from_group(float x, int gg, int l16) {
-    return __shfl(x, l16 + 16 * gg, 64);
+// The values that lanes (0, l16) .. (3, l16) of this wave hold (rows of 16
+// lanes), in every lane: one 32-lane and two 16-lane swaps (v_permlane32_swap
+// gives rows (0, 1, 0, 1) and (2, 3, 2, 3); v_permlane16_swap of each with
+// itself spreads its even and its odd row).
+__device__ __forceinline__ void rows_of(float x, float& x0, float& x1, float& x2, float& x3) {
+    const unsigned u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const auto b = __builtin_amdgcn_permlane16_swap(a[0], a[0], false, false);
+    const auto c = __builtin_amdgcn_permlane16_swap(a[1], a[1], false, false);
+    x0 = __uint_as_float(b[0]);
+    x1 = __uint_as_float(b[1]);
+    x2 = __uint_as_float(c[0]);
+    x3 = __uint_as_float(c[1]);
 }
 
 __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
@@ -619,8 +629,8 @@ __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
             run *= f.R[P2_W][q];
             gp[q] = run;
         }
-        const float g0 = from_group(run, 0, l16), g1 = from_group(run, 1, l16);
-        const float g2 = from_group(run, 2, l16), g3 = from_group(run, 3, l16);
+        float g0, g1, g2, g3;
+        rows_of(run, g0, g1, g2, g3);
         const float before = ((g >= 1 ? g0 : 1.f) * (g >= 2 ? g1 : 1.f)) * (g >= 3 ? g2 : 1.f);
         f.GL = ((g0 * g1) * g2) * g3;
         float at[4], rt[4], bh_[4], kh_[4], bbar[4], kbar[4];
@@ -765,17 +775,20 @@ __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
         const float sum_base = base[0] + base[1] + base[2] + base[3];
         const float sum_e = e[0] + e[1] + e[2] + e[3];
         const float sum_bk = bk[0] + bk[1] + bk[2] + bk[3];
-        float base_after = 0.f, e_after = 0.f, bk_before = 0.f, cs_all = 0.f;
+        float bs[4], es[4], ks[4], cg[4];
+        rows_of(sum_base, bs[0], bs[1], bs[2], bs[3]);
+        rows_of(sum_e, es[0], es[1], es[2], es[3]);
+        rows_of(sum_bk, ks[0], ks[1], ks[2], ks[3]);
+        rows_of(cs, cg[0], cg[1], cg[2], cg[3]);
+        float base_after = 0.f, e_after = 0.f, bk_before = 0.f;
+        const float cs_all = ((cg[0] + cg[1]) + cg[2]) + cg[3];
 #pragma unroll
         for (int g2 = 0; g2 < 4; ++g2) {
-            const float bs = from_group(sum_base, g2, l16), es = from_group(sum_e, g2, l16);
-            const float ks = from_group(sum_bk, g2, l16);
-            cs_all += from_group(cs, g2, l16);
             if (g2 > g) {
-                base_after += bs;
-                e_after += es;
+                base_after += bs[g2];
+                e_after += es[g2];
             }
-            if (g2 < g) bk_before += ks;
+            if (g2 < g) bk_before += ks[g2];
         }
         const float csL = cs_all * f.GL;
         float pbk[4];
