@@ -118,22 +118,25 @@ int wkv7_forward(const wkv7_desc *desc, const void *r, const void *w, const void
                  float *sT, void *tape, void *stream);
 
 /*
- * wkv7_forward with each head's sequence split in time, for problems with few
- * heads per compute unit, where one workgroup per head would leave most of the
- * device idle on a serial chain of T/16 chunks.  Same arguments and results as
+ * wkv7_forward with each head's sequence split in time, for the two shapes
+ * where one workgroup per head leaves the device idle on serial chains of
+ * T/16 chunks: few heads, and more heads than compute units (whose last,
+ * partial round of heads runs mostly alone).  Same arguments and results as
  * wkv7_forward (y, sT and tape agree with it to rounding), plus:
  *   segments   0: the library chooses from the device's compute-unit count
- *                 (split every head when B*H is at most a third of it; with
- *                 more heads than compute units, split the heads of the last,
- *                 partial round when they fill at most a third of it; segments
- *                 of at least 128 tokens; else no split);
- *              1: no split (exactly wkv7_forward);
- *              n >= 2: every head in up to n segments (fewer when T is short).
- *              Negative: WKV7_ERR_INVALID_ARG.  A split needs chunk_len = 16
- *              (WKV7_ERR_UNSUPPORTED for n >= 2 with chunk_len = 0).
+ *                 (B*H at most a third of it: every head by maps, below; more
+ *                 heads than compute units: the heads of the last, partial
+ *                 round by maps when they fill at most a third of it; else, or
+ *                 when T is too short for segments of 128 tokens, no split);
+ *              1 or -1: no split (exactly wkv7_forward);
+ *              n >= 2: every head in up to n segments by maps;
+ *              n <= -2: every head in up to -n sequential segments.
+ *              At most 16 segments; below -16: WKV7_ERR_INVALID_ARG.  A split
+ *              needs chunk_len = 16 (WKV7_ERR_UNSUPPORTED otherwise).
  *   workspace  wkv7_forward_split_workspace_bytes(desc, segments) bytes of
  *              device scratch, or NULL when that is 0; else WKV7_ERR_WORKSPACE.
- * Method: the state update is affine in the state, S <- S M_t + v_t k_t^T with
+ * Segments start at multiples of 32 tokens (the tape's state blocks).
+ * Maps: the state update is affine in the state, S <- S M_t + v_t k_t^T with
  * M_t = diag(w_t) + a_t b_t^T (the transition of "Paper Review: RWKV-7 Goose",
  * The approach), so a segment maps its entry state as S_out = S_in P + Hm,
  * P = the product of its transitions (a run from the identity with v = 0) and
@@ -141,8 +144,13 @@ int wkv7_forward(const wkv7_desc *desc, const void *r, const void *w, const void
  * outputs and the two map runs of segments 1 .. n-2 side by side; a small
  * kernel composes the entry states in fp32; a second launch re-runs segments
  * 1 .. n-1 from them with their outputs.  The serial chain per head falls
- * from T to about 2T/n tokens.  The automatic choice depends on the current
- * device: query the size and call on the same one.
+ * from T to about 2T/n tokens.
+ * Sequential: one workgroup per segment, numbered segment by segment over all
+ * heads; each waits for its head's previous segment to publish its final state
+ * (fp32, in the workspace) and publishes its own.  No extra work: the device
+ * takes segments as they come instead of whole heads.
+ * The automatic choice depends on the current device: query the size and call
+ * on the same one.
  */
 size_t wkv7_forward_split_workspace_bytes(const wkv7_desc *desc, int32_t segments);
 int wkv7_forward_split(const wkv7_desc *desc, const void *r, const void *w, const void *k,

@@ -40,6 +40,7 @@
 // register ring.  Chunks beyond T are all-padding (w = 1, everything else 0),
 // for which every stage is the identity on the state.
 
+#include "wkv7.h"
 #include "wkv7_device.h"
 #include "wkv7_internal.h"
 #include "wkv7_mfma.h"
@@ -150,14 +151,46 @@ __device__ __forceinline__ Work work_of(int blk, int pass, int T, const float* s
     return wk;
 }
 
+// Sequential segments (kSeq): every head runs as nseg segments in order, one
+// workgroup per segment, numbered segment-major: workgroup u runs segment
+// u / (B*H) of head u % (B*H).  Its entry state is the final state that the
+// head's previous segment (workgroup u - B*H) left in `states` (slot = head),
+// announced by the head's flag sync[head] = segments done.  Workgroups are
+// dispatched in order, so the one waited for started earlier and finishes
+// without waiting on any later one: the wait ends.  It is bounded all the same
+// (about a second), so that no fault elsewhere can turn it into a hang.
+constexpr int kSpinLimit = 1 << 24;
+
+template <bool kSeq>
 __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
     int B, int T, int H, const bf16_t* __restrict__ r, const bf16_t* __restrict__ w,
     const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const bf16_t* __restrict__ a,
     const bf16_t* __restrict__ b, const float* __restrict__ s0, bf16_t* __restrict__ y_all,
     float* __restrict__ sT, bf16_t* __restrict__ tape_all, int pass, int split_from, int nseg,
-    int seg_len, float* __restrict__ states) {
+    int seg_len, float* __restrict__ states, int* __restrict__ sync) {
     __shared__ FwdSmem sm;
-    const Work wk = work_of(blockIdx.x, pass, T, s0, sT, split_from, nseg, seg_len, states);
+    constexpr size_t NN = (size_t)kN * kN;
+    Work wk;
+    int seg = 0;
+    if (kSeq) {
+        const int nbh = B * H;
+        seg = blockIdx.x / nbh;
+        const int h = blockIdx.x % nbh;
+        if (threadIdx.x == 0 && seg > 0) {
+            for (int spin = 0; spin < kSpinLimit &&
+                               __hip_atomic_load(&sync[h], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < seg;
+                 ++spin)
+                __builtin_amdgcn_s_sleep(2);
+        }
+        __syncthreads();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // the previous segment's state
+        wk = Work{h, seg * seg_len, seg == nseg - 1 ? T : (seg + 1) * seg_len,
+                  seg == 0 ? (s0 ? s0 + (size_t)h * NN : nullptr) : states + (size_t)h * NN,
+                  seg == nseg - 1 ? (sT ? sT + (size_t)h * NN : nullptr) : states + (size_t)h * NN,
+                  false, false, true};
+    } else {
+        wk = work_of(blockIdx.x, pass, T, s0, sT, split_from, nseg, seg_len, states);
+    }
     const int bh = wk.bh;
     const int bb = bh / H, hh = bh % H;
     const int t_end = wk.t_end;
@@ -526,6 +559,19 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
             *reinterpret_cast<float4*>(dst + 16 * jt + 4 * g) =
                 make_float4(S[jt][0], S[jt][1], S[jt][2], S[jt][3]);
     }
+    if (kSeq) {
+        __syncthreads();   // every wave's share of the final state is stored
+        if (tid == 0) {
+            __threadfence();
+            __hip_atomic_store(&sync[bh], seg + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+// The per-head flags of the sequential segments start at zero.
+__global__ void seg_sync_init_kernel(int* __restrict__ sync, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) sync[i] = 0;
 }
 
 // Entry states of the split segments: S_in(s+1) = S_in(s) P(s) + Hm(s) for
@@ -542,21 +588,28 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(int nseg, float* __res
     const int t = threadIdx.x;
     const int i = (blockIdx.x % (kN / kCombineRows)) * kCombineRows + t / 16, li = t / 16;
     const int c4 = t % 16;
-    float4 pn[4], hn;
-    auto fetch = [&](int sg) __attribute__((always_inline)) {
-        const float4* P = reinterpret_cast<const float4*>(hst + (size_t)(2 * nseg + sg) * NN);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) pn[u] = P[t + 256 * u];   // rows 4u + t / 16 .. of P
-        hn = reinterpret_cast<const float4*>(hst + (size_t)(nseg + sg) * NN + i * kN)[c4];
-    };
+    // P (as 1024 float4, thread t taking t + 256 u) and this thread's piece of
+    // Hm, for step sg: plain named registers.
+    float4 pn0, pn1, pn2, pn3, hn;
+#define WKV7_COMBINE_FETCH(SG)                                                                  \
+    {                                                                                           \
+        const float4* P_ = reinterpret_cast<const float4*>(hst + (size_t)(2 * nseg + (SG)) * NN); \
+        pn0 = P_[t];                                                                            \
+        pn1 = P_[t + 256];                                                                      \
+        pn2 = P_[t + 512];                                                                      \
+        pn3 = P_[t + 768];                                                                      \
+        hn = reinterpret_cast<const float4*>(hst + (size_t)(nseg + (SG)) * NN + i * kN)[c4];      \
+    }
     *reinterpret_cast<float4*>(&Sr[li][4 * c4]) = reinterpret_cast<const float4*>(hst + NN + i * kN)[c4];
-    fetch(1);
+    WKV7_COMBINE_FETCH(1)
     for (int sg = 1; sg + 1 < nseg; ++sg) {
         const int buf = sg & 1;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) Pm[buf][(t + 256 * u) / 16][(t + 256 * u) % 16] = pn[u];
+        Pm[buf][t / 16][t % 16] = pn0;
+        Pm[buf][(t + 256) / 16][t % 16] = pn1;
+        Pm[buf][(t + 512) / 16][t % 16] = pn2;
+        Pm[buf][(t + 768) / 16][t % 16] = pn3;
         float4 acc = hn;
-        if (sg + 2 < nseg) fetch(sg + 1);
+        if (sg + 2 < nseg) WKV7_COMBINE_FETCH(sg + 1)
         __syncthreads();
 #pragma unroll 8
         for (int kk = 0; kk < kN; ++kk) {
@@ -571,6 +624,7 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(int nseg, float* __res
         reinterpret_cast<float4*>(hst + (size_t)(sg + 1) * NN + i * kN)[c4] = acc;
         *reinterpret_cast<float4*>(&Sr[li][4 * c4]) = acc;
     }
+#undef WKV7_COMBINE_FETCH
 }
 
 }  // namespace
@@ -579,21 +633,41 @@ hipError_t launch_chunk_fwd(const FwdArgs& p, int chunk_len, hipStream_t stream)
     return launch_chunk_fwd_split(p, chunk_len, FwdSplit{p.B * p.H, 1, p.T, nullptr}, stream);
 }
 
+hipError_t launch_chunk_fwd_sequential(const FwdArgs& p, int chunk_len, int nseg, int seg_len,
+                                       float* states, int* sync, hipStream_t stream) {
+    if (chunk_len != kL || !p.bf16) return hipErrorInvalidValue;
+    const int nbh = p.B * p.H;
+    if (nseg < 1 || seg_len <= 0 || seg_len % WKV7_TAPE_BLOCK != 0 ||
+        (long long)(nseg - 1) * seg_len >= p.T || !states || !sync ||
+        (long long)nbh * nseg > INT32_MAX)
+        return hipErrorInvalidValue;
+    seg_sync_init_kernel<<<dim3((nbh + 255) / 256), dim3(256), 0, stream>>>(sync, nbh);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    chunk_fwd_kernel<true><<<dim3(nbh * nseg), dim3(kThreads), 0, stream>>>(
+        p.B, p.T, p.H, static_cast<const bf16_t*>(p.r), static_cast<const bf16_t*>(p.w),
+        static_cast<const bf16_t*>(p.k), static_cast<const bf16_t*>(p.v),
+        static_cast<const bf16_t*>(p.a), static_cast<const bf16_t*>(p.b), p.s0,
+        static_cast<bf16_t*>(p.y), p.sT, static_cast<bf16_t*>(p.tape), 2, 0, nseg, seg_len, states,
+        sync);
+    return hipGetLastError();
+}
+
 hipError_t launch_chunk_fwd_split(const FwdArgs& p, int chunk_len, const FwdSplit& sp,
                                   hipStream_t stream) {
     if (chunk_len != kL || !p.bf16) return hipErrorInvalidValue;
     const int nbh = p.B * p.H;
     const int nsplit = nbh - sp.split_from;
-    if (nsplit < 0 || (nsplit > 0 && (sp.nseg < 2 || sp.seg_len % 32 != 0 || sp.seg_len <= 0 ||
+    if (nsplit < 0 || (nsplit > 0 && (sp.nseg < 2 || sp.seg_len % WKV7_TAPE_BLOCK != 0 || sp.seg_len <= 0 ||
                                        (long long)(sp.nseg - 1) * sp.seg_len >= p.T || !sp.states)))
         return hipErrorInvalidValue;
     auto run = [&](int pass, int grid) {
-        chunk_fwd_kernel<<<dim3(grid), dim3(kThreads), 0, stream>>>(
+        chunk_fwd_kernel<false><<<dim3(grid), dim3(kThreads), 0, stream>>>(
             p.B, p.T, p.H, static_cast<const bf16_t*>(p.r), static_cast<const bf16_t*>(p.w),
             static_cast<const bf16_t*>(p.k), static_cast<const bf16_t*>(p.v),
             static_cast<const bf16_t*>(p.a), static_cast<const bf16_t*>(p.b), p.s0,
             static_cast<bf16_t*>(p.y), p.sT, static_cast<bf16_t*>(p.tape), pass, sp.split_from,
-            sp.nseg, sp.seg_len, sp.states);
+            sp.nseg, sp.seg_len, sp.states, nullptr);
         return hipGetLastError();
     };
     hipError_t e = run(0, sp.split_from + (nsplit > 0 ? nsplit * (2 * sp.nseg - 3) : 0));

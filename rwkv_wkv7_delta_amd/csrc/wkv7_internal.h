@@ -55,6 +55,11 @@ struct FwdSplit {
 };
 hipError_t launch_chunk_fwd_split(const FwdArgs& p, int chunk_len, const FwdSplit& split,
                                   hipStream_t stream);
+// Every head as nseg segments of seg_len tokens run in order (one workgroup
+// per segment, segment-major); `states` holds one fp32 N x N state per head,
+// `sync` B*H ints (cleared by the launch).
+hipError_t launch_chunk_fwd_sequential(const FwdArgs& p, int chunk_len, int nseg, int seg_len,
+                                       float* states, int* sync, hipStream_t stream);
 // stages: bit 0 = the adjoint chain (dv, ds0, workspace), bit 1 = the per-key
 // gradients (dr, dw, dk, da, db; reads the workspace the chain wrote).
 enum { BWD_CHAIN = 1, BWD_KEYS = 2 };

@@ -89,6 +89,12 @@ def test_split_workspace_sizes(L):
     assert wk.split_workspace_bytes(d, 1) == 0
     assert wk.split_workspace_bytes(d, 40) == 48 * 3 * 16 * st      # at most 16 segments
     assert wk.split_workspace_bytes(d, -1) == 0
+    assert wk.split_workspace_bytes(d, -17) == 0
+    # Sequential segments: one fp32 state per head and one int flag per head
+    # (rounded up to 256 bytes), whatever the number of segments.
+    assert wk.split_workspace_bytes(d, -4) == 48 * st + 256
+    assert wk.split_workspace_bytes(wk.make_desc(8, 4096, 40, 64, wk.WKV7_BF16, 16), -4) == \
+        320 * st + 1280
     # T = 64: four segments would start at 0, 32, 64, 96; two fit.
     assert wk.split_workspace_bytes(wk.make_desc(1, 64, 2, 64, wk.WKV7_BF16, 16), 4) == 2 * 3 * 2 * st
     assert wk.split_workspace_bytes(wk.make_desc(1, 32, 2, 64, wk.WKV7_BF16, 16), 4) == 0
@@ -99,13 +105,15 @@ def test_split_forward_validation(L):
     d = wk.make_desc(1, 256, 1, 64, wk.WKV7_BF16, 16)
     f = L.wkv7_forward_split
     args = [FAKE] * 6 + [None, FAKE, None, None]
-    assert f(ctypes.byref(d), *args, -1, None, 0, None) == wk.WKV7_ERR_INVALID_ARG
+    assert f(ctypes.byref(d), *args, -17, None, 0, None) == wk.WKV7_ERR_INVALID_ARG
+    assert f(ctypes.byref(d), *args, -4, None, 0, None) == wk.WKV7_ERR_WORKSPACE
     assert f(ctypes.byref(d), *args, 4, None, 0, None) == wk.WKV7_ERR_WORKSPACE
     need = wk.split_workspace_bytes(d, 4)
     assert f(ctypes.byref(d), *args, 4, FAKE, need - 16, None) == wk.WKV7_ERR_WORKSPACE
     assert f(ctypes.byref(d), *args, 4, FAKE + 8, need, None) == wk.WKV7_ERR_INVALID_ARG
     d0 = wk.make_desc(1, 256, 1, 64, wk.WKV7_BF16, 0)
     assert f(ctypes.byref(d0), *args, 4, FAKE, need, None) == wk.WKV7_ERR_UNSUPPORTED
+    assert f(ctypes.byref(d0), *args, -4, FAKE, need, None) == wk.WKV7_ERR_UNSUPPORTED
     assert f(None, *args, 4, FAKE, need, None) == wk.WKV7_ERR_INVALID_ARG
     de = wk.make_desc(0, 256, 1, 64, wk.WKV7_BF16, 16)
     assert f(ctypes.byref(de), *args, 4, None, 0, None) == wk.WKV7_OK

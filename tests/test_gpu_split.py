@@ -1,11 +1,12 @@
 """GPU parity of the forward split in time (wkv7_forward_split).
 
-Each head's sequence runs as segments: segment 0 and the affine maps of the
-middle segments first, their entry states composed in fp32, then the remaining
-segments again with their outputs.  Every result (y, the final state, the tape
-and gradients computed from that tape) is compared with the fp64 oracle on the
-same seeded inputs, to the bf16 tolerance (max relative error <= 2e-2, cosine
->= 0.9999).
+Each head's sequence runs as segments, in one of two ways: by maps (segment 0
+and the affine maps of the middle segments first, their entry states composed
+in fp32, then the remaining segments again with their outputs), or
+sequentially (one workgroup per segment, each handing its final state to the
+next).  Every result (y, the final state, the tape and gradients computed from
+that tape) is compared with the fp64 oracle on the same seeded inputs, to the
+bf16 tolerance (max relative error <= 2e-2, cosine >= 0.9999).
 """
 
 import numpy as np
@@ -51,6 +52,43 @@ def test_split_fwd_matches_oracle(wk, segments, T):
     yr, sr = oracle.forward(*inp.tensors(), inp.s0)
     assert_close(y, yr, "bf16", f"split{segments} T={T} y")
     assert_close(sT, sr, "bf16", f"split{segments} T={T} sT")
+
+
+@pytest.mark.parametrize("segments", [-2, -3, -4, -7])
+@pytest.mark.parametrize("T", [100, 257, 512])
+def test_sequential_segments_match_oracle(wk, segments, T):
+    inp = synth.generate(2, T, 3, 64, dtype="bf16", seed=400 + T - segments, random_s0=True)
+    assert _plan_bytes(wk, inp, segments) > 0
+    y, sT, _ = _run(wk, inp, segments)
+    yr, sr = oracle.forward(*inp.tensors(), inp.s0)
+    assert_close(y, yr, "bf16", f"seq{-segments} T={T} y")
+    assert_close(sT, sr, "bf16", f"seq{-segments} T={T} sT")
+
+
+def test_sequential_segments_tape_and_backward(wk):
+    """The tape of a sequential split (segments [0, 64), [64, 128), [128, 150))
+    against the oracle's prefix states, and gradients computed from it."""
+    import torch
+    B, T, H = 1, 150, 2
+    inp = synth.generate(B, T, H, 64, dtype="bf16", seed=37, random_s0=True, backward=True)
+    _, _, tape = _run(wk, inp, -3, want_tape=True)
+    z, st = (to_np(x) for x in wk.split_tape(tape, B, T, H, 64))
+    xs = inp.tensors()
+    prefix = [inp.s0.astype(np.float64)]
+    for t in range(1, T):
+        prefix.append(oracle.forward(*(x[:, :t] for x in xs), inp.s0)[1])
+    zr = np.stack([np.einsum("bhij,bhj->bhi", prefix[t], xs[4][:, t].astype(np.float64))
+                   for t in range(T)], axis=1)
+    assert_close(z, zr, "bf16", "sequential tape z")
+    for m in range((T + 31) // 32):
+        assert_close(st[:, :, m], np.swapaxes(prefix[32 * m], -1, -2), "bf16", f"sequential tape state {m}")
+    dev = [to_dev(x, "bf16") for x in xs]
+    s0 = to_dev(inp.s0, "fp32")
+    g = wk.backward(*dev, to_dev(inp.dy, "bf16"), s0, None, tape)
+    torch.cuda.synchronize()
+    ref = oracle.backward(*xs, inp.s0, inp.dy, None)
+    for name, x, rr in zip(("dr", "dw", "dk", "dv", "da", "db", "ds0"), g, ref):
+        assert_close(to_np(x), rr, "bf16", f"sequential-tape {name}")
 
 
 def test_split_fwd_zero_state_and_short_last_segment(wk):
@@ -134,10 +172,32 @@ def test_split_fwd_partial_last_round(wk):
     assert_close(oracle.select_heads(sT, pairs, state=True), sr, "bf16", "tail split sT")
 
 
+def test_sequential_segments_2_9b_shape_sampled(wk):
+    """B=8, T=4096, H=40 as 4 sequential segments per head (1280 workgroups,
+    each waiting for its head's previous segment): sampled heads against the
+    oracle, the whole output against the unsplit forward's."""
+    import torch
+    B, T, H = 8, 4096, 40
+    inp = synth.generate(B, T, H, 64, dtype="bf16", seed=38, random_s0=True)
+    dev = [to_dev(x, "bf16") for x in inp.tensors()]
+    s0 = to_dev(inp.s0, "fp32")
+    y, sT, _ = wk.forward(*dev, s0, chunk_len=16, segments=-4)
+    y1, sT1, _ = wk.forward(*dev, s0, chunk_len=16)
+    torch.cuda.synchronize()
+    pairs = [(0, 0), (3, 21), (7, 39)]
+    sel = [oracle.select_heads(x, pairs) for x in inp.tensors()]
+    yr, sr = oracle.forward(*sel, oracle.select_heads(inp.s0, pairs, state=True))
+    yn, sn = to_np(y), to_np(sT)
+    assert_close(oracle.select_heads(yn, pairs), yr, "bf16", "2.9b sequential y")
+    assert_close(oracle.select_heads(sn, pairs, state=True), sr, "bf16", "2.9b sequential sT")
+    assert_close(yn, to_np(y1), "bf16", "2.9b sequential vs unsplit y")
+    assert_close(sn, to_np(sT1), "bf16", "2.9b sequential vs unsplit sT")
+
+
 def test_split_fwd_2_9b_shape_sampled(wk):
     """B=8, T=4096, H=40 (2.9B-model shape) with the automatic plan (the heads
     past the first full round are split) and the tape: sampled heads against
-    the oracle, the tape against the unsplit forward's."""
+    the oracle, the whole output and tape against the unsplit forward's."""
     import torch
     B, T, H = 8, 4096, 40
     inp = synth.generate(B, T, H, 64, dtype="bf16", seed=36)
@@ -154,5 +214,5 @@ def test_split_fwd_2_9b_shape_sampled(wk):
     assert_close(yn, to_np(y1), "bf16", "2.9b split vs unsplit y")
     z, st = wk.split_tape(tape, B, T, H, 64)
     z1, st1 = wk.split_tape(tape1, B, T, H, 64)
-    assert_close(to_np(z[6:]), to_np(z1[6:]), "bf16", "2.9b split tape z")
-    assert_close(to_np(st[6:]), to_np(st1[6:]), "bf16", "2.9b split tape states")
+    assert_close(to_np(z), to_np(z1), "bf16", "2.9b split tape z")
+    assert_close(to_np(st), to_np(st1), "bf16", "2.9b split tape states")

@@ -72,11 +72,12 @@ def mixed_shape_chains(asm: str):
 def mfma_under_partial_exec(asm: str, allowed_depth=None):
     """(line number, text) of every MFMA issued while more divergent regions
     are open than the function may have around it.  A region opens with an
-    s_and_saveexec / s_xor_saveexec / s_andn2_saveexec that saves EXEC to a new
-    register pair (an s_andn2_saveexec into a pair already saved is the else
-    half of an if/else: same region) and closes with the s_or_b64 exec that
-    restores that pair -- which also closes every region opened inside it (the
-    compiler often restores an outer mask without restoring the inner ones).
+    s_and_saveexec / s_xor_saveexec into a register pair not already saved; an
+    s_andn2_saveexec / s_or_saveexec enters the else half of an if/else (same
+    region).  A region closes with the s_or_b64 exec that restores its pair --
+    which also closes every region opened inside it (the compiler often
+    restores an outer mask without restoring the inner ones) -- or, when the
+    restored pair is not one saved on entry (an else half's), the innermost.
     allowed_depth maps a kernel-name fragment to the number of enclosing
     regions that are known to be wave-uniform (a role split by wave, which the
     compiler cannot prove uniform)."""
@@ -84,7 +85,7 @@ def mfma_under_partial_exec(asm: str, allowed_depth=None):
     bad = []
     stack = []
     allow = 0
-    save = re.compile(r"s_(?:and|xor|andn2)_saveexec_b64\s+(s\[\d+:\d+\])")
+    save = re.compile(r"s_(?:and|xor)_saveexec_b64\s+(s\[\d+:\d+\])")
     restore = re.compile(r"s_or_b64\s+exec,\s*exec,\s*(s\[\d+:\d+\])")
     for n, line in enumerate(asm.splitlines(), 1):
         t = line.strip()
