@@ -97,7 +97,8 @@ def _csv_rows(d, suffix):
 
 def _short(name):
     for k in KERNELS:
-        if f"::{k}(" in name:
+        # a plain kernel, or the plain instance of a kernel template
+        if f"::{k}(" in name or f"::{k}<false>(" in name:
             return k
     return None
 
