@@ -37,6 +37,10 @@ FWD_BYTES_PER_TH = 7 * 128          # forward: r, w, k, v, a, b in, y out
 ADJ_BYTES_PER_TH = 7 * 128          # adjoint pass: r, w, k, a, b, dy in, dv out
 GRAD_BYTES_PER_TH = 12 * 128        # gradient pass: r, w, k, v, a, b, dy in, dr, dw, dk, da, db out
 STATE_BYTES = 64 * 64 * 4           # one fp32 state
+# Template arguments of each kernel's instance for the general recurrence in one
+# launch (not the time-segmented or the a = b = 0 instances).
+PLAIN_INSTANCE = {"chunk_fwd_kernel": "<false, true>", "bwd_chain_kernel": "<true>",
+                  "bwd_keys_kernel": "<true>"}
 KERNELS = {   # kernel symbol -> (entry point that launches it alone, source, bytes per token-head)
     "chunk_fwd_kernel": ("wkv7_forward", "wkv7_chunk_fwd.hip", FWD_BYTES_PER_TH),
     "bwd_chain_kernel": ("wkv7_backward_adjoint", "wkv7_bwd.hip", ADJ_BYTES_PER_TH),
@@ -98,7 +102,7 @@ def _csv_rows(d, suffix):
 def _short(name):
     for k in KERNELS:
         # a plain kernel, or the plain instance of a kernel template
-        if f"::{k}(" in name or f"::{k}<false>(" in name:
+        if f"::{k}(" in name or f"::{k}{PLAIN_INSTANCE.get(k, '')}(" in name:
             return k
     return None
 
@@ -413,6 +417,38 @@ def secondary(torch, wk, dev):
                                "alg_GBs": round(nbytes / ms / 1e6, 1),
                                "frac_hbm": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
     del ins, s0, y
+    # a = b = 0 (the decay-only recurrence, a and b passed as NULL) at the
+    # 2.9B-model shape: the specialised forward (library's split plan, with its
+    # tape) and the overlapped backward (no da, db).
+    B, T, H = 8, 4096, 40
+    ins = _dev_inputs(torch, (B, T, H, N), dev, 5)[:4]
+    dy = torch.randn(B, T, H, N, device=dev).bfloat16()
+    aux = torch.cuda.Stream()
+    fdesc = wk.make_desc(B, T, H, N, wk.WKV7_BF16, 16)
+    tape = torch.empty(wk.tape_bytes(fdesc) // 2, device=dev, dtype=torch.bfloat16)
+    fws = torch.empty(max(wk.split_workspace_bytes(fdesc, 0) // 4, 4), device=dev)
+    bws = torch.empty(wk.workspace_bytes(fdesc, True) // 4, device=dev)
+    y = torch.empty_like(ins[0])
+    grads = [torch.empty_like(ins[0]) for _ in range(4)] + [None, None]
+
+    def fwd0():
+        wk.forward(*ins, None, None, None, chunk_len=16, want_state=False, out=y,
+                   segments=0, workspace=fws, tape_out=tape)
+
+    def step0():
+        fwd0()
+        wk.backward(*ins, None, None, dy, None, None, tape, want_ds0=False, workspace=bws,
+                    grads=grads, aux_stream=aux)
+
+    ms_f = _time(torch, fwd0, 10)
+    ms = _time(torch, step0, 10)
+    res["fwd_bwd_decay_only_2.9b"] = {
+        "workload": "B=8 T=4096 H=40 bf16, a = b = 0 (NULL), zero s0, split forward with tape "
+                    "+ overlapped backward (dr, dw, dk, dv)",
+        "ms": round(ms, 4), "tokens_per_s": round(B * T / ms * 1e3, 1),
+        "forward_ms": round(ms_f, 4),
+        "forward_alg_GBs": round(B * T * H * 5 * 128 / ms_f / 1e6, 1)}
+    del ins, dy, tape, fws, bws, y, grads
     # The 0.19B-model shape: few heads (48), so the T-long serial chain sets the
     # time (latency, not bandwidth); both forms of the forward.
     B, T, H = 4, 1024, 12

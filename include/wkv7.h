@@ -41,6 +41,14 @@
  *       WKV7_ERR_LAUNCH       the HIP runtime reported a launch error.
  *     No exception crosses the ABI.  There is no global mutable state, so
  *     concurrent calls on different streams are safe.
+ *   - a and b may both be NULL (with tokens; never just one of them): then
+ *     a = b = 0 and the transition is diagonal, S <- S diag(w_t) + v_t k_t^T,
+ *     the vector-decay recurrence that RWKV-7 extends ("Paper Review: RWKV-7
+ *     Goose", Background information on delta rule: RWKV-6 decays the state
+ *     with a diagonal transition).  Every entry point then runs kernels
+ *     specialised for it, which skip the removal terms; the forward does not
+ *     write the tape's Z part (the backward does not read it) and the
+ *     backward leaves da and db unwritten (they may be NULL).
  *   - Inputs must not alias outputs, except the decode state (in place).
  *   - Empty problems (B, H or T equal to 0) are valid.  With T = 0 the forward
  *     copies s0 (or zeros) to sT; y may then be NULL.

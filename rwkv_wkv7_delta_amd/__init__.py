@@ -8,7 +8,10 @@ built, every call raises.
 
 Per head the state S (N x N, row = value channel, column = key channel)
 evolves as ``S <- S (diag(w_t) + a_t b_t^T) + v_t k_t^T`` and ``y_t = S r_t``
-("Paper Review: RWKV-7 Goose", Architecture and The approach).
+("Paper Review: RWKV-7 Goose", Architecture and The approach).  Passing
+``a = b = None`` selects the decay-only recurrence ``S <- S diag(w_t) + v_t k_t^T``
+(a = b = 0; RWKV-6-style vector-decay linear attention), with specialised
+kernels that skip the removal terms; its backward returns ``da = db = None``.
 """
 
 from __future__ import annotations
@@ -122,6 +125,14 @@ def _check_tokens(ts, shape, dtype):
             raise ValueError(f"token tensor shape/dtype mismatch: {tuple(t.shape)} {t.dtype}")
 
 
+def _check_pair(a, b, shape, dtype):
+    """a and b: both token tensors, or both None (a = b = 0)."""
+    if (a is None) != (b is None):
+        raise ValueError("a and b must both be given or both be None")
+    if a is not None:
+        _check_tokens((a, b), shape, dtype)
+
+
 def _check_state(t, shape):
     torch = _torch()
     if t is None:
@@ -160,7 +171,8 @@ def split_tape(tape, B: int, T: int, H: int, N: int = HEAD_SIZE):
 
 
 def forward(r, w, k, v, a, b, s0=None, *, chunk_len: int = 0, want_state: bool = True,
-            want_tape: bool = False, out=None, segments: Optional[int] = None, workspace=None):
+            want_tape: bool = False, out=None, segments: Optional[int] = None, workspace=None,
+            tape_out=None):
     """Run the recurrence over [B, T, H, N] inputs.
 
     Returns ``(y, sT, tape)``; ``sT`` / ``tape`` are None unless requested (the
@@ -169,16 +181,24 @@ def forward(r, w, k, v, a, b, s0=None, *, chunk_len: int = 0, want_state: bool =
     ``segments`` (not None) selects wkv7_forward_split: 0 = the library's
     choice, 1 = no split, n >= 2 = every head in up to n time segments;
     ``workspace`` is then its device scratch (allocated here when None).
+    ``tape_out`` (a bf16 device tensor of at least ``tape_bytes`` bytes) receives
+    the tape instead of a new allocation.
     """
     torch = _torch()
     B, T, H, N = r.shape
-    _check_tokens((r, w, k, v, a, b), r.shape, r.dtype)
+    _check_tokens((r, w, k, v), r.shape, r.dtype)
+    _check_pair(a, b, r.shape, r.dtype)
     _check_state(s0, (B, H, N, N))
     desc = make_desc(B, T, H, N, _dtype_code(r), chunk_len)
     y = out if out is not None else torch.empty_like(r)
     sT = torch.empty((B, H, N, N), device=r.device, dtype=torch.float32) if want_state else None
     ck = None
-    if want_tape:
+    if tape_out is not None:
+        if not tape_out.is_cuda or not tape_out.is_contiguous() or \
+                tape_out.numel() * tape_out.element_size() < tape_bytes(desc):
+            raise ValueError("tape_out must be a contiguous device tensor of tape_bytes(desc) bytes")
+        ck = tape_out
+    elif want_tape:
         nbytes = tape_bytes(desc)
         ck = torch.empty(max(nbytes // 2, 8), device=r.device, dtype=torch.bfloat16)
     if segments is None:
@@ -215,17 +235,25 @@ def backward(r, w, k, v, a, b, dy, s0=None, dsT=None, tape=None, *, chunk_len: i
     selects the whole backward ("all") or one of its two stages ("adjoint",
     then "gradients" with the same ``workspace``, ``grads`` and ``ds0``).
     ``aux_stream`` (a torch stream) runs the whole backward on two streams
-    (wkv7_backward_overlapped).
+    (wkv7_backward_overlapped).  With ``a = b = None`` (a = b = 0) da and db
+    are not formed: they are returned (and may be passed in ``grads``) as None.
     """
     torch = _torch()
     B, T, H, N = r.shape
-    _check_tokens((r, w, k, v, a, b, dy), r.shape, r.dtype)
+    _check_tokens((r, w, k, v, dy), r.shape, r.dtype)
+    _check_pair(a, b, r.shape, r.dtype)
     _check_state(s0, (B, H, N, N))
     _check_state(dsT, (B, H, N, N))
     desc = make_desc(B, T, H, N, _dtype_code(r), chunk_len)
+    nab = 6 if a is not None else 4
     if grads is None:
-        grads = [torch.empty_like(r) for _ in range(6)]
-    _check_tokens(grads, r.shape, r.dtype)
+        grads = [torch.empty_like(r) for _ in range(nab)] + [None] * (6 - nab)
+    grads = list(grads)
+    if len(grads) != 6:
+        raise ValueError("grads holds (dr, dw, dk, dv, da, db)")
+    _check_tokens(grads[:nab], r.shape, r.dtype)
+    if a is None:
+        _check_pair(grads[4], grads[5], r.shape, r.dtype)
     if ds0 is None and want_ds0:
         ds0 = torch.empty((B, H, N, N), device=r.device, dtype=torch.float32)
     _check_state(ds0, (B, H, N, N))
@@ -252,7 +280,8 @@ def decode_step(r, w, k, v, a, b, state, out=None):
     """One token on resident states [B, H, N, N] (updated in place); returns y [B, H, N]."""
     torch = _torch()
     B, H, N = r.shape
-    _check_tokens((r, w, k, v, a, b), r.shape, r.dtype)
+    _check_tokens((r, w, k, v), r.shape, r.dtype)
+    _check_pair(a, b, r.shape, r.dtype)
     _check_state(state, (B, H, N, N))
     y = out if out is not None else torch.empty_like(r)
     st = lib().wkv7_decode_step(B, H, N, _dtype_code(r), _ptr(r), _ptr(w), _ptr(k), _ptr(v),

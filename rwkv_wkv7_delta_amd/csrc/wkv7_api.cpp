@@ -15,6 +15,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool req(const void* p) { return p != nullptr && aligned16(p); }
 // Optional pointer: null, or 16-byte aligned.
 bool opt(const void* p) { return p == nullptr || aligned16(p); }
+// The removal pair: both given (aligned), or both null for a = b = 0.
+bool pair(const void* a, const void* b) { return (a == nullptr && b == nullptr) || (req(a) && req(b)); }
 
 int check_desc(const wkv7_desc* d) {
     if (!d) return WKV7_ERR_INVALID_ARG;
@@ -173,7 +175,7 @@ int wkv7_forward(const wkv7_desc* desc, const void* r, const void* w, const void
     const int st = check_desc(desc);
     if (st != WKV7_OK) return st;
     const bool has_tokens = (int64_t)desc->B * desc->T * desc->H > 0;
-    if (has_tokens && !(req(r) && req(w) && req(k) && req(v) && req(a) && req(b) && req(y)))
+    if (has_tokens && !(req(r) && req(w) && req(k) && req(v) && pair(a, b) && req(y)))
         return WKV7_ERR_INVALID_ARG;
     if (!(opt(s0) && opt(sT) && opt(tape))) return WKV7_ERR_INVALID_ARG;
     return run_forward(desc, r, w, k, v, a, b, s0, y, sT, tape, static_cast<hipStream_t>(stream));
@@ -193,7 +195,7 @@ int wkv7_forward_split(const wkv7_desc* desc, const void* r, const void* w, cons
     if (segments < -kMaxSegments) return WKV7_ERR_INVALID_ARG;
     if ((segments > 1 || segments < -1) && desc->chunk_len != 16) return WKV7_ERR_UNSUPPORTED;
     const bool has_tokens = (int64_t)desc->B * desc->T * desc->H > 0;
-    if (has_tokens && !(req(r) && req(w) && req(k) && req(v) && req(a) && req(b) && req(y)))
+    if (has_tokens && !(req(r) && req(w) && req(k) && req(v) && pair(a, b) && req(y)))
         return WKV7_ERR_INVALID_ARG;
     if (!(opt(s0) && opt(sT) && opt(tape) && opt(workspace))) return WKV7_ERR_INVALID_ARG;
     const SplitPlan plan = plan_split(desc, segments, segments == 0 ? device_cus() : 0);
@@ -231,7 +233,7 @@ wkv7::BwdArgs slice(const wkv7_desc* d, int b0, int nb, const void* r, const voi
     auto tk = [&](const void* p) -> const void* {
         return p ? static_cast<const uint16_t*>(p) + (size_t)b0 * tok : nullptr;
     };
-    auto tkm = [&](void* p) -> void* { return static_cast<uint16_t*>(p) + (size_t)b0 * tok; };
+    auto tkm = [&](void* p) -> void* { return p ? static_cast<uint16_t*>(p) + (size_t)b0 * tok : nullptr; };
     auto sf = [&](const float* p) -> const float* { return p ? p + (size_t)b0 * sst : nullptr; };
     const uint16_t* tp = static_cast<const uint16_t*>(tape);
     uint16_t* wsp = static_cast<uint16_t*>(workspace);
@@ -258,8 +260,11 @@ int run_backward(const wkv7_desc* desc, const void* r, const void* w, const void
     if ((int64_t)desc->B * desc->H * ((desc->T + WKV7_TAPE_CHUNK - 1) / WKV7_TAPE_CHUNK) > INT32_MAX)
         return WKV7_ERR_UNSUPPORTED;
     const bool has_tokens = (int64_t)desc->B * desc->T * desc->H > 0;
-    if (has_tokens && !(req(r) && req(w) && req(k) && req(v) && req(a) && req(b) && req(dy) &&
-                        req(dr) && req(dw) && req(dk) && req(dv) && req(da) && req(db)))
+    // With a = b = 0 (both null) da and db are not written and may be null.
+    const bool ab = a != nullptr;
+    if (has_tokens && !(req(r) && req(w) && req(k) && req(v) && pair(a, b) && req(dy) &&
+                        req(dr) && req(dw) && req(dk) && req(dv) &&
+                        (ab ? req(da) && req(db) : opt(da) && opt(db))))
         return WKV7_ERR_INVALID_ARG;
     if (!(opt(s0) && opt(dsT) && opt(tape) && opt(ds0) && opt(workspace)))
         return WKV7_ERR_INVALID_ARG;
@@ -371,7 +376,7 @@ int wkv7_decode_step(int32_t B, int32_t H, int32_t N, int32_t dtype, const void*
     if (dtype != WKV7_F32 && dtype != WKV7_BF16) return WKV7_ERR_UNSUPPORTED;
     if ((int64_t)B * H > (int64_t)(1 << 28)) return WKV7_ERR_UNSUPPORTED;
     if ((int64_t)B * H == 0) return WKV7_OK;
-    if (!(req(r) && req(w) && req(k) && req(v) && req(a) && req(b) && req(state) && req(y)))
+    if (!(req(r) && req(w) && req(k) && req(v) && pair(a, b) && req(state) && req(y)))
         return WKV7_ERR_INVALID_ARG;
     wkv7::DecodeArgs p{B, H, dtype == WKV7_BF16, r, w, k, v, a, b, state, y};
     return from_hip(wkv7::launch_decode(p, static_cast<hipStream_t>(stream)));

@@ -105,6 +105,9 @@ struct __align__(16) P1Smem {
     bf16_t dSs[2][kN][kRow];      // the adjoint leaving the chunk as [j][i] (kept per 32 tokens)
 };
 
+// kAB = false: a = b = 0 (decay-only recurrence); a and b are not read and
+// stand as zero rows, so the removal terms vanish from every product.
+template <bool kAB>
 __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
     int T, int H, const bf16_t* __restrict__ r, const bf16_t* __restrict__ w,
     const bf16_t* __restrict__ k, const bf16_t* __restrict__ a, const bf16_t* __restrict__ b,
@@ -168,7 +171,14 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
         const int t = max(0, min(c * kL + ld_t, T - 1));
         const size_t off = tok_off(bb, t, hh, T, H) + ld_c8 * 8;
 #pragma unroll
-        for (int p = 0; p < 3; ++p) o.x[p] = *reinterpret_cast<const u32x4*>(sp_p[p] + off);
+        for (int p = 0; p < 3; ++p) {
+            if (kAB || !(p == 1 ? hi : p == 2 ? !hi : false)) {
+                o.x[p] = *reinterpret_cast<const u32x4*>(sp_p[p] + off);
+            } else {
+                const u32x4 z = {0u, 0u, 0u, 0u};   // a (p = 1, hi) or b (p = 2, lo): zero
+                o.x[p] = z;
+            }
+        }
     };
     auto stash_raw = [&](int c, const Raw& o) __attribute__((always_inline)) {
         if (c >= 0 && (c + 1) * kL <= T) {   // a whole chunk (the common case: no selects)
@@ -518,6 +528,9 @@ __device__ __forceinline__ void rows_of(float x, float& x0, float& x1, float& x2
     x3 = __uint_as_float(c[1]);
 }
 
+// kAB = false: a = b = 0; a, b and the removal read-outs Z are not read (they
+// stand as zero rows) and da, db are not written.
+template <bool kAB>
 __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
     int T, int H, int nch, int nblk, int nblocks, const bf16_t* __restrict__ r,
     const bf16_t* __restrict__ w, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
@@ -554,8 +567,13 @@ __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
             const int t = min((2 * m + h) * kL + ld_row, T - 1);
             const size_t off = tok_off(bh / H, t, bh % H, T, H) + 8 * ld_piece;
 #pragma unroll
-            for (int vi = 0; vi < 4; ++vi) o.x[h][vi] = *reinterpret_cast<const uint4*>(src4[vi] + off);
-            if (lo) o.x[h][4] = *reinterpret_cast<const uint4*>(tapeZ + off);
+            for (int vi = 0; vi < 4; ++vi) {
+                if (kAB || !(vi == 1 ? !lo : vi == 2 ? lo : false))
+                    o.x[h][vi] = *reinterpret_cast<const uint4*>(src4[vi] + off);
+                else
+                    o.x[h][vi] = make_uint4(0u, 0u, 0u, 0u);   // a (vi = 1, hi) or b (vi = 2, lo)
+            }
+            if (lo) o.x[h][4] = kAB ? *reinterpret_cast<const uint4*>(tapeZ + off) : make_uint4(0u, 0u, 0u, 0u);
         }
         const size_t sbase = (size_t)bi * kN * kN;
 #pragma unroll
@@ -838,10 +856,10 @@ __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
                 if (tid < 128) {
                     put(0, dr);
                     put(2, dk);
-                    put(4, db);
+                    if (kAB) put(4, db);
                 } else {
                     put(1, dw);
-                    put(3, da);
+                    if (kAB) put(3, da);
                 }
             }
         }
@@ -868,7 +886,8 @@ hipError_t launch_bwd(const BwdArgs& p, int chunk_len, int stages, hipStream_t s
     const bf16_t* b = static_cast<const bf16_t*>(p.b);
     const bf16_t* dy = static_cast<const bf16_t*>(p.dy);
     if (stages & BWD_CHAIN) {
-        bwd_chain_kernel<<<dim3(p.B * p.H), dim3(kP1Threads), 0, stream>>>(
+        auto chain = a ? bwd_chain_kernel<true> : bwd_chain_kernel<false>;
+        chain<<<dim3(p.B * p.H), dim3(kP1Threads), 0, stream>>>(
             p.T, p.H, r, w, k, a, b, dy, p.dsT, static_cast<bf16_t*>(p.dv), p.ds0,
             static_cast<bf16_t*>(p.workX), static_cast<bf16_t*>(p.workS), p.counter);
         const hipError_t e = hipGetLastError();
@@ -879,7 +898,8 @@ hipError_t launch_bwd(const BwdArgs& p, int chunk_len, int stages, hipStream_t s
     const int nblk = (nch + 1) / 2;
     const int nblocks = p.B * p.H * nblk;
     const int grid = nblocks < kP2Grid ? nblocks : kP2Grid;
-    bwd_keys_kernel<<<dim3(grid), dim3(kP2Threads), 0, stream>>>(
+    auto keys = a ? bwd_keys_kernel<true> : bwd_keys_kernel<false>;
+    keys<<<dim3(grid), dim3(kP2Threads), 0, stream>>>(
         p.T, p.H, nch, nblk, nblocks, r, w, k, v, a, b, dy, static_cast<const bf16_t*>(p.tapeZ),
         static_cast<const bf16_t*>(p.tapeS), static_cast<const bf16_t*>(p.workX),
         static_cast<const bf16_t*>(p.workS), static_cast<bf16_t*>(p.dr), static_cast<bf16_t*>(p.dw),

@@ -161,7 +161,12 @@ __device__ __forceinline__ Work work_of(int blk, int pass, int T, const float* s
 // (about a second), so that no fault elsewhere can turn it into a hang.
 constexpr int kSpinLimit = 1 << 24;
 
-template <bool kSeq>
+// kAB = false: a_t = b_t = 0 (decay-only linear attention, the RWKV-6-style
+// recurrence S <- S diag(w_t) + v_t k_t^T).  a and b are then not read; the
+// removal read-outs Z, the triangular inverse and the tiles Aak, Arb vanish,
+// leaving Y = Rt S0^T + Ark V and S_L^T = diag(G_L) S0^T + Kb^T V; the tape
+// holds only the block entry states (its Z part is not written).
+template <bool kSeq, bool kAB>
 __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
     int B, int T, int H, const bf16_t* __restrict__ r, const bf16_t* __restrict__ w,
     const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const bf16_t* __restrict__ a,
@@ -254,7 +259,14 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
         const int t = min(c * kL + ld_t, t_end - 1);
         const size_t off = tok_off(bb, t, hh, T, H) + ld_c8 * 8;
 #pragma unroll
-        for (int p = 0; p < 3; ++p) o.x[p] = *reinterpret_cast<const u32x4*>(sp_p[p] + off);
+        for (int p = 0; p < 3; ++p) {
+            if (kAB || !(p == 1 ? hi : p == 2 ? !hi : false)) {
+                o.x[p] = *reinterpret_cast<const u32x4*>(sp_p[p] + off);
+            } else {
+                const u32x4 z = {0u, 0u, 0u, 0u};   // a (p = 1, hi) or b (p = 2, lo): zero
+                o.x[p] = z;
+            }
+        }
     };
     auto stash_raw = [&](int c, const Raw& o) __attribute__((always_inline)) {
         if ((c + 1) * kL <= t_end) {   // a whole chunk (the common case: no selects)
@@ -317,11 +329,13 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
             bb4[cc] = bh4[cc] * GL;
             kb4[cc] = kh4[cc] * GL;
         }
-        *reinterpret_cast<bf16x4*>(&s.At[l16][j0]) = cvt4(at);
+        if (kAB) {
+            *reinterpret_cast<bf16x4*>(&s.At[l16][j0]) = cvt4(at);
+            *reinterpret_cast<bf16x4*>(&s.Bh[l16][j0]) = cvt4(bh4);
+            *reinterpret_cast<bf16x4*>(&s.Bb[l16][j0]) = cvt4(bb4);
+        }
         *reinterpret_cast<bf16x4*>(&s.Rt[l16][j0]) = cvt4(rt);
-        *reinterpret_cast<bf16x4*>(&s.Bh[l16][j0]) = cvt4(bh4);
         *reinterpret_cast<bf16x4*>(&s.Kh[l16][j0]) = cvt4(kh4);
-        *reinterpret_cast<bf16x4*>(&s.Bb[l16][j0]) = cvt4(bb4);
         *reinterpret_cast<bf16x4*>(&s.Kb[l16][j0]) = cvt4(kb4);
         *reinterpret_cast<uint2*>(&s.V[l16][j0]) = wk.vzero ? make_uint2(0u, 0u) : raw6[RAW_V];
         if (l16 == kL - 1) *reinterpret_cast<float4*>(&s.gL[16 * g + 4 * wp]) = make_float4(gt[0], gt[1], gt[2], gt[3]);
@@ -395,19 +409,21 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
     auto read_ST = [&](int c) __attribute__((always_inline)) -> STIn {
         const Slot& s = sm.sl[c % 3];
         STIn in;
-        in.Tm = __builtin_bit_cast(bf16x4, s.tiles[TILE_T][lane]);
-        in.Aak = __builtin_bit_cast(bf16x4, s.tiles[TILE_AK][lane]);
-        in.Arb = __builtin_bit_cast(bf16x4, s.tiles[TILE_RB][lane]);
         in.Ark = __builtin_bit_cast(bf16x4, s.tiles[TILE_RK][lane]);
         in.V = ld4_tr(tr_addr(&s.V[0][16 * wp], kRow, g, l16));   // [t][i] as a B operand
+        if (kAB) {
+            in.Tm = __builtin_bit_cast(bf16x4, s.tiles[TILE_T][lane]);
+            in.Aak = __builtin_bit_cast(bf16x4, s.tiles[TILE_AK][lane]);
+            in.Arb = __builtin_bit_cast(bf16x4, s.tiles[TILE_RB][lane]);
+        }
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
-            in.at[k2] = ld4x2(&s.At[l16][32 * k2 + 4 * g]);
+            if (kAB) in.at[k2] = ld4x2(&s.At[l16][32 * k2 + 4 * g]);
             in.rt[k2] = ld4x2(&s.Rt[l16][32 * k2 + 4 * g]);
         }
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
-            in.bbt[jt] = ld4_tr(tr_addr(&s.Bb[0][16 * jt], kRow, g, l16));   // Bb^T as an A operand
+            if (kAB) in.bbt[jt] = ld4_tr(tr_addr(&s.Bb[0][16 * jt], kRow, g, l16));   // Bb^T as an A operand
             in.kbt[jt] = ld4_tr(tr_addr(&s.Kb[0][16 * jt], kRow, g, l16));
         }
         in.gl = s.gL[lane];
@@ -424,18 +440,24 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
             const bf16x8 bs = cat8(Sb[2 * k2], Sb[2 * k2 + 1]);
-            Xs = mfma32(in.at[k2], bs, Xs);
+            if (kAB) Xs = mfma32(in.at[k2], bs, Xs);
             Ys = mfma32(in.rt[k2], bs, Ys);
         }
-        const f32x4 AkV = mfma16(in.Aak, in.V, zero4());
-        const bf16x4 Zb = cvt4(mfma16(in.Tm, cvt4(add4(Xs, AkV)), zero4()));
-        const f32x4 Yt = add4(Ys, mfma16(in.Ark, in.V, mfma16(in.Arb, Zb, zero4())));
+        bf16x4 Zb = {};
+        f32x4 Yt;
+        if (kAB) {
+            const f32x4 AkV = mfma16(in.Aak, in.V, zero4());
+            Zb = cvt4(mfma16(in.Tm, cvt4(add4(Xs, AkV)), zero4()));
+            Yt = add4(Ys, mfma16(in.Ark, in.V, mfma16(in.Arb, Zb, zero4())));
+        } else {
+            Yt = add4(Ys, mfma16(in.Ark, in.V, zero4()));
+        }
         const f32x4 dec[4] = {mul_row_lanes4<0>(in.gl, S[0]), mul_row_lanes4<1>(in.gl, S[1]),
                               mul_row_lanes4<2>(in.gl, S[2]), mul_row_lanes4<3>(in.gl, S[3])};
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
             const f32x4 acc = mfma16(in.kbt[jt], in.V, dec[jt]);   // G_L S^T + Kb^T V
-            S[jt] = mfma16(in.bbt[jt], Zb, acc);                    // + Bb^T Z
+            S[jt] = kAB ? mfma16(in.bbt[jt], Zb, acc) : acc;        // + Bb^T Z
         }
         // Outputs are staged in LDS in row layout (swap_layout: lane (g, l16)
         // holds 8 bytes of row l16) and leave next interval as whole 128-byte
@@ -443,7 +465,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
         const int i0 = 16 * wp + 4 * g;
         *reinterpret_cast<bf16x4*>(&sm.Ys[c & 1][l16][i0]) = swap_layout(cvt4(Yt), ident);
         if (tape) {
-            *reinterpret_cast<bf16x4*>(&sm.Zs[c & 1][l16][i0]) = swap_layout(Zb, ident);
+            if (kAB) *reinterpret_cast<bf16x4*>(&sm.Zs[c & 1][l16][i0]) = swap_layout(Zb, ident);
             if ((c & 1) == 0) {   // entry state of a 32-token block as [j][i]: row layout of S^T tile jt
 #pragma unroll
                 for (int jt = 0; jt < 4; ++jt)
@@ -458,7 +480,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
         const int row = (rtid >> 3) & 15, piece = rtid & 7;
         const int tt = c * kL + row;
         if (tt < t_end) {
-            bf16_t* base = rtid < 128 ? y : tapeZ;
+            bf16_t* base = rtid < 128 ? y : (kAB ? tapeZ : nullptr);
             const bf16_t(*src)[kRow] = rtid < 128 ? sm.Ys[c & 1] : sm.Zs[c & 1];
             if (base)
                 store_stream(base + tok_off(bb, tt, hh, T, H) + 8 * piece,
@@ -508,11 +530,11 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
         const int c_ = cb + it_;                                            \
         const ERaw er = read_E(c_);                                         \
         MWIn mi;                                                            \
-        if (it_ >= 1 && wp != 0) mi = read_MW(c_ - 1);                      \
+        if (it_ >= 1 && (kAB ? wp != 0 : wp == 3)) mi = read_MW(c_ - 1);    \
         stage_E(c_, er);                                                    \
         stash_raw(c_ + 1, RING);                                            \
         load_raw(c_ + 4, RING);                                             \
-        if (it_ >= 1 && wp != 0) stage_MW(c_ - 1, mi);                      \
+        if (it_ >= 1 && (kAB ? wp != 0 : wp == 3)) stage_MW(c_ - 1, mi);    \
         __syncthreads();                                                    \
     }
             // Ring slot of interval it is (it + 1) % 3: it = 0, 1, 2 -> rb1, rb2, rb0.
@@ -530,7 +552,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
             // Interval it: the inverse of chunk it-1 (after E(it-1), read by the
             // consumers' chain in interval it+1).
             for (int it = 0; it < n_it; ++it) {
-                if (it >= 1) stage_INV(cb + it - 1);
+                if (kAB && it >= 1) stage_INV(cb + it - 1);
                 __syncthreads();
             }
         } else {
@@ -644,7 +666,8 @@ hipError_t launch_chunk_fwd_sequential(const FwdArgs& p, int chunk_len, int nseg
     seg_sync_init_kernel<<<dim3((nbh + 255) / 256), dim3(256), 0, stream>>>(sync, nbh);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    chunk_fwd_kernel<true><<<dim3(nbh * nseg), dim3(kThreads), 0, stream>>>(
+    auto kern = p.a ? chunk_fwd_kernel<true, true> : chunk_fwd_kernel<true, false>;
+    kern<<<dim3(nbh * nseg), dim3(kThreads), 0, stream>>>(
         p.B, p.T, p.H, static_cast<const bf16_t*>(p.r), static_cast<const bf16_t*>(p.w),
         static_cast<const bf16_t*>(p.k), static_cast<const bf16_t*>(p.v),
         static_cast<const bf16_t*>(p.a), static_cast<const bf16_t*>(p.b), p.s0,
@@ -662,7 +685,8 @@ hipError_t launch_chunk_fwd_split(const FwdArgs& p, int chunk_len, const FwdSpli
                                        (long long)(sp.nseg - 1) * sp.seg_len >= p.T || !sp.states)))
         return hipErrorInvalidValue;
     auto run = [&](int pass, int grid) {
-        chunk_fwd_kernel<false><<<dim3(grid), dim3(kThreads), 0, stream>>>(
+        auto kern = p.a ? chunk_fwd_kernel<false, true> : chunk_fwd_kernel<false, false>;
+        kern<<<dim3(grid), dim3(kThreads), 0, stream>>>(
             p.B, p.T, p.H, static_cast<const bf16_t*>(p.r), static_cast<const bf16_t*>(p.w),
             static_cast<const bf16_t*>(p.k), static_cast<const bf16_t*>(p.v),
             static_cast<const bf16_t*>(p.a), static_cast<const bf16_t*>(p.b), p.s0,

@@ -26,7 +26,9 @@ namespace {
 constexpr int kTB = 16;  // tokens per LDS stage
 static_assert(kTB == 16, "the tape's removal read-outs and states follow 16-token chunks");
 
-template <typename Tin, int WAVES>
+// kAB = false: a = b = 0 (decay-only recurrence S <- S diag(w) + v k^T); a and
+// b are not read, z is not formed and the tape's Z part is not written.
+template <typename Tin, int WAVES, bool kAB>
 __global__ __launch_bounds__(64 * WAVES) void seq_fwd_kernel(
     int T, int H, const Tin* __restrict__ r, const Tin* __restrict__ w,
     const Tin* __restrict__ k, const Tin* __restrict__ v, const Tin* __restrict__ a,
@@ -63,9 +65,10 @@ __global__ __launch_bounds__(64 * WAVES) void seq_fwd_kernel(
 
     float4 pre[5][PER];
     float4 prev = make_float4(0.f, 0.f, 0.f, 0.f);
+    constexpr int NQ = kAB ? 5 : 3;   // token vectors staged: r, w, k (, a, b)
     auto load_regs = [&](int t0) {
 #pragma unroll
-        for (int q = 0; q < 5; ++q)
+        for (int q = 0; q < NQ; ++q)
 #pragma unroll
             for (int p = 0; p < PER; ++p) {
                 const int idx = tid + p * NT;
@@ -81,7 +84,7 @@ __global__ __launch_bounds__(64 * WAVES) void seq_fwd_kernel(
     };
     auto store_lds = [&]() {
 #pragma unroll
-        for (int q = 0; q < 5; ++q)
+        for (int q = 0; q < NQ; ++q)
 #pragma unroll
             for (int p = 0; p < PER; ++p) {
                 const int idx = tid + p * NT;
@@ -109,15 +112,22 @@ __global__ __launch_bounds__(64 * WAVES) void seq_fwd_kernel(
             dst[(cq * 4 + 3) * kN] = f2bf(S.w);
         }
         for (int t = 0; t < nt; ++t) {
-            const float4 A = sm[3][t][cq], Bv = sm[4][t][cq], W = sm[1][t][cq];
-            const float4 K = sm[2][t][cq], Rr = sm[0][t][cq];
+            const float4 W = sm[1][t][cq], K = sm[2][t][cq], Rr = sm[0][t][cq];
             const float vi = sv[t][rloc];
-            const float z = row16_sum(dot4(S, A));
-            if (cq == 0) sz[t][rloc] = z;
-            S.x = fmaf(vi, K.x, fmaf(z, Bv.x, S.x * W.x));
-            S.y = fmaf(vi, K.y, fmaf(z, Bv.y, S.y * W.y));
-            S.z = fmaf(vi, K.z, fmaf(z, Bv.z, S.z * W.z));
-            S.w = fmaf(vi, K.w, fmaf(z, Bv.w, S.w * W.w));
+            if (kAB) {
+                const float4 A = sm[3][t][cq], Bv = sm[4][t][cq];
+                const float z = row16_sum(dot4(S, A));
+                if (cq == 0) sz[t][rloc] = z;
+                S.x = fmaf(vi, K.x, fmaf(z, Bv.x, S.x * W.x));
+                S.y = fmaf(vi, K.y, fmaf(z, Bv.y, S.y * W.y));
+                S.z = fmaf(vi, K.z, fmaf(z, Bv.z, S.z * W.z));
+                S.w = fmaf(vi, K.w, fmaf(z, Bv.w, S.w * W.w));
+            } else {
+                S.x = fmaf(vi, K.x, S.x * W.x);
+                S.y = fmaf(vi, K.y, S.y * W.y);
+                S.z = fmaf(vi, K.z, S.z * W.z);
+                S.w = fmaf(vi, K.w, S.w * W.w);
+            }
             const float yy = row16_sum(dot4(S, Rr));
             if (cq == 0) sy[t][rloc] = yy;
         }
@@ -126,7 +136,7 @@ __global__ __launch_bounds__(64 * WAVES) void seq_fwd_kernel(
             const int t = idx / R, i = idx % R;
             Elem<Tin>::store1(y + tok_off(bb, t0 + t, hh, T, H) + rb * R + i, sy[t][i]);
         }
-        for (int idx = tid; tape && idx < nt * R; idx += NT) {
+        for (int idx = tid; kAB && tape && idx < nt * R; idx += NT) {
             const int t = idx / R, i = idx % R;
             tapeZ[tok_off(bb, t0 + t, hh, T, H) + rb * R + i] = f2bf(sz[t][i]);
         }
@@ -139,7 +149,7 @@ __global__ __launch_bounds__(64 * WAVES) void seq_fwd_kernel(
 // One token on resident states.  One workgroup of 4 waves per (b, h); each
 // wave updates 16 rows as 4 groups of 4 rows, every lane 4 consecutive
 // columns, so each state row is one contiguous 256-byte segment per 16 lanes.
-template <typename Tin>
+template <typename Tin, bool kAB>
 __global__ __launch_bounds__(256) void decode_kernel(
     const Tin* __restrict__ r, const Tin* __restrict__ w, const Tin* __restrict__ k,
     const Tin* __restrict__ v, const Tin* __restrict__ a, const Tin* __restrict__ b,
@@ -157,8 +167,10 @@ __global__ __launch_bounds__(256) void decode_kernel(
         S[g] = *reinterpret_cast<const float4*>(st + row * kN + cq * 4);
         vv[g] = Elem<Tin>::load1(v + io + row);
     }
-    const float4 A = Elem<Tin>::load4(a + io + cq * 4);
-    const float4 Bv = Elem<Tin>::load4(b + io + cq * 4);
+    // a = b = 0 (kAB false): nothing to load, z = 0.
+    const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 A = kAB ? Elem<Tin>::load4(a + io + cq * 4) : zero;
+    const float4 Bv = kAB ? Elem<Tin>::load4(b + io + cq * 4) : zero;
     const float4 W = Elem<Tin>::load4(w + io + cq * 4);
     const float4 K = Elem<Tin>::load4(k + io + cq * 4);
     const float4 Rr = Elem<Tin>::load4(r + io + cq * 4);
@@ -166,7 +178,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
     for (int g = 0; g < 4; ++g) {
         const int row = wave * 16 + g * 4 + (lane >> 4);
         float4 s = S[g];
-        const float z = row16_sum(dot4(s, A));
+        const float z = kAB ? row16_sum(dot4(s, A)) : 0.f;
         s.x = fmaf(vv[g], K.x, fmaf(z, Bv.x, s.x * W.x));
         s.y = fmaf(vv[g], K.y, fmaf(z, Bv.y, s.y * W.y));
         s.z = fmaf(vv[g], K.z, fmaf(z, Bv.z, s.z * W.z));
@@ -198,10 +210,12 @@ hipError_t launch_seq_fwd_t(const FwdArgs& p, hipStream_t stream) {
     Tin* y = static_cast<Tin*>(p.y);
     // Few heads: split each head's rows over 4 workgroups to occupy more CUs.
     if (BH < 512) {
-        seq_fwd_kernel<Tin, 4><<<dim3(BH * 4), dim3(256), 0, stream>>>(
+        auto kern = a ? seq_fwd_kernel<Tin, 4, true> : seq_fwd_kernel<Tin, 4, false>;
+        kern<<<dim3(BH * 4), dim3(256), 0, stream>>>(
             p.T, p.H, r, w, k, v, a, b, p.s0, y, p.sT, static_cast<bf16_t*>(p.tape));
     } else {
-        seq_fwd_kernel<Tin, 16><<<dim3(BH), dim3(1024), 0, stream>>>(
+        auto kern = a ? seq_fwd_kernel<Tin, 16, true> : seq_fwd_kernel<Tin, 16, false>;
+        kern<<<dim3(BH), dim3(1024), 0, stream>>>(
             p.T, p.H, r, w, k, v, a, b, p.s0, y, p.sT, static_cast<bf16_t*>(p.tape));
     }
     return hipGetLastError();
@@ -209,7 +223,8 @@ hipError_t launch_seq_fwd_t(const FwdArgs& p, hipStream_t stream) {
 
 template <typename Tin>
 hipError_t launch_decode_t(const DecodeArgs& p, hipStream_t stream) {
-    decode_kernel<Tin><<<dim3(p.B * p.H), dim3(256), 0, stream>>>(
+    auto kern = p.a ? decode_kernel<Tin, true> : decode_kernel<Tin, false>;
+    kern<<<dim3(p.B * p.H), dim3(256), 0, stream>>>(
         static_cast<const Tin*>(p.r), static_cast<const Tin*>(p.w),
         static_cast<const Tin*>(p.k), static_cast<const Tin*>(p.v),
         static_cast<const Tin*>(p.a), static_cast<const Tin*>(p.b), p.state,

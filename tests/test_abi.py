@@ -191,6 +191,31 @@ def test_decode_validation(L):
     assert f(0, 3, 64, wk.WKV7_BF16, *[FAKE] * 8, None) == wk.WKV7_OK
 
 
+def test_removal_pair_validation(L):
+    """a and b are both given or both NULL (a = b = 0); one alone is an invalid
+    argument.  With both NULL the backward accepts NULL da and db; with both
+    given it still requires them."""
+    d = wk.make_desc(1, 8, 1, 64, wk.WKV7_BF16, 16)
+    for ab in ([FAKE, None], [None, FAKE]):
+        assert _fwd(L, d, ptrs=[FAKE] * 4 + ab) == wk.WKV7_ERR_INVALID_ARG
+        assert L.wkv7_forward_split(ctypes.byref(d), *[FAKE] * 4, *ab, None, FAKE, None, None,
+                                    1, None, 0, None) == wk.WKV7_ERR_INVALID_ARG
+        assert L.wkv7_decode_step(1, 1, 64, wk.WKV7_BF16, *[FAKE] * 4, *ab, FAKE, FAKE, None) == \
+            wk.WKV7_ERR_INVALID_ARG
+        assert L.wkv7_backward(ctypes.byref(d), *[FAKE] * 4, *ab, None, FAKE, None, None,
+                               *[FAKE] * 6, None, FAKE, 1 << 30, None) == wk.WKV7_ERR_INVALID_ARG
+    # Both NULL: validation passes up to the workspace check (nothing is launched).
+    assert L.wkv7_backward(ctypes.byref(d), *[FAKE] * 4, None, None, None, FAKE, None, None,
+                           *[FAKE] * 4, None, None, None, None, 0, None) == wk.WKV7_ERR_WORKSPACE
+    assert L.wkv7_backward(ctypes.byref(d), *[FAKE] * 4, None, None, None, FAKE, None, None,
+                           *[FAKE] * 4, FAKE + 8, None, None, None, 0, None) == wk.WKV7_ERR_INVALID_ARG
+    # Both given: da and db are required.
+    assert L.wkv7_backward(ctypes.byref(d), *[FAKE] * 6, None, FAKE, None, None,
+                           *[FAKE] * 4, None, None, None, FAKE, 1 << 30, None) == wk.WKV7_ERR_INVALID_ARG
+    # Empty problems stay valid with a = b = NULL.
+    assert _fwd(L, wk.make_desc(0, 8, 4, 64, wk.WKV7_BF16, 16), ptrs=[FAKE] * 4 + [None, None]) == wk.WKV7_OK
+
+
 def test_binding_has_no_cpu_fallback():
     """The binding routes every call through libwkv7.so and never imports the oracle."""
     import inspect

@@ -422,6 +422,57 @@ def test_backward_linear_attention_closed_form():
     np.testing.assert_allclose(ds0, dsT + np.einsum("bthi,bthj->bhij", dy, r), atol=1e-12)
 
 
+def test_backward_decay_only_closed_form():
+    """a = b = 0 with decay: every gradient of L = sum_t <dy_t, y_t> + <dsT, S_T>
+    written out from y_t = s0 (G_t * r_t) + sum_{s<=t} v_s <k_s * P(s,t), r_t>
+    and S_T = s0 diag(G_T) + sum_s v_s (k_s * P(s,T))^T, where P(s,t) = the
+    product of w_u over s < u <= t and G_t = the product over u <= t.  dw_u
+    collects, divided by w_u, every term whose product contains w_u."""
+    B, T, H, N = 1, 7, 2, 5
+    r, k, v, dy = (_rand((B, T, H, N), s) for s in (55, 56, 57, 58))
+    w = rng0(59).uniform(0.3, 1.0, (B, T, H, N))
+    s0 = _rand((B, H, N, N), 60)
+    dsT = _rand((B, H, N, N), 61)
+    z = np.zeros_like(r)
+    dr, dw, dk, dv, da, db, ds0 = oracle.backward(r, w, k, v, z, z, s0, dy, dsT)
+    for hh in range(H):
+        R, W, K, V, DY = (x[0, :, hh] for x in (r, w, k, v, dy))
+        S0, DS = s0[0, hh], dsT[0, hh]
+
+        def P(s, t):                          # prod of w_u, s < u <= t
+            return np.prod(W[s + 1: t + 1], axis=0)
+
+        def G(t):                             # prod of w_u, u <= t
+            return np.prod(W[: t + 1], axis=0)
+
+        ref_dv = np.zeros((T, N)); ref_dk = np.zeros((T, N)); ref_dr = np.zeros((T, N))
+        ref_dw = np.zeros((T, N)); ref_ds0 = DS * G(T - 1)[None, :]
+        for t in range(T):
+            ref_dr[t] = (DY[t] @ S0) * G(t)
+            ref_ds0 += np.outer(DY[t], G(t) * R[t])
+            for s in range(t + 1):
+                vd = V[s] @ DY[t]
+                ref_dv[s] += DY[t] * np.dot(K[s] * P(s, t), R[t])
+                ref_dk[s] += vd * R[t] * P(s, t)
+                ref_dr[t] += vd * K[s] * P(s, t)
+        for s in range(T):
+            ref_dv[s] += DS @ (K[s] * P(s, T - 1))
+            ref_dk[s] += (V[s] @ DS) * P(s, T - 1)
+        for u in range(T):
+            acc = np.zeros(N)
+            for t in range(u, T):
+                acc += (DY[t] @ S0) * G(t) * R[t]
+                for s in range(u):
+                    acc += (V[s] @ DY[t]) * K[s] * R[t] * P(s, t)
+            for s in range(u):
+                acc += (V[s] @ DS) * K[s] * P(s, T - 1)
+            acc += np.einsum("ij,ij->j", DS, S0) * G(T - 1)
+            ref_dw[u] = acc / W[u]
+        for got, ref in ((dv, ref_dv), (dk, ref_dk), (dr, ref_dr), (dw, ref_dw)):
+            np.testing.assert_allclose(got[0, :, hh], ref, rtol=0, atol=1e-11)
+        np.testing.assert_allclose(ds0[0, hh], ref_ds0, rtol=0, atol=1e-11)
+
+
 @pytest.mark.parametrize("L", [1, 5, 16, 64])
 def test_chunked_backward_equals_sequential(L):
     inp = synth.generate(2, 70, 2, 16, dtype="bf16", seed=53, random_s0=True, backward=True)
