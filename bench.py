@@ -526,6 +526,32 @@ def secondary(torch, wk, dev):
                           "tokens_per_s": round(Bd2 / per_step * 1e3, 1),
                           "alg_GBs": round(nbytes / per_step / 1e6, 1),
                           "frac_hbm": round(nbytes / per_step / 1e6 / HBM_PEAK_GBS, 4)}
+    del st, one, yd
+    # Other head sizes at the same 168 MB of state: N = 128 (B = 64) and N = 32 (B = 1024).
+    for Nn, Bn in ((128, 64), (32, 1024)):
+        st = 0.1 * torch.randn(Bn, Hd, Nn, Nn, device=dev)
+        one = _dev_inputs(torch, (8, Bn, Hd, Nn), dev, 6)
+        yd = torch.empty(Bn, Hd, Nn, device=dev, dtype=torch.bfloat16)
+
+        def run_n():
+            for t in range(8):
+                wk.decode_step(*(x[t] for x in one), st, out=yd)
+
+        per_step = _time(torch, run_n, 5) / 8
+        nbytes = Bn * Hd * (2 * Nn * Nn * 4 + 7 * Nn * 2)
+        res[f"decode_n{Nn}"] = {"workload": f"B={Bn} H=40 N={Nn}, in-place steps, fp32 state, bf16 inputs",
+                                "us_per_step": round(per_step * 1e3, 2),
+                                "tokens_per_s": round(Bn / per_step * 1e3, 1),
+                                "alg_GBs": round(nbytes / per_step / 1e6, 1)}
+        del st, one, yd
+    # The sequential scan at N = 128 and N = 32 on the 0.19B-model token shape.
+    for Nn in (128, 32):
+        ins = _dev_inputs(torch, (4, 1024, 12, Nn), dev, 7)
+        y = torch.empty_like(ins[0])
+        ms = _time(torch, lambda: wk.forward(*ins, None, chunk_len=0, want_state=False, out=y), 10)
+        res[f"sequential_fwd_n{Nn}"] = {"workload": f"B=4 T=1024 H=12 N={Nn} bf16, zero s0, chunk_len=0",
+                                        "ms": round(ms, 4), "tokens_per_s": round(4 * 1024 / ms * 1e3, 1)}
+        del ins, y
     return res
 
 

@@ -36,7 +36,8 @@
  *   - Validation is synchronous and launches nothing on error:
  *       WKV7_ERR_INVALID_ARG  negative sizes, NULL required pointers, pointers
  *                             not 16-byte aligned, NULL desc;
- *       WKV7_ERR_UNSUPPORTED  N != 64, unknown dtype, unsupported chunk_len;
+ *       WKV7_ERR_UNSUPPORTED  unsupported head size (below), unknown dtype,
+ *                             unsupported chunk_len;
  *       WKV7_ERR_WORKSPACE    workspace smaller than wkv7_workspace_bytes();
  *       WKV7_ERR_LAUNCH       the HIP runtime reported a launch error.
  *     No exception crosses the ABI.  There is no global mutable state, so
@@ -64,7 +65,12 @@ extern "C" {
 #endif
 
 #define WKV7_ABI_VERSION 1
-#define WKV7_HEAD_SIZE 64        /* the only supported N */
+/* Head sizes: the sequential scan (chunk_len = 0) and the decode step take
+   N = 32, 64 or 128 (a larger N is the state expansion of "Millions of States:
+   Designing a Scalable MoE Architecture with RWKV-7 Meta-learner", Abstract);
+   the chunked form, wkv7_forward_split with segments and every backward entry
+   point take N = WKV7_HEAD_SIZE only. */
+#define WKV7_HEAD_SIZE 64
 #define WKV7_TAPE_CHUNK 16       /* tokens per chunk of the backward */
 #define WKV7_TAPE_BLOCK 32       /* tokens per state saved in the forward tape */
 
@@ -106,9 +112,10 @@ size_t wkv7_tape_bytes(const wkv7_desc *desc);
 /* Bytes of device scratch wkv7_backward needs: with_tape != 0 when the caller
    passes a tape written by wkv7_forward (the backward then keeps one per-token
    intermediate adjoint and the adjoint of the state leaving every 32-token block
-   there, as much again as the tape, plus 256 bytes of work queues), with_tape = 0 when it passes none (then a forward re-run also
-   writes its tape into the workspace: twice the tape).  0 on an invalid
-   descriptor. */
+   there, as much again as the tape, plus 256 bytes of work queues), with_tape =
+   0 when it passes none (then a forward re-run also writes its tape into the
+   workspace: twice the tape).  0 on an invalid descriptor or one the backward
+   does not take (N != WKV7_HEAD_SIZE). */
 size_t wkv7_workspace_bytes(const wkv7_desc *desc, int with_tape);
 
 /*

@@ -21,7 +21,9 @@ bool pair(const void* a, const void* b) { return (a == nullptr && b == nullptr) 
 int check_desc(const wkv7_desc* d) {
     if (!d) return WKV7_ERR_INVALID_ARG;
     if (d->B < 0 || d->T < 0 || d->H < 0 || d->N < 0) return WKV7_ERR_INVALID_ARG;
-    if (d->N != WKV7_HEAD_SIZE) return WKV7_ERR_UNSUPPORTED;
+    if (d->N != 32 && d->N != 64 && d->N != 128) return WKV7_ERR_UNSUPPORTED;
+    // The chunked form (and the backward, which is chunked) runs N = 64 only.
+    if (d->chunk_len != 0 && d->N != WKV7_HEAD_SIZE) return WKV7_ERR_UNSUPPORTED;
     if (d->dtype != WKV7_F32 && d->dtype != WKV7_BF16) return WKV7_ERR_UNSUPPORTED;
     if (d->chunk_len != 0 && d->chunk_len != 16) return WKV7_ERR_UNSUPPORTED;
     // The chunked form runs its products on bf16 matrix cores.
@@ -134,10 +136,10 @@ int run_forward(const wkv7_desc* d, const void* r, const void* w, const void* k,
                 void* tape, hipStream_t stream) {
     if ((int64_t)d->B * d->H == 0) return WKV7_OK;
     if (d->T == 0) {
-        if (sT) return from_hip(wkv7::launch_state_copy(d->B * d->H, s0, sT, stream));
+        if (sT) return from_hip(wkv7::launch_state_copy(d->B * d->H, d->N, s0, sT, stream));
         return WKV7_OK;
     }
-    wkv7::FwdArgs p{d->B, d->T, d->H, d->dtype == WKV7_BF16, r, w, k, v, a, b, s0, y, sT, tape};
+    wkv7::FwdArgs p{d->B, d->T, d->H, d->N, d->dtype == WKV7_BF16, r, w, k, v, a, b, s0, y, sT, tape};
     if (d->chunk_len == 0) return from_hip(wkv7::launch_seq_fwd(p, stream));
     return from_hip(wkv7::launch_chunk_fwd(p, d->chunk_len, stream));
 }
@@ -165,7 +167,7 @@ size_t wkv7_tape_bytes(const wkv7_desc* desc) {
 }
 
 size_t wkv7_workspace_bytes(const wkv7_desc* desc, int with_tape) {
-    if (check_desc(desc) != WKV7_OK) return 0;
+    if (check_desc(desc) != WKV7_OK || desc->N != WKV7_HEAD_SIZE) return 0;
     return tape_bytes_unchecked(desc) * (with_tape ? 1 : 2) + kQueueBytes;
 }
 
@@ -203,7 +205,7 @@ int wkv7_forward_split(const wkv7_desc* desc, const void* r, const void* w, cons
     if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return WKV7_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (need == 0) return run_forward(desc, r, w, k, v, a, b, s0, y, sT, tape, s);
-    const wkv7::FwdArgs p{desc->B, desc->T, desc->H, true, r, w, k, v, a, b, s0, y, sT, tape};
+    const wkv7::FwdArgs p{desc->B, desc->T, desc->H, desc->N, true, r, w, k, v, a, b, s0, y, sT, tape};
     if (plan.mode == 1) {
         float* states = static_cast<float*>(workspace);
         int* sync = reinterpret_cast<int*>(states + (size_t)desc->B * desc->H * desc->N * desc->N);
@@ -256,7 +258,7 @@ int run_backward(const wkv7_desc* desc, const void* r, const void* w, const void
     int st = check_desc(desc);
     if (st != WKV7_OK) return st;
     // The backward runs the chunked adjoint on bf16 matrix cores.
-    if (desc->dtype != WKV7_BF16) return WKV7_ERR_UNSUPPORTED;
+    if (desc->dtype != WKV7_BF16 || desc->N != WKV7_HEAD_SIZE) return WKV7_ERR_UNSUPPORTED;
     if ((int64_t)desc->B * desc->H * ((desc->T + WKV7_TAPE_CHUNK - 1) / WKV7_TAPE_CHUNK) > INT32_MAX)
         return WKV7_ERR_UNSUPPORTED;
     const bool has_tokens = (int64_t)desc->B * desc->T * desc->H > 0;
@@ -279,7 +281,7 @@ int run_backward(const wkv7_desc* desc, const void* r, const void* w, const void
     if (desc->T == 0) {
         // L = <dsT, S_T> with S_T = s0: ds0 = dsT.
         if (ds0 && (stages & wkv7::BWD_CHAIN))
-            return from_hip(wkv7::launch_state_copy(desc->B * desc->H, dsT, ds0, s));
+            return from_hip(wkv7::launch_state_copy(desc->B * desc->H, desc->N, dsT, ds0, s));
         return WKV7_OK;
     }
     char* ws = static_cast<char*>(workspace);
@@ -372,13 +374,13 @@ int wkv7_decode_step(int32_t B, int32_t H, int32_t N, int32_t dtype, const void*
                      const void* w, const void* k, const void* v, const void* a, const void* b,
                      float* state, void* y, void* stream) {
     if (B < 0 || H < 0 || N < 0) return WKV7_ERR_INVALID_ARG;
-    if (N != WKV7_HEAD_SIZE) return WKV7_ERR_UNSUPPORTED;
+    if (N != 32 && N != 64 && N != 128) return WKV7_ERR_UNSUPPORTED;
     if (dtype != WKV7_F32 && dtype != WKV7_BF16) return WKV7_ERR_UNSUPPORTED;
     if ((int64_t)B * H > (int64_t)(1 << 28)) return WKV7_ERR_UNSUPPORTED;
     if ((int64_t)B * H == 0) return WKV7_OK;
     if (!(req(r) && req(w) && req(k) && req(v) && pair(a, b) && req(state) && req(y)))
         return WKV7_ERR_INVALID_ARG;
-    wkv7::DecodeArgs p{B, H, dtype == WKV7_BF16, r, w, k, v, a, b, state, y};
+    wkv7::DecodeArgs p{B, H, N, dtype == WKV7_BF16, r, w, k, v, a, b, state, y};
     return from_hip(wkv7::launch_decode(p, static_cast<hipStream_t>(stream)));
 }
 

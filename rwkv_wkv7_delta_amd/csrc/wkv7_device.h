@@ -20,6 +20,9 @@ template <> struct Elem<float> {
     static __device__ __forceinline__ float4 load4(const float* p) {
         return *reinterpret_cast<const float4*>(p);
     }
+    static __device__ __forceinline__ float2 load2(const float* p) {
+        return *reinterpret_cast<const float2*>(p);
+    }
     static __device__ __forceinline__ float load1(const float* p) { return *p; }
     static __device__ __forceinline__ void store1(float* p, float x) { *p = x; }
     static __device__ __forceinline__ void store4(float* p, float4 x) {
@@ -45,6 +48,10 @@ template <> struct Elem<bf16_t> {
         const uint2 u = *reinterpret_cast<const uint2*>(p);
         return make_float4(bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y));
     }
+    static __device__ __forceinline__ float2 load2(const bf16_t* p) {
+        const uint32_t u = *reinterpret_cast<const uint32_t*>(p);
+        return make_float2(bf16_lo(u), bf16_hi(u));
+    }
     static __device__ __forceinline__ float load1(const bf16_t* p) {
         return __uint_as_float((uint32_t)(*p) << 16);
     }
@@ -56,6 +63,40 @@ template <> struct Elem<bf16_t> {
         *reinterpret_cast<uint2*>(p) = u;
     }
 };
+
+// C consecutive elements (C = 2, 4 or 8) as fp32, and the fp32 store of C values.
+template <int C, typename T>
+__device__ __forceinline__ void load_cols(const T* p, float (&x)[C]) {
+    static_assert(C == 2 || C % 4 == 0, "2, 4 or 8 columns per lane");
+    if constexpr (C == 2) {
+        const float2 f = Elem<T>::load2(p);
+        x[0] = f.x; x[1] = f.y;
+    } else {
+#pragma unroll
+        for (int i = 0; i < C; i += 4) {
+            const float4 f = Elem<T>::load4(p + i);
+            x[i] = f.x; x[i + 1] = f.y; x[i + 2] = f.z; x[i + 3] = f.w;
+        }
+    }
+}
+template <int C>
+__device__ __forceinline__ void store_cols(float* p, const float (&x)[C]) {
+    if constexpr (C == 2) {
+        *reinterpret_cast<float2*>(p) = make_float2(x[0], x[1]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < C; i += 4)
+            *reinterpret_cast<float4*>(p + i) = make_float4(x[i], x[i + 1], x[i + 2], x[i + 3]);
+    }
+}
+// In-lane part of a dot product, accumulated in column order.
+template <int C>
+__device__ __forceinline__ float dot_cols(const float (&s)[C], const float (&q)[C]) {
+    float acc = s[0] * q[0];
+#pragma unroll
+    for (int i = 1; i < C; ++i) acc = fmaf(s[i], q[i], acc);
+    return acc;
+}
 
 // ---------------------------------------------------------------------------
 // Sum over the 16 lanes of a DPP row; every lane of the row gets the total.

@@ -7,7 +7,7 @@
 namespace wkv7 {
 
 struct FwdArgs {
-    int B, T, H;
+    int B, T, H, N;   // N: 32, 64 or 128 for the sequential scan; 64 for the chunked form
     bool bf16;
     const void *r, *w, *k, *v, *a, *b;
     const float* s0;  // may be null
@@ -33,7 +33,7 @@ struct BwdArgs {
 };
 
 struct DecodeArgs {
-    int B, H;
+    int B, H, N;      // N: 32, 64 or 128
     bool bf16;
     const void *r, *w, *k, *v, *a, *b;
     float* state;
@@ -65,6 +65,6 @@ hipError_t launch_chunk_fwd_sequential(const FwdArgs& p, int chunk_len, int nseg
 enum { BWD_CHAIN = 1, BWD_KEYS = 2 };
 hipError_t launch_bwd(const BwdArgs& p, int chunk_len, int stages, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& p, hipStream_t stream);
-hipError_t launch_state_copy(int BH, const float* s0, float* sT, hipStream_t stream);
+hipError_t launch_state_copy(int BH, int N, const float* s0, float* sT, hipStream_t stream);
 
 }  // namespace wkv7

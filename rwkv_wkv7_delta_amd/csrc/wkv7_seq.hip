@@ -1,20 +1,23 @@
-// wkv7_seq.hip -- sequential WKV7 scan and single-token decode step (gfx950).
+// wkv7_seq.hip -- sequential WKV7 scan and single-token decode step (gfx950),
+// for head sizes N = 32, 64 and 128.
 //
 // Per (batch b, head h) the N x N fp32 state evolves token by token as
 //   z = S a_t;  S[i][j] = S[i][j] w_t[j] + z[i] b_t[j] + v_t[i] k_t[j];  y_t = S r_t
 // (generalised delta rule with a diagonal-plus-rank-one transition and a
 // read-out after the update: "Paper Review: RWKV-7 Goose", Architecture and
-// The approach).
+// The approach).  The head size is a template parameter: the state expansion
+// of "Millions of States: Designing a Scalable MoE Architecture with RWKV-7
+// Meta-learner" (Abstract) grows it.
 //
 // Lane ownership: right-multiplication acts on each state row separately and
 // row i only uses the scalar v_t[i], so value rows evolve independently.  A
-// wave holds 4 rows; 16 lanes share one row, each owning 4 consecutive key
-// columns as a float4 in VGPRs.  Row dot products (S a, S r) are a 4-term
-// in-lane FMA chain followed by a 16-lane DPP butterfly.  A workgroup of
-// WAVES waves owns 4*WAVES rows of one head; token vectors r,w,k,a,b (and the
-// workgroup's slice of v) are loaded coalesced, converted to fp32 and staged
-// through LDS 16 tokens at a time, with the next block prefetched into
-// registers while the current one is consumed.
+// wave holds 4 rows; 16 lanes share one row, each owning C = N/16 consecutive
+// key columns in VGPRs.  Row dot products (S a, S r) are a C-term in-lane FMA
+// chain followed by a 16-lane DPP butterfly.  A workgroup of WAVES waves owns
+// 4*WAVES rows of one head; token vectors r,w,k,a,b (and the workgroup's
+// slice of v) are loaded coalesced, converted to fp32 and staged through LDS
+// 16 tokens at a time, with the next block prefetched into registers while the
+// current one is consumed.
 
 #include "wkv7_device.h"
 #include "wkv7_internal.h"
@@ -26,21 +29,30 @@ namespace {
 constexpr int kTB = 16;  // tokens per LDS stage
 static_assert(kTB == 16, "the tape's removal read-outs and states follow 16-token chunks");
 
+// Token tensor offset for [B][T][H][N].
+template <int N>
+__device__ __forceinline__ size_t tok_off_n(int b, int t, int h, int T, int H) {
+    return (((size_t)b * T + t) * H + h) * N;
+}
+
 // kAB = false: a = b = 0 (decay-only recurrence S <- S diag(w) + v k^T); a and
 // b are not read, z is not formed and the tape's Z part is not written.
-template <typename Tin, int WAVES, bool kAB>
+template <typename Tin, int N, int WAVES, bool kAB>
 __global__ __launch_bounds__(64 * WAVES) void seq_fwd_kernel(
     int T, int H, const Tin* __restrict__ r, const Tin* __restrict__ w,
     const Tin* __restrict__ k, const Tin* __restrict__ v, const Tin* __restrict__ a,
     const Tin* __restrict__ b, const float* __restrict__ s0, Tin* __restrict__ y,
     float* __restrict__ sT, bf16_t* __restrict__ tape) {
+    constexpr int C = N / 16;        // key columns per lane
     constexpr int R = 4 * WAVES;     // state rows per workgroup
-    constexpr int NRB = kN / R;      // workgroups per head
+    constexpr int NRB = N / R;       // workgroups per head
     constexpr int NT = 64 * WAVES;   // threads
-    constexpr int CH = kTB * 16;     // float4 chunks per token vector per stage
+    constexpr int G4 = N / 4;        // 4-element groups per token vector
+    constexpr int CH = kTB * G4;     // ... per stage
     constexpr int PER = (CH + NT - 1) / NT;
+    static_assert(NRB >= 1 && NRB * R == N, "rows per workgroup must divide N");
 
-    __shared__ float4 sm[5][kTB][16];   // r, w, k, a, b as fp32
+    __shared__ __align__(16) float sm[5][kTB][N];   // r, w, k, a, b as fp32
     __shared__ float sv[kTB][R];        // this workgroup's v slice
     __shared__ float sy[kTB][R];        // read-outs before the coalesced store
     __shared__ float sz[kTB][R];        // removal read-outs z = S a, for the tape
@@ -52,16 +64,22 @@ __global__ __launch_bounds__(64 * WAVES) void seq_fwd_kernel(
     const int lane = tid & 63, wave = tid >> 6;
     const int rloc = wave * 4 + (lane >> 4);
     const int row = rb * R + rloc;
-    const int cq = lane & 15;           // float4 column index
+    const int cq = lane & 15;           // this lane's columns: C * cq .. C * cq + C - 1
     const Tin* src[5] = {r, w, k, a, b};
 
-    const size_t soff = ((size_t)bh * kN + row) * kN + cq * 4;
-    float4 S = s0 ? *reinterpret_cast<const float4*>(s0 + soff) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const size_t soff = ((size_t)bh * N + row) * N + cq * C;
+    float S[C];
+    if (s0) {
+        load_cols<C>(s0 + soff, S);
+    } else {
+#pragma unroll
+        for (int c = 0; c < C; ++c) S[c] = 0.f;
+    }
     // Tape for the backward: z as [B][T][H][N] bf16, then the state entering every
     // 32-token block as [B][H][nblk][N (key)][N (value)] bf16.
     const int nblk = (T + 31) / 32;
     bf16_t* const tapeZ = tape;
-    bf16_t* const tapeS = tape ? tape + (size_t)(gridDim.x / NRB) / H * T * H * kN : nullptr;
+    bf16_t* const tapeS = tape ? tape + (size_t)(gridDim.x / NRB) / H * T * H * N : nullptr;
 
     float4 pre[5][PER];
     float4 prev = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -72,14 +90,14 @@ __global__ __launch_bounds__(64 * WAVES) void seq_fwd_kernel(
 #pragma unroll
             for (int p = 0; p < PER; ++p) {
                 const int idx = tid + p * NT;
-                const int t = idx / 16, c = idx % 16;
+                const int t = idx / G4, c = idx % G4;
                 if (idx < CH && t0 + t < T)
-                    pre[q][p] = Elem<Tin>::load4(src[q] + tok_off(bb, t0 + t, hh, T, H) + c * 4);
+                    pre[q][p] = Elem<Tin>::load4(src[q] + tok_off_n<N>(bb, t0 + t, hh, T, H) + c * 4);
             }
         if (tid < kTB * (R / 4)) {
             const int t = tid / (R / 4), c = tid % (R / 4);
             if (t0 + t < T)
-                prev = Elem<Tin>::load4(v + tok_off(bb, t0 + t, hh, T, H) + rb * R + c * 4);
+                prev = Elem<Tin>::load4(v + tok_off_n<N>(bb, t0 + t, hh, T, H) + rb * R + c * 4);
         }
     };
     auto store_lds = [&]() {
@@ -88,7 +106,7 @@ __global__ __launch_bounds__(64 * WAVES) void seq_fwd_kernel(
 #pragma unroll
             for (int p = 0; p < PER; ++p) {
                 const int idx = tid + p * NT;
-                if (idx < CH) sm[q][idx / 16][idx % 16] = pre[q][p];
+                if (idx < CH) *reinterpret_cast<float4*>(&sm[q][idx / G4][(idx % G4) * 4]) = pre[q][p];
             }
         if (tid < kTB * (R / 4)) {
             const int t = tid / (R / 4), c = tid % (R / 4);
@@ -105,91 +123,96 @@ __global__ __launch_bounds__(64 * WAVES) void seq_fwd_kernel(
         const int nt = min(kTB, T - t0);
         if (t0 + kTB < T) load_regs(t0 + kTB);
         if (tape && t0 % 32 == 0) {   // entry state of block t0 / 32
-            bf16_t* dst = tapeS + ((size_t)bh * nblk + t0 / 32) * kN * kN + row;
-            dst[(cq * 4 + 0) * kN] = f2bf(S.x);
-            dst[(cq * 4 + 1) * kN] = f2bf(S.y);
-            dst[(cq * 4 + 2) * kN] = f2bf(S.z);
-            dst[(cq * 4 + 3) * kN] = f2bf(S.w);
+            bf16_t* dst = tapeS + ((size_t)bh * nblk + t0 / 32) * N * N + row;
+#pragma unroll
+            for (int c = 0; c < C; ++c) dst[(cq * C + c) * N] = f2bf(S[c]);
         }
         for (int t = 0; t < nt; ++t) {
-            const float4 W = sm[1][t][cq], K = sm[2][t][cq], Rr = sm[0][t][cq];
+            float W[C], K[C], Rr[C];
+            load_cols<C>(&sm[1][t][cq * C], W);
+            load_cols<C>(&sm[2][t][cq * C], K);
+            load_cols<C>(&sm[0][t][cq * C], Rr);
             const float vi = sv[t][rloc];
             if (kAB) {
-                const float4 A = sm[3][t][cq], Bv = sm[4][t][cq];
-                const float z = row16_sum(dot4(S, A));
+                float A[C], Bv[C];
+                load_cols<C>(&sm[3][t][cq * C], A);
+                load_cols<C>(&sm[4][t][cq * C], Bv);
+                const float z = row16_sum(dot_cols(S, A));
                 if (cq == 0) sz[t][rloc] = z;
-                S.x = fmaf(vi, K.x, fmaf(z, Bv.x, S.x * W.x));
-                S.y = fmaf(vi, K.y, fmaf(z, Bv.y, S.y * W.y));
-                S.z = fmaf(vi, K.z, fmaf(z, Bv.z, S.z * W.z));
-                S.w = fmaf(vi, K.w, fmaf(z, Bv.w, S.w * W.w));
+#pragma unroll
+                for (int c = 0; c < C; ++c) S[c] = fmaf(vi, K[c], fmaf(z, Bv[c], S[c] * W[c]));
             } else {
-                S.x = fmaf(vi, K.x, S.x * W.x);
-                S.y = fmaf(vi, K.y, S.y * W.y);
-                S.z = fmaf(vi, K.z, S.z * W.z);
-                S.w = fmaf(vi, K.w, S.w * W.w);
+#pragma unroll
+                for (int c = 0; c < C; ++c) S[c] = fmaf(vi, K[c], S[c] * W[c]);
             }
-            const float yy = row16_sum(dot4(S, Rr));
+            const float yy = row16_sum(dot_cols(S, Rr));
             if (cq == 0) sy[t][rloc] = yy;
         }
         __syncthreads();
         for (int idx = tid; y && idx < nt * R; idx += NT) {
             const int t = idx / R, i = idx % R;
-            Elem<Tin>::store1(y + tok_off(bb, t0 + t, hh, T, H) + rb * R + i, sy[t][i]);
+            Elem<Tin>::store1(y + tok_off_n<N>(bb, t0 + t, hh, T, H) + rb * R + i, sy[t][i]);
         }
         for (int idx = tid; kAB && tape && idx < nt * R; idx += NT) {
             const int t = idx / R, i = idx % R;
-            tapeZ[tok_off(bb, t0 + t, hh, T, H) + rb * R + i] = f2bf(sz[t][i]);
+            tapeZ[tok_off_n<N>(bb, t0 + t, hh, T, H) + rb * R + i] = f2bf(sz[t][i]);
         }
         if (t0 + kTB < T) store_lds();
         __syncthreads();
     }
-    if (sT) *reinterpret_cast<float4*>(sT + soff) = S;
+    if (sT) store_cols<C>(sT + soff, S);
 }
 
 // One token on resident states.  One workgroup of 4 waves per (b, h); each
-// wave updates 16 rows as 4 groups of 4 rows, every lane 4 consecutive
-// columns, so each state row is one contiguous 256-byte segment per 16 lanes.
-template <typename Tin, bool kAB>
+// wave updates N/4 rows as groups of 4 rows, every lane C = N/16 consecutive
+// columns, so each state row is one contiguous segment per 16 lanes.
+template <typename Tin, int N, bool kAB>
 __global__ __launch_bounds__(256) void decode_kernel(
     const Tin* __restrict__ r, const Tin* __restrict__ w, const Tin* __restrict__ k,
     const Tin* __restrict__ v, const Tin* __restrict__ a, const Tin* __restrict__ b,
     float* __restrict__ state, Tin* __restrict__ y) {
+    constexpr int C = N / 16;   // columns per lane
+    constexpr int G = N / 16;   // groups of 4 rows per wave
     const int bh = blockIdx.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int cq = lane & 15;
-    const size_t io = (size_t)bh * kN;
-    float* st = state + (size_t)bh * kN * kN;
-    float4 S[4];
-    float vv[4];
+    const size_t io = (size_t)bh * N;
+    float* st = state + (size_t)bh * N * N;
+    float S[G][C];
+    float vv[G];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        const int row = wave * 16 + g * 4 + (lane >> 4);
-        S[g] = *reinterpret_cast<const float4*>(st + row * kN + cq * 4);
+    for (int g = 0; g < G; ++g) {
+        const int row = wave * (N / 4) + g * 4 + (lane >> 4);
+        load_cols<C>(st + row * N + cq * C, S[g]);
         vv[g] = Elem<Tin>::load1(v + io + row);
     }
     // a = b = 0 (kAB false): nothing to load, z = 0.
-    const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
-    const float4 A = kAB ? Elem<Tin>::load4(a + io + cq * 4) : zero;
-    const float4 Bv = kAB ? Elem<Tin>::load4(b + io + cq * 4) : zero;
-    const float4 W = Elem<Tin>::load4(w + io + cq * 4);
-    const float4 K = Elem<Tin>::load4(k + io + cq * 4);
-    const float4 Rr = Elem<Tin>::load4(r + io + cq * 4);
+    float A[C], Bv[C], W[C], K[C], Rr[C];
+    if (kAB) {
+        load_cols<C>(a + io + cq * C, A);
+        load_cols<C>(b + io + cq * C, Bv);
+    }
+    load_cols<C>(w + io + cq * C, W);
+    load_cols<C>(k + io + cq * C, K);
+    load_cols<C>(r + io + cq * C, Rr);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        const int row = wave * 16 + g * 4 + (lane >> 4);
-        float4 s = S[g];
-        const float z = kAB ? row16_sum(dot4(s, A)) : 0.f;
-        s.x = fmaf(vv[g], K.x, fmaf(z, Bv.x, s.x * W.x));
-        s.y = fmaf(vv[g], K.y, fmaf(z, Bv.y, s.y * W.y));
-        s.z = fmaf(vv[g], K.z, fmaf(z, Bv.z, s.z * W.z));
-        s.w = fmaf(vv[g], K.w, fmaf(z, Bv.w, s.w * W.w));
-        const float yy = row16_sum(dot4(s, Rr));
+    for (int g = 0; g < G; ++g) {
+        const int row = wave * (N / 4) + g * 4 + (lane >> 4);
+        if (kAB) {
+            const float z = row16_sum(dot_cols(S[g], A));
+#pragma unroll
+            for (int c = 0; c < C; ++c) S[g][c] = fmaf(vv[g], K[c], fmaf(z, Bv[c], S[g][c] * W[c]));
+        } else {
+#pragma unroll
+            for (int c = 0; c < C; ++c) S[g][c] = fmaf(vv[g], K[c], S[g][c] * W[c]);
+        }
+        const float yy = row16_sum(dot_cols(S[g], Rr));
         if (cq == 0) Elem<Tin>::store1(y + io + row, yy);
-        *reinterpret_cast<float4*>(st + row * kN + cq * 4) = s;
+        store_cols<C>(st + row * N + cq * C, S[g]);
     }
 }
 
-// Copies (or zero-fills, when src is null) B*H fp32 states of N x N.
+// Copies (or zero-fills, when src is null) n4 float4 values.
 __global__ __launch_bounds__(256) void state_copy_kernel(size_t n4, const float* __restrict__ src,
                                                          float* __restrict__ dst) {
     const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
@@ -198,32 +221,40 @@ __global__ __launch_bounds__(256) void state_copy_kernel(size_t n4, const float*
             src ? reinterpret_cast<const float4*>(src)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
-template <typename Tin>
-hipError_t launch_seq_fwd_t(const FwdArgs& p, hipStream_t stream) {
-    const int BH = p.B * p.H;
-    const Tin* r = static_cast<const Tin*>(p.r);
-    const Tin* w = static_cast<const Tin*>(p.w);
-    const Tin* k = static_cast<const Tin*>(p.k);
-    const Tin* v = static_cast<const Tin*>(p.v);
+template <typename Tin, int N, int WAVES>
+hipError_t launch_seq_fwd_w(const FwdArgs& p, int blocks_per_head, hipStream_t stream) {
     const Tin* a = static_cast<const Tin*>(p.a);
-    const Tin* b = static_cast<const Tin*>(p.b);
-    Tin* y = static_cast<Tin*>(p.y);
-    // Few heads: split each head's rows over 4 workgroups to occupy more CUs.
-    if (BH < 512) {
-        auto kern = a ? seq_fwd_kernel<Tin, 4, true> : seq_fwd_kernel<Tin, 4, false>;
-        kern<<<dim3(BH * 4), dim3(256), 0, stream>>>(
-            p.T, p.H, r, w, k, v, a, b, p.s0, y, p.sT, static_cast<bf16_t*>(p.tape));
-    } else {
-        auto kern = a ? seq_fwd_kernel<Tin, 16, true> : seq_fwd_kernel<Tin, 16, false>;
-        kern<<<dim3(BH), dim3(1024), 0, stream>>>(
-            p.T, p.H, r, w, k, v, a, b, p.s0, y, p.sT, static_cast<bf16_t*>(p.tape));
-    }
+    auto kern = a ? seq_fwd_kernel<Tin, N, WAVES, true> : seq_fwd_kernel<Tin, N, WAVES, false>;
+    kern<<<dim3(p.B * p.H * blocks_per_head), dim3(64 * WAVES), 0, stream>>>(
+        p.T, p.H, static_cast<const Tin*>(p.r), static_cast<const Tin*>(p.w),
+        static_cast<const Tin*>(p.k), static_cast<const Tin*>(p.v), a,
+        static_cast<const Tin*>(p.b), p.s0, static_cast<Tin*>(p.y), p.sT,
+        static_cast<bf16_t*>(p.tape));
     return hipGetLastError();
 }
 
+template <typename Tin, int N>
+hipError_t launch_seq_fwd_n(const FwdArgs& p, hipStream_t stream) {
+    // Few heads: split each head's rows over workgroups of 4 waves (16 rows)
+    // to occupy more compute units; many heads: at most 16 waves per workgroup.
+    constexpr int WMANY = N / 4 < 16 ? N / 4 : 16;
+    if (p.B * p.H < 512) return launch_seq_fwd_w<Tin, N, 4>(p, N / 16, stream);
+    return launch_seq_fwd_w<Tin, N, WMANY>(p, N / (4 * WMANY), stream);
+}
+
 template <typename Tin>
-hipError_t launch_decode_t(const DecodeArgs& p, hipStream_t stream) {
-    auto kern = p.a ? decode_kernel<Tin, true> : decode_kernel<Tin, false>;
+hipError_t launch_seq_fwd_t(const FwdArgs& p, hipStream_t stream) {
+    switch (p.N) {
+        case 32: return launch_seq_fwd_n<Tin, 32>(p, stream);
+        case 64: return launch_seq_fwd_n<Tin, 64>(p, stream);
+        case 128: return launch_seq_fwd_n<Tin, 128>(p, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename Tin, int N>
+hipError_t launch_decode_n(const DecodeArgs& p, hipStream_t stream) {
+    auto kern = p.a ? decode_kernel<Tin, N, true> : decode_kernel<Tin, N, false>;
     kern<<<dim3(p.B * p.H), dim3(256), 0, stream>>>(
         static_cast<const Tin*>(p.r), static_cast<const Tin*>(p.w),
         static_cast<const Tin*>(p.k), static_cast<const Tin*>(p.v),
@@ -232,14 +263,24 @@ hipError_t launch_decode_t(const DecodeArgs& p, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <typename Tin>
+hipError_t launch_decode_t(const DecodeArgs& p, hipStream_t stream) {
+    switch (p.N) {
+        case 32: return launch_decode_n<Tin, 32>(p, stream);
+        case 64: return launch_decode_n<Tin, 64>(p, stream);
+        case 128: return launch_decode_n<Tin, 128>(p, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_seq_fwd(const FwdArgs& p, hipStream_t stream) {
     return p.bf16 ? launch_seq_fwd_t<bf16_t>(p, stream) : launch_seq_fwd_t<float>(p, stream);
 }
 
-hipError_t launch_state_copy(int BH, const float* s0, float* sT, hipStream_t stream) {
-    const size_t n4 = (size_t)BH * kN * kN / 4;
+hipError_t launch_state_copy(int BH, int N, const float* s0, float* sT, hipStream_t stream) {
+    const size_t n4 = (size_t)BH * N * N / 4;
     state_copy_kernel<<<dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream>>>(n4, s0, sT);
     return hipGetLastError();
 }

@@ -52,7 +52,10 @@ def test_tape_and_workspace_sizes(L):
     d = wk.make_desc(1, 65, 2, 64, wk.WKV7_F32, 0)   # 3 blocks of 32 tokens, the last ragged
     assert wk.tape_bytes(d) == 65 * 2 * 64 * 2 + 2 * 3 * 64 * 64 * 2
     assert wk.tape_bytes(wk.make_desc(3, 0, 2, 64, wk.WKV7_BF16, 16)) == 0
-    assert wk.tape_bytes(wk.make_desc(1, 64, 1, 32, wk.WKV7_F32, 0)) == 0   # invalid N
+    assert wk.tape_bytes(wk.make_desc(1, 64, 1, 48, wk.WKV7_F32, 0)) == 0   # invalid N
+    # N = 32: the scan writes a tape of the same layout; the backward (N = 64
+    # only) has no workspace size.
+    assert wk.tape_bytes(wk.make_desc(1, 64, 1, 32, wk.WKV7_F32, 0)) == 64 * 32 * 2 + 2 * 32 * 32 * 2
     assert wk.workspace_bytes(wk.make_desc(1, 64, 1, 32, wk.WKV7_F32, 0), True) == 0
 
 
@@ -66,7 +69,12 @@ def _fwd(L, d, ptrs=None, y=FAKE):
 
 def test_forward_validation(L):
     assert L.wkv7_forward(None, *[FAKE] * 6, None, FAKE, None, None, None) == wk.WKV7_ERR_INVALID_ARG
-    assert _fwd(L, wk.make_desc(1, 8, 1, 32, wk.WKV7_BF16, 0)) == wk.WKV7_ERR_UNSUPPORTED
+    assert _fwd(L, wk.make_desc(1, 8, 1, 48, wk.WKV7_BF16, 0)) == wk.WKV7_ERR_UNSUPPORTED
+    # N = 32 and 128: the sequential scan only (the chunked form runs N = 64).
+    assert _fwd(L, wk.make_desc(1, 8, 1, 32, wk.WKV7_BF16, 16)) == wk.WKV7_ERR_UNSUPPORTED
+    assert _fwd(L, wk.make_desc(1, 8, 1, 128, wk.WKV7_BF16, 16)) == wk.WKV7_ERR_UNSUPPORTED
+    assert _fwd(L, wk.make_desc(1, 8, 1, 128, wk.WKV7_BF16, 0), y=None) == wk.WKV7_ERR_INVALID_ARG
+    assert _fwd(L, wk.make_desc(0, 8, 1, 32, wk.WKV7_BF16, 0)) == wk.WKV7_OK
     assert _fwd(L, wk.make_desc(-1, 8, 1, 64, wk.WKV7_BF16, 0)) == wk.WKV7_ERR_INVALID_ARG
     assert _fwd(L, wk.make_desc(1, 8, 1, 64, 7, 0)) == wk.WKV7_ERR_UNSUPPORTED
     assert _fwd(L, wk.make_desc(1, 8, 1, 64, wk.WKV7_BF16, 8)) == wk.WKV7_ERR_UNSUPPORTED
@@ -140,6 +148,11 @@ def test_backward_validation(L):
     d32 = wk.make_desc(1, 8, 1, 64, wk.WKV7_F32, 0)
     assert L.wkv7_backward(ctypes.byref(d32), *args, FAKE, *grads, None, None, 0, None) == \
         wk.WKV7_ERR_UNSUPPORTED
+    # The backward is chunked: N = 64 only.
+    for n in (32, 128):
+        dn = wk.make_desc(1, 8, 1, n, wk.WKV7_BF16, 0)
+        assert L.wkv7_backward(ctypes.byref(dn), *args, FAKE, *grads, None, FAKE, 1 << 30, None) == \
+            wk.WKV7_ERR_UNSUPPORTED
     d0 = wk.make_desc(0, 8, 1, 64, wk.WKV7_BF16, 16)
     assert L.wkv7_backward(ctypes.byref(d0), *args, FAKE, *grads, None, None, 0, None) == wk.WKV7_OK
 
@@ -183,7 +196,10 @@ def test_backward_overlapped_validation(L):
 
 def test_decode_validation(L):
     f = L.wkv7_decode_step
-    assert f(1, 1, 32, wk.WKV7_BF16, *[FAKE] * 8, None) == wk.WKV7_ERR_UNSUPPORTED
+    assert f(1, 1, 48, wk.WKV7_BF16, *[FAKE] * 8, None) == wk.WKV7_ERR_UNSUPPORTED
+    assert f(0, 1, 32, wk.WKV7_BF16, *[FAKE] * 8, None) == wk.WKV7_OK
+    assert f(0, 1, 128, wk.WKV7_F32, *[FAKE] * 8, None) == wk.WKV7_OK
+    assert f(1, 1, 128, wk.WKV7_BF16, *[FAKE] * 6, None, FAKE, None) == wk.WKV7_ERR_INVALID_ARG
     assert f(-1, 1, 64, wk.WKV7_BF16, *[FAKE] * 8, None) == wk.WKV7_ERR_INVALID_ARG
     assert f(1, 1, 64, 5, *[FAKE] * 8, None) == wk.WKV7_ERR_UNSUPPORTED
     assert f(1, 1, 64, wk.WKV7_BF16, *[FAKE] * 6, None, FAKE, None) == wk.WKV7_ERR_INVALID_ARG
