@@ -17,6 +17,13 @@ typedef uint16_t bf16_t;         // raw IEEE bfloat16 bits
 template <typename T> struct Elem;
 
 template <> struct Elem<float> {
+    // Four elements as loaded (raw4) and their fp32 values (cvt): a prefetch keeps
+    // raw4 so that nothing uses the loaded registers before they are stashed.
+    typedef float4 raw4;
+    static __device__ __forceinline__ raw4 load_raw4(const float* p) {
+        return *reinterpret_cast<const float4*>(p);
+    }
+    static __device__ __forceinline__ float4 cvt(raw4 x) { return x; }
     static __device__ __forceinline__ float4 load4(const float* p) {
         return *reinterpret_cast<const float4*>(p);
     }
@@ -44,6 +51,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 template <> struct Elem<bf16_t> {
+    typedef uint2 raw4;
+    static __device__ __forceinline__ raw4 load_raw4(const bf16_t* p) {
+        return *reinterpret_cast<const uint2*>(p);
+    }
+    static __device__ __forceinline__ float4 cvt(raw4 u) {
+        return make_float4(bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y));
+    }
     static __device__ __forceinline__ float4 load4(const bf16_t* p) {
         const uint2 u = *reinterpret_cast<const uint2*>(p);
         return make_float4(bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y));

@@ -71,6 +71,10 @@ __global__ __launch_bounds__(64 * WAVES) void seq_fwd_kernel(
     float S[C];
     if (s0) {
         load_cols<C>(s0 + soff, S);
+        // Settle the load here: left pending on the path that skips the first
+        // stage (T = 0), it would make the compiler wait for the whole memory
+        // counter -- every stage's own prefetch -- before each use of S.
+        __builtin_amdgcn_s_waitcnt(0);
     } else {
 #pragma unroll
         for (int c = 0; c < C; ++c) S[c] = 0.f;
@@ -81,8 +85,11 @@ __global__ __launch_bounds__(64 * WAVES) void seq_fwd_kernel(
     bf16_t* const tapeZ = tape;
     bf16_t* const tapeS = tape ? tape + (size_t)(gridDim.x / NRB) / H * T * H * N : nullptr;
 
-    float4 pre[5][PER];
-    float4 prev = make_float4(0.f, 0.f, 0.f, 0.f);
+    // Prefetched elements stay as loaded (bf16 words) until stashed: converting
+    // them at the load would make the stage wait for its own prefetch.
+    typedef typename Elem<Tin>::raw4 raw4;
+    raw4 pre[5][PER];
+    raw4 prev = {};
     constexpr int NQ = kAB ? 5 : 3;   // token vectors staged: r, w, k (, a, b)
     auto load_regs = [&](int t0) {
 #pragma unroll
@@ -92,12 +99,12 @@ __global__ __launch_bounds__(64 * WAVES) void seq_fwd_kernel(
                 const int idx = tid + p * NT;
                 const int t = idx / G4, c = idx % G4;
                 if (idx < CH && t0 + t < T)
-                    pre[q][p] = Elem<Tin>::load4(src[q] + tok_off_n<N>(bb, t0 + t, hh, T, H) + c * 4);
+                    pre[q][p] = Elem<Tin>::load_raw4(src[q] + tok_off_n<N>(bb, t0 + t, hh, T, H) + c * 4);
             }
         if (tid < kTB * (R / 4)) {
             const int t = tid / (R / 4), c = tid % (R / 4);
             if (t0 + t < T)
-                prev = Elem<Tin>::load4(v + tok_off_n<N>(bb, t0 + t, hh, T, H) + rb * R + c * 4);
+                prev = Elem<Tin>::load_raw4(v + tok_off_n<N>(bb, t0 + t, hh, T, H) + rb * R + c * 4);
         }
     };
     auto store_lds = [&]() {
@@ -106,11 +113,11 @@ __global__ __launch_bounds__(64 * WAVES) void seq_fwd_kernel(
 #pragma unroll
             for (int p = 0; p < PER; ++p) {
                 const int idx = tid + p * NT;
-                if (idx < CH) *reinterpret_cast<float4*>(&sm[q][idx / G4][(idx % G4) * 4]) = pre[q][p];
+                if (idx < CH) *reinterpret_cast<float4*>(&sm[q][idx / G4][(idx % G4) * 4]) = Elem<Tin>::cvt(pre[q][p]);
             }
         if (tid < kTB * (R / 4)) {
             const int t = tid / (R / 4), c = tid % (R / 4);
-            *reinterpret_cast<float4*>(&sv[t][c * 4]) = prev;
+            *reinterpret_cast<float4*>(&sv[t][c * 4]) = Elem<Tin>::cvt(prev);
         }
     };
 
@@ -127,7 +134,10 @@ __global__ __launch_bounds__(64 * WAVES) void seq_fwd_kernel(
 #pragma unroll
             for (int c = 0; c < C; ++c) dst[(cq * C + c) * N] = f2bf(S[c]);
         }
-        for (int t = 0; t < nt; ++t) {
+        // One token of the recurrence on this lane's columns.  Whole stages are
+        // unrolled so that the LDS reads of later tokens overlap the dependent
+        // dot -> DPP sum -> update chain of the current one.
+        auto step = [&](int t) __attribute__((always_inline)) {
             float W[C], K[C], Rr[C];
             load_cols<C>(&sm[1][t][cq * C], W);
             load_cols<C>(&sm[2][t][cq * C], K);
@@ -147,6 +157,12 @@ __global__ __launch_bounds__(64 * WAVES) void seq_fwd_kernel(
             }
             const float yy = row16_sum(dot_cols(S, Rr));
             if (cq == 0) sy[t][rloc] = yy;
+        };
+        if (nt == kTB) {
+#pragma unroll
+            for (int t = 0; t < kTB; ++t) step(t);
+        } else {
+            for (int t = 0; t < nt; ++t) step(t);
         }
         __syncthreads();
         for (int idx = tid; y && idx < nt * R; idx += NT) {
