@@ -86,26 +86,29 @@ __global__ __launch_bounds__(64 * WAVES) void seq_fwd_kernel(
     bf16_t* const tapeS = tape ? tape + (size_t)(gridDim.x / NRB) / H * T * H * N : nullptr;
 
     // Prefetched elements stay as loaded (bf16 words) until stashed: converting
-    // them at the load would make the stage wait for its own prefetch.
+    // them at the load would make the stage wait for its own prefetch.  Every
+    // thread loads on every stage (indices clamped to the last token and the
+    // last piece: the surplus loads repeat valid addresses), so no load sits on
+    // a conditional path -- after such a path the compiler no longer knows
+    // which loads are done and waits for the whole memory counter, stores
+    // included, before reusing their registers.
     typedef typename Elem<Tin>::raw4 raw4;
     raw4 pre[5][PER];
-    raw4 prev = {};
+    raw4 prev;
     constexpr int NQ = kAB ? 5 : 3;   // token vectors staged: r, w, k (, a, b)
+    constexpr int VP = kTB * (R / 4); // 4-element pieces of this workgroup's v slice per stage
     auto load_regs = [&](int t0) {
 #pragma unroll
         for (int q = 0; q < NQ; ++q)
 #pragma unroll
             for (int p = 0; p < PER; ++p) {
-                const int idx = tid + p * NT;
-                const int t = idx / G4, c = idx % G4;
-                if (idx < CH && t0 + t < T)
-                    pre[q][p] = Elem<Tin>::load_raw4(src[q] + tok_off_n<N>(bb, t0 + t, hh, T, H) + c * 4);
+                const int idx = min(tid + p * NT, CH - 1);
+                const int t = min(t0 + idx / G4, T - 1), c = idx % G4;
+                pre[q][p] = Elem<Tin>::load_raw4(src[q] + tok_off_n<N>(bb, t, hh, T, H) + c * 4);
             }
-        if (tid < kTB * (R / 4)) {
-            const int t = tid / (R / 4), c = tid % (R / 4);
-            if (t0 + t < T)
-                prev = Elem<Tin>::load_raw4(v + tok_off_n<N>(bb, t0 + t, hh, T, H) + rb * R + c * 4);
-        }
+        const int vi = min(tid, VP - 1);
+        const int t = min(t0 + vi / (R / 4), T - 1), c = vi % (R / 4);
+        prev = Elem<Tin>::load_raw4(v + tok_off_n<N>(bb, t, hh, T, H) + rb * R + c * 4);
     };
     auto store_lds = [&]() {
 #pragma unroll
@@ -115,7 +118,7 @@ __global__ __launch_bounds__(64 * WAVES) void seq_fwd_kernel(
                 const int idx = tid + p * NT;
                 if (idx < CH) *reinterpret_cast<float4*>(&sm[q][idx / G4][(idx % G4) * 4]) = Elem<Tin>::cvt(pre[q][p]);
             }
-        if (tid < kTB * (R / 4)) {
+        if (tid < VP) {
             const int t = tid / (R / 4), c = tid % (R / 4);
             *reinterpret_cast<float4*>(&sv[t][c * 4]) = Elem<Tin>::cvt(prev);
         }
@@ -128,7 +131,7 @@ __global__ __launch_bounds__(64 * WAVES) void seq_fwd_kernel(
     __syncthreads();
     for (int t0 = 0; t0 < T; t0 += kTB) {
         const int nt = min(kTB, T - t0);
-        if (t0 + kTB < T) load_regs(t0 + kTB);
+        load_regs(t0 + kTB);   // the next stage (past the end: repeats the last token, unused)
         if (tape && t0 % 32 == 0) {   // entry state of block t0 / 32
             bf16_t* dst = tapeS + ((size_t)bh * nblk + t0 / 32) * N * N + row;
 #pragma unroll
@@ -136,7 +139,11 @@ __global__ __launch_bounds__(64 * WAVES) void seq_fwd_kernel(
         }
         // One token of the recurrence on this lane's columns.  Whole stages are
         // unrolled so that the LDS reads of later tokens overlap the dependent
-        // dot -> DPP sum -> update chain of the current one.
+        // dot -> DPP sum -> update chain of the current one.  The read-outs of
+        // token t stay in lane t of the row (a select, not a branched store,
+        // which would cut the stage into one basic block per token) and are
+        // written to LDS once per stage.
+        float y_lane = 0.f, z_lane = 0.f;
         auto step = [&](int t) __attribute__((always_inline)) {
             float W[C], K[C], Rr[C];
             load_cols<C>(&sm[1][t][cq * C], W);
@@ -148,7 +155,7 @@ __global__ __launch_bounds__(64 * WAVES) void seq_fwd_kernel(
                 load_cols<C>(&sm[3][t][cq * C], A);
                 load_cols<C>(&sm[4][t][cq * C], Bv);
                 const float z = row16_sum(dot_cols(S, A));
-                if (cq == 0) sz[t][rloc] = z;
+                z_lane = cq == t ? z : z_lane;
 #pragma unroll
                 for (int c = 0; c < C; ++c) S[c] = fmaf(vi, K[c], fmaf(z, Bv[c], S[c] * W[c]));
             } else {
@@ -156,7 +163,7 @@ __global__ __launch_bounds__(64 * WAVES) void seq_fwd_kernel(
                 for (int c = 0; c < C; ++c) S[c] = fmaf(vi, K[c], S[c] * W[c]);
             }
             const float yy = row16_sum(dot_cols(S, Rr));
-            if (cq == 0) sy[t][rloc] = yy;
+            y_lane = cq == t ? yy : y_lane;
         };
         if (nt == kTB) {
 #pragma unroll
@@ -164,16 +171,19 @@ __global__ __launch_bounds__(64 * WAVES) void seq_fwd_kernel(
         } else {
             for (int t = 0; t < nt; ++t) step(t);
         }
+        sy[cq][rloc] = y_lane;   // rows t >= nt hold nothing and are not stored
+        if (kAB) sz[cq][rloc] = z_lane;
         __syncthreads();
-        for (int idx = tid; y && idx < nt * R; idx += NT) {
-            const int t = idx / R, i = idx % R;
-            Elem<Tin>::store1(y + tok_off_n<N>(bb, t0 + t, hh, T, H) + rb * R + i, sy[t][i]);
+        // The next stage's rows go to LDS before this stage's outputs leave, so
+        // that the wait for the prefetch does not also wait for those stores.
+        store_lds();
+        static_assert(kTB * R == NT, "one read-out per thread and stage");
+        if (tid < nt * R) {
+            const int t = tid / R, i = tid % R;
+            const size_t o = tok_off_n<N>(bb, t0 + t, hh, T, H) + rb * R + i;
+            if (y) Elem<Tin>::store1(y + o, sy[t][i]);
+            if (kAB && tape) tapeZ[o] = f2bf(sz[t][i]);
         }
-        for (int idx = tid; kAB && tape && idx < nt * R; idx += NT) {
-            const int t = idx / R, i = idx % R;
-            tapeZ[tok_off_n<N>(bb, t0 + t, hh, T, H) + rb * R + i] = f2bf(sz[t][i]);
-        }
-        if (t0 + kTB < T) store_lds();
         __syncthreads();
     }
     if (sT) store_cols<C>(sT + soff, S);
