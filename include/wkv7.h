@@ -114,8 +114,10 @@ size_t wkv7_tape_bytes(const wkv7_desc *desc);
    intermediate adjoint and the adjoint of the state leaving every 32-token block
    there, as much again as the tape, plus 256 bytes of work queues), with_tape =
    0 when it passes none (then a forward re-run also writes its tape into the
-   workspace: twice the tape).  0 on an invalid descriptor or one the backward
-   does not take (N != WKV7_HEAD_SIZE). */
+   workspace: twice the tape).  With chunk_len = 0 (the sequential reverse
+   pass) the fp32 states every 16 tokens, B*H*ceil(T/16)*N*N*4 bytes, whatever
+   with_tape is.  0 on an invalid descriptor or one the backward does not take
+   (chunk_len = 16 with N != WKV7_HEAD_SIZE or fp32). */
 size_t wkv7_workspace_bytes(const wkv7_desc *desc, int with_tape);
 
 /*
@@ -188,8 +190,14 @@ int wkv7_forward_split(const wkv7_desc *desc, const void *r, const void *w, cons
  *   workspace   at least wkv7_workspace_bytes(desc, tape != NULL) bytes of
  *               device scratch (contents on entry are ignored); else
  *               WKV7_ERR_WORKSPACE.  Required whenever B*T*H > 0.
- * The gradients are computed chunk by chunk (16 tokens) on bf16 matrix cores
- * whatever desc->chunk_len is; only dtype = WKV7_BF16 is supported.
+ * desc->chunk_len selects the form:
+ *   16  chunk by chunk (16 tokens) on bf16 matrix cores: dtype = WKV7_BF16 and
+ *       N = 64 only (WKV7_ERR_UNSUPPORTED otherwise); uses the tape.
+ *   0   the sequential reverse recurrence token by token in fp32 on the vector
+ *       ALU (one workgroup per head): either dtype, N = 32, 64 or 128.  It
+ *       first re-runs the sequential forward to write fp32 states every 16
+ *       tokens into the workspace, B*H*ceil(T/16)*N*N*4 bytes (the size
+ *       wkv7_workspace_bytes returns for chunk_len = 0); `tape` is not used.
  */
 int wkv7_backward(const wkv7_desc *desc, const void *r, const void *w, const void *k,
                   const void *v, const void *a, const void *b, const float *s0,
@@ -204,7 +212,8 @@ int wkv7_backward(const wkv7_desc *desc, const void *r, const void *w, const voi
  * same arguments computes what wkv7_backward computes.  `tape` is required
  * (WKV7_ERR_INVALID_ARG when NULL and B*T*H > 0): the workspace carries the
  * first stage's results to the second, so both calls must receive the same
- * workspace, untouched in between.
+ * workspace, untouched in between.  Chunked form only (chunk_len = 0:
+ * WKV7_ERR_UNSUPPORTED).
  *   wkv7_backward_adjoint    the sequential part: the adjoint state carried
  *                            backwards through the chunks (the transposed
  *                            transition of "Paper Review: RWKV-7 Goose", The
@@ -240,6 +249,7 @@ int wkv7_backward_gradients(const wkv7_desc *desc, const void *r, const void *w,
  * in its last round).  All work has finished, as seen from `stream`, when the
  * work enqueued on `stream` has: `stream` waits for aux_stream's part.  The
  * library creates and destroys two events per call; it never synchronises.
+ * With chunk_len = 0 the sequential reverse pass runs on `stream` alone.
  */
 int wkv7_backward_overlapped(const wkv7_desc *desc, const void *r, const void *w, const void *k,
                              const void *v, const void *a, const void *b, const float *s0,

@@ -49,6 +49,13 @@ size_t tape_bytes_unchecked(const wkv7_desc* d) {
 // passed -- the tape of a forward re-run.
 constexpr size_t kQueueBytes = 256;
 
+// Workspace of the sequential reverse pass (chunk_len = 0): the fp32 state
+// entering every 16 tokens, [B][H][ceil(T/16)][N][N].
+size_t seq_ckpt_bytes(const wkv7_desc* d) {
+    const size_t nstg = ((size_t)d->T + 15) / 16;
+    return (size_t)d->B * d->H * nstg * d->N * d->N * sizeof(float);
+}
+
 int from_hip(hipError_t e) { return e == hipSuccess ? WKV7_OK : WKV7_ERR_LAUNCH; }
 
 // Compute units of the current device (0 if the runtime cannot say).
@@ -167,7 +174,9 @@ size_t wkv7_tape_bytes(const wkv7_desc* desc) {
 }
 
 size_t wkv7_workspace_bytes(const wkv7_desc* desc, int with_tape) {
-    if (check_desc(desc) != WKV7_OK || desc->N != WKV7_HEAD_SIZE) return 0;
+    if (check_desc(desc) != WKV7_OK) return 0;
+    if (desc->chunk_len == 0) return seq_ckpt_bytes(desc);
+    if (desc->dtype != WKV7_BF16 || desc->N != WKV7_HEAD_SIZE) return 0;
     return tape_bytes_unchecked(desc) * (with_tape ? 1 : 2) + kQueueBytes;
 }
 
@@ -257,8 +266,12 @@ int run_backward(const wkv7_desc* desc, const void* r, const void* w, const void
                  void* stream, int stages, void* aux) {
     int st = check_desc(desc);
     if (st != WKV7_OK) return st;
-    // The backward runs the chunked adjoint on bf16 matrix cores.
-    if (desc->dtype != WKV7_BF16 || desc->N != WKV7_HEAD_SIZE) return WKV7_ERR_UNSUPPORTED;
+    const bool seq = desc->chunk_len == 0;
+    // The chunked adjoint runs on bf16 matrix cores at N = 64; the sequential
+    // reverse pass (chunk_len = 0) takes either dtype and N = 32, 64, 128, and
+    // has no separate stages.
+    if (!seq && (desc->dtype != WKV7_BF16 || desc->N != WKV7_HEAD_SIZE)) return WKV7_ERR_UNSUPPORTED;
+    if (seq && stages != (wkv7::BWD_CHAIN | wkv7::BWD_KEYS)) return WKV7_ERR_UNSUPPORTED;
     if ((int64_t)desc->B * desc->H * ((desc->T + WKV7_TAPE_CHUNK - 1) / WKV7_TAPE_CHUNK) > INT32_MAX)
         return WKV7_ERR_UNSUPPORTED;
     const bool has_tokens = (int64_t)desc->B * desc->T * desc->H > 0;
@@ -274,7 +287,7 @@ int run_backward(const wkv7_desc* desc, const void* r, const void* w, const void
     // chain's results to the second stage, and a re-run would overwrite it.
     if (stages != (wkv7::BWD_CHAIN | wkv7::BWD_KEYS) && has_tokens && !tape)
         return WKV7_ERR_INVALID_ARG;
-    const size_t need = tape_bytes_unchecked(desc) * (tape ? 1 : 2) + kQueueBytes;
+    const size_t need = seq ? seq_ckpt_bytes(desc) : tape_bytes_unchecked(desc) * (tape ? 1 : 2) + kQueueBytes;
     if (has_tokens && (workspace == nullptr || workspace_bytes < need)) return WKV7_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if ((int64_t)desc->B * desc->H == 0) return WKV7_OK;
@@ -285,6 +298,14 @@ int run_backward(const wkv7_desc* desc, const void* r, const void* w, const void
         return WKV7_OK;
     }
     char* ws = static_cast<char*>(workspace);
+    if (seq) {
+        // The sequential reverse pass keeps its own fp32 checkpoints (the tape,
+        // if any, is not used).
+        const wkv7::SeqBwdArgs p{desc->B, desc->T, desc->H, desc->N, desc->dtype == WKV7_BF16,
+                                 r, w, k, v, a, b, dy, s0, dsT, dr, dw, dk, dv, da, db, ds0,
+                                 static_cast<float*>(workspace)};
+        return from_hip(wkv7::launch_seq_bwd(p, s));
+    }
     if (!tape) {
         // Re-run the forward (without y) into the last part of the workspace.
         void* own = ws + tape_bytes_unchecked(desc) + kQueueBytes;

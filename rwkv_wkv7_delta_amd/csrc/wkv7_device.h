@@ -169,6 +169,18 @@ __device__ __forceinline__ float row16_last(float x) {
     return __builtin_amdgcn_update_dpp(0.0f, x, 0x15F, 0xF, 0xF, false);
 }
 
+// Sum over the four 16-lane rows of a wave of the values at the same position
+// in the row, in every lane: v_permlane32_swap of x with itself gives the rows
+// (0, 1, 0, 1) and (2, 3, 2, 3); their sum s holds rows (0+2, 1+3, 0+2, 1+3);
+// v_permlane16_swap of s with itself gives (0+2) and (1+3) in every row.
+__device__ __forceinline__ float sum_rows4(float x) {
+    const unsigned u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const unsigned s = __float_as_uint(__uint_as_float(a[0]) + __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(s, s, false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Lane n of each row broadcast to the whole row (row_newbcast n).
 template <int n>
 __device__ __forceinline__ float row16_bcast(float x) {

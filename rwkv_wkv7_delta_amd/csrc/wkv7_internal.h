@@ -14,6 +14,8 @@ struct FwdArgs {
     void* y;          // may be null only when T == 0
     float* sT;        // may be null
     void* tape;       // may be null: bf16 Z [B][T][H][N] then entry states [B][H][nch][N][N]
+    float* ckpt = nullptr;   // sequential scan only, may be null: fp32 entry state of
+                             // every 16 tokens [B][H][ceil(T/16)][N][N]
 };
 
 struct BwdArgs {
@@ -30,6 +32,18 @@ struct BwdArgs {
     void* workX;       // dX [B][T][H][N] bf16
     void* workS;       // adjoint leaving every 32-token block [B][H][nblk][N][N] bf16
     int* counter;      // two ints: the per-key pass's block queue (reset by both passes)
+};
+
+// The sequential reverse pass: one workgroup per head over its fp32 checkpoints.
+struct SeqBwdArgs {
+    int B, T, H, N;
+    bool bf16;
+    const void *r, *w, *k, *v, *a, *b, *dy;   // a, b: both null for a = b = 0
+    const float* s0;    // may be null
+    const float* dsT;   // may be null
+    void *dr, *dw, *dk, *dv, *da, *db;        // da, db: null when a = b = 0
+    float* ds0;         // may be null
+    float* ckpt;        // [B][H][ceil(T/16)][N][N] fp32 scratch
 };
 
 struct DecodeArgs {
@@ -65,6 +79,8 @@ hipError_t launch_chunk_fwd_sequential(const FwdArgs& p, int chunk_len, int nseg
 enum { BWD_CHAIN = 1, BWD_KEYS = 2 };
 hipError_t launch_bwd(const BwdArgs& p, int chunk_len, int stages, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& p, hipStream_t stream);
+// Forward scan writing the checkpoints, then the reverse pass.
+hipError_t launch_seq_bwd(const SeqBwdArgs& p, hipStream_t stream);
 hipError_t launch_state_copy(int BH, int N, const float* s0, float* sT, hipStream_t stream);
 
 }  // namespace wkv7

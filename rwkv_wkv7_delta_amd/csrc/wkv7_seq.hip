@@ -42,7 +42,7 @@ __global__ __launch_bounds__(64 * WAVES) void seq_fwd_kernel(
     int T, int H, const Tin* __restrict__ r, const Tin* __restrict__ w,
     const Tin* __restrict__ k, const Tin* __restrict__ v, const Tin* __restrict__ a,
     const Tin* __restrict__ b, const float* __restrict__ s0, Tin* __restrict__ y,
-    float* __restrict__ sT, bf16_t* __restrict__ tape) {
+    float* __restrict__ sT, bf16_t* __restrict__ tape, float* __restrict__ ckpt) {
     constexpr int C = N / 16;        // key columns per lane
     constexpr int R = 4 * WAVES;     // state rows per workgroup
     constexpr int NRB = N / R;       // workgroups per head
@@ -137,6 +137,8 @@ __global__ __launch_bounds__(64 * WAVES) void seq_fwd_kernel(
 #pragma unroll
             for (int c = 0; c < C; ++c) dst[(cq * C + c) * N] = f2bf(S[c]);
         }
+        if (ckpt)   // fp32 entry state of every stage, for the sequential reverse pass
+            store_cols<C>(ckpt + (((size_t)bh * ((T + kTB - 1) / kTB) + t0 / kTB) * N + row) * N + cq * C, S);
         // One token of the recurrence on this lane's columns.  Whole stages are
         // unrolled so that the LDS reads of later tokens overlap the dependent
         // dot -> DPP sum -> update chain of the current one.  The read-outs of
@@ -238,6 +240,253 @@ __global__ __launch_bounds__(256) void decode_kernel(
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Sequential reverse pass: the adjoint recurrence token by token.  With the
+// adjoint G = dL/dS_t (after token t's write), going backwards in time:
+//   G += dy_t r_t^T;  dr_t = S_t^T dy_t;  dv_t = G k_t;  dk_t = G^T v_t;
+//   dw_t[j] = sum_i G[i][j] S_{t-1}[i][j];  z = S_{t-1} a_t;  dz = G b_t;
+//   db_t = G^T z;  da_t = S_{t-1}^T dz;  G <- G diag(w_t) + dz a_t^T
+// and ds0 = G at the end (the transposed transition of the forward step S <-
+// S (diag(w) + a b^T) + v k^T; "Paper Review: RWKV-7 Goose", The approach).
+//
+// One workgroup per head holds every row of G: rows are independent in the
+// recurrence, as in the forward (16 lanes per row, C = N/16 columns per lane,
+// RPL rows per 16-lane group).  The states S_t come from fp32 checkpoints at
+// every 16th token, written by the forward scan: per 16-token stage the pass
+// re-runs the forward from the checkpoint in sub-stages of KS tokens whose
+// states stay in registers (earlier sub-stages re-run again for later ones),
+// then steps G backwards over them.  The per-key gradients are sums over rows:
+// within a wave by lane swaps, across waves by LDS atomics into the stage's
+// [16][5][N] accumulator, which is written out once per stage.
+template <int N> struct SeqBwdShape {
+    static constexpr int WAVES = N / 4 < 16 ? N / 4 : 16;
+    static constexpr int RPL = N / (4 * WAVES);   // rows per 16-lane group
+    static constexpr int C = N / 16;              // columns per lane
+    // Tokens per sub-stage, whose states a lane keeps (RPL * C floats each):
+    // within the 128 VGPRs of a 16-wave workgroup, without spills.
+    static constexpr int KS = N == 32 ? 16 : N == 64 ? 8 : 1;
+};
+
+template <typename Tin, int N, bool kAB>
+__global__ __launch_bounds__(64 * SeqBwdShape<N>::WAVES) void seq_bwd_kernel(
+    int T, int H, const Tin* __restrict__ r, const Tin* __restrict__ w, const Tin* __restrict__ k,
+    const Tin* __restrict__ v, const Tin* __restrict__ a, const Tin* __restrict__ b,
+    const Tin* __restrict__ dy, const float* __restrict__ dsT, const float* __restrict__ ckpt,
+    Tin* __restrict__ dr, Tin* __restrict__ dw, Tin* __restrict__ dk, Tin* __restrict__ dv,
+    Tin* __restrict__ da, Tin* __restrict__ db, float* __restrict__ ds0) {
+    using Sh = SeqBwdShape<N>;
+    constexpr int WAVES = Sh::WAVES, RPL = Sh::RPL, C = Sh::C, KS = Sh::KS;
+    constexpr int NT = 64 * WAVES;
+    constexpr int NG = kAB ? 5 : 3;   // per-key gradients: dr, dw, dk (, da, db)
+    enum { VR, VW, VK, VV, VA, VB, VDY };
+    __shared__ __align__(16) float sm[7][kTB][N];     // r, w, k, v, a, b, dy of the stage
+    __shared__ __align__(16) float acc[kTB][5][N];    // dr, dw, dk, da, db of the stage
+    __shared__ float sdv[kTB][N];
+
+    const int bh = blockIdx.x;
+    const int bb = bh / H, hh = bh % H;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int grp = lane >> 4, cq = lane & 15;
+    const int row0 = (wave * 4 + grp) * RPL;          // rows row0 .. row0 + RPL - 1
+    const int nstg = (T + kTB - 1) / kTB;
+    auto off = [&](int t) { return (((size_t)bb * T + t) * H + hh) * N; };
+
+    float G[RPL][C];
+#pragma unroll
+    for (int rr = 0; rr < RPL; ++rr) {
+        if (dsT) {
+            load_cols<C>(dsT + ((size_t)bh * N + row0 + rr) * N + cq * C, G[rr]);
+        } else {
+#pragma unroll
+            for (int c = 0; c < C; ++c) G[rr][c] = 0.f;
+        }
+    }
+    for (int idx = tid; idx < kTB * 5 * N; idx += NT) (&acc[0][0][0])[idx] = 0.f;
+
+    // One forward token on the state rows S (as in the scan).
+    auto fwd = [&](int t, float (&S)[RPL][C]) __attribute__((always_inline)) {
+        float W[C], K[C], A[C], Bv[C];
+        load_cols<C>(&sm[VW][t][cq * C], W);
+        load_cols<C>(&sm[VK][t][cq * C], K);
+        if (kAB) {
+            load_cols<C>(&sm[VA][t][cq * C], A);
+            load_cols<C>(&sm[VB][t][cq * C], Bv);
+        }
+#pragma unroll
+        for (int rr = 0; rr < RPL; ++rr) {
+            const float vi = sm[VV][t][row0 + rr];
+            if (kAB) {
+                const float z = row16_sum(dot_cols(S[rr], A));
+#pragma unroll
+                for (int c = 0; c < C; ++c) S[rr][c] = fmaf(vi, K[c], fmaf(z, Bv[c], S[rr][c] * W[c]));
+            } else {
+#pragma unroll
+                for (int c = 0; c < C; ++c) S[rr][c] = fmaf(vi, K[c], S[rr][c] * W[c]);
+            }
+        }
+    };
+    // Sums a per-lane partial over every row of the head into acc[t][q].
+    auto add_rows = [&](int t, int q, const float (&p)[C]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            const float x = sum_rows4(p[c]);
+            if (grp == 0) atomicAdd(&acc[t][q][cq * C + c], x);
+        }
+    };
+    // One reverse token: St = S_t, Sp = S_{t-1}.  Each per-key sum is formed
+    // and reduced on its own (one partial live at a time), the token's vectors
+    // read from LDS where they are used.
+    auto bwd = [&](int t, const float (&St)[RPL][C], const float (&Sp)[RPL][C])
+        __attribute__((always_inline)) {
+        float V[C], p[C];
+        float dyi[RPL], vi[RPL];
+#pragma unroll
+        for (int rr = 0; rr < RPL; ++rr) {
+            dyi[rr] = sm[VDY][t][row0 + rr];
+            vi[rr] = sm[VV][t][row0 + rr];
+        }
+        load_cols<C>(&sm[VR][t][cq * C], V);
+#pragma unroll
+        for (int rr = 0; rr < RPL; ++rr)
+#pragma unroll
+            for (int c = 0; c < C; ++c) G[rr][c] = fmaf(dyi[rr], V[c], G[rr][c]);   // G = dL/dS_t
+        // dr_t = S_t^T dy_t
+#pragma unroll
+        for (int c = 0; c < C; ++c) p[c] = 0.f;
+#pragma unroll
+        for (int rr = 0; rr < RPL; ++rr)
+#pragma unroll
+            for (int c = 0; c < C; ++c) p[c] = fmaf(St[rr][c], dyi[rr], p[c]);
+        add_rows(t, 0, p);
+        // dk_t = G^T v_t
+#pragma unroll
+        for (int c = 0; c < C; ++c) p[c] = 0.f;
+#pragma unroll
+        for (int rr = 0; rr < RPL; ++rr)
+#pragma unroll
+            for (int c = 0; c < C; ++c) p[c] = fmaf(G[rr][c], vi[rr], p[c]);
+        add_rows(t, 2, p);
+        // dw_t[j] = sum_i G[i][j] S_{t-1}[i][j]
+#pragma unroll
+        for (int c = 0; c < C; ++c) p[c] = 0.f;
+#pragma unroll
+        for (int rr = 0; rr < RPL; ++rr)
+#pragma unroll
+            for (int c = 0; c < C; ++c) p[c] = fmaf(G[rr][c], Sp[rr][c], p[c]);
+        add_rows(t, 1, p);
+        // dv_t = G k_t: row i's value kept in lane rr of its group
+        load_cols<C>(&sm[VK][t][cq * C], V);
+        float dv_lane = 0.f;
+#pragma unroll
+        for (int rr = 0; rr < RPL; ++rr) {
+            const float dvi = row16_sum(dot_cols(G[rr], V));
+            dv_lane = cq == rr ? dvi : dv_lane;
+        }
+        if (cq < RPL) sdv[t][row0 + cq] = dv_lane;
+        if (kAB) {
+            // z = S_{t-1} a_t, dz = G b_t; db_t = G^T z, da_t = S_{t-1}^T dz
+            float z[RPL], dz[RPL];
+            load_cols<C>(&sm[VA][t][cq * C], V);
+#pragma unroll
+            for (int rr = 0; rr < RPL; ++rr) z[rr] = row16_sum(dot_cols(Sp[rr], V));
+            load_cols<C>(&sm[VB][t][cq * C], V);
+#pragma unroll
+            for (int rr = 0; rr < RPL; ++rr) dz[rr] = row16_sum(dot_cols(G[rr], V));
+#pragma unroll
+            for (int c = 0; c < C; ++c) p[c] = 0.f;
+#pragma unroll
+            for (int rr = 0; rr < RPL; ++rr)
+#pragma unroll
+                for (int c = 0; c < C; ++c) p[c] = fmaf(G[rr][c], z[rr], p[c]);
+            add_rows(t, 4, p);
+#pragma unroll
+            for (int c = 0; c < C; ++c) p[c] = 0.f;
+#pragma unroll
+            for (int rr = 0; rr < RPL; ++rr)
+#pragma unroll
+                for (int c = 0; c < C; ++c) p[c] = fmaf(Sp[rr][c], dz[rr], p[c]);
+            add_rows(t, 3, p);
+            // G <- G diag(w_t) + dz a_t^T
+            float W[C];
+            load_cols<C>(&sm[VW][t][cq * C], W);
+            load_cols<C>(&sm[VA][t][cq * C], V);
+#pragma unroll
+            for (int rr = 0; rr < RPL; ++rr)
+#pragma unroll
+                for (int c = 0; c < C; ++c) G[rr][c] = fmaf(dz[rr], V[c], G[rr][c] * W[c]);
+        } else {
+            load_cols<C>(&sm[VW][t][cq * C], V);
+#pragma unroll
+            for (int rr = 0; rr < RPL; ++rr)
+#pragma unroll
+                for (int c = 0; c < C; ++c) G[rr][c] *= V[c];
+        }
+    };
+
+    for (int stg = nstg - 1; stg >= 0; --stg) {
+        const int t0 = stg * kTB, nt = min(kTB, T - t0);
+        __syncthreads();   // the previous stage's rows and sums are consumed
+        const Tin* src[7] = {r, w, k, v, a, b, dy};
+        for (int idx = tid; idx < 7 * kTB * (N / 4); idx += NT) {
+            const int q = idx / (kTB * (N / 4)), rem = idx % (kTB * (N / 4));
+            const int t = rem / (N / 4), c = rem % (N / 4);
+            float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (t < nt && (kAB || (q != VA && q != VB)))
+                x = Elem<Tin>::load4(src[q] + off(t0 + t) + c * 4);
+            *reinterpret_cast<float4*>(&sm[q][t][c * 4]) = x;
+        }
+        __syncthreads();
+        const float* cp = ckpt + ((size_t)bh * nstg + stg) * N * N;
+        const int nsub = (nt + KS - 1) / KS;
+        for (int sub = nsub - 1; sub >= 0; --sub) {
+            float S[RPL][C];
+#pragma unroll
+            for (int rr = 0; rr < RPL; ++rr) load_cols<C>(cp + (size_t)(row0 + rr) * N + cq * C, S[rr]);
+            for (int t = 0; t < sub * KS; ++t) fwd(t, S);
+            float Ss[KS + 1][RPL][C];   // Ss[0]: the state before the sub-stage
+#pragma unroll
+            for (int rr = 0; rr < RPL; ++rr)
+#pragma unroll
+                for (int c = 0; c < C; ++c) Ss[0][rr][c] = S[rr][c];
+            const int kend = min(KS, nt - sub * KS);
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) {
+                if (kk < kend) {
+                    fwd(sub * KS + kk, S);
+#pragma unroll
+                    for (int rr = 0; rr < RPL; ++rr)
+#pragma unroll
+                        for (int c = 0; c < C; ++c) Ss[kk + 1][rr][c] = S[rr][c];
+                }
+            }
+#pragma unroll
+            for (int kk = KS - 1; kk >= 0; --kk)
+                if (kk < kend) bwd(sub * KS + kk, Ss[kk + 1], Ss[kk]);
+        }
+        __syncthreads();
+        for (int idx = tid; idx < nt * N; idx += NT) {
+            const int t = idx / N, j = idx % N;
+            const size_t o = off(t0 + t) + j;
+            Elem<Tin>::store1(dr + o, acc[t][0][j]);
+            Elem<Tin>::store1(dw + o, acc[t][1][j]);
+            Elem<Tin>::store1(dk + o, acc[t][2][j]);
+            Elem<Tin>::store1(dv + o, sdv[t][j]);
+            if (kAB) {
+                Elem<Tin>::store1(da + o, acc[t][3][j]);
+                Elem<Tin>::store1(db + o, acc[t][4][j]);
+            }
+#pragma unroll
+            for (int q = 0; q < 5; ++q) acc[t][q][j] = 0.f;
+        }
+    }
+    if (ds0) {
+#pragma unroll
+        for (int rr = 0; rr < RPL; ++rr) store_cols<C>(ds0 + ((size_t)bh * N + row0 + rr) * N + cq * C, G[rr]);
+    }
+}
+
 // Copies (or zero-fills, when src is null) n4 float4 values.
 __global__ __launch_bounds__(256) void state_copy_kernel(size_t n4, const float* __restrict__ src,
                                                          float* __restrict__ dst) {
@@ -255,7 +504,7 @@ hipError_t launch_seq_fwd_w(const FwdArgs& p, int blocks_per_head, hipStream_t s
         p.T, p.H, static_cast<const Tin*>(p.r), static_cast<const Tin*>(p.w),
         static_cast<const Tin*>(p.k), static_cast<const Tin*>(p.v), a,
         static_cast<const Tin*>(p.b), p.s0, static_cast<Tin*>(p.y), p.sT,
-        static_cast<bf16_t*>(p.tape));
+        static_cast<bf16_t*>(p.tape), p.ckpt);
     return hipGetLastError();
 }
 
@@ -299,6 +548,32 @@ hipError_t launch_decode_t(const DecodeArgs& p, hipStream_t stream) {
     }
 }
 
+template <typename Tin, int N>
+hipError_t launch_seq_bwd_n(const SeqBwdArgs& p, hipStream_t stream) {
+    FwdArgs f{p.B, p.T, p.H, N, p.bf16, p.r, p.w, p.k, p.v, p.a, p.b, p.s0, nullptr, nullptr, nullptr};
+    f.ckpt = p.ckpt;
+    hipError_t e = launch_seq_fwd_n<Tin, N>(f, stream);
+    if (e != hipSuccess) return e;
+    auto kern = p.a ? seq_bwd_kernel<Tin, N, true> : seq_bwd_kernel<Tin, N, false>;
+    kern<<<dim3(p.B * p.H), dim3(64 * SeqBwdShape<N>::WAVES), 0, stream>>>(
+        p.T, p.H, static_cast<const Tin*>(p.r), static_cast<const Tin*>(p.w),
+        static_cast<const Tin*>(p.k), static_cast<const Tin*>(p.v), static_cast<const Tin*>(p.a),
+        static_cast<const Tin*>(p.b), static_cast<const Tin*>(p.dy), p.dsT, p.ckpt,
+        static_cast<Tin*>(p.dr), static_cast<Tin*>(p.dw), static_cast<Tin*>(p.dk),
+        static_cast<Tin*>(p.dv), static_cast<Tin*>(p.da), static_cast<Tin*>(p.db), p.ds0);
+    return hipGetLastError();
+}
+
+template <typename Tin>
+hipError_t launch_seq_bwd_t(const SeqBwdArgs& p, hipStream_t stream) {
+    switch (p.N) {
+        case 32: return launch_seq_bwd_n<Tin, 32>(p, stream);
+        case 64: return launch_seq_bwd_n<Tin, 64>(p, stream);
+        case 128: return launch_seq_bwd_n<Tin, 128>(p, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_seq_fwd(const FwdArgs& p, hipStream_t stream) {
@@ -313,6 +588,10 @@ hipError_t launch_state_copy(int BH, int N, const float* s0, float* sT, hipStrea
 
 hipError_t launch_decode(const DecodeArgs& p, hipStream_t stream) {
     return p.bf16 ? launch_decode_t<bf16_t>(p, stream) : launch_decode_t<float>(p, stream);
+}
+
+hipError_t launch_seq_bwd(const SeqBwdArgs& p, hipStream_t stream) {
+    return p.bf16 ? launch_seq_bwd_t<bf16_t>(p, stream) : launch_seq_bwd_t<float>(p, stream);
 }
 
 }  // namespace wkv7

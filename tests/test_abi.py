@@ -53,10 +53,12 @@ def test_tape_and_workspace_sizes(L):
     assert wk.tape_bytes(d) == 65 * 2 * 64 * 2 + 2 * 3 * 64 * 64 * 2
     assert wk.tape_bytes(wk.make_desc(3, 0, 2, 64, wk.WKV7_BF16, 16)) == 0
     assert wk.tape_bytes(wk.make_desc(1, 64, 1, 48, wk.WKV7_F32, 0)) == 0   # invalid N
-    # N = 32: the scan writes a tape of the same layout; the backward (N = 64
-    # only) has no workspace size.
+    # N = 32: the scan writes a tape of the same layout; the sequential reverse
+    # pass's workspace holds fp32 states every 16 tokens; the chunked form
+    # (N = 64 only) has no size.
     assert wk.tape_bytes(wk.make_desc(1, 64, 1, 32, wk.WKV7_F32, 0)) == 64 * 32 * 2 + 2 * 32 * 32 * 2
-    assert wk.workspace_bytes(wk.make_desc(1, 64, 1, 32, wk.WKV7_F32, 0), True) == 0
+    assert wk.workspace_bytes(wk.make_desc(1, 64, 1, 32, wk.WKV7_F32, 0), True) == 4 * 32 * 32 * 4
+    assert wk.workspace_bytes(wk.make_desc(1, 64, 1, 32, wk.WKV7_BF16, 16), True) == 0
 
 
 FAKE = 1 << 20   # aligned, never dereferenced (validation fails first or nothing runs)
@@ -145,16 +147,35 @@ def test_backward_validation(L):
     big = wk.make_desc(1 << 14, 256, 1 << 14, 64, wk.WKV7_BF16, 16)
     assert L.wkv7_backward(ctypes.byref(big), *args, FAKE, *grads, None, FAKE, 1 << 40, None) == \
         wk.WKV7_ERR_UNSUPPORTED
-    d32 = wk.make_desc(1, 8, 1, 64, wk.WKV7_F32, 0)
+    # The chunked backward is bf16 at N = 64 (fp32 and other head sizes take
+    # chunk_len = 0, the sequential reverse pass).
+    d32 = wk.make_desc(1, 8, 1, 64, wk.WKV7_F32, 16)
     assert L.wkv7_backward(ctypes.byref(d32), *args, FAKE, *grads, None, None, 0, None) == \
         wk.WKV7_ERR_UNSUPPORTED
-    # The backward is chunked: N = 64 only.
     for n in (32, 128):
-        dn = wk.make_desc(1, 8, 1, n, wk.WKV7_BF16, 0)
+        dn = wk.make_desc(1, 8, 1, n, wk.WKV7_BF16, 16)
         assert L.wkv7_backward(ctypes.byref(dn), *args, FAKE, *grads, None, FAKE, 1 << 30, None) == \
             wk.WKV7_ERR_UNSUPPORTED
     d0 = wk.make_desc(0, 8, 1, 64, wk.WKV7_BF16, 16)
     assert L.wkv7_backward(ctypes.byref(d0), *args, FAKE, *grads, None, None, 0, None) == wk.WKV7_OK
+
+
+def test_sequential_backward_validation(L):
+    """chunk_len = 0 selects the sequential reverse pass: either dtype, N = 32, 64,
+    128, a workspace of fp32 states every 16 tokens, no separate stages."""
+    for n, dt in ((32, wk.WKV7_F32), (64, wk.WKV7_BF16), (128, wk.WKV7_F32)):
+        d = wk.make_desc(2, 33, 3, n, dt, 0)
+        need = 2 * 3 * 3 * n * n * 4          # ceil(33 / 16) = 3 states per head
+        assert wk.workspace_bytes(d, True) == need
+        assert wk.workspace_bytes(d, False) == need
+        args = [FAKE] * 6 + [None, FAKE, None]
+        assert L.wkv7_backward(ctypes.byref(d), *args, None, *[FAKE] * 6, None, FAKE, need - 16,
+                               None) == wk.WKV7_ERR_WORKSPACE
+        for name in ("wkv7_backward_adjoint", "wkv7_backward_gradients"):
+            assert getattr(L, name)(ctypes.byref(d), *args, FAKE, *[FAKE] * 6, None, FAKE, need,
+                                    None) == wk.WKV7_ERR_UNSUPPORTED, name
+    # The chunked backward stays bf16 at N = 64.
+    assert wk.workspace_bytes(wk.make_desc(1, 64, 1, 64, wk.WKV7_F32, 16), True) == 0
 
 
 def test_backward_stage_validation(L):
@@ -171,7 +192,7 @@ def test_backward_stage_validation(L):
             wk.WKV7_ERR_WORKSPACE, name
         assert f(ctypes.byref(d), *args, FAKE, *[FAKE] * 5, None, None, FAKE, need, None) == \
             wk.WKV7_ERR_INVALID_ARG, name
-        d32 = wk.make_desc(1, 8, 1, 64, wk.WKV7_F32, 0)
+        d32 = wk.make_desc(1, 8, 1, 64, wk.WKV7_F32, 0)   # sequential: no stages
         assert f(ctypes.byref(d32), *args, FAKE, *grads, None, FAKE, need, None) == \
             wk.WKV7_ERR_UNSUPPORTED, name
         d0 = wk.make_desc(0, 8, 1, 64, wk.WKV7_BF16, 16)
@@ -188,8 +209,10 @@ def test_backward_overlapped_validation(L):
         assert f(ctypes.byref(d), *args, None, *grads, None, None, 0, None, aux) == wk.WKV7_ERR_WORKSPACE
         assert f(ctypes.byref(d), *args, None, *[FAKE] * 5, None, None, FAKE, 1 << 30, None, aux) == \
             wk.WKV7_ERR_INVALID_ARG
-        d32 = wk.make_desc(1, 8, 1, 64, wk.WKV7_F32, 0)
+        d32 = wk.make_desc(1, 8, 1, 64, wk.WKV7_F32, 16)
         assert f(ctypes.byref(d32), *args, FAKE, *grads, None, None, 0, None, aux) == wk.WKV7_ERR_UNSUPPORTED
+        dseq = wk.make_desc(1, 8, 1, 64, wk.WKV7_F32, 0)
+        assert f(ctypes.byref(dseq), *args, FAKE, *grads, None, None, 0, None, aux) == wk.WKV7_ERR_WORKSPACE
         d0 = wk.make_desc(0, 8, 1, 64, wk.WKV7_BF16, 16)
         assert f(ctypes.byref(d0), *args, FAKE, *grads, None, None, 0, None, aux) == wk.WKV7_OK
 

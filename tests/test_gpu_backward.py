@@ -138,8 +138,9 @@ def test_bwd_overlapped_without_split_is_plain_backward(wk):
 
 @pytest.mark.parametrize("fwd_chunk", [0, 16])
 def test_bwd_without_tape_matches_tape_path(wk, fwd_chunk):
-    """Without a tape the library re-runs the forward (sequential or chunked) into
-    the workspace first."""
+    """Without a tape the chunked backward re-runs the chunked forward into the
+    workspace first; with chunk_len = 0 the sequential reverse pass runs, which
+    uses no tape either way."""
     inp = synth.generate(1, 150, 3, 64, dtype="bf16", seed=31, random_s0=True, backward=True)
     a = _gpu_grads(wk, inp, use_tape=True, fwd_chunk=fwd_chunk)
     b = _gpu_grads(wk, inp, use_tape=False, fwd_chunk=fwd_chunk)

@@ -166,7 +166,8 @@ def test_bwd(wk, T):
 
 @pytest.mark.parametrize("fwd_chunk", [0, 16])
 def test_bwd_without_tape(wk, fwd_chunk):
-    """No tape: the backward re-runs the specialised forward (scan or chunked)."""
+    """No tape: the chunked backward re-runs the specialised chunked forward;
+    chunk_len = 0 runs the specialised sequential reverse pass."""
     inp = _inputs(1, 150, 3, "bf16", 380, backward=True)
     for name, x, rr in zip(NAMES, _grads(wk, inp, use_tape=False, fwd_chunk=fwd_chunk),
                            _ref_grads(inp)):
