@@ -544,6 +544,18 @@ def secondary(torch, wk, dev):
                                 "tokens_per_s": round(Bn / per_step * 1e3, 1),
                                 "alg_GBs": round(nbytes / per_step / 1e6, 1)}
         del st, one, yd
+    # The sequential reverse pass (chunk_len = 0) on the 0.19B-model shape, fp32 inputs.
+    ins = [x.float() for x in _dev_inputs(torch, (4, 1024, 12, N), dev, 8)]
+    dyf = torch.randn(4, 1024, 12, N, device=dev)
+    sdesc = wk.make_desc(4, 1024, 12, N, wk.WKV7_F32, 0)
+    sws = torch.empty(wk.workspace_bytes(sdesc, False) // 4, device=dev)
+    sgr = [torch.empty_like(ins[0]) for _ in range(6)]
+    ms = _time(torch, lambda: wk.backward(*ins, dyf, None, None, None, chunk_len=0, workspace=sws,
+                                          grads=sgr, want_ds0=False), 3)
+    res["sequential_bwd_0.19b_fp32"] = {
+        "workload": "B=4 T=1024 H=12 N=64 fp32, zero s0, dy~N(0,1): checkpointing scan + reverse pass",
+        "ms": round(ms, 4), "tokens_per_s": round(4 * 1024 / ms * 1e3, 1)}
+    del ins, dyf, sws, sgr
     # The sequential scan at N = 128 and N = 32 on the 0.19B-model token shape.
     for Nn in (128, 32):
         ins = _dev_inputs(torch, (4, 1024, 12, Nn), dev, 7)

@@ -252,7 +252,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
 //
 // One workgroup per head holds every row of G: rows are independent in the
 // recurrence, as in the forward (16 lanes per row, C = N/16 columns per lane,
-// RPL rows per 16-lane group).  The states S_t come from fp32 checkpoints at
+// four rows per 16-lane group).  The states S_t come from fp32 checkpoints at
 // every 16th token, written by the forward scan: per 16-token stage the pass
 // re-runs the forward from the checkpoint in sub-stages of KS tokens whose
 // states stay in registers (earlier sub-stages re-run again for later ones),
@@ -260,12 +260,13 @@ __global__ __launch_bounds__(256) void decode_kernel(
 // within a wave by lane swaps, across waves by LDS atomics into the stage's
 // [16][5][N] accumulator, which is written out once per stage.
 template <int N> struct SeqBwdShape {
-    static constexpr int WAVES = N / 4 < 16 ? N / 4 : 16;
-    static constexpr int RPL = N / (4 * WAVES);   // rows per 16-lane group
+    // Four rows per 16-lane group: N/16 waves per head, so that the per-key sums
+    // meet in LDS from few waves (the atomics on one address serialise).
+    static constexpr int RPL = 4;                 // rows per 16-lane group
+    static constexpr int WAVES = N / (4 * RPL);
     static constexpr int C = N / 16;              // columns per lane
-    // Tokens per sub-stage, whose states a lane keeps (RPL * C floats each):
-    // within the 128 VGPRs of a 16-wave workgroup, without spills.
-    static constexpr int KS = N == 32 ? 16 : N == 64 ? 8 : 1;
+    // Tokens per sub-stage, whose states a lane keeps (RPL * C floats each).
+    static constexpr int KS = 64 / (RPL * C) < kTB ? 64 / (RPL * C) : kTB;
 };
 
 template <typename Tin, int N, bool kAB>
