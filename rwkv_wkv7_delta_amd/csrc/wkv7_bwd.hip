@@ -243,11 +243,11 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
             kb4[cc] = kh4[cc] * GL;
         }
         const bf16x4 atb = cvt4(at), rtb = cvt4(rt);
-        *reinterpret_cast<bf16x4*>(&s.At[l16][j0]) = atb;
+        if (kAB) *reinterpret_cast<bf16x4*>(&s.At[l16][j0]) = atb;
         *reinterpret_cast<bf16x4*>(&s.Rt[l16][j0]) = rtb;
-        *reinterpret_cast<bf16x4*>(&s.Bh[l16][j0]) = cvt4(bh4);
+        if (kAB) *reinterpret_cast<bf16x4*>(&s.Bh[l16][j0]) = cvt4(bh4);
         *reinterpret_cast<bf16x4*>(&s.Kh[l16][j0]) = cvt4(kh4);
-        *reinterpret_cast<bf16x4*>(&s.Bb[l16][j0]) = cvt4(bb4);
+        if (kAB) *reinterpret_cast<bf16x4*>(&s.Bb[l16][j0]) = cvt4(bb4);
         *reinterpret_cast<bf16x4*>(&s.Kb[l16][j0]) = cvt4(kb4);
         *reinterpret_cast<uint2*>(&s.dY[l16][j0]) = raw6[P1_DY];
         if (l16 == kL - 1) *reinterpret_cast<float4*>(&s.gL[16 * g + 4 * wp]) = make_float4(gt[0], gt[1], gt[2], gt[3]);
@@ -321,20 +321,22 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
     auto read_C = [&](int c) __attribute__((always_inline)) -> CIn {
         const P1Slot& s = sm.sl[slot_of(c)];
         CIn in;
-        in.TmT = __builtin_bit_cast(bf16x4, s.tiles[TILE_T][lane]);
-        in.ArbT = __builtin_bit_cast(bf16x4, s.tiles[TILE_RB][lane]);
-        in.AakT = __builtin_bit_cast(bf16x4, s.tiles[TILE_AK][lane]);
+        if (kAB) {
+            in.TmT = __builtin_bit_cast(bf16x4, s.tiles[TILE_T][lane]);
+            in.ArbT = __builtin_bit_cast(bf16x4, s.tiles[TILE_RB][lane]);
+            in.AakT = __builtin_bit_cast(bf16x4, s.tiles[TILE_AK][lane]);
+        }
         in.ArkT = __builtin_bit_cast(bf16x4, s.tiles[TILE_RK][lane]);
         in.dY = ld4_tr(tr_addr(&s.dY[0][16 * wp], kRow, g, l16));   // [t][i] as a B operand
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
-            in.bb[k2] = ld4x2(&s.Bb[l16][32 * k2 + 4 * g]);
+            if (kAB) in.bb[k2] = ld4x2(&s.Bb[l16][32 * k2 + 4 * g]);
             in.kb[k2] = ld4x2(&s.Kb[l16][32 * k2 + 4 * g]);
         }
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
             in.rtT[jt] = ld4_tr(tr_addr(&s.Rt[0][16 * jt], kRow, g, l16));   // Rt^T as an A operand
-            in.atT[jt] = ld4_tr(tr_addr(&s.At[0][16 * jt], kRow, g, l16));
+            if (kAB) in.atT[jt] = ld4_tr(tr_addr(&s.At[0][16 * jt], kRow, g, l16));
         }
         in.gl = s.gL[lane];
         return in;
@@ -344,22 +346,28 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) dSb[jt] = cvt4(dSt[jt]);
         // Partial sums of the two MFMA shapes meet on the vector ALU (add4).
+        // (a = b = 0: Bb, Arb, Aak vanish, so dZ = dX = 0 and only the Kb and
+        // Ark terms of dV remain.)
         f32x4 dZ = zero4(), dVk = zero4();
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
             const bf16x8 ds8 = cat8(dSb[2 * k2], dSb[2 * k2 + 1]);
-            dZ = mfma32(in.bb[k2], ds8, dZ);
+            if (kAB) dZ = mfma32(in.bb[k2], ds8, dZ);
             dVk = mfma32(in.kb[k2], ds8, dVk);
         }
-        dZ = add4(dZ, mfma16(in.ArbT, in.dY, zero4()));
-        const bf16x4 dXb = cvt4(mfma16(in.TmT, cvt4(dZ), zero4()));
-        f32x4 dV = mfma16(in.AakT, dXb, zero4());
+        bf16x4 dXb = {};
+        f32x4 dV = zero4();
+        if (kAB) {
+            dZ = add4(dZ, mfma16(in.ArbT, in.dY, zero4()));
+            dXb = cvt4(mfma16(in.TmT, cvt4(dZ), zero4()));
+            dV = mfma16(in.AakT, dXb, zero4());
+        }
         dV = mfma16(in.ArkT, in.dY, dV);
         const bf16x4 dVb = cvt4(add4(dV, dVk));
         // Staged in row layout (swap_layout), 8 bytes per lane.
         const int sb = c & 1;
         const int i0 = 16 * wp + 4 * g;
-        *reinterpret_cast<bf16x4*>(&sm.dXs[sb][l16][i0]) = swap_layout(dXb, ident);
+        if (kAB) *reinterpret_cast<bf16x4*>(&sm.dXs[sb][l16][i0]) = swap_layout(dXb, ident);
         *reinterpret_cast<bf16x4*>(&sm.dVs[sb][l16][i0]) = swap_layout(dVb, ident);
         if (keeps_dS(c)) {
 #pragma unroll
@@ -372,7 +380,7 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
             const f32x4 acc = mfma16(in.rtT[jt], in.dY, dec[jt]);
-            dSt[jt] = mfma16(in.atT[jt], dXb, acc);
+            dSt[jt] = kAB ? mfma16(in.atT[jt], dXb, acc) : acc;
         }
     };
 
@@ -383,7 +391,7 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
         const int sb = c & 1;
         const int row = (rtid >> 3) & 15, piece = rtid & 7;
         const int tt = c * kL + row;
-        if (tt < T) {
+        if (tt < T && (kAB || rtid < 128)) {   // a = b = 0: dX is zero, not stored
             bf16_t* base = rtid < 128 ? dv : wdX;
             const bf16_t(*src)[kRow] = rtid < 128 ? sm.dVs[sb] : sm.dXs[sb];
             store_stream(base + tok_off(bb, tt, hh, T, H) + 8 * piece,
@@ -426,11 +434,11 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
         const int it_ = (IT);                                                  \
         const ERaw er = read_E(chunk_of(it_));                                 \
         MWIn mi;                                                               \
-        if (it_ >= 1 && wp != 0) mi = read_MW(chunk_of(it_ - 1));              \
+        if (it_ >= 1 && (kAB ? wp != 0 : wp == 3)) mi = read_MW(chunk_of(it_ - 1)); \
         stage_E(chunk_of(it_), er);                                            \
         stash_raw(chunk_of(it_ + 1), RING);                                    \
         load_raw(chunk_of(it_ + 4), RING);                                     \
-        if (it_ >= 1 && wp != 0) stage_MW(chunk_of(it_ - 1), mi);              \
+        if (it_ >= 1 && (kAB ? wp != 0 : wp == 3)) stage_MW(chunk_of(it_ - 1), mi); \
         __syncthreads();                                                       \
     }
             for (int it = 0; it < n_it; it += 3) {
@@ -445,7 +453,7 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
             // Interval it: the inverse of chunk_of(it-1), read by the chain in
             // interval it+1.
             for (int it = 0; it < n_it; ++it) {
-                if (it >= 1) stage_INV(chunk_of(it - 1));
+                if (kAB && it >= 1) stage_INV(chunk_of(it - 1));
                 __syncthreads();
             }
         } else {
@@ -568,10 +576,10 @@ __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
             const size_t off = tok_off(bh / H, t, bh % H, T, H) + 8 * ld_piece;
 #pragma unroll
             for (int vi = 0; vi < 4; ++vi) {
-                if (kAB || !(vi == 1 ? !lo : vi == 2 ? lo : false))
+                if (kAB || !(vi == 1 ? !lo : vi == 2 ? lo : vi == 3 ? !lo : false))
                     o.x[h][vi] = *reinterpret_cast<const uint4*>(src4[vi] + off);
                 else
-                    o.x[h][vi] = make_uint4(0u, 0u, 0u, 0u);   // a (vi = 1, hi) or b (vi = 2, lo)
+                    o.x[h][vi] = make_uint4(0u, 0u, 0u, 0u);   // a, b or dX (zero when a = b = 0)
             }
             if (lo) o.x[h][4] = kAB ? *reinterpret_cast<const uint4*>(tapeZ + off) : make_uint4(0u, 0u, 0u, 0u);
         }
@@ -685,9 +693,12 @@ __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
             // [t][i] tiles of value block vb in accumulator layout (lane holds
             // [4g+q][l16]); fed as A operands they stand for their transposes.
             const bf16x4 Vt = ld4_tr(tr_addr(&sm.rows[0][P2_V][0][16 * vb], kRow, g, l16));
-            const bf16x4 Zt = ld4_tr(tr_addr(&sm.rows[0][P2_Z][0][16 * vb], kRow, g, l16));
             const bf16x4 dYt = ld4_tr(tr_addr(&sm.rows[1][P2_DY][0][16 * vb], kRow, g, l16));
-            const bf16x4 dXt = ld4_tr(tr_addr(&sm.rows[1][P2_DX][0][16 * vb], kRow, g, l16));
+            bf16x4 Zt = {}, dXt = {};
+            if (kAB) {
+                Zt = ld4_tr(tr_addr(&sm.rows[0][P2_Z][0][16 * vb], kRow, g, l16));
+                dXt = ld4_tr(tr_addr(&sm.rows[1][P2_DX][0][16 * vb], kRow, g, l16));
+            }
             const bf16x4 s0 = ld4(&sm.st[0][0][col][i0]);
             const bf16x4 ds1 = ld4(&sm.st[1][1][col][i0]);
             f32x4 sacc, dacc;
@@ -696,10 +707,10 @@ __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
                 sacc[q] = f0.GL * (float)s0[q];
                 dacc[q] = f1.GL * (float)ds1[q];
             }
-            sacc = mfma16(Vt, f0.kbI, sacc);    // + V^T Kb  ([i][j])
-            sacc = mfma16(Zt, f0.bbI, sacc);    // + Z^T Bb
-            dacc = mfma16(dYt, f1.rtI, dacc);   // + dY^T Rt
-            dacc = mfma16(dXt, f1.atI, dacc);   // + dX^T At
+            sacc = mfma16(Vt, f0.kbI, sacc);                // + V^T Kb  ([i][j])
+            if (kAB) sacc = mfma16(Zt, f0.bbI, sacc);       // + Z^T Bb
+            dacc = mfma16(dYt, f1.rtI, dacc);               // + dY^T Rt
+            if (kAB) dacc = mfma16(dXt, f1.atI, dacc);      // + dX^T At
             *reinterpret_cast<bf16x4*>(&sm.st[0][1][col][i0]) = cvt4(sacc);
             *reinterpret_cast<bf16x4*>(&sm.st[1][0][col][i0]) = cvt4(dacc);
         }
@@ -714,8 +725,10 @@ __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
             const int i0 = 32 * k2 + 8 * g;
-            dXr[k2] = ld8(&sm.rows[h][P2_DX][l16][i0]);
-            Zr[k2] = ld8(&sm.rows[h][P2_Z][l16][i0]);
+            if (kAB) {
+                dXr[k2] = ld8(&sm.rows[h][P2_DX][l16][i0]);
+                Zr[k2] = ld8(&sm.rows[h][P2_Z][l16][i0]);
+            }
             dYr[k2] = ld8(&sm.rows[h][P2_DY][l16][i0]);
             Vr[k2] = ld8(&sm.rows[h][P2_V][l16][i0]);
             S0c[k2] = ld8(&sm.st[0][h][col][i0]);
@@ -726,7 +739,8 @@ __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
         // dAab = tril_-1(dX Z^T), dAak = tril_-1(dX V^T), dArb = tril_0(dY Z^T),
         // dArk = tril_0(dY V^T) ([t][s], contracted over the value rows) and
         // leaves it in row layout for the others -------------------------------------
-        {
+        // (a = b = 0: dX = Z = 0, so only dArk, tile 3, is formed.)
+        if (kAB || wp == 3) {
             const bool dyrow = (wp & 2) != 0, vcol = (wp & 1) != 0;
             f32x4 At_s = zero4();
 #pragma unroll
@@ -748,25 +762,30 @@ __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
         f32x4 dAt = zero4(), dRt = zero4(), dBb = zero4(), dKb = zero4();
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
-            dAt = mfma32(dXr[k2], S0c[k2], dAt);     // dX S0
-            dRt = mfma32(dYr[k2], S0c[k2], dRt);     // dY S0
-            dBb = mfma32(Zr[k2], dSc[k2], dBb);      // Z dS
-            dKb = mfma32(Vr[k2], dSc[k2], dKb);      // V dS
+            if (kAB) dAt = mfma32(dXr[k2], S0c[k2], dAt);     // dX S0
+            dRt = mfma32(dYr[k2], S0c[k2], dRt);              // dY S0
+            if (kAB) dBb = mfma32(Zr[k2], dSc[k2], dBb);      // Z dS
+            dKb = mfma32(Vr[k2], dSc[k2], dKb);               // V dS
         }
         __syncthreads();   // the four adjoint tiles are in LDS
         // A tile read by rows is its A operand; read transposed, that of its
         // transpose.  The 16-deep partial sums join the 32-deep ones on the
         // vector ALU (add4).
-        const bf16x4 Aab = ld4(&sm.adj[0][l16][4 * g]), AabT = ld4_tr(tr_addr(&sm.adj[0][0][0], kTileRow, g, l16));
-        const bf16x4 Aak = ld4(&sm.adj[1][l16][4 * g]), AakT = ld4_tr(tr_addr(&sm.adj[1][0][0], kTileRow, g, l16));
-        const bf16x4 Arb = ld4(&sm.adj[2][l16][4 * g]), ArbT = ld4_tr(tr_addr(&sm.adj[2][0][0], kTileRow, g, l16));
         const bf16x4 Ark = ld4(&sm.adj[3][l16][4 * g]), ArkT = ld4_tr(tr_addr(&sm.adj[3][0][0], kTileRow, g, l16));
-        dAt = add4(dAt, mfma16(Aak, f.khI, mfma16(Aab, f.bhI, zero4())));    // + dAab Bh + dAak Kh
-        dRt = add4(dRt, mfma16(Ark, f.khI, mfma16(Arb, f.bhI, zero4())));    // + dArb Bh + dArk Kh
-        f32x4 dBh = mfma16(AabT, f.atI, zero4());                             // dAab^T At
-        dBh = mfma16(ArbT, f.rtI, dBh);                                       // + dArb^T Rt
-        f32x4 dKh = mfma16(AakT, f.atI, zero4());                             // dAak^T At
-        dKh = mfma16(ArkT, f.rtI, dKh);                                       // + dArk^T Rt
+        f32x4 dBh = zero4(), dKh = zero4();
+        if (kAB) {
+            const bf16x4 Aab = ld4(&sm.adj[0][l16][4 * g]), AabT = ld4_tr(tr_addr(&sm.adj[0][0][0], kTileRow, g, l16));
+            const bf16x4 Aak = ld4(&sm.adj[1][l16][4 * g]), AakT = ld4_tr(tr_addr(&sm.adj[1][0][0], kTileRow, g, l16));
+            const bf16x4 Arb = ld4(&sm.adj[2][l16][4 * g]), ArbT = ld4_tr(tr_addr(&sm.adj[2][0][0], kTileRow, g, l16));
+            dAt = add4(dAt, mfma16(Aak, f.khI, mfma16(Aab, f.bhI, zero4())));    // + dAab Bh + dAak Kh
+            dRt = add4(dRt, mfma16(Ark, f.khI, mfma16(Arb, f.bhI, zero4())));    // + dArb Bh + dArk Kh
+            dBh = mfma16(AabT, f.atI, zero4());                                   // dAab^T At
+            dBh = mfma16(ArbT, f.rtI, dBh);                                       // + dArb^T Rt
+            dKh = mfma16(AakT, f.atI, zero4());                                   // dAak^T At
+        } else {
+            dRt = add4(dRt, mfma16(Ark, f.khI, zero4()));                         // + dArk Kh
+        }
+        dKh = mfma16(ArkT, f.rtI, dKh);                                           // + dArk^T Rt
 
         // ---- sum_i dS[i][col] S0[i][col] over this lane's 16 value rows -----------
         float cs = 0.f;
@@ -786,9 +805,10 @@ __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
         float base[4], e[4], bk[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            e[q] = dAt[q] * (float)f.atI[q];
-            bk[q] = dBb[q] * (float)f.bbI[q] + dKb[q] * (float)f.kbI[q];
-            base[q] = dRt[q] * (float)f.rtI[q] - dBh[q] * (float)f.bhI[q] - dKh[q] * (float)f.khI[q];
+            e[q] = kAB ? dAt[q] * (float)f.atI[q] : 0.f;
+            bk[q] = kAB ? dBb[q] * (float)f.bbI[q] + dKb[q] * (float)f.kbI[q] : dKb[q] * (float)f.kbI[q];
+            base[q] = kAB ? dRt[q] * (float)f.rtI[q] - dBh[q] * (float)f.bhI[q] - dKh[q] * (float)f.khI[q]
+                          : dRt[q] * (float)f.rtI[q] - dKh[q] * (float)f.khI[q];
         }
         const float sum_base = base[0] + base[1] + base[2] + base[3];
         const float sum_e = e[0] + e[1] + e[2] + e[3];
