@@ -65,11 +65,12 @@ extern "C" {
 #endif
 
 #define WKV7_ABI_VERSION 1
-/* Head sizes: the sequential scan (chunk_len = 0) and the decode step take
-   N = 32, 64 or 128 (a larger N is the state expansion of "Millions of States:
-   Designing a Scalable MoE Architecture with RWKV-7 Meta-learner", Abstract);
-   the chunked form, wkv7_forward_split with segments and every backward entry
-   point take N = WKV7_HEAD_SIZE only. */
+/* Head sizes: the sequential forms (chunk_len = 0: the scan and the reverse
+   pass of wkv7_backward) and the decode step take N = 32, 64 or 128 (a larger N
+   is the state expansion of "Millions of States: Designing a Scalable MoE
+   Architecture with RWKV-7 Meta-learner", Abstract); the chunked forms
+   (chunk_len = 16: forward, wkv7_forward_split with segments, every backward
+   entry point) take N = WKV7_HEAD_SIZE only. */
 #define WKV7_HEAD_SIZE 64
 #define WKV7_TAPE_CHUNK 16       /* tokens per chunk of the backward */
 #define WKV7_TAPE_BLOCK 32       /* tokens per state saved in the forward tape */
@@ -84,8 +85,9 @@ typedef enum {
 
 typedef enum { WKV7_F32 = 0, WKV7_BF16 = 1 } wkv7_dtype;
 
-/* Problem descriptor.  chunk_len = 0 selects the sequential scan (one token
-   at a time, state rows in registers); 16 selects the chunked form, whose
+/* Problem descriptor.  chunk_len = 0 selects the sequential forms (one token
+   at a time, state rows in registers, fp32 arithmetic: the scan forward, the
+   reverse recurrence backward); 16 selects the chunked forms, whose
    intra-chunk products run on bf16 matrix cores with the carried state kept
    in fp32 (the pages state that training remains parallelisable: Abstract;
    Elamur summary, Summary). */
@@ -183,9 +185,10 @@ int wkv7_forward_split(const wkv7_desc *desc, const void *r, const void *w, cons
  *   s0          as given to the forward (NULL = zeros).
  *   dy          [B][T][H][N] upstream gradient of y (dtype).
  *   dsT         [B][H][N][N] fp32 upstream gradient of S_T, or NULL (= 0).
- *   tape        the tape written by wkv7_forward with the same inputs, or
- *               NULL; then the backward first re-runs the forward (sequential
- *               scan if desc->chunk_len = 0, chunked otherwise) to write it.
+ *   tape        chunked form: the tape written by wkv7_forward with the same
+ *               inputs (by either forward form), or NULL; then the backward
+ *               first re-runs the chunked forward to write it.  Not used by
+ *               the sequential form (chunk_len = 0).
  *   dr..db      [B][T][H][N] outputs (dtype).  ds0: [B][H][N][N] fp32 or NULL.
  *   workspace   at least wkv7_workspace_bytes(desc, tape != NULL) bytes of
  *               device scratch (contents on entry are ignored); else

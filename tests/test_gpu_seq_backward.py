@@ -110,3 +110,19 @@ def test_seq_bwd_without_ds0(wk):
     ref = oracle.backward(*inp.tensors(), inp.s0, inp.dy)
     for name, x, rr in zip(NAMES[:6], g[:6], ref[:6]):
         assert_close(to_np(x), rr, "fp32", f"no ds0 {name}")
+
+
+def test_seq_bwd_2_9b_shape_sampled(wk):
+    """B=8, T=4096, H=40, bf16, dy ~ N(0,1): the sequential reverse pass over the
+    whole 2.9B-model shape on the GPU, the oracle on sampled heads."""
+    import torch
+    inp = synth.generate(8, 4096, 40, 64, dtype="bf16", seed=0, backward=True)
+    dev = [to_dev(x, "bf16") for x in inp.tensors()]
+    g = wk.backward(*dev, to_dev(inp.dy, "bf16"), None, None, None, chunk_len=0)
+    torch.cuda.synchronize()
+    pairs = [(0, 0), (7, 39), (3, 21)]
+    sel = [oracle.select_heads(x, pairs) for x in inp.tensors()]
+    ref = oracle.backward(*sel, None, oracle.select_heads(inp.dy, pairs))
+    for name, x, rr in zip(NAMES[:6], g[:6], ref[:6]):
+        assert_close(oracle.select_heads(to_np(x), pairs), rr, "bf16", f"2.9b seq bwd {name}")
+    assert_close(oracle.select_heads(to_np(g[6]), pairs, state=True), ref[6], "bf16", "2.9b seq bwd ds0")
