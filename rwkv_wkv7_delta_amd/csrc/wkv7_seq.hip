@@ -257,11 +257,11 @@ __global__ __launch_bounds__(256) void decode_kernel(
 // re-runs the forward from the checkpoint in sub-stages of KS tokens whose
 // states stay in registers (earlier sub-stages re-run again for later ones),
 // then steps G backwards over them.  The per-key gradients are sums over rows:
-// within a wave by lane swaps, across waves by LDS atomics into the stage's
-// [16][5][N] accumulator, which is written out once per stage.
+// within a wave by lane swaps, across waves through per-wave LDS slots summed
+// once per sub-stage (atomics on shared addresses serialised across waves)
+// into the stage's [16][5][N] sums, which are written out once per stage.
 template <int N> struct SeqBwdShape {
-    // Four rows per 16-lane group: N/16 waves per head, so that the per-key sums
-    // meet in LDS from few waves (the atomics on one address serialise).
+    // Four rows per 16-lane group: N/16 waves per head.
     static constexpr int RPL = 4;                 // rows per 16-lane group
     static constexpr int WAVES = N / (4 * RPL);
     static constexpr int C = N / 16;              // columns per lane
@@ -283,7 +283,8 @@ __global__ __launch_bounds__(64 * SeqBwdShape<N>::WAVES) void seq_bwd_kernel(
     enum { VR, VW, VK, VV, VA, VB, VDY };
     __shared__ __align__(16) float sm[7][kTB][N];     // r, w, k, v, a, b, dy of the stage
     __shared__ __align__(16) float acc[kTB][5][N];    // dr, dw, dk, da, db of the stage
-    __shared__ float sdv[kTB][N];
+    __shared__ __align__(16) float part[WAVES][KS][5][N];   // per-wave sums of a sub-stage
+    __shared__ float sdv[kTB][N + 1];                 // column N: where surplus lanes write
 
     const int bh = blockIdx.x;
     const int bb = bh / H, hh = bh % H;
@@ -304,7 +305,6 @@ __global__ __launch_bounds__(64 * SeqBwdShape<N>::WAVES) void seq_bwd_kernel(
             for (int c = 0; c < C; ++c) G[rr][c] = 0.f;
         }
     }
-    for (int idx = tid; idx < kTB * 5 * N; idx += NT) (&acc[0][0][0])[idx] = 0.f;
 
     // One forward token on the state rows S (as in the scan).
     auto fwd = [&](int t, float (&S)[RPL][C]) __attribute__((always_inline)) {
@@ -328,18 +328,26 @@ __global__ __launch_bounds__(64 * SeqBwdShape<N>::WAVES) void seq_bwd_kernel(
             }
         }
     };
-    // Sums a per-lane partial over every row of the head into acc[t][q].
-    auto add_rows = [&](int t, int q, const float (&p)[C]) __attribute__((always_inline)) {
+    // Sums a per-lane partial over the wave's rows into its slot part[wave][kk][q].
+    // Every group then holds every column's sum; group g writes columns c = g
+    // (mod 4) of its lanes (a select, not a branch: no basic block ends here).
+    auto add_rows = [&](int kk, int q, const float (&p)[C]) __attribute__((always_inline)) {
+        float x[C];
 #pragma unroll
-        for (int c = 0; c < C; ++c) {
-            const float x = sum_rows4(p[c]);
-            if (grp == 0) atomicAdd(&acc[t][q][cq * C + c], x);
+        for (int c = 0; c < C; ++c) x[c] = sum_rows4(p[c]);
+#pragma unroll
+        for (int c0 = 0; c0 < C; c0 += 4) {
+            const int c = c0 + (C >= 4 ? grp : grp & 1);
+            float xs = x[c0];
+#pragma unroll
+            for (int u = 1; u < (C < 4 ? C : 4); ++u) xs = c == c0 + u ? x[c0 + u] : xs;
+            part[wave][kk][q][cq * C + c] = xs;
         }
     };
     // One reverse token: St = S_t, Sp = S_{t-1}.  Each per-key sum is formed
     // and reduced on its own (one partial live at a time), the token's vectors
     // read from LDS where they are used.
-    auto bwd = [&](int t, const float (&St)[RPL][C], const float (&Sp)[RPL][C])
+    auto bwd = [&](int t, int kk, const float (&St)[RPL][C], const float (&Sp)[RPL][C])
         __attribute__((always_inline)) {
         float V[C], p[C];
         float dyi[RPL], vi[RPL];
@@ -360,7 +368,7 @@ __global__ __launch_bounds__(64 * SeqBwdShape<N>::WAVES) void seq_bwd_kernel(
         for (int rr = 0; rr < RPL; ++rr)
 #pragma unroll
             for (int c = 0; c < C; ++c) p[c] = fmaf(St[rr][c], dyi[rr], p[c]);
-        add_rows(t, 0, p);
+        add_rows(kk, 0, p);
         // dk_t = G^T v_t
 #pragma unroll
         for (int c = 0; c < C; ++c) p[c] = 0.f;
@@ -368,7 +376,7 @@ __global__ __launch_bounds__(64 * SeqBwdShape<N>::WAVES) void seq_bwd_kernel(
         for (int rr = 0; rr < RPL; ++rr)
 #pragma unroll
             for (int c = 0; c < C; ++c) p[c] = fmaf(G[rr][c], vi[rr], p[c]);
-        add_rows(t, 2, p);
+        add_rows(kk, 2, p);
         // dw_t[j] = sum_i G[i][j] S_{t-1}[i][j]
 #pragma unroll
         for (int c = 0; c < C; ++c) p[c] = 0.f;
@@ -376,7 +384,7 @@ __global__ __launch_bounds__(64 * SeqBwdShape<N>::WAVES) void seq_bwd_kernel(
         for (int rr = 0; rr < RPL; ++rr)
 #pragma unroll
             for (int c = 0; c < C; ++c) p[c] = fmaf(G[rr][c], Sp[rr][c], p[c]);
-        add_rows(t, 1, p);
+        add_rows(kk, 1, p);
         // dv_t = G k_t: row i's value kept in lane rr of its group
         load_cols<C>(&sm[VK][t][cq * C], V);
         float dv_lane = 0.f;
@@ -385,7 +393,7 @@ __global__ __launch_bounds__(64 * SeqBwdShape<N>::WAVES) void seq_bwd_kernel(
             const float dvi = row16_sum(dot_cols(G[rr], V));
             dv_lane = cq == rr ? dvi : dv_lane;
         }
-        if (cq < RPL) sdv[t][row0 + cq] = dv_lane;
+        sdv[t][cq < RPL ? row0 + cq : N] = dv_lane;
         if (kAB) {
             // z = S_{t-1} a_t, dz = G b_t; db_t = G^T z, da_t = S_{t-1}^T dz
             float z[RPL], dz[RPL];
@@ -401,14 +409,14 @@ __global__ __launch_bounds__(64 * SeqBwdShape<N>::WAVES) void seq_bwd_kernel(
             for (int rr = 0; rr < RPL; ++rr)
 #pragma unroll
                 for (int c = 0; c < C; ++c) p[c] = fmaf(G[rr][c], z[rr], p[c]);
-            add_rows(t, 4, p);
+            add_rows(kk, 4, p);
 #pragma unroll
             for (int c = 0; c < C; ++c) p[c] = 0.f;
 #pragma unroll
             for (int rr = 0; rr < RPL; ++rr)
 #pragma unroll
                 for (int c = 0; c < C; ++c) p[c] = fmaf(Sp[rr][c], dz[rr], p[c]);
-            add_rows(t, 3, p);
+            add_rows(kk, 3, p);
             // G <- G diag(w_t) + dz a_t^T
             float W[C];
             load_cols<C>(&sm[VW][t][cq * C], W);
@@ -464,7 +472,16 @@ __global__ __launch_bounds__(64 * SeqBwdShape<N>::WAVES) void seq_bwd_kernel(
             }
 #pragma unroll
             for (int kk = KS - 1; kk >= 0; --kk)
-                if (kk < kend) bwd(sub * KS + kk, Ss[kk + 1], Ss[kk]);
+                if (kk < kend) bwd(sub * KS + kk, kk, Ss[kk + 1], Ss[kk]);
+            __syncthreads();   // every wave's sums of the sub-stage are in LDS
+            for (int idx = tid; idx < kend * NG * N; idx += NT) {
+                const int kk = idx / (NG * N), q = (idx / N) % NG, j = idx % N;
+                float x = part[0][kk][q][j];
+#pragma unroll
+                for (int wv = 1; wv < WAVES; ++wv) x += part[wv][kk][q][j];
+                acc[sub * KS + kk][q][j] = x;
+            }
+            __syncthreads();   // the slots are read before the next sub-stage writes them
         }
         __syncthreads();
         for (int idx = tid; idx < nt * N; idx += NT) {
@@ -478,8 +495,6 @@ __global__ __launch_bounds__(64 * SeqBwdShape<N>::WAVES) void seq_bwd_kernel(
                 Elem<Tin>::store1(da + o, acc[t][3][j]);
                 Elem<Tin>::store1(db + o, acc[t][4][j]);
             }
-#pragma unroll
-            for (int q = 0; q < 5; ++q) acc[t][q][j] = 0.f;
         }
     }
     if (ds0) {
