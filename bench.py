@@ -53,8 +53,11 @@ COPY_BYTES = 1 << 30                # calibration copy: 1 GiB read + 1 GiB writt
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=10)
-    p.add_argument("--warmup", type=int, default=3)
+    # 50 timed steps (about 80 ms of device time): the fixed cost of the first
+    # launch and the final synchronisation, about half a millisecond, then adds
+    # about 1 % to a step instead of several per cent at 10 steps.
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true")
     p.add_argument("--seed", type=int, default=0)
