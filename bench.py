@@ -203,7 +203,7 @@ def main():
         summarize_profile(*args.summarize_profile)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the benchmark runs on one GPU: the kernels work on one GPU's share (B*H heads); --gpus must be 1",
                           "gpus_requested": args.gpus}))
         sys.exit(2)
 
