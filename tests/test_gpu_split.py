@@ -216,3 +216,21 @@ def test_split_fwd_2_9b_shape_sampled(wk):
     z1, st1 = wk.split_tape(tape1, B, T, H, 64)
     assert_close(to_np(z), to_np(z1), "bf16", "2.9b split tape z")
     assert_close(to_np(st), to_np(st1), "bf16", "2.9b split tape states")
+
+
+def test_tape_into_caller_buffer(wk):
+    """forward(tape_out=...) writes the same tape into a caller's buffer, split or not."""
+    import torch
+    inp = synth.generate(2, 200, 3, 64, dtype="bf16", seed=610, random_s0=True)
+    dev = [to_dev(x, "bf16") for x in inp.tensors()]
+    s0 = to_dev(inp.s0, "fp32")
+    B, T, H, N = inp.r.shape
+    nbytes = wk.tape_bytes(wk.make_desc(B, T, H, N, wk.WKV7_BF16, 16))
+    for seg in (None, 0, 3):
+        _, _, ref = wk.forward(*dev, s0, chunk_len=16, want_tape=True, segments=seg)
+        buf = torch.full((nbytes // 2 + 64,), 3.0, device="cuda", dtype=torch.bfloat16)
+        _, _, got = wk.forward(*dev, s0, chunk_len=16, tape_out=buf, segments=seg)
+        torch.cuda.synchronize()
+        assert got.data_ptr() == buf.data_ptr()
+        assert torch.equal(buf[:nbytes // 2], ref[:nbytes // 2]), seg
+        assert bool((buf[nbytes // 2:] == 3.0).all())   # nothing written past the tape
