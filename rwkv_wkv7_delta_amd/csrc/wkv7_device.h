@@ -124,6 +124,19 @@ __device__ __forceinline__ float row16_sum(float x) {
     return x;
 }
 
+// Sum over each aligned group of P = 4, 8 or 16 lanes; every lane of the group
+// gets the total (quad_perm [1,0,3,2], quad_perm [2,3,0,1], then for 8 lanes
+// row_half_mirror, for 16 also row_mirror).
+template <int P>
+__device__ __forceinline__ float lanes_sum(float x) {
+    static_assert(P == 4 || P == 8 || P == 16, "groups of 4, 8 or 16 lanes");
+    x += __builtin_amdgcn_update_dpp(0.0f, x, 0xB1, 0xF, 0xF, false);
+    x += __builtin_amdgcn_update_dpp(0.0f, x, 0x4E, 0xF, 0xF, false);
+    if (P >= 8) x += __builtin_amdgcn_update_dpp(0.0f, x, 0x141, 0xF, 0xF, false);
+    if (P >= 16) x += __builtin_amdgcn_update_dpp(0.0f, x, 0x140, 0xF, 0xF, false);
+    return x;
+}
+
 // Inclusive running product over the 16 lanes of each DPP row, in lane order
 // (row_shr 1, 2, 4, 8; lanes shifted in from outside the row contribute 1).
 __device__ __forceinline__ float row16_cumprod(float x) {

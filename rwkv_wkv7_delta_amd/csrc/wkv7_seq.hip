@@ -37,14 +37,20 @@ __device__ __forceinline__ size_t tok_off_n(int b, int t, int h, int T, int H) {
 
 // kAB = false: a = b = 0 (decay-only recurrence S <- S diag(w) + v k^T); a and
 // b are not read, z is not formed and the tape's Z part is not written.
-template <typename Tin, int N, int WAVES, bool kAB>
+// P = lanes per state row (the lane-ownership knob): 16 keeps each token's
+// dependent chain short (few heads: the latency of T serial tokens decides);
+// 4 or 8 cut the per-row overhead of the row sums, selects and LDS reads
+// (many heads: the vector-ALU issue rate decides).
+template <typename Tin, int N, int WAVES, bool kAB, int P>
 __global__ __launch_bounds__(64 * WAVES) void seq_fwd_kernel(
     int T, int H, const Tin* __restrict__ r, const Tin* __restrict__ w,
     const Tin* __restrict__ k, const Tin* __restrict__ v, const Tin* __restrict__ a,
     const Tin* __restrict__ b, const float* __restrict__ s0, Tin* __restrict__ y,
     float* __restrict__ sT, bf16_t* __restrict__ tape, float* __restrict__ ckpt) {
-    constexpr int C = N / 16;        // key columns per lane
-    constexpr int R = 4 * WAVES;     // state rows per workgroup
+    constexpr int C = N / P;         // key columns per lane
+    constexpr int RW = 64 / P;       // state rows per wave
+    constexpr int R = RW * WAVES;    // state rows per workgroup
+    constexpr int NU = kTB / P;      // read-outs per lane and stage (token u P + lane in row)
     constexpr int NRB = N / R;       // workgroups per head
     constexpr int NT = 64 * WAVES;   // threads
     constexpr int G4 = N / 4;        // 4-element groups per token vector
@@ -62,9 +68,9 @@ __global__ __launch_bounds__(64 * WAVES) void seq_fwd_kernel(
     const int bb = bh / H, hh = bh % H;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int rloc = wave * 4 + (lane >> 4);
+    const int rloc = wave * RW + lane / P;
     const int row = rb * R + rloc;
-    const int cq = lane & 15;           // this lane's columns: C * cq .. C * cq + C - 1
+    const int cq = lane % P;            // this lane's columns: C * cq .. C * cq + C - 1
     const Tin* src[5] = {r, w, k, a, b};
 
     const size_t soff = ((size_t)bh * N + row) * N + cq * C;
@@ -142,10 +148,12 @@ __global__ __launch_bounds__(64 * WAVES) void seq_fwd_kernel(
         // One token of the recurrence on this lane's columns.  Whole stages are
         // unrolled so that the LDS reads of later tokens overlap the dependent
         // dot -> DPP sum -> update chain of the current one.  The read-outs of
-        // token t stay in lane t of the row (a select, not a branched store,
-        // which would cut the stage into one basic block per token) and are
-        // written to LDS once per stage.
-        float y_lane = 0.f, z_lane = 0.f;
+        // token t stay in lane t mod P of the row, slot t / P (a select, not a
+        // branched store, which would cut the stage into one basic block per
+        // token) and are written to LDS once per stage.
+        float y_l[NU], z_l[NU];
+#pragma unroll
+        for (int u = 0; u < NU; ++u) y_l[u] = z_l[u] = 0.f;
         auto step = [&](int t) __attribute__((always_inline)) {
             float W[C], K[C], Rr[C];
             load_cols<C>(&sm[1][t][cq * C], W);
@@ -156,16 +164,18 @@ __global__ __launch_bounds__(64 * WAVES) void seq_fwd_kernel(
                 float A[C], Bv[C];
                 load_cols<C>(&sm[3][t][cq * C], A);
                 load_cols<C>(&sm[4][t][cq * C], Bv);
-                const float z = row16_sum(dot_cols(S, A));
-                z_lane = cq == t ? z : z_lane;
+                const float z = lanes_sum<P>(dot_cols(S, A));
+#pragma unroll
+                for (int u = 0; u < NU; ++u) z_l[u] = (cq == t - u * P) ? z : z_l[u];
 #pragma unroll
                 for (int c = 0; c < C; ++c) S[c] = fmaf(vi, K[c], fmaf(z, Bv[c], S[c] * W[c]));
             } else {
 #pragma unroll
                 for (int c = 0; c < C; ++c) S[c] = fmaf(vi, K[c], S[c] * W[c]);
             }
-            const float yy = row16_sum(dot_cols(S, Rr));
-            y_lane = cq == t ? yy : y_lane;
+            const float yy = lanes_sum<P>(dot_cols(S, Rr));
+#pragma unroll
+            for (int u = 0; u < NU; ++u) y_l[u] = (cq == t - u * P) ? yy : y_l[u];
         };
         if (nt == kTB) {
 #pragma unroll
@@ -173,18 +183,25 @@ __global__ __launch_bounds__(64 * WAVES) void seq_fwd_kernel(
         } else {
             for (int t = 0; t < nt; ++t) step(t);
         }
-        sy[cq][rloc] = y_lane;   // rows t >= nt hold nothing and are not stored
-        if (kAB) sz[cq][rloc] = z_lane;
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {   // rows t >= nt hold nothing and are not stored
+            sy[u * P + cq][rloc] = y_l[u];
+            if (kAB) sz[u * P + cq][rloc] = z_l[u];
+        }
         __syncthreads();
         // The next stage's rows go to LDS before this stage's outputs leave, so
         // that the wait for the prefetch does not also wait for those stores.
         store_lds();
-        static_assert(kTB * R == NT, "one read-out per thread and stage");
-        if (tid < nt * R) {
-            const int t = tid / R, i = tid % R;
-            const size_t o = tok_off_n<N>(bb, t0 + t, hh, T, H) + rb * R + i;
-            if (y) Elem<Tin>::store1(y + o, sy[t][i]);
-            if (kAB && tape) tapeZ[o] = f2bf(sz[t][i]);
+        static_assert(kTB * R % NT == 0, "whole read-outs per thread and stage");
+#pragma unroll
+        for (int u = 0; u < kTB * R / NT; ++u) {
+            const int idx = tid + u * NT;
+            if (idx < nt * R) {
+                const int t = idx / R, i = idx % R;
+                const size_t o = tok_off_n<N>(bb, t0 + t, hh, T, H) + rb * R + i;
+                if (y) Elem<Tin>::store1(y + o, sy[t][i]);
+                if (kAB && tape) tapeZ[o] = f2bf(sz[t][i]);
+            }
         }
         __syncthreads();
     }
@@ -512,10 +529,10 @@ __global__ __launch_bounds__(256) void state_copy_kernel(size_t n4, const float*
             src ? reinterpret_cast<const float4*>(src)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
-template <typename Tin, int N, int WAVES>
+template <typename Tin, int N, int WAVES, int P>
 hipError_t launch_seq_fwd_w(const FwdArgs& p, int blocks_per_head, hipStream_t stream) {
     const Tin* a = static_cast<const Tin*>(p.a);
-    auto kern = a ? seq_fwd_kernel<Tin, N, WAVES, true> : seq_fwd_kernel<Tin, N, WAVES, false>;
+    auto kern = a ? seq_fwd_kernel<Tin, N, WAVES, true, P> : seq_fwd_kernel<Tin, N, WAVES, false, P>;
     kern<<<dim3(p.B * p.H * blocks_per_head), dim3(64 * WAVES), 0, stream>>>(
         p.T, p.H, static_cast<const Tin*>(p.r), static_cast<const Tin*>(p.w),
         static_cast<const Tin*>(p.k), static_cast<const Tin*>(p.v), a,
@@ -524,13 +541,21 @@ hipError_t launch_seq_fwd_w(const FwdArgs& p, int blocks_per_head, hipStream_t s
     return hipGetLastError();
 }
 
+// Heads from which the scan switches to the many-heads layout: it needs
+// several workgroups per compute unit to hide its longer per-token chain (at
+// 256 and 320 heads it measured from 5 % faster to 35 % slower).
+constexpr int kManyHeads = 512;
+
 template <typename Tin, int N>
 hipError_t launch_seq_fwd_n(const FwdArgs& p, hipStream_t stream) {
-    // Few heads: split each head's rows over workgroups of 4 waves (16 rows)
-    // to occupy more compute units; many heads: at most 16 waves per workgroup.
-    constexpr int WMANY = N / 4 < 16 ? N / 4 : 16;
-    if (p.B * p.H < 512) return launch_seq_fwd_w<Tin, N, 4>(p, N / 16, stream);
-    return launch_seq_fwd_w<Tin, N, WMANY>(p, N / (4 * WMANY), stream);
+    // Few heads: 16 lanes per row, each head's rows over workgroups of 4 waves
+    // (16 rows) to occupy more compute units.  Many heads: 4 lanes per row, one
+    // workgroup of N/16 waves per head (1.3-1.5x the 16-lane form at 512 to
+    // 1280 heads); N = 128 keeps 16 lanes per row in two workgroups of 16 waves
+    // (8 lanes per row measured 2 % slower there).
+    if (p.B * p.H < kManyHeads) return launch_seq_fwd_w<Tin, N, 4, 16>(p, N / 16, stream);
+    if constexpr (N == 128) return launch_seq_fwd_w<Tin, N, 16, 16>(p, 2, stream);
+    else return launch_seq_fwd_w<Tin, N, N / 16, 4>(p, 1, stream);
 }
 
 template <typename Tin>

@@ -63,10 +63,11 @@ def test_seq_fwd_ragged(wk, dtype, T):
     _check_fwd(wk, inp, 0, f"seq {dtype} T={T}")
 
 
-def test_seq_fwd_many_heads_launch(wk):
-    """B*H >= 512 takes the one-workgroup-per-head launch."""
-    inp = synth.generate(16, 40, 40, 64, dtype="bf16", seed=5, random_s0=True)
-    _check_fwd(wk, inp, 0, "seq 640 heads")
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_seq_fwd_many_heads_launch(wk, dtype):
+    """B*H >= 512 takes the one-workgroup-per-head launch with 4 lanes per state row."""
+    inp = synth.generate(16, 40, 40, 64, dtype=dtype, seed=5, random_s0=True)
+    _check_fwd(wk, inp, 0, f"seq 640 heads {dtype}")
 
 
 def test_seq_fwd_0_19b_full(wk):

@@ -52,7 +52,7 @@ def test_seq_fwd(wk, N, dtype, T):
 
 @pytest.mark.parametrize("N", [32, 128])
 def test_seq_fwd_many_heads_launch(wk, N):
-    """B*H >= 512: the many-heads launch (N = 128: two workgroups of 16 waves per head)."""
+    """B*H >= 512: the many-heads launch (4 lanes per row; N = 128: 16 lanes, two workgroups of 16 waves per head)."""
     inp = synth.generate(16, 40, 40, N, dtype="bf16", seed=410 + N, random_s0=True)
     _check_fwd(wk, inp, f"seq N={N} 640 heads")
 
