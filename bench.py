@@ -561,6 +561,23 @@ def secondary(torch, wk, dev):
         "workload": "B=4 T=1024 H=12 N=64 fp32, zero s0, dy~N(0,1): checkpointing scan + reverse pass",
         "ms": round(ms, 4), "tokens_per_s": round(4 * 1024 / ms * 1e3, 1)}
     del ins, dyf, sws, sgr
+    # The sequential scan with many heads: the 1.5B-model shape (256 heads, 16 lanes
+    # per state row) and 512 heads (4 lanes per state row).
+    for name, (Bs, Ts, Hs) in (("sequential_fwd_1.5b", (8, 4096, 32)),
+                               ("sequential_fwd_512_heads", (16, 2048, 32))):
+        ins = _dev_inputs(torch, (Bs, Ts, Hs, N), dev, 9)
+        y = torch.empty_like(ins[0])
+        qd = wk.make_desc(Bs, Ts, Hs, N, wk.WKV7_BF16, 0)
+        qp = [x.data_ptr() for x in ins]
+
+        def scan():
+            if L.wkv7_forward(ctypes.byref(qd), *qp, None, y.data_ptr(), None, None, stream) != 0:
+                raise RuntimeError("wkv7_forward failed")
+
+        ms = _time(torch, scan, 5)
+        res[name] = {"workload": f"B={Bs} T={Ts} H={Hs} N=64 bf16, zero s0, chunk_len=0",
+                     "ms": round(ms, 4), "tokens_per_s": round(Bs * Ts / ms * 1e3, 1)}
+        del ins, y
     # The sequential scan at N = 128 and N = 32 on the 0.19B-model token shape.
     for Nn in (128, 32):
         ins = _dev_inputs(torch, (4, 1024, 12, Nn), dev, 7)
