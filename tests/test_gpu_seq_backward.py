@@ -126,3 +126,22 @@ def test_seq_bwd_2_9b_shape_sampled(wk):
     for name, x, rr in zip(NAMES[:6], g[:6], ref[:6]):
         assert_close(oracle.select_heads(to_np(x), pairs), rr, "bf16", f"2.9b seq bwd {name}")
     assert_close(oracle.select_heads(to_np(g[6]), pairs, state=True), ref[6], "bf16", "2.9b seq bwd ds0")
+
+
+def test_many_heads_scan_tape_and_checkpoints(wk):
+    """640 heads (the scan's 4-lanes-per-row layout): the chunked backward from a tape
+    the scan wrote, and the sequential reverse pass (whose scan writes the fp32
+    checkpoints in that layout), both against the oracle."""
+    import torch
+    inp = synth.generate(16, 40, 40, 64, dtype="bf16", seed=550, random_s0=True, backward=True)
+    dev = [to_dev(x, "bf16") for x in inp.tensors()]
+    s0 = to_dev(inp.s0, "fp32")
+    dy = to_dev(inp.dy, "bf16")
+    _, _, tape = wk.forward(*dev, s0, chunk_len=0, want_state=False, want_tape=True)
+    gc = wk.backward(*dev, dy, s0, None, tape, chunk_len=16)
+    gs = wk.backward(*dev, dy, s0, None, None, chunk_len=0)
+    torch.cuda.synchronize()
+    ref = oracle.backward(*inp.tensors(), inp.s0, inp.dy)
+    for name, xc, xs, rr in zip(NAMES, gc, gs, ref):
+        assert_close(to_np(xc), rr, "bf16", f"640 heads, chunked from scan tape {name}")
+        assert_close(to_np(xs), rr, "bf16", f"640 heads, sequential {name}")
