@@ -208,18 +208,27 @@ __global__ __launch_bounds__(64 * WAVES) void seq_fwd_kernel(
     if (sT) store_cols<C>(sT + soff, S);
 }
 
-// One token on resident states.  One workgroup of 4 waves per (b, h); each
-// wave updates N/4 rows as groups of 4 rows, every lane C = N/16 consecutive
-// columns, so each state row is one contiguous segment per 16 lanes.
+// One token on resident states.  A workgroup of 4 waves holds 4 / WPH heads,
+// WPH waves per head (4, or 1 at N = 32, whose 4 KB state would leave a
+// 4-wave workgroup with too little to move); each wave updates N / WPH rows as
+// groups of 4 rows, every lane C = N/16 consecutive columns, so each state
+// row is one contiguous segment per 16 lanes.
+template <int N> struct DecodeShape {
+    static constexpr int WPH = N == 32 ? 1 : 4;   // waves per head
+    static constexpr int HPW = 4 / WPH;           // heads per workgroup
+};
 template <typename Tin, int N, bool kAB>
 __global__ __launch_bounds__(256) void decode_kernel(
-    const Tin* __restrict__ r, const Tin* __restrict__ w, const Tin* __restrict__ k,
+    int BH, const Tin* __restrict__ r, const Tin* __restrict__ w, const Tin* __restrict__ k,
     const Tin* __restrict__ v, const Tin* __restrict__ a, const Tin* __restrict__ b,
     float* __restrict__ state, Tin* __restrict__ y) {
-    constexpr int C = N / 16;   // columns per lane
-    constexpr int G = N / 16;   // groups of 4 rows per wave
-    const int bh = blockIdx.x;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    constexpr int WPH = DecodeShape<N>::WPH, HPW = DecodeShape<N>::HPW;
+    constexpr int C = N / 16;          // columns per lane
+    constexpr int G = N / (4 * WPH);   // groups of 4 rows per wave
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int bh = blockIdx.x * HPW + wv / WPH;
+    const int wave = wv % WPH;         // wave within the head
+    if (bh >= BH) return;              // the last workgroup's surplus waves (no barriers here)
     const int cq = lane & 15;
     const size_t io = (size_t)bh * N;
     float* st = state + (size_t)bh * N * N;
@@ -227,7 +236,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
     float vv[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-        const int row = wave * (N / 4) + g * 4 + (lane >> 4);
+        const int row = wave * (N / WPH) + g * 4 + (lane >> 4);
         load_cols<C>(st + row * N + cq * C, S[g]);
         vv[g] = Elem<Tin>::load1(v + io + row);
     }
@@ -242,7 +251,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
     load_cols<C>(r + io + cq * C, Rr);
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-        const int row = wave * (N / 4) + g * 4 + (lane >> 4);
+        const int row = wave * (N / WPH) + g * 4 + (lane >> 4);
         if (kAB) {
             const float z = row16_sum(dot_cols(S[g], A));
 #pragma unroll
@@ -571,8 +580,9 @@ hipError_t launch_seq_fwd_t(const FwdArgs& p, hipStream_t stream) {
 template <typename Tin, int N>
 hipError_t launch_decode_n(const DecodeArgs& p, hipStream_t stream) {
     auto kern = p.a ? decode_kernel<Tin, N, true> : decode_kernel<Tin, N, false>;
-    kern<<<dim3(p.B * p.H), dim3(256), 0, stream>>>(
-        static_cast<const Tin*>(p.r), static_cast<const Tin*>(p.w),
+    constexpr int HPW = DecodeShape<N>::HPW;
+    kern<<<dim3((p.B * p.H + HPW - 1) / HPW), dim3(256), 0, stream>>>(
+        p.B * p.H, static_cast<const Tin*>(p.r), static_cast<const Tin*>(p.w),
         static_cast<const Tin*>(p.k), static_cast<const Tin*>(p.v),
         static_cast<const Tin*>(p.a), static_cast<const Tin*>(p.b), p.state,
         static_cast<Tin*>(p.y));
