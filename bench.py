@@ -464,14 +464,18 @@ def secondary(torch, wk, dev):
     ptr = [x.data_ptr() for x in ins]
     stream = torch.cuda.current_stream().cuda_stream
     sdesc = wk.make_desc(B, T, H, N, wk.WKV7_BF16, 16)
-    sws_bytes = wk.split_workspace_bytes(sdesc, 0)
-    sws = torch.empty(max(sws_bytes // 4, 4), device=dev)
     qdesc = wk.make_desc(B, T, H, N, wk.WKV7_BF16, 0)
 
-    def split_call():
-        if L.wkv7_forward_split(ctypes.byref(sdesc), *ptr, None, y.data_ptr(), None, None, 0,
-                                sws.data_ptr(), sws_bytes, stream) != 0:
-            raise RuntimeError("wkv7_forward_split failed")
+    def split_call(d):
+        nbytes = wk.split_workspace_bytes(d, 0)
+        ws = torch.empty(max(nbytes // 4, 4), device=dev)
+
+        def fn():
+            if L.wkv7_forward_split(ctypes.byref(d), *ptr, None, y.data_ptr(), None, None, 0,
+                                    ws.data_ptr(), nbytes, stream) != 0:
+                raise RuntimeError("wkv7_forward_split failed")
+        fn.split = True
+        return fn
 
     def plain_call(d):
         def fn():
@@ -479,7 +483,7 @@ def secondary(torch, wk, dev):
                 raise RuntimeError("wkv7_forward failed")
         return fn
 
-    forms = (("chunked_split_fwd_0.19b", 16, split_call),
+    forms = (("chunked_split_fwd_0.19b", 16, split_call(sdesc)),
              ("chunked_fwd_0.19b", 16, plain_call(sdesc)),
              ("sequential_fwd_0.19b", 0, plain_call(qdesc)))
     reps = {name: [] for name, _, _ in forms}
@@ -488,12 +492,31 @@ def secondary(torch, wk, dev):
             reps[name].append(_time(torch, fn, 20))
     for name, cl, fn in forms:
         ms = float(np.median(reps[name]))
-        form = ("wkv7_forward_split, automatic plan (every head in time segments)"
-                if fn is split_call else f"chunk_len={cl}")
+        form = (f"chunk_len={cl}, wkv7_forward_split, automatic plan (every head in time "
+                "segments)" if getattr(fn, "split", False) else f"chunk_len={cl}")
         res[name] = {"workload": f"B=4 T=1024 H=12 bf16, zero s0, {form}",
                      "ms": round(ms, 4), "tokens_per_s": round(B * T / ms * 1e3, 1),
                      "us_per_16_tokens": round(ms * 1e3 / (T / 16), 3)}
-    del ins, y, sws
+    del ins, y
+    # One sequence of 4096 tokens, 12 heads: the scan's serial chain alone, and
+    # split in time by the library's plan.
+    B, T, H = 1, 4096, 12
+    ins = _dev_inputs(torch, (B, T, H, N), dev, 5)
+    y = torch.empty_like(ins[0])
+    ptr = [x.data_ptr() for x in ins]
+    qdesc = wk.make_desc(B, T, H, N, wk.WKV7_BF16, 0)
+    forms = (("sequential_split_fwd_12_heads", split_call(qdesc)),
+             ("sequential_fwd_12_heads", plain_call(qdesc)))
+    reps = {name: [] for name, _ in forms}
+    for _ in range(3):
+        for name, fn in forms:
+            reps[name].append(_time(torch, fn, 20))
+    for name, fn in forms:
+        ms = float(np.median(reps[name]))
+        form = ", wkv7_forward_split, automatic plan" if getattr(fn, "split", False) else ""
+        res[name] = {"workload": f"B=1 T=4096 H=12 bf16, zero s0, chunk_len=0{form}",
+                     "ms": round(ms, 4), "tokens_per_s": round(B * T / ms * 1e3, 1)}
+    del ins, y, forms
 
     # Decode steps through the C ABI with prepared arguments: a step takes tens
     # of microseconds on the device, the binding's own checks about as long.

@@ -103,7 +103,11 @@ int segment_length(int T, int& nseg) {
 SplitPlan plan_split(const wkv7_desc* d, int segments, int ncu) {
     const int nbh = d->B * d->H;
     const SplitPlan none{nbh, 1, d->T, 0};
-    if (nbh == 0 || d->T == 0 || d->chunk_len != 16 || segments == 1 || segments == -1) return none;
+    // The scan (chunk_len 0) splits by maps only, at N = 64.
+    const bool scan = d->chunk_len == 0;
+    if (nbh == 0 || d->T == 0 || segments == 1 || segments == -1 || (scan && d->N != 64) ||
+        (scan && segments < 0))
+        return none;
     int from = 0, nseg = segments, mode = 0;
     if (segments < 0) {
         mode = 1;
@@ -113,9 +117,15 @@ SplitPlan plan_split(const wkv7_desc* d, int segments, int ncu) {
         // the device; else, with more heads than compute units, split the heads
         // of the last, partial round when they are few enough (both by maps,
         // with as many segments as the device holds).
+        // The scan runs N/16 workgroups per head and no partial rounds: it
+        // splits every head when those fill at most half of the device (at
+        // 48 heads, 3/4 of it, segments measured no faster; at 320 heads
+        // the chunked form's tail split made the scan 14 % slower).
         if (ncu <= 0) return none;
         int part = nbh;
-        if (nbh > ncu) {
+        if (scan) {
+            if ((int64_t)nbh * (d->N / 16) * 2 > ncu) return none;
+        } else if (nbh > ncu) {
             part = nbh % ncu;
             from = nbh - part;
         }
@@ -204,7 +214,9 @@ int wkv7_forward_split(const wkv7_desc* desc, const void* r, const void* w, cons
     const int st = check_desc(desc);
     if (st != WKV7_OK) return st;
     if (segments < -kMaxSegments) return WKV7_ERR_INVALID_ARG;
-    if ((segments > 1 || segments < -1) && desc->chunk_len != 16) return WKV7_ERR_UNSUPPORTED;
+    if (desc->chunk_len == 0 ? (segments < -1 || (segments > 1 && desc->N != 64))
+                             : (segments > 1 || segments < -1) && desc->chunk_len != 16)
+        return WKV7_ERR_UNSUPPORTED;
     const bool has_tokens = (int64_t)desc->B * desc->T * desc->H > 0;
     if (has_tokens && !(req(r) && req(w) && req(k) && req(v) && pair(a, b) && req(y)))
         return WKV7_ERR_INVALID_ARG;
@@ -214,16 +226,17 @@ int wkv7_forward_split(const wkv7_desc* desc, const void* r, const void* w, cons
     if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return WKV7_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (need == 0) return run_forward(desc, r, w, k, v, a, b, s0, y, sT, tape, s);
-    const wkv7::FwdArgs p{desc->B, desc->T, desc->H, desc->N, true, r, w, k, v, a, b, s0, y, sT, tape};
+    const wkv7::FwdArgs p{desc->B, desc->T, desc->H, desc->N, desc->dtype == WKV7_BF16,
+                          r, w, k, v, a, b, s0, y, sT, tape};
+    const wkv7::FwdSplit sp{plan.split_from, plan.nseg, plan.seg_len, static_cast<float*>(workspace)};
+    if (desc->chunk_len == 0) return from_hip(wkv7::launch_seq_fwd_split(p, sp, s));
     if (plan.mode == 1) {
         float* states = static_cast<float*>(workspace);
         int* sync = reinterpret_cast<int*>(states + (size_t)desc->B * desc->H * desc->N * desc->N);
         return from_hip(wkv7::launch_chunk_fwd_sequential(p, 16, plan.nseg, plan.seg_len, states,
                                                           sync, s));
     }
-    return from_hip(wkv7::launch_chunk_fwd_split(
-        p, 16, wkv7::FwdSplit{plan.split_from, plan.nseg, plan.seg_len, static_cast<float*>(workspace)},
-        s));
+    return from_hip(wkv7::launch_chunk_fwd_split(p, 16, sp, s));
 }
 
 }  // extern "C"

@@ -92,65 +92,6 @@ struct Raw {
     u32x4 x[3];
 };
 
-// Work of one workgroup: a head over tokens [t_begin, t_end), started from the
-// state rows at `init` (else the identity when `ident`, else zero), with v
-// taken as zero when `vzero`; outputs (y, tape) only when `outs`; the final
-// state to `fin` when not null.
-struct Work {
-    int bh, t_begin, t_end;
-    const float* init;
-    float* fin;
-    bool ident, vzero, outs;
-};
-
-// blockIdx -> Work under a segment plan (FwdSplit): heads below split_from run
-// whole in pass 0; every later head runs in nseg segments of seg_len tokens.
-// Pass 0 also runs each split head's segment 0 (with outputs; its final state
-// is the entry state of segment 1) and, for segments 1 .. nseg-2, the two runs
-// whose final states give the segment's affine map S_out = S_in P + Hm: Hm from
-// zero with the real v, P from the identity with v = 0 (the recurrence is
-// affine in the state: S <- S M_t + v_t k_t^T).  Pass 1 re-runs segments
-// 1 .. nseg-1 from their entry states (composed in between), with outputs.
-// Per split head the workspace holds 3 nseg states: entry states (slot s),
-// Hm (nseg + s) and P (2 nseg + s).
-__device__ __forceinline__ Work work_of(int blk, int pass, int T, const float* s0, float* sT,
-                                        int split_from, int nseg, int seg_len, float* states) {
-    constexpr size_t NN = (size_t)kN * kN;
-    Work wk{0, 0, T, nullptr, nullptr, false, false, true};
-    if (pass == 0 && blk < split_from) {
-        wk.bh = blk;
-        wk.init = s0 ? s0 + (size_t)blk * NN : nullptr;
-        wk.fin = sT ? sT + (size_t)blk * NN : nullptr;
-        return wk;
-    }
-    const int j = pass == 0 ? blk - split_from : blk;
-    const int per = pass == 0 ? 2 * nseg - 3 : nseg - 1;
-    const int hs = j / per, rr = j % per;
-    wk.bh = split_from + hs;
-    float* const hst = states + (size_t)hs * 3 * nseg * NN;
-    if (pass == 0 && rr == 0) {
-        wk.t_end = seg_len;
-        wk.init = s0 ? s0 + (size_t)wk.bh * NN : nullptr;
-        wk.fin = hst + NN;
-    } else if (pass == 0) {
-        const int sg = 1 + (rr - 1) / 2;
-        const bool pm = ((rr - 1) & 1) != 0;
-        wk.t_begin = sg * seg_len;
-        wk.t_end = wk.t_begin + seg_len;
-        wk.ident = pm;
-        wk.vzero = pm;
-        wk.outs = false;
-        wk.fin = hst + (size_t)((pm ? 2 : 1) * nseg + sg) * NN;
-    } else {
-        const int sg = 1 + rr;
-        wk.t_begin = sg * seg_len;
-        wk.t_end = sg == nseg - 1 ? T : wk.t_begin + seg_len;
-        wk.init = hst + (size_t)sg * NN;
-        wk.fin = (sg == nseg - 1 && sT) ? sT + (size_t)wk.bh * NN : nullptr;
-    }
-    return wk;
-}
-
 // Sequential segments (kSeq): every head runs as nseg segments in order, one
 // workgroup per segment, numbered segment-major: workgroup u runs segment
 // u / (B*H) of head u % (B*H).  Its entry state is the final state that the
@@ -194,7 +135,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
                   seg == nseg - 1 ? (sT ? sT + (size_t)h * NN : nullptr) : states + (size_t)h * NN,
                   false, false, true};
     } else {
-        wk = work_of(blockIdx.x, pass, T, s0, sT, split_from, nseg, seg_len, states);
+        wk = work_of<kN>(blockIdx.x, pass, T, s0, sT, split_from, nseg, seg_len, states);
     }
     const int bh = wk.bh;
     const int bb = bh / H, hh = bh % H;
@@ -697,11 +638,16 @@ hipError_t launch_chunk_fwd_split(const FwdArgs& p, int chunk_len, const FwdSpli
     hipError_t e = run(0, sp.split_from + (nsplit > 0 ? nsplit * (2 * sp.nseg - 3) : 0));
     if (e != hipSuccess || nsplit == 0) return e;
     if (sp.nseg > 2) {
-        seg_combine_kernel<<<dim3(nsplit * (kN / kCombineRows)), dim3(256), 0, stream>>>(sp.nseg, sp.states);
-        e = hipGetLastError();
+        e = launch_seg_combine(nsplit, sp.nseg, sp.states, stream);
         if (e != hipSuccess) return e;
     }
     return run(1, nsplit * (sp.nseg - 1));
+}
+
+hipError_t launch_seg_combine(int nsplit, int nseg, float* states, hipStream_t stream) {
+    if (nsplit <= 0 || nseg < 3 || !states) return hipErrorInvalidValue;
+    seg_combine_kernel<<<dim3(nsplit * (kN / kCombineRows)), dim3(256), 0, stream>>>(nseg, states);
+    return hipGetLastError();
 }
 
 }  // namespace wkv7

@@ -215,4 +215,64 @@ __device__ __forceinline__ size_t tok_off(int b, int t, int h, int T, int H) {
     return (((size_t)b * T + t) * H + h) * kN;
 }
 
+// Work of one workgroup: a head over tokens [t_begin, t_end), started from the
+// state rows at `init` (else the identity when `ident`, else zero), with v
+// taken as zero when `vzero`; outputs (y, tape) only when `outs`; the final
+// state to `fin` when not null.
+struct Work {
+    int bh, t_begin, t_end;
+    const float* init;
+    float* fin;
+    bool ident, vzero, outs;
+};
+
+// blockIdx -> Work under a segment plan (FwdSplit): heads below split_from run
+// whole in pass 0; every later head runs in nseg segments of seg_len tokens.
+// Pass 0 also runs each split head's segment 0 (with outputs; its final state
+// is the entry state of segment 1) and, for segments 1 .. nseg-2, the two runs
+// whose final states give the segment's affine map S_out = S_in P + Hm: Hm from
+// zero with the real v, P from the identity with v = 0 (the recurrence is
+// affine in the state: S <- S M_t + v_t k_t^T).  Pass 1 re-runs segments
+// 1 .. nseg-1 from their entry states (composed in between), with outputs.
+// Per split head the workspace holds 3 nseg states: entry states (slot s),
+// Hm (nseg + s) and P (2 nseg + s).
+template <int N>
+__device__ __forceinline__ Work work_of(int blk, int pass, int T, const float* s0, float* sT,
+                                        int split_from, int nseg, int seg_len, float* states) {
+    constexpr size_t NN = (size_t)N * N;
+    Work wk{0, 0, T, nullptr, nullptr, false, false, true};
+    if (pass == 0 && blk < split_from) {
+        wk.bh = blk;
+        wk.init = s0 ? s0 + (size_t)blk * NN : nullptr;
+        wk.fin = sT ? sT + (size_t)blk * NN : nullptr;
+        return wk;
+    }
+    const int j = pass == 0 ? blk - split_from : blk;
+    const int per = pass == 0 ? 2 * nseg - 3 : nseg - 1;
+    const int hs = j / per, rr = j % per;
+    wk.bh = split_from + hs;
+    float* const hst = states + (size_t)hs * 3 * nseg * NN;
+    if (pass == 0 && rr == 0) {
+        wk.t_end = seg_len;
+        wk.init = s0 ? s0 + (size_t)wk.bh * NN : nullptr;
+        wk.fin = hst + NN;
+    } else if (pass == 0) {
+        const int sg = 1 + (rr - 1) / 2;
+        const bool pm = ((rr - 1) & 1) != 0;
+        wk.t_begin = sg * seg_len;
+        wk.t_end = wk.t_begin + seg_len;
+        wk.ident = pm;
+        wk.vzero = pm;
+        wk.outs = false;
+        wk.fin = hst + (size_t)((pm ? 2 : 1) * nseg + sg) * NN;
+    } else {
+        const int sg = 1 + rr;
+        wk.t_begin = sg * seg_len;
+        wk.t_end = sg == nseg - 1 ? T : wk.t_begin + seg_len;
+        wk.init = hst + (size_t)sg * NN;
+        wk.fin = (sg == nseg - 1 && sT) ? sT + (size_t)wk.bh * NN : nullptr;
+    }
+    return wk;
+}
+
 }  // namespace wkv7

@@ -69,6 +69,11 @@ struct FwdSplit {
 };
 hipError_t launch_chunk_fwd_split(const FwdArgs& p, int chunk_len, const FwdSplit& split,
                                   hipStream_t stream);
+// The sequential scan under the same plan (split heads: N = 64 only).
+hipError_t launch_seq_fwd_split(const FwdArgs& p, const FwdSplit& split, hipStream_t stream);
+// Entry states of segments 2 .. nseg-1 of nsplit split heads (N = 64), from
+// segment 0's final state and the maps in `states` (the plan's layout).
+hipError_t launch_seg_combine(int nsplit, int nseg, float* states, hipStream_t stream);
 // Every head as nseg segments of seg_len tokens run in order (one workgroup
 // per segment, segment-major); `states` holds one fp32 N x N state per head,
 // `sync` B*H ints (cleared by the launch).

@@ -41,12 +41,15 @@ __device__ __forceinline__ size_t tok_off_n(int b, int t, int h, int T, int H) {
 // dependent chain short (few heads: the latency of T serial tokens decides);
 // 4 or 8 cut the per-row overhead of the row sums, selects and LDS reads
 // (many heads: the vector-ALU issue rate decides).
+// Under a segment plan (pass, split_from, nseg, seg_len, states: see work_of)
+// a workgroup runs one segment, or one affine-map run, of its head.
 template <typename Tin, int N, int WAVES, bool kAB, int P>
 __global__ __launch_bounds__(64 * WAVES) void seq_fwd_kernel(
-    int T, int H, const Tin* __restrict__ r, const Tin* __restrict__ w,
+    int B, int T, int H, const Tin* __restrict__ r, const Tin* __restrict__ w,
     const Tin* __restrict__ k, const Tin* __restrict__ v, const Tin* __restrict__ a,
     const Tin* __restrict__ b, const float* __restrict__ s0, Tin* __restrict__ y,
-    float* __restrict__ sT, bf16_t* __restrict__ tape, float* __restrict__ ckpt) {
+    float* __restrict__ sT, bf16_t* __restrict__ tape, float* __restrict__ ckpt, int pass,
+    int split_from, int nseg, int seg_len, float* __restrict__ states) {
     constexpr int C = N / P;         // key columns per lane
     constexpr int RW = 64 / P;       // state rows per wave
     constexpr int R = RW * WAVES;    // state rows per workgroup
@@ -64,7 +67,8 @@ __global__ __launch_bounds__(64 * WAVES) void seq_fwd_kernel(
     __shared__ float sz[kTB][R];        // removal read-outs z = S a, for the tape
 
     const int rb = blockIdx.x % NRB;
-    const int bh = blockIdx.x / NRB;
+    const Work wk = work_of<N>(blockIdx.x / NRB, pass, T, s0, sT, split_from, nseg, seg_len, states);
+    const int bh = wk.bh;
     const int bb = bh / H, hh = bh % H;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -73,23 +77,26 @@ __global__ __launch_bounds__(64 * WAVES) void seq_fwd_kernel(
     const int cq = lane % P;            // this lane's columns: C * cq .. C * cq + C - 1
     const Tin* src[5] = {r, w, k, a, b};
 
-    const size_t soff = ((size_t)bh * N + row) * N + cq * C;
+    const size_t roff = (size_t)row * N + cq * C;   // this lane's piece of a head's state
     float S[C];
-    if (s0) {
-        load_cols<C>(s0 + soff, S);
+    if (wk.init) {
+        load_cols<C>(wk.init + roff, S);
         // Settle the load here: left pending on the path that skips the first
         // stage (T = 0), it would make the compiler wait for the whole memory
         // counter -- every stage's own prefetch -- before each use of S.
         __builtin_amdgcn_s_waitcnt(0);
     } else {
 #pragma unroll
-        for (int c = 0; c < C; ++c) S[c] = 0.f;
+        for (int c = 0; c < C; ++c) S[c] = (wk.ident && cq * C + c == row) ? 1.f : 0.f;
     }
     // Tape for the backward: z as [B][T][H][N] bf16, then the state entering every
-    // 32-token block as [B][H][nblk][N (key)][N (value)] bf16.
+    // 32-token block as [B][H][nblk][N (key)][N (value)] bf16 (segment runs with
+    // outputs write their own tokens and blocks; map runs write nothing).
     const int nblk = (T + 31) / 32;
-    bf16_t* const tapeZ = tape;
-    bf16_t* const tapeS = tape ? tape + (size_t)(gridDim.x / NRB) / H * T * H * N : nullptr;
+    bf16_t* const tapeZ = wk.outs ? tape : nullptr;
+    bf16_t* const tapeS = (tape && wk.outs) ? tape + (size_t)B * T * H * N : nullptr;
+    Tin* const yo = wk.outs ? y : nullptr;
+    float* const ck = wk.outs ? ckpt : nullptr;
 
     // Prefetched elements stay as loaded (bf16 words) until stashed: converting
     // them at the load would make the stage wait for its own prefetch.  Every
@@ -126,25 +133,28 @@ __global__ __launch_bounds__(64 * WAVES) void seq_fwd_kernel(
             }
         if (tid < VP) {
             const int t = tid / (R / 4), c = tid % (R / 4);
-            *reinterpret_cast<float4*>(&sv[t][c * 4]) = Elem<Tin>::cvt(prev);
+            // the P run of an affine map takes v = 0
+            *reinterpret_cast<float4*>(&sv[t][c * 4]) = wk.vzero ? make_float4(0.f, 0.f, 0.f, 0.f) : Elem<Tin>::cvt(prev);
         }
     };
 
-    if (T > 0) {
-        load_regs(0);
+    if (wk.t_begin < wk.t_end) {
+        load_regs(wk.t_begin);
         store_lds();
     }
     __syncthreads();
-    for (int t0 = 0; t0 < T; t0 += kTB) {
-        const int nt = min(kTB, T - t0);
-        load_regs(t0 + kTB);   // the next stage (past the end: repeats the last token, unused)
-        if (tape && t0 % 32 == 0) {   // entry state of block t0 / 32
+    // Segments start on multiples of 32 tokens, so stages and tape blocks keep
+    // their absolute positions.
+    for (int t0 = wk.t_begin; t0 < wk.t_end; t0 += kTB) {
+        const int nt = min(kTB, wk.t_end - t0);
+        load_regs(t0 + kTB);   // the next stage (past the end: other tokens, unused)
+        if (tapeS && t0 % 32 == 0) {   // entry state of block t0 / 32
             bf16_t* dst = tapeS + ((size_t)bh * nblk + t0 / 32) * N * N + row;
 #pragma unroll
             for (int c = 0; c < C; ++c) dst[(cq * C + c) * N] = f2bf(S[c]);
         }
-        if (ckpt)   // fp32 entry state of every stage, for the sequential reverse pass
-            store_cols<C>(ckpt + (((size_t)bh * ((T + kTB - 1) / kTB) + t0 / kTB) * N + row) * N + cq * C, S);
+        if (ck)   // fp32 entry state of every stage, for the sequential reverse pass
+            store_cols<C>(ck + (((size_t)bh * ((T + kTB - 1) / kTB) + t0 / kTB) * N + row) * N + cq * C, S);
         // One token of the recurrence on this lane's columns.  Whole stages are
         // unrolled so that the LDS reads of later tokens overlap the dependent
         // dot -> DPP sum -> update chain of the current one.  The read-outs of
@@ -199,13 +209,13 @@ __global__ __launch_bounds__(64 * WAVES) void seq_fwd_kernel(
             if (idx < nt * R) {
                 const int t = idx / R, i = idx % R;
                 const size_t o = tok_off_n<N>(bb, t0 + t, hh, T, H) + rb * R + i;
-                if (y) Elem<Tin>::store1(y + o, sy[t][i]);
-                if (kAB && tape) tapeZ[o] = f2bf(sz[t][i]);
+                if (yo) Elem<Tin>::store1(yo + o, sy[t][i]);
+                if (kAB && tapeZ) tapeZ[o] = f2bf(sz[t][i]);
             }
         }
         __syncthreads();
     }
-    if (sT) store_cols<C>(sT + soff, S);
+    if (wk.fin) store_cols<C>(wk.fin + roff, S);
 }
 
 // One token on resident states.  A workgroup of 4 waves holds 4 / WPH heads,
@@ -538,15 +548,18 @@ __global__ __launch_bounds__(256) void state_copy_kernel(size_t n4, const float*
             src ? reinterpret_cast<const float4*>(src)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
+// One launch of `units` head runs (whole heads, segments or map runs of the
+// pass, as work_of decodes them), blocks_per_head workgroups each.
 template <typename Tin, int N, int WAVES, int P>
-hipError_t launch_seq_fwd_w(const FwdArgs& p, int blocks_per_head, hipStream_t stream) {
+hipError_t launch_seq_fwd_w(const FwdArgs& p, int blocks_per_head, int units, int pass,
+                            const FwdSplit& sp, hipStream_t stream) {
     const Tin* a = static_cast<const Tin*>(p.a);
     auto kern = a ? seq_fwd_kernel<Tin, N, WAVES, true, P> : seq_fwd_kernel<Tin, N, WAVES, false, P>;
-    kern<<<dim3(p.B * p.H * blocks_per_head), dim3(64 * WAVES), 0, stream>>>(
-        p.T, p.H, static_cast<const Tin*>(p.r), static_cast<const Tin*>(p.w),
+    kern<<<dim3(units * blocks_per_head), dim3(64 * WAVES), 0, stream>>>(
+        p.B, p.T, p.H, static_cast<const Tin*>(p.r), static_cast<const Tin*>(p.w),
         static_cast<const Tin*>(p.k), static_cast<const Tin*>(p.v), a,
         static_cast<const Tin*>(p.b), p.s0, static_cast<Tin*>(p.y), p.sT,
-        static_cast<bf16_t*>(p.tape), p.ckpt);
+        static_cast<bf16_t*>(p.tape), p.ckpt, pass, sp.split_from, sp.nseg, sp.seg_len, sp.states);
     return hipGetLastError();
 }
 
@@ -556,23 +569,44 @@ hipError_t launch_seq_fwd_w(const FwdArgs& p, int blocks_per_head, hipStream_t s
 constexpr int kManyHeads = 512;
 
 template <typename Tin, int N>
-hipError_t launch_seq_fwd_n(const FwdArgs& p, hipStream_t stream) {
+hipError_t launch_seq_fwd_pass(const FwdArgs& p, int units, int pass, const FwdSplit& sp,
+                               hipStream_t stream) {
     // Few heads: 16 lanes per row, each head's rows over workgroups of 4 waves
     // (16 rows) to occupy more compute units.  Many heads: 4 lanes per row, one
     // workgroup of N/16 waves per head (1.3-1.5x the 16-lane form at 512 to
     // 1280 heads); N = 128 keeps 16 lanes per row in two workgroups of 16 waves
     // (8 lanes per row measured 2 % slower there).
-    if (p.B * p.H < kManyHeads) return launch_seq_fwd_w<Tin, N, 4, 16>(p, N / 16, stream);
-    if constexpr (N == 128) return launch_seq_fwd_w<Tin, N, 16, 16>(p, 2, stream);
-    else return launch_seq_fwd_w<Tin, N, N / 16, 4>(p, 1, stream);
+    if (units < kManyHeads) return launch_seq_fwd_w<Tin, N, 4, 16>(p, N / 16, units, pass, sp, stream);
+    if constexpr (N == 128) return launch_seq_fwd_w<Tin, N, 16, 16>(p, 2, units, pass, sp, stream);
+    else return launch_seq_fwd_w<Tin, N, N / 16, 4>(p, 1, units, pass, sp, stream);
+}
+
+// The scan under a segment plan: pass 0 (whole heads, segment 0 and the map
+// runs of every split head), the composition of the entry states, pass 1.
+template <typename Tin, int N>
+hipError_t launch_seq_fwd_n(const FwdArgs& p, const FwdSplit& sp, hipStream_t stream) {
+    const int nbh = p.B * p.H;
+    const int nsplit = nbh - sp.split_from;
+    if (nsplit < 0 || (nsplit > 0 && (N != 64 || sp.nseg < 2 || sp.seg_len <= 0 ||
+                                       sp.seg_len % 32 != 0 ||   // whole tape blocks
+                                       (long long)(sp.nseg - 1) * sp.seg_len >= p.T || !sp.states)))
+        return hipErrorInvalidValue;
+    hipError_t e = launch_seq_fwd_pass<Tin, N>(
+        p, sp.split_from + (nsplit > 0 ? nsplit * (2 * sp.nseg - 3) : 0), 0, sp, stream);
+    if (e != hipSuccess || nsplit == 0) return e;
+    if (sp.nseg > 2) {
+        e = launch_seg_combine(nsplit, sp.nseg, sp.states, stream);
+        if (e != hipSuccess) return e;
+    }
+    return launch_seq_fwd_pass<Tin, N>(p, nsplit * (sp.nseg - 1), 1, sp, stream);
 }
 
 template <typename Tin>
-hipError_t launch_seq_fwd_t(const FwdArgs& p, hipStream_t stream) {
+hipError_t launch_seq_fwd_t(const FwdArgs& p, const FwdSplit& sp, hipStream_t stream) {
     switch (p.N) {
-        case 32: return launch_seq_fwd_n<Tin, 32>(p, stream);
-        case 64: return launch_seq_fwd_n<Tin, 64>(p, stream);
-        case 128: return launch_seq_fwd_n<Tin, 128>(p, stream);
+        case 32: return launch_seq_fwd_n<Tin, 32>(p, sp, stream);
+        case 64: return launch_seq_fwd_n<Tin, 64>(p, sp, stream);
+        case 128: return launch_seq_fwd_n<Tin, 128>(p, sp, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -603,7 +637,7 @@ template <typename Tin, int N>
 hipError_t launch_seq_bwd_n(const SeqBwdArgs& p, hipStream_t stream) {
     FwdArgs f{p.B, p.T, p.H, N, p.bf16, p.r, p.w, p.k, p.v, p.a, p.b, p.s0, nullptr, nullptr, nullptr};
     f.ckpt = p.ckpt;
-    hipError_t e = launch_seq_fwd_n<Tin, N>(f, stream);
+    hipError_t e = launch_seq_fwd_n<Tin, N>(f, FwdSplit{p.B * p.H, 1, p.T, nullptr}, stream);
     if (e != hipSuccess) return e;
     auto kern = p.a ? seq_bwd_kernel<Tin, N, true> : seq_bwd_kernel<Tin, N, false>;
     kern<<<dim3(p.B * p.H), dim3(64 * SeqBwdShape<N>::WAVES), 0, stream>>>(
@@ -628,7 +662,11 @@ hipError_t launch_seq_bwd_t(const SeqBwdArgs& p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_seq_fwd(const FwdArgs& p, hipStream_t stream) {
-    return p.bf16 ? launch_seq_fwd_t<bf16_t>(p, stream) : launch_seq_fwd_t<float>(p, stream);
+    return launch_seq_fwd_split(p, FwdSplit{p.B * p.H, 1, p.T, nullptr}, stream);
+}
+
+hipError_t launch_seq_fwd_split(const FwdArgs& p, const FwdSplit& sp, hipStream_t stream) {
+    return p.bf16 ? launch_seq_fwd_t<bf16_t>(p, sp, stream) : launch_seq_fwd_t<float>(p, sp, stream);
 }
 
 hipError_t launch_state_copy(int BH, int N, const float* s0, float* sT, hipStream_t stream) {
