@@ -127,3 +127,23 @@ def test_scan_split_tape_matches_unsplit(wk, ab):
             assert not ab and name in ("da", "db")
             continue
         assert_close(to_np(g[j]), ref[j], "bf16", f"backward from split scan tape {name}")
+
+
+@pytest.mark.parametrize("T", [1, 32, 33, 64, 65])
+def test_scan_split_short_sequences(wk, T):
+    """Segments start at multiples of 32 tokens and the last keeps at least one:
+    T = 1 and 32 run unsplit, 33 as 32 + 1 tokens, 64 as 32 + 32, 65 as
+    32 + 32 + 1 (three segments: one map run)."""
+    inp = synth.generate(1, T, 2, 64, dtype="fp32", seed=560 + T, random_s0=True)
+    y, sT, _ = _run(wk, inp, 3)
+    yr, sr = oracle.forward(*inp.tensors(), inp.s0)
+    assert_close(y, yr, "fp32", f"scan split short T={T} y")
+    assert_close(sT, sr, "fp32", f"scan split short T={T} sT")
+
+
+def test_scan_split_empty_sequence(wk):
+    """T = 0: no tokens; the final state is s0."""
+    inp = synth.generate(1, 0, 2, 64, dtype="fp32", seed=570, random_s0=True)
+    y, sT, _ = _run(wk, inp, 4)
+    assert y.shape == (1, 0, 2, 64)
+    np.testing.assert_array_equal(sT, inp.s0)
