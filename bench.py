@@ -609,6 +609,20 @@ def secondary(torch, wk, dev):
         res[f"sequential_fwd_n{Nn}"] = {"workload": f"B=4 T=1024 H=12 N={Nn} bf16, zero s0, chunk_len=0",
                                         "ms": round(ms, 4), "tokens_per_s": round(4 * 1024 / ms * 1e3, 1)}
         del ins, y
+    # The scan split in time by the library's plan at N = 32 (0.19B token shape:
+    # 48 heads, 96 workgroups) and N = 128 (B=1 T=2048 H=4), each beside its
+    # unsplit time on the same inputs.
+    for Nn, (Bs, Ts, Hs) in ((32, (4, 1024, 12)), (128, (1, 2048, 4))):
+        ins = _dev_inputs(torch, (Bs, Ts, Hs, Nn), dev, 8)
+        y = torch.empty_like(ins[0])
+        ms = {seg: _time(torch, lambda: wk.forward(*ins, None, chunk_len=0, want_state=False, out=y,
+                                                   segments=seg), 10) for seg in (1, 0)}
+        res[f"sequential_split_fwd_n{Nn}"] = {
+            "workload": f"B={Bs} T={Ts} H={Hs} N={Nn} bf16, zero s0, chunk_len=0, "
+                        "wkv7_forward_split, automatic plan (both times through the binding)",
+            "ms": round(ms[0], 4), "tokens_per_s": round(Bs * Ts / ms[0] * 1e3, 1),
+            "unsplit_ms": round(ms[1], 4)}
+        del ins, y
     return res
 
 

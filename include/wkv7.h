@@ -147,16 +147,15 @@ int wkv7_forward(const wkv7_desc *desc, const void *r, const void *w, const void
  *                 heads than compute units: the heads of the last, partial
  *                 round by maps when they fill at most a third of it; the
  *                 scan: every head by maps when B*H*N/16 workgroups fill at
- *                 most half of it; else, or when T is too short for segments
- *                 of 128 tokens, no split);
+ *                 most half of it, at N = 128 in at most 4 segments; else, or
+ *                 when T is too short for segments of 128 tokens, no split);
  *              1 or -1: no split (exactly wkv7_forward);
  *              n >= 2: every head in up to n segments by maps;
  *              n <= -2: every head in up to -n sequential segments.
  *              At most 16 segments; below -16: WKV7_ERR_INVALID_ARG.  The
  *              chunked form (chunk_len = 16) splits both ways; the sequential
- *              scan (chunk_len = 0) splits by maps at N = 64 only (n <= -2, or
- *              n >= 2 at another N: WKV7_ERR_UNSUPPORTED; 0 at another N: no
- *              split).
+ *              scan (chunk_len = 0, N = 32, 64 or 128) by maps only (n <= -2:
+ *              WKV7_ERR_UNSUPPORTED).
  *   workspace  wkv7_forward_split_workspace_bytes(desc, segments) bytes of
  *              device scratch, or NULL when that is 0; else WKV7_ERR_WORKSPACE.
  * Segments start at multiples of 32 tokens (the tape's state blocks).

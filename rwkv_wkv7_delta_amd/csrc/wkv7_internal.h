@@ -69,7 +69,7 @@ struct FwdSplit {
 };
 hipError_t launch_chunk_fwd_split(const FwdArgs& p, int chunk_len, const FwdSplit& split,
                                   hipStream_t stream);
-// The sequential scan under the same plan (split heads: N = 64 only).
+// The sequential scan under the same plan (N = 32, 64 or 128).
 hipError_t launch_seq_fwd_split(const FwdArgs& p, const FwdSplit& split, hipStream_t stream);
 // Entry states of segments 2 .. nseg-1 of nsplit split heads (N = 64), from
 // segment 0's final state and the maps in `states` (the plan's layout).

@@ -548,6 +548,45 @@ __global__ __launch_bounds__(256) void state_copy_kernel(size_t n4, const float*
             src ? reinterpret_cast<const float4*>(src)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
+// Entry states of the split segments at any N (N = 64 has its own kernel):
+// S_in(s+1) = S_in(s) P(s) + Hm(s) for s = 1 .. nseg-2, in fp32, from
+// S_in(1) = segment 0's final state.  Workgroup (head, q) takes rows
+// 16 q .. 16 q + 15 of one split head through every step; thread t owns row
+// 16 q + t / 16 and columns t % 16 + 16 e.  Each step stages P in LDS.
+template <int N>
+__global__ __launch_bounds__(256) void seg_combine_n_kernel(int nseg, float* __restrict__ states) {
+    constexpr int NB = N / 16;   // workgroups per split head
+    constexpr int E = N / 16;    // columns per thread
+    constexpr size_t NN = (size_t)N * N;
+    __shared__ float Pm[N][N];
+    __shared__ float Sr[16][N];
+    float* const hst = states + (size_t)(blockIdx.x / NB) * 3 * nseg * NN;
+    const int t = threadIdx.x, li = t / 16, c = t % 16;
+    const size_t ro = (size_t)((blockIdx.x % NB) * 16 + li) * N;   // this thread's row
+#pragma unroll
+    for (int e = 0; e < E; ++e) Sr[li][c + 16 * e] = hst[NN + ro + c + 16 * e];
+    for (int sg = 1; sg + 1 < nseg; ++sg) {
+        const float* P = hst + (size_t)(2 * nseg + sg) * NN;
+        __syncthreads();   // the previous step's reads of Pm and writes of Sr are done
+        for (int q = t; q < N * N; q += 256) Pm[q / N][q % N] = P[q];
+        float acc[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] = hst[(size_t)(nseg + sg) * NN + ro + c + 16 * e];
+        __syncthreads();
+        for (int kk = 0; kk < N; ++kk) {
+            const float sik = Sr[li][kk];
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[e] = fmaf(sik, Pm[kk][c + 16 * e], acc[e]);
+        }
+        __syncthreads();   // every row of Sr is read before it is replaced
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            hst[(size_t)(sg + 1) * NN + ro + c + 16 * e] = acc[e];
+            Sr[li][c + 16 * e] = acc[e];
+        }
+    }
+}
+
 // One launch of `units` head runs (whole heads, segments or map runs of the
 // pass, as work_of decodes them), blocks_per_head workgroups each.
 template <typename Tin, int N, int WAVES, int P>
@@ -587,7 +626,7 @@ template <typename Tin, int N>
 hipError_t launch_seq_fwd_n(const FwdArgs& p, const FwdSplit& sp, hipStream_t stream) {
     const int nbh = p.B * p.H;
     const int nsplit = nbh - sp.split_from;
-    if (nsplit < 0 || (nsplit > 0 && (N != 64 || sp.nseg < 2 || sp.seg_len <= 0 ||
+    if (nsplit < 0 || (nsplit > 0 && (sp.nseg < 2 || sp.seg_len <= 0 ||
                                        sp.seg_len % 32 != 0 ||   // whole tape blocks
                                        (long long)(sp.nseg - 1) * sp.seg_len >= p.T || !sp.states)))
         return hipErrorInvalidValue;
@@ -595,7 +634,12 @@ hipError_t launch_seq_fwd_n(const FwdArgs& p, const FwdSplit& sp, hipStream_t st
         p, sp.split_from + (nsplit > 0 ? nsplit * (2 * sp.nseg - 3) : 0), 0, sp, stream);
     if (e != hipSuccess || nsplit == 0) return e;
     if (sp.nseg > 2) {
-        e = launch_seg_combine(nsplit, sp.nseg, sp.states, stream);
+        if constexpr (N == 64) {
+            e = launch_seg_combine(nsplit, sp.nseg, sp.states, stream);
+        } else {
+            seg_combine_n_kernel<N><<<dim3(nsplit * (N / 16)), dim3(256), 0, stream>>>(sp.nseg, sp.states);
+            e = hipGetLastError();
+        }
         if (e != hipSuccess) return e;
     }
     return launch_seq_fwd_pass<Tin, N>(p, nsplit * (sp.nseg - 1), 1, sp, stream);

@@ -108,11 +108,12 @@ def test_split_workspace_sizes(L):
     # T = 64: four segments would start at 0, 32, 64, 96; two fit.
     assert wk.split_workspace_bytes(wk.make_desc(1, 64, 2, 64, wk.WKV7_BF16, 16), 4) == 2 * 3 * 2 * st
     assert wk.split_workspace_bytes(wk.make_desc(1, 32, 2, 64, wk.WKV7_BF16, 16), 4) == 0
-    # The scan splits by maps at N = 64 only.
+    # The scan splits by maps only, at every head size.
     assert wk.split_workspace_bytes(wk.make_desc(1, 1024, 2, 64, wk.WKV7_BF16, 0), 4) == 2 * 3 * 4 * st
     assert wk.split_workspace_bytes(wk.make_desc(1, 1024, 2, 64, wk.WKV7_F32, 0), 4) == 2 * 3 * 4 * st
     assert wk.split_workspace_bytes(wk.make_desc(1, 1024, 2, 64, wk.WKV7_BF16, 0), -4) == 0
-    assert wk.split_workspace_bytes(wk.make_desc(1, 1024, 2, 32, wk.WKV7_BF16, 0), 4) == 0
+    assert wk.split_workspace_bytes(wk.make_desc(1, 1024, 2, 32, wk.WKV7_BF16, 0), 4) == 2 * 3 * 4 * st // 4
+    assert wk.split_workspace_bytes(wk.make_desc(1, 1024, 2, 128, wk.WKV7_F32, 0), 4) == 2 * 3 * 4 * st * 4
 
 
 def test_split_forward_validation(L):
@@ -129,7 +130,8 @@ def test_split_forward_validation(L):
     assert f(ctypes.byref(d0), *args, 4, FAKE, need - 16, None) == wk.WKV7_ERR_WORKSPACE
     assert f(ctypes.byref(d0), *args, -4, FAKE, need, None) == wk.WKV7_ERR_UNSUPPORTED
     d32 = wk.make_desc(1, 256, 1, 32, wk.WKV7_BF16, 0)
-    assert f(ctypes.byref(d32), *args, 4, FAKE, need, None) == wk.WKV7_ERR_UNSUPPORTED
+    assert f(ctypes.byref(d32), *args, 4, None, 0, None) == wk.WKV7_ERR_WORKSPACE
+    assert f(ctypes.byref(d32), *args, -4, None, 0, None) == wk.WKV7_ERR_UNSUPPORTED
     assert f(None, *args, 4, FAKE, need, None) == wk.WKV7_ERR_INVALID_ARG
     de = wk.make_desc(0, 256, 1, 64, wk.WKV7_BF16, 16)
     assert f(ctypes.byref(de), *args, 4, None, 0, None) == wk.WKV7_OK

@@ -1,5 +1,5 @@
 """GPU parity of the sequential scan split in time (wkv7_forward_split with
-chunk_len = 0, by maps, N = 64).
+chunk_len = 0, by maps; N = 32, 64 and 128).
 
 The state update is affine in the state, S <- S M_t + v_t k_t^T with
 M_t = diag(w_t) + a_t b_t^T ("Paper Review: RWKV-7 Goose", The approach), so a
@@ -58,6 +58,30 @@ def test_scan_split_matches_oracle(wk, dtype, segments, T):
     yr, sr = oracle.forward(*inp.tensors(), inp.s0)
     assert_close(y, yr, dtype, f"scan split{segments} {dtype} T={T} y")
     assert_close(sT, sr, dtype, f"scan split{segments} {dtype} T={T} sT")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("N", [32, 128])
+@pytest.mark.parametrize("T", [100, 257])
+def test_scan_split_head_sizes(wk, dtype, N, T):
+    """N = 32 and 128 (four segments: two compositions by the any-N kernel)."""
+    inp = synth.generate(2, T, 3, N, dtype=dtype, seed=580 + T + N, random_s0=True)
+    assert _plan_bytes(wk, inp, 4) > 0
+    y, sT, _ = _run(wk, inp, 4)
+    yr, sr = oracle.forward(*inp.tensors(), inp.s0)
+    assert_close(y, yr, dtype, f"scan split N={N} {dtype} T={T} y")
+    assert_close(sT, sr, dtype, f"scan split N={N} {dtype} T={T} sT")
+
+
+@pytest.mark.parametrize("N", [32, 128])
+def test_scan_split_head_sizes_auto(wk, N):
+    """The library's plan at few heads: B=1, T=2048, H=4."""
+    inp = synth.generate(1, 2048, 4, N, dtype="bf16", seed=590 + N, random_s0=True)
+    assert _plan_bytes(wk, inp, 0) > 0
+    y, sT, _ = _run(wk, inp, 0)
+    yr, sr = oracle.forward(*inp.tensors(), inp.s0)
+    assert_close(y, yr, "bf16", f"scan split auto N={N} y")
+    assert_close(sT, sr, "bf16", f"scan split auto N={N} sT")
 
 
 @pytest.mark.parametrize("segments", [2, 4])
