@@ -171,3 +171,17 @@ def test_scan_split_empty_sequence(wk):
     y, sT, _ = _run(wk, inp, 4)
     assert y.shape == (1, 0, 2, 64)
     np.testing.assert_array_equal(sT, inp.s0)
+
+
+@pytest.mark.parametrize("N", [32, 64, 128])
+def test_scan_split_sixteen_segments_fp32(wk, N):
+    """The most segments a plan takes (16 of 64 tokens, the last 40): fourteen
+    fp32 compositions in a row, held to the fp32 tolerance."""
+    inp = synth.generate(1, 1000, 2, N, dtype="fp32", seed=600 + N, random_s0=True)
+    B, T, H, _ = inp.r.shape
+    st = N * N * 4
+    assert _plan_bytes(wk, inp, 16) == B * H * 3 * 16 * st
+    y, sT, _ = _run(wk, inp, 16)
+    yr, sr = oracle.forward(*inp.tensors(), inp.s0)
+    assert_close(y, yr, "fp32", f"scan split 16 N={N} y")
+    assert_close(sT, sr, "fp32", f"scan split 16 N={N} sT")
