@@ -5,7 +5,7 @@
 // state S0, removal read-outs Z, read-out adjoint dY and the adjoint dS of
 // the chunk's exit state:
 //
-//   dZ  = Arb^T dY + Bb dS^T            dX = Tm^T dZ
+//   dZ  = Arb^T dY + Bb dS^T            dX = Tm^T dZ = (Tm^T Bb) dS^T + (Arb Tm)^T dY
 //   dV  = Aak^T dX + Ark^T dY + Kb dS^T
 //   dS0 = dS diag(G_L) + dY^T Rt + dX^T At       (adjoint carried to the previous chunk)
 //   dAab = tril_-1(dX Z^T)  dAak = tril_-1(dX V^T)
@@ -22,9 +22,11 @@
 // passes:
 //   pass 1 (one workgroup per head, chunks last to first): the adjoint chain,
 //     with the forward's producer/consumer structure -- producers rebuild the
-//     chunk's decay products, scaled vectors and 16x16 tiles, a ninth wave the
-//     triangular inverse; consumers own 16 value rows each of dS^T in
-//     accumulator tiles and emit dv, dX and the chunk's incoming dS;
+//     chunk's decay products, scaled vectors and 16x16 tiles, two more waves
+//     the triangular inverse (alternate chunks, each solve over two
+//     intervals) and the state-independent factors Tm^T Bb (over Bb) and
+//     (Arb Tm)^T; consumers own 16 value rows each of dS^T in accumulator
+//     tiles and emit dv, dX and the chunk's incoming dS;
 //   pass 2 (one independent wave per chunk and key block, no barriers): every
 //     per-key gradient, from pass 1's dX and dS and the forward's tape (entry
 //     states S0 and read-outs Z).
@@ -54,26 +56,6 @@ __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// (I - A)^-1 in accumulator layout (lane (g, l16) register q holds
-// T[4g+q][l16]) for strictly lower triangular A, as the doubling product
-// with left factors: P <- P + A^(2k) P, each A^(2k) fed through the registers
-// of its transpose.
-__device__ __forceinline__ f32x4 unit_lower_inverse_C(f32x4 A, f32x4 AT, int g, int l16) {
-    const f32x4 z = zero4();
-    const f32x4 A2 = mfma16(cvt4(AT), cvt4(A), z);
-    const f32x4 A2T = mfma16(cvt4(A), cvt4(AT), z);
-    const f32x4 A4 = mfma16(cvt4(A2T), cvt4(A2), z);
-    const f32x4 A4T = mfma16(cvt4(A2), cvt4(A2T), z);
-    const f32x4 A8T = mfma16(cvt4(A4), cvt4(A4T), z);
-    f32x4 P = A;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) P[q] += (4 * g + q == l16) ? 1.f : 0.f;
-    P = mfma16(cvt4(A2T), cvt4(P), P);   // P += A^2 P
-    P = mfma16(cvt4(A4T), cvt4(P), P);
-    P = mfma16(cvt4(A8T), cvt4(P), P);
-    return P;
-}
-
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 struct Raw {
     u32x4 x[3];
@@ -83,23 +65,34 @@ struct Raw {
 // Pass 1: the adjoint chain.
 // =============================================================================
 
-constexpr int kP1Threads = 576;   // 4 producer, 4 consumer waves, 1 inverse wave
+constexpr int kP1Threads = 640;   // 4 producer, 4 consumer, 2 inverse waves
+constexpr int kP1Slots = 4;
 enum { P1_R = 0, P1_W = 1, P1_K = 2, P1_A = 3, P1_B = 4, P1_DY = 5 };
-enum { TILE_T = 0, TILE_RB = 1, TILE_AK = 2, TILE_RK = 3 };
+// Tile images in a slot.  TILE_RB/TILE_RBL: hi and lo parts of Arb^T in
+// accumulator layout (Arb's A-operand image), from MW, TILE_RB replaced by INV
+// with the A-operand image of (Arb Tm)^T; TILE_AK, TILE_RK: the A-operand images
+// of Aak^T, Ark^T, from MW.
+enum { TILE_RB = 0, TILE_RBL = 1, TILE_AK = 2, TILE_RK = 3 };
 
 // Rows [t][j] (the chain reads At, Rt and dy transposed, which gives the
 // matrix-core operand layouts directly) and images: register contents stored
 // lane by lane (8 bytes per lane, read back by the same lane index).
 struct P1Slot {
-    bf16_t At[kL][kRow], Rt[kL][kRow], Bh[kL][kRow], Kh[kL][kRow];  // E -> MW, chain
-    bf16_t Bb[kL][kRow], Kb[kL][kRow], dY[kL][kRow];                // E -> chain
+    bf16_t At[kL][kRow], Rt[kL][kRow];                  // E -> MW, INV, chain
+    bf16_t Bb[kL][kRow];                                // E -> INV; Tm^T Bb from INV -> chain
+    bf16_t Kb[kL][kRow], dY[kL][kRow];                  // E -> chain
     float gL[kN];         // G_L of key 16 jt + 4 g + q at word 16 g + 4 jt + q
-    uint2 tiles[4][64];   // MW -> chain: A-operand register images of Tm^T, Arb^T, Aak^T, Ark^T
+    uint2 tiles[4][64];
+};
+// Bh and Kh, read only in the interval after E.
+struct P1SlotBK {
+    bf16_t Bh[kL][kRow], Kh[kL][kRow];
 };
 
 struct __align__(16) P1Smem {
     bf16_t raw[2][6][kL][kRow];   // r, w, k, a, b, dy of two chunks
-    P1Slot sl[3];
+    P1Slot sl[kP1Slots];
+    P1SlotBK bk[2];
     bf16_t dXs[2][kL][kRow];      // [t][i]
     bf16_t dVs[2][kL][kRow];      // [t][i]
     bf16_t dSs[2][kN][kRow];      // the adjoint leaving the chunk as [j][i] (kept per 32 tokens)
@@ -124,7 +117,7 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
     const int wave = tid >> 6;
     const bool producer = wave < 4;
     const bool consumer = wave >= 4 && wave < 8;
-    const bool inverter = wave == 8;
+    const bool inverter = wave >= 8;
     const int rtid = tid & 255;
     const int lane = tid & 63, wp = (tid >> 6) & 3;
     const int l16 = lane & 15, g = lane >> 4;
@@ -137,8 +130,9 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
     // Interval it handles chunks from the last one down; negative chunk
     // indices are all-padding, for which every stage is the identity.
     auto chunk_of = [&](int it) __attribute__((always_inline)) { return nch - 1 - it; };
-    // (chunk indices reach -6 in the padding intervals)
-    auto slot_of = [&](int c) __attribute__((always_inline)) { return (c + 9) % 3; };
+    // (negative chunk indices in the padding intervals: two's complement & keeps
+    // them in range)
+    auto slot_of = [&](int c) __attribute__((always_inline)) { return c & (kP1Slots - 1); };
 
     // The per-key pass that follows takes its blocks from a queue: start it empty.
     if (blockIdx.x == 0 && tid == 0) {
@@ -216,6 +210,7 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
     };
     auto stage_E = [&](int c, const ERaw& er) __attribute__((always_inline)) {
         P1Slot& s = sm.sl[slot_of(c)];
+        P1SlotBK& bk = sm.bk[c & 1];
         const uint2* raw6 = er.v;
         float X[6][4];
 #pragma unroll
@@ -245,25 +240,28 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
         const bf16x4 atb = cvt4(at), rtb = cvt4(rt);
         if (kAB) *reinterpret_cast<bf16x4*>(&s.At[l16][j0]) = atb;
         *reinterpret_cast<bf16x4*>(&s.Rt[l16][j0]) = rtb;
-        if (kAB) *reinterpret_cast<bf16x4*>(&s.Bh[l16][j0]) = cvt4(bh4);
-        *reinterpret_cast<bf16x4*>(&s.Kh[l16][j0]) = cvt4(kh4);
+        if (kAB) *reinterpret_cast<bf16x4*>(&bk.Bh[l16][j0]) = cvt4(bh4);
+        *reinterpret_cast<bf16x4*>(&bk.Kh[l16][j0]) = cvt4(kh4);
         if (kAB) *reinterpret_cast<bf16x4*>(&s.Bb[l16][j0]) = cvt4(bb4);
         *reinterpret_cast<bf16x4*>(&s.Kb[l16][j0]) = cvt4(kb4);
         *reinterpret_cast<uint2*>(&s.dY[l16][j0]) = raw6[P1_DY];
         if (l16 == kL - 1) *reinterpret_cast<float4*>(&s.gL[16 * g + 4 * wp]) = make_float4(gt[0], gt[1], gt[2], gt[3]);
     };
 
-    // ---- MW (producer): one 16x16 tile per wave, as an A-operand image ------------
-    // Wave p = 1..3 forms tile p from the rows of X = (At or Rt) and Y = (Bh or
-    // Kh): Arb (1), Aak (2), Ark (3); tile 0 (Aab, then its inverse Tm) comes
-    // from the inverse wave.
+    // ---- MW (producer): one 16x16 tile per wave ---------------------------------
+    // Wave p = 1..3 forms a tile from the rows of X = (At or Rt) and Y = (Bh or
+    // Kh): Arb (1), Aak (2), Ark (3); Aab and its inverse come from the inverse
+    // waves.  Waves 2, 3 form [t][s] = X_t . Y_s, whose accumulator registers are
+    // the A-operand images of Aak^T, Ark^T; wave 1 forms [s][t] (Arb's A-operand
+    // image, which the chain multiplies by Tm) in hi and lo parts.
     struct MWIn {
         bf16x8 xv[2], yv[2];
     };
     auto read_MW = [&](int c) __attribute__((always_inline)) -> MWIn {
         const P1Slot& s = sm.sl[slot_of(c)];
+        const P1SlotBK& bk = sm.bk[c & 1];
         const bf16_t(*Xr)[kRow] = (wp & 1) ? s.Rt : s.At;
-        const bf16_t(*Yr)[kRow] = (wp & 2) ? s.Kh : s.Bh;
+        const bf16_t(*Yr)[kRow] = (wp & 2) ? bk.Kh : bk.Bh;
         MWIn in;
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
@@ -275,45 +273,74 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
     auto stage_MW = [&](int c, const MWIn& in) __attribute__((always_inline)) {
         P1Slot& s = sm.sl[slot_of(c)];
         f32x4 P = zero4();
+        if (wp == 1) {
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2) P = mfma32(in.yv[k2], in.xv[k2], P);   // [s][t]
+#pragma unroll
+            for (int q = 0; q < 4; ++q) P[q] = (4 * g + q <= l16) ? P[q] : 0.f;   // s <= t
+            const Split4 rb = split4(P);
+            s.tiles[TILE_RB][lane] = __builtin_bit_cast(uint2, rb.hi);
+            s.tiles[TILE_RBL][lane] = __builtin_bit_cast(uint2, rb.lo);
+            return;
+        }
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) P = mfma32(in.xv[k2], in.yv[k2], P);   // [t][s] = X_t . Y_s
-        const bool diag = (wp & 1) != 0;   // Arb, Ark keep the diagonal
+        const bool diag = wp == 3;   // Ark keeps the diagonal
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int m = 4 * g + q, n = l16;
             P[q] = (n < m || (diag && n == m)) ? P[q] : 0.f;
         }
         // Accumulator registers of X fed as an A operand stand for X^T.
-        s.tiles[wp][lane] = __builtin_bit_cast(uint2, cvt4(P));
+        s.tiles[wp == 2 ? TILE_AK : TILE_RK][lane] = __builtin_bit_cast(uint2, cvt4(P));
     };
-    // ---- INV (inverse wave): Aab and Tm = (I - Aab)^-1 for tile 0 ----------------
-    // Wave 8 forms Aab from At and Bh (as MW would with wp = 0) and inverts it,
-    // keeping the long dependent MFMA chain of the inverse off the producers.
-    auto stage_INV = [&](int c) __attribute__((always_inline)) {
-        P1Slot& s = sm.sl[slot_of(c)];
+    // ---- INV (inverse waves): Aab, Tm = (I - Aab)^-1, Tm^T Bb, (Arb Tm)^T -------
+    // In the interval after E(c) a wave forms Aab from At and Bh, the inverses of
+    // its 4x4 diagonal blocks and N = Td L (wkv7_mfma.h); in the next it joins
+    // them into Tm and applies Tm, as hi and lo bf16 parts, to the factors of
+    // dX = (Tm^T Bb) dS^T + (Arb Tm)^T dY (the
+    // transpose of the forward's Z = (Tm At) S0^T + (Tm Aak) V, with the same
+    // cancellations kept inside these products):
+    //   the accumulator tile of Bb^T[keys 16 jt ..] Tm holds (Tm^T Bb)[l16][16 jt
+    //     + 4 g + q] -- its row layout, written over the same columns of Bb;
+    //   Arb Tm from Arb's A-operand image (hi and lo), whose accumulator
+    //     registers are the A-operand image of (Arb Tm)^T.
+    auto inv_begin = [&](int c) __attribute__((always_inline)) -> BlockInverse {
+        const P1Slot& s = sm.sl[slot_of(c)];
+        const P1SlotBK& bk = sm.bk[c & 1];
         bf16x8 xv[2], yv[2];
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
             xv[k2] = ld8(&s.At[l16][32 * k2 + 8 * g]);
-            yv[k2] = ld8(&s.Bh[l16][32 * k2 + 8 * g]);
+            yv[k2] = ld8(&bk.Bh[l16][32 * k2 + 8 * g]);
         }
-        f32x4 P = zero4(), PT = zero4();
+        f32x4 P = zero4();
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-            P = mfma32(xv[k2], yv[k2], P);     // [t][s]
-            PT = mfma32(yv[k2], xv[k2], PT);   // [s][t]
-        }
+        for (int k2 = 0; k2 < 2; ++k2) P = mfma32(xv[k2], yv[k2], P);   // [t][s]
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            P[q] = (l16 < 4 * g + q) ? P[q] : 0.f;
-            PT[q] = (4 * g + q < l16) ? PT[q] : 0.f;
+        for (int q = 0; q < 4; ++q) P[q] = (l16 < 4 * g + q) ? P[q] : 0.f;
+        return unit_lower_inverse_begin(P, g, l16);
+    };
+    auto inv_end = [&](int c, const BlockInverse& bi) __attribute__((always_inline)) {
+        P1Slot& s = sm.sl[slot_of(c)];
+        bf16x4 bbT[4];
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) bbT[jt] = ld4_tr(tr_addr(&s.Bb[0][16 * jt], kRow, g, l16));
+        const bf16x4 rbh = __builtin_bit_cast(bf16x4, s.tiles[TILE_RB][lane]);
+        const bf16x4 rbl = __builtin_bit_cast(bf16x4, s.tiles[TILE_RBL][lane]);
+        const Split4 tm = split4(unit_lower_inverse_cols_end(bi));
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+            const f32x4 d = mfma16(bbT[jt], tm.hi, mfma16(bbT[jt], tm.lo, zero4()));
+            *reinterpret_cast<bf16x4*>(&s.Bb[l16][16 * jt + 4 * g]) = cvt4(d);
         }
-        s.tiles[TILE_T][lane] = __builtin_bit_cast(uint2, cvt4(unit_lower_inverse_C(P, PT, g, l16)));
+        const f32x4 e = mfma16(rbh, tm.hi, mfma16(rbl, tm.hi, mfma16(rbh, tm.lo, zero4())));
+        s.tiles[TILE_RB][lane] = __builtin_bit_cast(uint2, cvt4(e));
     };
 
     // ---- chain (consumer): value rows `col` of the adjoint ------------------------
     struct CIn {
-        bf16x4 TmT, ArbT, AakT, ArkT, dY;
+        bf16x4 RbT, AakT, ArkT, dY;
         bf16x8 bb[2], kb[2];
         bf16x4 rtT[4], atT[4];
         float gl;   // G_L of key 16 jt + 4 g + q sits in lane 4 jt + q of row g
@@ -322,15 +349,14 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
         const P1Slot& s = sm.sl[slot_of(c)];
         CIn in;
         if (kAB) {
-            in.TmT = __builtin_bit_cast(bf16x4, s.tiles[TILE_T][lane]);
-            in.ArbT = __builtin_bit_cast(bf16x4, s.tiles[TILE_RB][lane]);
+            in.RbT = __builtin_bit_cast(bf16x4, s.tiles[TILE_RB][lane]);   // (Arb Tm)^T
             in.AakT = __builtin_bit_cast(bf16x4, s.tiles[TILE_AK][lane]);
         }
         in.ArkT = __builtin_bit_cast(bf16x4, s.tiles[TILE_RK][lane]);
         in.dY = ld4_tr(tr_addr(&s.dY[0][16 * wp], kRow, g, l16));   // [t][i] as a B operand
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
-            if (kAB) in.bb[k2] = ld4x2(&s.Bb[l16][32 * k2 + 4 * g]);
+            if (kAB) in.bb[k2] = ld4x2(&s.Bb[l16][32 * k2 + 4 * g]);   // Tm^T Bb
             in.kb[k2] = ld4x2(&s.Kb[l16][32 * k2 + 4 * g]);
         }
 #pragma unroll
@@ -345,21 +371,21 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
         bf16x4 dSb[4];
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) dSb[jt] = cvt4(dSt[jt]);
+        // dX = Tm^T dZ = (Tm^T Bb) dS^T + (Arb Tm)^T dY with both factors from INV.
         // Partial sums of the two MFMA shapes meet on the vector ALU (add4).
-        // (a = b = 0: Bb, Arb, Aak vanish, so dZ = dX = 0 and only the Kb and
-        // Ark terms of dV remain.)
-        f32x4 dZ = zero4(), dVk = zero4();
+        // (a = b = 0: Bb, Arb, Aak vanish, so dX = 0 and only the Kb and Ark
+        // terms of dV remain.)
+        f32x4 dXs = zero4(), dVk = zero4();
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
             const bf16x8 ds8 = cat8(dSb[2 * k2], dSb[2 * k2 + 1]);
-            if (kAB) dZ = mfma32(in.bb[k2], ds8, dZ);
+            if (kAB) dXs = mfma32(in.bb[k2], ds8, dXs);
             dVk = mfma32(in.kb[k2], ds8, dVk);
         }
         bf16x4 dXb = {};
         f32x4 dV = zero4();
         if (kAB) {
-            dZ = add4(dZ, mfma16(in.ArbT, in.dY, zero4()));
-            dXb = cvt4(mfma16(in.TmT, cvt4(dZ), zero4()));
+            dXb = cvt4(add4(dXs, mfma16(in.RbT, in.dY, zero4())));
             dV = mfma16(in.AakT, dXb, zero4());
         }
         dV = mfma16(in.ArkT, in.dY, dV);
@@ -408,10 +434,10 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
     };
 
     {
-        // Intervals 0 .. nch+2 carry real work; the count is rounded up to a
+        // Intervals 0 .. nch+3 carry real work; the count is rounded up to a
         // multiple of three for the unrolled producer loop.  The extra intervals
         // see only all-padding chunks (negative indices: identity, nothing stored).
-        const int n_it = (nch + 5) / 3 * 3;
+        const int n_it = (nch + 6) / 3 * 3;
         // Each role runs its own loop over the same number of intervals (one
         // barrier each), so the compiler sees only loads on the producer side
         // and only stores on the consumer side; with both kinds in one loop it
@@ -450,24 +476,33 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
         } else if (inverter) {
             __builtin_amdgcn_s_setprio(2);
             __syncthreads();
-            // Interval it: the inverse of chunk_of(it-1), read by the chain in
-            // interval it+1.
+            // chunk_of(j) belongs to wave 8 + (j & 1), which starts its inverse in
+            // interval j + 1 (after E) and finishes it, with the dX factors, in
+            // interval j + 2 (the chain reads them in interval j + 3): one half
+            // per wave and interval, `bi` carrying an inverse across one barrier.
+            const int par = wave & 1;
+            BlockInverse bi{zero4(), zero4(), zero4()};
             for (int it = 0; it < n_it; ++it) {
-                if (kAB && it >= 1) stage_INV(chunk_of(it - 1));
+                if (kAB && it >= 1) {
+                    if (((it - 1) & 1) == par)
+                        bi = inv_begin(chunk_of(it - 1));
+                    else if (it >= 2)
+                        inv_end(chunk_of(it - 2), bi);
+                }
                 __syncthreads();
             }
         } else {
             // The chain is the critical path: its waves issue first (then the
-            // inverse wave, then the producers) when several are ready.
+            // inverse waves, then the producers) when several are ready.
             __builtin_amdgcn_s_setprio(3);
             __syncthreads();
-            // Interval it: the chain on chunk_of(it-2), the stores of chunk_of(it-3).
+            // Interval it: the chain on chunk_of(it-3), the stores of chunk_of(it-4).
             for (int it = 0; it < n_it; ++it) {
-                if (it >= 2) {
-                    const CIn ci = read_C(chunk_of(it - 2));
-                    stage_C(chunk_of(it - 2), ci);
+                if (it >= 3) {
+                    const CIn ci = read_C(chunk_of(it - 3));
+                    stage_C(chunk_of(it - 3), ci);
                 }
-                if (it >= 3) store_out(chunk_of(it - 3));
+                if (it >= 4) store_out(chunk_of(it - 4));
                 __syncthreads();
             }
         }

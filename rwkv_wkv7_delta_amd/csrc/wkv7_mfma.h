@@ -120,26 +120,111 @@ __device__ __forceinline__ bf16x4 ld4_tr(const bf16_t* p) {
     return __builtin_bit_cast(bf16x4, r);
 }
 
-// (I - A)^-1 for a strictly lower triangular 16x16 A (so A^16 = 0) as the
-// doubling product (I + A)(I + A^2)(I + A^4)(I + A^8), all on bf16 MFMA with
-// fp32 accumulation.  Inputs are the accumulator tiles of A and A^T; C-layout
-// registers fed as an A operand stand for the transpose of their matrix, so
-// the chain needs no data movement.  Returns T^T in C layout, i.e. lane
-// (g, l16) register q holds T[l16][4g+q] -- exactly T's A-operand layout.
-__device__ __forceinline__ f32x4 unit_lower_inverse_T(f32x4 A, f32x4 AT, int g, int l16) {
-    const f32x4 z = zero4();
-    const f32x4 A2 = mfma16(cvt4(AT), cvt4(A), z);     // A A
-    const f32x4 A2T = mfma16(cvt4(A), cvt4(AT), z);    // A^T A^T
-    const f32x4 A4 = mfma16(cvt4(A2T), cvt4(A2), z);
-    const f32x4 A4T = mfma16(cvt4(A2), cvt4(A2T), z);
-    const f32x4 A8 = mfma16(cvt4(A4T), cvt4(A4), z);
-    f32x4 P = AT;                                      // (I + A)^T
+__device__ __forceinline__ f32x4 unpack4(bf16x4 x) {
+    const u32x2_t u = __builtin_bit_cast(u32x2_t, x);
+    f32x4 o;
+    o[0] = __uint_as_float(u[0] << 16);
+    o[1] = __uint_as_float(u[0] & 0xFFFF0000u);
+    o[2] = __uint_as_float(u[1] << 16);
+    o[3] = __uint_as_float(u[1] & 0xFFFF0000u);
+    return o;
+}
+
+// An fp32 tile as two bf16 operands, hi = bf16(x) and lo = bf16(x - hi): a
+// product summed as hi*hi' + hi*lo' + lo*hi' on the matrix core carries about
+// 16 significant bits of each factor instead of 8.
+struct Split4 {
+    bf16x4 hi, lo;
+};
+__device__ __forceinline__ Split4 split4(f32x4 x) {
+    Split4 s;
+    s.hi = cvt4(x);
+    s.lo = cvt4(x - unpack4(s.hi));
+    return s;
+}
+
+// D + X Y from hi and lo bf16 parts of both factors (X as its A-operand image,
+// Y as a B operand): hi*hi + hi*lo + lo*hi, the small terms first.
+__device__ __forceinline__ f32x4 mul3(const Split4& x, const Split4& y, f32x4 d) {
+    return mfma16(x.hi, y.hi, mfma16(x.hi, y.lo, mfma16(x.lo, y.hi, d)));
+}
+
+// Lane p of each group of four lanes (DPP quad_perm [p, p, p, p]).
+template <int p>
+__device__ __forceinline__ float quad_bcast(float x) {
+    return __builtin_amdgcn_update_dpp(0.0f, x, p * 0x55, 0xF, 0xF, false);
+}
+
+// T = (I - A)^-1 for a strictly lower triangular 16x16 A, accurate to about
+// 1e-5 relative to its largest entry, from four products on the matrix core:
+//   Td = the inverses of the four 4x4 diagonal blocks of I - A, in fp32;
+//   L  = A without its diagonal blocks;  N = Td L, strictly block-lower with
+//        four block rows, so N^4 = 0 and
+//   T  = (I - N)^-1 Td = (I + N)(I + N^2) Td.
+// The direct doubling product (I + A)(I + A^2)(I + A^4)(I + A^8) is exact in
+// exact arithmetic too, but its partial products hold binomial coefficients of
+// up to C(15, 7) = 6435 when removal keys repeat or correlate inside a chunk
+// (A[t][s] close to -1 for every s < t), and rounding those loses the O(1)
+// result entirely.  Here the only large-sum cancellations are inside the
+// 4x4 blocks, which are solved in fp32, and N's powers stay of order one; the
+// products take hi and lo bf16 parts of both factors (mul3).
+//
+// In the accumulator layout (lane (g, l16) register q holds A[4g+q][l16]) the
+// diagonal block of rows 4g.. sits in lanes l16 = 4g..4g+3 of row group g,
+// one DPP quad, lane c holding its column c.  So every lane of that quad
+// solves with the same six below-diagonal entries (quad broadcasts): lane c
+// gets column c of the block's inverse (its accumulator registers, Td) and row
+// c (the accumulator registers of Td^T).
+struct BlockInverse {
+    f32x4 Td, N, NT;   // accumulator tiles of Td, N = Td L and N^T
+};
+__device__ __forceinline__ BlockInverse unit_lower_inverse_begin(f32x4 A, int g, int l16) {
+    const float a10 = quad_bcast<0>(A[1]), a20 = quad_bcast<0>(A[2]), a30 = quad_bcast<0>(A[3]);
+    const float a21 = quad_bcast<1>(A[2]), a31 = quad_bcast<1>(A[3]);
+    const float a32 = quad_bcast<2>(A[3]);
+    const int c = l16 & 3;
+    const float e0 = c == 0 ? 1.f : 0.f, e1 = c == 1 ? 1.f : 0.f;
+    const float e2 = c == 2 ? 1.f : 0.f, e3 = c == 3 ? 1.f : 0.f;
+    // column c of the block inverse: x_q = [q == c] + sum_{p<q} A[q][p] x_p
+    const float x0 = e0;
+    const float x1 = fmaf(a10, x0, e1);
+    const float x2 = fmaf(a21, x1, fmaf(a20, x0, e2));
+    const float x3 = fmaf(a32, x2, fmaf(a31, x1, fmaf(a30, x0, e3)));
+    // row c: y_q = [q == c] + sum_{p>q} y_p A[p][q]
+    const float y3 = e3;
+    const float y2 = fmaf(y3, a32, e2);
+    const float y1 = fmaf(y3, a31, fmaf(y2, a21, e1));
+    const float y0 = fmaf(y3, a30, fmaf(y2, a20, fmaf(y1, a10, e0)));
+    const bool diag = (l16 >> 2) == g;
+    BlockInverse b;
+    f32x4 TdT, L;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) P[q] += (4 * g + q == l16) ? 1.f : 0.f;
-    P = mfma16(cvt4(A2), cvt4(P), P);                  // P^T += (A^2)^T P^T
-    P = mfma16(cvt4(A4), cvt4(P), P);
-    P = mfma16(cvt4(A8), cvt4(P), P);
-    return P;
+    for (int q = 0; q < 4; ++q) L[q] = diag ? 0.f : A[q];
+    b.Td[0] = diag ? x0 : 0.f; b.Td[1] = diag ? x1 : 0.f; b.Td[2] = diag ? x2 : 0.f; b.Td[3] = diag ? x3 : 0.f;
+    TdT[0] = diag ? y0 : 0.f; TdT[1] = diag ? y1 : 0.f; TdT[2] = diag ? y2 : 0.f; TdT[3] = diag ? y3 : 0.f;
+    const Split4 sL = split4(L), sTdT = split4(TdT);
+    b.N = mul3(sTdT, sL, zero4());    // Td L   (Td^T's registers are Td's A-operand image)
+    b.NT = mul3(sL, sTdT, zero4());   // L^T Td^T
+    return b;
+}
+// The accumulator tile of T^T (= T's A-operand image: lane (g, l16) register q
+// holds T[l16][4g+q]): T^T = Td^T (I + (N^T)^2)(I + N^T).
+__device__ __forceinline__ f32x4 unit_lower_inverse_rows_end(const BlockInverse& b, int g, int l16) {
+    const Split4 sN = split4(b.N), sNT = split4(b.NT);
+    const f32x4 N2 = mul3(sNT, sN, zero4());             // N N
+    f32x4 W1 = b.NT;                                      // I + N^T
+#pragma unroll
+    for (int q = 0; q < 4; ++q) W1[q] += (4 * g + q == l16) ? 1.f : 0.f;
+    const f32x4 W2 = mul3(split4(N2), split4(W1), W1);   // W1 + (N^T)^2 W1
+    return mul3(split4(b.Td), split4(W2), zero4());      // Td^T W2
+}
+// The accumulator tile of T (= T^T's A-operand image: lane (g, l16) register q
+// holds T[4g+q][l16]): T = (I + N)(I + N^2) Td.
+__device__ __forceinline__ f32x4 unit_lower_inverse_cols_end(const BlockInverse& b) {
+    const Split4 sN = split4(b.N), sNT = split4(b.NT);
+    const f32x4 NT2 = mul3(sN, sNT, zero4());             // N^T N^T
+    const f32x4 V2 = mul3(split4(NT2), split4(b.Td), b.Td);   // Td + N^2 Td
+    return mul3(sNT, split4(V2), V2);                     // V2 + N V2
 }
 
 }  // namespace wkv7
