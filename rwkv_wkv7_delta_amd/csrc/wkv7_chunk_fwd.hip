@@ -12,7 +12,7 @@
 //   Arb = tril_0(Rt Bh^T),  Ark = tril_0(Rt Kh^T)        (L x L)
 //   Tm  = (I - Aab)^-1                                   (unit lower triangular)
 //   X   = At S0^T + Aak V
-//   Z   = Tm X                       (row t of Z is z_t = S_{t-1} a_t)
+//   Z   = Tm X = (Tm At) S0^T + (Tm Aak) V   (row t of Z is z_t = S_{t-1} a_t)
 //   Y   = Rt S0^T + Arb Z + Ark V    (row t of Y is y_t)
 //   S_L^T = diag(G_L) S0^T + Kb^T V + Bb^T Z
 //
@@ -24,17 +24,28 @@
 //         consumers read Bb, Kb and v transposed (ds_read_b64_tr_b16), which
 //         is the layout their matrix-core products take;
 //     MW  one 16x16 tile each on waves 1..3: Aak, Arb, Ark.
-//   A ninth wave forms Aab and its triangular inverse Tm (a long chain of
-//   dependent matrix-core products, kept off the producers' path).
+//   Two more waves form Aab and its triangular inverse Tm = (I - Aab)^-1
+//   (4x4 diagonal blocks in fp32, joined on the matrix core: wkv7_mfma.h),
+//   off the producers' path: wave 8 for even chunks, wave 9 for odd ones, each
+//   inverse spread over two intervals.
+//   The second interval also applies Tm to the state-independent factors of
+//   Z: At' = Tm At (written over At) and Aak' = Tm Aak, from hi and lo bf16
+//   parts of Tm and Aak (At is exact in bf16).  Applying Tm to the factors
+//   instead of to X = At S0^T + Aak V keeps the cancellation that Tm X performs
+//   (rows of X grow along a chunk whose removal keys repeat, while Z stays of
+//   the order of v) inside those products, and the consumers' chain one
+//   product shorter.
 //   Consumer waves p = 0..3 own value rows 16p..16p+15 of the state, held as
 //   S^T in four 16x16 fp32 accumulator tiles (key blocks); an accumulator
 //   tile feeds the next product directly as its B operand (wkv7_mfma.h), so
-//   every state-dependent product (X, Z, Y, the state update) is a left
+//   every state-dependent product (Z, Y, the state update) is a left
 //   multiplication that reads the state straight from registers.
 // The work is software-pipelined with ONE barrier per chunk: in interval
-// `it` the producers run E(it) and MW(it-1) while the consumers run the
-// state chain of chunk it-2, storing its y (and tape) directly; chunk factors pass
-// through three rotating LDS slots.  Each role needs few enough registers for
+// `it` the producers run E(it) and MW(it-1), the inverse waves the first half
+// of chunk it-1's solve and the second half of chunk it-2's, and the
+// consumers the state chain of chunk it-3, storing its y (and tape); chunk
+// factors pass through four rotating LDS slots (Bh and Kh, read only in the
+// interval after E, through two).  Each role needs few enough registers for
 // two waves per SIMD, so a consumer's MFMA chain interleaves with a
 // producer's VALU work.  Raw token loads run three intervals ahead in a
 // register ring.  Chunks beyond T are all-padding (w = 1, everything else 0),
@@ -50,29 +61,40 @@ namespace wkv7 {
 namespace {
 
 constexpr int kL = 16;
-constexpr int kThreads = 576;   // 4 producer, 4 consumer waves, 1 inverse wave
+constexpr int kThreads = 640;   // 4 producer, 4 consumer, 2 inverse waves
 // LDS row stride (bf16 elements).  A 64-wide row would be exactly one sweep
 // of the four-byte banks, so the row reads below (16 lanes on 16 different
 // rows, same columns) would all hit the same banks; 144-byte rows spread them.
 constexpr int kRow = kN + 8;    // rows of 64 elements
 
 enum { RAW_R = 0, RAW_W = 1, RAW_K = 2, RAW_A = 3, RAW_B = 4, RAW_V = 5 };
-enum { TILE_T = 0, TILE_AK = 1, TILE_RB = 2, TILE_RK = 3 };
+// Tile images in a slot.  TILE_AK/TILE_AKL: hi and lo parts of Aak in
+// accumulator layout (Aak[4g+q][l16], the A-operand image of Aak^T), from MW;
+// INV replaces TILE_AK by the A-operand image of Aak' = Tm Aak.  TILE_RB,
+// TILE_RK: A-operand images of Arb, Ark, from MW.
+enum { TILE_AK = 0, TILE_AKL = 1, TILE_RB = 2, TILE_RK = 3 };
+constexpr int kSlots = 4;
 
 // Everything one chunk passes from the producers to the consumers: rows
 // [t][j] (the consumers read Bb, Kb and V transposed, which gives them the
 // matrix-core operand layouts directly) and "images", register contents
 // stored lane by lane (8 bytes per lane, read back by the same lane index).
 struct Slot {
-    bf16_t At[kL][kRow], Rt[kL][kRow], Bh[kL][kRow], Kh[kL][kRow];  // E -> MW, ST
-    bf16_t Bb[kL][kRow], Kb[kL][kRow], V[kL][kRow];                  // E -> ST
+    bf16_t At[kL][kRow];            // E -> MW, INV; At' = Tm At from INV -> ST
+    bf16_t Rt[kL][kRow];            // E -> MW, ST
+    bf16_t Bb[kL][kRow], Kb[kL][kRow], V[kL][kRow];   // E -> ST
     float gL[kN];   // E -> ST: G_L of key 16 jt + 4 g + q at word 16 g + 4 jt + q
-    uint2 tiles[4][64];   // MW -> ST: A-operand images of Tm, Aak, Arb, Ark (tile p from wave p)
+    uint2 tiles[4][64];
+};
+// Bh and Kh, read only in the interval after E.
+struct SlotBK {
+    bf16_t Bh[kL][kRow], Kh[kL][kRow];
 };
 
 struct __align__(16) FwdSmem {
     bf16_t raw[2][6][kL][kRow];   // r, w, k, a, b, v of two chunks (bf16 bits)
-    Slot sl[3];
+    Slot sl[kSlots];
+    SlotBK bk[2];
     bf16_t Ys[2][kL][kRow];       // read-outs, staged in row layout
     bf16_t Zs[2][kL][kRow];       // removal read-outs, staged for the tape
     bf16_t S0s[2][kN][kRow];      // chunk entry states as [j][i], staged for the tape
@@ -107,13 +129,16 @@ constexpr int kSpinLimit = 1 << 24;
 // removal read-outs Z, the triangular inverse and the tiles Aak, Arb vanish,
 // leaving Y = Rt S0^T + Ark V and S_L^T = diag(G_L) S0^T + Kb^T V; the tape
 // holds only the block entry states (its Z part is not written).
-template <bool kSeq, bool kAB>
+//
+// kCk: also write the fp32 state entering every chunk (a template parameter, so
+// that the kernel without it carries no trace of the stores).
+template <bool kSeq, bool kAB, bool kCk>
 __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
     int B, int T, int H, const bf16_t* __restrict__ r, const bf16_t* __restrict__ w,
     const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const bf16_t* __restrict__ a,
     const bf16_t* __restrict__ b, const float* __restrict__ s0, bf16_t* __restrict__ y_all,
-    float* __restrict__ sT, bf16_t* __restrict__ tape_all, int pass, int split_from, int nseg,
-    int seg_len, float* __restrict__ states, int* __restrict__ sync) {
+    float* __restrict__ sT, bf16_t* __restrict__ tape_all, float* __restrict__ ckpt_all, int pass,
+    int split_from, int nseg, int seg_len, float* __restrict__ states, int* __restrict__ sync) {
     __shared__ FwdSmem sm;
     constexpr size_t NN = (size_t)kN * kN;
     Work wk;
@@ -142,6 +167,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
     const int t_end = wk.t_end;
     bf16_t* const y = wk.outs ? y_all : nullptr;
     bf16_t* const tape = wk.outs ? tape_all : nullptr;
+    // fp32 state entering every chunk, [B][H][ceil(T/16)][N (value i)][N (key j)]
+    float* const ckpt = (kCk && wk.outs) ? ckpt_all : nullptr;
     const int tid = threadIdx.x;
     // Roles split by wave (the tests are uniform within a wave).  They are left
     // as per-lane conditions: branching on an SGPR copy of the wave index
@@ -149,7 +176,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
     const int wave = tid >> 6;
     const bool producer = wave < 4;
     const bool consumer = wave >= 4 && wave < 8;
-    const bool inverter = wave == 8;
+    const bool inverter = wave >= 8;
     const int rtid = tid & 255;               // index within the role
     const int lane = tid & 63, wp = (tid >> 6) & 3;
     const int l16 = lane & 15, g = lane >> 4;
@@ -243,7 +270,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
         return e;
     };
     auto stage_E = [&](int c, const ERaw& er) __attribute__((always_inline)) {
-        Slot& s = sm.sl[c % 3];
+        Slot& s = sm.sl[c % kSlots];
+        SlotBK& bk = sm.bk[c & 1];
         const uint2* raw6 = er.v;
         float X[6][4];
 #pragma unroll
@@ -272,28 +300,30 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
         }
         if (kAB) {
             *reinterpret_cast<bf16x4*>(&s.At[l16][j0]) = cvt4(at);
-            *reinterpret_cast<bf16x4*>(&s.Bh[l16][j0]) = cvt4(bh4);
+            *reinterpret_cast<bf16x4*>(&bk.Bh[l16][j0]) = cvt4(bh4);
             *reinterpret_cast<bf16x4*>(&s.Bb[l16][j0]) = cvt4(bb4);
         }
         *reinterpret_cast<bf16x4*>(&s.Rt[l16][j0]) = cvt4(rt);
-        *reinterpret_cast<bf16x4*>(&s.Kh[l16][j0]) = cvt4(kh4);
+        *reinterpret_cast<bf16x4*>(&bk.Kh[l16][j0]) = cvt4(kh4);
         *reinterpret_cast<bf16x4*>(&s.Kb[l16][j0]) = cvt4(kb4);
         *reinterpret_cast<uint2*>(&s.V[l16][j0]) = wk.vzero ? make_uint2(0u, 0u) : raw6[RAW_V];
         if (l16 == kL - 1) *reinterpret_cast<float4*>(&s.gL[16 * g + 4 * wp]) = make_float4(gt[0], gt[1], gt[2], gt[3]);
     };
 
-    // ---- MW (producer): one 16x16 tile per wave, as an A-operand image ------------
-    // Wave p forms tile p from the rows of X = (At or Rt) and Y = (Bh or Kh):
-    // Tm (p = 0, from Aab), Aak (1), Arb (2), Ark (3).  Accumulator registers of
-    // M^T fed as an A operand stand for M, so each wave forms the transposed
-    // product [s][t] = X_t . Y_s.
+    // ---- MW (producer): one 16x16 tile per wave ---------------------------------
+    // Wave p forms a tile from the rows of X = (At or Rt) and Y = (Bh or Kh):
+    // Aak (1), Arb (2), Ark (3).  Accumulator registers of M^T fed as an A
+    // operand stand for M, so waves 2, 3 form the transposed product [s][t] =
+    // X_t . Y_s (the A-operand images of Arb, Ark); wave 1 forms [t][s] (the
+    // accumulator layout of Aak, which PRE multiplies by Tm) in hi and lo parts.
     struct MWIn {
         bf16x8 xv[2], yv[2];
     };
     auto read_MW = [&](int c) __attribute__((always_inline)) -> MWIn {
-        const Slot& s = sm.sl[c % 3];
+        const Slot& s = sm.sl[c % kSlots];
+        const SlotBK& bk = sm.bk[c & 1];
         const bf16_t(*Xr)[kRow] = (wp & 2) ? s.Rt : s.At;
-        const bf16_t(*Yr)[kRow] = (wp & 1) ? s.Kh : s.Bh;
+        const bf16_t(*Yr)[kRow] = (wp & 1) ? bk.Kh : bk.Bh;
         MWIn in;
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
@@ -303,63 +333,88 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
         return in;
     };
     auto stage_MW = [&](int c, const MWIn& in) __attribute__((always_inline)) {
-        Slot& s = sm.sl[c % 3];
+        Slot& s = sm.sl[c % kSlots];
         f32x4 PT = zero4();
+        if (wp == 1) {
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2) PT = mfma32(in.xv[k2], in.yv[k2], PT);   // [t][s]
+#pragma unroll
+            for (int q = 0; q < 4; ++q) PT[q] = (l16 < 4 * g + q) ? PT[q] : 0.f;   // s < t
+            const Split4 ak = split4(PT);
+            s.tiles[TILE_AK][lane] = __builtin_bit_cast(uint2, ak.hi);
+            s.tiles[TILE_AKL][lane] = __builtin_bit_cast(uint2, ak.lo);
+            return;
+        }
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) PT = mfma32(in.yv[k2], in.xv[k2], PT);   // [s][t]
-        const bool diag = (wp & 2) != 0;   // Arb, Ark keep the diagonal
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int m = 4 * g + q, n = l16;   // m = s, n = t
-            PT[q] = (m < n || (diag && m == n)) ? PT[q] : 0.f;
+            const int m = 4 * g + q, n = l16;   // m = s, n = t; Arb, Ark keep the diagonal
+            PT[q] = m <= n ? PT[q] : 0.f;
         }
-        s.tiles[wp][lane] = __builtin_bit_cast(uint2, cvt4(PT));
+        s.tiles[wp == 2 ? TILE_RB : TILE_RK][lane] = __builtin_bit_cast(uint2, cvt4(PT));
     };
-    // ---- INV (inverse wave): Aab and Tm = (I - Aab)^-1 for tile 0 ----------------
-    // Wave 8 forms Aab from At and Bh (as MW does with wp = 0) and inverts it,
-    // so the long dependent MFMA chain of the inverse leaves the producers.
-    auto stage_INV = [&](int c) __attribute__((always_inline)) {
-        Slot& s = sm.sl[c % 3];
+    // ---- INV (inverse waves): Aab, Tm = (I - Aab)^-1, At' and Aak' -------------
+    // In the interval after E(c) a wave forms Aab from At and Bh, the inverses of
+    // its 4x4 diagonal blocks and N = Td L (wkv7_mfma.h); in the next it joins
+    // them into Tm and applies Tm, as hi and lo bf16 images, to the factors of Z:
+    //   At'^T tile jt = At^T[keys 16 jt ..] Tm^T, whose accumulator registers
+    //     hold At'[l16][16 jt + 4 g + q] -- the row layout of At', written over
+    //     the same columns of At (read first, by transposed reads);
+    //   Aak'^T = Aak^T Tm^T from Aak's accumulator layout (hi and lo), whose
+    //     accumulator registers are Aak''s A-operand image.
+    auto inv_begin = [&](int c) __attribute__((always_inline)) -> BlockInverse {
+        const Slot& s = sm.sl[c % kSlots];
+        const SlotBK& bk = sm.bk[c & 1];
         bf16x8 xv[2], yv[2];
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
             xv[k2] = ld8(&s.At[l16][32 * k2 + 8 * g]);
-            yv[k2] = ld8(&s.Bh[l16][32 * k2 + 8 * g]);
+            yv[k2] = ld8(&bk.Bh[l16][32 * k2 + 8 * g]);
         }
-        f32x4 P = zero4(), PT = zero4();
+        f32x4 P = zero4();
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-            PT = mfma32(yv[k2], xv[k2], PT);   // [s][t]
-            P = mfma32(xv[k2], yv[k2], P);     // [t][s]
-        }
+        for (int k2 = 0; k2 < 2; ++k2) P = mfma32(xv[k2], yv[k2], P);   // [t][s] = Aab[t][s]
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            PT[q] = (4 * g + q < l16) ? PT[q] : 0.f;
-            P[q] = (l16 < 4 * g + q) ? P[q] : 0.f;
+        for (int q = 0; q < 4; ++q) P[q] = (l16 < 4 * g + q) ? P[q] : 0.f;
+        return unit_lower_inverse_begin(P, g, l16);
+    };
+    auto inv_end = [&](int c, const BlockInverse& bi) __attribute__((always_inline)) {
+        Slot& s = sm.sl[c % kSlots];
+        bf16x4 atT[4];
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) atT[jt] = ld4_tr(tr_addr(&s.At[0][16 * jt], kRow, g, l16));
+        const bf16x4 akh = __builtin_bit_cast(bf16x4, s.tiles[TILE_AK][lane]);
+        const bf16x4 akl = __builtin_bit_cast(bf16x4, s.tiles[TILE_AKL][lane]);
+        const Split4 tm = split4(unit_lower_inverse_rows_end(bi, g, l16));
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+            const f32x4 d = mfma16(atT[jt], tm.hi, mfma16(atT[jt], tm.lo, zero4()));
+            *reinterpret_cast<bf16x4*>(&s.At[l16][16 * jt + 4 * g]) = cvt4(d);
         }
-        s.tiles[TILE_T][lane] = __builtin_bit_cast(uint2, cvt4(unit_lower_inverse_T(P, PT, g, l16)));
+        const f32x4 e = mfma16(akh, tm.hi, mfma16(akl, tm.hi, mfma16(akh, tm.lo, zero4())));
+        s.tiles[TILE_AK][lane] = __builtin_bit_cast(uint2, cvt4(e));
     };
 
     // ---- ST (consumer): value-row block `col` of the state chain of chunk c -----
     struct STIn {
-        bf16x4 Tm, Aak, Arb, Ark, V;
+        bf16x4 Aak, Arb, Ark, V;
         bf16x8 at[2], rt[2];
         bf16x4 bbt[4], kbt[4];
         float gl;   // G_L of key 16 jt + 4 g + q sits in lane 4 jt + q of row g
     };
     auto read_ST = [&](int c) __attribute__((always_inline)) -> STIn {
-        const Slot& s = sm.sl[c % 3];
+        const Slot& s = sm.sl[c % kSlots];
         STIn in;
         in.Ark = __builtin_bit_cast(bf16x4, s.tiles[TILE_RK][lane]);
         in.V = ld4_tr(tr_addr(&s.V[0][16 * wp], kRow, g, l16));   // [t][i] as a B operand
         if (kAB) {
-            in.Tm = __builtin_bit_cast(bf16x4, s.tiles[TILE_T][lane]);
-            in.Aak = __builtin_bit_cast(bf16x4, s.tiles[TILE_AK][lane]);
+            in.Aak = __builtin_bit_cast(bf16x4, s.tiles[TILE_AK][lane]);   // Aak' = Tm Aak
             in.Arb = __builtin_bit_cast(bf16x4, s.tiles[TILE_RB][lane]);
         }
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
-            if (kAB) in.at[k2] = ld4x2(&s.At[l16][32 * k2 + 4 * g]);
+            if (kAB) in.at[k2] = ld4x2(&s.At[l16][32 * k2 + 4 * g]);   // At' = Tm At
             in.rt[k2] = ld4x2(&s.Rt[l16][32 * k2 + 4 * g]);
         }
 #pragma unroll
@@ -371,12 +426,19 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
         return in;
     };
     auto stage_ST = [&](int c, const STIn& in) __attribute__((always_inline)) {
-        // Value block `col`: X = At S0^T + Aak V, Z = Tm X, Y = Rt S0^T + Arb Z + Ark V.
-        // The 32-deep products (over keys) and the 16-deep ones (over tokens)
-        // accumulate separately and meet on the vector ALU (add4).
+        // Value block `col`: Z = At' S0^T + Aak' V with At' = Tm At, Aak' = Tm Aak
+        // (from INV), Y = Rt S0^T + Arb Z + Ark V.  The 32-deep products (over
+        // keys) and the 16-deep ones (over tokens) accumulate separately and meet
+        // on the vector ALU (add4).
         bf16x4 Sb[4];
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) Sb[jt] = cvt4(S[jt]);
+        if (kCk && ckpt && c < c_end) {   // the entry state in fp32: row col, keys 16 jt + 4 g ..
+            float* dst = ckpt + (((size_t)bh * ((T + kL - 1) / kL) + c) * kN + col) * kN + 4 * g;
+#pragma unroll
+            for (int jt = 0; jt < 4; ++jt)
+                store_stream(dst + 16 * jt, __builtin_bit_cast(uint4, S[jt]));
+        }
         f32x4 Xs = zero4(), Ys = zero4();
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
@@ -387,8 +449,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
         bf16x4 Zb = {};
         f32x4 Yt;
         if (kAB) {
-            const f32x4 AkV = mfma16(in.Aak, in.V, zero4());
-            Zb = cvt4(mfma16(in.Tm, cvt4(add4(Xs, AkV)), zero4()));
+            Zb = cvt4(add4(Xs, mfma16(in.Aak, in.V, zero4())));
             Yt = add4(Ys, mfma16(in.Ark, in.V, mfma16(in.Arb, Zb, zero4())));
         } else {
             Yt = add4(Ys, mfma16(in.Ark, in.V, zero4()));
@@ -438,13 +499,13 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
     };
 
     if (t_end > wk.t_begin) {
-        // Intervals 0 .. nch+2 carry real work (chunk c_begin + i in interval
-        // i); the count is rounded up to a multiple of three for the unrolled
-        // producer loop.  The extra intervals see only all-padding chunks
-        // (identity on the state, nothing stored).
+        // Intervals 0 .. nch+3 carry real work (chunk c_begin + i enters in
+        // interval i); the count is rounded up to a multiple of three for the
+        // unrolled producer loop.  The extra intervals see only all-padding
+        // chunks (identity on the state, nothing stored).
         const int nch = c_end - c_begin;
         const int cb = c_begin;
-        const int n_it = (nch + 5) / 3 * 3;
+        const int n_it = (nch + 6) / 3 * 3;
         // Each role runs its own loop over the same number of intervals (one
         // barrier each), so the compiler sees only loads on the producer side
         // and only stores on the consumer side.  With both kinds in one loop it
@@ -463,8 +524,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
             load_raw(cb + 3, rb0);
             __syncthreads();
             // Interval it: E(it) and MW(it-1), stash chunk it+1 and load chunk
-            // it+4 into the ring slot it frees.  (A macro, not a lambda, so that
-            // the ring stays plain SSA values.)
+            // it+4 into the ring slot it frees.  (A macro, not a
+            // lambda, so that the ring stays plain SSA values.)
 #define WKV7_FWD_PRODUCE(IT, RING)                                          \
     {                                                                       \
         const int it_ = (IT);                                               \
@@ -490,10 +551,20 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
         } else if (inverter) {
             __builtin_amdgcn_s_setprio(2);
             __syncthreads();
-            // Interval it: the inverse of chunk it-1 (after E(it-1), read by the
-            // consumers' chain in interval it+1).
+            // Chunk cb + j belongs to wave 8 + (j & 1), which starts its inverse in
+            // interval j + 1 (after E) and finishes it, with At' and Aak', in
+            // interval j + 2 (the consumers read them in interval j + 3); so each
+            // of the two waves runs one half per interval, `bi` carrying an
+            // inverse across one barrier.
+            const int par = wave & 1;
+            BlockInverse bi{zero4(), zero4(), zero4()};
             for (int it = 0; it < n_it; ++it) {
-                if (kAB && it >= 1) stage_INV(cb + it - 1);
+                if (kAB && it >= 1) {
+                    if (((it - 1) & 1) == par)
+                        bi = inv_begin(cb + it - 1);
+                    else if (it >= 2)
+                        inv_end(cb + it - 2, bi);
+                }
                 __syncthreads();
             }
         } else {
@@ -503,12 +574,12 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
             // producers' traffic.
             __builtin_amdgcn_s_setprio(3);
             __syncthreads();
-            // Interval it: the state chain of chunk it-2 and the stores of chunk it-3.
+            // Interval it: the state chain of chunk it-3 and the stores of chunk it-4.
             for (int it = 0; it < n_it; ++it) {
-                if (it >= 2) {
-                    const STIn si = read_ST(cb + it - 2);
-                    stage_ST(cb + it - 2, si);
-                    if (it >= 3) store_out(cb + it - 3);
+                if (it >= 3) {
+                    const STIn si = read_ST(cb + it - 3);
+                    stage_ST(cb + it - 3, si);
+                    if (it >= 4) store_out(cb + it - 4);
                 }
                 __syncthreads();
             }
@@ -607,13 +678,14 @@ hipError_t launch_chunk_fwd_sequential(const FwdArgs& p, int chunk_len, int nseg
     seg_sync_init_kernel<<<dim3((nbh + 255) / 256), dim3(256), 0, stream>>>(sync, nbh);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    auto kern = p.a ? chunk_fwd_kernel<true, true> : chunk_fwd_kernel<true, false>;
+    auto kern = p.a ? (p.ckpt ? chunk_fwd_kernel<true, true, true> : chunk_fwd_kernel<true, true, false>)
+                    : (p.ckpt ? chunk_fwd_kernel<true, false, true> : chunk_fwd_kernel<true, false, false>);
     kern<<<dim3(nbh * nseg), dim3(kThreads), 0, stream>>>(
         p.B, p.T, p.H, static_cast<const bf16_t*>(p.r), static_cast<const bf16_t*>(p.w),
         static_cast<const bf16_t*>(p.k), static_cast<const bf16_t*>(p.v),
         static_cast<const bf16_t*>(p.a), static_cast<const bf16_t*>(p.b), p.s0,
-        static_cast<bf16_t*>(p.y), p.sT, static_cast<bf16_t*>(p.tape), 2, 0, nseg, seg_len, states,
-        sync);
+        static_cast<bf16_t*>(p.y), p.sT, static_cast<bf16_t*>(p.tape), p.ckpt, 2, 0, nseg, seg_len,
+        states, sync);
     return hipGetLastError();
 }
 
@@ -626,13 +698,14 @@ hipError_t launch_chunk_fwd_split(const FwdArgs& p, int chunk_len, const FwdSpli
                                        (long long)(sp.nseg - 1) * sp.seg_len >= p.T || !sp.states)))
         return hipErrorInvalidValue;
     auto run = [&](int pass, int grid) {
-        auto kern = p.a ? chunk_fwd_kernel<false, true> : chunk_fwd_kernel<false, false>;
+        auto kern = p.a ? (p.ckpt ? chunk_fwd_kernel<false, true, true> : chunk_fwd_kernel<false, true, false>)
+                        : (p.ckpt ? chunk_fwd_kernel<false, false, true> : chunk_fwd_kernel<false, false, false>);
         kern<<<dim3(grid), dim3(kThreads), 0, stream>>>(
             p.B, p.T, p.H, static_cast<const bf16_t*>(p.r), static_cast<const bf16_t*>(p.w),
             static_cast<const bf16_t*>(p.k), static_cast<const bf16_t*>(p.v),
             static_cast<const bf16_t*>(p.a), static_cast<const bf16_t*>(p.b), p.s0,
-            static_cast<bf16_t*>(p.y), p.sT, static_cast<bf16_t*>(p.tape), pass, sp.split_from,
-            sp.nseg, sp.seg_len, sp.states, nullptr);
+            static_cast<bf16_t*>(p.y), p.sT, static_cast<bf16_t*>(p.tape), p.ckpt, pass,
+            sp.split_from, sp.nseg, sp.seg_len, sp.states, nullptr);
         return hipGetLastError();
     };
     hipError_t e = run(0, sp.split_from + (nsplit > 0 ? nsplit * (2 * sp.nseg - 3) : 0));
