@@ -111,16 +111,34 @@ const char *wkv7_status_string(int status);
    0 on an invalid descriptor. */
 size_t wkv7_tape_bytes(const wkv7_desc *desc);
 
-/* Bytes of device scratch wkv7_backward needs: with_tape != 0 when the caller
-   passes a tape written by wkv7_forward (the backward then keeps one per-token
-   intermediate adjoint and the adjoint of the state leaving every 32-token block
-   there, as much again as the tape, plus 256 bytes of work queues), with_tape =
-   0 when it passes none (then a forward re-run also writes its tape into the
-   workspace: twice the tape).  With chunk_len = 0 (the sequential reverse
-   pass) the fp32 states every 16 tokens, B*H*ceil(T/16)*N*N*4 bytes, whatever
-   with_tape is.  0 on an invalid descriptor or one the backward does not take
-   (chunk_len = 16 with N != WKV7_HEAD_SIZE or fp32). */
-size_t wkv7_workspace_bytes(const wkv7_desc *desc, int with_tape);
+/* Bytes of the fp32 checkpoints that wkv7_forward_ckpt writes and the
+   sequential reverse pass (wkv7_backward with chunk_len = 0) reads:
+     S   [B][H][ceil(T/16)][N][N]  fp32: the state entering every 16-token
+                                   chunk (tokens 16m ..), element [i][j] =
+                                   S[i][j] (row = value channel).
+   This is the per-head state of "Paper Review: RWKV-7 Goose", The approach,
+   kept at chunk boundaries for the backward.  0 on an invalid descriptor. */
+size_t wkv7_ckpt_bytes(const wkv7_desc *desc);
+
+/* Bytes of device scratch that wkv7_backward needs when the caller supplies
+   nothing the forward wrote (no tape, no checkpoints): the size that always
+   suffices.  Equal to wkv7_backward_workspace_bytes(desc, 0). */
+size_t wkv7_workspace_bytes(const wkv7_desc *desc);
+
+/* Bytes of device scratch wkv7_backward needs, given whether the caller passes
+   a tape.
+   chunk_len = 16: with_tape != 0 when the caller passes a tape written by
+   wkv7_forward (the backward then keeps one per-token intermediate adjoint and
+   the adjoint of the state leaving every 32-token block there, as much again as
+   the tape, plus 256 bytes of work queues); with_tape = 0 when it passes none
+   (then a forward re-run also writes its tape into the workspace: twice the
+   tape).
+   chunk_len = 0 (the sequential reverse pass, which writes fp32 checkpoints
+   itself): wkv7_ckpt_bytes(desc), whatever with_tape is (wkv7_backward_ckpt,
+   which reads the caller's checkpoints, needs none).
+   0 on an invalid descriptor or one the backward does not take (chunk_len = 16
+   with N != WKV7_HEAD_SIZE or fp32). */
+size_t wkv7_backward_workspace_bytes(const wkv7_desc *desc, int with_tape);
 
 /*
  * Forward over a whole sequence.
@@ -135,6 +153,17 @@ size_t wkv7_workspace_bytes(const wkv7_desc *desc, int with_tape);
 int wkv7_forward(const wkv7_desc *desc, const void *r, const void *w, const void *k,
                  const void *v, const void *a, const void *b, const float *s0, void *y,
                  float *sT, void *tape, void *stream);
+
+/*
+ * wkv7_forward writing fp32 checkpoints instead of the tape: the same y and sT,
+ * and in `ckpt` (NULL, or wkv7_ckpt_bytes(desc) bytes) the fp32 state entering
+ * every 16-token chunk, layout at wkv7_ckpt_bytes.  Either form writes them
+ * (the scan from its registers every 16 tokens, the chunked form from its fp32
+ * carried state), and either form's checkpoints feed wkv7_backward_ckpt.
+ */
+int wkv7_forward_ckpt(const wkv7_desc *desc, const void *r, const void *w, const void *k,
+                      const void *v, const void *a, const void *b, const float *s0, void *y,
+                      float *sT, float *ckpt, void *stream);
 
 /*
  * wkv7_forward with each head's sequence split in time, for the two shapes
@@ -190,12 +219,12 @@ int wkv7_forward_split(const wkv7_desc *desc, const void *r, const void *w, cons
  *   dy          [B][T][H][N] upstream gradient of y (dtype).
  *   dsT         [B][H][N][N] fp32 upstream gradient of S_T, or NULL (= 0).
  *   tape        chunked form: the tape written by wkv7_forward with the same
- *               inputs (by either forward form), or NULL; then the backward
- *               first re-runs the chunked forward to write it.  Not used by
- *               the sequential form (chunk_len = 0).
+ *               inputs and s0 (by either forward form), or NULL; then the
+ *               backward first re-runs the chunked forward to write it.  Not
+ *               used by the sequential form (chunk_len = 0).
  *   dr..db      [B][T][H][N] outputs (dtype).  ds0: [B][H][N][N] fp32 or NULL.
- *   workspace   at least wkv7_workspace_bytes(desc, tape != NULL) bytes of
- *               device scratch (contents on entry are ignored); else
+ *   workspace   at least wkv7_backward_workspace_bytes(desc, tape != NULL)
+ *               bytes of device scratch (contents on entry are ignored); else
  *               WKV7_ERR_WORKSPACE.  Required whenever B*T*H > 0.
  * desc->chunk_len selects the form:
  *   16  chunk by chunk (16 tokens) on bf16 matrix cores: dtype = WKV7_BF16 and
@@ -203,14 +232,26 @@ int wkv7_forward_split(const wkv7_desc *desc, const void *r, const void *w, cons
  *   0   the sequential reverse recurrence token by token in fp32 on the vector
  *       ALU (one workgroup per head): either dtype, N = 32, 64 or 128.  It
  *       first re-runs the sequential forward to write fp32 states every 16
- *       tokens into the workspace, B*H*ceil(T/16)*N*N*4 bytes (the size
- *       wkv7_workspace_bytes returns for chunk_len = 0); `tape` is not used.
+ *       tokens into the workspace (wkv7_ckpt_bytes); wkv7_backward_ckpt
+ *       takes them from the caller instead.
  */
 int wkv7_backward(const wkv7_desc *desc, const void *r, const void *w, const void *k,
                   const void *v, const void *a, const void *b, const float *s0,
                   const void *dy, const float *dsT, const void *tape, void *dr, void *dw,
                   void *dk, void *dv, void *da, void *db, float *ds0, void *workspace,
                   size_t workspace_bytes, void *stream);
+
+/*
+ * The sequential reverse pass (desc->chunk_len = 0, else WKV7_ERR_UNSUPPORTED)
+ * from the caller's fp32 checkpoints instead of a re-run of the scan: `ckpt`
+ * (required when B*T*H > 0) holds what wkv7_forward_ckpt wrote for the same
+ * inputs and s0, by either forward form, wkv7_ckpt_bytes(desc) bytes.  Other
+ * arguments and results as wkv7_backward; no workspace.
+ */
+int wkv7_backward_ckpt(const wkv7_desc *desc, const void *r, const void *w, const void *k,
+                       const void *v, const void *a, const void *b, const float *s0,
+                       const void *dy, const float *dsT, const float *ckpt, void *dr, void *dw,
+                       void *dk, void *dv, void *da, void *db, float *ds0, void *stream);
 
 /*
  * The two stages of wkv7_backward as separate calls, for callers that schedule

@@ -34,8 +34,10 @@ HEAD_SIZE = 64
 TAPE_CHUNK = 16
 TAPE_BLOCK = 32
 
-EXPORTED = ("wkv7_abi_version", "wkv7_status_string", "wkv7_tape_bytes", "wkv7_workspace_bytes",
-            "wkv7_forward", "wkv7_forward_split_workspace_bytes", "wkv7_forward_split", "wkv7_backward", "wkv7_backward_adjoint", "wkv7_backward_gradients",
+EXPORTED = ("wkv7_abi_version", "wkv7_status_string", "wkv7_tape_bytes", "wkv7_ckpt_bytes",
+            "wkv7_workspace_bytes", "wkv7_backward_workspace_bytes", "wkv7_forward",
+            "wkv7_forward_ckpt", "wkv7_forward_split_workspace_bytes", "wkv7_forward_split",
+            "wkv7_backward", "wkv7_backward_ckpt", "wkv7_backward_adjoint", "wkv7_backward_gradients",
             "wkv7_backward_overlapped", "wkv7_decode_step")
 
 
@@ -73,10 +75,16 @@ def lib():
         L.wkv7_status_string.restype = ctypes.c_char_p
         L.wkv7_tape_bytes.argtypes = [D]
         L.wkv7_tape_bytes.restype = Z
-        L.wkv7_workspace_bytes.argtypes = [D, ctypes.c_int]
+        L.wkv7_ckpt_bytes.argtypes = [D]
+        L.wkv7_ckpt_bytes.restype = Z
+        L.wkv7_workspace_bytes.argtypes = [D]
         L.wkv7_workspace_bytes.restype = Z
+        L.wkv7_backward_workspace_bytes.argtypes = [D, ctypes.c_int]
+        L.wkv7_backward_workspace_bytes.restype = Z
         L.wkv7_forward.argtypes = [D] + [P] * 6 + [P, P, P, P, P]
         L.wkv7_forward.restype = ctypes.c_int
+        L.wkv7_forward_ckpt.argtypes = [D] + [P] * 6 + [P, P, P, P, P]
+        L.wkv7_forward_ckpt.restype = ctypes.c_int
         L.wkv7_forward_split_workspace_bytes.argtypes = [D, I]
         L.wkv7_forward_split_workspace_bytes.restype = Z
         L.wkv7_forward_split.argtypes = [D] + [P] * 6 + [P, P, P, P, I, P, Z, P]
@@ -85,6 +93,8 @@ def lib():
             fn = getattr(L, name)
             fn.argtypes = [D] + [P] * 6 + [P, P, P, P] + [P] * 6 + [P, P, Z, P]
             fn.restype = ctypes.c_int
+        L.wkv7_backward_ckpt.argtypes = [D] + [P] * 6 + [P, P, P, P] + [P] * 6 + [P, P]
+        L.wkv7_backward_ckpt.restype = ctypes.c_int
         L.wkv7_backward_overlapped.argtypes = [D] + [P] * 6 + [P, P, P, P] + [P] * 6 + [P, P, Z, P, P]
         L.wkv7_backward_overlapped.restype = ctypes.c_int
         L.wkv7_decode_step.argtypes = [I, I, I, I] + [P] * 6 + [P, P, P]
@@ -151,8 +161,13 @@ def tape_bytes(desc: Desc) -> int:
     return int(lib().wkv7_tape_bytes(ctypes.byref(desc)))
 
 
+def ckpt_bytes(desc: Desc) -> int:
+    return int(lib().wkv7_ckpt_bytes(ctypes.byref(desc)))
+
+
 def workspace_bytes(desc: Desc, with_tape: bool = True) -> int:
-    return int(lib().wkv7_workspace_bytes(ctypes.byref(desc), 1 if with_tape else 0))
+    """Backward scratch with or without a tape passed in (``with_tape``)."""
+    return int(lib().wkv7_backward_workspace_bytes(ctypes.byref(desc), 1 if with_tape else 0))
 
 
 def split_workspace_bytes(desc: Desc, segments: int = 0) -> int:
@@ -172,7 +187,7 @@ def split_tape(tape, B: int, T: int, H: int, N: int = HEAD_SIZE):
 
 def forward(r, w, k, v, a, b, s0=None, *, chunk_len: int = 0, want_state: bool = True,
             want_tape: bool = False, out=None, segments: Optional[int] = None, workspace=None,
-            tape_out=None):
+            tape_out=None, want_ckpt: bool = False):
     """Run the recurrence over [B, T, H, N] inputs.
 
     Returns ``(y, sT, tape)``; ``sT`` / ``tape`` are None unless requested (the
@@ -182,7 +197,10 @@ def forward(r, w, k, v, a, b, s0=None, *, chunk_len: int = 0, want_state: bool =
     choice, 1 = no split, n >= 2 = every head in up to n time segments;
     ``workspace`` is then its device scratch (allocated here when None).
     ``tape_out`` (a bf16 device tensor of at least ``tape_bytes`` bytes) receives
-    the tape instead of a new allocation.
+    the tape instead of a new allocation.  ``want_ckpt`` selects
+    wkv7_forward_ckpt instead: the third result is then the fp32 state entering
+    every 16 tokens, [B, H, ceil(T/16), N, N], which ``backward(...,
+    chunk_len=0, ckpt=...)`` reads.
     """
     torch = _torch()
     B, T, H, N = r.shape
@@ -192,6 +210,17 @@ def forward(r, w, k, v, a, b, s0=None, *, chunk_len: int = 0, want_state: bool =
     desc = make_desc(B, T, H, N, _dtype_code(r), chunk_len)
     y = out if out is not None else torch.empty_like(r)
     sT = torch.empty((B, H, N, N), device=r.device, dtype=torch.float32) if want_state else None
+    if want_ckpt:
+        if want_tape or tape_out is not None or segments is not None:
+            raise ValueError("want_ckpt excludes the tape and the split forward")
+        nst = (T + TAPE_CHUNK - 1) // TAPE_CHUNK
+        ck = torch.empty((B, H, nst, N, N), device=r.device, dtype=torch.float32)
+        st = lib().wkv7_forward_ckpt(ctypes.byref(desc), _ptr(r), _ptr(w), _ptr(k), _ptr(v),
+                                     _ptr(a), _ptr(b), _ptr(s0), _ptr(y), _ptr(sT), _ptr(ck),
+                                     _stream())
+        if st != WKV7_OK:
+            raise WKV7Error(st, "wkv7_forward_ckpt")
+        return y, sT, ck
     ck = None
     if tape_out is not None:
         if not tape_out.is_cuda or not tape_out.is_contiguous() or \
@@ -227,11 +256,14 @@ _STAGES = {"all": "wkv7_backward", "adjoint": "wkv7_backward_adjoint",
 
 def backward(r, w, k, v, a, b, dy, s0=None, dsT=None, tape=None, *, chunk_len: int = 16,
              want_ds0: bool = True, workspace=None, stage: str = "all", grads=None, ds0=None,
-             aux_stream=None):
+             aux_stream=None, ckpt=None):
     """Gradients of ``<dy, y> + <dsT, S_T>``: returns (dr, dw, dk, dv, da, db, ds0).
 
     ``tape`` is the one ``forward(..., want_tape=True)`` returned for the same
-    inputs, or None (the forward is then re-run inside the call).  ``stage``
+    inputs, or None (the forward is then re-run inside the call).  ``ckpt``
+    (``chunk_len=0`` only) is the fp32 checkpoint of ``forward(...,
+    want_ckpt=True)``: the sequential reverse pass then reads it
+    (wkv7_backward_ckpt) instead of re-running the scan.  ``stage``
     selects the whole backward ("all") or one of its two stages ("adjoint",
     then "gradients" with the same ``workspace``, ``grads`` and ``ds0``).
     ``aux_stream`` (a torch stream) runs the whole backward on two streams
@@ -257,6 +289,17 @@ def backward(r, w, k, v, a, b, dy, s0=None, dsT=None, tape=None, *, chunk_len: i
     if ds0 is None and want_ds0:
         ds0 = torch.empty((B, H, N, N), device=r.device, dtype=torch.float32)
     _check_state(ds0, (B, H, N, N))
+    if ckpt is not None:
+        nst = (T + TAPE_CHUNK - 1) // TAPE_CHUNK
+        _check_state(ckpt, (B, H, nst, N, N))
+        if tape is not None or aux_stream is not None or stage != "all" or chunk_len != 0:
+            raise ValueError("ckpt goes with chunk_len=0, no tape, the whole backward")
+        st = lib().wkv7_backward_ckpt(ctypes.byref(desc), _ptr(r), _ptr(w), _ptr(k), _ptr(v),
+                                      _ptr(a), _ptr(b), _ptr(s0), _ptr(dy), _ptr(dsT), _ptr(ckpt),
+                                      *[_ptr(x) for x in grads], _ptr(ds0), _stream())
+        if st != WKV7_OK:
+            raise WKV7Error(st, "wkv7_backward_ckpt")
+        return tuple(grads) + (ds0,)
     wsb = workspace_bytes(desc, tape is not None)
     ws = workspace
     if ws is None:

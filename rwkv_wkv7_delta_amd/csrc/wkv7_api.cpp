@@ -153,13 +153,14 @@ size_t split_bytes(const wkv7_desc* d, const SplitPlan& p) {
 
 int run_forward(const wkv7_desc* d, const void* r, const void* w, const void* k, const void* v,
                 const void* a, const void* b, const float* s0, void* y, float* sT,
-                void* tape, hipStream_t stream) {
+                void* tape, hipStream_t stream, float* ckpt = nullptr) {
     if ((int64_t)d->B * d->H == 0) return WKV7_OK;
     if (d->T == 0) {
         if (sT) return from_hip(wkv7::launch_state_copy(d->B * d->H, d->N, s0, sT, stream));
         return WKV7_OK;
     }
     wkv7::FwdArgs p{d->B, d->T, d->H, d->N, d->dtype == WKV7_BF16, r, w, k, v, a, b, s0, y, sT, tape};
+    p.ckpt = ckpt;
     if (d->chunk_len == 0) return from_hip(wkv7::launch_seq_fwd(p, stream));
     return from_hip(wkv7::launch_chunk_fwd(p, d->chunk_len, stream));
 }
@@ -186,12 +187,19 @@ size_t wkv7_tape_bytes(const wkv7_desc* desc) {
     return tape_bytes_unchecked(desc);
 }
 
-size_t wkv7_workspace_bytes(const wkv7_desc* desc, int with_tape) {
+size_t wkv7_ckpt_bytes(const wkv7_desc* desc) {
+    if (check_desc(desc) != WKV7_OK) return 0;
+    return seq_ckpt_bytes(desc);
+}
+
+size_t wkv7_backward_workspace_bytes(const wkv7_desc* desc, int with_tape) {
     if (check_desc(desc) != WKV7_OK) return 0;
     if (desc->chunk_len == 0) return seq_ckpt_bytes(desc);
     if (desc->dtype != WKV7_BF16 || desc->N != WKV7_HEAD_SIZE) return 0;
     return tape_bytes_unchecked(desc) * (with_tape ? 1 : 2) + kQueueBytes;
 }
+
+size_t wkv7_workspace_bytes(const wkv7_desc* desc) { return wkv7_backward_workspace_bytes(desc, 0); }
 
 int wkv7_forward(const wkv7_desc* desc, const void* r, const void* w, const void* k,
                  const void* v, const void* a, const void* b, const float* s0, void* y,
@@ -203,6 +211,19 @@ int wkv7_forward(const wkv7_desc* desc, const void* r, const void* w, const void
         return WKV7_ERR_INVALID_ARG;
     if (!(opt(s0) && opt(sT) && opt(tape))) return WKV7_ERR_INVALID_ARG;
     return run_forward(desc, r, w, k, v, a, b, s0, y, sT, tape, static_cast<hipStream_t>(stream));
+}
+
+int wkv7_forward_ckpt(const wkv7_desc* desc, const void* r, const void* w, const void* k,
+                      const void* v, const void* a, const void* b, const float* s0, void* y,
+                      float* sT, float* ckpt, void* stream) {
+    const int st = check_desc(desc);
+    if (st != WKV7_OK) return st;
+    const bool has_tokens = (int64_t)desc->B * desc->T * desc->H > 0;
+    if (has_tokens && !(req(r) && req(w) && req(k) && req(v) && pair(a, b) && req(y)))
+        return WKV7_ERR_INVALID_ARG;
+    if (!(opt(s0) && opt(sT) && opt(ckpt))) return WKV7_ERR_INVALID_ARG;
+    return run_forward(desc, r, w, k, v, a, b, s0, y, sT, nullptr, static_cast<hipStream_t>(stream),
+                       ckpt);
 }
 
 size_t wkv7_forward_split_workspace_bytes(const wkv7_desc* desc, int32_t segments) {
@@ -279,7 +300,7 @@ int run_backward(const wkv7_desc* desc, const void* r, const void* w, const void
                  const void* v, const void* a, const void* b, const float* s0, const void* dy,
                  const float* dsT, const void* tape, void* dr, void* dw, void* dk, void* dv,
                  void* da, void* db, float* ds0, void* workspace, size_t workspace_bytes,
-                 void* stream, int stages, void* aux) {
+                 void* stream, int stages, void* aux, const float* ckpt = nullptr) {
     int st = check_desc(desc);
     if (st != WKV7_OK) return st;
     const bool seq = desc->chunk_len == 0;
@@ -303,8 +324,12 @@ int run_backward(const wkv7_desc* desc, const void* r, const void* w, const void
     // chain's results to the second stage, and a re-run would overwrite it.
     if (stages != (wkv7::BWD_CHAIN | wkv7::BWD_KEYS) && has_tokens && !tape)
         return WKV7_ERR_INVALID_ARG;
-    const size_t need = seq ? seq_ckpt_bytes(desc) : tape_bytes_unchecked(desc) * (tape ? 1 : 2) + kQueueBytes;
-    if (has_tokens && (workspace == nullptr || workspace_bytes < need)) return WKV7_ERR_WORKSPACE;
+    // The sequential pass reads the caller's fp32 checkpoints (then it needs no
+    // scratch), else it writes its own; it never reads the tape.
+    const size_t need = seq ? (ckpt ? 0 : seq_ckpt_bytes(desc))
+                            : tape_bytes_unchecked(desc) * (tape ? 1 : 2) + kQueueBytes;
+    if (has_tokens && need > 0 && (workspace == nullptr || workspace_bytes < need))
+        return WKV7_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if ((int64_t)desc->B * desc->H == 0) return WKV7_OK;
     if (desc->T == 0) {
@@ -315,11 +340,12 @@ int run_backward(const wkv7_desc* desc, const void* r, const void* w, const void
     }
     char* ws = static_cast<char*>(workspace);
     if (seq) {
-        // The sequential reverse pass keeps its own fp32 checkpoints (the tape,
-        // if any, is not used).
+        // The sequential reverse pass reads fp32 checkpoints: the caller's or its
+        // own, written into the workspace first (the tape is not used).
         const wkv7::SeqBwdArgs p{desc->B, desc->T, desc->H, desc->N, desc->dtype == WKV7_BF16,
                                  r, w, k, v, a, b, dy, s0, dsT, dr, dw, dk, dv, da, db, ds0,
-                                 static_cast<float*>(workspace)};
+                                 ckpt ? const_cast<float*>(ckpt) : static_cast<float*>(workspace),
+                                 ckpt != nullptr};
         return from_hip(wkv7::launch_seq_bwd(p, s));
     }
     if (!tape) {
@@ -377,6 +403,18 @@ int wkv7_backward(const wkv7_desc* desc, const void* r, const void* w, const voi
     return run_backward(desc, r, w, k, v, a, b, s0, dy, dsT, tape, dr, dw, dk, dv, da, db, ds0,
                         workspace, workspace_bytes, stream, wkv7::BWD_CHAIN | wkv7::BWD_KEYS,
                         nullptr);
+}
+
+int wkv7_backward_ckpt(const wkv7_desc* desc, const void* r, const void* w, const void* k,
+                       const void* v, const void* a, const void* b, const float* s0,
+                       const void* dy, const float* dsT, const float* ckpt, void* dr, void* dw,
+                       void* dk, void* dv, void* da, void* db, float* ds0, void* stream) {
+    const int st = check_desc(desc);
+    if (st != WKV7_OK) return st;
+    if (desc->chunk_len != 0) return WKV7_ERR_UNSUPPORTED;
+    if ((int64_t)desc->B * desc->T * desc->H > 0 && !req(ckpt)) return WKV7_ERR_INVALID_ARG;
+    return run_backward(desc, r, w, k, v, a, b, s0, dy, dsT, nullptr, dr, dw, dk, dv, da, db, ds0,
+                        nullptr, 0, stream, wkv7::BWD_CHAIN | wkv7::BWD_KEYS, nullptr, ckpt);
 }
 
 int wkv7_backward_overlapped(const wkv7_desc* desc, const void* r, const void* w, const void* k,

@@ -14,8 +14,8 @@ struct FwdArgs {
     void* y;          // may be null only when T == 0
     float* sT;        // may be null
     void* tape;       // may be null: bf16 Z [B][T][H][N] then entry states [B][H][nch][N][N]
-    float* ckpt = nullptr;   // sequential scan only, may be null: fp32 entry state of
-                             // every 16 tokens [B][H][ceil(T/16)][N][N]
+    float* ckpt = nullptr;   // may be null: fp32 entry state of every 16 tokens
+                             // [B][H][ceil(T/16)][N][N] (runs with outputs write theirs)
 };
 
 struct BwdArgs {
@@ -43,7 +43,8 @@ struct SeqBwdArgs {
     const float* dsT;   // may be null
     void *dr, *dw, *dk, *dv, *da, *db;        // da, db: null when a = b = 0
     float* ds0;         // may be null
-    float* ckpt;        // [B][H][ceil(T/16)][N][N] fp32 scratch
+    float* ckpt;        // [B][H][ceil(T/16)][N][N] fp32: scratch the pass fills first, or
+    bool ckpt_given;    // the caller's checkpoints (then no forward re-run)
 };
 
 struct DecodeArgs {

@@ -679,10 +679,12 @@ hipError_t launch_decode_t(const DecodeArgs& p, hipStream_t stream) {
 
 template <typename Tin, int N>
 hipError_t launch_seq_bwd_n(const SeqBwdArgs& p, hipStream_t stream) {
-    FwdArgs f{p.B, p.T, p.H, N, p.bf16, p.r, p.w, p.k, p.v, p.a, p.b, p.s0, nullptr, nullptr, nullptr};
-    f.ckpt = p.ckpt;
-    hipError_t e = launch_seq_fwd_n<Tin, N>(f, FwdSplit{p.B * p.H, 1, p.T, nullptr}, stream);
-    if (e != hipSuccess) return e;
+    if (!p.ckpt_given) {
+        FwdArgs f{p.B, p.T, p.H, N, p.bf16, p.r, p.w, p.k, p.v, p.a, p.b, p.s0, nullptr, nullptr, nullptr};
+        f.ckpt = const_cast<float*>(p.ckpt);
+        const hipError_t e = launch_seq_fwd_n<Tin, N>(f, FwdSplit{p.B * p.H, 1, p.T, nullptr}, stream);
+        if (e != hipSuccess) return e;
+    }
     auto kern = p.a ? seq_bwd_kernel<Tin, N, true> : seq_bwd_kernel<Tin, N, false>;
     kern<<<dim3(p.B * p.H), dim3(64 * SeqBwdShape<N>::WAVES), 0, stream>>>(
         p.T, p.H, static_cast<const Tin*>(p.r), static_cast<const Tin*>(p.w),

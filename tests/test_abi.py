@@ -57,8 +57,58 @@ def test_tape_and_workspace_sizes(L):
     # pass's workspace holds fp32 states every 16 tokens; the chunked form
     # (N = 64 only) has no size.
     assert wk.tape_bytes(wk.make_desc(1, 64, 1, 32, wk.WKV7_F32, 0)) == 64 * 32 * 2 + 2 * 32 * 32 * 2
+    assert wk.workspace_bytes(wk.make_desc(1, 64, 1, 32, wk.WKV7_F32, 0), False) == 4 * 32 * 32 * 4
     assert wk.workspace_bytes(wk.make_desc(1, 64, 1, 32, wk.WKV7_F32, 0), True) == 4 * 32 * 32 * 4
     assert wk.workspace_bytes(wk.make_desc(1, 64, 1, 32, wk.WKV7_BF16, 16), True) == 0
+
+
+def test_ckpt_and_one_argument_workspace_sizes(L):
+    """wkv7_ckpt_bytes: the fp32 state entering every 16 tokens, [B][H][ceil(T/16)][N][N],
+    for either form; wkv7_workspace_bytes(desc): the backward's scratch when the
+    caller passes nothing the forward wrote (= wkv7_backward_workspace_bytes(desc, 0))."""
+    for B, T, H, N, dt, cl in ((8, 4096, 40, 64, wk.WKV7_BF16, 16), (2, 33, 3, 32, wk.WKV7_F32, 0),
+                               (1, 1, 1, 128, wk.WKV7_BF16, 0), (3, 0, 2, 64, wk.WKV7_BF16, 16)):
+        d = wk.make_desc(B, T, H, N, dt, cl)
+        assert L.wkv7_ckpt_bytes(ctypes.byref(d)) == B * H * ((T + 15) // 16) * N * N * 4
+        assert wk.ckpt_bytes(d) == L.wkv7_ckpt_bytes(ctypes.byref(d))
+        assert L.wkv7_workspace_bytes(ctypes.byref(d)) == \
+            L.wkv7_backward_workspace_bytes(ctypes.byref(d), 0)
+    d = wk.make_desc(8, 4096, 40, 64, wk.WKV7_BF16, 16)
+    assert L.wkv7_workspace_bytes(ctypes.byref(d)) == 2 * wk.tape_bytes(d) + 256
+    d = wk.make_desc(2, 33, 3, 32, wk.WKV7_F32, 0)
+    assert L.wkv7_workspace_bytes(ctypes.byref(d)) == wk.ckpt_bytes(d)
+    for bad in (wk.make_desc(1, 8, 1, 48, wk.WKV7_BF16, 0), wk.make_desc(-1, 8, 1, 64, wk.WKV7_BF16, 0)):
+        assert L.wkv7_ckpt_bytes(ctypes.byref(bad)) == 0
+        assert L.wkv7_workspace_bytes(ctypes.byref(bad)) == 0
+    assert L.wkv7_ckpt_bytes(None) == 0 and L.wkv7_workspace_bytes(None) == 0
+
+
+def test_backward_ckpt_validation(L):
+    """wkv7_backward_ckpt: the sequential reverse pass (chunk_len 0) from the
+    caller's fp32 checkpoints, which are required; no workspace."""
+    f = L.wkv7_backward_ckpt
+    d = wk.make_desc(1, 8, 1, 64, wk.WKV7_BF16, 0)
+    args = [FAKE] * 6 + [None, FAKE, None]
+    assert f(None, *args, FAKE, *[FAKE] * 6, None, None) == wk.WKV7_ERR_INVALID_ARG
+    assert f(ctypes.byref(d), *args, None, *[FAKE] * 6, None, None) == wk.WKV7_ERR_INVALID_ARG
+    assert f(ctypes.byref(d), *args, FAKE + 8, *[FAKE] * 6, None, None) == wk.WKV7_ERR_INVALID_ARG
+    assert f(ctypes.byref(d), *args, FAKE, *[FAKE] * 5, None, None, None) == wk.WKV7_ERR_INVALID_ARG
+    d16 = wk.make_desc(1, 8, 1, 64, wk.WKV7_BF16, 16)
+    assert f(ctypes.byref(d16), *args, FAKE, *[FAKE] * 6, None, None) == wk.WKV7_ERR_UNSUPPORTED
+    d0 = wk.make_desc(0, 8, 1, 64, wk.WKV7_BF16, 0)
+    assert f(ctypes.byref(d0), *args, None, *[FAKE] * 6, None, None) == wk.WKV7_OK
+
+
+def test_forward_ckpt_validation(L):
+    f = L.wkv7_forward_ckpt
+    d = wk.make_desc(1, 8, 1, 64, wk.WKV7_BF16, 16)
+    assert f(None, *[FAKE] * 6, None, FAKE, None, FAKE, None) == wk.WKV7_ERR_INVALID_ARG
+    assert f(ctypes.byref(d), *[FAKE] * 6, None, FAKE, None, FAKE + 8, None) == wk.WKV7_ERR_INVALID_ARG
+    assert f(ctypes.byref(d), *[FAKE] * 6, None, None, None, FAKE, None) == wk.WKV7_ERR_INVALID_ARG
+    assert f(ctypes.byref(wk.make_desc(1, 8, 1, 32, wk.WKV7_BF16, 16)), *[FAKE] * 6, None, FAKE,
+             None, FAKE, None) == wk.WKV7_ERR_UNSUPPORTED
+    assert f(ctypes.byref(wk.make_desc(0, 8, 1, 64, wk.WKV7_BF16, 16)), *[FAKE] * 6, None, FAKE,
+             None, FAKE, None) == wk.WKV7_OK
 
 
 FAKE = 1 << 20   # aligned, never dereferenced (validation fails first or nothing runs)
@@ -174,7 +224,7 @@ def test_sequential_backward_validation(L):
     for n, dt in ((32, wk.WKV7_F32), (64, wk.WKV7_BF16), (128, wk.WKV7_F32)):
         d = wk.make_desc(2, 33, 3, n, dt, 0)
         need = 2 * 3 * 3 * n * n * 4          # ceil(33 / 16) = 3 states per head
-        assert wk.workspace_bytes(d, True) == need
+        assert wk.workspace_bytes(d, True) == need   # the tape is not used
         assert wk.workspace_bytes(d, False) == need
         args = [FAKE] * 6 + [None, FAKE, None]
         assert L.wkv7_backward(ctypes.byref(d), *args, None, *[FAKE] * 6, None, FAKE, need - 16,
@@ -219,8 +269,9 @@ def test_backward_overlapped_validation(L):
             wk.WKV7_ERR_INVALID_ARG
         d32 = wk.make_desc(1, 8, 1, 64, wk.WKV7_F32, 16)
         assert f(ctypes.byref(d32), *args, FAKE, *grads, None, None, 0, None, aux) == wk.WKV7_ERR_UNSUPPORTED
+        # (the sequential pass without checkpoints: it needs scratch for its own)
         dseq = wk.make_desc(1, 8, 1, 64, wk.WKV7_F32, 0)
-        assert f(ctypes.byref(dseq), *args, FAKE, *grads, None, None, 0, None, aux) == wk.WKV7_ERR_WORKSPACE
+        assert f(ctypes.byref(dseq), *args, None, *grads, None, None, 0, None, aux) == wk.WKV7_ERR_WORKSPACE
         d0 = wk.make_desc(0, 8, 1, 64, wk.WKV7_BF16, 16)
         assert f(ctypes.byref(d0), *args, FAKE, *grads, None, None, 0, None, aux) == wk.WKV7_OK
 
