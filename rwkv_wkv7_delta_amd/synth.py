@@ -151,3 +151,117 @@ def generate_workload(wl: Workload, seed: int = 0, *, T: Optional[int] = None,
                         token_shape=(TT, BB, wl.H, wl.N))
     return generate(BB, TT, wl.H, wl.N, dtype=wl.dtype, seed=seed,
                     random_s0=wl.random_s0, backward=wl.backward)
+
+
+# ---------------------------------------------------------------------------
+# Special-case inputs: the regimes the pages single out.  As above, these only
+# draw and round inputs.
+# ---------------------------------------------------------------------------
+
+EDGE_KINDS = ("linear", "replace", "correlated", "swap", "steep_decay", "dyadic")
+
+# Smallest decay the chunked form is asked to take: w^16 = 1e-28 (the chunk
+# algebra divides by running products of 16 decays).
+STEEP_DECAY = float(np.exp(np.log(1e-28) / 16))
+
+
+def generate_edge(kind: str, B: int, T: int, H: int, N: int = 64, *, dtype: str = "bf16",
+                  seed: int = 0, random_s0: bool = True, backward: bool = False,
+                  pool: int = 3) -> Inputs:
+    """Inputs for one special regime (``kind`` in ``EDGE_KINDS``), shape [B, T, H, N].
+
+    * ``linear``: w = 1 and a = b = 0 (linear attention: "Paper Review: RWKV-7
+      Goose", Background information on delta rule); r, k, v ~ N(0, 1).
+    * ``replace``: w = 1, alpha = 1, k = kappa (write key = unit removal key),
+      with kappa drawn per token from ``pool`` unit keys per head, so keys repeat
+      inside every chunk (exact value replacement: "RWKV-7 Goose with Expressive
+      Dynamic State Evolution", Abstract).
+    * ``correlated``: removal keys with cosine about 0.8 to a shared direction
+      per head, alpha in [0.9, 1], w in [0.95, 1], k ~ N(0, 1).
+    * ``swap``: w = 1, alpha = 2 and kappa = (e_i - e_j) / sqrt(2) for random
+      i != j per token, so the transition swaps two key columns ("copy" state
+      transitions: "Paper Review", Architecture).
+    * ``steep_decay``: a quarter of the channels decay at STEEP_DECAY (w^16 =
+      1e-28, the edge of the chunked form's domain), the rest as in ``generate``.
+    * ``dyadic``: every entry of r, k, v, a, b in {0, +-1/2, +-1} (a and b with
+      two non-zeros per token), w in {1/2, 1}, s0 in {0, +-1/2}: sums of such
+      values are exact in fp32 while they stay small.
+    Draw order (PCG64 ``seed``): r, k, v, then the kind's own draws, then s0, dy.
+    """
+    if kind not in EDGE_KINDS:
+        raise ValueError(f"kind must be one of {EDGE_KINDS}")
+    shape = (B, T, H, N)
+    rng = np.random.default_rng(seed)
+
+    def rnd(x: np.ndarray) -> np.ndarray:
+        x32 = np.asarray(x).astype(np.float32)
+        return round_to_bf16(x32) if dtype == "bf16" else x32
+
+    def unit(x: np.ndarray) -> np.ndarray:
+        return x / np.linalg.norm(x, axis=-1, keepdims=True)
+
+    if kind == "dyadic":
+        vals = np.array([0.0, 0.5, -0.5, 1.0, -1.0])
+        r = vals[rng.integers(0, 5, shape)]
+        k = vals[rng.integers(0, 5, shape)]
+        v = vals[rng.integers(0, 5, shape)]
+        w = np.where(rng.random(shape) < 0.5, 0.5, 1.0)
+        a = np.zeros(shape)
+        b = np.zeros(shape)
+        idx = rng.integers(0, N, shape[:-1] + (2,))
+        sgn = vals[rng.integers(1, 5, shape[:-1] + (4,))]
+        np.put_along_axis(a, idx, sgn[..., :2], axis=-1)
+        np.put_along_axis(b, idx[..., ::-1], sgn[..., 2:], axis=-1)
+    else:
+        r = rng.standard_normal(shape)
+        k = rng.standard_normal(shape)
+        v = rng.standard_normal(shape)
+        if kind == "linear":
+            w = np.ones(shape)
+            a = np.zeros(shape)
+            b = np.zeros(shape)
+        elif kind == "replace":
+            keys = unit(rng.standard_normal((B, H, pool, N)))
+            pick = rng.integers(0, pool, (B, T, H))
+            kappa = keys[np.arange(B)[:, None, None], np.arange(H)[None, None, :], pick]
+            w = np.ones(shape)
+            a = -kappa
+            b = kappa
+            k = kappa
+        elif kind == "correlated":
+            base = unit(rng.standard_normal((B, 1, H, N)))
+            kappa = unit(base + 0.55 * unit(rng.standard_normal(shape)))
+            alpha = rng.uniform(0.9, 1.0, shape)
+            w = rng.uniform(0.95, 1.0, shape)
+            a = -kappa
+            b = kappa * alpha
+        elif kind == "swap":
+            i = rng.integers(0, N, (B, T, H))
+            j = (i + rng.integers(1, N, (B, T, H))) % N
+            kappa = np.zeros(shape)
+            np.put_along_axis(kappa, i[..., None], 1.0, axis=-1)
+            np.put_along_axis(kappa, j[..., None], -1.0, axis=-1)
+            kappa /= np.sqrt(2.0)
+            w = np.ones(shape)
+            a = -kappa
+            b = 2.0 * kappa
+        else:  # steep_decay
+            u = rng.standard_normal(shape)
+            w = np.exp(-DECAY_SCALE * _sigmoid(u))
+            w = np.where(rng.random(shape) < 0.25, STEEP_DECAY, w)
+            kappa = unit(rng.standard_normal(shape))
+            alpha = _sigmoid(rng.standard_normal(shape))
+            a = -kappa
+            b = kappa * alpha
+    s0 = None
+    if random_s0:
+        if kind == "dyadic":
+            s0 = (np.array([0.0, 0.5, -0.5])[rng.integers(0, 3, (B, H, N, N))]).astype(np.float32)
+        else:
+            s0 = (0.1 * rng.standard_normal((B, H, N, N))).astype(np.float32)
+    dy = dsT = None
+    if backward:
+        dy = rnd(rng.standard_normal(shape))
+        dsT = np.zeros((B, H, N, N), dtype=np.float32)
+    return Inputs(r=rnd(r), w=rnd(w), k=rnd(k), v=rnd(v), a=rnd(a), b=rnd(b), s0=s0, dy=dy,
+                  dsT=dsT, dtype=dtype, meta=dict(B=B, T=T, H=H, N=N, seed=seed, kind=kind))

@@ -46,3 +46,23 @@ def to_dev(x, dtype):
 def to_np(t):
     import torch
     return t.detach().float().cpu().numpy() if t.dtype != torch.float64 else t.cpu().numpy()
+
+
+def frac_bits(x):
+    """Largest number of fractional binary digits among the non-zero entries of x
+    (fp64 values; every finite double is a dyadic rational)."""
+    x = np.asarray(x, dtype=np.float64).ravel()
+    x = x[x != 0]
+    if x.size == 0:
+        return 0
+    m, e = np.frexp(x)
+    mi = np.abs(m * 2.0 ** 53).astype(np.int64)
+    tz = np.zeros_like(mi)
+    t = mi.copy()
+    for _ in range(54):
+        z = (t & 1) == 0
+        if not z.any():
+            break
+        tz += z
+        t = np.where(z, t >> 1, t)
+    return int(np.max(53 - e - tz))
