@@ -68,11 +68,9 @@ struct Raw {
 constexpr int kP1Threads = 640;   // 4 producer, 4 consumer, 2 inverse waves
 constexpr int kP1Slots = 4;
 enum { P1_R = 0, P1_W = 1, P1_K = 2, P1_A = 3, P1_B = 4, P1_DY = 5 };
-// Tile images in a slot.  TILE_RB/TILE_RBL: hi and lo parts of Arb^T in
-// accumulator layout (Arb's A-operand image), from MW, TILE_RB replaced by INV
-// with the A-operand image of (Arb Tm)^T; TILE_AK, TILE_RK: the A-operand images
-// of Aak^T, Ark^T, from MW.
-enum { TILE_RB = 0, TILE_RBL = 1, TILE_AK = 2, TILE_RK = 3 };
+// Tile images in a slot: the A-operand image of (Arb Tm)^T, from INV; those of
+// Aak^T, Ark^T, from MW.
+enum { TILE_RB = 0, TILE_AK = 1, TILE_RK = 2 };
 
 // Rows [t][j] (the chain reads At, Rt and dy transposed, which gives the
 // matrix-core operand layouts directly) and images: register contents stored
@@ -82,7 +80,7 @@ struct P1Slot {
     bf16_t Bb[kL][kRow];                                // E -> INV; Tm^T Bb from INV -> chain
     bf16_t Kb[kL][kRow], dY[kL][kRow];                  // E -> chain
     float gL[kN];         // G_L of key 16 jt + 4 g + q at word 16 g + 4 jt + q
-    uint2 tiles[4][64];
+    uint2 tiles[3][64];
 };
 // Bh and Kh, read only in the interval after E.
 struct P1SlotBK {
@@ -249,11 +247,9 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
     };
 
     // ---- MW (producer): one 16x16 tile per wave ---------------------------------
-    // Wave p = 1..3 forms a tile from the rows of X = (At or Rt) and Y = (Bh or
-    // Kh): Arb (1), Aak (2), Ark (3); Aab and its inverse come from the inverse
-    // waves.  Waves 2, 3 form [t][s] = X_t . Y_s, whose accumulator registers are
-    // the A-operand images of Aak^T, Ark^T; wave 1 forms [s][t] (Arb's A-operand
-    // image, which the chain multiplies by Tm) in hi and lo parts.
+    // Waves 2, 3 form Aak = tril_-1(At Kh^T), Ark = tril_0(Rt Kh^T) as [t][s] =
+    // X_t . Y_s, whose accumulator registers are the A-operand images of Aak^T,
+    // Ark^T; Aab, Arb and the inverse come from the inverse waves.
     struct MWIn {
         bf16x8 xv[2], yv[2];
     };
@@ -261,7 +257,7 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
         const P1Slot& s = sm.sl[slot_of(c)];
         const P1SlotBK& bk = sm.bk[c & 1];
         const bf16_t(*Xr)[kRow] = (wp & 1) ? s.Rt : s.At;
-        const bf16_t(*Yr)[kRow] = (wp & 2) ? bk.Kh : bk.Bh;
+        const bf16_t(*Yr)[kRow] = bk.Kh;
         MWIn in;
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
@@ -273,16 +269,6 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
     auto stage_MW = [&](int c, const MWIn& in) __attribute__((always_inline)) {
         P1Slot& s = sm.sl[slot_of(c)];
         f32x4 P = zero4();
-        if (wp == 1) {
-#pragma unroll
-            for (int k2 = 0; k2 < 2; ++k2) P = mfma32(in.yv[k2], in.xv[k2], P);   // [s][t]
-#pragma unroll
-            for (int q = 0; q < 4; ++q) P[q] = (4 * g + q <= l16) ? P[q] : 0.f;   // s <= t
-            const Split4 rb = split4(P);
-            s.tiles[TILE_RB][lane] = __builtin_bit_cast(uint2, rb.hi);
-            s.tiles[TILE_RBL][lane] = __builtin_bit_cast(uint2, rb.lo);
-            return;
-        }
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) P = mfma32(in.xv[k2], in.yv[k2], P);   // [t][s] = X_t . Y_s
         const bool diag = wp == 3;   // Ark keeps the diagonal
@@ -295,9 +281,10 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
         s.tiles[wp == 2 ? TILE_AK : TILE_RK][lane] = __builtin_bit_cast(uint2, cvt4(P));
     };
     // ---- INV (inverse waves): Aab, Tm = (I - Aab)^-1, Tm^T Bb, (Arb Tm)^T -------
-    // In the interval after E(c) a wave forms Aab from At and Bh, the inverses of
-    // its 4x4 diagonal blocks and N = Td L (wkv7_mfma.h); in the next it joins
-    // them into Tm and applies Tm, as hi and lo bf16 parts, to the factors of
+    // In the interval after E(c) a wave forms Aab = tril_-1(At Bh^T) and Arb^T
+    // (Arb = tril_0(Rt Bh^T), as [s][t]), the inverses of Aab's 4x4 diagonal
+    // blocks and N = Td L (wkv7_mfma.h); in the next it joins them into Tm and
+    // applies Tm, as hi and lo bf16 parts, to the factors of
     // dX = (Tm^T Bb) dS^T + (Arb Tm)^T dY (the
     // transpose of the forward's Z = (Tm At) S0^T + (Tm Aak) V, with the same
     // cancellations kept inside these products):
@@ -305,37 +292,45 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
     //     + 4 g + q] -- its row layout, written over the same columns of Bb;
     //   Arb Tm from Arb's A-operand image (hi and lo), whose accumulator
     //     registers are the A-operand image of (Arb Tm)^T.
-    auto inv_begin = [&](int c) __attribute__((always_inline)) -> BlockInverse {
+    struct InvState {
+        BlockInverse bi;
+        f32x4 ArbT;   // accumulator layout [s][t]: Arb's A-operand image
+    };
+    auto inv_begin = [&](int c) __attribute__((always_inline)) -> InvState {
         const P1Slot& s = sm.sl[slot_of(c)];
         const P1SlotBK& bk = sm.bk[c & 1];
-        bf16x8 xv[2], yv[2];
+        bf16x8 xv[2], yv[2], rv[2];
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
             xv[k2] = ld8(&s.At[l16][32 * k2 + 8 * g]);
             yv[k2] = ld8(&bk.Bh[l16][32 * k2 + 8 * g]);
+            rv[k2] = ld8(&s.Rt[l16][32 * k2 + 8 * g]);
         }
-        f32x4 P = zero4();
+        f32x4 P = zero4(), R = zero4();
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) P = mfma32(xv[k2], yv[k2], P);   // [t][s]
+        for (int k2 = 0; k2 < 2; ++k2) {
+            P = mfma32(xv[k2], yv[k2], P);   // [t][s] = Aab[t][s]
+            R = mfma32(yv[k2], rv[k2], R);   // [s][t] = Arb[t][s]
+        }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) P[q] = (l16 < 4 * g + q) ? P[q] : 0.f;
-        return unit_lower_inverse_begin(P, g, l16);
+        for (int q = 0; q < 4; ++q) {
+            P[q] = (l16 < 4 * g + q) ? P[q] : 0.f;    // s < t
+            R[q] = (4 * g + q <= l16) ? R[q] : 0.f;   // s <= t
+        }
+        return InvState{unit_lower_inverse_begin(P, g, l16), R};
     };
-    auto inv_end = [&](int c, const BlockInverse& bi) __attribute__((always_inline)) {
+    auto inv_end = [&](int c, const InvState& st) __attribute__((always_inline)) {
         P1Slot& s = sm.sl[slot_of(c)];
         bf16x4 bbT[4];
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) bbT[jt] = ld4_tr(tr_addr(&s.Bb[0][16 * jt], kRow, g, l16));
-        const bf16x4 rbh = __builtin_bit_cast(bf16x4, s.tiles[TILE_RB][lane]);
-        const bf16x4 rbl = __builtin_bit_cast(bf16x4, s.tiles[TILE_RBL][lane]);
-        const Split4 tm = split4(unit_lower_inverse_cols_end(bi));
+        const Split4 tm = split4(unit_lower_inverse_cols_end(st.bi));
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
             const f32x4 d = mfma16(bbT[jt], tm.hi, mfma16(bbT[jt], tm.lo, zero4()));
             *reinterpret_cast<bf16x4*>(&s.Bb[l16][16 * jt + 4 * g]) = cvt4(d);
         }
-        const f32x4 e = mfma16(rbh, tm.hi, mfma16(rbl, tm.hi, mfma16(rbh, tm.lo, zero4())));
-        s.tiles[TILE_RB][lane] = __builtin_bit_cast(uint2, cvt4(e));
+        s.tiles[TILE_RB][lane] = __builtin_bit_cast(uint2, cvt4(mul3(split4(st.ArbT), tm, zero4())));
     };
 
     // ---- chain (consumer): value rows `col` of the adjoint ------------------------
@@ -460,11 +455,11 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
         const int it_ = (IT);                                                  \
         const ERaw er = read_E(chunk_of(it_));                                 \
         MWIn mi;                                                               \
-        if (it_ >= 1 && (kAB ? wp != 0 : wp == 3)) mi = read_MW(chunk_of(it_ - 1)); \
+        if (it_ >= 1 && (kAB ? wp >= 2 : wp == 3)) mi = read_MW(chunk_of(it_ - 1)); \
         stage_E(chunk_of(it_), er);                                            \
         stash_raw(chunk_of(it_ + 1), RING);                                    \
         load_raw(chunk_of(it_ + 4), RING);                                     \
-        if (it_ >= 1 && (kAB ? wp != 0 : wp == 3)) stage_MW(chunk_of(it_ - 1), mi); \
+        if (it_ >= 1 && (kAB ? wp >= 2 : wp == 3)) stage_MW(chunk_of(it_ - 1), mi); \
         __syncthreads();                                                       \
     }
             for (int it = 0; it < n_it; it += 3) {
@@ -479,15 +474,15 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
             // chunk_of(j) belongs to wave 8 + (j & 1), which starts its inverse in
             // interval j + 1 (after E) and finishes it, with the dX factors, in
             // interval j + 2 (the chain reads them in interval j + 3): one half
-            // per wave and interval, `bi` carrying an inverse across one barrier.
+            // per wave and interval, `st` carrying an inverse across one barrier.
             const int par = wave & 1;
-            BlockInverse bi{zero4(), zero4(), zero4()};
+            InvState st{{zero4(), zero4(), zero4()}, zero4()};
             for (int it = 0; it < n_it; ++it) {
                 if (kAB && it >= 1) {
                     if (((it - 1) & 1) == par)
-                        bi = inv_begin(chunk_of(it - 1));
+                        st = inv_begin(chunk_of(it - 1));
                     else if (it >= 2)
-                        inv_end(chunk_of(it - 2), bi);
+                        inv_end(chunk_of(it - 2), st);
                 }
                 __syncthreads();
             }

@@ -23,8 +23,8 @@
 //         accesses, the running product over tokens a DPP scan); the
 //         consumers read Bb, Kb and v transposed (ds_read_b64_tr_b16), which
 //         is the layout their matrix-core products take;
-//     MW  one 16x16 tile each on waves 1..3: Aak, Arb, Ark.
-//   Two more waves form Aab and its triangular inverse Tm = (I - Aab)^-1
+//     MW  one 16x16 tile each on waves 2, 3: Arb, Ark.
+//   Two more waves form Aab, Aak and the triangular inverse Tm = (I - Aab)^-1
 //   (4x4 diagonal blocks in fp32, joined on the matrix core: wkv7_mfma.h),
 //   off the producers' path: wave 8 for even chunks, wave 9 for odd ones, each
 //   inverse spread over two intervals.
@@ -68,11 +68,9 @@ constexpr int kThreads = 640;   // 4 producer, 4 consumer, 2 inverse waves
 constexpr int kRow = kN + 8;    // rows of 64 elements
 
 enum { RAW_R = 0, RAW_W = 1, RAW_K = 2, RAW_A = 3, RAW_B = 4, RAW_V = 5 };
-// Tile images in a slot.  TILE_AK/TILE_AKL: hi and lo parts of Aak in
-// accumulator layout (Aak[4g+q][l16], the A-operand image of Aak^T), from MW;
-// INV replaces TILE_AK by the A-operand image of Aak' = Tm Aak.  TILE_RB,
-// TILE_RK: A-operand images of Arb, Ark, from MW.
-enum { TILE_AK = 0, TILE_AKL = 1, TILE_RB = 2, TILE_RK = 3 };
+// Tile images in a slot: the A-operand images of Aak' = Tm Aak (from INV) and
+// of Arb, Ark (from MW).
+enum { TILE_AK = 0, TILE_RB = 1, TILE_RK = 2 };
 constexpr int kSlots = 4;
 
 // Everything one chunk passes from the producers to the consumers: rows
@@ -84,7 +82,7 @@ struct Slot {
     bf16_t Rt[kL][kRow];            // E -> MW, ST
     bf16_t Bb[kL][kRow], Kb[kL][kRow], V[kL][kRow];   // E -> ST
     float gL[kN];   // E -> ST: G_L of key 16 jt + 4 g + q at word 16 g + 4 jt + q
-    uint2 tiles[4][64];
+    uint2 tiles[3][64];
 };
 // Bh and Kh, read only in the interval after E.
 struct SlotBK {
@@ -311,18 +309,16 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
     };
 
     // ---- MW (producer): one 16x16 tile per wave ---------------------------------
-    // Wave p forms a tile from the rows of X = (At or Rt) and Y = (Bh or Kh):
-    // Aak (1), Arb (2), Ark (3).  Accumulator registers of M^T fed as an A
-    // operand stand for M, so waves 2, 3 form the transposed product [s][t] =
-    // X_t . Y_s (the A-operand images of Arb, Ark); wave 1 forms [t][s] (the
-    // accumulator layout of Aak, which PRE multiplies by Tm) in hi and lo parts.
+    // Waves 2, 3 form Arb = tril_0(Rt Bh^T), Ark = tril_0(Rt Kh^T) as the
+    // transposed product [s][t] = Rt_t . Y_s: accumulator registers of M^T fed
+    // as an A operand stand for M, so these are the A-operand images.
     struct MWIn {
         bf16x8 xv[2], yv[2];
     };
     auto read_MW = [&](int c) __attribute__((always_inline)) -> MWIn {
         const Slot& s = sm.sl[c % kSlots];
         const SlotBK& bk = sm.bk[c & 1];
-        const bf16_t(*Xr)[kRow] = (wp & 2) ? s.Rt : s.At;
+        const bf16_t(*Xr)[kRow] = s.Rt;
         const bf16_t(*Yr)[kRow] = (wp & 1) ? bk.Kh : bk.Bh;
         MWIn in;
 #pragma unroll
@@ -335,16 +331,6 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
     auto stage_MW = [&](int c, const MWIn& in) __attribute__((always_inline)) {
         Slot& s = sm.sl[c % kSlots];
         f32x4 PT = zero4();
-        if (wp == 1) {
-#pragma unroll
-            for (int k2 = 0; k2 < 2; ++k2) PT = mfma32(in.xv[k2], in.yv[k2], PT);   // [t][s]
-#pragma unroll
-            for (int q = 0; q < 4; ++q) PT[q] = (l16 < 4 * g + q) ? PT[q] : 0.f;   // s < t
-            const Split4 ak = split4(PT);
-            s.tiles[TILE_AK][lane] = __builtin_bit_cast(uint2, ak.hi);
-            s.tiles[TILE_AKL][lane] = __builtin_bit_cast(uint2, ak.lo);
-            return;
-        }
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) PT = mfma32(in.yv[k2], in.xv[k2], PT);   // [s][t]
 #pragma unroll
@@ -354,46 +340,55 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
         }
         s.tiles[wp == 2 ? TILE_RB : TILE_RK][lane] = __builtin_bit_cast(uint2, cvt4(PT));
     };
-    // ---- INV (inverse waves): Aab, Tm = (I - Aab)^-1, At' and Aak' -------------
-    // In the interval after E(c) a wave forms Aab from At and Bh, the inverses of
-    // its 4x4 diagonal blocks and N = Td L (wkv7_mfma.h); in the next it joins
-    // them into Tm and applies Tm, as hi and lo bf16 images, to the factors of Z:
+    // ---- INV (inverse waves): Aab, Aak, Tm = (I - Aab)^-1, At' and Aak' --------
+    // In the interval after E(c) a wave forms Aab = tril_-1(At Bh^T) and Aak =
+    // tril_-1(At Kh^T) (accumulator layout [t][s]), the inverses of Aab's 4x4
+    // diagonal blocks and N = Td L (wkv7_mfma.h); in the next it joins them into
+    // Tm and applies Tm, as hi and lo bf16 images, to the factors of Z:
     //   At'^T tile jt = At^T[keys 16 jt ..] Tm^T, whose accumulator registers
     //     hold At'[l16][16 jt + 4 g + q] -- the row layout of At', written over
     //     the same columns of At (read first, by transposed reads);
     //   Aak'^T = Aak^T Tm^T from Aak's accumulator layout (hi and lo), whose
     //     accumulator registers are Aak''s A-operand image.
-    auto inv_begin = [&](int c) __attribute__((always_inline)) -> BlockInverse {
+    struct InvState {
+        BlockInverse bi;
+        f32x4 Aak;   // accumulator layout [t][s]
+    };
+    auto inv_begin = [&](int c) __attribute__((always_inline)) -> InvState {
         const Slot& s = sm.sl[c % kSlots];
         const SlotBK& bk = sm.bk[c & 1];
-        bf16x8 xv[2], yv[2];
+        bf16x8 xv[2], yv[2], kv[2];
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
             xv[k2] = ld8(&s.At[l16][32 * k2 + 8 * g]);
             yv[k2] = ld8(&bk.Bh[l16][32 * k2 + 8 * g]);
+            kv[k2] = ld8(&bk.Kh[l16][32 * k2 + 8 * g]);
         }
-        f32x4 P = zero4();
+        f32x4 P = zero4(), K = zero4();
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) P = mfma32(xv[k2], yv[k2], P);   // [t][s] = Aab[t][s]
+        for (int k2 = 0; k2 < 2; ++k2) {
+            P = mfma32(xv[k2], yv[k2], P);   // [t][s] = Aab[t][s]
+            K = mfma32(xv[k2], kv[k2], K);   // [t][s] = Aak[t][s]
+        }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) P[q] = (l16 < 4 * g + q) ? P[q] : 0.f;
-        return unit_lower_inverse_begin(P, g, l16);
+        for (int q = 0; q < 4; ++q) {
+            P[q] = (l16 < 4 * g + q) ? P[q] : 0.f;
+            K[q] = (l16 < 4 * g + q) ? K[q] : 0.f;
+        }
+        return InvState{unit_lower_inverse_begin(P, g, l16), K};
     };
-    auto inv_end = [&](int c, const BlockInverse& bi) __attribute__((always_inline)) {
+    auto inv_end = [&](int c, const InvState& st) __attribute__((always_inline)) {
         Slot& s = sm.sl[c % kSlots];
         bf16x4 atT[4];
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) atT[jt] = ld4_tr(tr_addr(&s.At[0][16 * jt], kRow, g, l16));
-        const bf16x4 akh = __builtin_bit_cast(bf16x4, s.tiles[TILE_AK][lane]);
-        const bf16x4 akl = __builtin_bit_cast(bf16x4, s.tiles[TILE_AKL][lane]);
-        const Split4 tm = split4(unit_lower_inverse_rows_end(bi, g, l16));
+        const Split4 tm = split4(unit_lower_inverse_rows_end(st.bi, g, l16));
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
             const f32x4 d = mfma16(atT[jt], tm.hi, mfma16(atT[jt], tm.lo, zero4()));
             *reinterpret_cast<bf16x4*>(&s.At[l16][16 * jt + 4 * g]) = cvt4(d);
         }
-        const f32x4 e = mfma16(akh, tm.hi, mfma16(akl, tm.hi, mfma16(akh, tm.lo, zero4())));
-        s.tiles[TILE_AK][lane] = __builtin_bit_cast(uint2, cvt4(e));
+        s.tiles[TILE_AK][lane] = __builtin_bit_cast(uint2, cvt4(mul3(split4(st.Aak), tm, zero4())));
     };
 
     // ---- ST (consumer): value-row block `col` of the state chain of chunk c -----
@@ -532,11 +527,11 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
         const int c_ = cb + it_;                                            \
         const ERaw er = read_E(c_);                                         \
         MWIn mi;                                                            \
-        if (it_ >= 1 && (kAB ? wp != 0 : wp == 3)) mi = read_MW(c_ - 1);    \
+        if (it_ >= 1 && (kAB ? wp >= 2 : wp == 3)) mi = read_MW(c_ - 1);    \
         stage_E(c_, er);                                                    \
         stash_raw(c_ + 1, RING);                                            \
         load_raw(c_ + 4, RING);                                             \
-        if (it_ >= 1 && (kAB ? wp != 0 : wp == 3)) stage_MW(c_ - 1, mi);    \
+        if (it_ >= 1 && (kAB ? wp >= 2 : wp == 3)) stage_MW(c_ - 1, mi);    \
         __syncthreads();                                                    \
     }
             // Ring slot of interval it is (it + 1) % 3: it = 0, 1, 2 -> rb1, rb2, rb0.
@@ -554,16 +549,16 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
             // Chunk cb + j belongs to wave 8 + (j & 1), which starts its inverse in
             // interval j + 1 (after E) and finishes it, with At' and Aak', in
             // interval j + 2 (the consumers read them in interval j + 3); so each
-            // of the two waves runs one half per interval, `bi` carrying an
+            // of the two waves runs one half per interval, `st` carrying an
             // inverse across one barrier.
             const int par = wave & 1;
-            BlockInverse bi{zero4(), zero4(), zero4()};
+            InvState st{{zero4(), zero4(), zero4()}, zero4()};
             for (int it = 0; it < n_it; ++it) {
                 if (kAB && it >= 1) {
                     if (((it - 1) & 1) == par)
-                        bi = inv_begin(cb + it - 1);
+                        st = inv_begin(cb + it - 1);
                     else if (it >= 2)
-                        inv_end(cb + it - 2, bi);
+                        inv_end(cb + it - 2, st);
                 }
                 __syncthreads();
             }
