@@ -37,7 +37,8 @@
  *       WKV7_ERR_INVALID_ARG  negative sizes, NULL required pointers, pointers
  *                             not 16-byte aligned, NULL desc;
  *       WKV7_ERR_UNSUPPORTED  unsupported head size (below), unknown dtype,
- *                             unsupported chunk_len;
+ *                             unsupported chunk_len, T above INT32_MAX - 64,
+ *                             more than 2^28 heads (B*H);
  *       WKV7_ERR_WORKSPACE    workspace smaller than wkv7_workspace_bytes();
  *       WKV7_ERR_LAUNCH       the HIP runtime reported a launch error.
  *     No exception crosses the ABI.  There is no global mutable state, so
@@ -200,7 +201,14 @@ int wkv7_forward_ckpt(const wkv7_desc *desc, const void *r, const void *w, const
  * Sequential: one workgroup per segment, numbered segment by segment over all
  * heads; each waits for its head's previous segment to publish its final state
  * (fp32, in the workspace) and publishes its own.  No extra work: the device
- * takes segments as they come instead of whole heads.
+ * takes segments as they come instead of whole heads.  This relies on the
+ * device dispatching a grid's workgroups in order (a segment waits only for
+ * one dispatched before it).  The wait is bounded (about a second; the
+ * environment variable WKV7_SEGMENT_SPIN_LIMIT sets the number of polls): a
+ * segment whose wait expires starts from a NaN state, so its y, tape and
+ * final state, and those of the head's later segments, are NaN -- an expired
+ * wait never yields plausible but wrong results.  The status stays WKV7_OK
+ * (the launch cannot report it); check the outputs when in doubt.
  * The automatic choice depends on the current device: query the size and call
  * on the same one.
  */

@@ -4,6 +4,7 @@
 #include "wkv7.h"
 
 #include <hip/hip_runtime.h>
+#include <stdlib.h>
 
 #include "wkv7_internal.h"
 
@@ -30,6 +31,8 @@ int check_desc(const wkv7_desc* d) {
     if (d->chunk_len != 0 && d->dtype != WKV7_BF16) return WKV7_ERR_UNSUPPORTED;
     // Grid dimensions are B*H (times 4) workgroups.
     if ((int64_t)d->B * d->H > (int64_t)(1 << 28)) return WKV7_ERR_UNSUPPORTED;
+    // Token and chunk indices are 32-bit in the kernels and their launchers.
+    if (d->T > INT32_MAX - 64) return WKV7_ERR_UNSUPPORTED;
     return WKV7_OK;
 }
 
@@ -84,17 +87,31 @@ int device_cus() {
 constexpr int kMaxSegments = 16;
 constexpr int kMinSegmentTokens = 128;
 
+// Polls of a sequential segment's wait for its predecessor (each a short sleep:
+// about a second in all); WKV7_SEGMENT_SPIN_LIMIT, a non-negative integer,
+// overrides it (a small value forces the wait to expire, for testing that an
+// expired wait shows as NaN outputs).
+int segment_spin_limit() {
+    const char* e = getenv("WKV7_SEGMENT_SPIN_LIMIT");
+    if (e && *e) {
+        char* end = nullptr;
+        const long v = strtol(e, &end, 10);
+        if (end && *end == '\0' && v >= 0 && v <= (1L << 30)) return (int)v;
+    }
+    return 1 << 24;
+}
+
 struct SplitPlan {
     int split_from, nseg, seg_len, mode;
 };
 
 int segment_length(int T, int& nseg) {
     // Segments start at multiples of the tape's state block; the last one must
-    // keep at least one token.
+    // keep at least one token.  (64-bit arithmetic: T may be close to INT32_MAX.)
     while (nseg >= 2) {
-        const int per = (T + nseg - 1) / nseg;
-        const int len = (per + WKV7_TAPE_BLOCK - 1) / WKV7_TAPE_BLOCK * WKV7_TAPE_BLOCK;
-        if ((int64_t)(nseg - 1) * len < T) return len;
+        const int64_t per = ((int64_t)T + nseg - 1) / nseg;
+        const int64_t len = (per + WKV7_TAPE_BLOCK - 1) / WKV7_TAPE_BLOCK * WKV7_TAPE_BLOCK;
+        if ((nseg - 1) * len < T) return (int)len;
         --nseg;
     }
     return T;
@@ -231,10 +248,15 @@ size_t wkv7_forward_split_workspace_bytes(const wkv7_desc* desc, int32_t segment
     return split_bytes(desc, plan_split(desc, segments, segments == 0 ? device_cus() : 0));
 }
 
-int wkv7_forward_split(const wkv7_desc* desc, const void* r, const void* w, const void* k,
-                       const void* v, const void* a, const void* b, const float* s0, void* y,
-                       float* sT, void* tape, int32_t segments, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// wkv7_forward_split.
+int run_forward_split(const wkv7_desc* desc, const void* r, const void* w, const void* k,
+                      const void* v, const void* a, const void* b, const float* s0, void* y,
+                      float* sT, void* tape, int32_t segments, void* workspace,
+                      size_t workspace_bytes, void* stream) {
     const int st = check_desc(desc);
     if (st != WKV7_OK) return st;
     if (segments < -kMaxSegments) return WKV7_ERR_INVALID_ARG;
@@ -258,9 +280,21 @@ int wkv7_forward_split(const wkv7_desc* desc, const void* r, const void* w, cons
         float* states = static_cast<float*>(workspace);
         int* sync = reinterpret_cast<int*>(states + (size_t)desc->B * desc->H * desc->N * desc->N);
         return from_hip(wkv7::launch_chunk_fwd_sequential(p, 16, plan.nseg, plan.seg_len, states,
-                                                          sync, s));
+                                                          sync, segment_spin_limit(), s));
     }
     return from_hip(wkv7::launch_chunk_fwd_split(p, 16, sp, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int wkv7_forward_split(const wkv7_desc* desc, const void* r, const void* w, const void* k,
+                       const void* v, const void* a, const void* b, const float* s0, void* y,
+                       float* sT, void* tape, int32_t segments, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    return run_forward_split(desc, r, w, k, v, a, b, s0, y, sT, tape, segments, workspace,
+                             workspace_bytes, stream);
 }
 
 }  // extern "C"
@@ -309,7 +343,7 @@ int run_backward(const wkv7_desc* desc, const void* r, const void* w, const void
     // has no separate stages.
     if (!seq && (desc->dtype != WKV7_BF16 || desc->N != WKV7_HEAD_SIZE)) return WKV7_ERR_UNSUPPORTED;
     if (seq && stages != (wkv7::BWD_CHAIN | wkv7::BWD_KEYS)) return WKV7_ERR_UNSUPPORTED;
-    if ((int64_t)desc->B * desc->H * ((desc->T + WKV7_TAPE_CHUNK - 1) / WKV7_TAPE_CHUNK) > INT32_MAX)
+    if ((int64_t)desc->B * desc->H * (((int64_t)desc->T + WKV7_TAPE_CHUNK - 1) / WKV7_TAPE_CHUNK) > INT32_MAX)
         return WKV7_ERR_UNSUPPORTED;
     const bool has_tokens = (int64_t)desc->B * desc->T * desc->H > 0;
     // With a = b = 0 (both null) da and db are not written and may be null.
@@ -376,7 +410,7 @@ int run_backward(const wkv7_desc* desc, const void* r, const void* w, const void
     hipEvent_t chained = nullptr, keyed = nullptr;
     if (hipEventCreateWithFlags(&chained, hipEventDisableTiming) != hipSuccess) return WKV7_ERR_LAUNCH;
     if (hipEventCreateWithFlags(&keyed, hipEventDisableTiming) != hipSuccess) {
-        hipEventDestroy(chained);
+        (void)hipEventDestroy(chained);
         return WKV7_ERR_LAUNCH;
     }
     hipError_t e = wkv7::launch_bwd(g1, 16, wkv7::BWD_CHAIN, s);
@@ -386,8 +420,8 @@ int run_backward(const wkv7_desc* desc, const void* r, const void* w, const void
     if (e == hipSuccess) e = hipEventRecord(keyed, s2);
     if (e == hipSuccess) e = wkv7::launch_bwd(g2, 16, wkv7::BWD_CHAIN | wkv7::BWD_KEYS, s);
     if (e == hipSuccess) e = hipStreamWaitEvent(s, keyed, 0);
-    hipEventDestroy(chained);
-    hipEventDestroy(keyed);
+    (void)hipEventDestroy(chained);
+    (void)hipEventDestroy(keyed);
     return from_hip(e);
 }
 

@@ -116,11 +116,14 @@ struct Raw {
 // workgroup per segment, numbered segment-major: workgroup u runs segment
 // u / (B*H) of head u % (B*H).  Its entry state is the final state that the
 // head's previous segment (workgroup u - B*H) left in `states` (slot = head),
-// announced by the head's flag sync[head] = segments done.  Workgroups are
-// dispatched in order, so the one waited for started earlier and finishes
-// without waiting on any later one: the wait ends.  It is bounded all the same
-// (about a second), so that no fault elsewhere can turn it into a hang.
-constexpr int kSpinLimit = 1 << 24;
+// announced by the head's flag sync[head] = segments done.  The scheme assumes
+// that the device dispatches a grid's workgroups in order: the one waited for
+// was dispatched earlier and finishes without waiting on any later one, so the
+// wait ends.  It is bounded all the same (`spin_limit` polls, about a second by
+// default), so that no fault elsewhere can turn it into a hang; a workgroup
+// whose wait expires starts from a NaN state instead of the unpublished one,
+// so its y, tape and final state -- and those of every later segment of the
+// head, which start from them -- come out NaN rather than plausibly wrong.
 
 // kAB = false: a_t = b_t = 0 (decay-only linear attention, the RWKV-6-style
 // recurrence S <- S diag(w_t) + v_t k_t^T).  a and b are then not read; the
@@ -136,22 +139,34 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
     const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const bf16_t* __restrict__ a,
     const bf16_t* __restrict__ b, const float* __restrict__ s0, bf16_t* __restrict__ y_all,
     float* __restrict__ sT, bf16_t* __restrict__ tape_all, float* __restrict__ ckpt_all, int pass,
-    int split_from, int nseg, int seg_len, float* __restrict__ states, int* __restrict__ sync) {
+    int split_from, int nseg, int seg_len, float* __restrict__ states, int* __restrict__ sync,
+    int spin_limit) {
     __shared__ FwdSmem sm;
+    __shared__ int entry_lost_sm;
     constexpr size_t NN = (size_t)kN * kN;
     Work wk;
     int seg = 0;
+    bool entry_lost = false;
     if (kSeq) {
         const int nbh = B * H;
         seg = blockIdx.x / nbh;
         const int h = blockIdx.x % nbh;
-        if (threadIdx.x == 0 && seg > 0) {
-            for (int spin = 0; spin < kSpinLimit &&
-                               __hip_atomic_load(&sync[h], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < seg;
-                 ++spin)
-                __builtin_amdgcn_s_sleep(2);
+        if (threadIdx.x == 0) {
+            int lost = 0;
+            if (seg > 0) {
+                for (int spin = 0;
+                     __hip_atomic_load(&sync[h], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < seg; ++spin) {
+                    if (spin >= spin_limit) {
+                        lost = 1;
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(2);
+                }
+            }
+            entry_lost_sm = lost;
         }
         __syncthreads();
+        entry_lost = entry_lost_sm != 0;
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // the previous segment's state
         wk = Work{h, seg * seg_len, seg == nseg - 1 ? T : (seg + 1) * seg_len,
                   seg == 0 ? (s0 ? s0 + (size_t)h * NN : nullptr) : states + (size_t)h * NN,
@@ -193,7 +208,11 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt) S[jt] = zero4();
     if (consumer) {
-        if (wk.init) {
+        if (kSeq && entry_lost) {
+            const float nan = __builtin_nanf("");
+#pragma unroll
+            for (int jt = 0; jt < 4; ++jt) S[jt] = f32x4{nan, nan, nan, nan};
+        } else if (wk.init) {
             const float* base = wk.init + (size_t)col * kN;
 #pragma unroll
             for (int jt = 0; jt < 4; ++jt) {
@@ -663,7 +682,7 @@ hipError_t launch_chunk_fwd(const FwdArgs& p, int chunk_len, hipStream_t stream)
 }
 
 hipError_t launch_chunk_fwd_sequential(const FwdArgs& p, int chunk_len, int nseg, int seg_len,
-                                       float* states, int* sync, hipStream_t stream) {
+                                       float* states, int* sync, int spin_limit, hipStream_t stream) {
     if (chunk_len != kL || !p.bf16) return hipErrorInvalidValue;
     const int nbh = p.B * p.H;
     if (nseg < 1 || seg_len <= 0 || seg_len % WKV7_TAPE_BLOCK != 0 ||
@@ -680,7 +699,7 @@ hipError_t launch_chunk_fwd_sequential(const FwdArgs& p, int chunk_len, int nseg
         static_cast<const bf16_t*>(p.k), static_cast<const bf16_t*>(p.v),
         static_cast<const bf16_t*>(p.a), static_cast<const bf16_t*>(p.b), p.s0,
         static_cast<bf16_t*>(p.y), p.sT, static_cast<bf16_t*>(p.tape), p.ckpt, 2, 0, nseg, seg_len,
-        states, sync);
+        states, sync, spin_limit < 0 ? 0 : spin_limit);
     return hipGetLastError();
 }
 
@@ -700,7 +719,7 @@ hipError_t launch_chunk_fwd_split(const FwdArgs& p, int chunk_len, const FwdSpli
             static_cast<const bf16_t*>(p.k), static_cast<const bf16_t*>(p.v),
             static_cast<const bf16_t*>(p.a), static_cast<const bf16_t*>(p.b), p.s0,
             static_cast<bf16_t*>(p.y), p.sT, static_cast<bf16_t*>(p.tape), p.ckpt, pass,
-            sp.split_from, sp.nseg, sp.seg_len, sp.states, nullptr);
+            sp.split_from, sp.nseg, sp.seg_len, sp.states, nullptr, 0);
         return hipGetLastError();
     };
     hipError_t e = run(0, sp.split_from + (nsplit > 0 ? nsplit * (2 * sp.nseg - 3) : 0));

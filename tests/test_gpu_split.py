@@ -234,3 +234,37 @@ def test_tape_into_caller_buffer(wk):
         assert got.data_ptr() == buf.data_ptr()
         assert torch.equal(buf[:nbytes // 2], ref[:nbytes // 2]), seg
         assert bool((buf[nbytes // 2:] == 3.0).all())   # nothing written past the tape
+
+
+def test_expired_segment_wait_shows_as_nan(wk, monkeypatch):
+    """Sequential segments with the wait forced to expire from the host
+    (WKV7_SEGMENT_SPIN_LIMIT=0: no polling, so a segment whose predecessor has
+    not yet published gives up at once).  Every kernel still exits normally,
+    and no segment is ever silently wrong: each is either the oracle's result or
+    entirely NaN, a NaN segment makes every later segment of its head and the
+    final state NaN."""
+    monkeypatch.setenv("WKV7_SEGMENT_SPIN_LIMIT", "0")
+    B, T, H, nseg = 4, 512, 8, 4
+    inp = synth.generate(B, T, H, 64, dtype="bf16", seed=78, random_s0=True)
+    y, sT, _ = _run(wk, inp, -nseg)
+    yr, sr = oracle.forward(*inp.tensors(), inp.s0)
+    seg_len = T // nseg
+    lost_heads = 0
+    for b in range(B):
+        for h in range(H):
+            lost = False
+            for sg in range(nseg):
+                blk = y[b, sg * seg_len:(sg + 1) * seg_len, h]
+                if np.isnan(blk).all():
+                    lost = True
+                    continue
+                assert not lost, f"head ({b}, {h}) segment {sg} follows a NaN segment but is not NaN"
+                assert not np.isnan(blk).any(), f"head ({b}, {h}) segment {sg} partly NaN"
+                ref = yr[b, sg * seg_len:(sg + 1) * seg_len, h]
+                assert np.abs(blk - ref).max() <= 2e-2 * np.abs(ref).max(), f"head ({b}, {h}) segment {sg}"
+            if lost:
+                lost_heads += 1
+                assert np.isnan(sT[b, h]).all()
+            else:
+                assert_close(sT[b, h], sr[b, h], "bf16", f"head ({b}, {h}) sT")
+    print(f"{lost_heads} of {B * H} heads had a segment whose wait expired")
