@@ -81,8 +81,13 @@ typedef enum {
     WKV7_ERR_INVALID_ARG = 1,
     WKV7_ERR_UNSUPPORTED = 2,
     WKV7_ERR_WORKSPACE = 3,
-    WKV7_ERR_LAUNCH = 4
+    WKV7_ERR_LAUNCH = 4,
+    WKV7_ERR_STATIC_SCRATCH = 5   /* the call needs more than WKV7_STATIC_SCRATCH_BYTES */
 } wkv7_status;
+
+/* Size of the device scratch that wkv7_forward_split_static uses in place of a
+   workspace (one copy per device, held until the process ends). */
+#define WKV7_STATIC_SCRATCH_BYTES (16u << 20)
 
 typedef enum { WKV7_F32 = 0, WKV7_BF16 = 1 } wkv7_dtype;
 
@@ -217,6 +222,26 @@ int wkv7_forward_split(const wkv7_desc *desc, const void *r, const void *w, cons
                        const void *v, const void *a, const void *b, const float *s0, void *y,
                        float *sT, void *tape, int32_t segments, void *workspace,
                        size_t workspace_bytes, void *stream);
+
+/*
+ * wkv7_forward_split without a workspace, for callers that cannot allocate
+ * device memory (code under stream capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments (minus the workspace) and results
+ * as wkv7_forward_split: the segment plan's scratch (the entry states and maps,
+ * or the sequential segments' states and flags) lives in a fixed device buffer
+ * of WKV7_STATIC_SCRATCH_BYTES inside the library, one per device.  A call
+ * whose plan needs more returns WKV7_ERR_STATIC_SCRATCH and launches nothing
+ * (wkv7_forward_split_workspace_bytes gives the need).  The call allocates
+ * nothing: the buffer's device address is looked up on the first call on each
+ * device.  Every call on a device shares that device's buffer, so calls that
+ * overlap on one device (other streams, other threads) race: serialise them.
+ * The buffer keeps the previous call's contents; nothing in it is read before
+ * the call writes it (the sequential segments' flags are cleared by a kernel).
+ */
+int wkv7_forward_split_static(const wkv7_desc *desc, const void *r, const void *w,
+                              const void *k, const void *v, const void *a, const void *b,
+                              const float *s0, void *y, float *sT, void *tape, int32_t segments,
+                              void *stream);
 
 /*
  * Gradients of the scalar  L = sum_t <dy_t, y_t> + <dsT, S_T>  with respect to

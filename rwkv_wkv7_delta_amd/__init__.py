@@ -28,6 +28,8 @@ WKV7_ERR_INVALID_ARG = 1
 WKV7_ERR_UNSUPPORTED = 2
 WKV7_ERR_WORKSPACE = 3
 WKV7_ERR_LAUNCH = 4
+WKV7_ERR_STATIC_SCRATCH = 5
+STATIC_SCRATCH_BYTES = 16 << 20
 WKV7_F32 = 0
 WKV7_BF16 = 1
 HEAD_SIZE = 64
@@ -37,6 +39,7 @@ TAPE_BLOCK = 32
 EXPORTED = ("wkv7_abi_version", "wkv7_status_string", "wkv7_tape_bytes", "wkv7_ckpt_bytes",
             "wkv7_workspace_bytes", "wkv7_backward_workspace_bytes", "wkv7_forward",
             "wkv7_forward_ckpt", "wkv7_forward_split_workspace_bytes", "wkv7_forward_split",
+            "wkv7_forward_split_static",
             "wkv7_backward", "wkv7_backward_ckpt", "wkv7_backward_adjoint", "wkv7_backward_gradients",
             "wkv7_backward_overlapped", "wkv7_decode_step")
 
@@ -89,6 +92,8 @@ def lib():
         L.wkv7_forward_split_workspace_bytes.restype = Z
         L.wkv7_forward_split.argtypes = [D] + [P] * 6 + [P, P, P, P, I, P, Z, P]
         L.wkv7_forward_split.restype = ctypes.c_int
+        L.wkv7_forward_split_static.argtypes = [D] + [P] * 6 + [P, P, P, P, I, P]
+        L.wkv7_forward_split_static.restype = ctypes.c_int
         for name in ("wkv7_backward", "wkv7_backward_adjoint", "wkv7_backward_gradients"):
             fn = getattr(L, name)
             fn.argtypes = [D] + [P] * 6 + [P, P, P, P] + [P] * 6 + [P, P, Z, P]
@@ -187,7 +192,7 @@ def split_tape(tape, B: int, T: int, H: int, N: int = HEAD_SIZE):
 
 def forward(r, w, k, v, a, b, s0=None, *, chunk_len: int = 0, want_state: bool = True,
             want_tape: bool = False, out=None, segments: Optional[int] = None, workspace=None,
-            tape_out=None, want_ckpt: bool = False):
+            tape_out=None, want_ckpt: bool = False, static_scratch: bool = False):
     """Run the recurrence over [B, T, H, N] inputs.
 
     Returns ``(y, sT, tape)``; ``sT`` / ``tape`` are None unless requested (the
@@ -195,7 +200,9 @@ def forward(r, w, k, v, a, b, s0=None, *, chunk_len: int = 0, want_state: bool =
     ``chunk_len`` 0 = sequential scan, 16 = chunked bf16-MFMA form.
     ``segments`` (not None) selects wkv7_forward_split: 0 = the library's
     choice, 1 = no split, n >= 2 = every head in up to n time segments;
-    ``workspace`` is then its device scratch (allocated here when None).
+    ``workspace`` is then its device scratch (allocated here when None), or,
+    with ``static_scratch``, wkv7_forward_split_static runs instead, with the
+    library's own fixed scratch (nothing is allocated for it).
     ``tape_out`` (a bf16 device tensor of at least ``tape_bytes`` bytes) receives
     the tape instead of a new allocation.  ``want_ckpt`` selects
     wkv7_forward_ckpt instead: the third result is then the fp32 state entering
@@ -235,6 +242,13 @@ def forward(r, w, k, v, a, b, s0=None, *, chunk_len: int = 0, want_state: bool =
                                 _ptr(b), _ptr(s0), _ptr(y), _ptr(sT), _ptr(ck), _stream())
         if st != WKV7_OK:
             raise WKV7Error(st, "wkv7_forward")
+        return y, sT, ck
+    if static_scratch:
+        st = lib().wkv7_forward_split_static(ctypes.byref(desc), _ptr(r), _ptr(w), _ptr(k), _ptr(v),
+                                             _ptr(a), _ptr(b), _ptr(s0), _ptr(y), _ptr(sT), _ptr(ck),
+                                             segments, _stream())
+        if st != WKV7_OK:
+            raise WKV7Error(st, "wkv7_forward_split_static")
         return y, sT, ck
     wsb = split_workspace_bytes(desc, segments)
     ws = workspace

@@ -195,6 +195,9 @@ const char* wkv7_status_string(int status) {
         case WKV7_ERR_UNSUPPORTED: return "unsupported configuration (head size, dtype or chunk length)";
         case WKV7_ERR_WORKSPACE: return "workspace too small";
         case WKV7_ERR_LAUNCH: return "kernel launch failed";
+        case WKV7_ERR_STATIC_SCRATCH:
+            return "the call needs more scratch than the library's static buffer holds "
+                   "(WKV7_STATIC_SCRATCH_BYTES = 16 MiB); use wkv7_forward_split with a workspace";
         default: return "unknown status";
     }
 }
@@ -252,11 +255,12 @@ size_t wkv7_forward_split_workspace_bytes(const wkv7_desc* desc, int32_t segment
 
 namespace {
 
-// wkv7_forward_split.
+// wkv7_forward_split; `use_static` takes the scratch from the library's static
+// buffer instead of `workspace`.
 int run_forward_split(const wkv7_desc* desc, const void* r, const void* w, const void* k,
                       const void* v, const void* a, const void* b, const float* s0, void* y,
                       float* sT, void* tape, int32_t segments, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+                      size_t workspace_bytes, void* stream, bool use_static) {
     const int st = check_desc(desc);
     if (st != WKV7_OK) return st;
     if (segments < -kMaxSegments) return WKV7_ERR_INVALID_ARG;
@@ -269,6 +273,11 @@ int run_forward_split(const wkv7_desc* desc, const void* r, const void* w, const
     if (!(opt(s0) && opt(sT) && opt(tape) && opt(workspace))) return WKV7_ERR_INVALID_ARG;
     const SplitPlan plan = plan_split(desc, segments, segments == 0 ? device_cus() : 0);
     const size_t need = split_bytes(desc, plan);
+    if (use_static && need > 0) {
+        if (need > WKV7_STATIC_SCRATCH_BYTES) return WKV7_ERR_STATIC_SCRATCH;
+        if (wkv7::static_scratch(&workspace) != hipSuccess) return WKV7_ERR_LAUNCH;
+        workspace_bytes = WKV7_STATIC_SCRATCH_BYTES;
+    }
     if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return WKV7_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (need == 0) return run_forward(desc, r, w, k, v, a, b, s0, y, sT, tape, s);
@@ -294,7 +303,15 @@ int wkv7_forward_split(const wkv7_desc* desc, const void* r, const void* w, cons
                        float* sT, void* tape, int32_t segments, void* workspace,
                        size_t workspace_bytes, void* stream) {
     return run_forward_split(desc, r, w, k, v, a, b, s0, y, sT, tape, segments, workspace,
-                             workspace_bytes, stream);
+                             workspace_bytes, stream, false);
+}
+
+int wkv7_forward_split_static(const wkv7_desc* desc, const void* r, const void* w,
+                              const void* k, const void* v, const void* a, const void* b,
+                              const float* s0, void* y, float* sT, void* tape, int32_t segments,
+                              void* stream) {
+    return run_forward_split(desc, r, w, k, v, a, b, s0, y, sT, tape, segments, nullptr, 0, stream,
+                             true);
 }
 
 }  // extern "C"

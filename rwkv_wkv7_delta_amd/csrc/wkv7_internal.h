@@ -89,5 +89,8 @@ hipError_t launch_decode(const DecodeArgs& p, hipStream_t stream);
 // Forward scan writing the checkpoints, then the reverse pass.
 hipError_t launch_seq_bwd(const SeqBwdArgs& p, hipStream_t stream);
 hipError_t launch_state_copy(int BH, int N, const float* s0, float* sT, hipStream_t stream);
+// Device address of the current device's static scratch (WKV7_STATIC_SCRATCH_BYTES),
+// looked up once per device.
+hipError_t static_scratch(void** ptr);
 
 }  // namespace wkv7

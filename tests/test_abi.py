@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(L):
 
 def test_version_and_status_strings(L):
     assert L.wkv7_abi_version() == 1
-    for s in range(5):
+    for s in range(6):
         assert len(L.wkv7_status_string(s)) > 0
     assert L.wkv7_status_string(99) == b"unknown status"
 
@@ -185,6 +185,25 @@ def test_split_forward_validation(L):
     assert f(None, *args, 4, FAKE, need, None) == wk.WKV7_ERR_INVALID_ARG
     de = wk.make_desc(0, 256, 1, 64, wk.WKV7_BF16, 16)
     assert f(ctypes.byref(de), *args, 4, None, 0, None) == wk.WKV7_OK
+
+
+def test_split_static_validation(L):
+    """wkv7_forward_split_static validates like wkv7_forward_split and refuses a
+    plan that needs more than the static scratch before touching the device."""
+    f = L.wkv7_forward_split_static
+    args = [FAKE] * 6 + [None, FAKE, None, None]
+    d = wk.make_desc(1, 256, 1, 64, wk.WKV7_BF16, 16)
+    assert f(None, *args, 4, None) == wk.WKV7_ERR_INVALID_ARG
+    assert f(ctypes.byref(d), *args, -17, None) == wk.WKV7_ERR_INVALID_ARG
+    assert f(ctypes.byref(d), *[FAKE] * 5, FAKE + 8, None, FAKE, None, None, 4, None) == \
+        wk.WKV7_ERR_INVALID_ARG
+    assert f(ctypes.byref(wk.make_desc(1, 256, 1, 32, wk.WKV7_BF16, 16)), *args, 4, None) == \
+        wk.WKV7_ERR_UNSUPPORTED
+    big = wk.make_desc(4, 4096, 32, 64, wk.WKV7_BF16, 16)   # 128 heads x 16 segments x 3 maps
+    assert wk.split_workspace_bytes(big, 16) > wk.STATIC_SCRATCH_BYTES
+    assert f(ctypes.byref(big), *args, 16, None) == wk.WKV7_ERR_STATIC_SCRATCH
+    assert b"static" in L.wkv7_status_string(wk.WKV7_ERR_STATIC_SCRATCH)
+    assert f(ctypes.byref(wk.make_desc(0, 256, 1, 64, wk.WKV7_BF16, 16)), *args, 4, None) == wk.WKV7_OK
 
 
 def test_backward_validation(L):
