@@ -13,7 +13,10 @@ Parity pins (see the CPU tests): linear-attention and decay-only closed
 forms, exact value replacement, the DeltaNet SGD step, the Householder swap,
 exact rational arithmetic on dyadic inputs, brute-force matrix products,
 linearity / permutation invariants, decode = forward, continuation, chunked =
-sequential, and central finite differences for the gradients.
+sequential, and central finite differences for the gradients; for the step
+after the read-out (``epilogue``), a hand-worked fixture, the two-channel
+closed form, the one-hot term, and identity / moment / linearity / gate /
+affine / invariance properties.
 """
 
 from __future__ import annotations
@@ -56,6 +59,7 @@ def _load():
         lib.wkv7_oracle_backward.argtypes = [I, I, I, I] + [P] * 6 + [P, P, P] + [P] * 7 + [I]
         lib.wkv7_oracle_backward_chunked.argtypes = ([I, I, I, I, I] + [P] * 6 + [P, P, P]
                                                      + [P] * 7 + [I])
+        lib.wkv7_oracle_epilogue.argtypes = [I, I, I, I] + [P] * 8 + [ctypes.c_double, I, P, I]
         lib.wkv7_oracle_max_threads.restype = I
         _lib = lib
     return _lib
@@ -139,6 +143,34 @@ def decode_step(r, w, k, v, a, b, state, *, nthreads: int = 0):
     y = np.zeros((B, H, N))
     lib.wkv7_oracle_decode_step(B, H, N, *map(_ptr, ins), _ptr(st), _ptr(y), nthreads)
     return y, st
+
+
+def epilogue(y, r, k, v, g=None, u=None, gamma=None, beta=None, *, eps: float = 1e-5,
+             mode: int = 1, nthreads: int = 0):
+    """The step after the read-out (wkv7_oracle.c), fp64: with s = r . (u * k),
+    mode 0: g (y + s v); mode 1: g (norm(y) + s v); mode 2: g norm(y + s v).
+
+    Token tensors [B, T, H, N]; u, gamma, beta [H, N]; None means g = 1, u = 0,
+    gamma = 1, beta = 0."""
+    lib = _load()
+    toks = [_f64(x) for x in (y, r, k, v)]
+    B, T, H, N = _shape(toks[0])
+    for x in toks:
+        if x.shape != (B, T, H, N):
+            raise ValueError("token tensors must share one shape")
+    g = _f64(g)
+    if g is not None and g.shape != (B, T, H, N):
+        raise ValueError("g must have the token tensors' shape")
+    per_head = [_f64(x) for x in (u, gamma, beta)]
+    for x in per_head:
+        if x is not None and x.shape != (H, N):
+            raise ValueError("u, gamma, beta must be [H, N]")
+    if mode not in (0, 1, 2):
+        raise ValueError("mode must be 0, 1 or 2")
+    out = np.zeros((B, T, H, N))
+    lib.wkv7_oracle_epilogue(B, T, H, N, *map(_ptr, toks), _ptr(g), *map(_ptr, per_head),
+                             float(eps), int(mode), _ptr(out), nthreads)
+    return out
 
 
 def select_heads(x: Optional[np.ndarray], pairs, state: bool = False):

@@ -25,7 +25,10 @@
  *     insertion of the new value, and the receptance reads the state once it
  *     has been updated ("Paper Review", section The approach);
  *   - constant memory and constant time per token at inference (Abstract):
- *     the decode step is one iteration of the same loop on a resident state.
+ *     the decode step is one iteration of the same loop on a resident state;
+ *   - after the read-out, the receptance also attends to the current token and
+ *     the result is normalised per head and gated ("Paper Review", The
+ *     approach): wkv7_oracle_epilogue, its reading stated there.
  *
  * Readings taken where the pages are silent: z uses the undecayed previous
  * state (sum form, not (S diag(w)) a); y is read after the update; w is the
@@ -559,5 +562,59 @@ void wkv7_oracle_backward_chunked(int B, int T, int H, int N, int L, const doubl
         free(V); free(X); free(Z); free(dY); free(dZ); free(dX); free(dV);
         free(dAt); free(dRt); free(dBh); free(dKh); free(dBb); free(dKb); free(dlg);
         free(dAab); free(dAak); free(dArb); free(dArk); free(dlgL);
+    }
+}
+
+/*
+ * The step after the read-out, per token and head (fp64).  "Paper Review:
+ * RWKV-7 Goose", The approach: the receptance also attends to the current token
+ * without storing it in the state, and the result is normalised, combined
+ * across heads and gated (the combination, an output projection, lies outside
+ * this step).  The pages fix neither the current-token formula nor the
+ * normalisation, nor the order of the two; the reading taken, with the learned
+ * parts as inputs:
+ *   s      = sum_j r_t[j] u[j] k_t[j]                    (u: one vector per head)
+ *   norm x = gamma (x - mean x) / sqrt(var x + eps) + beta over the head's N
+ *            channels, var the mean squared deviation
+ *   mode 0: out = g_t (y_t + s v_t)                       (no normalisation)
+ *   mode 1: out = g_t (norm(y_t) + s v_t)
+ *   mode 2: out = g_t norm(y_t + s v_t)
+ * Layouts: y, r, k, v, g, out [B][T][H][N]; u, gamma, beta [H][N].  NULL
+ * means g = 1, u = 0, gamma = 1, beta = 0.
+ */
+void wkv7_oracle_epilogue(int B, int T, int H, int N, const double *y, const double *r,
+                          const double *k, const double *v, const double *g, const double *u,
+                          const double *gamma, const double *beta, double eps, int mode,
+                          double *out, int nthreads) {
+    shape_t sh = {B, T, H, N};
+    const long rows = (long)B * T * H;
+#pragma omp parallel for schedule(static) num_threads(pick_threads(nthreads))
+    for (long row = 0; row < rows; ++row) {
+        const int h = (int)(row % H);
+        const long t = row / H;
+        const int b = (int)(t / T), tt = (int)(t % T);
+        const size_t o = tok(&sh, b, tt, h);
+        double *x = malloc(sizeof(double) * (size_t)N);
+        double s = 0.0;
+        if (u)
+            for (int j = 0; j < N; ++j) s += r[o + j] * u[(size_t)h * N + j] * k[o + j];
+        /* x = what is normalised (mode 1, 2) or the result before the gate (mode 0) */
+        for (int i = 0; i < N; ++i) x[i] = (mode == 1) ? y[o + i] : y[o + i] + s * v[o + i];
+        if (mode != 0) {
+            double mean = 0.0, var = 0.0;
+            for (int i = 0; i < N; ++i) mean += x[i];
+            mean /= N;
+            for (int i = 0; i < N; ++i) var += (x[i] - mean) * (x[i] - mean);
+            var /= N;
+            const double inv_sd = 1.0 / sqrt(var + eps);
+            for (int i = 0; i < N; ++i) {
+                double n = (x[i] - mean) * inv_sd;
+                if (gamma) n *= gamma[(size_t)h * N + i];
+                if (beta) n += beta[(size_t)h * N + i];
+                x[i] = (mode == 1) ? n + s * v[o + i] : n;
+            }
+        }
+        for (int i = 0; i < N; ++i) out[o + i] = (g ? g[o + i] : 1.0) * x[i];
+        free(x);
     }
 }

@@ -1,7 +1,8 @@
 /* The fp64 oracle under AddressSanitizer and UndefinedBehaviorSanitizer: every
  * entry point on small ragged shapes (one thread), with two of its own
  * identities as a sanity check -- T decode steps equal the sequence forward,
- * and the chunked rearrangement equals the sequential recurrence.  Exit status
+ * and the chunked rearrangement equals the sequential recurrence -- plus the
+ * step after the read-out in its three modes.  Exit status
  * = number of failed checks. */
 #include <math.h>
 #include <stdio.h>
@@ -28,6 +29,10 @@ void wkv7_oracle_backward_chunked(int B, int T, int H, int N, int L, const doubl
                                   const double *dy, const double *dsT, double *dr, double *dw,
                                   double *dk, double *dv, double *da, double *db, double *ds0,
                                   int nthreads);
+void wkv7_oracle_epilogue(int B, int T, int H, int N, const double *y, const double *r,
+                          const double *k, const double *v, const double *g, const double *u,
+                          const double *gamma, const double *beta, double eps, int mode,
+                          double *out, int nthreads);
 
 static unsigned long long rng = 88172645463325252ull;
 static double uni(void) {   /* xorshift64, uniform in (-1, 1) */
@@ -98,6 +103,18 @@ int main(void) {
     wkv7_oracle_forward(0, T, H, N, r, w, k, v, a, b, NULL, y, sT, 1);
     wkv7_oracle_backward(B, T, H, N, r, w, k, v, a, b, NULL, dy, NULL, g1[0], g1[1], g1[2], g1[3],
                          g1[4], g1[5], g1[6], 1);
+    /* the step after the read-out: every mode, with and without the optional
+       inputs; mode 0 without term and gate is the identity */
+    double *u = fill((size_t)H * N, -1, 1), *gam = fill((size_t)H * N, 0.5, 1.5);
+    double *bet = fill((size_t)H * N, -0.2, 0.2);
+    for (int mode = 0; mode < 3; ++mode) {
+        wkv7_oracle_epilogue(B, T, H, N, y, r, k, v, dy, u, gam, bet, 1e-5, mode, y2, 1);
+        wkv7_oracle_epilogue(B, T, H, N, y, r, k, v, NULL, NULL, NULL, NULL, 1e-5, mode, y2, 1);
+    }
+    wkv7_oracle_epilogue(B, T, H, N, y, r, k, v, NULL, NULL, NULL, NULL, 0.0, 0, y2, 1);
+    if (maxdiff(y, y2, nt) != 0.0) { fprintf(stderr, "epilogue identity\n"); ++failures; }
+    wkv7_oracle_epilogue(B, 0, H, N, y, r, k, v, NULL, NULL, NULL, NULL, 0.0, 1, y2, 1);
+    free(u); free(gam); free(bet);
     for (int q = 0; q < 7; ++q) { free(g1[q]); free(g2[q]); }
     for (int q = 0; q < 6; ++q) free(tok[q]);
     free(yt); free(st); free(r); free(k); free(v); free(w); free(a); free(b); free(s0); free(dy);
