@@ -350,6 +350,60 @@ int wkv7_decode_step(int32_t B, int32_t H, int32_t N, int32_t dtype, const void 
                      const void *w, const void *k, const void *v, const void *a,
                      const void *b, float *state, void *y, void *stream);
 
+/*
+ * The step after the read-out ("Paper Review: RWKV-7 Goose", The approach:
+ * the receptance also attends to the current token without storing it in the
+ * state, and the result is normalised per head and gated; combining the heads
+ * through the output projection is not part of it).  The pages fix neither the
+ * current-token formula, the normalisation nor their order; the library takes
+ * them with the learned parts as inputs.  Per token t and head h, over the
+ * head's N channels:
+ *     s       = r_t . (u_h * k_t)                         (a scalar)
+ *     norm(x) = gamma_h * (x - mean(x)) / sqrt(var(x) + eps) + beta_h,
+ *               var = the mean squared deviation (divisor N)
+ *     WKV7_EPI_PLAIN:     out_t = g_t * (y_t + s v_t)
+ *     WKV7_EPI_NORM_TERM: out_t = g_t * (norm(y_t) + s v_t)
+ *     WKV7_EPI_TERM_NORM: out_t = g_t * norm(y_t + s v_t)
+ * (* elementwise).  The arithmetic is fp32; the result is written in dtype.
+ */
+typedef enum { WKV7_EPI_PLAIN = 0, WKV7_EPI_NORM_TERM = 1, WKV7_EPI_TERM_NORM = 2 } wkv7_epi_mode;
+
+/* The learned parts and settings (device pointers to fp32 [H][N], each
+   16-byte aligned, or NULL). */
+typedef struct {
+    const float *u;      /* current-token weights; NULL: no current-token term */
+    const float *gamma;  /* scale after normalising; NULL = 1 */
+    const float *beta;   /* shift after normalising; NULL = 0 */
+    float eps;           /* added to the variance: finite, >= 0 */
+    int32_t mode;        /* wkv7_epi_mode */
+} wkv7_epilogue_params;
+
+/*
+ * The step after the read-out on its own, over [B][T][H][N] tensors in
+ * desc->dtype with N = 32, 64 or 128 (desc->chunk_len is ignored): reads y (a
+ * read-out such as wkv7_forward's), r, k and v (only with params->u), g (the
+ * gate; NULL = 1) and writes out, which may be y itself (in place) but must
+ * not overlap the other inputs.  params must not be NULL.  WKV7_ERR_INVALID_ARG
+ * for an unknown mode, a negative or non-finite eps, or a missing pointer.
+ */
+int wkv7_epilogue(const wkv7_desc *desc, const void *y, const void *r, const void *k,
+                  const void *v, const void *g, const wkv7_epilogue_params *params, void *out,
+                  void *stream);
+
+/*
+ * wkv7_forward followed by the step after the read-out: out receives the
+ * result in place of y (y itself is not written), sT the final state (may be
+ * NULL); no tape.  With chunk_len = 16 the step is fused into the chunked
+ * forward kernel, which applies it to the fp32 read-outs before anything is
+ * stored (y never reaches memory); with chunk_len = 0 the scan writes y into
+ * out and wkv7_epilogue runs on it in place.  Arguments otherwise as
+ * wkv7_forward and wkv7_epilogue.
+ */
+int wkv7_forward_epilogue(const wkv7_desc *desc, const void *r, const void *w, const void *k,
+                          const void *v, const void *a, const void *b, const float *s0,
+                          const void *g, const wkv7_epilogue_params *params, void *out,
+                          float *sT, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -41,7 +41,8 @@ EXPORTED = ("wkv7_abi_version", "wkv7_status_string", "wkv7_tape_bytes", "wkv7_c
             "wkv7_forward_ckpt", "wkv7_forward_split_workspace_bytes", "wkv7_forward_split",
             "wkv7_forward_split_static",
             "wkv7_backward", "wkv7_backward_ckpt", "wkv7_backward_adjoint", "wkv7_backward_gradients",
-            "wkv7_backward_overlapped", "wkv7_decode_step")
+            "wkv7_backward_overlapped", "wkv7_decode_step", "wkv7_epilogue",
+            "wkv7_forward_epilogue")
 
 
 class WKV7Error(RuntimeError):
@@ -49,6 +50,11 @@ class WKV7Error(RuntimeError):
         self.status = status
         msg = lib().wkv7_status_string(status).decode() if _lib is not None else str(status)
         super().__init__(f"{where}: status {status} ({msg})")
+
+
+class EpilogueParams(ctypes.Structure):
+    _fields_ = [("u", ctypes.c_void_p), ("gamma", ctypes.c_void_p), ("beta", ctypes.c_void_p),
+                ("eps", ctypes.c_float), ("mode", ctypes.c_int32)]
 
 
 class Desc(ctypes.Structure):
@@ -104,6 +110,11 @@ def lib():
         L.wkv7_backward_overlapped.restype = ctypes.c_int
         L.wkv7_decode_step.argtypes = [I, I, I, I] + [P] * 6 + [P, P, P]
         L.wkv7_decode_step.restype = ctypes.c_int
+        E = ctypes.POINTER(EpilogueParams)
+        L.wkv7_epilogue.argtypes = [D] + [P] * 5 + [E, P, P]
+        L.wkv7_epilogue.restype = ctypes.c_int
+        L.wkv7_forward_epilogue.argtypes = [D] + [P] * 7 + [P, E, P, P, P]
+        L.wkv7_forward_epilogue.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -262,6 +273,65 @@ def forward(r, w, k, v, a, b, s0=None, *, chunk_len: int = 0, want_state: bool =
     if st != WKV7_OK:
         raise WKV7Error(st, "wkv7_forward_split")
     return y, sT, ck
+
+
+EPI_PLAIN, EPI_NORM_TERM, EPI_TERM_NORM = 0, 1, 2
+
+
+def _epilogue_params(u, gamma, beta, eps: float, mode: int, H: int, N: int) -> EpilogueParams:
+    torch = _torch()
+    for t in (u, gamma, beta):
+        if t is not None and (not t.is_cuda or not t.is_contiguous() or t.dtype != torch.float32
+                              or tuple(t.shape) != (H, N)):
+            raise ValueError("u, gamma, beta must be contiguous float32 device tensors of [H, N]")
+    return EpilogueParams(_ptr(u), _ptr(gamma), _ptr(beta), float(eps), int(mode))
+
+
+def epilogue(y, r, k, v, g=None, u=None, gamma=None, beta=None, *, eps: float = 1e-5,
+             mode: int = EPI_NORM_TERM, out=None):
+    """The step after the read-out (wkv7_epilogue): with s = r . (u * k) per token
+    and head, mode 0: g (y + s v); 1: g (norm(y) + s v); 2: g norm(y + s v).
+    Token tensors [B, T, H, N] (y's dtype); u, gamma, beta float32 [H, N] or
+    None (no term / 1 / 0); g None = 1.  ``out`` may be ``y`` (in place)."""
+    torch = _torch()
+    B, T, H, N = y.shape
+    _check_tokens([y] + [t for t in (r, k, v) if t is not None or u is not None], y.shape, y.dtype)
+    if g is not None:
+        _check_tokens((g,), y.shape, y.dtype)
+    o = out if out is not None else torch.empty_like(y)
+    _check_tokens((o,), y.shape, y.dtype)
+    prm = _epilogue_params(u, gamma, beta, eps, mode, H, N)
+    desc = make_desc(B, T, H, N, _dtype_code(y), 0)
+    st = lib().wkv7_epilogue(ctypes.byref(desc), _ptr(y), _ptr(r), _ptr(k), _ptr(v), _ptr(g),
+                             ctypes.byref(prm), _ptr(o), _stream())
+    if st != WKV7_OK:
+        raise WKV7Error(st, "wkv7_epilogue")
+    return o
+
+
+def forward_epilogue(r, w, k, v, a, b, s0=None, g=None, u=None, gamma=None, beta=None, *,
+                     eps: float = 1e-5, mode: int = EPI_NORM_TERM, chunk_len: int = 16,
+                     want_state: bool = True, out=None):
+    """The recurrence and then the step after the read-out (wkv7_forward_epilogue;
+    fused into the chunked kernel when chunk_len = 16).  Returns ``(out, sT)``."""
+    torch = _torch()
+    B, T, H, N = r.shape
+    _check_tokens((r, w, k, v), r.shape, r.dtype)
+    _check_pair(a, b, r.shape, r.dtype)
+    _check_state(s0, (B, H, N, N))
+    if g is not None:
+        _check_tokens((g,), r.shape, r.dtype)
+    o = out if out is not None else torch.empty_like(r)
+    _check_tokens((o,), r.shape, r.dtype)
+    sT = torch.empty((B, H, N, N), device=r.device, dtype=torch.float32) if want_state else None
+    prm = _epilogue_params(u, gamma, beta, eps, mode, H, N)
+    desc = make_desc(B, T, H, N, _dtype_code(r), chunk_len)
+    st = lib().wkv7_forward_epilogue(ctypes.byref(desc), _ptr(r), _ptr(w), _ptr(k), _ptr(v),
+                                     _ptr(a), _ptr(b), _ptr(s0), _ptr(g), ctypes.byref(prm),
+                                     _ptr(o), _ptr(sT), _stream())
+    if st != WKV7_OK:
+        raise WKV7Error(st, "wkv7_forward_epilogue")
+    return o, sT
 
 
 _STAGES = {"all": "wkv7_backward", "adjoint": "wkv7_backward_adjoint",

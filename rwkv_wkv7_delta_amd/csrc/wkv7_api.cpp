@@ -4,6 +4,7 @@
 #include "wkv7.h"
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdlib.h>
 
 #include "wkv7_internal.h"
@@ -180,6 +181,23 @@ int run_forward(const wkv7_desc* d, const void* r, const void* w, const void* k,
     p.ckpt = ckpt;
     if (d->chunk_len == 0) return from_hip(wkv7::launch_seq_fwd(p, stream));
     return from_hip(wkv7::launch_chunk_fwd(p, d->chunk_len, stream));
+}
+
+// The step after the read-out: settings valid and the per-head vectors aligned.
+bool epi_params_ok(const wkv7_epilogue_params* e) {
+    return e != nullptr && e->mode >= WKV7_EPI_PLAIN && e->mode <= WKV7_EPI_TERM_NORM &&
+           isfinite(e->eps) && e->eps >= 0.f && opt(e->u) && opt(e->gamma) && opt(e->beta);
+}
+
+wkv7::EpiParams epi_params(const wkv7_epilogue_params* e, const void* g) {
+    wkv7::EpiParams p;
+    p.g = g;
+    p.u = e->u;
+    p.gamma = e->gamma;
+    p.beta = e->beta;
+    p.eps = e->eps;
+    p.mode = e->mode;
+    return p;
 }
 
 }  // namespace
@@ -508,6 +526,46 @@ int wkv7_decode_step(int32_t B, int32_t H, int32_t N, int32_t dtype, const void*
         return WKV7_ERR_INVALID_ARG;
     wkv7::DecodeArgs p{B, H, N, dtype == WKV7_BF16, r, w, k, v, a, b, state, y};
     return from_hip(wkv7::launch_decode(p, static_cast<hipStream_t>(stream)));
+}
+
+int wkv7_epilogue(const wkv7_desc* desc, const void* y, const void* r, const void* k,
+                  const void* v, const void* g, const wkv7_epilogue_params* params, void* out,
+                  void* stream) {
+    if (!desc) return WKV7_ERR_INVALID_ARG;
+    wkv7_desc d = *desc;
+    d.chunk_len = 0;   // any form's read-out
+    const int st = check_desc(&d);
+    if (st != WKV7_OK) return st;
+    if (!epi_params_ok(params)) return WKV7_ERR_INVALID_ARG;
+    const bool has_tokens = (int64_t)d.B * d.T * d.H > 0;
+    if (has_tokens && !(req(y) && req(out) && opt(g))) return WKV7_ERR_INVALID_ARG;
+    if (has_tokens && params->u && !(req(r) && req(k) && req(v))) return WKV7_ERR_INVALID_ARG;
+    if (!has_tokens) return WKV7_OK;
+    const wkv7::EpiArgs p{d.B, d.T, d.H, d.N, d.dtype == WKV7_BF16, y, r, k, v, epi_params(params, g), out};
+    return from_hip(wkv7::launch_epilogue(p, static_cast<hipStream_t>(stream)));
+}
+
+int wkv7_forward_epilogue(const wkv7_desc* desc, const void* r, const void* w, const void* k,
+                          const void* v, const void* a, const void* b, const float* s0,
+                          const void* g, const wkv7_epilogue_params* params, void* out,
+                          float* sT, void* stream) {
+    const int st = check_desc(desc);
+    if (st != WKV7_OK) return st;
+    if (!epi_params_ok(params)) return WKV7_ERR_INVALID_ARG;
+    const bool has_tokens = (int64_t)desc->B * desc->T * desc->H > 0;
+    if (has_tokens && !(req(r) && req(w) && req(k) && req(v) && pair(a, b) && req(out) && opt(g)))
+        return WKV7_ERR_INVALID_ARG;
+    if (!(opt(s0) && opt(sT))) return WKV7_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (!has_tokens || desc->chunk_len == 0) {
+        // The scan writes y into out (nothing at all without tokens), then the
+        // step runs on it in place.
+        const int fs = run_forward(desc, r, w, k, v, a, b, s0, out, sT, nullptr, s);
+        if (fs != WKV7_OK || !has_tokens) return fs;
+        return wkv7_epilogue(desc, out, r, k, v, g, params, out, stream);
+    }
+    wkv7::FwdArgs p{desc->B, desc->T, desc->H, desc->N, true, r, w, k, v, a, b, s0, out, sT, nullptr};
+    return from_hip(wkv7::launch_chunk_fwd_epilogue(p, epi_params(params, g), s));
 }
 
 }  // extern "C"

@@ -53,6 +53,7 @@
 
 #include "wkv7.h"
 #include "wkv7_device.h"
+#include "wkv7_epilogue.h"
 #include "wkv7_internal.h"
 #include "wkv7_mfma.h"
 
@@ -62,6 +63,10 @@ namespace {
 
 constexpr int kL = 16;
 constexpr int kThreads = 640;   // 4 producer, 4 consumer, 2 inverse waves
+// With the step after the read-out fused: 2 more waves for it.  Waves go to the
+// four SIMDs in turn, so these take the two SIMDs that held only two waves; at
+// three waves per SIMD either way, the register budget per wave is the same.
+constexpr int kThreadsEpi = 768;
 // LDS row stride (bf16 elements).  A 64-wide row would be exactly one sweep
 // of the four-byte banks, so the row reads below (16 lanes on 16 different
 // rows, same columns) would all hit the same banks; 144-byte rows spread them.
@@ -97,6 +102,21 @@ struct __align__(16) FwdSmem {
     bf16_t Zs[2][kL][kRow];       // removal read-outs, staged for the tape
     bf16_t S0s[2][kN][kRow];      // chunk entry states as [j][i], staged for the tape
 };
+// With the step after the read-out fused (kEpi: no tape), the read-outs are
+// staged in fp32 over the space of Ys and Zs, and the tape's state staging S0s
+// holds the step's own buffers (EpiSmem).
+constexpr int kYfRow = kN + 4;
+static_assert(offsetof(FwdSmem, Zs) == offsetof(FwdSmem, Ys) + sizeof(FwdSmem::Ys) &&
+                  offsetof(FwdSmem, Ys) % 16 == 0 &&
+                  2 * kL * kYfRow * sizeof(float) <= sizeof(FwdSmem::Ys) + sizeof(FwdSmem::Zs),
+              "fp32 read-out staging fits over Ys and Zs");
+struct EpiSmem {
+    float ugb[3][kN];          // this head's u, gamma, beta
+    float Es[8][kL];           // r . (u * k) per token of chunk c at [c % 8], from interval c to c+4
+    bf16_t Vr[2][kL][kRow];    // v rows of chunk c at [c % 2], copied out of its slot in interval c+3
+};
+static_assert(sizeof(EpiSmem) <= sizeof(FwdSmem::S0s) && offsetof(FwdSmem, S0s) % 16 == 0,
+              "the step's buffers fit over the tape's state staging");
 
 __device__ __forceinline__ float bf2f(bf16_t x) { return __uint_as_float((uint32_t)x << 16); }
 __device__ __forceinline__ bf16x4 ld4(const bf16_t* p) {
@@ -133,15 +153,21 @@ struct Raw {
 //
 // kCk: also write the fp32 state entering every chunk (a template parameter, so
 // that the kernel without it carries no trace of the stores).
-template <bool kSeq, bool kAB, bool kCk>
-__global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
+//
+// kEpi: y_all receives the step after the read-out (wkv7_epilogue.h, settings
+// `ep`) instead of y, computed from the fp32 read-outs by the inverse waves;
+// no tape.
+template <bool kSeq, bool kAB, bool kCk, bool kEpi>
+__global__ __launch_bounds__(kEpi ? kThreadsEpi : kThreads) void chunk_fwd_kernel(
     int B, int T, int H, const bf16_t* __restrict__ r, const bf16_t* __restrict__ w,
     const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const bf16_t* __restrict__ a,
     const bf16_t* __restrict__ b, const float* __restrict__ s0, bf16_t* __restrict__ y_all,
     float* __restrict__ sT, bf16_t* __restrict__ tape_all, float* __restrict__ ckpt_all, int pass,
     int split_from, int nseg, int seg_len, float* __restrict__ states, int* __restrict__ sync,
-    int spin_limit) {
+    int spin_limit, EpiParams ep) {
     __shared__ FwdSmem sm;
+    float(*const Yf)[kL][kYfRow] = reinterpret_cast<float(*)[kL][kYfRow]>(&sm.Ys[0][0][0]);
+    EpiSmem& es = *reinterpret_cast<EpiSmem*>(&sm.S0s[0][0][0]);
     __shared__ int entry_lost_sm;
     constexpr size_t NN = (size_t)kN * kN;
     Work wk;
@@ -189,7 +215,8 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
     const int wave = tid >> 6;
     const bool producer = wave < 4;
     const bool consumer = wave >= 4 && wave < 8;
-    const bool inverter = wave >= 8;
+    const bool inverter = wave >= 8 && wave < 10;
+    const bool epi_wave = kEpi && wave >= 10;
     const int rtid = tid & 255;               // index within the role
     const int lane = tid & 63, wp = (tid >> 6) & 3;
     const int l16 = lane & 15, g = lane >> 4;
@@ -479,6 +506,12 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
         // holds 8 bytes of row l16) and leave next interval as whole 128-byte
         // rows (store_out), which HBM takes far better than 32-byte pieces.
         const int i0 = 16 * wp + 4 * g;
+        if constexpr (kEpi) {
+            // fp32, row layout: register q holds y of token 4 g + q, value row col
+#pragma unroll
+            for (int q = 0; q < 4; ++q) Yf[c & 1][4 * g + q][col] = Yt[q];
+            return;
+        }
         *reinterpret_cast<bf16x4*>(&sm.Ys[c & 1][l16][i0]) = swap_layout(cvt4(Yt), ident);
         if (tape) {
             if (kAB) *reinterpret_cast<bf16x4*>(&sm.Zs[c & 1][l16][i0]) = swap_layout(Zb, ident);
@@ -512,6 +545,79 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
         }
     };
 
+    // ---- EPI (kEpi: waves 10, 11): the step after the read-out ----------------
+    // Two waves take 8 tokens of a chunk each (wave 10: tokens 0-7, wave 11:
+    // 8-15), a group of 8 lanes per token with 8 values per lane:
+    //   interval c:   r . (u * k) from the chunk's raw r and k (in LDS for E);
+    //   interval c+3: its v rows, copied out of the chunk's slot (E reuses the
+    //                 slot in c+4), while the state chain stages its fp32 y;
+    //   interval c+4: the step, and the store of the result.
+    // g, the only input read from memory for it, is loaded three intervals
+    // ahead, as the producers load theirs.
+    const int epi_row = 8 * (wave & 1) + (lane >> 3), epi_piece = lane & 7;   // waves 10, 11
+    auto epi_load_g = [&](int c) __attribute__((always_inline)) -> uint4 {
+        const int t = min(c * kL + epi_row, t_end - 1);   // in bounds; rows past T are not stored
+        return *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(ep.g) +
+                                               tok_off(bb, t, hh, T, H) + 8 * epi_piece);
+    };
+    auto unpack8 = [](uint4 q, float (&x)[8]) __attribute__((always_inline)) {
+        const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = bf16_lo(w4[i]);
+            x[2 * i + 1] = bf16_hi(w4[i]);
+        }
+    };
+    auto epi_coef = [&](int c) __attribute__((always_inline)) {
+        const bf16_t(*Rr)[kL][kRow] = sm.raw[c & 1];
+        float rr[8], kk[8], uu[8];
+        unpack8(*reinterpret_cast<const uint4*>(&Rr[RAW_R][epi_row][8 * epi_piece]), rr);
+        unpack8(*reinterpret_cast<const uint4*>(&Rr[RAW_K][epi_row][8 * epi_piece]), kk);
+        load_cols<8>(&es.ugb[0][8 * epi_piece], uu);
+        float sp = rr[0] * uu[0] * kk[0];
+#pragma unroll
+        for (int q = 1; q < 8; ++q) sp = fmaf(rr[q] * uu[q], kk[q], sp);
+        sp = lanes_sum<8>(sp);
+        if (epi_piece == 0) es.Es[c & 7][epi_row] = sp;
+    };
+    auto epi_copy = [&](int c) __attribute__((always_inline)) {
+        *reinterpret_cast<uint4*>(&es.Vr[c & 1][epi_row][8 * epi_piece]) =
+            *reinterpret_cast<const uint4*>(&sm.sl[c % kSlots].V[epi_row][8 * epi_piece]);
+    };
+    auto epi_store = [&](int c, uint4 graw) __attribute__((always_inline)) {
+        const int tt = c * kL + epi_row;
+        if (tt >= t_end) return;
+        float x[8], vv[8], gt[8];
+        const float4 y0 = *reinterpret_cast<const float4*>(&Yf[c & 1][epi_row][8 * epi_piece]);
+        const float4 y1 = *reinterpret_cast<const float4*>(&Yf[c & 1][epi_row][8 * epi_piece + 4]);
+        x[0] = y0.x; x[1] = y0.y; x[2] = y0.z; x[3] = y0.w;
+        x[4] = y1.x; x[5] = y1.y; x[6] = y1.z; x[7] = y1.w;
+        const bool term = ep.u != nullptr;
+        float sc = 0.f;
+        if (term) {
+            unpack8(*reinterpret_cast<const uint4*>(&es.Vr[c & 1][epi_row][8 * epi_piece]), vv);
+            sc = es.Es[c & 7][epi_row];
+        } else {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) vv[q] = 0.f;
+        }
+        if (ep.g) {
+            unpack8(graw, gt);
+        } else {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) gt[q] = 1.f;
+        }
+        // the coefficient is already the whole row's: one lane's share of it is
+        // a 1/8 part of a group sum; hand it over as that share
+        float gm[8], bt[8];
+        load_cols<8>(&es.ugb[1][8 * epi_piece], gm);
+        load_cols<8>(&es.ugb[2][8 * epi_piece], bt);
+        epilogue_row<8, 8>(x, vv, sc, term, gm, bt, gt, ep.eps, ep.mode);
+        const uint4 o = make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                                   pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7]));
+        store_stream(y + tok_off(bb, tt, hh, T, H) + 8 * epi_piece, o);
+    };
+
     if (t_end > wk.t_begin) {
         // Intervals 0 .. nch+3 carry real work (chunk c_begin + i enters in
         // interval i); the count is rounded up to a multiple of three for the
@@ -519,6 +625,16 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
         // chunks (identity on the state, nothing stored).
         const int nch = c_end - c_begin;
         const int cb = c_begin;
+        if (kEpi && tid < 3 * kN / 4) {
+            // u, gamma, beta of this head into LDS (absent: 0, 1, 0); every role
+            // passes a barrier before its first use
+            const int vec = tid / (kN / 4), q4 = tid % (kN / 4);
+            const float* src = vec == 0 ? ep.u : vec == 1 ? ep.gamma : ep.beta;
+            const float fill = vec == 1 ? 1.f : 0.f;
+            *reinterpret_cast<float4*>(&es.ugb[vec][4 * q4]) =
+                src ? *reinterpret_cast<const float4*>(src + (size_t)hh * kN + 4 * q4)
+                    : make_float4(fill, fill, fill, fill);
+        }
         const int n_it = (nch + 6) / 3 * 3;
         // Each role runs its own loop over the same number of intervals (one
         // barrier each), so the compiler sees only loads on the producer side
@@ -581,6 +697,23 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
                 }
                 __syncthreads();
             }
+        } else if (epi_wave) {
+            __syncthreads();
+            // Interval it: the step for chunk it-4, v of chunk it-3, r . (u * k)
+            // of chunk it; g of chunks it-4, it-3, it-2 in g0, g1, g2 (loaded in
+            // intervals it-3, it-2, it-1).
+            uint4 g0{}, g1{}, g2{};
+            for (int it = 0; it < n_it; ++it) {
+                if (it >= 4) epi_store(cb + it - 4, g0);
+                if (ep.u) {
+                    if (it >= 3) epi_copy(cb + it - 3);
+                    epi_coef(cb + it);
+                }
+                g0 = g1;
+                g1 = g2;
+                if (ep.g && it >= 1) g2 = epi_load_g(cb + it - 1);
+                __syncthreads();
+            }
         } else {
             // The state chain is the critical path: its waves issue first (then
             // the inverse wave, then the producers) when several are ready, so
@@ -593,7 +726,7 @@ __global__ __launch_bounds__(kThreads) void chunk_fwd_kernel(
                 if (it >= 3) {
                     const STIn si = read_ST(cb + it - 3);
                     stage_ST(cb + it - 3, si);
-                    if (it >= 4) store_out(cb + it - 4);
+                    if (!kEpi && it >= 4) store_out(cb + it - 4);
                 }
                 __syncthreads();
             }
@@ -692,14 +825,14 @@ hipError_t launch_chunk_fwd_sequential(const FwdArgs& p, int chunk_len, int nseg
     seg_sync_init_kernel<<<dim3((nbh + 255) / 256), dim3(256), 0, stream>>>(sync, nbh);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    auto kern = p.a ? (p.ckpt ? chunk_fwd_kernel<true, true, true> : chunk_fwd_kernel<true, true, false>)
-                    : (p.ckpt ? chunk_fwd_kernel<true, false, true> : chunk_fwd_kernel<true, false, false>);
+    auto kern = p.a ? (p.ckpt ? chunk_fwd_kernel<true, true, true, false> : chunk_fwd_kernel<true, true, false, false>)
+                    : (p.ckpt ? chunk_fwd_kernel<true, false, true, false> : chunk_fwd_kernel<true, false, false, false>);
     kern<<<dim3(nbh * nseg), dim3(kThreads), 0, stream>>>(
         p.B, p.T, p.H, static_cast<const bf16_t*>(p.r), static_cast<const bf16_t*>(p.w),
         static_cast<const bf16_t*>(p.k), static_cast<const bf16_t*>(p.v),
         static_cast<const bf16_t*>(p.a), static_cast<const bf16_t*>(p.b), p.s0,
         static_cast<bf16_t*>(p.y), p.sT, static_cast<bf16_t*>(p.tape), p.ckpt, 2, 0, nseg, seg_len,
-        states, sync, spin_limit < 0 ? 0 : spin_limit);
+        states, sync, spin_limit < 0 ? 0 : spin_limit, EpiParams{});
     return hipGetLastError();
 }
 
@@ -712,14 +845,14 @@ hipError_t launch_chunk_fwd_split(const FwdArgs& p, int chunk_len, const FwdSpli
                                        (long long)(sp.nseg - 1) * sp.seg_len >= p.T || !sp.states)))
         return hipErrorInvalidValue;
     auto run = [&](int pass, int grid) {
-        auto kern = p.a ? (p.ckpt ? chunk_fwd_kernel<false, true, true> : chunk_fwd_kernel<false, true, false>)
-                        : (p.ckpt ? chunk_fwd_kernel<false, false, true> : chunk_fwd_kernel<false, false, false>);
+        auto kern = p.a ? (p.ckpt ? chunk_fwd_kernel<false, true, true, false> : chunk_fwd_kernel<false, true, false, false>)
+                        : (p.ckpt ? chunk_fwd_kernel<false, false, true, false> : chunk_fwd_kernel<false, false, false, false>);
         kern<<<dim3(grid), dim3(kThreads), 0, stream>>>(
             p.B, p.T, p.H, static_cast<const bf16_t*>(p.r), static_cast<const bf16_t*>(p.w),
             static_cast<const bf16_t*>(p.k), static_cast<const bf16_t*>(p.v),
             static_cast<const bf16_t*>(p.a), static_cast<const bf16_t*>(p.b), p.s0,
             static_cast<bf16_t*>(p.y), p.sT, static_cast<bf16_t*>(p.tape), p.ckpt, pass,
-            sp.split_from, sp.nseg, sp.seg_len, sp.states, nullptr, 0);
+            sp.split_from, sp.nseg, sp.seg_len, sp.states, nullptr, 0, EpiParams{});
         return hipGetLastError();
     };
     hipError_t e = run(0, sp.split_from + (nsplit > 0 ? nsplit * (2 * sp.nseg - 3) : 0));
@@ -729,6 +862,18 @@ hipError_t launch_chunk_fwd_split(const FwdArgs& p, int chunk_len, const FwdSpli
         if (e != hipSuccess) return e;
     }
     return run(1, nsplit * (sp.nseg - 1));
+}
+
+hipError_t launch_chunk_fwd_epilogue(const FwdArgs& p, const EpiParams& e, hipStream_t stream) {
+    if (!p.bf16 || p.tape || p.ckpt || e.mode < 0 || e.mode > 2) return hipErrorInvalidValue;
+    const int nbh = p.B * p.H;
+    auto kern = p.a ? chunk_fwd_kernel<false, true, false, true> : chunk_fwd_kernel<false, false, false, true>;
+    kern<<<dim3(nbh), dim3(kThreadsEpi), 0, stream>>>(
+        p.B, p.T, p.H, static_cast<const bf16_t*>(p.r), static_cast<const bf16_t*>(p.w),
+        static_cast<const bf16_t*>(p.k), static_cast<const bf16_t*>(p.v),
+        static_cast<const bf16_t*>(p.a), static_cast<const bf16_t*>(p.b), p.s0,
+        static_cast<bf16_t*>(p.y), p.sT, nullptr, nullptr, 0, nbh, 1, p.T, nullptr, nullptr, 0, e);
+    return hipGetLastError();
 }
 
 hipError_t launch_seg_combine(int nsplit, int nseg, float* states, hipStream_t stream) {

@@ -55,6 +55,30 @@ struct DecodeArgs {
     void* y;
 };
 
+// The learned parts and settings of the step after the read-out (wkv7_epilogue.h).
+struct EpiParams {
+    const void* g = nullptr;        // gate [B][T][H][N] in the token dtype; null = 1
+    const float* u = nullptr;       // [H][N]: current-token weights; null = no term
+    const float* gamma = nullptr;   // [H][N]; null = 1
+    const float* beta = nullptr;    // [H][N]; null = 0
+    float eps = 0.f;
+    int mode = 0;                   // 0: no norm; 1: norm, then term; 2: term, then norm
+};
+
+// The step after the read-out on its own: y -> out (out may be y).
+struct EpiArgs {
+    int B, T, H, N;   // N: 32, 64 or 128
+    bool bf16;
+    const void *y, *r, *k, *v;   // r, k, v are read only with the term (u)
+    EpiParams e;
+    void* out;
+};
+
+hipError_t launch_epilogue(const EpiArgs& p, hipStream_t stream);
+// The chunked forward with the step after the read-out fused: p.y receives its
+// result; no tape, no checkpoints, no split.
+hipError_t launch_chunk_fwd_epilogue(const FwdArgs& p, const EpiParams& e, hipStream_t stream);
+
 hipError_t launch_seq_fwd(const FwdArgs& p, hipStream_t stream);
 hipError_t launch_chunk_fwd(const FwdArgs& p, int chunk_len, hipStream_t stream);
 

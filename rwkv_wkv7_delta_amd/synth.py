@@ -265,3 +265,39 @@ def generate_edge(kind: str, B: int, T: int, H: int, N: int = 64, *, dtype: str 
         dsT = np.zeros((B, H, N, N), dtype=np.float32)
     return Inputs(r=rnd(r), w=rnd(w), k=rnd(k), v=rnd(v), a=rnd(a), b=rnd(b), s0=s0, dy=dy,
                   dsT=dsT, dtype=dtype, meta=dict(B=B, T=T, H=H, N=N, seed=seed, kind=kind))
+
+
+# ---------------------------------------------------------------------------
+# Inputs of the step after the read-out (current-token term, per-head
+# normalisation, gate).  The pages give no values for its learned parts; the
+# recipe takes a gate in (0, 1) and parts of order one.
+# ---------------------------------------------------------------------------
+
+@dataclass
+class EpilogueInputs:
+    g: np.ndarray       # [B, T, H, N] gate, sigmoid(N(0, 1)), rounded like the tokens
+    u: np.ndarray       # [H, N] fp32 current-token weights, 0.5 N(0, 1)
+    gamma: np.ndarray   # [H, N] fp32, 1 + 0.2 N(0, 1)
+    beta: np.ndarray    # [H, N] fp32, 0.2 N(0, 1)
+    y: np.ndarray       # [B, T, H, N] a stand-in read-out, 0.3 + N(0, 1) (mean off zero)
+
+
+def generate_epilogue(B: int, T: int, H: int, N: int = 64, *, dtype: str = "bf16",
+                      seed: int = 0) -> EpilogueInputs:
+    """Learned parts (and a stand-in read-out for the step on its own).  Draw
+    order (PCG64 ``seed``): g, u, gamma, beta, y; fp64 rounded to fp32, and
+    g, y again to bf16 for bf16 workloads."""
+    if dtype not in ("fp32", "bf16"):
+        raise ValueError(f"dtype must be fp32 or bf16, got {dtype!r}")
+    rng = np.random.default_rng(seed)
+
+    def rnd(x: np.ndarray) -> np.ndarray:
+        x32 = np.asarray(x).astype(np.float32)
+        return round_to_bf16(x32) if dtype == "bf16" else x32
+
+    g = rnd(_sigmoid(rng.standard_normal((B, T, H, N))))
+    u = (0.5 * rng.standard_normal((H, N))).astype(np.float32)
+    gamma = (1.0 + 0.2 * rng.standard_normal((H, N))).astype(np.float32)
+    beta = (0.2 * rng.standard_normal((H, N))).astype(np.float32)
+    y = rnd(0.3 + rng.standard_normal((B, T, H, N)))
+    return EpilogueInputs(g=g, u=u, gamma=gamma, beta=beta, y=y)

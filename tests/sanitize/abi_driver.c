@@ -55,6 +55,11 @@ int main(void) {
                 CHECK(st != WKV7_ERR_LAUNCH || !big);
                 st = wkv7_forward_split(&d, F, F, F, F, F, F, NULL, NULL, NULL, NULL, 4, NULL, 0, NULL);
                 CHECK(st != WKV7_ERR_LAUNCH || !big);
+                wkv7_epilogue_params ep = {NULL, NULL, NULL, 1e-5f, ci % 3};
+                st = wkv7_epilogue(&d, F, F, F, F, NULL, &ep, NULL, NULL);
+                CHECK(st != WKV7_ERR_LAUNCH || !big);
+                st = wkv7_forward_epilogue(&d, F, F, F, F, F, F, NULL, NULL, &ep, NULL, NULL, NULL);
+                CHECK(st != WKV7_ERR_LAUNCH || !big);
             }
     /* explicit statuses */
     wkv7_desc d = D(1, 8, 1, 64, WKV7_BF16, 16);
@@ -72,6 +77,9 @@ int main(void) {
     CHECK(wkv7_decode_step(-1, 1, 64, WKV7_BF16, F, F, F, F, F, F, F, F, NULL) == WKV7_ERR_INVALID_ARG);
     CHECK(wkv7_decode_step(0, 1, 64, WKV7_BF16, F, F, F, F, F, F, F, F, NULL) == WKV7_OK);
     CHECK(wkv7_decode_step(1, 1, 64, WKV7_F32, F, F, F, F, F, M, F, F, NULL) == WKV7_ERR_INVALID_ARG);
+    wkv7_epilogue_params bad = {NULL, NULL, NULL, -1.0f, 1};
+    CHECK(wkv7_epilogue(&d, F, F, F, F, NULL, &bad, F, NULL) == WKV7_ERR_INVALID_ARG);
+    CHECK(wkv7_epilogue(&d, F, F, F, F, NULL, NULL, F, NULL) == WKV7_ERR_INVALID_ARG);
     /* sizes: exact values */
     d = D(8, 4096, 40, 64, WKV7_BF16, 16);
     CHECK(wkv7_ckpt_bytes(&d) == (size_t)8 * 40 * 256 * 64 * 64 * 4);

@@ -18,6 +18,10 @@ hipError_t launch_bwd(const BwdArgs&, int, int, hipStream_t) { return hipErrorIn
 hipError_t launch_decode(const DecodeArgs&, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_seq_bwd(const SeqBwdArgs&, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_state_copy(int, int, const float*, float*, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_epilogue(const EpiArgs&, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_chunk_fwd_epilogue(const FwdArgs&, const EpiParams&, hipStream_t) {
+    return hipErrorInvalidValue;
+}
 hipError_t static_scratch(void** ptr) {
     *ptr = nullptr;
     return hipErrorInvalidValue;

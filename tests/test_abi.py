@@ -333,6 +333,65 @@ def test_removal_pair_validation(L):
     assert _fwd(L, wk.make_desc(0, 8, 4, 64, wk.WKV7_BF16, 16), ptrs=[FAKE] * 4 + [None, None]) == wk.WKV7_OK
 
 
+def test_epilogue_validation(L):
+    """wkv7_epilogue: settings, pointers and shapes are checked before any launch."""
+    f = L.wkv7_epilogue
+    P = wk.EpilogueParams
+    ok = P(None, None, None, 1e-5, wk.EPI_NORM_TERM)
+    d = wk.make_desc(2, 8, 3, 64, wk.WKV7_BF16, 16)
+    toks = [FAKE] * 4   # y, r, k, v
+    assert f(ctypes.byref(d), *toks, None, None, FAKE, None) == wk.WKV7_ERR_INVALID_ARG  # params
+    for bad in (P(None, None, None, 1e-5, 3), P(None, None, None, 1e-5, -1),
+                P(None, None, None, -1e-5, 1), P(None, None, None, float("nan"), 1),
+                P(None, None, None, float("inf"), 1), P(FAKE + 4, None, None, 1e-5, 1),
+                P(None, FAKE + 8, None, 1e-5, 1), P(None, None, FAKE + 2, 1e-5, 1)):
+        assert f(ctypes.byref(d), *toks, None, ctypes.byref(bad), FAKE, None) == \
+            wk.WKV7_ERR_INVALID_ARG
+    assert f(ctypes.byref(d), None, *toks[1:], None, ctypes.byref(ok), FAKE, None) == \
+        wk.WKV7_ERR_INVALID_ARG   # y
+    assert f(ctypes.byref(d), *toks, None, ctypes.byref(ok), None, None) == \
+        wk.WKV7_ERR_INVALID_ARG   # out
+    assert f(ctypes.byref(d), *toks, FAKE + 8, ctypes.byref(ok), FAKE, None) == \
+        wk.WKV7_ERR_INVALID_ARG   # misaligned gate
+    with_u = P(FAKE, None, None, 1e-5, 1)
+    for i in range(1, 4):   # the term reads r, k and v
+        args = list(toks)
+        args[i] = None
+        assert f(ctypes.byref(d), *args, None, ctypes.byref(with_u), FAKE, None) == \
+            wk.WKV7_ERR_INVALID_ARG
+    assert f(ctypes.byref(wk.make_desc(2, 8, 3, 48, wk.WKV7_BF16, 0)), *toks, None,
+             ctypes.byref(ok), FAKE, None) == wk.WKV7_ERR_UNSUPPORTED
+    assert f(ctypes.byref(wk.make_desc(2, 8, 3, 64, 7, 0)), *toks, None, ctypes.byref(ok), FAKE,
+             None) == wk.WKV7_ERR_UNSUPPORTED
+    assert f(None, *toks, None, ctypes.byref(ok), FAKE, None) == wk.WKV7_ERR_INVALID_ARG
+    # empty problems: nothing to do, no pointer needed
+    for e in (wk.make_desc(0, 8, 3, 64, wk.WKV7_F32, 0), wk.make_desc(2, 0, 3, 128, wk.WKV7_BF16, 0)):
+        assert f(ctypes.byref(e), None, None, None, None, None, ctypes.byref(ok), None, None) == \
+            wk.WKV7_OK
+
+
+def test_forward_epilogue_validation(L):
+    f = L.wkv7_forward_epilogue
+    ok = wk.EpilogueParams(None, None, None, 1e-5, wk.EPI_NORM_TERM)
+    ins = [FAKE] * 6 + [None]   # r, w, k, v, a, b, s0
+    d = wk.make_desc(1, 32, 2, 64, wk.WKV7_BF16, 16)
+    assert f(ctypes.byref(d), *ins, None, None, FAKE, None, None) == wk.WKV7_ERR_INVALID_ARG
+    assert f(ctypes.byref(d), *ins, None, ctypes.byref(ok), None, None, None) == \
+        wk.WKV7_ERR_INVALID_ARG   # out
+    assert f(ctypes.byref(d), *[FAKE] * 4, FAKE, None, None, None, ctypes.byref(ok), FAKE, None,
+             None) == wk.WKV7_ERR_INVALID_ARG   # a without b
+    assert f(ctypes.byref(d), *ins, None, ctypes.byref(wk.EpilogueParams(None, None, None, 0.0, 9)),
+             FAKE, None, None) == wk.WKV7_ERR_INVALID_ARG
+    assert f(ctypes.byref(wk.make_desc(1, 32, 2, 64, wk.WKV7_F32, 16)), *ins, None,
+             ctypes.byref(ok), FAKE, None, None) == wk.WKV7_ERR_UNSUPPORTED
+    assert f(ctypes.byref(wk.make_desc(1, 32, 2, 32, wk.WKV7_BF16, 16)), *ins, None,
+             ctypes.byref(ok), FAKE, None, None) == wk.WKV7_ERR_UNSUPPORTED
+    assert f(ctypes.byref(d), *ins[:6], FAKE + 4, None, ctypes.byref(ok), FAKE, None, None) == \
+        wk.WKV7_ERR_INVALID_ARG   # misaligned s0
+    assert f(ctypes.byref(wk.make_desc(0, 32, 2, 64, wk.WKV7_BF16, 16)), *[None] * 8,
+             ctypes.byref(ok), None, None, None) == wk.WKV7_OK
+
+
 def test_binding_has_no_cpu_fallback():
     """The binding routes every call through libwkv7.so and never imports the oracle."""
     import inspect
