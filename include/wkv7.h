@@ -395,8 +395,9 @@ int wkv7_epilogue(const wkv7_desc *desc, const void *y, const void *r, const voi
  * result in place of y (y itself is not written), sT the final state (may be
  * NULL); no tape.  With chunk_len = 16 the step is fused into the chunked
  * forward kernel, which applies it to the fp32 read-outs before anything is
- * stored (y never reaches memory); with chunk_len = 0 the scan writes y into
- * out and wkv7_epilogue runs on it in place.  Arguments otherwise as
+ * stored (y never reaches memory) when T * H * N * 2 < 2^31 (its per-head
+ * offsets are 32-bit); otherwise, and with chunk_len = 0, the forward writes y
+ * (in dtype) into out and wkv7_epilogue runs on it in place.  Arguments otherwise as
  * wkv7_forward and wkv7_epilogue.
  */
 int wkv7_forward_epilogue(const wkv7_desc *desc, const void *r, const void *w, const void *k,

@@ -557,9 +557,10 @@ int wkv7_forward_epilogue(const wkv7_desc* desc, const void* r, const void* w, c
         return WKV7_ERR_INVALID_ARG;
     if (!(opt(s0) && opt(sT))) return WKV7_ERR_INVALID_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (!has_tokens || desc->chunk_len == 0) {
-        // The scan writes y into out (nothing at all without tokens), then the
-        // step runs on it in place.
+    if (!has_tokens || desc->chunk_len == 0 || !wkv7::chunk_fwd_epilogue_fits(desc->T, desc->H)) {
+        // The forward writes y into out (nothing at all without tokens), then
+        // the step runs on it in place: the scan, and chunked problems too large
+        // for the fused kernel's 32-bit offsets.
         const int fs = run_forward(desc, r, w, k, v, a, b, s0, out, sT, nullptr, s);
         if (fs != WKV7_OK || !has_tokens) return fs;
         return wkv7_epilogue(desc, out, r, k, v, g, params, out, stream);

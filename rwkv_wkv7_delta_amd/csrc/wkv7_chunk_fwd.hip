@@ -77,6 +77,7 @@ enum { RAW_R = 0, RAW_W = 1, RAW_K = 2, RAW_A = 3, RAW_B = 4, RAW_V = 5 };
 // of Arb, Ark (from MW).
 enum { TILE_AK = 0, TILE_RB = 1, TILE_RK = 2 };
 constexpr int kSlots = 4;
+static_assert((kSlots & (kSlots - 1)) == 0, "slot indices are taken with a mask");
 
 // Everything one chunk passes from the producers to the consumers: rows
 // [t][j] (the consumers read Bb, Kb and V transposed, which gives them the
@@ -553,12 +554,28 @@ __global__ __launch_bounds__(kEpi ? kThreadsEpi : kThreads) void chunk_fwd_kerne
     //                 slot in c+4), while the state chain stages its fp32 y;
     //   interval c+4: the step, and the store of the result.
     // g, the only input read from memory for it, is loaded three intervals
-    // ahead, as the producers load theirs.
+    // ahead, as the producers load theirs.  g and the result go through buffer
+    // resources bounded to this head's tokens of its batch row (the launcher
+    // keeps T * H * N * 2 bytes below 2^31), so rows past T, and the rows of the
+    // chunks before the first that the steady-state loop also visits, are
+    // dropped by the hardware's range check: every memory access of the loop is
+    // unconditional, and the wait for a load three intervals old counts exactly.
     const int epi_row = 8 * (wave & 1) + (lane >> 3), epi_piece = lane & 7;   // waves 10, 11
-    auto epi_load_g = [&](int c) __attribute__((always_inline)) -> uint4 {
-        const int t = min(c * kL + epi_row, t_end - 1);   // in bounds; rows past T are not stored
-        return *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(ep.g) +
-                                               tok_off(bb, t, hh, T, H) + 8 * epi_piece);
+    typedef unsigned int epi_u4 __attribute__((ext_vector_type(4)));
+    const int epi_row_bytes = H * kN * 2;
+    auto head_rsrc = [&](const void* base) __attribute__((always_inline)) {
+        return __builtin_amdgcn_make_buffer_rsrc(
+            base ? const_cast<bf16_t*>(static_cast<const bf16_t*>(base) + ((size_t)bb * T * H + hh) * kN)
+                 : nullptr,
+            (short)0, base ? T * epi_row_bytes : 0, 0x00020000);
+    };
+    // byte offset of this lane's piece of token c * 16 + epi_row (negative for
+    // the chunks before the first: out of range as an unsigned offset)
+    auto epi_off = [&](int c) __attribute__((always_inline)) {
+        return (c * kL + epi_row) * epi_row_bytes + 16 * epi_piece;
+    };
+    auto epi_load_g = [&](const __amdgpu_buffer_rsrc_t& rs, int c) __attribute__((always_inline)) -> uint4 {
+        return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, epi_off(c), 0, 0));
     };
     auto unpack8 = [](uint4 q, float (&x)[8]) __attribute__((always_inline)) {
         const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
@@ -582,11 +599,9 @@ __global__ __launch_bounds__(kEpi ? kThreadsEpi : kThreads) void chunk_fwd_kerne
     };
     auto epi_copy = [&](int c) __attribute__((always_inline)) {
         *reinterpret_cast<uint4*>(&es.Vr[c & 1][epi_row][8 * epi_piece]) =
-            *reinterpret_cast<const uint4*>(&sm.sl[c % kSlots].V[epi_row][8 * epi_piece]);
+            *reinterpret_cast<const uint4*>(&sm.sl[c & (kSlots - 1)].V[epi_row][8 * epi_piece]);
     };
-    auto epi_store = [&](int c, uint4 graw) __attribute__((always_inline)) {
-        const int tt = c * kL + epi_row;
-        if (tt >= t_end) return;
+    auto epi_store = [&](const __amdgpu_buffer_rsrc_t& rs, int c, uint4 graw) __attribute__((always_inline)) {
         float x[8], vv[8], gt[8];
         const float4 y0 = *reinterpret_cast<const float4*>(&Yf[c & 1][epi_row][8 * epi_piece]);
         const float4 y1 = *reinterpret_cast<const float4*>(&Yf[c & 1][epi_row][8 * epi_piece + 4]);
@@ -613,9 +628,9 @@ __global__ __launch_bounds__(kEpi ? kThreadsEpi : kThreads) void chunk_fwd_kerne
         load_cols<8>(&es.ugb[1][8 * epi_piece], gm);
         load_cols<8>(&es.ugb[2][8 * epi_piece], bt);
         epilogue_row<8, 8>(x, vv, sc, term, gm, bt, gt, ep.eps, ep.mode);
-        const uint4 o = make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
-                                   pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7]));
-        store_stream(y + tok_off(bb, tt, hh, T, H) + 8 * epi_piece, o);
+        const epi_u4 o = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                          pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
+        __builtin_amdgcn_raw_buffer_store_b128(o, rs, epi_off(c), 0, 2);   // non-temporal
     };
 
     if (t_end > wk.t_begin) {
@@ -698,22 +713,32 @@ __global__ __launch_bounds__(kEpi ? kThreadsEpi : kThreads) void chunk_fwd_kerne
                 __syncthreads();
             }
         } else if (epi_wave) {
+            const __amdgpu_buffer_rsrc_t out_rs = head_rsrc(y), g_rs = head_rsrc(ep.g);
             __syncthreads();
-            // Interval it: the step for chunk it-4, v of chunk it-3, r . (u * k)
-            // of chunk it; g of chunks it-4, it-3, it-2 in g0, g1, g2 (loaded in
-            // intervals it-3, it-2, it-1).
-            uint4 g0{}, g1{}, g2{};
-            for (int it = 0; it < n_it; ++it) {
-                if (it >= 4) epi_store(cb + it - 4, g0);
-                if (ep.u) {
-                    if (it >= 3) epi_copy(cb + it - 3);
-                    epi_coef(cb + it);
-                }
-                g0 = g1;
-                g1 = g2;
-                if (ep.g && it >= 1) g2 = epi_load_g(cb + it - 1);
-                __syncthreads();
+            // Interval it: the step for chunk it-4 (its g loaded in interval it-3
+            // into ring register it % 3), v of chunk it-3, r . (u * k) of chunk
+            // it, and the load of g for chunk it-1 into the register just freed.
+            // Unrolled by three (a macro, three named registers) so that the ring
+            // is never copied; every step runs from interval 0 on, on chunks
+            // before the first whose stores fall out of range.
+#define WKV7_EPI_STEP(IT, GREG)                                             \
+    {                                                                       \
+        const int it_ = (IT);                                               \
+        epi_store(out_rs, cb + it_ - 4, GREG);                              \
+        if (ep.u) {                                                         \
+            epi_copy(cb + it_ - 3);                                         \
+            epi_coef(cb + it_);                                             \
+        }                                                                   \
+        GREG = epi_load_g(g_rs, cb + it_ - 1);                              \
+        __syncthreads();                                                    \
+    }
+            uint4 ga{}, gb{}, gc{};
+            for (int it = 0; it < n_it; it += 3) {
+                WKV7_EPI_STEP(it, ga);
+                WKV7_EPI_STEP(it + 1, gb);
+                WKV7_EPI_STEP(it + 2, gc);
             }
+#undef WKV7_EPI_STEP
         } else {
             // The state chain is the critical path: its waves issue first (then
             // the inverse wave, then the producers) when several are ready, so
@@ -866,6 +891,7 @@ hipError_t launch_chunk_fwd_split(const FwdArgs& p, int chunk_len, const FwdSpli
 
 hipError_t launch_chunk_fwd_epilogue(const FwdArgs& p, const EpiParams& e, hipStream_t stream) {
     if (!p.bf16 || p.tape || p.ckpt || e.mode < 0 || e.mode > 2) return hipErrorInvalidValue;
+    if (!chunk_fwd_epilogue_fits(p.T, p.H)) return hipErrorInvalidValue;   // 32-bit buffer offsets
     const int nbh = p.B * p.H;
     auto kern = p.a ? chunk_fwd_kernel<false, true, false, true> : chunk_fwd_kernel<false, false, false, true>;
     kern<<<dim3(nbh), dim3(kThreadsEpi), 0, stream>>>(

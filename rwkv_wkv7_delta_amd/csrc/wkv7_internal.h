@@ -76,8 +76,10 @@ struct EpiArgs {
 
 hipError_t launch_epilogue(const EpiArgs& p, hipStream_t stream);
 // The chunked forward with the step after the read-out fused: p.y receives its
-// result; no tape, no checkpoints, no split.
+// result; no tape, no checkpoints, no split.  It addresses a head's tokens of one
+// batch row with 32-bit byte offsets, so it takes T * H * 64 * 2 < 2^31 only.
 hipError_t launch_chunk_fwd_epilogue(const FwdArgs& p, const EpiParams& e, hipStream_t stream);
+inline bool chunk_fwd_epilogue_fits(int T, int H) { return (long long)T * H * 64 * 2 < (1LL << 31); }
 
 hipError_t launch_seq_fwd(const FwdArgs& p, hipStream_t stream);
 hipError_t launch_chunk_fwd(const FwdArgs& p, int chunk_len, hipStream_t stream);
