@@ -46,7 +46,17 @@ KERNELS = {   # kernel symbol -> (entry point that launches it alone, source, by
     "bwd_chain_kernel": ("wkv7_backward_adjoint", "wkv7_bwd.hip", ADJ_BYTES_PER_TH),
     "bwd_keys_kernel": ("wkv7_backward_gradients", "wkv7_bwd.hip", GRAD_BYTES_PER_TH),
 }
+# Algorithmic bytes per token-head of a whole training step: the forward reads
+# r, w, k, v, a, b and writes y (7 vectors); the backward reads r, w, k, v, a,
+# b, dy and writes the six token gradients (13 vectors).
+STEP_BYTES_PER_TH = 20 * 128
+BF16_MFMA_PEAK_TFLOPS = 2500.0      # dense bf16 matrix-core peak
 PROFILE_JSON = os.path.join(ROOT, "profiles", "hbm_traffic_fwd_bwd_2.9b.json")
+SQ_JSON = os.path.join(ROOT, "profiles", "sq_counters_fwd_bwd_2.9b.json")
+SQ_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES",
+               "SQ_INSTS_VALU", "SQ_ACTIVE_INST_VALU", "SQ_WAIT_INST_LDS", "SQ_LDS_BANK_CONFLICT",
+               "SQ_INSTS_LDS", "GRBM_GUI_ACTIVE")
+MOPS_FLOPS = 512                    # SQ_INSTS_VALU_MFMA_MOPS_*: matrix-core work in units of 512 flops
 COPY_BYTES = 1 << 30                # calibration copy: 1 GiB read + 1 GiB written
 
 
@@ -63,6 +73,17 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run one plain 1 GiB device copy (for scaling HBM counters)")
+    p.add_argument("--workload", choices=("step", "chunked_fwd_1.5b"), default="step",
+                   help="chunked_fwd_1.5b: time only the chunked forward at the 1.5B-model shape "
+                        "(the line under secondary) and print it")
+    p.add_argument("--summarize-sq", nargs=5,
+                   metavar=("STEP_PMC_DIR", "STEP_STEPS", "CFG_PMC_DIR", "CFG_REPS", "CMD"),
+                   help="turn two rocprofv3 --pmc runs of this script (SQ_COUNTERS; the step, "
+                        "then --workload chunked_fwd_1.5b) into "
+                        "profiles/sq_counters_fwd_bwd_2.9b.{md,json} and exit")
+    p.add_argument("--summarize-ktrace", nargs=4, metavar=("KTRACE_DIR", "LAST_N", "CMD", "OUT"),
+                   help="per-kernel durations of the last LAST_N launches of each kernel in a "
+                        "rocprofv3 kernel trace, as a markdown table in OUT; then exit")
     p.add_argument("--summarize-profile", nargs=6,
                    metavar=("KTRACE_DIR", "KTRACE_STEPS", "FETCH_DIR", "WRITE_DIR", "PMC_STEPS", "CMD"),
                    help="turn rocprofv3 outputs of this script into profiles/ summaries and exit "
@@ -77,6 +98,19 @@ def src_digest(*names):
         with open(os.path.join(ROOT, "rwkv_wkv7_delta_amd", "csrc", n), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def load_sq(kernel, digest):
+    """Matrix-core and LDS figures of `kernel` from the committed SQ-counter
+    summary, or None when absent or when the kernel's source changed since."""
+    if not os.path.exists(SQ_JSON):
+        return None
+    with open(SQ_JSON) as f:
+        rec = json.load(f)
+    k = rec.get("kernels", {}).get(kernel)
+    if not k or k.get("source_digest") != digest:
+        return None
+    return k
 
 
 def load_traffic(kernel, digest):
@@ -197,10 +231,141 @@ def summarize_profile(ktrace_dir, ktrace_steps, fetch_dir, write_dir, pmc_steps,
     print("\n".join(lines))
 
 
+def _sq_per_kernel(pmc_dir, steps, select):
+    """Average per dispatch of every counter over the last `steps` dispatches of
+    each kernel that `select(name)` maps to a key (`pmc_dir`: comma-separated
+    directories of counter passes over the same program)."""
+    per = {}
+    for d in pmc_dir.split(","):   # one directory per counter pass
+        for r in _csv_rows(d, "counter_collection.csv"):
+            k = select(r["Kernel_Name"])
+            if k:
+                per.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(
+                    (int(r["Dispatch_Id"]), float(r["Counter_Value"])))
+    out = {}
+    for k, cs in per.items():
+        out[k] = {}
+        for c, vals in cs.items():
+            agg = {}
+            for did, v in vals:   # one dispatch may report a counter in several rows
+                agg[did] = agg.get(did, 0.0) + v
+            last = [agg[d] for d in sorted(agg)[-steps:]]
+            out[k][c] = float(np.mean(last))
+    return out
+
+
+def summarize_sq(step_dir, step_steps, cfg_dir, cfg_steps, cmd):
+    """profiles/sq_counters_fwd_bwd_2.9b.{md,json} from two rocprofv3 --pmc runs
+    of this script with SQ_COUNTERS: the training step's three kernels (their
+    one-at-a-time launches) and the chunked forward at the 1.5B-model shape."""
+    step = _sq_per_kernel(step_dir, int(step_steps), _short)
+    cfg = _sq_per_kernel(cfg_dir, int(cfg_steps),
+                         lambda n: "chunk_fwd_kernel (1.5B shape)" if "chunk_fwd_kernel" in n else None)
+    rec = {"command": cmd, "counters": list(SQ_COUNTERS), "mops_flops": MOPS_FLOPS, "kernels": {}}
+    lines = ["# rocprofv3 SQ counters: the training step's kernels (2.9B-model shape) and the "
+             "chunked forward (1.5B-model shape)", "",
+             "Command (run from the repository root; one counter pass per workload):", "",
+             "```", cmd, "```", "",
+             "Per dispatch, averaged over the one-at-a-time launches.  MFMA flops = "
+             f"SQ_INSTS_VALU_MFMA_MOPS_BF16 x {MOPS_FLOPS}.  Ratios: MFMA busy / CU busy = "
+             "SQ_VALU_MFMA_BUSY_CYCLES / SQ_BUSY_CU_CYCLES; VALU busy / CU busy = "
+             "SQ_ACTIVE_INST_VALU / SQ_BUSY_CU_CYCLES; LDS wait per LDS instruction = "
+             "SQ_WAIT_INST_LDS / SQ_INSTS_LDS; bank-conflict cycles per LDS instruction = "
+             "SQ_LDS_BANK_CONFLICT / SQ_INSTS_LDS.", "",
+             "| kernel | MFMA GFLOP / launch | MFMA busy / CU busy | VALU insts (M) | "
+             "VALU busy / CU busy | LDS insts (M) | LDS wait / LDS inst | conflict cycles / LDS inst | "
+             "GRBM_GUI_ACTIVE |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    srcs = {k: v[1] for k, v in KERNELS.items()}
+    rows = [(k, v, srcs[k]) for k, v in step.items()] + \
+           [(k, v, "wkv7_chunk_fwd.hip") for k, v in cfg.items()]
+    for k, c, src in rows:
+        g = lambda n: c.get(n, float("nan"))
+        busy = g("SQ_BUSY_CU_CYCLES")
+        nlds = g("SQ_INSTS_LDS")
+        flops = g("SQ_INSTS_VALU_MFMA_MOPS_BF16") * MOPS_FLOPS
+        rec["kernels"][k] = {"source": src, "source_digest": src_digest(src), "counters": c,
+                             "mfma_flops_per_launch": flops,
+                             "mfma_busy_over_cu_busy": g("SQ_VALU_MFMA_BUSY_CYCLES") / busy,
+                             "valu_busy_over_cu_busy": g("SQ_ACTIVE_INST_VALU") / busy,
+                             "lds_wait_per_lds_inst": g("SQ_WAIT_INST_LDS") / nlds,
+                             "bank_conflict_cycles_per_lds_inst": g("SQ_LDS_BANK_CONFLICT") / nlds}
+        e = rec["kernels"][k]
+        lines.append(f"| {k} | {flops / 1e9:.1f} | {e['mfma_busy_over_cu_busy']:.3f} | "
+                     f"{g('SQ_INSTS_VALU') / 1e6:.1f} | {e['valu_busy_over_cu_busy']:.3f} | "
+                     f"{nlds / 1e6:.1f} | {e['lds_wait_per_lds_inst']:.2f} | "
+                     f"{e['bank_conflict_cycles_per_lds_inst']:.3f} | {g('GRBM_GUI_ACTIVE'):.4g} |")
+    lines += ["", "Raw averages per dispatch:", "",
+              "| kernel | " + " | ".join(SQ_COUNTERS) + " |",
+              "|---|" + "---|" * len(SQ_COUNTERS)]
+    for k, c, _ in rows:
+        lines.append(f"| {k} | " + " | ".join(f"{c.get(n, float('nan')):.4g}" for n in SQ_COUNTERS) + " |")
+    with open(SQ_JSON, "w") as f:
+        json.dump(rec, f, indent=1)
+    with open(os.path.join(ROOT, "profiles", "sq_counters_fwd_bwd_2.9b.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_ktrace(ktrace_dir, last_n, cmd, out):
+    """Per-kernel durations of the last `last_n` launches in a kernel trace."""
+    last_n = int(last_n)
+    stats = {r["Name"]: (int(r["Calls"]), float(r["AverageNs"]))
+             for r in _csv_rows(ktrace_dir, "kernel_stats.csv")}
+    launches = {}
+    for r in _csv_rows(ktrace_dir, "kernel_trace.csv"):
+        launches.setdefault(r["Kernel_Name"], []).append(
+            (int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    lines = ["# rocprofv3 kernel trace", "", "Command (run from the repository root):", "",
+             "```", cmd, "```", "",
+             f"Durations of each kernel's last {last_n} launches (the timed ones), and the "
+             "--stats line (every launch in the process).", "",
+             "| kernel | launches used | median us | mean us | min us | max us | --stats calls / avg us |",
+             "|---|---|---|---|---|---|---|"]
+    for name, ls in sorted(launches.items(), key=lambda kv: -len(kv[1])):
+        ls.sort()
+        d = np.array([e - b for b, e in ls[-last_n:]], dtype=np.float64) / 1e3
+        short = name.split("(")[0].replace("wkv7::(anonymous namespace)::", "")[:70]
+        calls, avg = stats.get(name, (0, float("nan")))
+        lines.append(f"| {short} | {len(d)} | {np.median(d):.1f} | {d.mean():.1f} | {d.min():.1f} | "
+                     f"{d.max():.1f} | {calls} / {avg / 1e3:.1f} |")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def chunked_fwd_15b(torch, wk, dev, reps=25):
+    """The chunked forward at the 1.5B-model shape (B=8, T=4096, H=32, s0 ~
+    0.1 N(0,1), final state returned): `reps` single calls, each between HIP
+    events on the launch stream, after three untimed ones; median and spread."""
+    B, T, H, N = 8, 4096, 32, 64
+    ins = _dev_inputs(torch, (B, T, H, N), dev, 1)
+    s0 = 0.1 * torch.randn(B, H, N, N, device=dev)
+    y = torch.empty_like(ins[0])
+    fn = lambda: wk.forward(*ins, s0, chunk_len=16, out=y)
+    for _ in range(3):
+        fn()
+    t = np.array([_time(torch, fn, 1) for _ in range(reps)])
+    ms = float(np.median(t))
+    nbytes = B * T * H * FWD_BYTES_PER_TH + 2 * B * H * STATE_BYTES
+    return {"workload": "B=8 T=4096 H=32 bf16, s0~0.1N(0,1), L=16, returns sT",
+            "reps": reps, "ms": round(ms, 4),
+            "ms_p10_p90": [round(float(np.percentile(t, 10)), 4), round(float(np.percentile(t, 90)), 4)],
+            "tokens_per_s": round(B * T / ms * 1e3, 1),
+            "alg_GBs": round(nbytes / ms / 1e6, 1),
+            "frac_hbm": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
+
+
 def main():
     args = parse()
     if args.summarize_profile:
         summarize_profile(*args.summarize_profile)
+        return
+    if args.summarize_sq:
+        summarize_sq(*args.summarize_sq)
+        return
+    if args.summarize_ktrace:
+        summarize_ktrace(*args.summarize_ktrace)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "the benchmark runs on one GPU: the kernels work on one GPU's share (B*H heads); --gpus must be 1",
@@ -213,6 +378,10 @@ def main():
 
     wk.lib()   # fails loudly if the HIP library is missing
     dev = torch.device("cuda:0")
+    if args.workload == "chunked_fwd_1.5b":
+        print(json.dumps({"workload": "chunked_fwd_1.5b", **chunked_fwd_15b(torch, wk, dev)}),
+              flush=True)
+        return
     wl = synth.WORKLOADS["fwd_bwd_2.9b"]
     B, T, H, N = wl.B, wl.T, wl.H, wl.N
     t_gen = time.time()
@@ -339,6 +508,10 @@ def main():
                             "algorithmic_bytes": nbytes,
                             "achieved_GBs": round(nbytes / (ms * 1e-3) / 1e9, 1),
                             "hbm_bytes_counted": load_traffic(name, src_digest(src))}
+    for name, ms in kernel_ms.items():
+        sq = load_sq(name, src_digest(KERNELS[name][1]))
+        per_kernel[name]["mfma_pct"] = (None if sq is None else round(
+            100.0 * sq["mfma_flops_per_launch"] / (ms * 1e-3) / (BF16_MFMA_PEAK_TFLOPS * 1e12), 2))
     dominant = max(kernel_ms, key=kernel_ms.get)
     dk = per_kernel[dominant]
     achieved = dk["achieved_GBs"]
@@ -351,7 +524,19 @@ def main():
                                     "stages launched one at a time (one kernel per call, HIP "
                                     "events around each); their sum per step: "
                                     f"{staged_ms:.4f} ms",
-                "step_parts": halves}
+                "step_parts": halves,
+                "mfma_pct": dk["mfma_pct"],
+                "mfma_pct_note": "matrix-core flops per launch (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512, "
+                                 "committed counter summary, null once the kernel's source "
+                                 "changed) over the live launch time, against 2.5 PFLOP/s"}
+    step_bytes = th * STEP_BYTES_PER_TH
+    step_roofline = {"bound": "hbm", "bytes_per_token_head": STEP_BYTES_PER_TH,
+                     "achieved": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "note": "the whole step: 7 token vectors through the forward (r, w, k, v, a, "
+                             "b in, y out) and 13 through the backward (r, w, k, v, a, b, dy in, "
+                             "6 gradients out), 128 bytes each, over ms_per_step"}
 
     out = {
         "metric": "WKV7 fwd+bwd tokens/s (H=40,N=64,T=4096) and achieved HBM GB/s / MFMA % peak",
@@ -372,6 +557,7 @@ def main():
                    "global_batch": B, "seq_len": T, "heads": H, "head_size": N,
                    "parallelism": "none (1 GPU)"},
         "roofline": roofline,
+        "step_roofline": step_roofline,
     }
 
     if not args.no_secondary:
@@ -409,17 +595,52 @@ def _time(torch, fn, n):
 
 def secondary(torch, wk, dev):
     res = {}
-    B, T, H, N = 8, 4096, 32, 64
-    ins = _dev_inputs(torch, (B, T, H, N), dev, 1)
-    s0 = 0.1 * torch.randn(B, H, N, N, device=dev)
+    N = 64
+    res["chunked_fwd_1.5b"] = chunked_fwd_15b(torch, wk, dev)
+    # The step after the read-out (current-token term, per-head normalisation,
+    # gate) at the 2.9B-model shape: on its own (HBM-bound: y, r, k, v, g read,
+    # the result written, 6 x 128 bytes per token-head), and after the chunked
+    # forward, as a second kernel or fused into it.
+    B, T, H = 8, 4096, 40
+    ins = _dev_inputs(torch, (B, T, H, N), dev, 7)
+    g = torch.sigmoid(torch.randn(B, T, H, N, device=dev)).bfloat16()
+    u, gamma, beta = (torch.randn(H, N, device=dev) * sc + off
+                      for sc, off in ((0.5, 0.0), (0.2, 1.0), (0.2, 0.0)))
     y = torch.empty_like(ins[0])
-    ms = _time(torch, lambda: wk.forward(*ins, s0, chunk_len=16, out=y), 5)
-    nbytes = B * T * H * FWD_BYTES_PER_TH + 2 * B * H * STATE_BYTES
-    res["chunked_fwd_1.5b"] = {"workload": "B=8 T=4096 H=32 bf16, s0~0.1N(0,1), L=16, returns sT",
-                               "ms": round(ms, 4), "tokens_per_s": round(B * T / ms * 1e3, 1),
-                               "alg_GBs": round(nbytes / ms / 1e6, 1),
-                               "frac_hbm": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
-    del ins, s0, y
+    out = torch.empty_like(ins[0])
+    parts = dict(g=g, u=u, gamma=gamma, beta=beta, eps=1e-5, mode=wk.EPI_NORM_TERM)
+
+    def epi_alone():
+        wk.epilogue(y, ins[0], ins[2], ins[3], out=out, **parts)
+
+    def fwd_plain():
+        wk.forward(*ins, None, chunk_len=16, want_state=False, out=y)
+
+    def fwd_then_epi():
+        fwd_plain()
+        epi_alone()
+
+    def fwd_fused():
+        wk.forward_epilogue(*ins, None, chunk_len=16, want_state=False, out=out, **parts)
+
+    forms = (("epilogue", epi_alone), ("forward", fwd_plain), ("forward_then_epilogue", fwd_then_epi),
+             ("forward_epilogue_fused", fwd_fused))
+    reps = {name: [] for name, _ in forms}
+    for _ in range(3):
+        for name, fn in forms:
+            reps[name].append(_time(torch, fn, 10))
+    med = {name: float(np.median(v)) for name, v in reps.items()}
+    epi_bytes = B * T * H * 6 * N * 2
+    res["epilogue_2.9b"] = {
+        "workload": "B=8 T=4096 H=40 N=64 bf16, mode norm-then-term with u, gamma, beta, g "
+                    "(medians of 3 interleaved repetitions of 10 calls)",
+        "epilogue_ms": round(med["epilogue"], 4),
+        "epilogue_alg_GBs": round(epi_bytes / med["epilogue"] / 1e6, 1),
+        "epilogue_frac_hbm": round(epi_bytes / med["epilogue"] / 1e6 / HBM_PEAK_GBS, 4),
+        "forward_ms": round(med["forward"], 4),
+        "forward_then_epilogue_ms": round(med["forward_then_epilogue"], 4),
+        "forward_epilogue_fused_ms": round(med["forward_epilogue_fused"], 4)}
+    del ins, g, u, gamma, beta, y, out, parts
     # a = b = 0 (the decay-only recurrence, a and b passed as NULL) at the
     # 2.9B-model shape: the specialised forward (library's split plan, with its
     # tape) and the overlapped backward (no da, db).
@@ -628,10 +849,10 @@ def secondary(torch, wk, dev):
 
 def cpu_baseline(inp, wl, grads, y, ds0):
     """fp64 oracle (test infrastructure) on the same workload (all heads, full
-    T: a few seconds on 16 host cores); also checks the GPU outputs against it."""
+    T: a few seconds on the host's cores); also checks the GPU outputs against it."""
     import oracle
     from tests._util import maxrel, cosine
-    threads = min(16, len(os.sched_getaffinity(0)))
+    threads = len(os.sched_getaffinity(0))   # every core this process may run on
     pairs = [(b, h) for b in range(wl.B) for h in range(wl.H)]
     sel = [oracle.select_heads(x, pairs) for x in inp.tensors()]
     dsel = oracle.select_heads(inp.dy, pairs)
