@@ -31,6 +31,10 @@ COMMON = [
     # accumulator tile back on the vector ALU; accumulation registers would need
     # a copy instruction per element).
     "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+    # Atomics here come from a single lane (work queues, flags); the optimizer's
+    # wave-aggregated form reads the result back at once, which makes the issuing
+    # wave wait for the atomic's round trip where it is issued.
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wno-unused-command-line-argument",
 ]
 

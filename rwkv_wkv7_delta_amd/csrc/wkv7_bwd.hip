@@ -593,8 +593,11 @@ __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
     // and stashed in LDS when the block comes up, tokens past T as padding
     // (w = 1, everything else 0). ------------------------------------------------
     const int ld_row = (tid >> 3) & 15, ld_piece = tid & 7;
-    const bool lo = tid < 128;
-    const bf16_t* const src4[4] = {lo ? r : w, lo ? k : a, lo ? b : dy, lo ? v : wdX};
+    const bool lo = wp < 2;   // threads 0..127 (a wave-uniform choice)
+    // With a = b = 0 the slots of a, b and dX load r instead (every thread issues
+    // the same loads) and are stashed as zeros.
+    const bf16_t* const src4[4] = {lo ? r : w, lo ? k : (kAB ? a : r), lo ? (kAB ? b : r) : dy,
+                                   lo ? v : (kAB ? wdX : r)};
     struct P2Raw {
         uint4 x[2][5], s[4];
     };
@@ -605,13 +608,10 @@ __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
             const int t = min((2 * m + h) * kL + ld_row, T - 1);
             const size_t off = tok_off(bh / H, t, bh % H, T, H) + 8 * ld_piece;
 #pragma unroll
-            for (int vi = 0; vi < 4; ++vi) {
-                if (kAB || !(vi == 1 ? !lo : vi == 2 ? lo : vi == 3 ? !lo : false))
-                    o.x[h][vi] = *reinterpret_cast<const uint4*>(src4[vi] + off);
-                else
-                    o.x[h][vi] = make_uint4(0u, 0u, 0u, 0u);   // a, b or dX (zero when a = b = 0)
-            }
-            if (lo) o.x[h][4] = kAB ? *reinterpret_cast<const uint4*>(tapeZ + off) : make_uint4(0u, 0u, 0u, 0u);
+            for (int vi = 0; vi < 4; ++vi) o.x[h][vi] = *reinterpret_cast<const uint4*>(src4[vi] + off);
+            // (threads 128..255 load the same Z pieces as 0..127 and drop them, so
+            // that every thread issues the same loads)
+            o.x[h][4] = kAB ? *reinterpret_cast<const uint4*>(tapeZ + off) : make_uint4(0u, 0u, 0u, 0u);
         }
         const size_t sbase = (size_t)bi * kN * kN;
 #pragma unroll
@@ -631,8 +631,10 @@ __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
 #pragma unroll
             for (int vi = 0; vi < 4; ++vi) {
                 const unsigned pad = (!lo && vi == 0) ? 0x3F803F80u : 0u;
+                // a = b = 0: a (vi 1, threads 128..), b (vi 2, threads ..127), dX (vi 3, 128..)
+                const bool zero = !kAB && (vi == 1 ? !lo : vi == 2 ? lo : vi == 3 ? !lo : false);
                 *reinterpret_cast<uint4*>(&sm.rows[h][lo ? set_lo[vi] : set_hi[vi]][ld_row][8 * ld_piece]) =
-                    ok ? o.x[h][vi] : make_uint4(pad, pad, pad, pad);
+                    (ok && !zero) ? o.x[h][vi] : make_uint4(pad, pad, pad, pad);
             }
             if (lo)
                 *reinterpret_cast<uint4*>(&sm.rows[h][P2_Z][ld_row][8 * ld_piece]) =
@@ -648,12 +650,34 @@ __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
 
     // Blocks come from a queue (counter[0]), so workgroups that start late (the
     // compute units may still be busy with other work) simply take fewer; the
-    // loads of the next block are in flight while the current one is computed.
+    // loads of the next block are in flight while the current one is computed,
+    // and so is the queue's answer for the block after it (popped one block
+    // early: waiting for an atomic's return right away costs a round trip per
+    // block).  Every memory access in the loop is unconditional -- loads of a
+    // block past the end re-read the last one, stores out of range fall outside
+    // their buffer resource -- so the wait before a stash covers exactly the
+    // loads it needs and the queue's answer, not the previous block's stores.
     if (tid == 0) next_block = atomicAdd(&counter[0], 1);
     __syncthreads();
-    int bi = next_block;
+    // (block indices as scalars: everything addressed from them is uniform)
+    int bi = __builtin_amdgcn_readfirstlane(next_block);
+    int q_ans = 0;   // the queue's answer in flight (thread 0)
+    if (tid == 0) q_ans = atomicAdd(&counter[0], 1);
     P2Raw nxt;
-    if (bi < nblocks) load_block(bi, nxt);
+    if (bi < nblocks) {
+        load_block(bi, nxt);
+        // As many stores (into a resource of no bytes: dropped) as a block
+        // issues after its loads, after them (the scheduler may not hoist them),
+        // so that the loop is entered with the same pending memory operations as
+        // from its own end and the wait before the stash need not drain the
+        // counter.
+        __builtin_amdgcn_sched_barrier(0);
+        const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(nullptr, (short)0, 0, 0x00020000);
+        typedef unsigned int su4 __attribute__((ext_vector_type(4)));
+        const su4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int q = 0; q < 6; ++q) __builtin_amdgcn_raw_buffer_store_b128(zero, none, 16 * tid + 4096 * q, 0, 2);
+    }
     while (bi < nblocks) {
     const int m = bi % nblk;
     const int bh = bi / nblk;
@@ -661,10 +685,11 @@ __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
     const int c0 = 2 * m;
     const int nh = c0 + 1 < nch ? 2 : 1;   // chunks in this block
     stash_block(bi, nh, nxt);
-    if (tid == 0) next_block = atomicAdd(&counter[0], 1);
+    if (tid == 0) next_block = q_ans;
     __syncthreads();
-    const int bn = next_block;
-    if (bn < nblocks) load_block(bn, nxt);
+    const int bn = __builtin_amdgcn_readfirstlane(next_block);
+    if (tid == 0) q_ans = atomicAdd(&counter[0], 1);
+    load_block(min(bn, nblocks - 1), nxt);
 
     // ---- decay products and scaled vectors of column `col` in chunk h ----------
     auto factors = [&](int h) __attribute__((always_inline)) -> KeyFactors {
@@ -746,7 +771,10 @@ __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
         }
     }
 
-    for (int h = 0; h < nh; ++h) {
+    // Both chunks always (a block with one has an all-padding second chunk whose
+    // stores fall out of range), unrolled: a fixed count of stores per block.
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
         const int t0 = (c0 + h) * kL;
         const KeyFactors f = factors(h);
         // ---- the chunk's rows (row l16, 8 values at 32 k2 + 8 g) and column
@@ -896,21 +924,26 @@ __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
         *reinterpret_cast<bf16x4*>(&sm.rows[h][4][l16][j0]) = swap_layout(cvt4(o_db), ident);
         __syncthreads();
         {
+            // Three 16-byte stores per thread: waves 0, 1 write dr, dk, db and
+            // waves 2, 3 dw, da (and nothing: a resource of no bytes), each
+            // through a resource holding this chunk's rows of the head.
             const int row = (tid >> 3) & 15, piece = tid & 7;
-            const int t = t0 + row;
-            if (t < T) {
-                const size_t off = tok_off(bb, t, hh, T, H) + 8 * piece;
-                auto put = [&](int set, bf16_t* dst) __attribute__((always_inline)) {
-                    store_stream(dst + off, *reinterpret_cast<const uint4*>(&sm.rows[h][set][row][8 * piece]));
-                };
-                if (tid < 128) {
-                    put(0, dr);
-                    put(2, dk);
-                    if (kAB) put(4, db);
-                } else {
-                    put(1, dw);
-                    if (kAB) put(3, da);
-                }
+            const bool lo_w = wp < 2;
+            const int rows_in = max(0, min(kL, T - t0));
+            const size_t base = tok_off(bb, t0, hh, T, H);
+            const int voff = row * (H * kN * 2) + 16 * piece;
+            bf16_t* const dsts[3] = {lo_w ? dr : dw, lo_w ? dk : (kAB ? da : nullptr),
+                                     lo_w ? (kAB ? db : nullptr) : nullptr};
+            const int sets[3] = {lo_w ? 0 : 1, lo_w ? 2 : 3, 4};
+#pragma unroll
+            for (int q = 0; q < 3; ++q) {
+                const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                    dsts[q] ? dsts[q] + base : nullptr, (short)0, dsts[q] ? rows_in * (H * kN * 2) : 0,
+                    0x00020000);
+                typedef unsigned int su4 __attribute__((ext_vector_type(4)));
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    __builtin_bit_cast(su4, *reinterpret_cast<const uint4*>(&sm.rows[h][sets[q]][row][8 * piece])),
+                    rs, voff, 0, 2);   // non-temporal
             }
         }
     }
