@@ -925,26 +925,28 @@ __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
         __syncthreads();
         {
             // Three 16-byte stores per thread: waves 0, 1 write dr, dk, db and
-            // waves 2, 3 dw, da (and nothing: a resource of no bytes), each
-            // through a resource holding this chunk's rows of the head.
+            // waves 2, 3 dw, da (and nothing), each through a resource holding
+            // this chunk's rows of the head.
             const int row = (tid >> 3) & 15, piece = tid & 7;
             const bool lo_w = wp < 2;
-            const int rows_in = max(0, min(kL, T - t0));
+            // (a scalar: the clamp would otherwise land in a vector register, and
+            // a resource built from one needs a loop over its distinct values)
+            const int rows_in = __builtin_amdgcn_readfirstlane(max(0, min(kL, T - t0)));
             const size_t base = tok_off(bb, t0, hh, T, H);
             const int voff = row * (H * kN * 2) + 16 * piece;
-            bf16_t* const dsts[3] = {lo_w ? dr : dw, lo_w ? dk : (kAB ? da : nullptr),
-                                     lo_w ? (kAB ? db : nullptr) : nullptr};
-            const int sets[3] = {lo_w ? 0 : 1, lo_w ? 2 : 3, 4};
-#pragma unroll
-            for (int q = 0; q < 3; ++q) {
+            typedef unsigned int su4 __attribute__((ext_vector_type(4)));
+            // dst: never null (a stand-in where the output is absent); `on`: a
+            // scalar condition, off = a resource of no bytes
+            auto put = [&](bf16_t* dst, bool on, int set) __attribute__((always_inline)) {
                 const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-                    dsts[q] ? dsts[q] + base : nullptr, (short)0, dsts[q] ? rows_in * (H * kN * 2) : 0,
-                    0x00020000);
-                typedef unsigned int su4 __attribute__((ext_vector_type(4)));
+                    dst + base, (short)0, on ? rows_in * (H * kN * 2) : 0, 0x00020000);
                 __builtin_amdgcn_raw_buffer_store_b128(
-                    __builtin_bit_cast(su4, *reinterpret_cast<const uint4*>(&sm.rows[h][sets[q]][row][8 * piece])),
+                    __builtin_bit_cast(su4, *reinterpret_cast<const uint4*>(&sm.rows[h][set][row][8 * piece])),
                     rs, voff, 0, 2);   // non-temporal
-            }
+            };
+            put(lo_w ? dr : dw, true, lo_w ? 0 : 1);
+            put(lo_w ? dk : (kAB ? da : dk), lo_w || kAB, lo_w ? 2 : 3);
+            put(kAB ? db : dr, lo_w && kAB, 4);
         }
     }
     __syncthreads();   // the output rows are read before the next stash overwrites them
