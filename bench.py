@@ -318,14 +318,17 @@ def summarize_ktrace(ktrace_dir, last_n, cmd, out):
             (int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
     lines = ["# rocprofv3 kernel trace", "", "Command (run from the repository root):", "",
              "```", cmd, "```", "",
-             f"Durations of each kernel's last {last_n} launches (the timed ones), and the "
-             "--stats line (every launch in the process).", "",
+             f"Durations of each of the library's kernels over its last {last_n} launches (the "
+             "timed ones), and the --stats line (every launch in the process); the input "
+             "generator's torch kernels are left out.", "",
              "| kernel | launches used | median us | mean us | min us | max us | --stats calls / avg us |",
              "|---|---|---|---|---|---|---|"]
     for name, ls in sorted(launches.items(), key=lambda kv: -len(kv[1])):
+        if "wkv7::" not in name:
+            continue
         ls.sort()
         d = np.array([e - b for b, e in ls[-last_n:]], dtype=np.float64) / 1e3
-        short = name.split("(")[0].replace("wkv7::(anonymous namespace)::", "")[:70]
+        short = name.replace("void ", "").replace("wkv7::(anonymous namespace)::", "").split("(")[0][:70]
         calls, avg = stats.get(name, (0, float("nan")))
         lines.append(f"| {short} | {len(d)} | {np.median(d):.1f} | {d.mean():.1f} | {d.min():.1f} | "
                      f"{d.max():.1f} | {calls} / {avg / 1e3:.1f} |")
@@ -334,10 +337,12 @@ def summarize_ktrace(ktrace_dir, last_n, cmd, out):
     print("\n".join(lines))
 
 
-def chunked_fwd_15b(torch, wk, dev, reps=25):
+def chunked_fwd_15b(torch, wk, dev, reps=25, calls=4):
     """The chunked forward at the 1.5B-model shape (B=8, T=4096, H=32, s0 ~
-    0.1 N(0,1), final state returned): `reps` single calls, each between HIP
-    events on the launch stream, after three untimed ones; median and spread."""
+    0.1 N(0,1), final state returned): `reps` repetitions of `calls` back-to-back
+    calls between HIP events on the launch stream (so that the host's launch
+    time between calls stays hidden), after three untimed ones; the median per
+    call and its spread."""
     B, T, H, N = 8, 4096, 32, 64
     ins = _dev_inputs(torch, (B, T, H, N), dev, 1)
     s0 = 0.1 * torch.randn(B, H, N, N, device=dev)
@@ -345,11 +350,11 @@ def chunked_fwd_15b(torch, wk, dev, reps=25):
     fn = lambda: wk.forward(*ins, s0, chunk_len=16, out=y)
     for _ in range(3):
         fn()
-    t = np.array([_time(torch, fn, 1) for _ in range(reps)])
+    t = np.array([_time(torch, fn, calls) for _ in range(reps)])
     ms = float(np.median(t))
     nbytes = B * T * H * FWD_BYTES_PER_TH + 2 * B * H * STATE_BYTES
     return {"workload": "B=8 T=4096 H=32 bf16, s0~0.1N(0,1), L=16, returns sT",
-            "reps": reps, "ms": round(ms, 4),
+            "reps": reps, "calls_per_rep": calls, "ms": round(ms, 4),
             "ms_p10_p90": [round(float(np.percentile(t, 10)), 4), round(float(np.percentile(t, 90)), 4)],
             "tokens_per_s": round(B * T / ms * 1e3, 1),
             "alg_GBs": round(nbytes / ms / 1e6, 1),
