@@ -69,9 +69,9 @@ extern "C" {
 /* Head sizes: the sequential forms (chunk_len = 0: the scan and the reverse
    pass of wkv7_backward) and the decode step take N = 32, 64 or 128 (a larger N
    is the state expansion of "Millions of States: Designing a Scalable MoE
-   Architecture with RWKV-7 Meta-learner", Abstract); the chunked forms
-   (chunk_len = 16: forward, wkv7_forward_split with segments, every backward
-   entry point) take N = WKV7_HEAD_SIZE only. */
+   Architecture with RWKV-7 Meta-learner", Abstract); the chunked forward
+   (chunk_len = 16: wkv7_forward, _ckpt, _split, _static, _epilogue) takes N = 32
+   or WKV7_HEAD_SIZE, the chunked backward entry points N = WKV7_HEAD_SIZE. */
 #define WKV7_HEAD_SIZE 64
 #define WKV7_TAPE_CHUNK 16       /* tokens per chunk of the backward */
 #define WKV7_TAPE_BLOCK 32       /* tokens per state saved in the forward tape */
@@ -393,11 +393,11 @@ int wkv7_epilogue(const wkv7_desc *desc, const void *y, const void *r, const voi
 /*
  * wkv7_forward followed by the step after the read-out: out receives the
  * result in place of y (y itself is not written), sT the final state (may be
- * NULL); no tape.  With chunk_len = 16 the step is fused into the chunked
- * forward kernel, which applies it to the fp32 read-outs before anything is
- * stored (y never reaches memory) when T * H * N * 2 < 2^31 (its per-head
- * offsets are 32-bit); otherwise, and with chunk_len = 0, the forward writes y
- * (in dtype) into out and wkv7_epilogue runs on it in place.  Arguments otherwise as
+ * NULL); no tape.  With chunk_len = 16 and N = 64 the step is fused into the
+ * chunked forward kernel, which applies it to the fp32 read-outs before
+ * anything is stored (y never reaches memory) when T * H * N * 2 < 2^31 (its
+ * per-head offsets are 32-bit); otherwise (and with chunk_len = 0) the forward
+ * writes y (in dtype) into out and wkv7_epilogue runs on it in place.  Arguments otherwise as
  * wkv7_forward and wkv7_epilogue.
  */
 int wkv7_forward_epilogue(const wkv7_desc *desc, const void *r, const void *w, const void *k,

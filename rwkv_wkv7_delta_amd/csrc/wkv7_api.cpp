@@ -24,8 +24,8 @@ int check_desc(const wkv7_desc* d) {
     if (!d) return WKV7_ERR_INVALID_ARG;
     if (d->B < 0 || d->T < 0 || d->H < 0 || d->N < 0) return WKV7_ERR_INVALID_ARG;
     if (d->N != 32 && d->N != 64 && d->N != 128) return WKV7_ERR_UNSUPPORTED;
-    // The chunked form (and the backward, which is chunked) runs N = 64 only.
-    if (d->chunk_len != 0 && d->N != WKV7_HEAD_SIZE) return WKV7_ERR_UNSUPPORTED;
+    // The chunked forward runs N = 32 and 64 (its backward N = 64: run_backward).
+    if (d->chunk_len != 0 && d->N != 32 && d->N != WKV7_HEAD_SIZE) return WKV7_ERR_UNSUPPORTED;
     if (d->dtype != WKV7_F32 && d->dtype != WKV7_BF16) return WKV7_ERR_UNSUPPORTED;
     if (d->chunk_len != 0 && d->chunk_len != 16) return WKV7_ERR_UNSUPPORTED;
     // The chunked form runs its products on bf16 matrix cores.
@@ -139,6 +139,8 @@ SplitPlan plan_split(const wkv7_desc* d, int segments, int ncu) {
         // 48 heads, 3/4 of it, segments measured no faster; at 320 heads
         // the chunked form's tail split made the scan 14 % slower).
         if (ncu <= 0) return none;
+        // The chunked form at N = 32 runs two workgroups per compute unit.
+        if (!scan && d->N == 32) ncu *= 2;
         int part = nbh;
         if (scan) {
             if ((int64_t)nbh * (d->N / 16) * 2 > ncu) return none;
@@ -557,10 +559,11 @@ int wkv7_forward_epilogue(const wkv7_desc* desc, const void* r, const void* w, c
         return WKV7_ERR_INVALID_ARG;
     if (!(opt(s0) && opt(sT))) return WKV7_ERR_INVALID_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (!has_tokens || desc->chunk_len == 0 || !wkv7::chunk_fwd_epilogue_fits(desc->T, desc->H)) {
+    if (!has_tokens || desc->chunk_len == 0 || desc->N != WKV7_HEAD_SIZE ||
+        !wkv7::chunk_fwd_epilogue_fits(desc->T, desc->H)) {
         // The forward writes y into out (nothing at all without tokens), then
-        // the step runs on it in place: the scan, and chunked problems too large
-        // for the fused kernel's 32-bit offsets.
+        // the step runs on it in place: the scan, the chunked form at N = 32, and
+        // chunked problems too large for the fused kernel's 32-bit offsets.
         const int fs = run_forward(desc, r, w, k, v, a, b, s0, out, sT, nullptr, s);
         if (fs != WKV7_OK || !has_tokens) return fs;
         return wkv7_epilogue(desc, out, r, k, v, g, params, out, stream);

@@ -62,15 +62,26 @@ namespace wkv7 {
 namespace {
 
 constexpr int kL = 16;
-constexpr int kThreads = 640;   // 4 producer, 4 consumer, 2 inverse waves
-// With the step after the read-out fused: 2 more waves for it.  Waves go to the
-// four SIMDs in turn, so these take the two SIMDs that held only two waves; at
-// three waves per SIMD either way, the register budget per wave is the same.
-constexpr int kThreadsEpi = 768;
-// LDS row stride (bf16 elements).  A 64-wide row would be exactly one sweep
-// of the four-byte banks, so the row reads below (16 lanes on 16 different
-// rows, same columns) would all hit the same banks; 144-byte rows spread them.
-constexpr int kRow = kN + 8;    // rows of 64 elements
+// The kernel's shape for head size N = 32 or 64: N/16 producer and N/16
+// consumer waves (16 key columns or value rows each) and two inverse waves
+// (640 threads at N = 64, 384 at N = 32, where two workgroups share a compute
+// unit).  With the step after the read-out fused (N = 64): 2 more waves for
+// it.  Waves go to the four SIMDs in turn, so these take the two SIMDs that
+// held only two waves; at three waves per SIMD either way, the register budget
+// per wave is the same.
+template <int N>
+struct FwdShape {
+    static_assert(N == 32 || N == 64, "head sizes of the chunked forward");
+    static constexpr int P = N / 16;              // producer waves = consumer waves
+    static constexpr int threads = 64 * (2 * P + 2);
+    static constexpr int threads_epi = threads + 128;
+    static constexpr int blocks_per_cu = N == 32 ? 2 : 1;
+    // LDS row stride (bf16 elements).  A row of 64 would be exactly one sweep
+    // of the four-byte banks, so the row reads below (16 lanes on 16 different
+    // rows, same columns) would all hit the same banks; 8 more elements spread them.
+    static constexpr int row = N + 8;
+};
+constexpr int kRow = FwdShape<64>::row;
 
 enum { RAW_R = 0, RAW_W = 1, RAW_K = 2, RAW_A = 3, RAW_B = 4, RAW_V = 5 };
 // Tile images in a slot: the A-operand images of Aak' = Tm Aak (from INV) and
@@ -83,40 +94,46 @@ static_assert((kSlots & (kSlots - 1)) == 0, "slot indices are taken with a mask"
 // [t][j] (the consumers read Bb, Kb and V transposed, which gives them the
 // matrix-core operand layouts directly) and "images", register contents
 // stored lane by lane (8 bytes per lane, read back by the same lane index).
+template <int N>
 struct Slot {
+    static constexpr int kRow = FwdShape<N>::row;
     bf16_t At[kL][kRow];            // E -> MW, INV; At' = Tm At from INV -> ST
     bf16_t Rt[kL][kRow];            // E -> MW, ST
     bf16_t Bb[kL][kRow], Kb[kL][kRow], V[kL][kRow];   // E -> ST
-    float gL[kN];   // E -> ST: G_L of key 16 jt + 4 g + q at word 16 g + 4 jt + q
+    float gL[64];   // E -> ST: G_L of key 16 jt + 4 g + q at word 16 g + 4 jt + q
     uint2 tiles[3][64];
 };
 // Bh and Kh, read only in the interval after E.
+template <int N>
 struct SlotBK {
+    static constexpr int kRow = FwdShape<N>::row;
     bf16_t Bh[kL][kRow], Kh[kL][kRow];
 };
 
+template <int N>
 struct __align__(16) FwdSmem {
+    static constexpr int kRow = FwdShape<N>::row;
     bf16_t raw[2][6][kL][kRow];   // r, w, k, a, b, v of two chunks (bf16 bits)
-    Slot sl[kSlots];
-    SlotBK bk[2];
+    Slot<N> sl[kSlots];
+    SlotBK<N> bk[2];
     bf16_t Ys[2][kL][kRow];       // read-outs, staged in row layout
     bf16_t Zs[2][kL][kRow];       // removal read-outs, staged for the tape
-    bf16_t S0s[2][kN][kRow];      // chunk entry states as [j][i], staged for the tape
+    bf16_t S0s[2][N][kRow];       // chunk entry states as [j][i], staged for the tape
 };
-// With the step after the read-out fused (kEpi: no tape), the read-outs are
-// staged in fp32 over the space of Ys and Zs, and the tape's state staging S0s
-// holds the step's own buffers (EpiSmem).
+// With the step after the read-out fused (kEpi, N = 64: no tape), the
+// read-outs are staged in fp32 over the space of Ys and Zs, and the tape's
+// state staging S0s holds the step's own buffers (EpiSmem).
 constexpr int kYfRow = kN + 4;
-static_assert(offsetof(FwdSmem, Zs) == offsetof(FwdSmem, Ys) + sizeof(FwdSmem::Ys) &&
-                  offsetof(FwdSmem, Ys) % 16 == 0 &&
-                  2 * kL * kYfRow * sizeof(float) <= sizeof(FwdSmem::Ys) + sizeof(FwdSmem::Zs),
+static_assert(offsetof(FwdSmem<64>, Zs) == offsetof(FwdSmem<64>, Ys) + sizeof(FwdSmem<64>::Ys) &&
+                  offsetof(FwdSmem<64>, Ys) % 16 == 0 &&
+                  2 * kL * kYfRow * sizeof(float) <= sizeof(FwdSmem<64>::Ys) + sizeof(FwdSmem<64>::Zs),
               "fp32 read-out staging fits over Ys and Zs");
 struct EpiSmem {
     float ugb[3][kN];          // this head's u, gamma, beta
     float Es[8][kL];           // r . (u * k) per token of chunk c at [c % 8], from interval c to c+4
     bf16_t Vr[2][kL][kRow];    // v rows of chunk c at [c % 2], copied out of its slot in interval c+3
 };
-static_assert(sizeof(EpiSmem) <= sizeof(FwdSmem::S0s) && offsetof(FwdSmem, S0s) % 16 == 0,
+static_assert(sizeof(EpiSmem) <= sizeof(FwdSmem<64>::S0s) && offsetof(FwdSmem<64>, S0s) % 16 == 0,
               "the step's buffers fit over the tape's state staging");
 
 __device__ __forceinline__ float bf2f(bf16_t x) { return __uint_as_float((uint32_t)x << 16); }
@@ -155,18 +172,26 @@ struct Raw {
 // kCk: also write the fp32 state entering every chunk (a template parameter, so
 // that the kernel without it carries no trace of the stores).
 //
-// kEpi: y_all receives the step after the read-out (wkv7_epilogue.h, settings
-// `ep`) instead of y, computed from the fp32 read-outs by the inverse waves;
-// no tape.
-template <bool kSeq, bool kAB, bool kCk, bool kEpi>
-__global__ __launch_bounds__(kEpi ? kThreadsEpi : kThreads) void chunk_fwd_kernel(
+// kEpi (N = 64): y_all receives the step after the read-out (wkv7_epilogue.h,
+// settings `ep`) instead of y, computed from the fp32 read-outs by two more
+// waves; no tape.
+template <int N, bool kSeq, bool kAB, bool kCk, bool kEpi>
+__global__ __launch_bounds__(kEpi ? FwdShape<N>::threads_epi : FwdShape<N>::threads,
+                             FwdShape<N>::blocks_per_cu) void chunk_fwd_kernel(
     int B, int T, int H, const bf16_t* __restrict__ r, const bf16_t* __restrict__ w,
     const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const bf16_t* __restrict__ a,
     const bf16_t* __restrict__ b, const float* __restrict__ s0, bf16_t* __restrict__ y_all,
     float* __restrict__ sT, bf16_t* __restrict__ tape_all, float* __restrict__ ckpt_all, int pass,
     int split_from, int nseg, int seg_len, float* __restrict__ states, int* __restrict__ sync,
     int spin_limit, EpiParams ep) {
-    __shared__ FwdSmem sm;
+    static_assert(!kEpi || N == 64, "the fused step is built for N = 64");
+    // (these hide the file-scope N = 64 constants in the body below)
+    constexpr int kN = N, kRow = FwdShape<N>::row;
+    constexpr int kP = FwdShape<N>::P;          // producer (and consumer) waves
+    constexpr int K2 = N / 32, JT = N / 16;     // 32-deep halves, 16-wide key tiles
+    using Slot = wkv7::Slot<N>;
+    using SlotBK = wkv7::SlotBK<N>;
+    __shared__ FwdSmem<N> sm;
     float(*const Yf)[kL][kYfRow] = reinterpret_cast<float(*)[kL][kYfRow]>(&sm.Ys[0][0][0]);
     EpiSmem& es = *reinterpret_cast<EpiSmem*>(&sm.S0s[0][0][0]);
     __shared__ int entry_lost_sm;
@@ -200,7 +225,7 @@ __global__ __launch_bounds__(kEpi ? kThreadsEpi : kThreads) void chunk_fwd_kerne
                   seg == nseg - 1 ? (sT ? sT + (size_t)h * NN : nullptr) : states + (size_t)h * NN,
                   false, false, true};
     } else {
-        wk = work_of<kN>(blockIdx.x, pass, T, s0, sT, split_from, nseg, seg_len, states);
+        wk = work_of<N>(blockIdx.x, pass, T, s0, sT, split_from, nseg, seg_len, states);
     }
     const int bh = wk.bh;
     const int bb = bh / H, hh = bh % H;
@@ -214,12 +239,12 @@ __global__ __launch_bounds__(kEpi ? kThreadsEpi : kThreads) void chunk_fwd_kerne
     // as per-lane conditions: branching on an SGPR copy of the wave index
     // measured several per cent slower.
     const int wave = tid >> 6;
-    const bool producer = wave < 4;
-    const bool consumer = wave >= 4 && wave < 8;
-    const bool inverter = wave >= 8 && wave < 10;
-    const bool epi_wave = kEpi && wave >= 10;
-    const int rtid = tid & 255;               // index within the role
-    const int lane = tid & 63, wp = (tid >> 6) & 3;
+    const bool producer = wave < kP;
+    const bool consumer = wave >= kP && wave < 2 * kP;
+    const bool inverter = wave >= 2 * kP && wave < 2 * kP + 2;
+    const bool epi_wave = kEpi && wave >= 2 * kP + 2;
+    const int rtid = tid & (64 * kP - 1);     // index within the role
+    const int lane = tid & 63, wp = (tid >> 6) & (kP - 1);
     const int l16 = lane & 15, g = lane >> 4;
     const int col = 16 * wp + l16;            // key column (producer) / value row (consumer)
     // Chunks [c_begin, c_end) of the sequence (t_begin is a multiple of 32).
@@ -232,18 +257,18 @@ __global__ __launch_bounds__(kEpi ? kThreadsEpi : kThreads) void chunk_fwd_kerne
     bf16_t* const tapeS = tape ? tape + (size_t)B * T * H * kN : nullptr;
 
     // ---- consumer state: S^T tiles, lane holds S[col][16 jt + 4 g + q] ----------
-    f32x4 S[4];
+    f32x4 S[JT];
 #pragma unroll
-    for (int jt = 0; jt < 4; ++jt) S[jt] = zero4();
+    for (int jt = 0; jt < JT; ++jt) S[jt] = zero4();
     if (consumer) {
         if (kSeq && entry_lost) {
             const float nan = __builtin_nanf("");
 #pragma unroll
-            for (int jt = 0; jt < 4; ++jt) S[jt] = f32x4{nan, nan, nan, nan};
+            for (int jt = 0; jt < JT; ++jt) S[jt] = f32x4{nan, nan, nan, nan};
         } else if (wk.init) {
             const float* base = wk.init + (size_t)col * kN;
 #pragma unroll
-            for (int jt = 0; jt < 4; ++jt) {
+            for (int jt = 0; jt < JT; ++jt) {
                 const float4 x = *reinterpret_cast<const float4*>(base + 16 * jt + 4 * g);
                 S[jt][0] = x.x; S[jt][1] = x.y; S[jt][2] = x.z; S[jt][3] = x.w;
             }
@@ -253,24 +278,25 @@ __global__ __launch_bounds__(kEpi ? kThreadsEpi : kThreads) void chunk_fwd_kerne
             __builtin_amdgcn_s_waitcnt(0);
         } else if (wk.ident) {
 #pragma unroll
-            for (int jt = 0; jt < 4; ++jt)
+            for (int jt = 0; jt < JT; ++jt)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) S[jt][q] = col == 16 * jt + 4 * g + q ? 1.f : 0.f;
         }
     }
 
-    // ---- producer raw loads: 6 vectors x 16 tokens x 64 = 768 x 16 bytes.  Thread
-    // rtid loads vector 2p + (rtid >= 128), token (rtid >> 3) & 15, columns
-    // 8 (rtid & 7) .. +7, for p = 0, 1, 2.  Loads are branch-free (tokens from
+    // ---- producer raw loads: 6 vectors x 16 tokens x N = 12 N pieces of 16 bytes
+    // over 4 N threads.  Thread rtid loads vector 2p + (rtid >= 2N), token
+    // (rtid / (N/8)) & 15, columns 8 (rtid % (N/8)) .. +7, for p = 0, 1, 2.
+    // Loads are branch-free (tokens from
     // t_end on re-read token t_end-1 and become padding when stashed) and are
     // issued three intervals before use into a three-deep register ring; the
     // stash into LDS happens one interval before use.
-    const bool hi = rtid >= 128;
+    const bool hi = rtid >= 2 * kN;
     const bf16_t* const sp_p[3] = {hi ? w : r, hi ? a : k, hi ? v : b};
-    const int ld_t = (rtid >> 3) & 15, ld_c8 = rtid & 7;
+    const int ld_t = (rtid / (kN / 8)) & 15, ld_c8 = rtid & (kN / 8 - 1);
     auto load_raw = [&](int c, Raw& o) __attribute__((always_inline)) {
         const int t = min(c * kL + ld_t, t_end - 1);
-        const size_t off = tok_off(bb, t, hh, T, H) + ld_c8 * 8;
+        const size_t off = tok_off<N>(bb, t, hh, T, H) + ld_c8 * 8;
 #pragma unroll
         for (int p = 0; p < 3; ++p) {
             if (kAB || !(p == 1 ? hi : p == 2 ? !hi : false)) {
@@ -356,11 +382,12 @@ __global__ __launch_bounds__(kEpi ? kThreadsEpi : kThreads) void chunk_fwd_kerne
     };
 
     // ---- MW (producer): one 16x16 tile per wave ---------------------------------
-    // Waves 2, 3 form Arb = tril_0(Rt Bh^T), Ark = tril_0(Rt Kh^T) as the
-    // transposed product [s][t] = Rt_t . Y_s: accumulator registers of M^T fed
-    // as an A operand stand for M, so these are the A-operand images.
+    // The last two producer waves (2, 3 at N = 64; 0, 1 at N = 32) form Arb =
+    // tril_0(Rt Bh^T), Ark = tril_0(Rt Kh^T) as the transposed product [s][t] =
+    // Rt_t . Y_s: accumulator registers of M^T fed as an A operand stand for M,
+    // so these are the A-operand images.
     struct MWIn {
-        bf16x8 xv[2], yv[2];
+        bf16x8 xv[K2], yv[K2];
     };
     auto read_MW = [&](int c) __attribute__((always_inline)) -> MWIn {
         const Slot& s = sm.sl[c % kSlots];
@@ -369,7 +396,7 @@ __global__ __launch_bounds__(kEpi ? kThreadsEpi : kThreads) void chunk_fwd_kerne
         const bf16_t(*Yr)[kRow] = (wp & 1) ? bk.Kh : bk.Bh;
         MWIn in;
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
+        for (int k2 = 0; k2 < K2; ++k2) {
             in.xv[k2] = ld8(&Xr[l16][32 * k2 + 8 * g]);
             in.yv[k2] = ld8(&Yr[l16][32 * k2 + 8 * g]);
         }
@@ -379,13 +406,13 @@ __global__ __launch_bounds__(kEpi ? kThreadsEpi : kThreads) void chunk_fwd_kerne
         Slot& s = sm.sl[c % kSlots];
         f32x4 PT = zero4();
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) PT = mfma32(in.yv[k2], in.xv[k2], PT);   // [s][t]
+        for (int k2 = 0; k2 < K2; ++k2) PT = mfma32(in.yv[k2], in.xv[k2], PT);   // [s][t]
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int m = 4 * g + q, n = l16;   // m = s, n = t; Arb, Ark keep the diagonal
             PT[q] = m <= n ? PT[q] : 0.f;
         }
-        s.tiles[wp == 2 ? TILE_RB : TILE_RK][lane] = __builtin_bit_cast(uint2, cvt4(PT));
+        s.tiles[(wp & 1) == 0 ? TILE_RB : TILE_RK][lane] = __builtin_bit_cast(uint2, cvt4(PT));
     };
     // ---- INV (inverse waves): Aab, Aak, Tm = (I - Aab)^-1, At' and Aak' --------
     // In the interval after E(c) a wave forms Aab = tril_-1(At Bh^T) and Aak =
@@ -404,16 +431,16 @@ __global__ __launch_bounds__(kEpi ? kThreadsEpi : kThreads) void chunk_fwd_kerne
     auto inv_begin = [&](int c) __attribute__((always_inline)) -> InvState {
         const Slot& s = sm.sl[c % kSlots];
         const SlotBK& bk = sm.bk[c & 1];
-        bf16x8 xv[2], yv[2], kv[2];
+        bf16x8 xv[K2], yv[K2], kv[K2];
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
+        for (int k2 = 0; k2 < K2; ++k2) {
             xv[k2] = ld8(&s.At[l16][32 * k2 + 8 * g]);
             yv[k2] = ld8(&bk.Bh[l16][32 * k2 + 8 * g]);
             kv[k2] = ld8(&bk.Kh[l16][32 * k2 + 8 * g]);
         }
         f32x4 P = zero4(), K = zero4();
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
+        for (int k2 = 0; k2 < K2; ++k2) {
             P = mfma32(xv[k2], yv[k2], P);   // [t][s] = Aab[t][s]
             K = mfma32(xv[k2], kv[k2], K);   // [t][s] = Aak[t][s]
         }
@@ -426,12 +453,12 @@ __global__ __launch_bounds__(kEpi ? kThreadsEpi : kThreads) void chunk_fwd_kerne
     };
     auto inv_end = [&](int c, const InvState& st) __attribute__((always_inline)) {
         Slot& s = sm.sl[c % kSlots];
-        bf16x4 atT[4];
+        bf16x4 atT[JT];
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt) atT[jt] = ld4_tr(tr_addr(&s.At[0][16 * jt], kRow, g, l16));
+        for (int jt = 0; jt < JT; ++jt) atT[jt] = ld4_tr(tr_addr(&s.At[0][16 * jt], kRow, g, l16));
         const Split4 tm = split4(unit_lower_inverse_rows_end(st.bi, g, l16));
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
+        for (int jt = 0; jt < JT; ++jt) {
             const f32x4 d = mfma16(atT[jt], tm.hi, mfma16(atT[jt], tm.lo, zero4()));
             *reinterpret_cast<bf16x4*>(&s.At[l16][16 * jt + 4 * g]) = cvt4(d);
         }
@@ -441,8 +468,8 @@ __global__ __launch_bounds__(kEpi ? kThreadsEpi : kThreads) void chunk_fwd_kerne
     // ---- ST (consumer): value-row block `col` of the state chain of chunk c -----
     struct STIn {
         bf16x4 Aak, Arb, Ark, V;
-        bf16x8 at[2], rt[2];
-        bf16x4 bbt[4], kbt[4];
+        bf16x8 at[K2], rt[K2];
+        bf16x4 bbt[JT], kbt[JT];
         float gl;   // G_L of key 16 jt + 4 g + q sits in lane 4 jt + q of row g
     };
     auto read_ST = [&](int c) __attribute__((always_inline)) -> STIn {
@@ -455,12 +482,12 @@ __global__ __launch_bounds__(kEpi ? kThreadsEpi : kThreads) void chunk_fwd_kerne
             in.Arb = __builtin_bit_cast(bf16x4, s.tiles[TILE_RB][lane]);
         }
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
+        for (int k2 = 0; k2 < K2; ++k2) {
             if (kAB) in.at[k2] = ld4x2(&s.At[l16][32 * k2 + 4 * g]);   // At' = Tm At
             in.rt[k2] = ld4x2(&s.Rt[l16][32 * k2 + 4 * g]);
         }
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
+        for (int jt = 0; jt < JT; ++jt) {
             if (kAB) in.bbt[jt] = ld4_tr(tr_addr(&s.Bb[0][16 * jt], kRow, g, l16));   // Bb^T as an A operand
             in.kbt[jt] = ld4_tr(tr_addr(&s.Kb[0][16 * jt], kRow, g, l16));
         }
@@ -472,18 +499,18 @@ __global__ __launch_bounds__(kEpi ? kThreadsEpi : kThreads) void chunk_fwd_kerne
         // (from INV), Y = Rt S0^T + Arb Z + Ark V.  The 32-deep products (over
         // keys) and the 16-deep ones (over tokens) accumulate separately and meet
         // on the vector ALU (add4).
-        bf16x4 Sb[4];
+        bf16x4 Sb[JT];
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt) Sb[jt] = cvt4(S[jt]);
+        for (int jt = 0; jt < JT; ++jt) Sb[jt] = cvt4(S[jt]);
         if (kCk && ckpt && c < c_end) {   // the entry state in fp32: row col, keys 16 jt + 4 g ..
             float* dst = ckpt + (((size_t)bh * ((T + kL - 1) / kL) + c) * kN + col) * kN + 4 * g;
 #pragma unroll
-            for (int jt = 0; jt < 4; ++jt)
+            for (int jt = 0; jt < JT; ++jt)
                 store_stream(dst + 16 * jt, __builtin_bit_cast(uint4, S[jt]));
         }
         f32x4 Xs = zero4(), Ys = zero4();
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
+        for (int k2 = 0; k2 < K2; ++k2) {
             const bf16x8 bs = cat8(Sb[2 * k2], Sb[2 * k2 + 1]);
             if (kAB) Xs = mfma32(in.at[k2], bs, Xs);
             Ys = mfma32(in.rt[k2], bs, Ys);
@@ -496,10 +523,15 @@ __global__ __launch_bounds__(kEpi ? kThreadsEpi : kThreads) void chunk_fwd_kerne
         } else {
             Yt = add4(Ys, mfma16(in.Ark, in.V, zero4()));
         }
-        const f32x4 dec[4] = {mul_row_lanes4<0>(in.gl, S[0]), mul_row_lanes4<1>(in.gl, S[1]),
-                              mul_row_lanes4<2>(in.gl, S[2]), mul_row_lanes4<3>(in.gl, S[3])};
+        f32x4 dec[JT];
+        dec[0] = mul_row_lanes4<0>(in.gl, S[0]);
+        dec[1] = mul_row_lanes4<1>(in.gl, S[1]);
+        if constexpr (JT > 2) {
+            dec[2] = mul_row_lanes4<2>(in.gl, S[2]);
+            dec[3] = mul_row_lanes4<3>(in.gl, S[3]);
+        }
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
+        for (int jt = 0; jt < JT; ++jt) {
             const f32x4 acc = mfma16(in.kbt[jt], in.V, dec[jt]);   // G_L S^T + Kb^T V
             S[jt] = kAB ? mfma16(in.bbt[jt], Zb, acc) : acc;        // + Bb^T Z
         }
@@ -518,28 +550,29 @@ __global__ __launch_bounds__(kEpi ? kThreadsEpi : kThreads) void chunk_fwd_kerne
             if (kAB) *reinterpret_cast<bf16x4*>(&sm.Zs[c & 1][l16][i0]) = swap_layout(Zb, ident);
             if ((c & 1) == 0) {   // entry state of a 32-token block as [j][i]: row layout of S^T tile jt
 #pragma unroll
-                for (int jt = 0; jt < 4; ++jt)
+                for (int jt = 0; jt < JT; ++jt)
                     *reinterpret_cast<bf16x4*>(&sm.S0s[(c >> 1) & 1][16 * jt + l16][i0]) =
                         swap_layout(Sb[jt], ident);
             }
         }
     };
-    // Staged outputs of chunk c to global memory; 8 consecutive threads write
-    // one 128-byte row with 16-byte stores.
+    // Staged outputs of chunk c to global memory; N/8 consecutive threads write
+    // one row (128 bytes at N = 64) with 16-byte stores: threads 0 .. 2N-1 the
+    // read-outs, 2N .. 4N-1 the removal read-outs.
     auto store_out = [&](int c) __attribute__((always_inline)) {
-        const int row = (rtid >> 3) & 15, piece = rtid & 7;
+        const int row = (rtid / (kN / 8)) & 15, piece = rtid & (kN / 8 - 1);
         const int tt = c * kL + row;
         if (tt < t_end) {
-            bf16_t* base = rtid < 128 ? y : (kAB ? tapeZ : nullptr);
-            const bf16_t(*src)[kRow] = rtid < 128 ? sm.Ys[c & 1] : sm.Zs[c & 1];
+            bf16_t* base = rtid < 2 * kN ? y : (kAB ? tapeZ : nullptr);
+            const bf16_t(*src)[kRow] = rtid < 2 * kN ? sm.Ys[c & 1] : sm.Zs[c & 1];
             if (base)
-                store_stream(base + tok_off(bb, tt, hh, T, H) + 8 * piece,
+                store_stream(base + tok_off<N>(bb, tt, hh, T, H) + 8 * piece,
                              *reinterpret_cast<const uint4*>(&src[row][8 * piece]));
         }
         if (tape && c < c_end && (c & 1) == 0) {
 #pragma unroll
-            for (int k2 = 0; k2 < 2; ++k2) {
-                const int j = 32 * k2 + (rtid >> 3);
+            for (int k2 = 0; k2 < K2; ++k2) {
+                const int j = 32 * k2 + rtid / (kN / 8);   // 32 rows of the state per pass
                 store_stream(tapeS + (((size_t)bh * nblk + (c >> 1)) * kN + j) * kN + 8 * piece,
                              *reinterpret_cast<const uint4*>(&sm.S0s[(c >> 1) & 1][j][8 * piece]));
             }
@@ -677,11 +710,11 @@ __global__ __launch_bounds__(kEpi ? kThreadsEpi : kThreads) void chunk_fwd_kerne
         const int c_ = cb + it_;                                            \
         const ERaw er = read_E(c_);                                         \
         MWIn mi;                                                            \
-        if (it_ >= 1 && (kAB ? wp >= 2 : wp == 3)) mi = read_MW(c_ - 1);    \
+        if (it_ >= 1 && (kAB ? wp >= kP - 2 : wp == kP - 1)) mi = read_MW(c_ - 1); \
         stage_E(c_, er);                                                    \
         stash_raw(c_ + 1, RING);                                            \
         load_raw(c_ + 4, RING);                                             \
-        if (it_ >= 1 && (kAB ? wp >= 2 : wp == 3)) stage_MW(c_ - 1, mi);    \
+        if (it_ >= 1 && (kAB ? wp >= kP - 2 : wp == kP - 1)) stage_MW(c_ - 1, mi); \
         __syncthreads();                                                    \
     }
             // Ring slot of interval it is (it + 1) % 3: it = 0, 1, 2 -> rb1, rb2, rb0.
@@ -761,7 +794,7 @@ __global__ __launch_bounds__(kEpi ? kThreadsEpi : kThreads) void chunk_fwd_kerne
     if (wk.fin && consumer) {
         float* dst = wk.fin + (size_t)col * kN;
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt)
+        for (int jt = 0; jt < JT; ++jt)
             *reinterpret_cast<float4*>(dst + 16 * jt + 4 * g) =
                 make_float4(S[jt][0], S[jt][1], S[jt][2], S[jt][3]);
     }
@@ -839,20 +872,18 @@ hipError_t launch_chunk_fwd(const FwdArgs& p, int chunk_len, hipStream_t stream)
     return launch_chunk_fwd_split(p, chunk_len, FwdSplit{p.B * p.H, 1, p.T, nullptr}, stream);
 }
 
-hipError_t launch_chunk_fwd_sequential(const FwdArgs& p, int chunk_len, int nseg, int seg_len,
-                                       float* states, int* sync, int spin_limit, hipStream_t stream) {
-    if (chunk_len != kL || !p.bf16) return hipErrorInvalidValue;
+namespace {
+
+template <int N>
+hipError_t launch_chunk_fwd_sequential_n(const FwdArgs& p, int nseg, int seg_len, float* states,
+                                         int* sync, int spin_limit, hipStream_t stream) {
     const int nbh = p.B * p.H;
-    if (nseg < 1 || seg_len <= 0 || seg_len % WKV7_TAPE_BLOCK != 0 ||
-        (long long)(nseg - 1) * seg_len >= p.T || !states || !sync ||
-        (long long)nbh * nseg > INT32_MAX)
-        return hipErrorInvalidValue;
     seg_sync_init_kernel<<<dim3((nbh + 255) / 256), dim3(256), 0, stream>>>(sync, nbh);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    auto kern = p.a ? (p.ckpt ? chunk_fwd_kernel<true, true, true, false> : chunk_fwd_kernel<true, true, false, false>)
-                    : (p.ckpt ? chunk_fwd_kernel<true, false, true, false> : chunk_fwd_kernel<true, false, false, false>);
-    kern<<<dim3(nbh * nseg), dim3(kThreads), 0, stream>>>(
+    auto kern = p.a ? (p.ckpt ? chunk_fwd_kernel<N, true, true, true, false> : chunk_fwd_kernel<N, true, true, false, false>)
+                    : (p.ckpt ? chunk_fwd_kernel<N, true, false, true, false> : chunk_fwd_kernel<N, true, false, false, false>);
+    kern<<<dim3(nbh * nseg), dim3(FwdShape<N>::threads), 0, stream>>>(
         p.B, p.T, p.H, static_cast<const bf16_t*>(p.r), static_cast<const bf16_t*>(p.w),
         static_cast<const bf16_t*>(p.k), static_cast<const bf16_t*>(p.v),
         static_cast<const bf16_t*>(p.a), static_cast<const bf16_t*>(p.b), p.s0,
@@ -861,18 +892,14 @@ hipError_t launch_chunk_fwd_sequential(const FwdArgs& p, int chunk_len, int nseg
     return hipGetLastError();
 }
 
-hipError_t launch_chunk_fwd_split(const FwdArgs& p, int chunk_len, const FwdSplit& sp,
-                                  hipStream_t stream) {
-    if (chunk_len != kL || !p.bf16) return hipErrorInvalidValue;
+template <int N>
+hipError_t launch_chunk_fwd_split_n(const FwdArgs& p, const FwdSplit& sp, hipStream_t stream) {
     const int nbh = p.B * p.H;
     const int nsplit = nbh - sp.split_from;
-    if (nsplit < 0 || (nsplit > 0 && (sp.nseg < 2 || sp.seg_len % WKV7_TAPE_BLOCK != 0 || sp.seg_len <= 0 ||
-                                       (long long)(sp.nseg - 1) * sp.seg_len >= p.T || !sp.states)))
-        return hipErrorInvalidValue;
     auto run = [&](int pass, int grid) {
-        auto kern = p.a ? (p.ckpt ? chunk_fwd_kernel<false, true, true, false> : chunk_fwd_kernel<false, true, false, false>)
-                        : (p.ckpt ? chunk_fwd_kernel<false, false, true, false> : chunk_fwd_kernel<false, false, false, false>);
-        kern<<<dim3(grid), dim3(kThreads), 0, stream>>>(
+        auto kern = p.a ? (p.ckpt ? chunk_fwd_kernel<N, false, true, true, false> : chunk_fwd_kernel<N, false, true, false, false>)
+                        : (p.ckpt ? chunk_fwd_kernel<N, false, false, true, false> : chunk_fwd_kernel<N, false, false, false, false>);
+        kern<<<dim3(grid), dim3(FwdShape<N>::threads), 0, stream>>>(
             p.B, p.T, p.H, static_cast<const bf16_t*>(p.r), static_cast<const bf16_t*>(p.w),
             static_cast<const bf16_t*>(p.k), static_cast<const bf16_t*>(p.v),
             static_cast<const bf16_t*>(p.a), static_cast<const bf16_t*>(p.b), p.s0,
@@ -883,18 +910,52 @@ hipError_t launch_chunk_fwd_split(const FwdArgs& p, int chunk_len, const FwdSpli
     hipError_t e = run(0, sp.split_from + (nsplit > 0 ? nsplit * (2 * sp.nseg - 3) : 0));
     if (e != hipSuccess || nsplit == 0) return e;
     if (sp.nseg > 2) {
-        e = launch_seg_combine(nsplit, sp.nseg, sp.states, stream);
+        // (the scan's composition serves every head size; N = 64 has its own)
+        e = N == 64 ? launch_seg_combine(nsplit, sp.nseg, sp.states, stream)
+                    : launch_seg_combine_n(N, nsplit, sp.nseg, sp.states, stream);
         if (e != hipSuccess) return e;
     }
     return run(1, nsplit * (sp.nseg - 1));
 }
 
+}  // namespace
+
+hipError_t launch_chunk_fwd_sequential(const FwdArgs& p, int chunk_len, int nseg, int seg_len,
+                                       float* states, int* sync, int spin_limit, hipStream_t stream) {
+    if (chunk_len != kL || !p.bf16) return hipErrorInvalidValue;
+    const int nbh = p.B * p.H;
+    if (nseg < 1 || seg_len <= 0 || seg_len % WKV7_TAPE_BLOCK != 0 ||
+        (long long)(nseg - 1) * seg_len >= p.T || !states || !sync ||
+        (long long)nbh * nseg > INT32_MAX)
+        return hipErrorInvalidValue;
+    switch (p.N) {
+        case 32: return launch_chunk_fwd_sequential_n<32>(p, nseg, seg_len, states, sync, spin_limit, stream);
+        case 64: return launch_chunk_fwd_sequential_n<64>(p, nseg, seg_len, states, sync, spin_limit, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_chunk_fwd_split(const FwdArgs& p, int chunk_len, const FwdSplit& sp,
+                                  hipStream_t stream) {
+    if (chunk_len != kL || !p.bf16) return hipErrorInvalidValue;
+    const int nbh = p.B * p.H;
+    const int nsplit = nbh - sp.split_from;
+    if (nsplit < 0 || (nsplit > 0 && (sp.nseg < 2 || sp.seg_len % WKV7_TAPE_BLOCK != 0 || sp.seg_len <= 0 ||
+                                       (long long)(sp.nseg - 1) * sp.seg_len >= p.T || !sp.states)))
+        return hipErrorInvalidValue;
+    switch (p.N) {
+        case 32: return launch_chunk_fwd_split_n<32>(p, sp, stream);
+        case 64: return launch_chunk_fwd_split_n<64>(p, sp, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 hipError_t launch_chunk_fwd_epilogue(const FwdArgs& p, const EpiParams& e, hipStream_t stream) {
-    if (!p.bf16 || p.tape || p.ckpt || e.mode < 0 || e.mode > 2) return hipErrorInvalidValue;
+    if (!p.bf16 || p.N != 64 || p.tape || p.ckpt || e.mode < 0 || e.mode > 2) return hipErrorInvalidValue;
     if (!chunk_fwd_epilogue_fits(p.T, p.H)) return hipErrorInvalidValue;   // 32-bit buffer offsets
     const int nbh = p.B * p.H;
-    auto kern = p.a ? chunk_fwd_kernel<false, true, false, true> : chunk_fwd_kernel<false, false, false, true>;
-    kern<<<dim3(nbh), dim3(kThreadsEpi), 0, stream>>>(
+    auto kern = p.a ? chunk_fwd_kernel<64, false, true, false, true> : chunk_fwd_kernel<64, false, false, false, true>;
+    kern<<<dim3(nbh), dim3(FwdShape<64>::threads_epi), 0, stream>>>(
         p.B, p.T, p.H, static_cast<const bf16_t*>(p.r), static_cast<const bf16_t*>(p.w),
         static_cast<const bf16_t*>(p.k), static_cast<const bf16_t*>(p.v),
         static_cast<const bf16_t*>(p.a), static_cast<const bf16_t*>(p.b), p.s0,

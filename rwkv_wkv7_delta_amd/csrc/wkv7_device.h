@@ -211,8 +211,9 @@ __device__ __forceinline__ void store_stream(void* dst, uint4 x) {
 }
 
 // Token tensor offset for [B][T][H][N].
+template <int N = kN>
 __device__ __forceinline__ size_t tok_off(int b, int t, int h, int T, int H) {
-    return (((size_t)b * T + t) * H + h) * kN;
+    return (((size_t)b * T + t) * H + h) * N;
 }
 
 // Work of one workgroup: a head over tokens [t_begin, t_end), started from the

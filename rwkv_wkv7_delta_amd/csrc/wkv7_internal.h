@@ -101,6 +101,8 @@ hipError_t launch_seq_fwd_split(const FwdArgs& p, const FwdSplit& split, hipStre
 // Entry states of segments 2 .. nseg-1 of nsplit split heads (N = 64), from
 // segment 0's final state and the maps in `states` (the plan's layout).
 hipError_t launch_seg_combine(int nsplit, int nseg, float* states, hipStream_t stream);
+// The same composition for N = 32 or 128 (wkv7_seq.hip).
+hipError_t launch_seg_combine_n(int N, int nsplit, int nseg, float* states, hipStream_t stream);
 // Every head as nseg segments of seg_len tokens run in order (one workgroup
 // per segment, segment-major); `states` holds one fp32 N x N state per head,
 // `sync` B*H ints (cleared by the launch).  A segment polls its predecessor's

@@ -715,6 +715,20 @@ hipError_t launch_seq_fwd_split(const FwdArgs& p, const FwdSplit& sp, hipStream_
     return p.bf16 ? launch_seq_fwd_t<bf16_t>(p, sp, stream) : launch_seq_fwd_t<float>(p, sp, stream);
 }
 
+hipError_t launch_seg_combine_n(int N, int nsplit, int nseg, float* states, hipStream_t stream) {
+    if (nsplit <= 0 || nseg < 3 || !states) return hipErrorInvalidValue;
+    switch (N) {
+        case 32:
+            seg_combine_n_kernel<32><<<dim3(nsplit * 2), dim3(256), 0, stream>>>(nseg, states);
+            break;
+        case 128:
+            seg_combine_n_kernel<128><<<dim3(nsplit * 8), dim3(256), 0, stream>>>(nseg, states);
+            break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_state_copy(int BH, int N, const float* s0, float* sT, hipStream_t stream) {
     const size_t n4 = (size_t)BH * N * N / 4;
     state_copy_kernel<<<dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream>>>(n4, s0, sT);

@@ -105,7 +105,7 @@ def test_forward_ckpt_validation(L):
     assert f(None, *[FAKE] * 6, None, FAKE, None, FAKE, None) == wk.WKV7_ERR_INVALID_ARG
     assert f(ctypes.byref(d), *[FAKE] * 6, None, FAKE, None, FAKE + 8, None) == wk.WKV7_ERR_INVALID_ARG
     assert f(ctypes.byref(d), *[FAKE] * 6, None, None, None, FAKE, None) == wk.WKV7_ERR_INVALID_ARG
-    assert f(ctypes.byref(wk.make_desc(1, 8, 1, 32, wk.WKV7_BF16, 16)), *[FAKE] * 6, None, FAKE,
+    assert f(ctypes.byref(wk.make_desc(1, 8, 1, 128, wk.WKV7_BF16, 16)), *[FAKE] * 6, None, FAKE,
              None, FAKE, None) == wk.WKV7_ERR_UNSUPPORTED
     assert f(ctypes.byref(wk.make_desc(0, 8, 1, 64, wk.WKV7_BF16, 16)), *[FAKE] * 6, None, FAKE,
              None, FAKE, None) == wk.WKV7_OK
@@ -122,9 +122,9 @@ def _fwd(L, d, ptrs=None, y=FAKE):
 def test_forward_validation(L):
     assert L.wkv7_forward(None, *[FAKE] * 6, None, FAKE, None, None, None) == wk.WKV7_ERR_INVALID_ARG
     assert _fwd(L, wk.make_desc(1, 8, 1, 48, wk.WKV7_BF16, 0)) == wk.WKV7_ERR_UNSUPPORTED
-    # N = 32 and 128: the sequential scan only (the chunked form runs N = 64).
-    assert _fwd(L, wk.make_desc(1, 8, 1, 32, wk.WKV7_BF16, 16)) == wk.WKV7_ERR_UNSUPPORTED
+    # N = 128: the sequential scan only (the chunked forward runs N = 32 and 64).
     assert _fwd(L, wk.make_desc(1, 8, 1, 128, wk.WKV7_BF16, 16)) == wk.WKV7_ERR_UNSUPPORTED
+    assert _fwd(L, wk.make_desc(1, 8, 1, 32, wk.WKV7_F32, 16)) == wk.WKV7_ERR_UNSUPPORTED
     assert _fwd(L, wk.make_desc(1, 8, 1, 128, wk.WKV7_BF16, 0), y=None) == wk.WKV7_ERR_INVALID_ARG
     assert _fwd(L, wk.make_desc(0, 8, 1, 32, wk.WKV7_BF16, 0)) == wk.WKV7_OK
     assert _fwd(L, wk.make_desc(-1, 8, 1, 64, wk.WKV7_BF16, 0)) == wk.WKV7_ERR_INVALID_ARG
@@ -197,7 +197,7 @@ def test_split_static_validation(L):
     assert f(ctypes.byref(d), *args, -17, None) == wk.WKV7_ERR_INVALID_ARG
     assert f(ctypes.byref(d), *[FAKE] * 5, FAKE + 8, None, FAKE, None, None, 4, None) == \
         wk.WKV7_ERR_INVALID_ARG
-    assert f(ctypes.byref(wk.make_desc(1, 256, 1, 32, wk.WKV7_BF16, 16)), *args, 4, None) == \
+    assert f(ctypes.byref(wk.make_desc(1, 256, 1, 128, wk.WKV7_BF16, 16)), *args, 4, None) == \
         wk.WKV7_ERR_UNSUPPORTED
     big = wk.make_desc(4, 4096, 32, 64, wk.WKV7_BF16, 16)   # 128 heads x 16 segments x 3 maps
     assert wk.split_workspace_bytes(big, 16) > wk.STATIC_SCRATCH_BYTES
@@ -384,7 +384,7 @@ def test_forward_epilogue_validation(L):
              FAKE, None, None) == wk.WKV7_ERR_INVALID_ARG
     assert f(ctypes.byref(wk.make_desc(1, 32, 2, 64, wk.WKV7_F32, 16)), *ins, None,
              ctypes.byref(ok), FAKE, None, None) == wk.WKV7_ERR_UNSUPPORTED
-    assert f(ctypes.byref(wk.make_desc(1, 32, 2, 32, wk.WKV7_BF16, 16)), *ins, None,
+    assert f(ctypes.byref(wk.make_desc(1, 32, 2, 128, wk.WKV7_BF16, 16)), *ins, None,
              ctypes.byref(ok), FAKE, None, None) == wk.WKV7_ERR_UNSUPPORTED
     assert f(ctypes.byref(d), *ins[:6], FAKE + 4, None, ctypes.byref(ok), FAKE, None, None) == \
         wk.WKV7_ERR_INVALID_ARG   # misaligned s0
