@@ -602,6 +602,24 @@ def secondary(torch, wk, dev):
     res = {}
     N = 64
     res["chunked_fwd_1.5b"] = chunked_fwd_15b(torch, wk, dev)
+    # The chunked forward at head size 32 over the same model width as the
+    # 1.5B shape (H=64 heads of 32 channels, 512 heads: two workgroups per
+    # compute unit).
+    B, T, H, N2 = 8, 4096, 64, 32
+    ins = _dev_inputs(torch, (B, T, H, N2), dev, 2)
+    s0 = 0.1 * torch.randn(B, H, N2, N2, device=dev)
+    y = torch.empty_like(ins[0])
+    fn = lambda: wk.forward(*ins, s0, chunk_len=16, out=y)
+    for _ in range(3):
+        fn()
+    ms = float(np.median([_time(torch, fn, 4) for _ in range(10)]))
+    nbytes = B * T * H * 7 * N2 * 2 + 2 * B * H * N2 * N2 * 4
+    res["chunked_fwd_n32"] = {"workload": "B=8 T=4096 H=64 N=32 bf16, s0~0.1N(0,1), L=16, returns sT "
+                                          "(median of 10 repetitions of 4 calls)",
+                              "ms": round(ms, 4), "tokens_per_s": round(B * T / ms * 1e3, 1),
+                              "alg_GBs": round(nbytes / ms / 1e6, 1),
+                              "frac_hbm": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
+    del ins, s0, y
     # The step after the read-out (current-token term, per-head normalisation,
     # gate) at the 2.9B-model shape: on its own (HBM-bound: y, r, k, v, g read,
     # the result written, 6 x 128 bytes per token-head), and after the chunked

@@ -24,7 +24,7 @@ int check_desc(const wkv7_desc* d) {
     if (!d) return WKV7_ERR_INVALID_ARG;
     if (d->B < 0 || d->T < 0 || d->H < 0 || d->N < 0) return WKV7_ERR_INVALID_ARG;
     if (d->N != 32 && d->N != 64 && d->N != 128) return WKV7_ERR_UNSUPPORTED;
-    // The chunked forward runs N = 32 and 64 (its backward N = 64: run_backward).
+    // The chunked forms run N = 32 and 64.
     if (d->chunk_len != 0 && d->N != 32 && d->N != WKV7_HEAD_SIZE) return WKV7_ERR_UNSUPPORTED;
     if (d->dtype != WKV7_F32 && d->dtype != WKV7_BF16) return WKV7_ERR_UNSUPPORTED;
     if (d->chunk_len != 0 && d->chunk_len != 16) return WKV7_ERR_UNSUPPORTED;
@@ -235,7 +235,7 @@ size_t wkv7_ckpt_bytes(const wkv7_desc* desc) {
 size_t wkv7_backward_workspace_bytes(const wkv7_desc* desc, int with_tape) {
     if (check_desc(desc) != WKV7_OK) return 0;
     if (desc->chunk_len == 0) return seq_ckpt_bytes(desc);
-    if (desc->dtype != WKV7_BF16 || desc->N != WKV7_HEAD_SIZE) return 0;
+    if (desc->dtype != WKV7_BF16) return 0;
     return tape_bytes_unchecked(desc) * (with_tape ? 1 : 2) + kQueueBytes;
 }
 
@@ -357,11 +357,13 @@ wkv7::BwdArgs slice(const wkv7_desc* d, int b0, int nb, const void* r, const voi
     const uint16_t* tp = static_cast<const uint16_t*>(tape);
     uint16_t* wsp = static_cast<uint16_t*>(workspace);
     int* queue = reinterpret_cast<int*>(static_cast<char*>(workspace) + tape_bytes_unchecked(d)) + 2 * group;
-    return wkv7::BwdArgs{nb, d->T, d->H, true, tk(r), tk(w), tk(k), tk(v), tk(a), tk(b), sf(s0),
-                         tk(dy), sf(dsT), tp + (size_t)b0 * tok, tp + ztot + (size_t)b0 * st,
-                         tkm(dr), tkm(dw), tkm(dk), tkm(dv), tkm(da), tkm(db),
-                         ds0 ? ds0 + (size_t)b0 * sst : nullptr, wsp + (size_t)b0 * tok,
-                         wsp + ztot + (size_t)b0 * st, queue};
+    wkv7::BwdArgs p{nb, d->T, d->H, true, tk(r), tk(w), tk(k), tk(v), tk(a), tk(b), sf(s0),
+                    tk(dy), sf(dsT), tp + (size_t)b0 * tok, tp + ztot + (size_t)b0 * st,
+                    tkm(dr), tkm(dw), tkm(dk), tkm(dv), tkm(da), tkm(db),
+                    ds0 ? ds0 + (size_t)b0 * sst : nullptr, wsp + (size_t)b0 * tok,
+                    wsp + ztot + (size_t)b0 * st, queue};
+    p.N = d->N;
+    return p;
 }
 
 // Shared by every backward entry point.  stages: the passes to run; aux: a
@@ -375,10 +377,10 @@ int run_backward(const wkv7_desc* desc, const void* r, const void* w, const void
     int st = check_desc(desc);
     if (st != WKV7_OK) return st;
     const bool seq = desc->chunk_len == 0;
-    // The chunked adjoint runs on bf16 matrix cores at N = 64; the sequential
-    // reverse pass (chunk_len = 0) takes either dtype and N = 32, 64, 128, and
-    // has no separate stages.
-    if (!seq && (desc->dtype != WKV7_BF16 || desc->N != WKV7_HEAD_SIZE)) return WKV7_ERR_UNSUPPORTED;
+    // The chunked adjoint runs on bf16 matrix cores at N = 32 and 64; the
+    // sequential reverse pass (chunk_len = 0) takes either dtype and N = 32, 64,
+    // 128, and has no separate stages.
+    if (!seq && desc->dtype != WKV7_BF16) return WKV7_ERR_UNSUPPORTED;
     if (seq && stages != (wkv7::BWD_CHAIN | wkv7::BWD_KEYS)) return WKV7_ERR_UNSUPPORTED;
     if ((int64_t)desc->B * desc->H * (((int64_t)desc->T + WKV7_TAPE_CHUNK - 1) / WKV7_TAPE_CHUNK) > INT32_MAX)
         return WKV7_ERR_UNSUPPORTED;
@@ -431,7 +433,8 @@ int run_backward(const wkv7_desc* desc, const void* r, const void* w, const void
     // in one round, and its per-key pass runs beside the second group's chain.
     int b1 = desc->B;
     if (aux && desc->B > 1) {
-        const int ncu = device_cus();
+        // (at N = 32 two chains share a compute unit)
+        const int ncu = device_cus() * (desc->N == 32 ? 2 : 1);
         if (ncu > 0 && (int64_t)desc->B * desc->H > ncu) {
             b1 = ncu / desc->H;
             if (b1 < 1) b1 = 1;

@@ -40,7 +40,9 @@ namespace wkv7 {
 namespace {
 
 constexpr int kL = 16;
-constexpr int kRow = kN + 8;    // padded LDS rows (see wkv7_chunk_fwd.hip)
+// Padded LDS rows (see wkv7_chunk_fwd.hip), for head size N = 32 or 64.
+template <int N>
+constexpr int kRowOf = N + 8;
 
 __device__ __forceinline__ float bf2f(bf16_t x) { return __uint_as_float((uint32_t)x << 16); }
 __device__ __forceinline__ bf16x4 ld4(const bf16_t* p) {
@@ -65,7 +67,10 @@ struct Raw {
 // Pass 1: the adjoint chain.
 // =============================================================================
 
-constexpr int kP1Threads = 640;   // 4 producer, 4 consumer, 2 inverse waves
+// N/16 producer, N/16 consumer, 2 inverse waves (640 threads at N = 64; 384 at
+// N = 32, two workgroups per compute unit).
+template <int N>
+constexpr int kP1Threads = 64 * (2 * (N / 16) + 2);
 constexpr int kP1Slots = 4;
 enum { P1_R = 0, P1_W = 1, P1_K = 2, P1_A = 3, P1_B = 4, P1_DY = 5 };
 // Tile images in a slot: the A-operand image of (Arb Tm)^T, from INV; those of
@@ -75,37 +80,49 @@ enum { TILE_RB = 0, TILE_AK = 1, TILE_RK = 2 };
 // Rows [t][j] (the chain reads At, Rt and dy transposed, which gives the
 // matrix-core operand layouts directly) and images: register contents stored
 // lane by lane (8 bytes per lane, read back by the same lane index).
+template <int N>
 struct P1Slot {
+    static constexpr int kRow = kRowOf<N>;
     bf16_t At[kL][kRow], Rt[kL][kRow];                  // E -> MW, INV, chain
     bf16_t Bb[kL][kRow];                                // E -> INV; Tm^T Bb from INV -> chain
     bf16_t Kb[kL][kRow], dY[kL][kRow];                  // E -> chain
-    float gL[kN];         // G_L of key 16 jt + 4 g + q at word 16 g + 4 jt + q
+    float gL[64];         // G_L of key 16 jt + 4 g + q at word 16 g + 4 jt + q
     uint2 tiles[3][64];
 };
 // Bh and Kh, read only in the interval after E.
+template <int N>
 struct P1SlotBK {
+    static constexpr int kRow = kRowOf<N>;
     bf16_t Bh[kL][kRow], Kh[kL][kRow];
 };
 
+template <int N>
 struct __align__(16) P1Smem {
+    static constexpr int kRow = kRowOf<N>;
     bf16_t raw[2][6][kL][kRow];   // r, w, k, a, b, dy of two chunks
-    P1Slot sl[kP1Slots];
-    P1SlotBK bk[2];
+    P1Slot<N> sl[kP1Slots];
+    P1SlotBK<N> bk[2];
     bf16_t dXs[2][kL][kRow];      // [t][i]
     bf16_t dVs[2][kL][kRow];      // [t][i]
-    bf16_t dSs[2][kN][kRow];      // the adjoint leaving the chunk as [j][i] (kept per 32 tokens)
+    bf16_t dSs[2][N][kRow];       // the adjoint leaving the chunk as [j][i] (kept per 32 tokens)
 };
 
 // kAB = false: a = b = 0 (decay-only recurrence); a and b are not read and
 // stand as zero rows, so the removal terms vanish from every product.
-template <bool kAB>
-__global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
+template <int N, bool kAB>
+__global__ __launch_bounds__(kP1Threads<N>, N == 32 ? 2 : 1) void bwd_chain_kernel(
     int T, int H, const bf16_t* __restrict__ r, const bf16_t* __restrict__ w,
     const bf16_t* __restrict__ k, const bf16_t* __restrict__ a, const bf16_t* __restrict__ b,
     const bf16_t* __restrict__ dy, const float* __restrict__ dsT, bf16_t* __restrict__ dv,
     float* __restrict__ ds0, bf16_t* __restrict__ wdX, bf16_t* __restrict__ wdS,
     int* __restrict__ counter) {
-    __shared__ P1Smem sm;
+    // (these hide the file-scope N = 64 constants in the body below)
+    constexpr int kN = N, kRow = kRowOf<N>;
+    constexpr int kP = N / 16;                  // producer (and consumer) waves
+    constexpr int K2 = N / 32, JT = N / 16;     // 32-deep halves, 16-wide key tiles
+    using P1Slot = wkv7::P1Slot<N>;
+    using P1SlotBK = wkv7::P1SlotBK<N>;
+    __shared__ P1Smem<N> sm;
     const int bh = blockIdx.x;
     const int bb = bh / H, hh = bh % H;
     const int tid = threadIdx.x;
@@ -113,11 +130,11 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
     // as per-lane conditions: branching on an SGPR copy of the wave index
     // measured several per cent slower.
     const int wave = tid >> 6;
-    const bool producer = wave < 4;
-    const bool consumer = wave >= 4 && wave < 8;
-    const bool inverter = wave >= 8;
-    const int rtid = tid & 255;
-    const int lane = tid & 63, wp = (tid >> 6) & 3;
+    const bool producer = wave < kP;
+    const bool consumer = wave >= kP && wave < 2 * kP;
+    const bool inverter = wave >= 2 * kP;
+    const int rtid = tid & (64 * kP - 1);
+    const int lane = tid & 63, wp = (tid >> 6) & (kP - 1);
     const int l16 = lane & 15, g = lane >> 4;
     const int col = 16 * wp + l16;
     const int nch = (T + kL - 1) / kL;
@@ -139,13 +156,13 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
     }
 
     // ---- consumer adjoint: dS^T tiles, lane holds dS[col][16 jt + 4 g + q] -------
-    f32x4 dSt[4];
+    f32x4 dSt[JT];
 #pragma unroll
-    for (int jt = 0; jt < 4; ++jt) dSt[jt] = zero4();
+    for (int jt = 0; jt < JT; ++jt) dSt[jt] = zero4();
     if (consumer && dsT) {
         const float* base = dsT + ((size_t)bh * kN + col) * kN;
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
+        for (int jt = 0; jt < JT; ++jt) {
             const float4 x = *reinterpret_cast<const float4*>(base + 16 * jt + 4 * g);
             dSt[jt][0] = x.x; dSt[jt][1] = x.y; dSt[jt][2] = x.z; dSt[jt][3] = x.w;
         }
@@ -156,12 +173,12 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
     }
 
     // ---- producer raw loads (as in the forward; vector 5 is dy) -------------------
-    const bool hi = rtid >= 128;
+    const bool hi = rtid >= 2 * kN;
     const bf16_t* const sp_p[3] = {hi ? w : r, hi ? a : k, hi ? dy : b};
-    const int ld_t = (rtid >> 3) & 15, ld_c8 = rtid & 7;
+    const int ld_t = (rtid / (kN / 8)) & 15, ld_c8 = rtid & (kN / 8 - 1);
     auto load_raw = [&](int c, Raw& o) __attribute__((always_inline)) {
         const int t = max(0, min(c * kL + ld_t, T - 1));
-        const size_t off = tok_off(bb, t, hh, T, H) + ld_c8 * 8;
+        const size_t off = tok_off<N>(bb, t, hh, T, H) + ld_c8 * 8;
 #pragma unroll
         for (int p = 0; p < 3; ++p) {
             if (kAB || !(p == 1 ? hi : p == 2 ? !hi : false)) {
@@ -247,11 +264,12 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
     };
 
     // ---- MW (producer): one 16x16 tile per wave ---------------------------------
-    // Waves 2, 3 form Aak = tril_-1(At Kh^T), Ark = tril_0(Rt Kh^T) as [t][s] =
-    // X_t . Y_s, whose accumulator registers are the A-operand images of Aak^T,
-    // Ark^T; Aab, Arb and the inverse come from the inverse waves.
+    // The last two producer waves (2, 3 at N = 64; 0, 1 at N = 32) form Aak =
+    // tril_-1(At Kh^T), Ark = tril_0(Rt Kh^T) as [t][s] = X_t . Y_s, whose
+    // accumulator registers are the A-operand images of Aak^T, Ark^T; Aab, Arb
+    // and the inverse come from the inverse waves.
     struct MWIn {
-        bf16x8 xv[2], yv[2];
+        bf16x8 xv[K2], yv[K2];
     };
     auto read_MW = [&](int c) __attribute__((always_inline)) -> MWIn {
         const P1Slot& s = sm.sl[slot_of(c)];
@@ -260,7 +278,7 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
         const bf16_t(*Yr)[kRow] = bk.Kh;
         MWIn in;
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
+        for (int k2 = 0; k2 < K2; ++k2) {
             in.xv[k2] = ld8(&Xr[l16][32 * k2 + 8 * g]);
             in.yv[k2] = ld8(&Yr[l16][32 * k2 + 8 * g]);
         }
@@ -270,15 +288,15 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
         P1Slot& s = sm.sl[slot_of(c)];
         f32x4 P = zero4();
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) P = mfma32(in.xv[k2], in.yv[k2], P);   // [t][s] = X_t . Y_s
-        const bool diag = wp == 3;   // Ark keeps the diagonal
+        for (int k2 = 0; k2 < K2; ++k2) P = mfma32(in.xv[k2], in.yv[k2], P);   // [t][s] = X_t . Y_s
+        const bool diag = (wp & 1) != 0;   // Ark keeps the diagonal
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int m = 4 * g + q, n = l16;
             P[q] = (n < m || (diag && n == m)) ? P[q] : 0.f;
         }
         // Accumulator registers of X fed as an A operand stand for X^T.
-        s.tiles[wp == 2 ? TILE_AK : TILE_RK][lane] = __builtin_bit_cast(uint2, cvt4(P));
+        s.tiles[(wp & 1) == 0 ? TILE_AK : TILE_RK][lane] = __builtin_bit_cast(uint2, cvt4(P));
     };
     // ---- INV (inverse waves): Aab, Tm = (I - Aab)^-1, Tm^T Bb, (Arb Tm)^T -------
     // In the interval after E(c) a wave forms Aab = tril_-1(At Bh^T) and Arb^T
@@ -299,16 +317,16 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
     auto inv_begin = [&](int c) __attribute__((always_inline)) -> InvState {
         const P1Slot& s = sm.sl[slot_of(c)];
         const P1SlotBK& bk = sm.bk[c & 1];
-        bf16x8 xv[2], yv[2], rv[2];
+        bf16x8 xv[K2], yv[K2], rv[K2];
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
+        for (int k2 = 0; k2 < K2; ++k2) {
             xv[k2] = ld8(&s.At[l16][32 * k2 + 8 * g]);
             yv[k2] = ld8(&bk.Bh[l16][32 * k2 + 8 * g]);
             rv[k2] = ld8(&s.Rt[l16][32 * k2 + 8 * g]);
         }
         f32x4 P = zero4(), R = zero4();
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
+        for (int k2 = 0; k2 < K2; ++k2) {
             P = mfma32(xv[k2], yv[k2], P);   // [t][s] = Aab[t][s]
             R = mfma32(yv[k2], rv[k2], R);   // [s][t] = Arb[t][s]
         }
@@ -321,12 +339,12 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
     };
     auto inv_end = [&](int c, const InvState& st) __attribute__((always_inline)) {
         P1Slot& s = sm.sl[slot_of(c)];
-        bf16x4 bbT[4];
+        bf16x4 bbT[JT];
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt) bbT[jt] = ld4_tr(tr_addr(&s.Bb[0][16 * jt], kRow, g, l16));
+        for (int jt = 0; jt < JT; ++jt) bbT[jt] = ld4_tr(tr_addr(&s.Bb[0][16 * jt], kRow, g, l16));
         const Split4 tm = split4(unit_lower_inverse_cols_end(st.bi));
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
+        for (int jt = 0; jt < JT; ++jt) {
             const f32x4 d = mfma16(bbT[jt], tm.hi, mfma16(bbT[jt], tm.lo, zero4()));
             *reinterpret_cast<bf16x4*>(&s.Bb[l16][16 * jt + 4 * g]) = cvt4(d);
         }
@@ -336,8 +354,8 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
     // ---- chain (consumer): value rows `col` of the adjoint ------------------------
     struct CIn {
         bf16x4 RbT, AakT, ArkT, dY;
-        bf16x8 bb[2], kb[2];
-        bf16x4 rtT[4], atT[4];
+        bf16x8 bb[K2], kb[K2];
+        bf16x4 rtT[JT], atT[JT];
         float gl;   // G_L of key 16 jt + 4 g + q sits in lane 4 jt + q of row g
     };
     auto read_C = [&](int c) __attribute__((always_inline)) -> CIn {
@@ -350,12 +368,12 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
         in.ArkT = __builtin_bit_cast(bf16x4, s.tiles[TILE_RK][lane]);
         in.dY = ld4_tr(tr_addr(&s.dY[0][16 * wp], kRow, g, l16));   // [t][i] as a B operand
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
+        for (int k2 = 0; k2 < K2; ++k2) {
             if (kAB) in.bb[k2] = ld4x2(&s.Bb[l16][32 * k2 + 4 * g]);   // Tm^T Bb
             in.kb[k2] = ld4x2(&s.Kb[l16][32 * k2 + 4 * g]);
         }
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
+        for (int jt = 0; jt < JT; ++jt) {
             in.rtT[jt] = ld4_tr(tr_addr(&s.Rt[0][16 * jt], kRow, g, l16));   // Rt^T as an A operand
             if (kAB) in.atT[jt] = ld4_tr(tr_addr(&s.At[0][16 * jt], kRow, g, l16));
         }
@@ -363,16 +381,16 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
         return in;
     };
     auto stage_C = [&](int c, const CIn& in) __attribute__((always_inline)) {
-        bf16x4 dSb[4];
+        bf16x4 dSb[JT];
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt) dSb[jt] = cvt4(dSt[jt]);
+        for (int jt = 0; jt < JT; ++jt) dSb[jt] = cvt4(dSt[jt]);
         // dX = Tm^T dZ = (Tm^T Bb) dS^T + (Arb Tm)^T dY with both factors from INV.
         // Partial sums of the two MFMA shapes meet on the vector ALU (add4).
         // (a = b = 0: Bb, Arb, Aak vanish, so dX = 0 and only the Kb and Ark
         // terms of dV remain.)
         f32x4 dXs = zero4(), dVk = zero4();
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
+        for (int k2 = 0; k2 < K2; ++k2) {
             const bf16x8 ds8 = cat8(dSb[2 * k2], dSb[2 * k2 + 1]);
             if (kAB) dXs = mfma32(in.bb[k2], ds8, dXs);
             dVk = mfma32(in.kb[k2], ds8, dVk);
@@ -392,36 +410,42 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
         *reinterpret_cast<bf16x4*>(&sm.dVs[sb][l16][i0]) = swap_layout(dVb, ident);
         if (keeps_dS(c)) {
 #pragma unroll
-            for (int jt = 0; jt < 4; ++jt)   // as [j][i]: row layout of the dS^T tile of key block jt
+            for (int jt = 0; jt < JT; ++jt)   // as [j][i]: row layout of the dS^T tile of key block jt
                 *reinterpret_cast<bf16x4*>(&sm.dSs[sb][16 * jt + l16][i0]) = swap_layout(dSb[jt], ident);
         }
         // dS0^T = G_L dS^T + Rt^T dY + At^T dX
-        const f32x4 dec[4] = {mul_row_lanes4<0>(in.gl, dSt[0]), mul_row_lanes4<1>(in.gl, dSt[1]),
-                              mul_row_lanes4<2>(in.gl, dSt[2]), mul_row_lanes4<3>(in.gl, dSt[3])};
+        f32x4 dec[JT];
+        dec[0] = mul_row_lanes4<0>(in.gl, dSt[0]);
+        dec[1] = mul_row_lanes4<1>(in.gl, dSt[1]);
+        if constexpr (JT > 2) {
+            dec[2] = mul_row_lanes4<2>(in.gl, dSt[2]);
+            dec[3] = mul_row_lanes4<3>(in.gl, dSt[3]);
+        }
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
+        for (int jt = 0; jt < JT; ++jt) {
             const f32x4 acc = mfma16(in.rtT[jt], in.dY, dec[jt]);
             dSt[jt] = kAB ? mfma16(in.atT[jt], dXb, acc) : acc;
         }
     };
 
     // ---- outputs of chunk c (consumers): dv and dX rows, the chunk's exit adjoint --
-    // 8 consecutive threads write one 128-byte row with 16-byte stores.
+    // N/8 consecutive threads write one row (128 bytes at N = 64) with 16-byte
+    // stores: threads 0 .. 2N-1 dv, 2N .. 4N-1 dX.
     auto store_out = [&](int c) __attribute__((always_inline)) {
         if (c < 0) return;
         const int sb = c & 1;
-        const int row = (rtid >> 3) & 15, piece = rtid & 7;
+        const int row = (rtid / (kN / 8)) & 15, piece = rtid & (kN / 8 - 1);
         const int tt = c * kL + row;
-        if (tt < T && (kAB || rtid < 128)) {   // a = b = 0: dX is zero, not stored
-            bf16_t* base = rtid < 128 ? dv : wdX;
-            const bf16_t(*src)[kRow] = rtid < 128 ? sm.dVs[sb] : sm.dXs[sb];
-            store_stream(base + tok_off(bb, tt, hh, T, H) + 8 * piece,
+        if (tt < T && (kAB || rtid < 2 * kN)) {   // a = b = 0: dX is zero, not stored
+            bf16_t* base = rtid < 2 * kN ? dv : wdX;
+            const bf16_t(*src)[kRow] = rtid < 2 * kN ? sm.dVs[sb] : sm.dXs[sb];
+            store_stream(base + tok_off<N>(bb, tt, hh, T, H) + 8 * piece,
                          *reinterpret_cast<const uint4*>(&src[row][8 * piece]));
         }
         if (keeps_dS(c)) {
 #pragma unroll
-            for (int k2 = 0; k2 < 2; ++k2) {
-                const int j = 32 * k2 + (rtid >> 3);
+            for (int k2 = 0; k2 < K2; ++k2) {
+                const int j = 32 * k2 + rtid / (kN / 8);   // 32 rows of the adjoint per pass
                 store_stream(wdS + (((size_t)bh * nblk + (c >> 1)) * kN + j) * kN + 8 * piece,
                              *reinterpret_cast<const uint4*>(&sm.dSs[sb][j][8 * piece]));
             }
@@ -455,11 +479,11 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
         const int it_ = (IT);                                                  \
         const ERaw er = read_E(chunk_of(it_));                                 \
         MWIn mi;                                                               \
-        if (it_ >= 1 && (kAB ? wp >= 2 : wp == 3)) mi = read_MW(chunk_of(it_ - 1)); \
+        if (it_ >= 1 && (kAB ? wp >= kP - 2 : wp == kP - 1)) mi = read_MW(chunk_of(it_ - 1)); \
         stage_E(chunk_of(it_), er);                                            \
         stash_raw(chunk_of(it_ + 1), RING);                                    \
         load_raw(chunk_of(it_ + 4), RING);                                     \
-        if (it_ >= 1 && (kAB ? wp >= 2 : wp == 3)) stage_MW(chunk_of(it_ - 1), mi); \
+        if (it_ >= 1 && (kAB ? wp >= kP - 2 : wp == kP - 1)) stage_MW(chunk_of(it_ - 1), mi); \
         __syncthreads();                                                       \
     }
             for (int it = 0; it < n_it; it += 3) {
@@ -506,7 +530,7 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
     if (ds0 && consumer) {
         float* dst = ds0 + ((size_t)bh * kN + col) * kN;
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt)
+        for (int jt = 0; jt < JT; ++jt)
             *reinterpret_cast<float4*>(dst + 16 * jt + 4 * g) =
                 make_float4(dSt[jt][0], dSt[jt][1], dSt[jt][2], dSt[jt][3]);
     }
@@ -526,19 +550,26 @@ __global__ __launch_bounds__(kP1Threads) void bwd_chain_kernel(
 // of c0 and of c1.  Wave p owns key columns 16p .. 16p+15 throughout, and
 // reads and writes only its own rows of the [j][i] states.
 
-constexpr int kP2Threads = 256;   // the four key blocks
-constexpr int kP2Grid = 512;      // two resident workgroups per compute unit, looping over blocks
+// One wave per key block of 16 columns (256 threads at N = 64, 128 at N = 32).
+template <int N>
+constexpr int kP2Threads = 4 * N;
+// Workgroups per launch: two per compute unit at N = 64, four at N = 32 (each
+// looping over blocks).
+template <int N>
+constexpr int kP2Grid = N == 32 ? 1024 : 512;
 
 // Rows of a chunk staged in LDS: the six token inputs the gradients need,
 // then dX and Z; and the entry state and exit adjoint of both chunks as [j][i].
 enum { P2_R = 0, P2_W = 1, P2_K = 2, P2_A = 3, P2_B = 4, P2_DY = 5, P2_V = 6, P2_DX = 7, P2_Z = 8 };
-// The chunk's four L x L adjoints dAab, dAak, dArb, dArk (tile p from wave p),
-// bf16 in row layout; 20-element rows keep both the row reads and the
-// transposed reads of a tile nearly free of bank conflicts.
+// The chunk's four L x L adjoints dAab, dAak, dArb, dArk (tile p from wave
+// p mod N/16), bf16 in row layout; 20-element rows keep both the row reads and
+// the transposed reads of a tile nearly free of bank conflicts.
 constexpr int kTileRow = 20;
+template <int N>
 struct __align__(16) P2Smem {
+    static constexpr int kRow = kRowOf<N>;
     bf16_t rows[2][9][kL][kRow];
-    bf16_t st[2][2][kN][kRow];   // [S0 | dS][chunk of the pair][j][i]
+    bf16_t st[2][2][N][kRow];    // [S0 | dS][chunk of the pair][j][i]
     bf16_t adj[4][kL][kTileRow];
 };
 
@@ -568,8 +599,8 @@ __device__ __forceinline__ void rows_of(float x, float& x0, float& x1, float& x2
 
 // kAB = false: a = b = 0; a, b and the removal read-outs Z are not read (they
 // stand as zero rows) and da, db are not written.
-template <bool kAB>
-__global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
+template <int N, bool kAB>
+__global__ __launch_bounds__(kP2Threads<N>) void bwd_keys_kernel(
     int T, int H, int nch, int nblk, int nblocks, const bf16_t* __restrict__ r,
     const bf16_t* __restrict__ w, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ a, const bf16_t* __restrict__ b, const bf16_t* __restrict__ dy,
@@ -577,7 +608,12 @@ __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
     const bf16_t* __restrict__ wdX, const bf16_t* __restrict__ wdS, bf16_t* __restrict__ dr,
     bf16_t* __restrict__ dw, bf16_t* __restrict__ dk, bf16_t* __restrict__ da,
     bf16_t* __restrict__ db, int* __restrict__ counter) {
-    __shared__ P2Smem sm;
+    // (these hide the file-scope N = 64 constants in the body below)
+    constexpr int kN = N, kRow = kRowOf<N>;
+    constexpr int kP = N / 16;                  // waves: one per key block
+    constexpr int K2 = N / 32, JT = N / 16;     // 32-deep halves, 16-wide blocks
+    constexpr int SP = N / 32;                  // 16-byte pieces of a state per thread
+    __shared__ P2Smem<N> sm;
     __shared__ int next_block;
     const int tid = threadIdx.x;
     // The wave index as a scalar (so that per-wave choices are uniform).
@@ -585,40 +621,40 @@ __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
     const int l16 = lane & 15, g = lane >> 4;
     const int col = 16 * wp + l16;     // key column j of this lane
 
-    // ---- loads of one block: both chunks' rows as whole 128-byte rows (8 threads
-    // per row, 16 bytes each; threads 0..127: r, k, b, v, Z, 128..255: w, a, dy,
-    // dX), the block's entry state and exit adjoint (two 16-byte pieces each).
+    // ---- loads of one block: both chunks' rows as whole rows (N/8 threads per
+    // row, 16 bytes each; threads 0..2N-1: r, k, b, v, Z, 2N..4N-1: w, a, dy,
+    // dX), the block's entry state and exit adjoint (N/32 16-byte pieces each).
     // Both chunks are loaded even when the block has one (the second is then all
     // padding and never used).  They are issued one block ahead into registers
     // and stashed in LDS when the block comes up, tokens past T as padding
     // (w = 1, everything else 0). ------------------------------------------------
-    const int ld_row = (tid >> 3) & 15, ld_piece = tid & 7;
-    const bool lo = wp < 2;   // threads 0..127 (a wave-uniform choice)
+    const int ld_row = (tid / (kN / 8)) & 15, ld_piece = tid & (kN / 8 - 1);
+    const bool lo = wp < kP / 2;   // threads 0..2N-1 (a wave-uniform choice)
     // With a = b = 0 the slots of a, b and dX load r instead (every thread issues
     // the same loads) and are stashed as zeros.
     const bf16_t* const src4[4] = {lo ? r : w, lo ? k : (kAB ? a : r), lo ? (kAB ? b : r) : dy,
                                    lo ? v : (kAB ? wdX : r)};
     struct P2Raw {
-        uint4 x[2][5], s[4];
+        uint4 x[2][5], s[2 * SP];
     };
     auto load_block = [&](int bi, P2Raw& o) __attribute__((always_inline)) {
         const int m = bi % nblk, bh = bi / nblk;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int t = min((2 * m + h) * kL + ld_row, T - 1);
-            const size_t off = tok_off(bh / H, t, bh % H, T, H) + 8 * ld_piece;
+            const size_t off = tok_off<N>(bh / H, t, bh % H, T, H) + 8 * ld_piece;
 #pragma unroll
             for (int vi = 0; vi < 4; ++vi) o.x[h][vi] = *reinterpret_cast<const uint4*>(src4[vi] + off);
-            // (threads 128..255 load the same Z pieces as 0..127 and drop them, so
+            // (threads 2N.. load the same Z pieces as ..2N-1 and drop them, so
             // that every thread issues the same loads)
             o.x[h][4] = kAB ? *reinterpret_cast<const uint4*>(tapeZ + off) : make_uint4(0u, 0u, 0u, 0u);
         }
         const size_t sbase = (size_t)bi * kN * kN;
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-            const int j = (tid >> 3) + 32 * h2;
+        for (int h2 = 0; h2 < SP; ++h2) {
+            const int j = tid / (kN / 8) + 32 * h2;
             o.s[h2] = *reinterpret_cast<const uint4*>(tapeS + sbase + j * kN + 8 * ld_piece);
-            o.s[2 + h2] = *reinterpret_cast<const uint4*>(wdS + sbase + j * kN + 8 * ld_piece);
+            o.s[SP + h2] = *reinterpret_cast<const uint4*>(wdS + sbase + j * kN + 8 * ld_piece);
         }
     };
     auto stash_block = [&](int bi, int nh, const P2Raw& o) __attribute__((always_inline)) {
@@ -631,7 +667,7 @@ __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
 #pragma unroll
             for (int vi = 0; vi < 4; ++vi) {
                 const unsigned pad = (!lo && vi == 0) ? 0x3F803F80u : 0u;
-                // a = b = 0: a (vi 1, threads 128..), b (vi 2, threads ..127), dX (vi 3, 128..)
+                // a = b = 0: a (vi 1, threads 2N..), b (vi 2, threads ..2N-1), dX (vi 3, 2N..)
                 const bool zero = !kAB && (vi == 1 ? !lo : vi == 2 ? lo : vi == 3 ? !lo : false);
                 *reinterpret_cast<uint4*>(&sm.rows[h][lo ? set_lo[vi] : set_hi[vi]][ld_row][8 * ld_piece]) =
                     (ok && !zero) ? o.x[h][vi] : make_uint4(pad, pad, pad, pad);
@@ -641,10 +677,10 @@ __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
                     ok ? o.x[h][4] : make_uint4(0u, 0u, 0u, 0u);
         }
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-            const int j = (tid >> 3) + 32 * h2;
+        for (int h2 = 0; h2 < SP; ++h2) {
+            const int j = tid / (kN / 8) + 32 * h2;
             *reinterpret_cast<uint4*>(&sm.st[0][0][j][8 * ld_piece]) = o.s[h2];
-            *reinterpret_cast<uint4*>(&sm.st[1][nh - 1][j][8 * ld_piece]) = o.s[2 + h2];
+            *reinterpret_cast<uint4*>(&sm.st[1][nh - 1][j][8 * ld_piece]) = o.s[SP + h2];
         }
     };
 
@@ -743,7 +779,7 @@ __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
     if (nh == 2) {
         const KeyFactors f0 = factors(0), f1 = factors(1);
 #pragma unroll
-        for (int vb = 0; vb < 4; ++vb) {
+        for (int vb = 0; vb < JT; ++vb) {
             const int i0 = 16 * vb + 4 * g;
             // [t][i] tiles of value block vb in accumulator layout (lane holds
             // [4g+q][l16]); fed as A operands they stand for their transposes.
@@ -779,9 +815,9 @@ __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
         const KeyFactors f = factors(h);
         // ---- the chunk's rows (row l16, 8 values at 32 k2 + 8 g) and column
         // `col` of S0 and dS ----------------------------------------------------------
-        bf16x8 dXr[2], Zr[2], dYr[2], Vr[2], S0c[2], dSc[2];
+        bf16x8 dXr[K2], Zr[K2], dYr[K2], Vr[K2], S0c[K2], dSc[K2];
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
+        for (int k2 = 0; k2 < K2; ++k2) {
             const int i0 = 32 * k2 + 8 * g;
             if (kAB) {
                 dXr[k2] = ld8(&sm.rows[h][P2_DX][l16][i0]);
@@ -793,16 +829,19 @@ __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
             dSc[k2] = ld8(&sm.st[1][h][col][i0]);
         }
 
-        // ---- the L x L adjoints, one per wave: wave p forms tile p of
-        // dAab = tril_-1(dX Z^T), dAak = tril_-1(dX V^T), dArb = tril_0(dY Z^T),
-        // dArk = tril_0(dY V^T) ([t][s], contracted over the value rows) and
-        // leaves it in row layout for the others -------------------------------------
+        // ---- the L x L adjoints: wave p forms tiles p, p + N/16, .. (one each at
+        // N = 64, two at N = 32) of dAab = tril_-1(dX Z^T), dAak = tril_-1(dX V^T),
+        // dArb = tril_0(dY Z^T), dArk = tril_0(dY V^T) ([t][s], contracted over
+        // the value rows) and leaves them in row layout for the others -----------------
         // (a = b = 0: dX = Z = 0, so only dArk, tile 3, is formed.)
-        if (kAB || wp == 3) {
-            const bool dyrow = (wp & 2) != 0, vcol = (wp & 1) != 0;
+#pragma unroll
+        for (int i = 0; i < 4 / kP; ++i) {
+          const int tp = wp + kP * i;
+          if (kAB || tp == 3) {
+            const bool dyrow = (tp & 2) != 0, vcol = (tp & 1) != 0;
             f32x4 At_s = zero4();
 #pragma unroll
-            for (int k2 = 0; k2 < 2; ++k2)
+            for (int k2 = 0; k2 < K2; ++k2)
                 At_s = mfma32(dyrow ? dYr[k2] : dXr[k2], vcol ? Vr[k2] : Zr[k2], At_s);
             // bf16 bits of the four values, taken from the packed words with
             // integer shifts (a bit_cast of a single element of a bf16 vector
@@ -813,13 +852,14 @@ __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
             for (int q = 0; q < 4; ++q) {
                 const int t = 4 * g + q, s_ = l16;   // accumulator layout: [t][s] = [4g+q][l16]
                 const bool keep = dyrow ? s_ <= t : s_ < t;
-                sm.adj[wp][t][s_] = (bf16_t)(keep ? bits[q] : 0u);
+                sm.adj[tp][t][s_] = (bf16_t)(keep ? bits[q] : 0u);
             }
+          }
         }
         // ---- the contractions over value rows that involve this wave's columns ------
         f32x4 dAt = zero4(), dRt = zero4(), dBb = zero4(), dKb = zero4();
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
+        for (int k2 = 0; k2 < K2; ++k2) {
             if (kAB) dAt = mfma32(dXr[k2], S0c[k2], dAt);     // dX S0
             dRt = mfma32(dYr[k2], S0c[k2], dRt);              // dY S0
             if (kAB) dBb = mfma32(Zr[k2], dSc[k2], dBb);      // Z dS
@@ -848,7 +888,7 @@ __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
         // ---- sum_i dS[i][col] S0[i][col] over this lane's 16 value rows -----------
         float cs = 0.f;
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
+        for (int k2 = 0; k2 < K2; ++k2) {
             const bf16x2_v* ds2 = reinterpret_cast<const bf16x2_v*>(&dSc[k2]);
             const bf16x2_v* s02 = reinterpret_cast<const bf16x2_v*>(&S0c[k2]);
 #pragma unroll
@@ -924,15 +964,15 @@ __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
         *reinterpret_cast<bf16x4*>(&sm.rows[h][4][l16][j0]) = swap_layout(cvt4(o_db), ident);
         __syncthreads();
         {
-            // Three 16-byte stores per thread: waves 0, 1 write dr, dk, db and
-            // waves 2, 3 dw, da (and nothing), each through a resource holding
-            // this chunk's rows of the head.
-            const int row = (tid >> 3) & 15, piece = tid & 7;
-            const bool lo_w = wp < 2;
+            // Three 16-byte stores per thread: the first half of the waves write
+            // dr, dk, db and the second dw, da (and nothing), each through a
+            // resource holding this chunk's rows of the head.
+            const int row = (tid / (kN / 8)) & 15, piece = tid & (kN / 8 - 1);
+            const bool lo_w = wp < kP / 2;
             // (a scalar: the clamp would otherwise land in a vector register, and
             // a resource built from one needs a loop over its distinct values)
             const int rows_in = __builtin_amdgcn_readfirstlane(max(0, min(kL, T - t0)));
-            const size_t base = tok_off(bb, t0, hh, T, H);
+            const size_t base = tok_off<N>(bb, t0, hh, T, H);
             const int voff = row * (H * kN * 2) + 16 * piece;
             typedef unsigned int su4 __attribute__((ext_vector_type(4)));
             // dst: never null (a stand-in where the output is absent); `on`: a
@@ -961,8 +1001,10 @@ __global__ __launch_bounds__(kP2Threads) void bwd_keys_kernel(
 
 }  // namespace
 
-hipError_t launch_bwd(const BwdArgs& p, int chunk_len, int stages, hipStream_t stream) {
-    if (chunk_len != kL || !p.bf16) return hipErrorInvalidValue;
+namespace {
+
+template <int N>
+hipError_t launch_bwd_n(const BwdArgs& p, int stages, hipStream_t stream) {
     const bf16_t* r = static_cast<const bf16_t*>(p.r);
     const bf16_t* w = static_cast<const bf16_t*>(p.w);
     const bf16_t* k = static_cast<const bf16_t*>(p.k);
@@ -971,8 +1013,8 @@ hipError_t launch_bwd(const BwdArgs& p, int chunk_len, int stages, hipStream_t s
     const bf16_t* b = static_cast<const bf16_t*>(p.b);
     const bf16_t* dy = static_cast<const bf16_t*>(p.dy);
     if (stages & BWD_CHAIN) {
-        auto chain = a ? bwd_chain_kernel<true> : bwd_chain_kernel<false>;
-        chain<<<dim3(p.B * p.H), dim3(kP1Threads), 0, stream>>>(
+        auto chain = a ? bwd_chain_kernel<N, true> : bwd_chain_kernel<N, false>;
+        chain<<<dim3(p.B * p.H), dim3(kP1Threads<N>), 0, stream>>>(
             p.T, p.H, r, w, k, a, b, dy, p.dsT, static_cast<bf16_t*>(p.dv), p.ds0,
             static_cast<bf16_t*>(p.workX), static_cast<bf16_t*>(p.workS), p.counter);
         const hipError_t e = hipGetLastError();
@@ -982,14 +1024,25 @@ hipError_t launch_bwd(const BwdArgs& p, int chunk_len, int stages, hipStream_t s
     const int nch = (p.T + kL - 1) / kL;
     const int nblk = (nch + 1) / 2;
     const int nblocks = p.B * p.H * nblk;
-    const int grid = nblocks < kP2Grid ? nblocks : kP2Grid;
-    auto keys = a ? bwd_keys_kernel<true> : bwd_keys_kernel<false>;
-    keys<<<dim3(grid), dim3(kP2Threads), 0, stream>>>(
+    const int grid = nblocks < kP2Grid<N> ? nblocks : kP2Grid<N>;
+    auto keys = a ? bwd_keys_kernel<N, true> : bwd_keys_kernel<N, false>;
+    keys<<<dim3(grid), dim3(kP2Threads<N>), 0, stream>>>(
         p.T, p.H, nch, nblk, nblocks, r, w, k, v, a, b, dy, static_cast<const bf16_t*>(p.tapeZ),
         static_cast<const bf16_t*>(p.tapeS), static_cast<const bf16_t*>(p.workX),
         static_cast<const bf16_t*>(p.workS), static_cast<bf16_t*>(p.dr), static_cast<bf16_t*>(p.dw),
         static_cast<bf16_t*>(p.dk), static_cast<bf16_t*>(p.da), static_cast<bf16_t*>(p.db), p.counter);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdArgs& p, int chunk_len, int stages, hipStream_t stream) {
+    if (chunk_len != kL || !p.bf16) return hipErrorInvalidValue;
+    switch (p.N) {
+        case 32: return launch_bwd_n<32>(p, stages, stream);
+        case 64: return launch_bwd_n<64>(p, stages, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace wkv7

@@ -32,6 +32,7 @@ struct BwdArgs {
     void* workX;       // dX [B][T][H][N] bf16
     void* workS;       // adjoint leaving every 32-token block [B][H][nblk][N][N] bf16
     int* counter;      // two ints: the per-key pass's block queue (reset by both passes)
+    int N = 64;        // head size: 32 or 64
 };
 
 // The sequential reverse pass: one workgroup per head over its fp32 checkpoints.

@@ -59,7 +59,10 @@ def test_tape_and_workspace_sizes(L):
     assert wk.tape_bytes(wk.make_desc(1, 64, 1, 32, wk.WKV7_F32, 0)) == 64 * 32 * 2 + 2 * 32 * 32 * 2
     assert wk.workspace_bytes(wk.make_desc(1, 64, 1, 32, wk.WKV7_F32, 0), False) == 4 * 32 * 32 * 4
     assert wk.workspace_bytes(wk.make_desc(1, 64, 1, 32, wk.WKV7_F32, 0), True) == 4 * 32 * 32 * 4
-    assert wk.workspace_bytes(wk.make_desc(1, 64, 1, 32, wk.WKV7_BF16, 16), True) == 0
+    # the chunked backward at N = 32: its own scratch (dX, block adjoints) and the queues
+    assert wk.workspace_bytes(wk.make_desc(1, 64, 1, 32, wk.WKV7_BF16, 16), True) == \
+        64 * 32 * 2 + 2 * 32 * 32 * 2 + 256
+    assert wk.workspace_bytes(wk.make_desc(1, 64, 1, 128, wk.WKV7_BF16, 16), True) == 0
 
 
 def test_ckpt_and_one_argument_workspace_sizes(L):
@@ -224,12 +227,12 @@ def test_backward_validation(L):
     big = wk.make_desc(1 << 14, 256, 1 << 14, 64, wk.WKV7_BF16, 16)
     assert L.wkv7_backward(ctypes.byref(big), *args, FAKE, *grads, None, FAKE, 1 << 40, None) == \
         wk.WKV7_ERR_UNSUPPORTED
-    # The chunked backward is bf16 at N = 64 (fp32 and other head sizes take
+    # The chunked backward is bf16 at N = 32 and 64 (fp32 and N = 128 take
     # chunk_len = 0, the sequential reverse pass).
     d32 = wk.make_desc(1, 8, 1, 64, wk.WKV7_F32, 16)
     assert L.wkv7_backward(ctypes.byref(d32), *args, FAKE, *grads, None, None, 0, None) == \
         wk.WKV7_ERR_UNSUPPORTED
-    for n in (32, 128):
+    for n in (48, 128):
         dn = wk.make_desc(1, 8, 1, n, wk.WKV7_BF16, 16)
         assert L.wkv7_backward(ctypes.byref(dn), *args, FAKE, *grads, None, FAKE, 1 << 30, None) == \
             wk.WKV7_ERR_UNSUPPORTED

@@ -163,3 +163,79 @@ def test_forward_epilogue_at_n32(wk):
     ref = oracle.epilogue(yr, inp.r, inp.k, inp.v, e.g, e.u, e.gamma, e.beta, eps=1e-5, mode=1)
     assert_close(to_np(out), ref, "bf16", "N=32 forward + step")
     assert_close(to_np(sT), sr, "bf16", "N=32 forward + step sT")
+
+
+# ---------------------------------------------------------------------------
+# The chunked backward at N = 32
+# ---------------------------------------------------------------------------
+
+NAMES = ("dr", "dw", "dk", "dv", "da", "db", "ds0")
+
+
+def _grads(wk, inp, dsT=None, use_tape=True, decay_only=False, aux=False, chunk_len=16):
+    import torch
+    dev = [to_dev(x, "bf16") for x in inp.tensors()]
+    if decay_only:
+        dev[4] = dev[5] = None
+    s0 = to_dev(inp.s0, "fp32") if inp.s0 is not None else None
+    dy = to_dev(inp.dy, "bf16")
+    dsT_d = to_dev(dsT, "fp32") if dsT is not None else None
+    tape = None
+    if use_tape and chunk_len == 16:
+        _, _, tape = wk.forward(*dev, s0, chunk_len=16, want_state=False, want_tape=True)
+    g = wk.backward(*dev, dy, s0, dsT_d, tape, chunk_len=chunk_len,
+                    aux_stream=torch.cuda.Stream() if aux else None)
+    torch.cuda.synchronize()
+    return [None if x is None else to_np(x) for x in g]
+
+
+def _ref_grads(inp, dsT=None, decay_only=False):
+    r, w, k, v, a, b = inp.tensors()
+    if decay_only:
+        a, b = np.zeros_like(a), np.zeros_like(b)
+    return oracle.backward(r, w, k, v, a, b, inp.s0, inp.dy, dsT)
+
+
+def _check(got, ref, what, decay_only=False):
+    for name, x, rr in zip(NAMES, got, ref):
+        if decay_only and name in ("da", "db"):
+            assert x is None
+            continue
+        assert_close(x, rr, "bf16", f"{what} {name}")
+
+
+@pytest.mark.parametrize("T", [1, 16, 33, 64, 100, 200])
+def test_backward_ragged(wk, T):
+    inp = synth.generate(2, T, 2, N, dtype="bf16", seed=800 + T, random_s0=True, backward=True)
+    dsT = (0.1 * np.random.default_rng(T).standard_normal(inp.s0.shape)).astype(np.float32)
+    _check(_grads(wk, inp, dsT), _ref_grads(inp, dsT), f"N=32 T={T}")
+
+
+def test_backward_without_tape_and_decay_only(wk):
+    inp = synth.generate(2, 150, 3, N, dtype="bf16", seed=810, random_s0=True, backward=True)
+    _check(_grads(wk, inp, use_tape=False), _ref_grads(inp), "N=32 no tape")
+    _check(_grads(wk, inp, decay_only=True), _ref_grads(inp, decay_only=True), "N=32 a=b=0", True)
+
+
+def test_backward_matches_sequential_reverse_pass(wk):
+    inp = synth.generate(2, 200, 3, N, dtype="bf16", seed=811, random_s0=True, backward=True)
+    chunked = _grads(wk, inp)
+    seq = _grads(wk, inp, chunk_len=0)
+    for name, x, y in zip(NAMES, chunked, seq):
+        assert_close(x, y, "bf16", f"N=32 chunked vs sequential {name}")
+
+
+def test_backward_many_heads_two_streams(wk):
+    """B=16, T=512, H=40 (640 heads, more than two per compute unit): the
+    two-stream backward splits the batch rows; sampled heads against the oracle."""
+    import torch
+    inp = synth.generate(16, 512, 40, N, dtype="bf16", seed=812, random_s0=True, backward=True)
+    got = _grads(wk, inp, aux=True)
+    pairs = [(0, 0), (5, 17), (11, 39), (15, 3)]
+    sel = [oracle.select_heads(x, pairs) for x in inp.tensors()]
+    ref = oracle.backward(*sel, oracle.select_heads(inp.s0, pairs, state=True),
+                          oracle.select_heads(inp.dy, pairs))
+    for name, x, rr in zip(NAMES, got, ref):
+        xs = oracle.select_heads(x, pairs, state=(name == "ds0"))
+        assert_close(xs, rr, "bf16", f"N=32 640 heads {name}")
+        assert np.all(np.isfinite(x))
