@@ -462,6 +462,10 @@ __global__ __launch_bounds__(kP1Threads<N>, N == 32 ? 2 : 1) void bwd_chain_kern
         // and only stores on the consumer side; with both kinds in one loop it
         // must treat the memory counter as unordered and drain it completely.
         if (producer) {
+            // The producers set each interval's length: they issue at the inverse
+            // waves' priority (below the state chain), which measured about 2 %
+            // faster than the default at the 2.9B shape.
+            __builtin_amdgcn_s_setprio(2);
             Raw rb0, rb1, rb2;
             load_raw(chunk_of(0), rb0);
             load_raw(chunk_of(1), rb1);

@@ -691,6 +691,10 @@ __global__ __launch_bounds__(kEpi ? FwdShape<N>::threads_epi : FwdShape<N>::thre
         // completely, which serialises the producers' read-ahead and makes the
         // consumers wait for their own previous stores.
         if (producer) {
+            // The producers set each interval's length: they issue at the inverse
+            // waves' priority (below the state chain), which measured about 2 %
+            // faster than the default at the 2.9B shape.
+            __builtin_amdgcn_s_setprio(2);
             // Register ring: the raw loads of chunk c live in ring slot c % 3
             // until stashed (three named variables, never an array, so that the
             // ring is neither promoted to LDS nor to scratch).
