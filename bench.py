@@ -39,8 +39,8 @@ GRAD_BYTES_PER_TH = 12 * 128        # gradient pass: r, w, k, v, a, b, dy in, dr
 STATE_BYTES = 64 * 64 * 4           # one fp32 state
 # Template arguments of each kernel's instance for the general recurrence in one
 # launch (not the time-segmented or the a = b = 0 instances).
-PLAIN_INSTANCE = {"chunk_fwd_kernel": "<false, true, false, false>", "bwd_chain_kernel": "<true>",
-                  "bwd_keys_kernel": "<true>"}
+PLAIN_INSTANCE = {"chunk_fwd_kernel": "<64, false, true, false, false>", "bwd_chain_kernel": "<64, true>",
+                  "bwd_keys_kernel": "<64, true>"}
 KERNELS = {   # kernel symbol -> (entry point that launches it alone, source, bytes per token-head)
     "chunk_fwd_kernel": ("wkv7_forward", "wkv7_chunk_fwd.hip", FWD_BYTES_PER_TH),
     "bwd_chain_kernel": ("wkv7_backward_adjoint", "wkv7_bwd.hip", ADJ_BYTES_PER_TH),
