@@ -44,12 +44,15 @@ __device__ __forceinline__ f32x4 mul_row_lanes4(float f, f32x4 x) {
     return o;
 }
 
-// Accumulator chains never mix shapes.  On gfx950 a 16x16x16 MFMA whose
-// accumulator input is the result of a 16x16x32 MFMA (or the reverse) reads
-// stale accumulator registers unless 5 wait states separate the two, and the
-// compiler does not insert them (same-shape chains forward correctly).  Partial
-// sums of different shapes are therefore added with vector ALU instructions
-// (add4); the compiler does protect a vector ALU read of an MFMA result.
+// Accumulator chains never mix shapes.  The CDNA3/CDNA4 ISA reference guides'
+// table of required independent instructions between dependent matrix (XDL)
+// operations lets an MFMA take the previous MFMA's result as its accumulator
+// input (SrcC) back to back only when both are the same instruction; a SrcC
+// written by an MFMA of another shape needs wait states that depend on the
+// writer's pass count.  Rather than rely on those being inserted, partial sums
+// of different shapes are added with vector ALU instructions (add4), whose read
+// of an MFMA result the compiler does protect; tests/test_mfma_chains.py checks
+// the built kernels for mixed-shape chains.
 __device__ __forceinline__ f32x4 add4(f32x4 a, f32x4 b) { return a + b; }
 
 // An MFMA runs across the whole wave: with part of the EXEC mask off it does

@@ -1,10 +1,11 @@
 """Static checks of the compiled kernels' MFMA use (hipcc, no GPU needed).
 
-1. No MFMA accumulator chain mixes shapes.  On gfx950 a
-   v_mfma_f32_16x16x16_bf16 whose accumulator input (SrcC) was written by a
-   v_mfma_f32_16x16x32_bf16 (or the reverse) needs 5 wait states that the
-   compiler does not insert; the kernels keep every chain within one shape and
-   join partial sums on the vector ALU.
+1. No MFMA accumulator chain mixes shapes.  The CDNA3/CDNA4 ISA guides allow
+   an MFMA to take the previous MFMA's result as its accumulator input (SrcC)
+   back to back only when both are the same instruction; a SrcC written by an
+   MFMA of another shape (v_mfma_f32_16x16x16_bf16 after
+   v_mfma_f32_16x16x32_bf16, or the reverse) needs wait states.  The kernels
+   keep every chain within one shape and join partial sums on the vector ALU.
 2. No MFMA runs under a divergent branch (between an s_and_saveexec and the
    s_or_b64 exec that closes it): with part of EXEC off the product is wrong.
 
