@@ -180,7 +180,7 @@ int wkv7_forward_ckpt(const wkv7_desc *desc, const void *r, const void *w, const
  *   segments   0: the library chooses from the device's compute-unit count
  *                 (B*H at most a third of it: every head by maps, below; more
  *                 heads than compute units: the heads of the last, partial
- *                 round by maps when they fill at most a third of it; the
+ *                 round by maps when they fill at most a fifth of it; the
  *                 scan: every head by maps when B*H*N/16 workgroups fill at
  *                 most half of it, at N = 128 in at most 4 segments; else, or
  *                 when T is too short for segments of 128 tokens, no split);

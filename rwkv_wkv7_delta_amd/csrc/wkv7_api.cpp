@@ -132,8 +132,12 @@ SplitPlan plan_split(const wkv7_desc* d, int segments, int ncu) {
     } else if (segments == 0) {
         // Automatic: split every head when the heads fill at most a third of
         // the device; else, with more heads than compute units, split the heads
-        // of the last, partial round when they are few enough (both by maps,
-        // with as many segments as the device holds).
+        // of the last, partial round when they fill at most a fifth of it (both
+        // by maps, with as many segments as the device holds).  On 256 compute
+        // units (B = 8, T = 4096) the partial-round split took 0.341 against
+        // 0.453 ms unsplit at 272 heads and 0.373 against 0.463 ms at 288, but
+        // 0.462 against 0.456 ms at 320: there the second round's 64 heads start
+        // as soon as the first round's faster heads finish.
         // The scan runs N/16 workgroups per head and no partial rounds: it
         // splits every head when those fill at most half of the device (at
         // 48 heads, 3/4 of it, segments measured no faster; at 320 heads
@@ -147,6 +151,7 @@ SplitPlan plan_split(const wkv7_desc* d, int segments, int ncu) {
         } else if (nbh > ncu) {
             part = nbh % ncu;
             from = nbh - part;
+            if (5 * part > ncu) return none;
         }
         if (part == 0 || 3 * part > ncu) return none;
         nseg = (ncu / part + 3) / 2;

@@ -123,7 +123,7 @@ __global__ __launch_bounds__(kP1Threads<N>, N == 32 ? 2 : 1) void bwd_chain_kern
     using P1Slot = wkv7::P1Slot<N>;
     using P1SlotBK = wkv7::P1SlotBK<N>;
     __shared__ P1Smem<N> sm;
-    const int bh = blockIdx.x;
+    const int bh = spread_heads(blockIdx.x, gridDim.x);
     const int bb = bh / H, hh = bh % H;
     const int tid = threadIdx.x;
     // Roles split by wave (the tests are uniform within a wave).  They are left

@@ -235,6 +235,19 @@ struct Work {
 // zero with the real v, P from the identity with v = 0 (the recurrence is
 // affine in the state: S <- S M_t + v_t k_t^T).  Pass 1 re-runs segments
 // 1 .. nseg-1 from their entry states (composed in between), with outputs.
+// The head that workgroup `blk` of `n` one-head workgroups takes.  The device
+// hands workgroups to its eight XCDs in turn (workgroup u to XCD u mod 8), and
+// heads whose index is the same mod 8 sit at the same place of every token row,
+// which under the full round's memory traffic can make one such group slower
+// than the rest (at H = 40 the heads = 3 mod 8 by about a fifth).  Rotating the
+// heads of every group of eight workgroups by the group's index gives each XCD
+// every residue, so no XCD holds all the slow heads and the work queued behind
+// them (the next round, the split heads' runs) starts on time everywhere.
+__device__ __forceinline__ int spread_heads(int blk, int n) {
+    const int q = blk >> 3;
+    return 8 * q + 8 > n ? blk : 8 * q + ((blk + q) & 7);
+}
+
 // Per split head the workspace holds 3 nseg states: entry states (slot s),
 // Hm (nseg + s) and P (2 nseg + s).
 template <int N>
@@ -243,9 +256,9 @@ __device__ __forceinline__ Work work_of(int blk, int pass, int T, const float* s
     constexpr size_t NN = (size_t)N * N;
     Work wk{0, 0, T, nullptr, nullptr, false, false, true};
     if (pass == 0 && blk < split_from) {
-        wk.bh = blk;
-        wk.init = s0 ? s0 + (size_t)blk * NN : nullptr;
-        wk.fin = sT ? sT + (size_t)blk * NN : nullptr;
+        wk.bh = spread_heads(blk, split_from);
+        wk.init = s0 ? s0 + (size_t)wk.bh * NN : nullptr;
+        wk.fin = sT ? sT + (size_t)wk.bh * NN : nullptr;
         return wk;
     }
     const int j = pass == 0 ? blk - split_from : blk;

@@ -155,6 +155,23 @@ def test_split_fwd_0_19b_automatic(wk):
     assert_close(sT, sr, "bf16", "auto split 0.19b sT")
 
 
+def test_split_plan_thresholds(wk):
+    """The automatic plan's thresholds on this device (no launch): every head
+    split when the heads fill at most a third of the compute units, the last
+    partial round split when it fills at most a fifth of them, else none."""
+    import torch
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+
+    def plan(H):
+        return wk.split_workspace_bytes(wk.make_desc(1, 640, H, 64, wk.WKV7_BF16, 16), 0)
+
+    assert plan(ncu // 3) > 0
+    assert plan(ncu // 2) == 0
+    assert plan(ncu + ncu // 8) > 0
+    assert plan(ncu + ncu // 4) == 0
+    assert plan(2 * ncu) == 0
+
+
 def test_split_fwd_partial_last_round(wk):
     """More heads than compute units: the automatic plan splits only the heads
     of the last, partial round.  Sampled heads on both sides of the boundary."""
@@ -194,18 +211,20 @@ def test_sequential_segments_2_9b_shape_sampled(wk):
     assert_close(sn, to_np(sT1), "bf16", "2.9b sequential vs unsplit sT")
 
 
-def test_split_fwd_2_9b_shape_sampled(wk):
-    """B=8, T=4096, H=40 (2.9B-model shape) with the automatic plan (the heads
-    past the first full round are split) and the tape: sampled heads against
-    the oracle, the whole output and tape against the unsplit forward's."""
+@pytest.mark.parametrize("H", [36, 40])
+def test_split_fwd_2_9b_shape_sampled(wk, H):
+    """B=8, T=4096 with the automatic plan and the tape: H=40 (the 2.9B-model
+    shape, 320 heads, left whole on 256 compute units) and H=36 (288 heads, whose
+    32 past the first full round are split there).  Sampled heads against the
+    oracle, the whole output and tape against the unsplit forward's."""
     import torch
-    B, T, H = 8, 4096, 40
+    B, T = 8, 4096
     inp = synth.generate(B, T, H, 64, dtype="bf16", seed=36)
     dev = [to_dev(x, "bf16") for x in inp.tensors()]
     y, sT, tape = wk.forward(*dev, None, chunk_len=16, want_tape=True, segments=0)
     y1, sT1, tape1 = wk.forward(*dev, None, chunk_len=16, want_tape=True)
     torch.cuda.synchronize()
-    pairs = [(0, 0), (6, 15), (6, 16), (7, 39), (7, 2)]
+    pairs = [(0, 0), (6, 15), (6, 16), (7, H - 1), (7, 2), (7, 4)]
     sel = [oracle.select_heads(x, pairs) for x in inp.tensors()]
     yr, sr = oracle.forward(*sel, None)
     yn, sn = to_np(y), to_np(sT)
