@@ -417,8 +417,8 @@ def main():
              stream.cuda_stream)
 
     # The step's forward: wkv7_forward_split with the library's own plan (with
-    # more heads than compute units, the heads of the last, partial round run
-    # split in time).
+    # more heads than compute units, a small last, partial round of heads runs
+    # split in time; 320 heads on 256 compute units run whole).
     sws_bytes = wk.split_workspace_bytes(desc, 0)
     sws = torch.empty(max(sws_bytes // 4, 4), device=dev, dtype=torch.float32)
 

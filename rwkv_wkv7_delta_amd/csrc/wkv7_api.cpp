@@ -83,8 +83,9 @@ int device_cus() {
 //     instead of whole heads.  Only on request: at 320 heads on 256 compute
 //     units it measured 476 us (n = 2) to 499 us (n = 4) for the 2.9B-shape
 //     forward with tape, against 465 us for maps on the last, partial round of
-//     heads (segments often wait for their predecessor from the round just
-//     before, and every segment pays the pipeline fill).
+//     heads and 456 us for no split once the heads were spread over the XCDs
+//     (every segment pays the pipeline fill, and heads that no longer step
+//     through the tokens together read their token rows at different times).
 constexpr int kMaxSegments = 16;
 constexpr int kMinSegmentTokens = 128;
 
