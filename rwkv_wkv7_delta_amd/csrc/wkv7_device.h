@@ -227,14 +227,6 @@ struct Work {
     bool ident, vzero, outs;
 };
 
-// blockIdx -> Work under a segment plan (FwdSplit): heads below split_from run
-// whole in pass 0; every later head runs in nseg segments of seg_len tokens.
-// Pass 0 also runs each split head's segment 0 (with outputs; its final state
-// is the entry state of segment 1) and, for segments 1 .. nseg-2, the two runs
-// whose final states give the segment's affine map S_out = S_in P + Hm: Hm from
-// zero with the real v, P from the identity with v = 0 (the recurrence is
-// affine in the state: S <- S M_t + v_t k_t^T).  Pass 1 re-runs segments
-// 1 .. nseg-1 from their entry states (composed in between), with outputs.
 // The head that workgroup `blk` of `n` one-head workgroups takes.  The device
 // hands workgroups to its eight XCDs in turn (workgroup u to XCD u mod 8), and
 // heads whose index is the same mod 8 sit at the same place of every token row,
@@ -248,6 +240,14 @@ __device__ __forceinline__ int spread_heads(int blk, int n) {
     return 8 * q + 8 > n ? blk : 8 * q + ((blk + q) & 7);
 }
 
+// blockIdx -> Work under a segment plan (FwdSplit): heads below split_from run
+// whole in pass 0; every later head runs in nseg segments of seg_len tokens.
+// Pass 0 also runs each split head's segment 0 (with outputs; its final state
+// is the entry state of segment 1) and, for segments 1 .. nseg-2, the two runs
+// whose final states give the segment's affine map S_out = S_in P + Hm: Hm from
+// zero with the real v, P from the identity with v = 0 (the recurrence is
+// affine in the state: S <- S M_t + v_t k_t^T).  Pass 1 re-runs segments
+// 1 .. nseg-1 from their entry states (composed in between), with outputs.
 // Per split head the workspace holds 3 nseg states: entry states (slot s),
 // Hm (nseg + s) and P (2 nseg + s).
 template <int N>
