@@ -218,6 +218,21 @@ int wkv7_forward_ckpt(const wkv7_desc *desc, const void *r, const void *w, const
  * on the same one.
  */
 size_t wkv7_forward_split_workspace_bytes(const wkv7_desc *desc, int32_t segments);
+
+/* The plan wkv7_forward_split would run for `segments` on the current device,
+ * returned without running it (for logs and tuning): heads [split_from, B*H)
+ * run in nseg segments of seg_len tokens (the last takes the rest), by maps or
+ * sequentially; with no split, split_from = B*H, nseg = 1 and seg_len = T.
+ * Returns WKV7_OK, or the status wkv7_forward_split returns for that desc and
+ * segments (plan NULL: WKV7_ERR_INVALID_ARG). */
+enum { WKV7_SPLIT_NONE = 0, WKV7_SPLIT_MAPS = 1, WKV7_SPLIT_SEQUENTIAL = 2 };
+typedef struct {
+    int32_t kind;         /* WKV7_SPLIT_* */
+    int32_t split_from;
+    int32_t nseg;
+    int32_t seg_len;
+} wkv7_split_plan;
+int wkv7_forward_split_plan(const wkv7_desc *desc, int32_t segments, wkv7_split_plan *plan);
 int wkv7_forward_split(const wkv7_desc *desc, const void *r, const void *w, const void *k,
                        const void *v, const void *a, const void *b, const float *s0, void *y,
                        float *sT, void *tape, int32_t segments, void *workspace,

@@ -38,7 +38,8 @@ TAPE_BLOCK = 32
 
 EXPORTED = ("wkv7_abi_version", "wkv7_status_string", "wkv7_tape_bytes", "wkv7_ckpt_bytes",
             "wkv7_workspace_bytes", "wkv7_backward_workspace_bytes", "wkv7_forward",
-            "wkv7_forward_ckpt", "wkv7_forward_split_workspace_bytes", "wkv7_forward_split",
+            "wkv7_forward_ckpt", "wkv7_forward_split_workspace_bytes", "wkv7_forward_split_plan",
+            "wkv7_forward_split",
             "wkv7_forward_split_static",
             "wkv7_backward", "wkv7_backward_ckpt", "wkv7_backward_adjoint", "wkv7_backward_gradients",
             "wkv7_backward_overlapped", "wkv7_decode_step", "wkv7_epilogue",
@@ -55,6 +56,14 @@ class WKV7Error(RuntimeError):
 class EpilogueParams(ctypes.Structure):
     _fields_ = [("u", ctypes.c_void_p), ("gamma", ctypes.c_void_p), ("beta", ctypes.c_void_p),
                 ("eps", ctypes.c_float), ("mode", ctypes.c_int32)]
+
+
+class SplitPlan(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("split_from", ctypes.c_int32), ("nseg", ctypes.c_int32),
+                ("seg_len", ctypes.c_int32)]
+
+
+WKV7_SPLIT_NONE, WKV7_SPLIT_MAPS, WKV7_SPLIT_SEQUENTIAL = 0, 1, 2
 
 
 class Desc(ctypes.Structure):
@@ -96,6 +105,8 @@ def lib():
         L.wkv7_forward_ckpt.restype = ctypes.c_int
         L.wkv7_forward_split_workspace_bytes.argtypes = [D, I]
         L.wkv7_forward_split_workspace_bytes.restype = Z
+        L.wkv7_forward_split_plan.argtypes = [D, I, ctypes.POINTER(SplitPlan)]
+        L.wkv7_forward_split_plan.restype = ctypes.c_int
         L.wkv7_forward_split.argtypes = [D] + [P] * 6 + [P, P, P, P, I, P, Z, P]
         L.wkv7_forward_split.restype = ctypes.c_int
         L.wkv7_forward_split_static.argtypes = [D] + [P] * 6 + [P, P, P, P, I, P]
@@ -188,6 +199,15 @@ def workspace_bytes(desc: Desc, with_tape: bool = True) -> int:
 
 def split_workspace_bytes(desc: Desc, segments: int = 0) -> int:
     return int(lib().wkv7_forward_split_workspace_bytes(ctypes.byref(desc), segments))
+
+
+def split_plan(desc: Desc, segments: int = 0) -> SplitPlan:
+    """The plan wkv7_forward_split would run (kind, split_from, nseg, seg_len)."""
+    plan = SplitPlan()
+    st = lib().wkv7_forward_split_plan(ctypes.byref(desc), segments, ctypes.byref(plan))
+    if st != WKV7_OK:
+        raise WKV7Error(st, "wkv7_forward_split_plan")
+    return plan
 
 
 def split_tape(tape, B: int, T: int, H: int, N: int = HEAD_SIZE):

@@ -277,6 +277,19 @@ size_t wkv7_forward_split_workspace_bytes(const wkv7_desc* desc, int32_t segment
     return split_bytes(desc, plan_split(desc, segments, segments == 0 ? device_cus() : 0));
 }
 
+int wkv7_forward_split_plan(const wkv7_desc* desc, int32_t segments, wkv7_split_plan* plan) {
+    const int st = check_desc(desc);
+    if (st != WKV7_OK) return st;
+    if (plan == nullptr || segments < -kMaxSegments) return WKV7_ERR_INVALID_ARG;
+    if (desc->chunk_len == 0 && segments < -1) return WKV7_ERR_UNSUPPORTED;
+    const SplitPlan p = plan_split(desc, segments, segments == 0 ? device_cus() : 0);
+    plan->kind = p.nseg < 2 ? WKV7_SPLIT_NONE : p.mode == 1 ? WKV7_SPLIT_SEQUENTIAL : WKV7_SPLIT_MAPS;
+    plan->split_from = p.split_from;
+    plan->nseg = p.nseg;
+    plan->seg_len = p.seg_len;
+    return WKV7_OK;
+}
+
 }  // extern "C"
 
 namespace {

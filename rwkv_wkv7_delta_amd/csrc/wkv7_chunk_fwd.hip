@@ -16,7 +16,7 @@
 //   Y   = Rt S0^T + Arb Z + Ark V    (row t of Y is y_t)
 //   S_L^T = diag(G_L) S0^T + Kb^T V + Bb^T Z
 //
-// Mapping to gfx950: one workgroup of 9 waves per (b, h), split by role.
+// Mapping to gfx950: one workgroup of 10 waves per (b, h), split by role.
 //   Producer waves p = 0..3 build each chunk's state-independent factors:
 //     E   decay products and scaled vectors for key columns 16p..16p+15, in
 //         row layout (a lane per token, four columns each: 8-byte LDS

@@ -169,6 +169,28 @@ def test_split_workspace_sizes(L):
     assert wk.split_workspace_bytes(wk.make_desc(1, 1024, 2, 128, wk.WKV7_F32, 0), 4) == 2 * 3 * 4 * st * 4
 
 
+def test_split_plan_query(L):
+    """The plan query for explicit segment counts (no device needed) and its
+    errors, which are those of wkv7_forward_split."""
+    d = wk.make_desc(4, 1024, 12, 64, wk.WKV7_BF16, 16)
+    p = wk.split_plan(d, 4)
+    assert (p.kind, p.split_from, p.nseg, p.seg_len) == (wk.WKV7_SPLIT_MAPS, 0, 4, 256)
+    p = wk.split_plan(d, 1)
+    assert (p.kind, p.split_from, p.nseg, p.seg_len) == (wk.WKV7_SPLIT_NONE, 48, 1, 1024)
+    p = wk.split_plan(d, -3)   # 1024 / 3 rounded up to whole 32-token blocks
+    assert (p.kind, p.split_from, p.nseg, p.seg_len) == (wk.WKV7_SPLIT_SEQUENTIAL, 0, 3, 352)
+    p = wk.split_plan(wk.make_desc(1, 32, 2, 64, wk.WKV7_BF16, 16), 4)   # one block: no split
+    assert (p.kind, p.split_from, p.nseg) == (wk.WKV7_SPLIT_NONE, 2, 1)
+    plan = wk.SplitPlan()
+    assert L.wkv7_forward_split_plan(ctypes.byref(d), 4, None) == wk.WKV7_ERR_INVALID_ARG
+    assert L.wkv7_forward_split_plan(ctypes.byref(d), -17, ctypes.byref(plan)) == wk.WKV7_ERR_INVALID_ARG
+    assert L.wkv7_forward_split_plan(None, 4, ctypes.byref(plan)) == wk.WKV7_ERR_INVALID_ARG
+    scan = wk.make_desc(1, 1024, 2, 64, wk.WKV7_BF16, 0)
+    assert L.wkv7_forward_split_plan(ctypes.byref(scan), -4, ctypes.byref(plan)) == wk.WKV7_ERR_UNSUPPORTED
+    bad = wk.make_desc(1, 64, 1, 48, wk.WKV7_BF16, 16)
+    assert L.wkv7_forward_split_plan(ctypes.byref(bad), 4, ctypes.byref(plan)) == wk.WKV7_ERR_UNSUPPORTED
+
+
 def test_split_forward_validation(L):
     d = wk.make_desc(1, 256, 1, 64, wk.WKV7_BF16, 16)
     f = L.wkv7_forward_split

@@ -158,18 +158,28 @@ def test_split_fwd_0_19b_automatic(wk):
 def test_split_plan_thresholds(wk):
     """The automatic plan's thresholds on this device (no launch): every head
     split when the heads fill at most a third of the compute units, the last
-    partial round split when it fills at most a fifth of them, else none."""
+    partial round split when it fills at most a fifth of them, else none; no
+    split when T is too short for two segments of 128 tokens."""
     import torch
     ncu = torch.cuda.get_device_properties(0).multi_processor_count
 
-    def plan(H):
-        return wk.split_workspace_bytes(wk.make_desc(1, 640, H, 64, wk.WKV7_BF16, 16), 0)
+    def plan(H, T=640):
+        d = wk.make_desc(1, T, H, 64, wk.WKV7_BF16, 16)
+        p = wk.split_plan(d, 0)
+        assert (wk.split_workspace_bytes(d, 0) > 0) == (p.kind == wk.WKV7_SPLIT_MAPS)
+        return p.kind, p.split_from
 
-    assert plan(ncu // 3) > 0
-    assert plan(ncu // 2) == 0
-    assert plan(ncu + ncu // 8) > 0
-    assert plan(ncu + ncu // 4) == 0
-    assert plan(2 * ncu) == 0
+    M, NO = wk.WKV7_SPLIT_MAPS, wk.WKV7_SPLIT_NONE
+    assert plan(ncu // 3) == (M, 0)
+    assert plan(ncu // 3 + 1) == (NO, ncu // 3 + 1)
+    assert plan(ncu) == (NO, ncu)
+    assert plan(ncu + ncu // 8) == (M, ncu)
+    assert plan(ncu + ncu // 5) == (M, ncu)
+    assert plan(ncu + ncu // 4) == (NO, ncu + ncu // 4)
+    assert plan(2 * ncu) == (NO, 2 * ncu)
+    assert plan(ncu // 4, T=160) == (NO, ncu // 4)
+    p = wk.split_plan(wk.make_desc(1, 640, ncu // 8, 64, wk.WKV7_BF16, 16), 0)
+    assert p.kind == M and p.nseg >= 2 and p.seg_len % 32 == 0 and (p.nseg - 1) * p.seg_len < 640
 
 
 def test_split_fwd_partial_last_round(wk):
