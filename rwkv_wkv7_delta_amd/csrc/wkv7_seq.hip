@@ -294,15 +294,21 @@ __global__ __launch_bounds__(256) void decode_kernel(
 // states stay in registers (earlier sub-stages re-run again for later ones),
 // then steps G backwards over them.  The per-key gradients are sums over rows:
 // within a wave by lane swaps, across waves through per-wave LDS slots summed
-// once per sub-stage (atomics on shared addresses serialised across waves)
-// into the stage's [16][5][N] sums, which are written out once per stage.
+// once per sub-stage (atomics on shared addresses serialised across waves),
+// and stored from there.
 template <int N> struct SeqBwdShape {
     // Four rows per 16-lane group: N/16 waves per head.
     static constexpr int RPL = 4;                 // rows per 16-lane group
     static constexpr int WAVES = N / (4 * RPL);
     static constexpr int C = N / 16;              // columns per lane
-    // Tokens per sub-stage, whose states a lane keeps (RPL * C floats each).
-    static constexpr int KS = 64 / (RPL * C) < kTB ? 64 / (RPL * C) : kTB;
+    // Tokens per sub-stage, whose states a lane keeps (RPL * C floats each):
+    // 8 at N = 32 and 64, 2 at N = 128 (72, 144 and 96 floats per lane; at
+    // N = 128 a fourth state spills past the 256 registers that two waves per
+    // SIMD leave each wave, and at N = 32 one sub-stage of 16 tokens measured
+    // slower than two of 8).  Each sub-stage re-runs the stage's forward from
+    // its checkpoint, so a 16-token stage costs 16 + KS (0 + 1 + .. + 16/KS - 1)
+    // forward steps: 24, 24 and 72.
+    static constexpr int KS = N == 128 ? 2 : 8;
 };
 
 template <typename Tin, int N, bool kAB>
@@ -318,9 +324,8 @@ __global__ __launch_bounds__(64 * SeqBwdShape<N>::WAVES) void seq_bwd_kernel(
     constexpr int NG = kAB ? 5 : 3;   // per-key gradients: dr, dw, dk (, da, db)
     enum { VR, VW, VK, VV, VA, VB, VDY };
     __shared__ __align__(16) float sm[7][kTB][N];     // r, w, k, v, a, b, dy of the stage
-    __shared__ __align__(16) float acc[kTB][5][N];    // dr, dw, dk, da, db of the stage
-    __shared__ __align__(16) float part[WAVES][KS][5][N];   // per-wave sums of a sub-stage
-    __shared__ float sdv[kTB][N + 1];                 // column N: where surplus lanes write
+    __shared__ __align__(16) float part[WAVES][KS][NG][N];   // per-wave sums of a sub-stage
+    __shared__ float sdv[KS][N + 1];                  // column N: where surplus lanes write
 
     const int bh = blockIdx.x;
     const int bb = bh / H, hh = bh % H;
@@ -364,7 +369,8 @@ __global__ __launch_bounds__(64 * SeqBwdShape<N>::WAVES) void seq_bwd_kernel(
             }
         }
     };
-    // Sums a per-lane partial over the wave's rows into its slot part[wave][kk][q].
+    // Sums a per-lane partial over the wave's rows into its slot part[wave][kk][q]
+    // (q: 0 dr, 1 dw, 2 dk, 3 da, 4 db).
     // Every group then holds every column's sum; group g writes columns c = g
     // (mod 4) of its lanes (a select, not a branch: no basic block ends here).
     auto add_rows = [&](int kk, int q, const float (&p)[C]) __attribute__((always_inline)) {
@@ -429,7 +435,7 @@ __global__ __launch_bounds__(64 * SeqBwdShape<N>::WAVES) void seq_bwd_kernel(
             const float dvi = row16_sum(dot_cols(G[rr], V));
             dv_lane = cq == rr ? dvi : dv_lane;
         }
-        sdv[t][cq < RPL ? row0 + cq : N] = dv_lane;
+        sdv[kk][cq < RPL ? row0 + cq : N] = dv_lane;
         if (kAB) {
             // z = S_{t-1} a_t, dz = G b_t; db_t = G^T z, da_t = S_{t-1}^T dz
             float z[RPL], dz[RPL];
@@ -509,28 +515,27 @@ __global__ __launch_bounds__(64 * SeqBwdShape<N>::WAVES) void seq_bwd_kernel(
 #pragma unroll
             for (int kk = KS - 1; kk >= 0; --kk)
                 if (kk < kend) bwd(sub * KS + kk, kk, Ss[kk + 1], Ss[kk]);
-            __syncthreads();   // every wave's sums of the sub-stage are in LDS
-            for (int idx = tid; idx < kend * NG * N; idx += NT) {
-                const int kk = idx / (NG * N), q = (idx / N) % NG, j = idx % N;
-                float x = part[0][kk][q][j];
+            __syncthreads();   // every wave's sums and dv rows of the sub-stage are in LDS
+            for (int idx = tid; idx < kend * N; idx += NT) {
+                const int kk = idx / N, j = idx % N;
+                float x[NG];
 #pragma unroll
-                for (int wv = 1; wv < WAVES; ++wv) x += part[wv][kk][q][j];
-                acc[sub * KS + kk][q][j] = x;
+                for (int q = 0; q < NG; ++q) {
+                    x[q] = part[0][kk][q][j];
+#pragma unroll
+                    for (int wv = 1; wv < WAVES; ++wv) x[q] += part[wv][kk][q][j];
+                }
+                const size_t o = off(t0 + sub * KS + kk) + j;
+                Elem<Tin>::store1(dr + o, x[0]);
+                Elem<Tin>::store1(dw + o, x[1]);
+                Elem<Tin>::store1(dk + o, x[2]);
+                Elem<Tin>::store1(dv + o, sdv[kk][j]);
+                if (kAB) {
+                    Elem<Tin>::store1(da + o, x[NG > 3 ? 3 : 0]);
+                    Elem<Tin>::store1(db + o, x[NG > 4 ? 4 : 0]);
+                }
             }
             __syncthreads();   // the slots are read before the next sub-stage writes them
-        }
-        __syncthreads();
-        for (int idx = tid; idx < nt * N; idx += NT) {
-            const int t = idx / N, j = idx % N;
-            const size_t o = off(t0 + t) + j;
-            Elem<Tin>::store1(dr + o, acc[t][0][j]);
-            Elem<Tin>::store1(dw + o, acc[t][1][j]);
-            Elem<Tin>::store1(dk + o, acc[t][2][j]);
-            Elem<Tin>::store1(dv + o, sdv[t][j]);
-            if (kAB) {
-                Elem<Tin>::store1(da + o, acc[t][3][j]);
-                Elem<Tin>::store1(db + o, acc[t][4][j]);
-            }
         }
     }
     if (ds0) {
