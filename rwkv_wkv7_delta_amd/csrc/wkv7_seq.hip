@@ -19,6 +19,8 @@
 // 16 tokens at a time, with the next block prefetched into registers while the
 // current one is consumed.
 
+#include <type_traits>
+
 #include "wkv7_device.h"
 #include "wkv7_internal.h"
 
@@ -296,29 +298,36 @@ __global__ __launch_bounds__(256) void decode_kernel(
 // within a wave by lane swaps, across waves through per-wave LDS slots summed
 // once per sub-stage (atomics on shared addresses serialised across waves),
 // and stored from there.
-template <int N> struct SeqBwdShape {
-    // Four rows per 16-lane group: N/16 waves per head.
+template <int N, int kSplit = 1> struct SeqBwdShape {
+    // Four rows per 16-lane group: N/16 waves per head, over kSplit workgroups.
     static constexpr int RPL = 4;                 // rows per 16-lane group
-    static constexpr int WAVES = N / (4 * RPL);
+    static constexpr int WAVES = N / (4 * RPL * kSplit);   // waves per workgroup
     static constexpr int C = N / 16;              // columns per lane
     // Tokens per sub-stage, whose states a lane keeps (RPL * C floats each):
     // 8 at N = 32 and 64, 2 at N = 128 (72, 144 and 96 floats per lane; at
     // N = 128 a fourth state spills past the 256 registers that two waves per
     // SIMD leave each wave, and at N = 32 one sub-stage of 16 tokens measured
-    // slower than two of 8).  Each sub-stage re-runs the stage's forward from
-    // its checkpoint, so a 16-token stage costs 16 + KS (0 + 1 + .. + 16/KS - 1)
-    // forward steps: 24, 24 and 72.
-    static constexpr int KS = N == 128 ? 2 : 8;
+    // slower than two of 8); 4 at N = 128 over two workgroups, whose four waves
+    // have a SIMD each and twice the registers.  Each sub-stage re-runs the
+    // stage's forward from its checkpoint, so a 16-token stage costs
+    // 16 + KS (0 + 1 + .. + 16/KS - 1) forward steps: 24, 24 and 72 (40).
+    static constexpr int KS = kSplit == 2 ? 4 : N == 128 ? 2 : 8;
 };
 
-template <typename Tin, int N, bool kAB>
-__global__ __launch_bounds__(64 * SeqBwdShape<N>::WAVES) void seq_bwd_kernel(
+// kSplit = 2 (fp32 only): a head's rows over two workgroups (block 2 bh + half
+// takes rows half N/2 ..); each adds its rows' share of the per-key sums to
+// outputs that start at zero, so every element receives exactly two fp32
+// additions onto 0, whose result does not depend on their order.
+template <typename Tin, int N, bool kAB, int kSplit = 1>
+__global__ __launch_bounds__((64 * SeqBwdShape<N, kSplit>::WAVES)) void seq_bwd_kernel(
     int T, int H, const Tin* __restrict__ r, const Tin* __restrict__ w, const Tin* __restrict__ k,
     const Tin* __restrict__ v, const Tin* __restrict__ a, const Tin* __restrict__ b,
     const Tin* __restrict__ dy, const float* __restrict__ dsT, const float* __restrict__ ckpt,
     Tin* __restrict__ dr, Tin* __restrict__ dw, Tin* __restrict__ dk, Tin* __restrict__ dv,
     Tin* __restrict__ da, Tin* __restrict__ db, float* __restrict__ ds0) {
-    using Sh = SeqBwdShape<N>;
+    using Sh = SeqBwdShape<N, kSplit>;
+    static_assert(kSplit == 1 || (kSplit == 2 && std::is_same<Tin, float>::value),
+                  "rows over two workgroups accumulate in fp32 outputs");
     constexpr int WAVES = Sh::WAVES, RPL = Sh::RPL, C = Sh::C, KS = Sh::KS;
     constexpr int NT = 64 * WAVES;
     constexpr int NG = kAB ? 5 : 3;   // per-key gradients: dr, dw, dk (, da, db)
@@ -327,12 +336,13 @@ __global__ __launch_bounds__(64 * SeqBwdShape<N>::WAVES) void seq_bwd_kernel(
     __shared__ __align__(16) float part[WAVES][KS][NG][N];   // per-wave sums of a sub-stage
     __shared__ float sdv[KS][N + 1];                  // column N: where surplus lanes write
 
-    const int bh = blockIdx.x;
+    const int bh = blockIdx.x / kSplit, half = blockIdx.x % kSplit;
     const int bb = bh / H, hh = bh % H;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int grp = lane >> 4, cq = lane & 15;
-    const int row0 = (wave * 4 + grp) * RPL;          // rows row0 .. row0 + RPL - 1
+    constexpr int NR = N / kSplit;                   // rows of this workgroup
+    const int row0 = half * NR + (wave * 4 + grp) * RPL;   // rows row0 .. row0 + RPL - 1
     const int nstg = (T + kTB - 1) / kTB;
     auto off = [&](int t) { return (((size_t)bb * T + t) * H + hh) * N; };
 
@@ -526,13 +536,29 @@ __global__ __launch_bounds__(64 * SeqBwdShape<N>::WAVES) void seq_bwd_kernel(
                     for (int wv = 1; wv < WAVES; ++wv) x[q] += part[wv][kk][q][j];
                 }
                 const size_t o = off(t0 + sub * KS + kk) + j;
-                Elem<Tin>::store1(dr + o, x[0]);
-                Elem<Tin>::store1(dw + o, x[1]);
-                Elem<Tin>::store1(dk + o, x[2]);
-                Elem<Tin>::store1(dv + o, sdv[kk][j]);
-                if (kAB) {
-                    Elem<Tin>::store1(da + o, x[NG > 3 ? 3 : 0]);
-                    Elem<Tin>::store1(db + o, x[NG > 4 ? 4 : 0]);
+                if constexpr (kSplit == 1) {
+                    Elem<Tin>::store1(dr + o, x[0]);
+                    Elem<Tin>::store1(dw + o, x[1]);
+                    Elem<Tin>::store1(dk + o, x[2]);
+                    Elem<Tin>::store1(dv + o, sdv[kk][j]);
+                    if (kAB) {
+                        Elem<Tin>::store1(da + o, x[NG > 3 ? 3 : 0]);
+                        Elem<Tin>::store1(db + o, x[NG > 4 ? 4 : 0]);
+                    }
+                } else {
+                    unsafeAtomicAdd(dr + o, x[0]);
+                    unsafeAtomicAdd(dw + o, x[1]);
+                    unsafeAtomicAdd(dk + o, x[2]);
+                    if (kAB) {
+                        unsafeAtomicAdd(da + o, x[NG > 3 ? 3 : 0]);
+                        unsafeAtomicAdd(db + o, x[NG > 4 ? 4 : 0]);
+                    }
+                }
+            }
+            if constexpr (kSplit > 1) {   // dv: this workgroup's rows
+                for (int idx = tid; idx < kend * NR; idx += NT) {
+                    const int kk = idx / NR, j = half * NR + idx % NR;
+                    Elem<Tin>::store1(dv + off(t0 + sub * KS + kk) + j, sdv[kk][j]);
                 }
             }
             __syncthreads();   // the slots are read before the next sub-stage writes them
@@ -689,6 +715,29 @@ hipError_t launch_seq_bwd_n(const SeqBwdArgs& p, hipStream_t stream) {
         f.ckpt = const_cast<float*>(p.ckpt);
         const hipError_t e = launch_seq_fwd_n<Tin, N>(f, FwdSplit{p.B * p.H, 1, p.T, nullptr}, stream);
         if (e != hipSuccess) return e;
+    }
+    if constexpr (N == 128 && std::is_same<Tin, float>::value) {
+        if (p.split_rows) {
+            // The per-key outputs start at zero (a fill kernel: no memset node
+            // if the caller captures the stream).
+            const size_t n4 = (size_t)p.B * p.T * p.H * N / 4;
+            float* outs[5] = {static_cast<float*>(p.dr), static_cast<float*>(p.dw),
+                              static_cast<float*>(p.dk), static_cast<float*>(p.da),
+                              static_cast<float*>(p.db)};
+            for (int q = 0; q < (p.a ? 5 : 3); ++q) {
+                state_copy_kernel<<<dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream>>>(n4, nullptr, outs[q]);
+                const hipError_t e = hipGetLastError();
+                if (e != hipSuccess) return e;
+            }
+            auto kern = p.a ? seq_bwd_kernel<float, N, true, 2> : seq_bwd_kernel<float, N, false, 2>;
+            kern<<<dim3(2 * p.B * p.H), dim3(64 * SeqBwdShape<N, 2>::WAVES), 0, stream>>>(
+                p.T, p.H, static_cast<const float*>(p.r), static_cast<const float*>(p.w),
+                static_cast<const float*>(p.k), static_cast<const float*>(p.v),
+                static_cast<const float*>(p.a), static_cast<const float*>(p.b),
+                static_cast<const float*>(p.dy), p.dsT, p.ckpt, outs[0], outs[1], outs[2],
+                static_cast<float*>(p.dv), outs[3], outs[4], p.ds0);
+            return hipGetLastError();
+        }
     }
     auto kern = p.a ? seq_bwd_kernel<Tin, N, true> : seq_bwd_kernel<Tin, N, false>;
     kern<<<dim3(p.B * p.H), dim3(64 * SeqBwdShape<N>::WAVES), 0, stream>>>(
