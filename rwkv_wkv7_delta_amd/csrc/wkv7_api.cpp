@@ -438,10 +438,10 @@ int run_backward(const wkv7_desc* desc, const void* r, const void* w, const void
                            r, w, k, v, a, b, dy, s0, dsT, dr, dw, dk, dv, da, db, ds0,
                            ckpt ? const_cast<float*>(ckpt) : static_cast<float*>(workspace),
                            ckpt != nullptr};
-        // N = 128 in fp32 with few heads: each head's rows over two workgroups
-        // (0.19B shape, B = 4, T = 1024, H = 12: 5.65 -> 3.75 ms).
+        // N = 128 with few heads: each head's rows over two workgroups (0.19B
+        // shape, B = 4, T = 1024, H = 12: fp32 5.65 -> 3.75 ms, bf16 5.6 -> 3.66).
         const int64_t nbh = (int64_t)desc->B * desc->H;
-        p.split_rows = desc->N == 128 && desc->dtype == WKV7_F32 && 2 * nbh <= device_cus() &&
+        p.split_rows = desc->N == 128 && 2 * nbh <= device_cus() &&
                        nbh * desc->T * desc->N / 1024 < INT32_MAX;
         return from_hip(wkv7::launch_seq_bwd(p, s));
     }

@@ -46,8 +46,8 @@ struct SeqBwdArgs {
     float* ds0;         // may be null
     float* ckpt;        // [B][H][ceil(T/16)][N][N] fp32: scratch the pass fills first, or
     bool ckpt_given;    // the caller's checkpoints (then no forward re-run)
-    // N = 128, fp32: each head's rows over two workgroups (the caller's choice:
-    // when twice B*H workgroups fit the device at once)
+    // N = 128: each head's rows over two workgroups (the caller's choice: when
+    // twice B*H workgroups fit the device at once)
     bool split_rows = false;
 };
 

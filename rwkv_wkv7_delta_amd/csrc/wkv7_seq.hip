@@ -314,10 +314,11 @@ template <int N, int kSplit = 1> struct SeqBwdShape {
     static constexpr int KS = kSplit == 2 ? 4 : N == 128 ? 2 : 8;
 };
 
-// kSplit = 2 (fp32 only): a head's rows over two workgroups (block 2 bh + half
-// takes rows half N/2 ..); each adds its rows' share of the per-key sums to
-// outputs that start at zero, so every element receives exactly two fp32
-// additions onto 0, whose result does not depend on their order.
+// kSplit = 2: a head's rows over two workgroups (block 2 bh + half takes rows
+// half N/2 ..); each adds its rows' share of the per-key sums to outputs that
+// start at zero (fp32 atomics, or packed bf16 ones on pairs of columns), so
+// every element receives exactly two additions onto 0, whose result does not
+// depend on their order.  In bf16 each share is rounded before the addition.
 template <typename Tin, int N, bool kAB, int kSplit = 1>
 __global__ __launch_bounds__((64 * SeqBwdShape<N, kSplit>::WAVES)) void seq_bwd_kernel(
     int T, int H, const Tin* __restrict__ r, const Tin* __restrict__ w, const Tin* __restrict__ k,
@@ -326,8 +327,7 @@ __global__ __launch_bounds__((64 * SeqBwdShape<N, kSplit>::WAVES)) void seq_bwd_
     Tin* __restrict__ dr, Tin* __restrict__ dw, Tin* __restrict__ dk, Tin* __restrict__ dv,
     Tin* __restrict__ da, Tin* __restrict__ db, float* __restrict__ ds0) {
     using Sh = SeqBwdShape<N, kSplit>;
-    static_assert(kSplit == 1 || (kSplit == 2 && std::is_same<Tin, float>::value),
-                  "rows over two workgroups accumulate in fp32 outputs");
+    static_assert(kSplit == 1 || kSplit == 2, "rows over one or two workgroups");
     constexpr int WAVES = Sh::WAVES, RPL = Sh::RPL, C = Sh::C, KS = Sh::KS;
     constexpr int NT = 64 * WAVES;
     constexpr int NG = kAB ? 5 : 3;   // per-key gradients: dr, dw, dk (, da, db)
@@ -526,17 +526,17 @@ __global__ __launch_bounds__((64 * SeqBwdShape<N, kSplit>::WAVES)) void seq_bwd_
             for (int kk = KS - 1; kk >= 0; --kk)
                 if (kk < kend) bwd(sub * KS + kk, kk, Ss[kk + 1], Ss[kk]);
             __syncthreads();   // every wave's sums and dv rows of the sub-stage are in LDS
-            for (int idx = tid; idx < kend * N; idx += NT) {
-                const int kk = idx / N, j = idx % N;
-                float x[NG];
+            if constexpr (kSplit == 1) {
+                for (int idx = tid; idx < kend * N; idx += NT) {
+                    const int kk = idx / N, j = idx % N;
+                    float x[NG];
 #pragma unroll
-                for (int q = 0; q < NG; ++q) {
-                    x[q] = part[0][kk][q][j];
+                    for (int q = 0; q < NG; ++q) {
+                        x[q] = part[0][kk][q][j];
 #pragma unroll
-                    for (int wv = 1; wv < WAVES; ++wv) x[q] += part[wv][kk][q][j];
-                }
-                const size_t o = off(t0 + sub * KS + kk) + j;
-                if constexpr (kSplit == 1) {
+                        for (int wv = 1; wv < WAVES; ++wv) x[q] += part[wv][kk][q][j];
+                    }
+                    const size_t o = off(t0 + sub * KS + kk) + j;
                     Elem<Tin>::store1(dr + o, x[0]);
                     Elem<Tin>::store1(dw + o, x[1]);
                     Elem<Tin>::store1(dk + o, x[2]);
@@ -545,20 +545,42 @@ __global__ __launch_bounds__((64 * SeqBwdShape<N, kSplit>::WAVES)) void seq_bwd_
                         Elem<Tin>::store1(da + o, x[NG > 3 ? 3 : 0]);
                         Elem<Tin>::store1(db + o, x[NG > 4 ? 4 : 0]);
                     }
-                } else {
-                    unsafeAtomicAdd(dr + o, x[0]);
-                    unsafeAtomicAdd(dw + o, x[1]);
-                    unsafeAtomicAdd(dk + o, x[2]);
+                }
+            } else {
+                // this workgroup's share of the per-key sums, PW columns per atomic
+                constexpr int PW = std::is_same<Tin, float>::value ? 1 : 2;
+                for (int idx = tid; idx < kend * (N / PW); idx += NT) {
+                    const int kk = idx / (N / PW), j = PW * (idx % (N / PW));
+                    float x[NG][PW];
+#pragma unroll
+                    for (int q = 0; q < NG; ++q)
+#pragma unroll
+                        for (int e = 0; e < PW; ++e) {
+                            x[q][e] = part[0][kk][q][j + e];
+#pragma unroll
+                            for (int wv = 1; wv < WAVES; ++wv) x[q][e] += part[wv][kk][q][j + e];
+                        }
+                    const size_t o = off(t0 + sub * KS + kk) + j;
+                    auto add = [&](Tin* dst, const float (&xv)[PW]) __attribute__((always_inline)) {
+                        if constexpr (PW == 1) {
+                            unsafeAtomicAdd(dst, xv[0]);
+                        } else {
+                            typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+                            const bf16x2v pv = {(__bf16)xv[0], (__bf16)xv[1]};
+                            __builtin_amdgcn_global_atomic_fadd_v2bf16(reinterpret_cast<bf16x2v*>(dst), pv);
+                        }
+                    };
+                    add(dr + o, x[0]);
+                    add(dw + o, x[1]);
+                    add(dk + o, x[2]);
                     if (kAB) {
-                        unsafeAtomicAdd(da + o, x[NG > 3 ? 3 : 0]);
-                        unsafeAtomicAdd(db + o, x[NG > 4 ? 4 : 0]);
+                        add(da + o, x[NG > 3 ? 3 : 0]);
+                        add(db + o, x[NG > 4 ? 4 : 0]);
                     }
                 }
-            }
-            if constexpr (kSplit > 1) {   // dv: this workgroup's rows
-                for (int idx = tid; idx < kend * NR; idx += NT) {
-                    const int kk = idx / NR, j = half * NR + idx % NR;
-                    Elem<Tin>::store1(dv + off(t0 + sub * KS + kk) + j, sdv[kk][j]);
+                for (int idx = tid; idx < kend * NR; idx += NT) {   // dv: this workgroup's rows
+                    const int kk = idx / NR, jr = half * NR + idx % NR;
+                    Elem<Tin>::store1(dv + off(t0 + sub * KS + kk) + jr, sdv[kk][jr]);
                 }
             }
             __syncthreads();   // the slots are read before the next sub-stage writes them
@@ -716,26 +738,26 @@ hipError_t launch_seq_bwd_n(const SeqBwdArgs& p, hipStream_t stream) {
         const hipError_t e = launch_seq_fwd_n<Tin, N>(f, FwdSplit{p.B * p.H, 1, p.T, nullptr}, stream);
         if (e != hipSuccess) return e;
     }
-    if constexpr (N == 128 && std::is_same<Tin, float>::value) {
+    if constexpr (N == 128) {
         if (p.split_rows) {
             // The per-key outputs start at zero (a fill kernel: no memset node
             // if the caller captures the stream).
-            const size_t n4 = (size_t)p.B * p.T * p.H * N / 4;
-            float* outs[5] = {static_cast<float*>(p.dr), static_cast<float*>(p.dw),
-                              static_cast<float*>(p.dk), static_cast<float*>(p.da),
-                              static_cast<float*>(p.db)};
+            const size_t n16 = (size_t)p.B * p.T * p.H * N * sizeof(Tin) / 16;
+            Tin* outs[5] = {static_cast<Tin*>(p.dr), static_cast<Tin*>(p.dw), static_cast<Tin*>(p.dk),
+                            static_cast<Tin*>(p.da), static_cast<Tin*>(p.db)};
             for (int q = 0; q < (p.a ? 5 : 3); ++q) {
-                state_copy_kernel<<<dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream>>>(n4, nullptr, outs[q]);
+                state_copy_kernel<<<dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, stream>>>(
+                    n16, nullptr, reinterpret_cast<float*>(outs[q]));
                 const hipError_t e = hipGetLastError();
                 if (e != hipSuccess) return e;
             }
-            auto kern = p.a ? seq_bwd_kernel<float, N, true, 2> : seq_bwd_kernel<float, N, false, 2>;
+            auto kern = p.a ? seq_bwd_kernel<Tin, N, true, 2> : seq_bwd_kernel<Tin, N, false, 2>;
             kern<<<dim3(2 * p.B * p.H), dim3(64 * SeqBwdShape<N, 2>::WAVES), 0, stream>>>(
-                p.T, p.H, static_cast<const float*>(p.r), static_cast<const float*>(p.w),
-                static_cast<const float*>(p.k), static_cast<const float*>(p.v),
-                static_cast<const float*>(p.a), static_cast<const float*>(p.b),
-                static_cast<const float*>(p.dy), p.dsT, p.ckpt, outs[0], outs[1], outs[2],
-                static_cast<float*>(p.dv), outs[3], outs[4], p.ds0);
+                p.T, p.H, static_cast<const Tin*>(p.r), static_cast<const Tin*>(p.w),
+                static_cast<const Tin*>(p.k), static_cast<const Tin*>(p.v),
+                static_cast<const Tin*>(p.a), static_cast<const Tin*>(p.b),
+                static_cast<const Tin*>(p.dy), p.dsT, p.ckpt, outs[0], outs[1], outs[2],
+                static_cast<Tin*>(p.dv), outs[3], outs[4], p.ds0);
             return hipGetLastError();
         }
     }

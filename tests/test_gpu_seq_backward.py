@@ -71,32 +71,32 @@ def test_seq_bwd_decay_only(wk, N):
     _check(wk, inp, f"seq bwd a=b=0 N={N}", ab=False)
 
 
-def test_seq_bwd_n128_fp32_both_layouts(wk):
-    """N = 128, fp32: with at most half as many heads as compute units each
-    head's rows run over two workgroups (each adds its rows' share of the
-    per-key sums to outputs cleared first); with more heads, over one.  Sampled
-    heads of both against the oracle."""
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_seq_bwd_n128_both_layouts(wk, dtype):
+    """N = 128: with at most half as many heads as compute units each head's rows
+    run over two workgroups (each adds its rows' share of the per-key sums to
+    outputs cleared first: fp32 atomics, or packed bf16 ones); with more heads,
+    over one.  Sampled heads of both against the oracle."""
     ncu = __import__("torch").cuda.get_device_properties(0).multi_processor_count
-    inp = synth.generate(1, 45, ncu // 2, 128, dtype="fp32", seed=560, random_s0=True, backward=True)
+    H = ncu // 2
+    inp = synth.generate(1, 45, H, 128, dtype=dtype, seed=560, random_s0=True, backward=True)
     dsT = (0.1 * np.random.default_rng(561).standard_normal(inp.s0.shape)).astype(np.float32)
     g = _grads(wk, inp, dsT)
-    H = ncu // 2
     pairs = [(0, 0), (0, 1), (0, H // 2), (0, H - 1)]
     sel = [oracle.select_heads(x, pairs) for x in inp.tensors()]
     ref = oracle.backward(*sel, oracle.select_heads(inp.s0, pairs, state=True),
                           oracle.select_heads(inp.dy, pairs), oracle.select_heads(dsT, pairs, state=True))
-    for name, x, rr in zip(NAMES[:6], g[:6], ref[:6]):
-        assert_close(oracle.select_heads(x, pairs), rr, "fp32", f"two workgroups {name}")
-    assert_close(oracle.select_heads(g[6], pairs, state=True), ref[6], "fp32", "two workgroups ds0")
-    inp = synth.generate(1, 40, ncu // 2 + 1, 128, dtype="fp32", seed=562, random_s0=True, backward=True)
-    g = _grads(wk, inp)
+    for name, x, rr in zip(NAMES, g, ref):
+        assert_close(oracle.select_heads(x, pairs, state=name == "ds0"), rr, dtype, f"two workgroups {name}")
     H = ncu // 2 + 1
+    inp = synth.generate(1, 40, H, 128, dtype=dtype, seed=562, random_s0=True, backward=True)
+    g = _grads(wk, inp)
     pairs = [(0, 0), (0, H // 3), (0, H - 1)]
     sel = [oracle.select_heads(x, pairs) for x in inp.tensors()]
     ref = oracle.backward(*sel, oracle.select_heads(inp.s0, pairs, state=True),
                           oracle.select_heads(inp.dy, pairs))
     for name, x, rr in zip(NAMES, g, ref):
-        assert_close(oracle.select_heads(x, pairs, state=name == "ds0"), rr, "fp32", f"one workgroup {name}")
+        assert_close(oracle.select_heads(x, pairs, state=name == "ds0"), rr, dtype, f"one workgroup {name}")
 
 
 def test_seq_bwd_fp32_small_workload(wk):
