@@ -73,9 +73,12 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run one plain 1 GiB device copy (for scaling HBM counters)")
-    p.add_argument("--workload", choices=("step", "chunked_fwd_1.5b"), default="step",
+    p.add_argument("--workload", choices=("step", "chunked_fwd_1.5b", "sequential_bwd_2.9b"),
+                   default="step",
                    help="chunked_fwd_1.5b: time only the chunked forward at the 1.5B-model shape "
-                        "(the line under secondary) and print it")
+                        "(the line under secondary) and print it; sequential_bwd_2.9b: the "
+                        "sequential reverse pass (checkpointing scan + adjoint) at the 2.9B-model "
+                        "shape in bf16, two calls (for counter runs)")
     p.add_argument("--summarize-sq", nargs=5,
                    metavar=("STEP_PMC_DIR", "STEP_STEPS", "CFG_PMC_DIR", "CFG_REPS", "CMD"),
                    help="turn two rocprofv3 --pmc runs of this script (SQ_COUNTERS; the step, "
@@ -361,6 +364,32 @@ def chunked_fwd_15b(torch, wk, dev, reps=25, calls=4):
             "frac_hbm": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
 
 
+def sequential_bwd_29b(torch, wk, dev, calls=2):
+    """The sequential reverse pass (chunk_len = 0: the checkpointing scan, then
+    the adjoint) at the 2.9B-model shape in bf16, zero s0, dy ~ N(0,1), no ds0:
+    `calls` calls, each between HIP events (few, so that a counter run stays
+    short); the last call's time."""
+    B, T, H, N = 8, 4096, 40, 64
+    ins = _dev_inputs(torch, (B, T, H, N), dev, 12)
+    g = torch.Generator(device=dev)
+    g.manual_seed(13)
+    dy = torch.randn(B, T, H, N, device=dev, generator=g).bfloat16()
+    desc = wk.make_desc(B, T, H, N, wk.WKV7_BF16, 0)
+    ws = torch.empty(wk.workspace_bytes(desc, False) // 4 + 64, device=dev)
+    grads = [torch.empty_like(ins[0]) for _ in range(6)]
+    ms = 0.0
+    for _ in range(calls):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        wk.backward(*ins, dy, None, None, None, chunk_len=0, workspace=ws, grads=grads, want_ds0=False)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+    return {"shape": "B=8 T=4096 H=40 N=64 bf16, zero s0, dy~N(0,1)", "calls": calls,
+            "ms": round(ms, 3), "tokens_per_s": round(B * T / ms * 1e3, 1)}
+
+
 def main():
     args = parse()
     if args.summarize_profile:
@@ -385,6 +414,10 @@ def main():
     dev = torch.device("cuda:0")
     if args.workload == "chunked_fwd_1.5b":
         print(json.dumps({"workload": "chunked_fwd_1.5b", **chunked_fwd_15b(torch, wk, dev)}),
+              flush=True)
+        return
+    if args.workload == "sequential_bwd_2.9b":
+        print(json.dumps({"workload": "sequential_bwd_2.9b", **sequential_bwd_29b(torch, wk, dev)}),
               flush=True)
         return
     wl = synth.WORKLOADS["fwd_bwd_2.9b"]
