@@ -301,8 +301,8 @@ __global__ __launch_bounds__(kP1Threads<N>, N == 32 ? 2 : 1) void bwd_chain_kern
     // ---- INV (inverse waves): Aab, Tm = (I - Aab)^-1, Tm^T Bb, (Arb Tm)^T -------
     // In the interval after E(c) a wave forms Aab = tril_-1(At Bh^T) and Arb^T
     // (Arb = tril_0(Rt Bh^T), as [s][t]), the inverses of Aab's 4x4 diagonal
-    // blocks and N = Td L (wkv7_mfma.h); in the next it joins them into Tm and
-    // applies Tm, as hi and lo bf16 parts, to the factors of
+    // blocks, N = Td L and N^T N^T (wkv7_mfma.h); in the next it joins them into
+    // Tm and applies Tm, as hi and lo bf16 parts, to the factors of
     // dX = (Tm^T Bb) dS^T + (Arb Tm)^T dY (the
     // transpose of the forward's Z = (Tm At) S0^T + (Tm Aak) V, with the same
     // cancellations kept inside these products):
@@ -335,7 +335,7 @@ __global__ __launch_bounds__(kP1Threads<N>, N == 32 ? 2 : 1) void bwd_chain_kern
             P[q] = (l16 < 4 * g + q) ? P[q] : 0.f;    // s < t
             R[q] = (4 * g + q <= l16) ? R[q] : 0.f;   // s <= t
         }
-        return InvState{unit_lower_inverse_begin(P, g, l16), R};
+        return InvState{unit_lower_inverse_begin<false>(P, g, l16), R};
     };
     auto inv_end = [&](int c, const InvState& st) __attribute__((always_inline)) {
         P1Slot& s = sm.sl[slot_of(c)];

@@ -417,8 +417,8 @@ __global__ __launch_bounds__(kEpi ? FwdShape<N>::threads_epi : FwdShape<N>::thre
     // ---- INV (inverse waves): Aab, Aak, Tm = (I - Aab)^-1, At' and Aak' --------
     // In the interval after E(c) a wave forms Aab = tril_-1(At Bh^T) and Aak =
     // tril_-1(At Kh^T) (accumulator layout [t][s]), the inverses of Aab's 4x4
-    // diagonal blocks and N = Td L (wkv7_mfma.h); in the next it joins them into
-    // Tm and applies Tm, as hi and lo bf16 images, to the factors of Z:
+    // diagonal blocks, N = Td L and N N (wkv7_mfma.h); in the next it joins them
+    // into Tm and applies Tm, as hi and lo bf16 images, to the factors of Z:
     //   At'^T tile jt = At^T[keys 16 jt ..] Tm^T, whose accumulator registers
     //     hold At'[l16][16 jt + 4 g + q] -- the row layout of At', written over
     //     the same columns of At (read first, by transposed reads);
@@ -449,7 +449,7 @@ __global__ __launch_bounds__(kEpi ? FwdShape<N>::threads_epi : FwdShape<N>::thre
             P[q] = (l16 < 4 * g + q) ? P[q] : 0.f;
             K[q] = (l16 < 4 * g + q) ? K[q] : 0.f;
         }
-        return InvState{unit_lower_inverse_begin(P, g, l16), K};
+        return InvState{unit_lower_inverse_begin<true>(P, g, l16), K};
     };
     auto inv_end = [&](int c, const InvState& st) __attribute__((always_inline)) {
         Slot& s = sm.sl[c % kSlots];

@@ -178,9 +178,15 @@ __device__ __forceinline__ float quad_bcast(float x) {
 // solves with the same six below-diagonal entries (quad broadcasts): lane c
 // gets column c of the block's inverse (its accumulator registers, Td) and row
 // c (the accumulator registers of Td^T).
+//
+// The work comes in two stages, which the kernels run in consecutive intervals
+// on one wave: _begin forms Td, N and also the first product of the join (N N
+// for the rows form, N^T N^T for the columns form), so that the two stages
+// issue about as much work each; _end finishes T.
 struct BlockInverse {
-    f32x4 Td, N, NT;   // accumulator tiles of Td, N = Td L and N^T
+    f32x4 Td, NT, P;   // accumulator tiles of Td, N^T and the join's first product
 };
+template <bool kRows>
 __device__ __forceinline__ BlockInverse unit_lower_inverse_begin(f32x4 A, int g, int l16) {
     const float a10 = quad_bcast<0>(A[1]), a20 = quad_bcast<0>(A[2]), a30 = quad_bcast<0>(A[3]);
     const float a21 = quad_bcast<1>(A[2]), a31 = quad_bcast<1>(A[3]);
@@ -206,28 +212,28 @@ __device__ __forceinline__ BlockInverse unit_lower_inverse_begin(f32x4 A, int g,
     b.Td[0] = diag ? x0 : 0.f; b.Td[1] = diag ? x1 : 0.f; b.Td[2] = diag ? x2 : 0.f; b.Td[3] = diag ? x3 : 0.f;
     TdT[0] = diag ? y0 : 0.f; TdT[1] = diag ? y1 : 0.f; TdT[2] = diag ? y2 : 0.f; TdT[3] = diag ? y3 : 0.f;
     const Split4 sL = split4(L), sTdT = split4(TdT);
-    b.N = mul3(sTdT, sL, zero4());    // Td L   (Td^T's registers are Td's A-operand image)
-    b.NT = mul3(sL, sTdT, zero4());   // L^T Td^T
+    const f32x4 N = mul3(sTdT, sL, zero4());   // Td L   (Td^T's registers are Td's A-operand image)
+    b.NT = mul3(sL, sTdT, zero4());            // L^T Td^T
+    const Split4 sN = split4(N), sNT = split4(b.NT);
+    b.P = kRows ? mul3(sNT, sN, zero4())       // N N
+                : mul3(sN, sNT, zero4());      // N^T N^T
     return b;
 }
 // The accumulator tile of T^T (= T's A-operand image: lane (g, l16) register q
-// holds T[l16][4g+q]): T^T = Td^T (I + (N^T)^2)(I + N^T).
+// holds T[l16][4g+q]): T^T = Td^T (I + (N^T)^2)(I + N^T), from the rows form
+// of _begin.
 __device__ __forceinline__ f32x4 unit_lower_inverse_rows_end(const BlockInverse& b, int g, int l16) {
-    const Split4 sN = split4(b.N), sNT = split4(b.NT);
-    const f32x4 N2 = mul3(sNT, sN, zero4());             // N N
     f32x4 W1 = b.NT;                                      // I + N^T
 #pragma unroll
     for (int q = 0; q < 4; ++q) W1[q] += (4 * g + q == l16) ? 1.f : 0.f;
-    const f32x4 W2 = mul3(split4(N2), split4(W1), W1);   // W1 + (N^T)^2 W1
+    const f32x4 W2 = mul3(split4(b.P), split4(W1), W1);  // W1 + (N^T)^2 W1
     return mul3(split4(b.Td), split4(W2), zero4());      // Td^T W2
 }
 // The accumulator tile of T (= T^T's A-operand image: lane (g, l16) register q
-// holds T[4g+q][l16]): T = (I + N)(I + N^2) Td.
+// holds T[4g+q][l16]): T = (I + N)(I + N^2) Td, from the columns form of _begin.
 __device__ __forceinline__ f32x4 unit_lower_inverse_cols_end(const BlockInverse& b) {
-    const Split4 sN = split4(b.N), sNT = split4(b.NT);
-    const f32x4 NT2 = mul3(sN, sNT, zero4());             // N^T N^T
-    const f32x4 V2 = mul3(split4(NT2), split4(b.Td), b.Td);   // Td + N^2 Td
-    return mul3(sNT, split4(V2), V2);                     // V2 + N V2
+    const f32x4 V2 = mul3(split4(b.P), split4(b.Td), b.Td);   // Td + N^2 Td
+    return mul3(split4(b.NT), split4(V2), V2);                // V2 + N V2
 }
 
 }  // namespace wkv7
