@@ -138,12 +138,15 @@ size_t wkv7_workspace_bytes(const wkv7_desc *desc);
    the adjoint of the state leaving every 32-token block there, as much again as
    the tape, plus 256 bytes of work queues); with_tape = 0 when it passes none
    (then a forward re-run also writes its tape into the workspace: twice the
-   tape).
+   tape); and, when the adjoint chain runs in time segments (below, at
+   wkv7_backward), from the next 256-byte boundary 3 * nseg fp32 N x N states
+   per head.  That choice depends on the current device: query the size and
+   call on the same one.
    chunk_len = 0 (the sequential reverse pass, which writes fp32 checkpoints
    itself): wkv7_ckpt_bytes(desc), whatever with_tape is (wkv7_backward_ckpt,
    which reads the caller's checkpoints, needs none).
    0 on an invalid descriptor or one the backward does not take (chunk_len = 16
-   with N != WKV7_HEAD_SIZE or fp32). */
+   with fp32). */
 size_t wkv7_backward_workspace_bytes(const wkv7_desc *desc, int with_tape);
 
 /*
@@ -276,7 +279,16 @@ int wkv7_forward_split_static(const wkv7_desc *desc, const void *r, const void *
  *               WKV7_ERR_WORKSPACE.  Required whenever B*T*H > 0.
  * desc->chunk_len selects the form:
  *   16  chunk by chunk (16 tokens) on bf16 matrix cores: dtype = WKV7_BF16 and
- *       N = 64 only (WKV7_ERR_UNSUPPORTED otherwise); uses the tape.
+ *       N = 32 or 64 (WKV7_ERR_UNSUPPORTED otherwise); uses the tape.  The
+ *       adjoint chain (a serial run per head from the last chunk to the
+ *       first) runs in time segments when wkv7_forward_split's automatic plan
+ *       for the same desc splits every head (few heads; see there): the
+ *       adjoint is affine in itself, so a segment maps the adjoint at its
+ *       right edge as dS_left = dS_right P + H (P: the run from the identity
+ *       with dy = 0, H: the run from zero), and a first launch runs the last
+ *       segment and the maps of the middle ones, a small kernel composes the
+ *       entry adjoints in fp32, a second launch runs the other segments
+ *       (gradients agree with the unsplit chain to rounding).
  *   0   the sequential reverse recurrence token by token in fp32 on the vector
  *       ALU (one workgroup per head): either dtype, N = 32, 64 or 128.  It
  *       first re-runs the sequential forward to write fp32 states every 16

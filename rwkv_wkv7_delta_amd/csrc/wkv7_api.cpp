@@ -50,7 +50,8 @@ size_t tape_bytes_unchecked(const wkv7_desc* d) {
 // Workspace of the backward: its own scratch (dX per token, then the adjoint
 // leaving every 32-token block: as large as the tape), the per-key pass's
 // block queues (two groups of two ints, in 256 bytes), then -- when no tape is
-// passed -- the tape of a forward re-run.
+// passed -- the tape of a forward re-run, then (from a 256-byte boundary) the
+// states of the adjoint chain's time split, when there is one.
 constexpr size_t kQueueBytes = 256;
 
 // Workspace of the sequential reverse pass (chunk_len = 0): the fp32 state
@@ -168,6 +169,25 @@ SplitPlan plan_split(const wkv7_desc* d, int segments, int ncu) {
     return SplitPlan{from, nseg, len, mode};
 }
 
+size_t split_bytes(const wkv7_desc* d, const SplitPlan& p);
+
+// The chunked backward splits its adjoint chain in time under the forward's
+// automatic plan when that plan splits every head (few heads: the chain is one
+// serial run per head, like the forward's); its states follow the rest of the
+// workspace.
+SplitPlan plan_bwd(const wkv7_desc* d) {
+    const SplitPlan none{d->B * d->H, 1, d->T, 0};
+    if (d->chunk_len == 0) return none;
+    const SplitPlan p = plan_split(d, 0, device_cus());
+    return p.nseg >= 2 && p.mode == 0 && p.split_from == 0 ? p : none;
+}
+
+// Offset of the split states in the backward's workspace, and its whole size.
+size_t bwd_states_offset(const wkv7_desc* d, bool with_tape) {
+    return (tape_bytes_unchecked(d) * (with_tape ? 1 : 2) + kQueueBytes + 255) / 256 * 256;
+}
+size_t bwd_workspace_bytes(const wkv7_desc* d, bool with_tape, const SplitPlan& bp);
+
 size_t split_bytes(const wkv7_desc* d, const SplitPlan& p) {
     const size_t nbh = (size_t)d->B * d->H;
     const size_t st = (size_t)d->N * d->N * sizeof(float);
@@ -175,6 +195,11 @@ size_t split_bytes(const wkv7_desc* d, const SplitPlan& p) {
     if (p.mode == 1) return nbh * st + (nbh * sizeof(int) + 255) / 256 * 256;
     const size_t nsplit = nbh - p.split_from;
     return nsplit == 0 ? 0 : nsplit * 3 * p.nseg * st;
+}
+
+size_t bwd_workspace_bytes(const wkv7_desc* d, bool with_tape, const SplitPlan& bp) {
+    if (bp.nseg >= 2) return bwd_states_offset(d, with_tape) + split_bytes(d, bp);
+    return tape_bytes_unchecked(d) * (with_tape ? 1 : 2) + kQueueBytes;
 }
 
 int run_forward(const wkv7_desc* d, const void* r, const void* w, const void* k, const void* v,
@@ -242,7 +267,7 @@ size_t wkv7_backward_workspace_bytes(const wkv7_desc* desc, int with_tape) {
     if (check_desc(desc) != WKV7_OK) return 0;
     if (desc->chunk_len == 0) return seq_ckpt_bytes(desc);
     if (desc->dtype != WKV7_BF16) return 0;
-    return tape_bytes_unchecked(desc) * (with_tape ? 1 : 2) + kQueueBytes;
+    return bwd_workspace_bytes(desc, with_tape != 0, plan_bwd(desc));
 }
 
 size_t wkv7_workspace_bytes(const wkv7_desc* desc) { return wkv7_backward_workspace_bytes(desc, 0); }
@@ -418,8 +443,9 @@ int run_backward(const wkv7_desc* desc, const void* r, const void* w, const void
         return WKV7_ERR_INVALID_ARG;
     // The sequential pass reads the caller's fp32 checkpoints (then it needs no
     // scratch), else it writes its own; it never reads the tape.
+    const SplitPlan bp = seq ? SplitPlan{desc->B * desc->H, 1, desc->T, 0} : plan_bwd(desc);
     const size_t need = seq ? (ckpt ? 0 : seq_ckpt_bytes(desc))
-                            : tape_bytes_unchecked(desc) * (tape ? 1 : 2) + kQueueBytes;
+                            : bwd_workspace_bytes(desc, tape != nullptr, bp);
     if (has_tokens && need > 0 && (workspace == nullptr || workspace_bytes < need))
         return WKV7_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -445,6 +471,7 @@ int run_backward(const wkv7_desc* desc, const void* r, const void* w, const void
                        nbh * desc->T * desc->N / 1024 < INT32_MAX;
         return from_hip(wkv7::launch_seq_bwd(p, s));
     }
+    const bool tape_given = tape != nullptr;
     if (!tape) {
         // Re-run the forward (without y) into the last part of the workspace.
         void* own = ws + tape_bytes_unchecked(desc) + kQueueBytes;
@@ -465,8 +492,13 @@ int run_backward(const wkv7_desc* desc, const void* r, const void* w, const void
             if (b1 > desc->B - 1) b1 = desc->B - 1;
         }
     }
-    const wkv7::BwdArgs g1 = slice(desc, 0, b1, r, w, k, v, a, b, s0, dy, dsT, tape, dr, dw, dk, dv,
-                                   da, db, ds0, ws, 0);
+    wkv7::BwdArgs g1 = slice(desc, 0, b1, r, w, k, v, a, b, s0, dy, dsT, tape, dr, dw, dk, dv,
+                             da, db, ds0, ws, 0);
+    if (bp.nseg >= 2 && b1 == desc->B) {   // the adjoint chain in time segments
+        g1.nseg = bp.nseg;
+        g1.seg_len = bp.seg_len;
+        g1.states = reinterpret_cast<float*>(ws + bwd_states_offset(desc, tape_given));
+    }
     if (b1 == desc->B) return from_hip(wkv7::launch_bwd(g1, 16, stages, s));
     const wkv7::BwdArgs g2 = slice(desc, b1, desc->B - b1, r, w, k, v, a, b, s0, dy, dsT, tape,
                                    dr, dw, dk, dv, da, db, ds0, ws, 1);

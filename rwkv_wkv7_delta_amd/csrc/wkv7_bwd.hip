@@ -31,6 +31,7 @@
 //     per-key gradient, from pass 1's dX and dS and the forward's tape (entry
 //     states S0 and read-outs Z).
 
+#include "wkv7.h"
 #include "wkv7_device.h"
 #include "wkv7_internal.h"
 #include "wkv7_mfma.h"
@@ -107,6 +108,61 @@ struct __align__(16) P1Smem {
     bf16_t dSs[2][N][kRow];       // the adjoint leaving the chunk as [j][i] (kept per 32 tokens)
 };
 
+// Segments in time (nseg >= 2; every head split): the adjoint is affine in
+// itself, dS_left = dS_right P + H over a segment (rows of dS evolve
+// independently given the chunk factors), with P the run from the identity
+// with dy = 0 and H the run from zero with the real dy.  Segments are numbered
+// from the end (s' = nseg - 1 - s), so that the composition of the entry
+// adjoints has the forward's form (seg_combine_kernel, the same layout of 3
+// nseg states per head: entry adjoints at s', H at nseg + s', P at 2 nseg + s').
+//   pass 0: the last segment from dsT with its outputs (its left-edge adjoint
+//           to entry slot 1), and the two map runs of every middle segment;
+//   pass 1: segments s' = 1 .. nseg-1 from their entry adjoints, with outputs
+//           (the first segment's left-edge adjoint is ds0).
+// nseg = 1: one workgroup per head over the whole sequence.
+struct ChainWork {
+    int bh, c_lo, c_hi;   // chunks [c_lo, c_hi), run from the last down
+    const float* init;    // the adjoint at the right edge (else the identity when ident, else 0)
+    float* fin;           // where the adjoint at the left edge goes (or null)
+    bool ident, dyzero, outs;
+};
+__device__ __forceinline__ ChainWork chain_work(int blk, int nblk_grid, int nch, int pass, int nseg,
+                                                int seg_chunks, const float* dsT, float* ds0,
+                                                float* states, size_t NN) {
+    ChainWork cw{0, 0, nch, nullptr, nullptr, false, false, true};
+    if (nseg <= 1) {
+        cw.bh = spread_heads(blk, nblk_grid);
+        cw.init = dsT ? dsT + (size_t)cw.bh * NN : nullptr;
+        cw.fin = ds0 ? ds0 + (size_t)cw.bh * NN : nullptr;
+        return cw;
+    }
+    const int per = pass == 0 ? 2 * nseg - 3 : nseg - 1;
+    const int hs = blk / per, rr = blk % per;
+    float* const hst = states + (size_t)hs * 3 * nseg * NN;
+    cw.bh = hs;
+    if (pass == 0 && rr == 0) {   // the last segment, for real
+        cw.c_lo = (nseg - 1) * seg_chunks;
+        cw.init = dsT ? dsT + (size_t)hs * NN : nullptr;
+        cw.fin = hst + NN;
+        return cw;
+    }
+    const int sp = pass == 0 ? 1 + (rr - 1) / 2 : 1 + rr;   // s'
+    const int sg = nseg - 1 - sp;                            // s
+    cw.c_lo = sg * seg_chunks;
+    cw.c_hi = cw.c_lo + seg_chunks;
+    if (pass == 0) {
+        const bool pm = ((rr - 1) & 1) != 0;   // the P run
+        cw.ident = pm;
+        cw.dyzero = pm;
+        cw.outs = false;
+        cw.fin = hst + (size_t)((pm ? 2 : 1) * nseg + sp) * NN;
+    } else {
+        cw.init = hst + (size_t)sp * NN;
+        cw.fin = (sg == 0 && ds0) ? ds0 + (size_t)hs * NN : nullptr;
+    }
+    return cw;
+}
+
 // kAB = false: a = b = 0 (decay-only recurrence); a and b are not read and
 // stand as zero rows, so the removal terms vanish from every product.
 template <int N, bool kAB>
@@ -115,7 +171,7 @@ __global__ __launch_bounds__(kP1Threads<N>, N == 32 ? 2 : 1) void bwd_chain_kern
     const bf16_t* __restrict__ k, const bf16_t* __restrict__ a, const bf16_t* __restrict__ b,
     const bf16_t* __restrict__ dy, const float* __restrict__ dsT, bf16_t* __restrict__ dv,
     float* __restrict__ ds0, bf16_t* __restrict__ wdX, bf16_t* __restrict__ wdS,
-    int* __restrict__ counter) {
+    int* __restrict__ counter, int pass, int nseg, int seg_chunks, float* __restrict__ states) {
     // (these hide the file-scope N = 64 constants in the body below)
     constexpr int kN = N, kRow = kRowOf<N>;
     constexpr int kP = N / 16;                  // producer (and consumer) waves
@@ -123,8 +179,12 @@ __global__ __launch_bounds__(kP1Threads<N>, N == 32 ? 2 : 1) void bwd_chain_kern
     using P1Slot = wkv7::P1Slot<N>;
     using P1SlotBK = wkv7::P1SlotBK<N>;
     __shared__ P1Smem<N> sm;
-    const int bh = spread_heads(blockIdx.x, gridDim.x);
+    const int nch = (T + kL - 1) / kL;
+    const ChainWork cw = chain_work(blockIdx.x, gridDim.x, nch, pass, nseg, seg_chunks, dsT, ds0,
+                                    states, (size_t)kN * kN);
+    const int bh = cw.bh;
     const int bb = bh / H, hh = bh % H;
+    const int c_lo = cw.c_lo;
     const int tid = threadIdx.x;
     // Roles split by wave (the tests are uniform within a wave).  They are left
     // as per-lane conditions: branching on an SGPR copy of the wave index
@@ -137,14 +197,14 @@ __global__ __launch_bounds__(kP1Threads<N>, N == 32 ? 2 : 1) void bwd_chain_kern
     const int lane = tid & 63, wp = (tid >> 6) & (kP - 1);
     const int l16 = lane & 15, g = lane >> 4;
     const int col = 16 * wp + l16;
-    const int nch = (T + kL - 1) / kL;
     // wdX: [B][T][H][N]; wdS: [B][H][nblk][N][N]
     const int nblk = (nch + 1) / 2;
     // The adjoint leaving a 32-token block: after chunk c when c is odd or the last.
-    auto keeps_dS = [&](int c) __attribute__((always_inline)) { return c >= 0 && ((c & 1) || c == nch - 1); };
-    // Interval it handles chunks from the last one down; negative chunk
-    // indices are all-padding, for which every stage is the identity.
-    auto chunk_of = [&](int it) __attribute__((always_inline)) { return nch - 1 - it; };
+    auto keeps_dS = [&](int c) __attribute__((always_inline)) { return c >= c_lo && ((c & 1) || c == nch - 1); };
+    // Interval it handles chunks from the last one of the range down; chunks
+    // below c_lo (negative ones too) are all-padding, for which every stage is
+    // the identity.
+    auto chunk_of = [&](int it) __attribute__((always_inline)) { return cw.c_hi - 1 - it; };
     // (negative chunk indices in the padding intervals: two's complement & keeps
     // them in range)
     auto slot_of = [&](int c) __attribute__((always_inline)) { return c & (kP1Slots - 1); };
@@ -159,8 +219,13 @@ __global__ __launch_bounds__(kP1Threads<N>, N == 32 ? 2 : 1) void bwd_chain_kern
     f32x4 dSt[JT];
 #pragma unroll
     for (int jt = 0; jt < JT; ++jt) dSt[jt] = zero4();
-    if (consumer && dsT) {
-        const float* base = dsT + ((size_t)bh * kN + col) * kN;
+    if (consumer && cw.ident) {
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) dSt[jt][q] = col == 16 * jt + 4 * g + q ? 1.f : 0.f;
+    } else if (consumer && cw.init) {
+        const float* base = cw.init + (size_t)col * kN;
 #pragma unroll
         for (int jt = 0; jt < JT; ++jt) {
             const float4 x = *reinterpret_cast<const float4*>(base + 16 * jt + 4 * g);
@@ -190,14 +255,14 @@ __global__ __launch_bounds__(kP1Threads<N>, N == 32 ? 2 : 1) void bwd_chain_kern
         }
     };
     auto stash_raw = [&](int c, const Raw& o) __attribute__((always_inline)) {
-        if (c >= 0 && (c + 1) * kL <= T) {   // a whole chunk (the common case: no selects)
+        if (c >= c_lo && (c + 1) * kL <= T) {   // a whole chunk (the common case: no selects)
 #pragma unroll
             for (int p = 0; p < 3; ++p)
                 *reinterpret_cast<u32x4*>(&sm.raw[c & 1][2 * p + (hi ? 1 : 0)][ld_t][ld_c8 * 8]) = o.x[p];
             return;
         }
         const int t = c * kL + ld_t;
-        const bool ok = c >= 0 && t < T;
+        const bool ok = c >= c_lo && t < T;
 #pragma unroll
         for (int p = 0; p < 3; ++p) {
             const unsigned pad = (p == 0 && hi) ? 0x3F803F80u : 0u;   // padding: w = 1
@@ -259,7 +324,7 @@ __global__ __launch_bounds__(kP1Threads<N>, N == 32 ? 2 : 1) void bwd_chain_kern
         *reinterpret_cast<bf16x4*>(&bk.Kh[l16][j0]) = cvt4(kh4);
         if (kAB) *reinterpret_cast<bf16x4*>(&s.Bb[l16][j0]) = cvt4(bb4);
         *reinterpret_cast<bf16x4*>(&s.Kb[l16][j0]) = cvt4(kb4);
-        *reinterpret_cast<uint2*>(&s.dY[l16][j0]) = raw6[P1_DY];
+        *reinterpret_cast<uint2*>(&s.dY[l16][j0]) = cw.dyzero ? make_uint2(0u, 0u) : raw6[P1_DY];
         if (l16 == kL - 1) *reinterpret_cast<float4*>(&s.gL[16 * g + 4 * wp]) = make_float4(gt[0], gt[1], gt[2], gt[3]);
     };
 
@@ -432,7 +497,7 @@ __global__ __launch_bounds__(kP1Threads<N>, N == 32 ? 2 : 1) void bwd_chain_kern
     // N/8 consecutive threads write one row (128 bytes at N = 64) with 16-byte
     // stores: threads 0 .. 2N-1 dv, 2N .. 4N-1 dX.
     auto store_out = [&](int c) __attribute__((always_inline)) {
-        if (c < 0) return;
+        if (c < c_lo || !cw.outs) return;
         const int sb = c & 1;
         const int row = (rtid / (kN / 8)) & 15, piece = rtid & (kN / 8 - 1);
         const int tt = c * kL + row;
@@ -453,10 +518,10 @@ __global__ __launch_bounds__(kP1Threads<N>, N == 32 ? 2 : 1) void bwd_chain_kern
     };
 
     {
-        // Intervals 0 .. nch+3 carry real work; the count is rounded up to a
-        // multiple of three for the unrolled producer loop.  The extra intervals
-        // see only all-padding chunks (negative indices: identity, nothing stored).
-        const int n_it = (nch + 6) / 3 * 3;
+        // Intervals 0 .. (c_hi - c_lo)+3 carry real work; the count is rounded up
+        // to a multiple of three for the unrolled producer loop.  The extra
+        // intervals see only all-padding chunks (identity, nothing stored).
+        const int n_it = (cw.c_hi - c_lo + 6) / 3 * 3;
         // Each role runs its own loop over the same number of intervals (one
         // barrier each), so the compiler sees only loads on the producer side
         // and only stores on the consumer side; with both kinds in one loop it
@@ -531,8 +596,8 @@ __global__ __launch_bounds__(kP1Threads<N>, N == 32 ? 2 : 1) void bwd_chain_kern
         }
     }
 
-    if (ds0 && consumer) {
-        float* dst = ds0 + ((size_t)bh * kN + col) * kN;
+    if (cw.fin && consumer) {
+        float* dst = cw.fin + (size_t)col * kN;
 #pragma unroll
         for (int jt = 0; jt < JT; ++jt)
             *reinterpret_cast<float4*>(dst + 16 * jt + 4 * g) =
@@ -1018,11 +1083,25 @@ hipError_t launch_bwd_n(const BwdArgs& p, int stages, hipStream_t stream) {
     const bf16_t* dy = static_cast<const bf16_t*>(p.dy);
     if (stages & BWD_CHAIN) {
         auto chain = a ? bwd_chain_kernel<N, true> : bwd_chain_kernel<N, false>;
-        chain<<<dim3(p.B * p.H), dim3(kP1Threads<N>), 0, stream>>>(
-            p.T, p.H, r, w, k, a, b, dy, p.dsT, static_cast<bf16_t*>(p.dv), p.ds0,
-            static_cast<bf16_t*>(p.workX), static_cast<bf16_t*>(p.workS), p.counter);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        const int nbh = p.B * p.H;
+        auto run = [&](int pass, int grid) {
+            chain<<<dim3(grid), dim3(kP1Threads<N>), 0, stream>>>(
+                p.T, p.H, r, w, k, a, b, dy, p.dsT, static_cast<bf16_t*>(p.dv), p.ds0,
+                static_cast<bf16_t*>(p.workX), static_cast<bf16_t*>(p.workS), p.counter, pass,
+                p.nseg, p.seg_len / kL, p.states);
+            return hipGetLastError();
+        };
+        if (p.nseg <= 1) {
+            const hipError_t e = run(0, nbh);
+            if (e != hipSuccess) return e;
+        } else {
+            hipError_t e = run(0, nbh * (2 * p.nseg - 3));
+            if (e == hipSuccess && p.nseg > 2)
+                e = N == 64 ? launch_seg_combine(nbh, p.nseg, p.states, stream)
+                            : launch_seg_combine_n(N, nbh, p.nseg, p.states, stream);
+            if (e == hipSuccess) e = run(1, nbh * (p.nseg - 1));
+            if (e != hipSuccess) return e;
+        }
     }
     if (!(stages & BWD_KEYS)) return hipSuccess;
     const int nch = (p.T + kL - 1) / kL;
@@ -1042,6 +1121,10 @@ hipError_t launch_bwd_n(const BwdArgs& p, int stages, hipStream_t stream) {
 
 hipError_t launch_bwd(const BwdArgs& p, int chunk_len, int stages, hipStream_t stream) {
     if (chunk_len != kL || !p.bf16) return hipErrorInvalidValue;
+    if (p.nseg > 1 && (p.seg_len <= 0 || p.seg_len % WKV7_TAPE_BLOCK != 0 || !p.states ||
+                       (long long)(p.nseg - 1) * p.seg_len >= p.T ||
+                       (long long)p.B * p.H * (2 * p.nseg - 3) > INT32_MAX))
+        return hipErrorInvalidValue;
     switch (p.N) {
         case 32: return launch_bwd_n<32>(p, stages, stream);
         case 64: return launch_bwd_n<64>(p, stages, stream);

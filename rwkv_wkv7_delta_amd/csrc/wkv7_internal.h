@@ -33,6 +33,11 @@ struct BwdArgs {
     void* workS;       // adjoint leaving every 32-token block [B][H][nblk][N][N] bf16
     int* counter;      // two ints: the per-key pass's block queue (reset by both passes)
     int N = 64;        // head size: 32 or 64
+    // The adjoint chain in time segments (nseg >= 2, every head): segments of
+    // seg_len tokens (a multiple of 32; the last takes the rest) composed by
+    // maps; `states` holds 3 * nseg fp32 N x N states per head.  nseg = 1: none.
+    int nseg = 1, seg_len = 0;
+    float* states = nullptr;
 };
 
 // The sequential reverse pass: one workgroup per head over its fp32 checkpoints.

@@ -86,9 +86,12 @@ def test_graph_split_forward_static_scratch(wk):
     _check_replays(torch, g, outs, ref, "split forward, static scratch")
 
 
-def test_graph_chunked_backward(wk):
+@pytest.mark.parametrize("T", [150, 640])
+def test_graph_chunked_backward(wk, T):
+    """T = 640 with 8 heads: the adjoint chain in time segments (two launches
+    and the composition of the entry adjoints between them)."""
     import torch
-    B, T, H = 2, 150, 4
+    B, H = 2, 4
     ins, s0, dy = _inputs(B, T, H, 64, "bf16", 803)
     _, _, tape = wk.forward(*ins, s0, chunk_len=16, want_tape=True)
     d = wk.make_desc(B, T, H, 64, wk.WKV7_BF16, 16)
