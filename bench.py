@@ -653,6 +653,28 @@ def secondary(torch, wk, dev):
                               "alg_GBs": round(nbytes / ms / 1e6, 1),
                               "frac_hbm": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
     del ins, s0, y
+    # The chunked forward at head size 128: the 1.5B model's channels as 16
+    # heads of 128 (each head's rows over two workgroups), 40 heads of 128
+    # (320 heads: one workgroup per head), and the 0.19B token shape (48 heads,
+    # beside the scan's line at N = 128).
+    n128 = {}
+    for name, (B, T, H) in (("1.5b_width", (8, 4096, 16)), ("h40", (8, 4096, 40)),
+                            ("0.19b_tokens", (4, 1024, 12))):
+        ins = _dev_inputs(torch, (B, T, H, 128), dev, 3)
+        s0 = 0.1 * torch.randn(B, H, 128, 128, device=dev)
+        y = torch.empty_like(ins[0])
+        fn = lambda: wk.forward(*ins, s0, chunk_len=16, out=y)
+        for _ in range(3):
+            fn()
+        ms = float(np.median([_time(torch, fn, 4) for _ in range(10)]))
+        nbytes = B * T * H * 7 * 128 * 2 + 2 * B * H * 128 * 128 * 4
+        n128[name] = {"B": B, "T": T, "H": H, "ms": round(ms, 4),
+                      "tokens_per_s": round(B * T / ms * 1e3, 1),
+                      "alg_GBs": round(nbytes / ms / 1e6, 1),
+                      "frac_hbm": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
+        del ins, s0, y
+    res["chunked_fwd_n128"] = {"workload": "N=128 bf16, s0~0.1N(0,1), L=16, returns sT (median of "
+                                           "10 repetitions of 4 calls)", **n128}
     # The step after the read-out (current-token term, per-head normalisation,
     # gate) at the 2.9B-model shape: on its own (HBM-bound: y, r, k, v, g read,
     # the result written, 6 x 128 bytes per token-head), and after the chunked

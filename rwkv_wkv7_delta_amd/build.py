@@ -21,7 +21,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["wkv7_api.cpp", "wkv7_seq.hip", "wkv7_chunk_fwd.hip", "wkv7_bwd.hip", "wkv7_static.hip",
-           "wkv7_epilogue.hip"]
+           "wkv7_epilogue.hip", "wkv7_chunk128.hip"]
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

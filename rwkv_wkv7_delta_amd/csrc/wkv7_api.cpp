@@ -24,8 +24,8 @@ int check_desc(const wkv7_desc* d) {
     if (!d) return WKV7_ERR_INVALID_ARG;
     if (d->B < 0 || d->T < 0 || d->H < 0 || d->N < 0) return WKV7_ERR_INVALID_ARG;
     if (d->N != 32 && d->N != 64 && d->N != 128) return WKV7_ERR_UNSUPPORTED;
-    // The chunked forms run N = 32 and 64.
-    if (d->chunk_len != 0 && d->N != 32 && d->N != WKV7_HEAD_SIZE) return WKV7_ERR_UNSUPPORTED;
+    // Every form takes N = 32, 64 and 128, except the chunked backward (N = 32,
+    // 64: run_backward) and the chunked forward's tape and time split at N = 128.
     if (d->dtype != WKV7_F32 && d->dtype != WKV7_BF16) return WKV7_ERR_UNSUPPORTED;
     if (d->chunk_len != 0 && d->chunk_len != 16) return WKV7_ERR_UNSUPPORTED;
     // The chunked form runs its products on bf16 matrix cores.
@@ -36,6 +36,10 @@ int check_desc(const wkv7_desc* d) {
     if (d->T > INT32_MAX - 64) return WKV7_ERR_UNSUPPORTED;
     return WKV7_OK;
 }
+
+// The chunked form at N = 128 writes no tape, has no chunked backward and no
+// time split: one kernel whose heads split by value rows instead.
+bool no_tape(const wkv7_desc* d) { return d->chunk_len != 0 && d->N == 128; }
 
 // Tape: bf16 removal read-outs [B][T][H][N], then the bf16 state entering every
 // 32-token block [B][H][ceil(T/32)][N][N].  The backward's own scratch (dX, and
@@ -125,7 +129,8 @@ SplitPlan plan_split(const wkv7_desc* d, int segments, int ncu) {
     const SplitPlan none{nbh, 1, d->T, 0};
     // The scan (chunk_len 0) splits by maps only.
     const bool scan = d->chunk_len == 0;
-    if (nbh == 0 || d->T == 0 || segments == 1 || segments == -1 || (scan && segments < 0))
+    if (nbh == 0 || d->T == 0 || segments == 1 || segments == -1 || (scan && segments < 0) ||
+        no_tape(d))
         return none;
     int from = 0, nseg = segments, mode = 0;
     if (segments < 0) {
@@ -213,6 +218,15 @@ int run_forward(const wkv7_desc* d, const void* r, const void* w, const void* k,
     wkv7::FwdArgs p{d->B, d->T, d->H, d->N, d->dtype == WKV7_BF16, r, w, k, v, a, b, s0, y, sT, tape};
     p.ckpt = ckpt;
     if (d->chunk_len == 0) return from_hip(wkv7::launch_seq_fwd(p, stream));
+    if (d->N == 128) {
+        // No tape at N = 128 (the chunked backward takes N = 32 and 64).  Each
+        // head's rows over two workgroups of four waves while the heads do not
+        // fill the device, else one workgroup of eight waves per head.
+        if (tape) return WKV7_ERR_UNSUPPORTED;
+        const int ncu = device_cus();
+        const int waves = ncu > 0 && (int64_t)d->B * d->H >= ncu ? 8 : 4;
+        return from_hip(wkv7::launch_chunk_fwd128(p, waves, stream));
+    }
     return from_hip(wkv7::launch_chunk_fwd(p, d->chunk_len, stream));
 }
 
@@ -254,7 +268,7 @@ const char* wkv7_status_string(int status) {
 }
 
 size_t wkv7_tape_bytes(const wkv7_desc* desc) {
-    if (check_desc(desc) != WKV7_OK) return 0;
+    if (check_desc(desc) != WKV7_OK || no_tape(desc)) return 0;
     return tape_bytes_unchecked(desc);
 }
 
@@ -266,7 +280,7 @@ size_t wkv7_ckpt_bytes(const wkv7_desc* desc) {
 size_t wkv7_backward_workspace_bytes(const wkv7_desc* desc, int with_tape) {
     if (check_desc(desc) != WKV7_OK) return 0;
     if (desc->chunk_len == 0) return seq_ckpt_bytes(desc);
-    if (desc->dtype != WKV7_BF16) return 0;
+    if (desc->dtype != WKV7_BF16 || no_tape(desc)) return 0;
     return bwd_workspace_bytes(desc, with_tape != 0, plan_bwd(desc));
 }
 
@@ -307,6 +321,7 @@ int wkv7_forward_split_plan(const wkv7_desc* desc, int32_t segments, wkv7_split_
     if (st != WKV7_OK) return st;
     if (plan == nullptr || segments < -kMaxSegments) return WKV7_ERR_INVALID_ARG;
     if (desc->chunk_len == 0 && segments < -1) return WKV7_ERR_UNSUPPORTED;
+    if (no_tape(desc) && (segments > 1 || segments < -1)) return WKV7_ERR_UNSUPPORTED;
     const SplitPlan p = plan_split(desc, segments, segments == 0 ? device_cus() : 0);
     plan->kind = p.nseg < 2 ? WKV7_SPLIT_NONE : p.mode == 1 ? WKV7_SPLIT_SEQUENTIAL : WKV7_SPLIT_MAPS;
     plan->split_from = p.split_from;
@@ -329,7 +344,7 @@ int run_forward_split(const wkv7_desc* desc, const void* r, const void* w, const
     if (st != WKV7_OK) return st;
     if (segments < -kMaxSegments) return WKV7_ERR_INVALID_ARG;
     if (desc->chunk_len == 0 ? segments < -1
-                             : (segments > 1 || segments < -1) && desc->chunk_len != 16)
+                             : (segments > 1 || segments < -1) && (desc->chunk_len != 16 || no_tape(desc)))
         return WKV7_ERR_UNSUPPORTED;
     const bool has_tokens = (int64_t)desc->B * desc->T * desc->H > 0;
     if (has_tokens && !(req(r) && req(w) && req(k) && req(v) && pair(a, b) && req(y)))
@@ -424,7 +439,7 @@ int run_backward(const wkv7_desc* desc, const void* r, const void* w, const void
     // The chunked adjoint runs on bf16 matrix cores at N = 32 and 64; the
     // sequential reverse pass (chunk_len = 0) takes either dtype and N = 32, 64,
     // 128, and has no separate stages.
-    if (!seq && desc->dtype != WKV7_BF16) return WKV7_ERR_UNSUPPORTED;
+    if (!seq && (desc->dtype != WKV7_BF16 || no_tape(desc))) return WKV7_ERR_UNSUPPORTED;
     if (seq && stages != (wkv7::BWD_CHAIN | wkv7::BWD_KEYS)) return WKV7_ERR_UNSUPPORTED;
     if ((int64_t)desc->B * desc->H * (((int64_t)desc->T + WKV7_TAPE_CHUNK - 1) / WKV7_TAPE_CHUNK) > INT32_MAX)
         return WKV7_ERR_UNSUPPORTED;

@@ -108,8 +108,9 @@ def test_forward_ckpt_validation(L):
     assert f(None, *[FAKE] * 6, None, FAKE, None, FAKE, None) == wk.WKV7_ERR_INVALID_ARG
     assert f(ctypes.byref(d), *[FAKE] * 6, None, FAKE, None, FAKE + 8, None) == wk.WKV7_ERR_INVALID_ARG
     assert f(ctypes.byref(d), *[FAKE] * 6, None, None, None, FAKE, None) == wk.WKV7_ERR_INVALID_ARG
-    assert f(ctypes.byref(wk.make_desc(1, 8, 1, 128, wk.WKV7_BF16, 16)), *[FAKE] * 6, None, FAKE,
-             None, FAKE, None) == wk.WKV7_ERR_UNSUPPORTED
+    # the chunked form at N = 128 writes checkpoints too: validated like the others
+    assert f(ctypes.byref(wk.make_desc(1, 8, 1, 128, wk.WKV7_BF16, 16)), *[FAKE] * 6, None, None,
+             None, FAKE, None) == wk.WKV7_ERR_INVALID_ARG
     assert f(ctypes.byref(wk.make_desc(0, 8, 1, 64, wk.WKV7_BF16, 16)), *[FAKE] * 6, None, FAKE,
              None, FAKE, None) == wk.WKV7_OK
 
@@ -125,8 +126,13 @@ def _fwd(L, d, ptrs=None, y=FAKE):
 def test_forward_validation(L):
     assert L.wkv7_forward(None, *[FAKE] * 6, None, FAKE, None, None, None) == wk.WKV7_ERR_INVALID_ARG
     assert _fwd(L, wk.make_desc(1, 8, 1, 48, wk.WKV7_BF16, 0)) == wk.WKV7_ERR_UNSUPPORTED
-    # N = 128: the sequential scan only (the chunked forward runs N = 32 and 64).
-    assert _fwd(L, wk.make_desc(1, 8, 1, 128, wk.WKV7_BF16, 16)) == wk.WKV7_ERR_UNSUPPORTED
+    # N = 128, chunked: no tape (the chunked backward runs N = 32 and 64), checked
+    # before anything is launched; y is required as everywhere.
+    d128 = wk.make_desc(1, 8, 1, 128, wk.WKV7_BF16, 16)
+    assert L.wkv7_forward(ctypes.byref(d128), *[FAKE] * 6, None, FAKE, None, FAKE, None) == \
+        wk.WKV7_ERR_UNSUPPORTED
+    assert _fwd(L, d128, y=None) == wk.WKV7_ERR_INVALID_ARG
+    assert wk.tape_bytes(d128) == 0
     assert _fwd(L, wk.make_desc(1, 8, 1, 32, wk.WKV7_F32, 16)) == wk.WKV7_ERR_UNSUPPORTED
     assert _fwd(L, wk.make_desc(1, 8, 1, 128, wk.WKV7_BF16, 0), y=None) == wk.WKV7_ERR_INVALID_ARG
     assert _fwd(L, wk.make_desc(0, 8, 1, 32, wk.WKV7_BF16, 0)) == wk.WKV7_OK
@@ -410,7 +416,7 @@ def test_forward_epilogue_validation(L):
     assert f(ctypes.byref(wk.make_desc(1, 32, 2, 64, wk.WKV7_F32, 16)), *ins, None,
              ctypes.byref(ok), FAKE, None, None) == wk.WKV7_ERR_UNSUPPORTED
     assert f(ctypes.byref(wk.make_desc(1, 32, 2, 128, wk.WKV7_BF16, 16)), *ins, None,
-             ctypes.byref(ok), FAKE, None, None) == wk.WKV7_ERR_UNSUPPORTED
+             ctypes.byref(ok), None, None, None) == wk.WKV7_ERR_INVALID_ARG   # out, at N = 128 too
     assert f(ctypes.byref(d), *ins[:6], FAKE + 4, None, ctypes.byref(ok), FAKE, None, None) == \
         wk.WKV7_ERR_INVALID_ARG   # misaligned s0
     assert f(ctypes.byref(wk.make_desc(0, 32, 2, 64, wk.WKV7_BF16, 16)), *[None] * 8,
