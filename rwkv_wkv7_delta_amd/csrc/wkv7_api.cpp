@@ -219,13 +219,9 @@ int run_forward(const wkv7_desc* d, const void* r, const void* w, const void* k,
     p.ckpt = ckpt;
     if (d->chunk_len == 0) return from_hip(wkv7::launch_seq_fwd(p, stream));
     if (d->N == 128) {
-        // No tape at N = 128 (the chunked backward takes N = 32 and 64).  Each
-        // head's rows over two workgroups of four waves while the heads do not
-        // fill the device, else one workgroup of eight waves per head.
+        // No tape at N = 128 (the chunked backward takes N = 32 and 64).
         if (tape) return WKV7_ERR_UNSUPPORTED;
-        const int ncu = device_cus();
-        const int waves = ncu > 0 && (int64_t)d->B * d->H >= ncu ? 8 : 4;
-        return from_hip(wkv7::launch_chunk_fwd128(p, waves, stream));
+        return from_hip(wkv7::launch_chunk_fwd128(p, stream));
     }
     return from_hip(wkv7::launch_chunk_fwd(p, d->chunk_len, stream));
 }
