@@ -391,6 +391,9 @@ __global__ __launch_bounds__(kThreads128, 1) void chunk128_fwd_kernel(
             // the whole memory counter (and so on the chunks' stores)
             __builtin_amdgcn_s_waitcnt(0);
         }
+        // the state chain and the inverse wave issue before the producers
+        // when several waves of a SIMD are ready
+        __builtin_amdgcn_s_setprio(3);
         __syncthreads();
         for (int i = 0; i < nch + 2; ++i) {
             store_y(i - 3);
@@ -422,6 +425,7 @@ __global__ __launch_bounds__(kThreads128, 1) void chunk128_fwd_kernel(
         }
     } else {
         // ---- the inverse wave: chunk i-1's inverse in interval i
+        __builtin_amdgcn_s_setprio(3);
         __syncthreads();
         for (int i = 0; i < nch + 2; ++i) {
             if (kAB) stage_inverse(i - 1);
