@@ -73,10 +73,12 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run one plain 1 GiB device copy (for scaling HBM counters)")
-    p.add_argument("--workload", choices=("step", "chunked_fwd_1.5b", "sequential_bwd_2.9b"),
+    p.add_argument("--workload", choices=("step", "chunked_fwd_1.5b", "chunked_fwd_n128",
+                                          "sequential_bwd_2.9b"),
                    default="step",
                    help="chunked_fwd_1.5b: time only the chunked forward at the 1.5B-model shape "
-                        "(the line under secondary) and print it; sequential_bwd_2.9b: the "
+                        "(the line under secondary) and print it; chunked_fwd_n128: the same "
+                        "at N = 128 over the 1.5B model's channels (H = 16); sequential_bwd_2.9b: the "
                         "sequential reverse pass (checkpointing scan + adjoint) at the 2.9B-model "
                         "shape in bf16, two calls (for counter runs)")
     p.add_argument("--summarize-sq", nargs=5,
@@ -364,6 +366,28 @@ def chunked_fwd_15b(torch, wk, dev, reps=25, calls=4):
             "frac_hbm": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
 
 
+def chunked_fwd_n128(torch, wk, dev, reps=25, calls=4):
+    """The chunked forward at head size 128 over the 1.5B model's channels
+    (B=8, T=4096, H=16 heads of 128, s0 ~ 0.1 N(0,1), final state returned),
+    timed as chunked_fwd_15b times the N = 64 shape."""
+    B, T, H, N = 8, 4096, 16, 128
+    ins = _dev_inputs(torch, (B, T, H, N), dev, 3)
+    s0 = 0.1 * torch.randn(B, H, N, N, device=dev)
+    y = torch.empty_like(ins[0])
+    fn = lambda: wk.forward(*ins, s0, chunk_len=16, out=y)
+    for _ in range(3):
+        fn()
+    t = np.array([_time(torch, fn, calls) for _ in range(reps)])
+    ms = float(np.median(t))
+    nbytes = B * T * H * 7 * N * 2 + 2 * B * H * N * N * 4
+    return {"workload": "B=8 T=4096 H=16 N=128 bf16, s0~0.1N(0,1), L=16, returns sT",
+            "reps": reps, "calls_per_rep": calls, "ms": round(ms, 4),
+            "ms_p10_p90": [round(float(np.percentile(t, 10)), 4), round(float(np.percentile(t, 90)), 4)],
+            "tokens_per_s": round(B * T / ms * 1e3, 1),
+            "alg_GBs": round(nbytes / ms / 1e6, 1),
+            "frac_hbm": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
+
+
 def sequential_bwd_29b(torch, wk, dev, calls=2):
     """The sequential reverse pass (chunk_len = 0: the checkpointing scan, then
     the adjoint) at the 2.9B-model shape in bf16, zero s0, dy ~ N(0,1), no ds0:
@@ -414,6 +438,10 @@ def main():
     dev = torch.device("cuda:0")
     if args.workload == "chunked_fwd_1.5b":
         print(json.dumps({"workload": "chunked_fwd_1.5b", **chunked_fwd_15b(torch, wk, dev)}),
+              flush=True)
+        return
+    if args.workload == "chunked_fwd_n128":
+        print(json.dumps({"workload": "chunked_fwd_n128", **chunked_fwd_n128(torch, wk, dev)}),
               flush=True)
         return
     if args.workload == "sequential_bwd_2.9b":
@@ -657,9 +685,8 @@ def secondary(torch, wk, dev):
     # heads of 128 (each head's rows over two workgroups), 40 heads of 128
     # (320 heads: one workgroup per head), and the 0.19B token shape (48 heads,
     # beside the scan's line at N = 128).
-    n128 = {}
-    for name, (B, T, H) in (("1.5b_width", (8, 4096, 16)), ("h40", (8, 4096, 40)),
-                            ("0.19b_tokens", (4, 1024, 12))):
+    n128 = {"1.5b_width": chunked_fwd_n128(torch, wk, dev)}
+    for name, (B, T, H) in (("h40", (8, 4096, 40)), ("0.19b_tokens", (4, 1024, 12))):
         ins = _dev_inputs(torch, (B, T, H, 128), dev, 3)
         s0 = 0.1 * torch.randn(B, H, 128, 128, device=dev)
         y = torch.empty_like(ins[0])
@@ -673,8 +700,9 @@ def secondary(torch, wk, dev):
                       "alg_GBs": round(nbytes / ms / 1e6, 1),
                       "frac_hbm": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
         del ins, s0, y
-    res["chunked_fwd_n128"] = {"workload": "N=128 bf16, s0~0.1N(0,1), L=16, returns sT (median of "
-                                           "10 repetitions of 4 calls)", **n128}
+    res["chunked_fwd_n128"] = {"workload": "N=128 bf16, s0~0.1N(0,1), L=16, returns sT (1.5b_width: "
+                                           "median of 25 repetitions of 4 calls; the others of 10)",
+                               **n128}
     # The step after the read-out (current-token term, per-head normalisation,
     # gate) at the 2.9B-model shape: on its own (HBM-bound: y, r, k, v, g read,
     # the result written, 6 x 128 bytes per token-head), and after the chunked

@@ -67,11 +67,17 @@ extern "C" {
 
 #define WKV7_ABI_VERSION 1
 /* Head sizes: the sequential forms (chunk_len = 0: the scan and the reverse
-   pass of wkv7_backward) and the decode step take N = 32, 64 or 128 (a larger N
-   is the state expansion of "Millions of States: Designing a Scalable MoE
-   Architecture with RWKV-7 Meta-learner", Abstract); the chunked forward
-   (chunk_len = 16: wkv7_forward, _ckpt, _split, _static, _epilogue) takes N = 32
-   or WKV7_HEAD_SIZE, the chunked backward entry points N = WKV7_HEAD_SIZE. */
+   pass of wkv7_backward), the decode step and the chunked forward (chunk_len =
+   16: wkv7_forward, _ckpt, _split, _static, _epilogue) take N = 32, 64 or 128
+   (a larger N is the state expansion of "Millions of States: Designing a
+   Scalable MoE Architecture with RWKV-7 Meta-learner", Abstract); the chunked
+   backward entry points take N = 32 or WKV7_HEAD_SIZE.  At N = 128 the chunked
+   forward writes no tape (tape must be NULL, else WKV7_ERR_UNSUPPORTED) and
+   does not split in time (wkv7_forward_split: segments 0, 1 or -1 run it
+   whole; others return WKV7_ERR_UNSUPPORTED); it writes fp32 checkpoints
+   (wkv7_forward_ckpt), from which wkv7_backward_ckpt (chunk_len = 0) trains.
+   It splits each head's value rows over two workgroups instead, which form
+   the chunk factors each. */
 #define WKV7_HEAD_SIZE 64
 #define WKV7_TAPE_CHUNK 16       /* tokens per chunk of the backward */
 #define WKV7_TAPE_BLOCK 32       /* tokens per state saved in the forward tape */
@@ -114,7 +120,8 @@ const char *wkv7_status_string(int status);
      S   [B][H][ceil(T/32)][N][N]  bf16: the state entering every 32-token block
                                    (tokens 32m ..), stored key-major (element
                                    [j][i] = S[i][j]).
-   0 on an invalid descriptor. */
+   0 on an invalid descriptor, and at N = 128 with chunk_len = 16 (that form
+   writes no tape). */
 size_t wkv7_tape_bytes(const wkv7_desc *desc);
 
 /* Bytes of the fp32 checkpoints that wkv7_forward_ckpt writes and the
@@ -146,7 +153,7 @@ size_t wkv7_workspace_bytes(const wkv7_desc *desc);
    itself): wkv7_ckpt_bytes(desc), whatever with_tape is (wkv7_backward_ckpt,
    which reads the caller's checkpoints, needs none).
    0 on an invalid descriptor or one the backward does not take (chunk_len = 16
-   with fp32). */
+   with fp32, or at N = 128). */
 size_t wkv7_backward_workspace_bytes(const wkv7_desc *desc, int with_tape);
 
 /*
@@ -157,7 +164,8 @@ size_t wkv7_backward_workspace_bytes(const wkv7_desc *desc, int with_tape);
  *   sT                [B][H][N][N] fp32 final state, or NULL.
  *   tape              NULL, or wkv7_tape_bytes(desc) bytes: receives the
  *                     removal read-outs and chunk entry states for
- *                     wkv7_backward (layout at wkv7_tape_bytes).
+ *                     wkv7_backward (layout at wkv7_tape_bytes).  NULL for
+ *                     the chunked form at N = 128 (else WKV7_ERR_UNSUPPORTED).
  */
 int wkv7_forward(const wkv7_desc *desc, const void *r, const void *w, const void *k,
                  const void *v, const void *a, const void *b, const float *s0, void *y,
