@@ -86,6 +86,9 @@ def parse():
                    help="turn two rocprofv3 --pmc runs of this script (SQ_COUNTERS; the step, "
                         "then --workload chunked_fwd_1.5b) into "
                         "profiles/sq_counters_fwd_bwd_2.9b.{md,json} and exit")
+    p.add_argument("--summarize-sq-n128", nargs=3, metavar=("PMC_DIRS", "REPS", "CMD"),
+                   help="turn two rocprofv3 --pmc runs of --workload chunked_fwd_n128 (SQ_COUNTERS) "
+                        "into profiles/sq_counters_chunked_fwd_n128.md and exit")
     p.add_argument("--summarize-ktrace", nargs=4, metavar=("KTRACE_DIR", "LAST_N", "CMD", "OUT"),
                    help="per-kernel durations of the last LAST_N launches of each kernel in a "
                         "rocprofv3 kernel trace, as a markdown table in OUT; then exit")
@@ -312,6 +315,34 @@ def summarize_sq(step_dir, step_steps, cfg_dir, cfg_steps, cmd):
     print("\n".join(lines))
 
 
+def summarize_sq_n128(pmc_dirs, reps, cmd):
+    """profiles/sq_counters_chunked_fwd_n128.md from the two SQ_COUNTERS passes of
+    --workload chunked_fwd_n128: the N = 128 chunked forward's timed launches."""
+    c = _sq_per_kernel(pmc_dirs, int(reps),
+                       lambda n: "chunk128_fwd_kernel" if "chunk128_fwd_kernel<true, false>" in n else None)
+    c = c["chunk128_fwd_kernel"]
+    g = lambda n: c.get(n, float("nan"))
+    busy, nlds = g("SQ_BUSY_CU_CYCLES"), g("SQ_INSTS_LDS")
+    flops = g("SQ_INSTS_VALU_MFMA_MOPS_BF16") * MOPS_FLOPS
+    lines = ["# rocprofv3 SQ counters: the chunked forward at N = 128 (B=8, T=4096, H=16)", "",
+             "Command (run from the repository root; two counter passes):", "",
+             "```", cmd, "```", "",
+             "Per dispatch, averaged over the timed launches; the ratios as in "
+             "sq_counters_fwd_bwd_2.9b.md (busy ratios summed over a compute unit's four SIMDs).", "",
+             "| kernel | MFMA GFLOP / launch | MFMA busy / CU busy | VALU insts (M) | VALU busy / CU busy | "
+             "LDS insts (M) | LDS wait / LDS inst | conflict cycles / LDS inst | GRBM_GUI_ACTIVE |",
+             "|---|---|---|---|---|---|---|---|---|",
+             f"| chunk128_fwd_kernel | {flops / 1e9:.1f} | {g('SQ_VALU_MFMA_BUSY_CYCLES') / busy:.3f} | "
+             f"{g('SQ_INSTS_VALU') / 1e6:.1f} | {g('SQ_ACTIVE_INST_VALU') / busy:.3f} | {nlds / 1e6:.1f} | "
+             f"{g('SQ_WAIT_INST_LDS') / nlds:.2f} | {g('SQ_LDS_BANK_CONFLICT') / nlds:.3f} | "
+             f"{g('GRBM_GUI_ACTIVE'):.4g} |", "",
+             "| " + " | ".join(SQ_COUNTERS) + " |", "|" + "---|" * len(SQ_COUNTERS),
+             "| " + " | ".join(f"{g(n):.4g}" for n in SQ_COUNTERS) + " |"]
+    with open(os.path.join(ROOT, "profiles", "sq_counters_chunked_fwd_n128.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def summarize_ktrace(ktrace_dir, last_n, cmd, out):
     """Per-kernel durations of the last `last_n` launches in a kernel trace."""
     last_n = int(last_n)
@@ -424,6 +455,9 @@ def main():
         return
     if args.summarize_ktrace:
         summarize_ktrace(*args.summarize_ktrace)
+        return
+    if args.summarize_sq_n128:
+        summarize_sq_n128(*args.summarize_sq_n128)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "the benchmark runs on one GPU: the kernels work on one GPU's share (B*H heads); --gpus must be 1",

@@ -73,6 +73,17 @@ def test_graph_chunked_forward_with_tape(wk):
     _check_replays(torch, g, outs, ref, "chunked forward")
 
 
+def test_graph_chunked_forward_n128_with_ckpt(wk):
+    """The chunked forward at N = 128 (two workgroups per head, their factor
+    slots in LDS) with fp32 checkpoints."""
+    import torch
+    ins, s0, _ = _inputs(2, 150, 3, 128, "bf16", 809)
+    fn = lambda: wk.forward(*ins, s0, chunk_len=16, want_ckpt=True)
+    ref = [x.clone() for x in fn() if x is not None]
+    g, outs = _capture(torch, fn)
+    _check_replays(torch, g, outs, ref, "chunked forward N = 128")
+
+
 def test_graph_split_forward_static_scratch(wk):
     """The no-allocation entry with the automatic plan on few heads (time
     segments by maps in the library's static scratch, and their composition)."""
