@@ -734,8 +734,27 @@ def secondary(torch, wk, dev):
                       "alg_GBs": round(nbytes / ms / 1e6, 1),
                       "frac_hbm": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
         del ins, s0, y
+    # few heads (B=1, T=4096, H=12: 24 workgroups unsplit), split in time by the
+    # automatic plan
+    B, T, H = 1, 4096, 12
+    ins = _dev_inputs(torch, (B, T, H, 128), dev, 4)
+    s0 = 0.1 * torch.randn(B, H, 128, 128, device=dev)
+    y = torch.empty_like(ins[0])
+    desc = wk.make_desc(B, T, H, 128, wk.WKV7_BF16, 16)
+    ws = torch.empty(max(wk.split_workspace_bytes(desc, 0) // 4, 4), device=dev)
+    few = {}
+    for name, seg in (("unsplit_ms", None), ("split_ms", 0)):
+        fn = lambda: wk.forward(*ins, s0, chunk_len=16, out=y, segments=seg, workspace=ws)
+        for _ in range(3):
+            fn()
+        few[name] = round(float(np.median([_time(torch, fn, 4) for _ in range(10)])), 4)
+    few["segments"] = int(wk.split_plan(desc, 0).nseg)
+    few["tokens_per_s"] = round(B * T / few["split_ms"] * 1e3, 1)
+    n128["12_heads_split"] = {"B": B, "T": T, "H": H, **few}
+    del ins, s0, y, ws
     res["chunked_fwd_n128"] = {"workload": "N=128 bf16, s0~0.1N(0,1), L=16, returns sT (1.5b_width: "
-                                           "median of 25 repetitions of 4 calls; the others of 10)",
+                                           "median of 25 repetitions of 4 calls; the others of 10; "
+                                           "12_heads_split: wkv7_forward_split, automatic plan)",
                                **n128}
     # The step after the read-out (current-token term, per-head normalisation,
     # gate) at the 2.9B-model shape: on its own (HBM-bound: y, r, k, v, g read,

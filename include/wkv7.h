@@ -73,11 +73,10 @@ extern "C" {
    Scalable MoE Architecture with RWKV-7 Meta-learner", Abstract); the chunked
    backward entry points take N = 32 or WKV7_HEAD_SIZE.  At N = 128 the chunked
    forward writes no tape (tape must be NULL, else WKV7_ERR_UNSUPPORTED) and
-   does not split in time (wkv7_forward_split: segments 0, 1 or -1 run it
-   whole; others return WKV7_ERR_UNSUPPORTED); it writes fp32 checkpoints
-   (wkv7_forward_ckpt), from which wkv7_backward_ckpt (chunk_len = 0) trains.
-   It splits each head's value rows over two workgroups instead, which form
-   the chunk factors each. */
+   splits in time by maps only (wkv7_forward_split: segments <= -2 return
+   WKV7_ERR_UNSUPPORTED); it writes fp32 checkpoints (wkv7_forward_ckpt), from
+   which wkv7_backward_ckpt (chunk_len = 0) trains.  It splits each head's
+   value rows over two workgroups, which form the chunk factors each. */
 #define WKV7_HEAD_SIZE 64
 #define WKV7_TAPE_CHUNK 16       /* tokens per chunk of the backward */
 #define WKV7_TAPE_BLOCK 32       /* tokens per state saved in the forward tape */
@@ -193,15 +192,17 @@ int wkv7_forward_ckpt(const wkv7_desc *desc, const void *r, const void *w, const
  *                 heads than compute units: the heads of the last, partial
  *                 round by maps when they fill at most a fifth of it; the
  *                 scan: every head by maps when B*H*N/16 workgroups fill at
- *                 most half of it, at N = 128 in at most 4 segments; else, or
+ *                 most half of it; the chunked form at N = 128: every head
+ *                 by maps when its two workgroups per head fill at most a
+ *                 third of it; at N = 128 in at most 4 segments; else, or
  *                 when T is too short for segments of 128 tokens, no split);
  *              1 or -1: no split (exactly wkv7_forward);
  *              n >= 2: every head in up to n segments by maps;
  *              n <= -2: every head in up to -n sequential segments.
  *              At most 16 segments; below -16: WKV7_ERR_INVALID_ARG.  The
- *              chunked form (chunk_len = 16) splits both ways; the sequential
- *              scan (chunk_len = 0, N = 32, 64 or 128) by maps only (n <= -2:
- *              WKV7_ERR_UNSUPPORTED).
+ *              chunked form (chunk_len = 16) at N = 32 and 64 splits both
+ *              ways; at N = 128, and the sequential scan (chunk_len = 0, N =
+ *              32, 64 or 128), by maps only (n <= -2: WKV7_ERR_UNSUPPORTED).
  *   workspace  wkv7_forward_split_workspace_bytes(desc, segments) bytes of
  *              device scratch, or NULL when that is 0; else WKV7_ERR_WORKSPACE.
  * Segments start at multiples of 32 tokens (the tape's state blocks).

@@ -38,7 +38,8 @@ int check_desc(const wkv7_desc* d) {
 }
 
 // The chunked form at N = 128 writes no tape, has no chunked backward and no
-// time split: one kernel whose heads split by value rows instead.
+// sequential segments (its heads split by value rows over two workgroups; it
+// splits in time by maps).
 bool no_tape(const wkv7_desc* d) { return d->chunk_len != 0 && d->N == 128; }
 
 // Tape: bf16 removal read-outs [B][T][H][N], then the bf16 state entering every
@@ -129,8 +130,7 @@ SplitPlan plan_split(const wkv7_desc* d, int segments, int ncu) {
     const SplitPlan none{nbh, 1, d->T, 0};
     // The scan (chunk_len 0) splits by maps only.
     const bool scan = d->chunk_len == 0;
-    if (nbh == 0 || d->T == 0 || segments == 1 || segments == -1 || (scan && segments < 0) ||
-        no_tape(d))
+    if (nbh == 0 || d->T == 0 || segments == 1 || segments == -1 || ((scan || no_tape(d)) && segments < 0))
         return none;
     int from = 0, nseg = segments, mode = 0;
     if (segments < 0) {
@@ -150,11 +150,16 @@ SplitPlan plan_split(const wkv7_desc* d, int segments, int ncu) {
         // 48 heads, 3/4 of it, segments measured no faster; at 320 heads
         // the chunked form's tail split made the scan 14 % slower).
         if (ncu <= 0) return none;
-        // The chunked form at N = 32 runs two workgroups per compute unit.
+        // The chunked form at N = 32 runs two workgroups per compute unit; at
+        // N = 128 two workgroups per head, each on a compute unit of its own
+        // (every head split when the pairs fill at most a third of the device).
         if (!scan && d->N == 32) ncu *= 2;
+        if (no_tape(d)) ncu /= 2;
         int part = nbh;
         if (scan) {
             if ((int64_t)nbh * (d->N / 16) * 2 > ncu) return none;
+        } else if (no_tape(d)) {
+            if (nbh > ncu) return none;
         } else if (nbh > ncu) {
             part = nbh % ncu;
             from = nbh - part;
@@ -162,10 +167,12 @@ SplitPlan plan_split(const wkv7_desc* d, int segments, int ncu) {
         }
         if (part == 0 || 3 * part > ncu) return none;
         nseg = (ncu / part + 3) / 2;
-        // The N = 128 scan pays more for its map runs and compositions: with 4
-        // or 12 heads 4 segments measured best (2.3x and 1.2x; 16 segments
-        // no faster than none).
-        if (scan && d->N == 128 && nseg > 4) nseg = 4;
+        // At N = 128 the map runs and the compositions cost more: with 4 or 12
+        // heads 4 segments measured best for the scan (2.3x and 1.2x; 16
+        // segments no faster than none) and about best for the chunked form
+        // (B = 1: T = 2048, H = 4 0.170 -> 0.145 ms, 16 segments 0.340; T = 4096,
+        // H = 12 0.337 -> 0.229 ms, 6 segments 0.219).
+        if (d->N == 128 && nseg > 4) nseg = 4;
         if (nseg > d->T / kMinSegmentTokens) nseg = d->T / kMinSegmentTokens;
     }
     if (nseg > kMaxSegments) nseg = kMaxSegments;
@@ -316,8 +323,7 @@ int wkv7_forward_split_plan(const wkv7_desc* desc, int32_t segments, wkv7_split_
     const int st = check_desc(desc);
     if (st != WKV7_OK) return st;
     if (plan == nullptr || segments < -kMaxSegments) return WKV7_ERR_INVALID_ARG;
-    if (desc->chunk_len == 0 && segments < -1) return WKV7_ERR_UNSUPPORTED;
-    if (no_tape(desc) && (segments > 1 || segments < -1)) return WKV7_ERR_UNSUPPORTED;
+    if ((desc->chunk_len == 0 || no_tape(desc)) && segments < -1) return WKV7_ERR_UNSUPPORTED;
     const SplitPlan p = plan_split(desc, segments, segments == 0 ? device_cus() : 0);
     plan->kind = p.nseg < 2 ? WKV7_SPLIT_NONE : p.mode == 1 ? WKV7_SPLIT_SEQUENTIAL : WKV7_SPLIT_MAPS;
     plan->split_from = p.split_from;
@@ -339,9 +345,10 @@ int run_forward_split(const wkv7_desc* desc, const void* r, const void* w, const
     const int st = check_desc(desc);
     if (st != WKV7_OK) return st;
     if (segments < -kMaxSegments) return WKV7_ERR_INVALID_ARG;
-    if (desc->chunk_len == 0 ? segments < -1
-                             : (segments > 1 || segments < -1) && (desc->chunk_len != 16 || no_tape(desc)))
+    if (desc->chunk_len == 0 || no_tape(desc) ? segments < -1
+                                              : (segments > 1 || segments < -1) && desc->chunk_len != 16)
         return WKV7_ERR_UNSUPPORTED;
+    if (no_tape(desc) && tape) return WKV7_ERR_UNSUPPORTED;
     const bool has_tokens = (int64_t)desc->B * desc->T * desc->H > 0;
     if (has_tokens && !(req(r) && req(w) && req(k) && req(v) && pair(a, b) && req(y)))
         return WKV7_ERR_INVALID_ARG;
@@ -360,6 +367,7 @@ int run_forward_split(const wkv7_desc* desc, const void* r, const void* w, const
                           r, w, k, v, a, b, s0, y, sT, tape};
     const wkv7::FwdSplit sp{plan.split_from, plan.nseg, plan.seg_len, static_cast<float*>(workspace)};
     if (desc->chunk_len == 0) return from_hip(wkv7::launch_seq_fwd_split(p, sp, s));
+    if (no_tape(desc)) return from_hip(wkv7::launch_chunk_fwd128_split(p, sp, s));
     if (plan.mode == 1) {
         float* states = static_cast<float*>(workspace);
         int* sync = reinterpret_cast<int*>(states + (size_t)desc->B * desc->H * desc->N * desc->N);

@@ -41,6 +41,11 @@
 // wkv7_mfma.h.  Chunks are padded past T (w = 1, everything else 0: the
 // identity on the state), and the chunks before the first (-2, -1) are run as
 // identities, so every loop body is the same in every interval.
+//
+// Each workgroup pair runs one item of the segment plan of the time split
+// (work_of: a whole head, or one segment of it from its entry state, or one of
+// a segment's two map runs, from the identity with v = 0 and from zero), as
+// the N = 64 form's workgroups do; a map run's rows are the rows of the map.
 
 #include "wkv7.h"
 #include "wkv7_device.h"
@@ -103,26 +108,35 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // kAB = false: a = b = 0 (no removal terms: Y = Rt S0^T + Ark V, S_L^T =
 // diag(G_L) S0^T + Kb^T V; the inverse wave idles); kCk: also the fp32 state
 // entering every chunk, [B][H][ceil(T/16)][N][N] (row = value channel).
+// nitems: the launch's items of the segment plan (two workgroups each).
 template <bool kAB, bool kCk>
 __global__ __launch_bounds__(kThreads128, 1) void chunk128_fwd_kernel(
     int B, int T, int H, const bf16_t* __restrict__ r, const bf16_t* __restrict__ w,
     const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const bf16_t* __restrict__ a,
-    const bf16_t* __restrict__ b, const float* __restrict__ s0, bf16_t* __restrict__ y,
-    float* __restrict__ sT, float* __restrict__ ckpt) {
+    const bf16_t* __restrict__ b, const float* __restrict__ s0, bf16_t* __restrict__ y_all,
+    float* __restrict__ sT, float* __restrict__ ckpt_all, int nitems, int pass, int split_from,
+    int nseg, int seg_len, float* __restrict__ states) {
     constexpr size_t NN = (size_t)kN128 * kN128;
     __shared__ Smem128 sm;
 
     // Workgroups go to the eight XCDs in turn (u to XCD u mod 8).  Groups of 8
-    // heads take 16 consecutive workgroups, part-major, so that the two parts
-    // of a head share an XCD and run at about the same time.
-    const int nbh = B * H;
+    // items take 16 consecutive workgroups, part-major, so that the two parts
+    // of an item share an XCD and run at about the same time.
     const int u = blockIdx.x;
     const int grp = u / 16, within = u % 16;
-    const int m = min(8, nbh - 8 * grp);
+    const int m = min(8, nitems - 8 * grp);
     const int part = within / m;
-    const int bh = 8 * grp + within % m;
+    const Work wk = work_of<kN128>(8 * grp + within % m, pass, T, s0, sT, split_from, nseg, seg_len, states);
+    const int bh = wk.bh;
     const int bb = bh / H, hh = bh % H;
     const int rb = part * kRows;                // first value row of this workgroup
+    // Chunks c_begin .. c_begin + nch - 1 of the sequence; tokens from t_end on
+    // are padding (t_begin is a multiple of 32).
+    const int t_end = wk.t_end, c_begin = wk.t_begin / kL;
+    const int nch = (t_end + kL - 1) / kL - c_begin;
+    const int nch_all = (T + kL - 1) / kL;      // chunks of the checkpoints' layout
+    bf16_t* const y = wk.outs ? y_all : nullptr;
+    float* const ckpt = (kCk && wk.outs) ? ckpt_all : nullptr;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     // A scalar copy of the wave index: the role branches are scalar (no
@@ -130,7 +144,6 @@ __global__ __launch_bounds__(kThreads128, 1) void chunk128_fwd_kernel(
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);
     const int l16 = lane & 15, g = lane >> 4;
     const int col = rb + 16 * (wave & 3) + l16;   // value row of this lane (state chain)
-    const int nch = (T + kL - 1) / kL;
     const bf16x4 ident = identity_b(g, l16);
 
     // ---- raw rows (producers): 6 vectors x 16 tokens x 16 pieces of 16 bytes
@@ -145,7 +158,7 @@ __global__ __launch_bounds__(kThreads128, 1) void chunk128_fwd_kernel(
         return vhi ? src6[2 * e + 1] : src6[2 * e];
     };
     auto load_raw = [&](int c, u32x4 (&o)[kPieces]) __attribute__((always_inline)) {
-        const int t = min(c * kL + ld_t, T - 1);
+        const int t = min((c_begin + c) * kL + ld_t, t_end - 1);
         const size_t off = tok_off<kN128>(bb, t, hh, T, H) + 8 * ld_c8;
 #pragma unroll
         for (int e = 0; e < kPieces; ++e) {
@@ -159,7 +172,7 @@ __global__ __launch_bounds__(kThreads128, 1) void chunk128_fwd_kernel(
         }
     };
     auto stash_raw = [&](int c, const u32x4 (&o)[kPieces]) __attribute__((always_inline)) {
-        const bool ok = c * kL + ld_t < T;
+        const bool ok = (c_begin + c) * kL + ld_t < t_end;
 #pragma unroll
         for (int e = 0; e < kPieces; ++e) {
             const int vi = 2 * e + vhi;
@@ -216,7 +229,7 @@ __global__ __launch_bounds__(kThreads128, 1) void chunk128_fwd_kernel(
         *reinterpret_cast<bf16x4*>(&s.Rt[l16][j0]) = cvt4(rt);
         *reinterpret_cast<bf16x4*>(&bk.Kh[l16][j0]) = cvt4(kh4);
         *reinterpret_cast<bf16x4*>(&s.Kb[l16][j0]) = cvt4(kb4);
-        *reinterpret_cast<uint2*>(&s.V[l16][j0]) = q6[R_V];
+        *reinterpret_cast<uint2*>(&s.V[l16][j0]) = wk.vzero ? make_uint2(0u, 0u) : q6[R_V];
         // every lane of the row holds G_L of keys j0 .. j0+3 and writes it (the
         // same 16 bytes to the same place: no branch)
         *reinterpret_cast<f32x4*>(&s.gL[64 * (cg >> 2) + 16 * g + 4 * (cg & 3)]) = gl4;
@@ -296,8 +309,8 @@ __global__ __launch_bounds__(kThreads128, 1) void chunk128_fwd_kernel(
         bf16x4 Sb[kJT];
 #pragma unroll
         for (int jt = 0; jt < kJT; ++jt) Sb[jt] = cvt4(S[jt]);
-        if (kCk && c >= 0) {   // the entry state in fp32: row col, keys 16 jt + 4 g ..
-            float* dst = ckpt + (((size_t)bh * nch + c) * kN128 + col) * kN128 + 4 * g;
+        if (kCk && ckpt && c >= 0) {   // the entry state in fp32: row col, keys 16 jt + 4 g ..
+            float* dst = ckpt + (((size_t)bh * nch_all + c_begin + c) * kN128 + col) * kN128 + 4 * g;
 #pragma unroll
             for (int jt = 0; jt < kJT; ++jt) store_stream(dst + 16 * jt, __builtin_bit_cast(uint4, S[jt]));
         }
@@ -348,10 +361,10 @@ __global__ __launch_bounds__(kThreads128, 1) void chunk128_fwd_kernel(
     // Staged read-outs of chunk c: 16 tokens x 64 values, 8 pieces of 16 bytes
     // per token, from the first 128 threads of the state chain.
     auto store_y = [&](int c) __attribute__((always_inline)) {
-        if (tid < 2 * kRows) {
+        if (y && tid < 2 * kRows) {
             const int row = tid / 8, piece = tid % 8;
-            const int tt = c * kL + row;
-            if (tt >= 0 && tt < T)
+            const int tt = (c_begin + c) * kL + row;
+            if (c >= 0 && tt < t_end)
                 store_stream(y + tok_off<kN128>(bb, tt, hh, T, H) + rb + 8 * piece,
                              *reinterpret_cast<const uint4*>(&sm.Ys[c & 1][row][8 * piece]));
         }
@@ -380,8 +393,8 @@ __global__ __launch_bounds__(kThreads128, 1) void chunk128_fwd_kernel(
 
     if (wave_s < kCons) {
         // ---- the state chain: chain(i-2) and the stores of chunk i-3 in interval i
-        if (s0) {
-            const float* base = s0 + (size_t)bh * NN + (size_t)col * kN128;
+        if (wk.init) {
+            const float* base = wk.init + (size_t)col * kN128;
 #pragma unroll
             for (int jt = 0; jt < kJT; ++jt) {
                 const float4 x = *reinterpret_cast<const float4*>(base + 16 * jt + 4 * g);
@@ -390,6 +403,11 @@ __global__ __launch_bounds__(kThreads128, 1) void chunk128_fwd_kernel(
             // settled here: left pending, every later use of S would wait on
             // the whole memory counter (and so on the chunks' stores)
             __builtin_amdgcn_s_waitcnt(0);
+        } else if (wk.ident) {
+#pragma unroll
+            for (int jt = 0; jt < kJT; ++jt)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) S[jt][q] = col == 16 * jt + 4 * g + q ? 1.f : 0.f;
         }
         // the state chain and the inverse wave issue before the producers
         // when several waves of a SIMD are ready
@@ -401,8 +419,8 @@ __global__ __launch_bounds__(kThreads128, 1) void chunk128_fwd_kernel(
             __syncthreads();
         }
         store_y(nch - 1);
-        if (sT) {
-            float* dst = sT + (size_t)bh * NN + (size_t)col * kN128;
+        if (wk.fin) {
+            float* dst = wk.fin + (size_t)col * kN128;
 #pragma unroll
             for (int jt = 0; jt < kJT; ++jt)
                 *reinterpret_cast<float4*>(dst + 16 * jt + 4 * g) =
@@ -435,24 +453,51 @@ __global__ __launch_bounds__(kThreads128, 1) void chunk128_fwd_kernel(
 }
 
 template <bool kAB, bool kCk>
-hipError_t launch_k(const FwdArgs& p, hipStream_t stream) {
-    chunk128_fwd_kernel<kAB, kCk><<<dim3(2 * p.B * p.H), dim3(kThreads128), 0, stream>>>(
+hipError_t launch_k(const FwdArgs& p, int nitems, int pass, const FwdSplit& sp, hipStream_t stream) {
+    if (nitems == 0) return hipSuccess;
+    chunk128_fwd_kernel<kAB, kCk><<<dim3(2 * nitems), dim3(kThreads128), 0, stream>>>(
         p.B, p.T, p.H, static_cast<const bf16_t*>(p.r), static_cast<const bf16_t*>(p.w),
         static_cast<const bf16_t*>(p.k), static_cast<const bf16_t*>(p.v),
         static_cast<const bf16_t*>(p.a), static_cast<const bf16_t*>(p.b), p.s0,
-        static_cast<bf16_t*>(p.y), p.sT, p.ckpt);
+        static_cast<bf16_t*>(p.y), p.sT, p.ckpt, nitems, pass, sp.split_from, sp.nseg, sp.seg_len,
+        sp.states);
     return hipGetLastError();
+}
+
+hipError_t launch_pass(const FwdArgs& p, int nitems, int pass, const FwdSplit& sp, hipStream_t stream) {
+    if (p.a) return p.ckpt ? launch_k<true, true>(p, nitems, pass, sp, stream)
+                           : launch_k<true, false>(p, nitems, pass, sp, stream);
+    return p.ckpt ? launch_k<false, true>(p, nitems, pass, sp, stream)
+                  : launch_k<false, false>(p, nitems, pass, sp, stream);
 }
 
 }  // namespace
 
 hipError_t launch_chunk_fwd128(const FwdArgs& p, hipStream_t stream) {
+    return launch_chunk_fwd128_split(p, FwdSplit{p.B * p.H, 1, p.T, nullptr}, stream);
+}
+
+hipError_t launch_chunk_fwd128_split(const FwdArgs& p, const FwdSplit& sp, hipStream_t stream) {
     if (!p.bf16 || p.N != kN128 || p.tape || p.T <= 0 || !p.y || (long long)p.B * p.H * 2 > INT32_MAX)
         return hipErrorInvalidValue;
     if ((p.a == nullptr) != (p.b == nullptr)) return hipErrorInvalidValue;
-    if (p.B * p.H == 0) return hipSuccess;
-    if (p.a) return p.ckpt ? launch_k<true, true>(p, stream) : launch_k<true, false>(p, stream);
-    return p.ckpt ? launch_k<false, true>(p, stream) : launch_k<false, false>(p, stream);
+    const int nbh = p.B * p.H;
+    const int nsplit = nbh - sp.split_from;
+    if (nsplit < 0 || (nsplit > 0 && (sp.nseg < 2 || sp.seg_len % WKV7_TAPE_BLOCK != 0 || sp.seg_len <= 0 ||
+                                       (long long)(sp.nseg - 1) * sp.seg_len >= p.T || !sp.states)))
+        return hipErrorInvalidValue;
+    if ((long long)2 * (sp.split_from + (long long)nsplit * (2 * sp.nseg - 3 > 0 ? 2 * sp.nseg - 3 : 0)) > INT32_MAX)
+        return hipErrorInvalidValue;
+    if (nbh == 0) return hipSuccess;
+    // Pass 0: whole heads, each split head's segment 0 and its map runs; then
+    // the entry states composed in fp32; pass 1: the segments from them.
+    hipError_t e = launch_pass(p, sp.split_from + (nsplit > 0 ? nsplit * (2 * sp.nseg - 3) : 0), 0, sp, stream);
+    if (e != hipSuccess || nsplit == 0) return e;
+    if (sp.nseg > 2) {
+        e = launch_seg_combine_n(kN128, nsplit, sp.nseg, sp.states, stream);
+        if (e != hipSuccess) return e;
+    }
+    return launch_pass(p, nsplit * (sp.nseg - 1), 1, sp, stream);
 }
 
 }  // namespace wkv7

@@ -95,6 +95,9 @@ hipError_t launch_chunk_fwd(const FwdArgs& p, int chunk_len, hipStream_t stream)
 // The chunked forward at N = 128 (wkv7_chunk128.hip): each head's value rows
 // over two workgroups; y, sT and ckpt as in FwdArgs, no tape.
 hipError_t launch_chunk_fwd128(const FwdArgs& p, hipStream_t stream);
+// The same under a segment plan (maps only; FwdSplit below).
+struct FwdSplit;
+hipError_t launch_chunk_fwd128_split(const FwdArgs& p, const FwdSplit& split, hipStream_t stream);
 
 // Segment plan of the chunked forward, split in time.  Heads [0, split_from)
 // run whole; heads [split_from, B*H) run as nseg >= 2 segments of seg_len

@@ -228,7 +228,8 @@ def test_split_static_validation(L):
     assert f(ctypes.byref(d), *args, -17, None) == wk.WKV7_ERR_INVALID_ARG
     assert f(ctypes.byref(d), *[FAKE] * 5, FAKE + 8, None, FAKE, None, None, 4, None) == \
         wk.WKV7_ERR_INVALID_ARG
-    assert f(ctypes.byref(wk.make_desc(1, 256, 1, 128, wk.WKV7_BF16, 16)), *args, 4, None) == \
+    # the chunked form at N = 128 splits by maps only
+    assert f(ctypes.byref(wk.make_desc(1, 256, 1, 128, wk.WKV7_BF16, 16)), *args, -2, None) == \
         wk.WKV7_ERR_UNSUPPORTED
     big = wk.make_desc(4, 4096, 32, 64, wk.WKV7_BF16, 16)   # 128 heads x 16 segments x 3 maps
     assert wk.split_workspace_bytes(big, 16) > wk.STATIC_SCRATCH_BYTES

@@ -3,10 +3,9 @@
 The state expansion of "Millions of States: Designing a Scalable MoE
 Architecture with RWKV-7 Meta-learner" (Abstract) read as a larger head of the
 same recurrence.  At N = 128 the chunked forward splits each head's value rows
-over the waves of one workgroup (eight waves, when the heads fill the device)
-or of two (four waves each, when they do not): both launches are exercised
-below (320 heads and more take eight waves on a 256-compute-unit device).
-bf16 inputs with an fp32 state: max relative error <= 2e-2, cosine >= 0.9999.
+over two workgroups, each of which forms the chunk factors itself, and splits
+in time by affine maps.  bf16 inputs with an fp32 state: max relative error
+<= 2e-2, cosine >= 0.9999.
 """
 
 import numpy as np
@@ -92,9 +91,9 @@ def test_chunked_matches_scan(wk):
     assert_close(sc, ss, "bf16", "N=128 chunk vs scan sT")
 
 
-def test_many_heads_one_workgroup_per_head(wk):
-    """B=8, T=256, H=40 (320 heads: one eight-wave workgroup per head), every
-    head against the oracle."""
+def test_many_heads_several_rounds(wk):
+    """B=8, T=256, H=40 (320 heads, 640 workgroups: more than one round on the
+    device), every head against the oracle."""
     inp = synth.generate(8, 256, 40, N, dtype="bf16", seed=922, random_s0=True)
     y, sT, _ = _run(wk, inp)
     yr, sr = _ref(inp)
@@ -165,8 +164,9 @@ def test_forward_epilogue(wk):
 
 
 def test_what_n128_does_not_take(wk):
-    """No tape (the chunked backward takes N = 32 and 64), no explicit time
-    split, no chunked backward; the automatic split plan runs it unsplit."""
+    """No tape (the chunked backward takes N = 32 and 64), no sequential
+    segments, no chunked backward; too short for segments, the automatic
+    split plan runs it unsplit."""
     import torch
     inp = synth.generate(1, 64, 2, N, dtype="bf16", seed=960, random_s0=True)
     dev, s0 = _dev(inp)
@@ -179,7 +179,11 @@ def test_what_n128_does_not_take(wk):
     with pytest.raises(wk.WKV7Error):
         wk.forward(*dev, s0, chunk_len=16, want_tape=True)
     with pytest.raises(wk.WKV7Error):
-        wk.forward(*dev, s0, chunk_len=16, segments=2)
+        wk.forward(*dev, s0, chunk_len=16, want_tape=True, segments=2)
+    with pytest.raises(wk.WKV7Error):
+        wk.forward(*dev, s0, chunk_len=16, segments=-2)
+    with pytest.raises(wk.WKV7Error):
+        wk.split_plan(desc, -2)
     with pytest.raises(wk.WKV7Error):
         wk.backward(*dev, to_dev(inp.r, "bf16"), s0, None, None, chunk_len=16)
     y, sT, _ = _run(wk, inp, segments=0)
@@ -188,9 +192,54 @@ def test_what_n128_does_not_take(wk):
     assert_close(sT, sr, "bf16", "N=128 automatic plan sT")
 
 
+@pytest.mark.parametrize("segments", [2, 3, 5])
+def test_split_in_time_by_maps(wk, segments):
+    """Every head in 2, 3 or 5 time segments by affine maps (ragged T, random
+    s0; the composition is the scan's N = 128 kernel)."""
+    inp = synth.generate(2, 290, 3, N, dtype="bf16", seed=980 + segments, random_s0=True)
+    B, T, H, _ = inp.r.shape
+    desc = wk.make_desc(B, T, H, N, wk.WKV7_BF16, 16)
+    assert wk.split_plan(desc, segments).nseg == segments
+    assert wk.split_workspace_bytes(desc, segments) == B * H * 3 * segments * N * N * 4
+    y, sT, _ = _run(wk, inp, segments=segments)
+    yr, sr = _ref(inp)
+    assert_close(y, yr, "bf16", f"N=128 split {segments} y")
+    assert_close(sT, sr, "bf16", f"N=128 split {segments} sT")
+
+
+def test_split_decay_only_and_static_scratch(wk):
+    inp = synth.generate(1, 300, 2, N, dtype="bf16", seed=990, random_s0=True)
+    y, sT, _ = _run(wk, inp, decay_only=True, segments=3)
+    yr, sr = _ref(inp, decay_only=True)
+    assert_close(y, yr, "bf16", "N=128 split a=b=0 y")
+    assert_close(sT, sr, "bf16", "N=128 split a=b=0 sT")
+    y, sT, _ = _run(wk, inp, segments=4, static_scratch=True)
+    yr, sr = _ref(inp)
+    assert_close(y, yr, "bf16", "N=128 split in the static scratch y")
+    assert_close(sT, sr, "bf16", "N=128 split in the static scratch sT")
+
+
+def test_split_automatic_few_heads(wk):
+    """B=1, T=4096, H=12 (24 workgroups unsplit): the library's plan splits
+    every head; sampled heads against the oracle, the rest against the unsplit run."""
+    inp = synth.generate(1, 4096, 12, N, dtype="bf16", seed=995, random_s0=True)
+    desc = wk.make_desc(1, 4096, 12, N, wk.WKV7_BF16, 16)
+    plan = wk.split_plan(desc, 0)
+    assert plan.nseg >= 2 and plan.split_from == 0
+    y, sT, _ = _run(wk, inp, segments=0)
+    yu, su, _ = _run(wk, inp)
+    assert_close(y, yu, "bf16", "N=128 automatic split vs unsplit y")
+    assert_close(sT, su, "bf16", "N=128 automatic split vs unsplit sT")
+    pairs = [(0, 0), (0, 7), (0, 11)]
+    sel = [oracle.select_heads(x, pairs) for x in inp.tensors()]
+    yr, sr = oracle.forward(*sel, oracle.select_heads(inp.s0, pairs, state=True))
+    assert_close(oracle.select_heads(y, pairs), yr, "bf16", "N=128 automatic split y")
+    assert_close(oracle.select_heads(sT, pairs, state=True), sr, "bf16", "N=128 automatic split sT")
+
+
 def test_1_5b_width_sampled(wk):
     """B=8, T=4096, H=16 (the 1.5B model's channels as 128-wide heads: 128
-    heads, two four-wave workgroups each, the bench's N = 128 workload),
+    heads, two workgroups each, the bench's N = 128 workload),
     random s0: sampled heads at full T against the oracle, every output finite."""
     inp = synth.generate(8, 4096, 16, N, dtype="bf16", seed=970, random_s0=True)
     y, sT, _ = _run(wk, inp)
