@@ -7,7 +7,7 @@
 namespace wkv7 {
 
 struct FwdArgs {
-    int B, T, H, N;   // N: 32, 64 or 128 for the sequential scan; 64 for the chunked form
+    int B, T, H, N;   // N: 32, 64 or 128 (the chunked form at 128: no tape)
     bool bf16;
     const void *r, *w, *k, *v, *a, *b;
     const float* s0;  // may be null
