@@ -319,7 +319,7 @@ def summarize_sq_n128(pmc_dirs, reps, cmd):
     """profiles/sq_counters_chunked_fwd_n128.md from the two SQ_COUNTERS passes of
     --workload chunked_fwd_n128: the N = 128 chunked forward's timed launches."""
     c = _sq_per_kernel(pmc_dirs, int(reps),
-                       lambda n: "chunk128_fwd_kernel" if "chunk128_fwd_kernel<true, false>" in n else None)
+                       lambda n: "chunk128_fwd_kernel" if "chunk128_fwd_kernel<2, true, false>" in n else None)
     c = c["chunk128_fwd_kernel"]
     g = lambda n: c.get(n, float("nan"))
     busy, nlds = g("SQ_BUSY_CU_CYCLES"), g("SQ_INSTS_LDS")

@@ -228,7 +228,7 @@ int run_forward(const wkv7_desc* d, const void* r, const void* w, const void* k,
     if (d->N == 128) {
         // No tape at N = 128 (the chunked backward takes N = 32 and 64).
         if (tape) return WKV7_ERR_UNSUPPORTED;
-        return from_hip(wkv7::launch_chunk_fwd128(p, stream));
+        return from_hip(wkv7::launch_chunk_fwd128(p, device_cus(), stream));
     }
     return from_hip(wkv7::launch_chunk_fwd(p, d->chunk_len, stream));
 }
@@ -367,7 +367,7 @@ int run_forward_split(const wkv7_desc* desc, const void* r, const void* w, const
                           r, w, k, v, a, b, s0, y, sT, tape};
     const wkv7::FwdSplit sp{plan.split_from, plan.nseg, plan.seg_len, static_cast<float*>(workspace)};
     if (desc->chunk_len == 0) return from_hip(wkv7::launch_seq_fwd_split(p, sp, s));
-    if (no_tape(desc)) return from_hip(wkv7::launch_chunk_fwd128_split(p, sp, s));
+    if (no_tape(desc)) return from_hip(wkv7::launch_chunk_fwd128_split(p, sp, device_cus(), s));
     if (plan.mode == 1) {
         float* states = static_cast<float*>(workspace);
         int* sync = reinterpret_cast<int*>(states + (size_t)desc->B * desc->H * desc->N * desc->N);

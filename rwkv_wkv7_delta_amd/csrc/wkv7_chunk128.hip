@@ -64,16 +64,27 @@ constexpr int kR128 = kN128 + 8;
 constexpr int kJT = kN128 / 16;   // key tiles of 16
 constexpr int kK2 = kN128 / 32;   // 32-deep contraction steps over the keys
 constexpr int kSlots128 = 3;
-constexpr int kRows = 64;          // value rows per workgroup (two per head)
-constexpr int kCons = kRows / 16;  // state-chain waves
-constexpr int kProd = 8;           // producer waves (one key group of 16 each)
-constexpr int kThreads128 = 64 * (kCons + kProd + 1);
-constexpr int kPieces = 6 * kL * (kN128 / 8) / (64 * kProd);   // 16-byte raw pieces per producer thread
+// kParts workgroups per head (2, or 1 when two would not fit the device at
+// once): 128 / kParts value rows each, 16 per state-chain wave; 8 producers of
+// one key group each (two parts) or 4 of two (one part); either way 13 waves.
+template <int kParts>
+struct Shape128 {
+    static_assert(kParts == 1 || kParts == 2, "one or two workgroups per head");
+    static constexpr int kRows = kN128 / kParts;          // value rows per workgroup
+    static constexpr int kCons = kRows / 16;              // state-chain waves
+    static constexpr int kProd = kParts == 2 ? 8 : 4;     // producer waves
+    static constexpr int kGroups = 8 / kProd;             // key groups of 16 per producer
+    static constexpr int kPieces = 6 * kL * (kN128 / 8) / (64 * kProd);   // 16-byte raw pieces per producer thread
+    // the producers that form Aak, Arb, Ark (the last three)
+    static constexpr int P_AK = kProd - 3, P_RB = kProd - 2, P_RK = kProd - 1;
+};
+constexpr int kThreads128 = 64 * 13;
+static_assert(64 * (Shape128<1>::kCons + Shape128<1>::kProd + 1) == kThreads128 &&
+                  64 * (Shape128<2>::kCons + Shape128<2>::kProd + 1) == kThreads128,
+              "thirteen waves either way");
 
 enum { R_R = 0, R_W = 1, R_K = 2, R_A = 3, R_B = 4, R_V = 5 };
-// products of a chunk in a slot (Aab stays in the inverse wave), by the
-// producer that forms them
-enum { P_AK = 5, P_RB = 6, P_RK = 7 };
+// (the products of a chunk in a slot: Aak, Arb, Ark; Aab stays in the inverse wave)
 
 // What one chunk passes from E and the products to the state chain.
 struct Slot128 {
@@ -88,6 +99,7 @@ struct Slot128 {
 struct BK128 {
     bf16_t Bh[kL][kR128], Kh[kL][kR128];
 };
+template <int kRows>
 struct __align__(16) Smem128 {
     bf16_t raw[2][6][kL][kR128];    // r, w, k, a, b, v of two chunks (bf16 bits)
     Slot128 sl[kSlots128];
@@ -109,21 +121,24 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // diag(G_L) S0^T + Kb^T V; the inverse wave idles); kCk: also the fp32 state
 // entering every chunk, [B][H][ceil(T/16)][N][N] (row = value channel).
 // nitems: the launch's items of the segment plan (two workgroups each).
-template <bool kAB, bool kCk>
+template <int kParts, bool kAB, bool kCk>
 __global__ __launch_bounds__(kThreads128, 1) void chunk128_fwd_kernel(
     int B, int T, int H, const bf16_t* __restrict__ r, const bf16_t* __restrict__ w,
     const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const bf16_t* __restrict__ a,
     const bf16_t* __restrict__ b, const float* __restrict__ s0, bf16_t* __restrict__ y_all,
     float* __restrict__ sT, float* __restrict__ ckpt_all, int nitems, int pass, int split_from,
     int nseg, int seg_len, float* __restrict__ states) {
+    using Sh = Shape128<kParts>;
+    constexpr int kRows = Sh::kRows, kCons = Sh::kCons, kProd = Sh::kProd, kPieces = Sh::kPieces;
+    constexpr int P_AK = Sh::P_AK, P_RB = Sh::P_RB, P_RK = Sh::P_RK;
     constexpr size_t NN = (size_t)kN128 * kN128;
-    __shared__ Smem128 sm;
+    __shared__ Smem128<kRows> sm;
 
     // Workgroups go to the eight XCDs in turn (u to XCD u mod 8).  Groups of 8
-    // items take 16 consecutive workgroups, part-major, so that the two parts
+    // items take 8 kParts consecutive workgroups, part-major, so that the parts
     // of an item share an XCD and run at about the same time.
     const int u = blockIdx.x;
-    const int grp = u / 16, within = u % 16;
+    const int grp = u / (8 * kParts), within = u % (8 * kParts);
     const int m = min(8, nitems - 8 * grp);
     const int part = within / m;
     const Work wk = work_of<kN128>(8 * grp + within % m, pass, T, s0, sT, split_from, nseg, seg_len, states);
@@ -143,26 +158,29 @@ __global__ __launch_bounds__(kThreads128, 1) void chunk128_fwd_kernel(
     // matrix-core product runs with part of EXEC off).
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);
     const int l16 = lane & 15, g = lane >> 4;
-    const int col = rb + 16 * (wave & 3) + l16;   // value row of this lane (state chain)
+    const int col = rb + 16 * (wave & (kCons - 1)) + l16;   // value row of this lane (state chain)
     const bf16x4 ident = identity_b(g, l16);
 
     // ---- raw rows (producers): 6 vectors x 16 tokens x 16 pieces of 16 bytes
-    // per chunk; producer thread p takes pieces p + 512 e (e = 0 .. 2): vector
-    // 2 e + p / 256, token (p / 16) % 16, columns 8 (p % 16) .. +7 (a token row
-    // of a vector is 16 consecutive threads).
+    // per chunk; producer thread p takes pieces p + 64 kProd e: with 8
+    // producers (e = 0 .. 2) vector 2 e + p / 256, with 4 (e = 0 .. 5) vector
+    // e; token (p / 16) % 16, columns 8 (p % 16) .. +7 (a token row of a vector
+    // is 16 consecutive threads).
     const int ptid = tid - 64 * kCons;
     const int ld_t = (ptid >> 4) & 15, ld_c8 = ptid & 15;
-    const int vhi = __builtin_amdgcn_readfirstlane(ptid >> 8);   // 0 or 1 for producers
+    const int vhi = kProd == 8 ? __builtin_amdgcn_readfirstlane(ptid >> 8) : 0;   // 0 or 1 for producers
+    auto vec_of = [&](int e) __attribute__((always_inline)) { return kProd == 8 ? 2 * e + vhi : e; };
     auto src_of = [&](int e) __attribute__((always_inline)) -> const bf16_t* {
         const bf16_t* const src6[6] = {r, w, k, a, b, v};
-        return vhi ? src6[2 * e + 1] : src6[2 * e];
+        if constexpr (kProd == 8) return vhi ? src6[2 * e + 1] : src6[2 * e];
+        else return src6[e];
     };
     auto load_raw = [&](int c, u32x4 (&o)[kPieces]) __attribute__((always_inline)) {
         const int t = min((c_begin + c) * kL + ld_t, t_end - 1);
         const size_t off = tok_off<kN128>(bb, t, hh, T, H) + 8 * ld_c8;
 #pragma unroll
         for (int e = 0; e < kPieces; ++e) {
-            const int vi = 2 * e + vhi;
+            const int vi = vec_of(e);
             if (kAB || (vi != R_A && vi != R_B)) {
                 o[e] = *reinterpret_cast<const u32x4*>(src_of(e) + off);
             } else {
@@ -175,7 +193,7 @@ __global__ __launch_bounds__(kThreads128, 1) void chunk128_fwd_kernel(
         const bool ok = (c_begin + c) * kL + ld_t < t_end;
 #pragma unroll
         for (int e = 0; e < kPieces; ++e) {
-            const int vi = 2 * e + vhi;
+            const int vi = vec_of(e);
             const unsigned pad = vi == R_W ? 0x3F803F80u : 0u;   // padding: w = 1, the rest 0
             const u32x4 padv = {pad, pad, pad, pad};
             *reinterpret_cast<u32x4*>(&sm.raw[c & 1][vi][ld_t][8 * ld_c8]) = ok ? o[e] : padv;
@@ -358,11 +376,11 @@ __global__ __launch_bounds__(kThreads128, 1) void chunk128_fwd_kernel(
     };
 
 
-    // Staged read-outs of chunk c: 16 tokens x 64 values, 8 pieces of 16 bytes
-    // per token, from the first 128 threads of the state chain.
+    // Staged read-outs of chunk c: 16 tokens x kRows values, kRows / 8 pieces
+    // of 16 bytes per token, from the first 2 kRows threads of the state chain.
     auto store_y = [&](int c) __attribute__((always_inline)) {
         if (y && tid < 2 * kRows) {
-            const int row = tid / 8, piece = tid % 8;
+            const int row = tid / (kRows / 8), piece = tid % (kRows / 8);
             const int tt = (c_begin + c) * kL + row;
             if (c >= 0 && tt < t_end)
                 store_stream(y + tok_off<kN128>(bb, tt, hh, T, H) + rb + 8 * piece,
@@ -437,7 +455,8 @@ __global__ __launch_bounds__(kThreads128, 1) void chunk128_fwd_kernel(
         for (int i = 0; i < nch + 2; ++i) {
             stash_raw(i + 1, ring);
             load_raw(i + 2, ring);
-            stage_E(i, pw);
+#pragma unroll
+            for (int e = 0; e < Sh::kGroups; ++e) stage_E(i, pw + kProd * e);
             if (kAB ? pw >= P_AK : pw == P_RK) stage_products(i - 1, pw);
             __syncthreads();
         }
@@ -452,10 +471,10 @@ __global__ __launch_bounds__(kThreads128, 1) void chunk128_fwd_kernel(
     }
 }
 
-template <bool kAB, bool kCk>
+template <int kParts, bool kAB, bool kCk>
 hipError_t launch_k(const FwdArgs& p, int nitems, int pass, const FwdSplit& sp, hipStream_t stream) {
     if (nitems == 0) return hipSuccess;
-    chunk128_fwd_kernel<kAB, kCk><<<dim3(2 * nitems), dim3(kThreads128), 0, stream>>>(
+    chunk128_fwd_kernel<kParts, kAB, kCk><<<dim3(kParts * nitems), dim3(kThreads128), 0, stream>>>(
         p.B, p.T, p.H, static_cast<const bf16_t*>(p.r), static_cast<const bf16_t*>(p.w),
         static_cast<const bf16_t*>(p.k), static_cast<const bf16_t*>(p.v),
         static_cast<const bf16_t*>(p.a), static_cast<const bf16_t*>(p.b), p.s0,
@@ -464,20 +483,27 @@ hipError_t launch_k(const FwdArgs& p, int nitems, int pass, const FwdSplit& sp, 
     return hipGetLastError();
 }
 
-hipError_t launch_pass(const FwdArgs& p, int nitems, int pass, const FwdSplit& sp, hipStream_t stream) {
-    if (p.a) return p.ckpt ? launch_k<true, true>(p, nitems, pass, sp, stream)
-                           : launch_k<true, false>(p, nitems, pass, sp, stream);
-    return p.ckpt ? launch_k<false, true>(p, nitems, pass, sp, stream)
-                  : launch_k<false, false>(p, nitems, pass, sp, stream);
+template <int kParts>
+hipError_t launch_pass_p(const FwdArgs& p, int nitems, int pass, const FwdSplit& sp, hipStream_t stream) {
+    if (p.a) return p.ckpt ? launch_k<kParts, true, true>(p, nitems, pass, sp, stream)
+                           : launch_k<kParts, true, false>(p, nitems, pass, sp, stream);
+    return p.ckpt ? launch_k<kParts, false, true>(p, nitems, pass, sp, stream)
+                  : launch_k<kParts, false, false>(p, nitems, pass, sp, stream);
+}
+// Two workgroups per item while they fit the device in one round, else one.
+hipError_t launch_pass(const FwdArgs& p, int nitems, int pass, const FwdSplit& sp, int ncu,
+                       hipStream_t stream) {
+    if (ncu > 0 && 2LL * nitems > ncu) return launch_pass_p<1>(p, nitems, pass, sp, stream);
+    return launch_pass_p<2>(p, nitems, pass, sp, stream);
 }
 
 }  // namespace
 
-hipError_t launch_chunk_fwd128(const FwdArgs& p, hipStream_t stream) {
-    return launch_chunk_fwd128_split(p, FwdSplit{p.B * p.H, 1, p.T, nullptr}, stream);
+hipError_t launch_chunk_fwd128(const FwdArgs& p, int ncu, hipStream_t stream) {
+    return launch_chunk_fwd128_split(p, FwdSplit{p.B * p.H, 1, p.T, nullptr}, ncu, stream);
 }
 
-hipError_t launch_chunk_fwd128_split(const FwdArgs& p, const FwdSplit& sp, hipStream_t stream) {
+hipError_t launch_chunk_fwd128_split(const FwdArgs& p, const FwdSplit& sp, int ncu, hipStream_t stream) {
     if (!p.bf16 || p.N != kN128 || p.tape || p.T <= 0 || !p.y || (long long)p.B * p.H * 2 > INT32_MAX)
         return hipErrorInvalidValue;
     if ((p.a == nullptr) != (p.b == nullptr)) return hipErrorInvalidValue;
@@ -491,13 +517,13 @@ hipError_t launch_chunk_fwd128_split(const FwdArgs& p, const FwdSplit& sp, hipSt
     if (nbh == 0) return hipSuccess;
     // Pass 0: whole heads, each split head's segment 0 and its map runs; then
     // the entry states composed in fp32; pass 1: the segments from them.
-    hipError_t e = launch_pass(p, sp.split_from + (nsplit > 0 ? nsplit * (2 * sp.nseg - 3) : 0), 0, sp, stream);
+    hipError_t e = launch_pass(p, sp.split_from + (nsplit > 0 ? nsplit * (2 * sp.nseg - 3) : 0), 0, sp, ncu, stream);
     if (e != hipSuccess || nsplit == 0) return e;
     if (sp.nseg > 2) {
         e = launch_seg_combine_n(kN128, nsplit, sp.nseg, sp.states, stream);
         if (e != hipSuccess) return e;
     }
-    return launch_pass(p, nsplit * (sp.nseg - 1), 1, sp, stream);
+    return launch_pass(p, nsplit * (sp.nseg - 1), 1, sp, ncu, stream);
 }
 
 }  // namespace wkv7

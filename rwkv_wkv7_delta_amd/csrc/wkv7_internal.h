@@ -93,11 +93,12 @@ inline bool chunk_fwd_epilogue_fits(int T, int H) { return (long long)T * H * 64
 hipError_t launch_seq_fwd(const FwdArgs& p, hipStream_t stream);
 hipError_t launch_chunk_fwd(const FwdArgs& p, int chunk_len, hipStream_t stream);
 // The chunked forward at N = 128 (wkv7_chunk128.hip): each head's value rows
-// over two workgroups; y, sT and ckpt as in FwdArgs, no tape.
-hipError_t launch_chunk_fwd128(const FwdArgs& p, hipStream_t stream);
+// over two workgroups, or one when two would not fit the device's `ncu`
+// compute units at once; y, sT and ckpt as in FwdArgs, no tape.
+hipError_t launch_chunk_fwd128(const FwdArgs& p, int ncu, hipStream_t stream);
 // The same under a segment plan (maps only; FwdSplit below).
 struct FwdSplit;
-hipError_t launch_chunk_fwd128_split(const FwdArgs& p, const FwdSplit& split, hipStream_t stream);
+hipError_t launch_chunk_fwd128_split(const FwdArgs& p, const FwdSplit& split, int ncu, hipStream_t stream);
 
 // Segment plan of the chunked forward, split in time.  Heads [0, split_from)
 // run whole; heads [split_from, B*H) run as nseg >= 2 segments of seg_len

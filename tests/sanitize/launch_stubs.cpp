@@ -6,8 +6,8 @@
 namespace wkv7 {
 hipError_t launch_seq_fwd(const FwdArgs&, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_chunk_fwd(const FwdArgs&, int, hipStream_t) { return hipErrorInvalidValue; }
-hipError_t launch_chunk_fwd128(const FwdArgs&, hipStream_t) { return hipErrorInvalidValue; }
-hipError_t launch_chunk_fwd128_split(const FwdArgs&, const FwdSplit&, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_chunk_fwd128(const FwdArgs&, int, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_chunk_fwd128_split(const FwdArgs&, const FwdSplit&, int, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_chunk_fwd_split(const FwdArgs&, int, const FwdSplit&, hipStream_t) {
     return hipErrorInvalidValue;
 }
