@@ -76,7 +76,8 @@ extern "C" {
    splits in time by maps only (wkv7_forward_split: segments <= -2 return
    WKV7_ERR_UNSUPPORTED); it writes fp32 checkpoints (wkv7_forward_ckpt), from
    which wkv7_backward_ckpt (chunk_len = 0) trains.  It splits each head's
-   value rows over two workgroups, which form the chunk factors each. */
+   value rows over two workgroups, which form the chunk factors each, while
+   those fit the device at once (else one workgroup per head). */
 #define WKV7_HEAD_SIZE 64
 #define WKV7_TAPE_CHUNK 16       /* tokens per chunk of the backward */
 #define WKV7_TAPE_BLOCK 32       /* tokens per state saved in the forward tape */

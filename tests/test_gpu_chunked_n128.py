@@ -249,3 +249,29 @@ def test_1_5b_width_sampled(wk):
     assert_close(oracle.select_heads(y, pairs), yr, "bf16", "N=128 1.5B width y")
     assert_close(oracle.select_heads(sT, pairs, state=True), sr, "bf16", "N=128 1.5B width sT")
     assert np.all(np.isfinite(y)) and np.all(np.isfinite(sT))
+
+
+def test_many_heads_checkpoints(wk):
+    """B=8, T=96, H=40 (one workgroup per head): the chunked form's fp32
+    checkpoints against the scan's (same layout) and y against the oracle."""
+    import torch
+    inp = synth.generate(8, 96, 40, N, dtype="bf16", seed=1001, random_s0=True)
+    dev, s0 = _dev(inp)
+    yc, _, ckc = wk.forward(*dev, s0, chunk_len=16, want_ckpt=True)
+    ys, _, cks = wk.forward(*dev, s0, chunk_len=0, want_ckpt=True)
+    torch.cuda.synchronize()
+    assert_close(to_np(ckc), to_np(cks), "bf16", "N=128 320 heads ckpt vs scan")
+    pairs = [(0, 0), (3, 21), (7, 39)]
+    sel = [oracle.select_heads(x, pairs) for x in inp.tensors()]
+    yr, _ = oracle.forward(*sel, oracle.select_heads(inp.s0, pairs, state=True))
+    assert_close(oracle.select_heads(to_np(yc), pairs), yr, "bf16", "N=128 320 heads ckpt run y")
+
+
+def test_many_heads_split_explicit(wk):
+    """B=8, T=256, H=40 in 3 segments by maps: 960 items in the first launch,
+    one workgroup each (map runs from the identity with v = 0 and from zero)."""
+    inp = synth.generate(8, 256, 40, N, dtype="bf16", seed=1002, random_s0=True)
+    y, sT, _ = _run(wk, inp, segments=3)
+    yr, sr = _ref(inp)
+    assert_close(y, yr, "bf16", "N=128 320 heads split y")
+    assert_close(sT, sr, "bf16", "N=128 320 heads split sT")
