@@ -752,6 +752,26 @@ def secondary(torch, wk, dev):
     few["tokens_per_s"] = round(B * T / few["split_ms"] * 1e3, 1)
     n128["12_heads_split"] = {"B": B, "T": T, "H": H, **few}
     del ins, s0, y, ws
+    # the training step at N = 128 (0.19B token shape): the chunked forward
+    # writing fp32 checkpoints, then the sequential reverse pass from them
+    B, T, H = 4, 1024, 12
+    ins = _dev_inputs(torch, (B, T, H, 128), dev, 5)
+    dyn = torch.randn(B, T, H, 128, device=dev).bfloat16()
+    grads = [torch.empty_like(ins[0]) for _ in range(6)]
+    ds0 = torch.empty(B, H, 128, 128, device=dev)
+
+    def step128():
+        yv, _, ck = wk.forward(*ins, None, chunk_len=16, want_state=False, want_ckpt=True)
+        wk.backward(*ins, dyn, None, None, None, chunk_len=0, ckpt=ck, grads=grads, ds0=ds0)
+
+    for _ in range(2):
+        step128()
+    ms = float(np.median([_time(torch, step128, 2) for _ in range(5)]))
+    n128["train_step_0.19b_tokens"] = {"B": B, "T": T, "H": H, "ms": round(ms, 4),
+                                       "tokens_per_s": round(B * T / ms * 1e3, 1),
+                                       "note": "wkv7_forward_ckpt (chunked) + wkv7_backward_ckpt "
+                                               "(sequential reverse pass), all 7 gradients"}
+    del ins, dyn, grads, ds0
     res["chunked_fwd_n128"] = {"workload": "N=128 bf16, s0~0.1N(0,1), L=16, returns sT (1.5b_width: "
                                            "median of 25 repetitions of 4 calls; the others of 10; "
                                            "12_heads_split: wkv7_forward_split, automatic plan)",
