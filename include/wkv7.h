@@ -195,7 +195,9 @@ int wkv7_forward_ckpt(const wkv7_desc *desc, const void *r, const void *w, const
  *                 scan: every head by maps when B*H*N/16 workgroups fill at
  *                 most half of it; the chunked form at N = 128: every head
  *                 by maps when its two workgroups per head fill at most a
- *                 third of it; at N = 128 in at most 4 segments; else, or
+ *                 third of it, and with more heads than compute units those
+ *                 of the last round when they fill at most a quarter of it;
+ *                 at N = 128 in at most 4 segments; else, or
  *                 when T is too short for segments of 128 tokens, no split);
  *              1 or -1: no split (exactly wkv7_forward);
  *              n >= 2: every head in up to n segments by maps;

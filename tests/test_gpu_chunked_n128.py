@@ -275,3 +275,24 @@ def test_many_heads_split_explicit(wk):
     yr, sr = _ref(inp)
     assert_close(y, yr, "bf16", "N=128 320 heads split y")
     assert_close(sT, sr, "bf16", "N=128 320 heads split sT")
+
+
+def test_split_partial_round_automatic(wk):
+    """B=8, T=512, H=36 (288 heads: one workgroup each, a last round of 32 on a
+    256-compute-unit device): the automatic plan splits the last round's heads
+    by maps; all heads against the unsplit run, sampled ones against the oracle."""
+    inp = synth.generate(8, 512, 36, N, dtype="bf16", seed=1003, random_s0=True)
+    desc = wk.make_desc(8, 512, 36, N, wk.WKV7_BF16, 16)
+    plan = wk.split_plan(desc, 0)
+    y, sT, _ = _run(wk, inp, segments=0)
+    yu, su, _ = _run(wk, inp)
+    assert_close(y, yu, "bf16", "N=128 partial-round split vs unsplit y")
+    assert_close(sT, su, "bf16", "N=128 partial-round split vs unsplit sT")
+    pairs = [(0, 0), (7, 35), (7, 20), (7, 10)]   # (7, 20..35): heads of the split last round
+    sel = [oracle.select_heads(x, pairs) for x in inp.tensors()]
+    yr, sr = oracle.forward(*sel, oracle.select_heads(inp.s0, pairs, state=True))
+    assert_close(oracle.select_heads(y, pairs), yr, "bf16", "N=128 partial-round split y")
+    assert_close(oracle.select_heads(sT, pairs, state=True), sr, "bf16", "N=128 partial-round split sT")
+    import torch
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert plan.split_from == 256 and plan.nseg >= 2
