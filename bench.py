@@ -724,7 +724,11 @@ def secondary(torch, wk, dev):
         ins = _dev_inputs(torch, (B, T, H, 128), dev, 3)
         s0 = 0.1 * torch.randn(B, H, 128, 128, device=dev)
         y = torch.empty_like(ins[0])
-        fn = lambda: wk.forward(*ins, s0, chunk_len=16, out=y)
+        # (wkv7_forward_split, automatic plan: at 320 heads the last round's
+        # heads split in time; at 48 heads no split)
+        d128 = wk.make_desc(B, T, H, 128, wk.WKV7_BF16, 16)
+        ws128 = torch.empty(max(wk.split_workspace_bytes(d128, 0) // 4, 4), device=dev)
+        fn = lambda: wk.forward(*ins, s0, chunk_len=16, out=y, segments=0, workspace=ws128)
         for _ in range(3):
             fn()
         ms = float(np.median([_time(torch, fn, 4) for _ in range(10)]))
@@ -732,8 +736,9 @@ def secondary(torch, wk, dev):
         n128[name] = {"B": B, "T": T, "H": H, "ms": round(ms, 4),
                       "tokens_per_s": round(B * T / ms * 1e3, 1),
                       "alg_GBs": round(nbytes / ms / 1e6, 1),
-                      "frac_hbm": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
-        del ins, s0, y
+                      "frac_hbm": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4),
+                      "plan_nseg": int(wk.split_plan(d128, 0).nseg)}
+        del ins, s0, y, ws128
     # few heads (B=1, T=4096, H=12: 24 workgroups unsplit), split in time by the
     # automatic plan
     B, T, H = 1, 4096, 12
@@ -773,8 +778,9 @@ def secondary(torch, wk, dev):
                                                "(sequential reverse pass), all 7 gradients"}
     del ins, dyn, grads, ds0
     res["chunked_fwd_n128"] = {"workload": "N=128 bf16, s0~0.1N(0,1), L=16, returns sT (1.5b_width: "
-                                           "median of 25 repetitions of 4 calls; the others of 10; "
-                                           "12_heads_split: wkv7_forward_split, automatic plan)",
+                                           "wkv7_forward, median of 25 repetitions of 4 calls; the others "
+                                           "of 10; h40, 0.19b_tokens, 12_heads_split: "
+                                           "wkv7_forward_split, automatic plan)",
                                **n128}
     # The step after the read-out (current-token term, per-head normalisation,
     # gate) at the 2.9B-model shape: on its own (HBM-bound: y, r, k, v, g read,
